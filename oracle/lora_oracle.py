@@ -1,0 +1,174 @@
+"""Plain float64 CPU oracle for the LoRA linear layer -- TEST INFRASTRUCTURE.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this module.  It shares no code with the HIP library or its Python
+binding, and the product path never calls it.
+
+Everything here is the textbook definition written out in numpy float64 on
+the inputs as given (promoted exactly to float64).  The d x d product B.A is
+never formed except in `merged_weight`, which exists for the deployment
+identity and for tests on tiny shapes.
+
+Sources (the four web pages about Unsloth; page titles as printed):
+  [P1] "UnSloth加速库集成：编译级优化带来的性能飞跃" (UnSloth integration:
+       compile-level optimisation), section "为什么标准LoRA会慢？" (why
+       standard LoRA is slow): dW = B A with A in R^{r x d}, B in R^{d x r},
+       forward h = W x + B (A x).
+  [P3] "Unsloth — 微调 2-5x 加速", section "核心要点" (core points), item 2:
+       the backward products are re-associated so that only rank-r
+       intermediates exist; item 3: 4-bit weights are dequantised inside the
+       matmul.
+  [P4] "ms-swift高效微调组合：LoRA+UnSloth提速实践", section 1.2 "梯度计算
+       绕过Autograd": LoRA gradients written in closed form (the printed
+       formulas drop the input and the scale; the forms below are the exact
+       vector-Jacobian products of the forward).
+  [P2] "ms-swift框架下UnSloth与Liger-Kernel优化实战", section "UnSloth：让
+       LoRA真正“低秩”起来": the backbone W is frozen, so no dW exists.
+
+Readings where the pages are silent or garbled:
+  * scale s = lora_alpha / r multiplies the low-rank term (the pages show
+    lora_alpha as a config knob but no formula);
+  * one token per row: X[M,K] holds tokens x d_in, W[N,K] is d_out x d_in,
+    A[r,K], B[N,r]; H = X W^T + s (X A^T) B^T is P1's h = W x + B(A x) with
+    x a column of X^T;
+  * no bias, no dropout.
+"""
+from __future__ import annotations
+
+from statistics import NormalDist
+
+import numpy as np
+
+__all__ = [
+    "lora_scale", "forward", "backward", "backward_dx", "backward_lora",
+    "merged_weight", "bf16_round", "f16_to_f64", "codebook4", "dequant4",
+]
+
+
+def _f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64)
+
+
+def lora_scale(alpha: float, r: int) -> float:
+    """s = lora_alpha / r."""
+    return float(alpha) / float(r)
+
+
+def forward(X, W, A, B, s):
+    """[P1] forward, row form: U = X A^T, H = X W^T + s U B^T.
+
+    Returns (H, U) in float64.
+    """
+    X, W, A, B = _f64(X), _f64(W), _f64(A), _f64(B)
+    U = X @ A.T
+    H = X @ W.T + float(s) * (U @ B.T)
+    return H, U
+
+
+def backward_dx(dY, W, A, B, s):
+    """Input gradient of L = <dY, H>: dX = dY W + s (dY B) A  ([P3] item 2 order).
+
+    Row-local: rows of dX depend only on the same rows of dY.
+    """
+    dY, W, A, B = _f64(dY), _f64(W), _f64(A), _f64(B)
+    V = dY @ B
+    return dY @ W + float(s) * (V @ A)
+
+
+def backward_lora(dY, X, A, B, s):
+    """Adapter gradients of L = <dY, H>  ([P4] section 1.2, corrected).
+
+    dA = s (dY B)^T X  [r,K];  dB = s dY^T (X A^T)  [N,r].  Both sum over tokens.
+    """
+    dY, X, A, B = _f64(dY), _f64(X), _f64(A), _f64(B)
+    V = dY @ B
+    U = X @ A.T
+    dA = float(s) * (V.T @ X)
+    dB = float(s) * (dY.T @ U)
+    return dA, dB
+
+
+def backward(dY, X, W, A, B, s):
+    """(dX, dA, dB); W is frozen so no dW is produced ([P2])."""
+    dX = backward_dx(dY, W, A, B, s)
+    dA, dB = backward_lora(dY, X, A, B, s)
+    return dX, dA, dB
+
+
+def merged_weight(W, A, B, s):
+    """W' = W + s B A  (fold the adapter into the frozen weight; tiny shapes only)."""
+    return _f64(W) + float(s) * (_f64(B) @ _f64(A))
+
+
+# ----------------------------------------------------------------------------
+# Number formats
+# ----------------------------------------------------------------------------
+
+def bf16_round(x) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even); returns float32.
+
+    bfloat16 keeps the top 16 bits of the float32 encoding.  Rounding adds
+    0x7FFF plus the lowest kept bit before truncating.  NaN stays NaN.
+    """
+    f = np.ascontiguousarray(x, dtype=np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    keep_lsb = (u >> 16) & 1
+    rounded = ((u + 0x7FFF + keep_lsb) >> 16) << 16
+    out = (rounded & 0xFFFFFFFF).astype(np.uint32).view(np.float32)
+    return np.where(np.isnan(f), f, out)
+
+
+def f16_to_f64(h) -> np.ndarray:
+    """IEEE binary16 bit patterns (or float16 values) to float64, exactly.
+
+    Decoded from the fields: sign, 5-bit exponent (bias 15), 10-bit mantissa.
+    """
+    bits = np.asarray(h)
+    bits = bits.view(np.uint16) if bits.dtype == np.float16 else bits.astype(np.uint16)
+    b = bits.astype(np.int64)
+    sign = np.where(b >> 15, -1.0, 1.0)
+    e = (b >> 10) & 0x1F
+    m = (b & 0x3FF).astype(np.float64)
+    normal = sign * np.ldexp(1.0 + m / 1024.0, (e - 15).astype(np.int64))
+    sub = sign * np.ldexp(m / 1024.0, -14)
+    inf_nan = np.where(m == 0, sign * np.inf, np.nan)
+    return np.where(e == 0, sub, np.where(e == 31, inf_nan, normal))
+
+
+def codebook4() -> np.ndarray:
+    """16-entry 4-bit codebook: c_i = Phi^-1((i+0.5)/16) / Phi^-1(15.5/16).
+
+    Evaluated in float64 and rounded once to float32 (returned as float32).
+    """
+    nd = NormalDist()
+    top = nd.inv_cdf(15.5 / 16.0)
+    vals = [nd.inv_cdf((i + 0.5) / 16.0) / top for i in range(16)]
+    return np.array(vals, dtype=np.float64).astype(np.float32)
+
+
+def dequant4(codes, absmax, codebook, out: str = "bf16") -> np.ndarray:
+    """Dequantise 4-bit codes ([P3] core point 3: int4 weights restored inside the matmul).
+
+    codes[N, K/2] uint8: element k is the low nibble of byte k/2 when k is
+    even, the high nibble when k is odd.  absmax[N, K/64]: fp16, one per block
+    of 64 consecutive elements along K.  Each weight is the float32 product
+    codebook[code] * float32(absmax) (IEEE, round to nearest even), then for
+    out="bf16" rounded to bfloat16; out="f32" keeps the float32 product.
+    Returns float32 values [N, K].
+    """
+    codes = np.asarray(codes, dtype=np.uint8)
+    N, half = codes.shape
+    K = 2 * half
+    idx = np.empty((N, K), dtype=np.int64)
+    idx[:, 0::2] = codes & 0x0F
+    idx[:, 1::2] = codes >> 4
+    cb = np.asarray(codebook, dtype=np.float32)
+    scale = f16_to_f64(absmax).astype(np.float32)          # exact: fp16 embeds in fp32
+    per_elem = np.repeat(scale, K // scale.shape[1], axis=1)
+    # float64 product of two float32 values is exact; one rounding to float32 = IEEE fp32 multiply
+    prod = (cb[idx].astype(np.float64) * per_elem.astype(np.float64)).astype(np.float32)
+    if out == "f32":
+        return prod
+    if out == "bf16":
+        return bf16_round(prod)
+    raise ValueError("out must be 'bf16' or 'f32'")

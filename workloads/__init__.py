@@ -1,0 +1,191 @@
+"""Seeded synthetic inputs for the LoRA linear layer (shared by tests, bench and smoke).
+
+This module only *draws* inputs: it holds none of the layer's arithmetic (no
+product, no gradient, no dequantisation).  Both the HIP path and the CPU
+oracle are fed from here, so the two sides see exactly the same numbers.
+
+Shapes follow the pages' workloads:
+  * hidden 4096, rank 8 ("q_proj, hidden_size=4096, rank=8": page "ms-swift高效
+    微调组合：LoRA+UnSloth提速实践", section 1.2 "算子融合");
+  * max_length 2048 (same page, section 2.2, experiment table);
+  * MLP shapes 4096 <-> 11008 and a full decoder layer (Qwen/Llama-7B family,
+    pages' model choices), rank 16 / 64;
+  * 4-bit frozen weights with rank 16, alpha 32 (page "ms-swift框架下UnSloth与
+    Liger-Kernel优化实战", code listing with load_in_4bit=True).
+The pages measure on a dataset with pretrained weights; seeded Gaussian draws
+of the same shapes stand in for them (no dataset or checkpoint is used).
+
+Distributions: X, dY ~ N(0, 1); W, B ~ N(0, 0.02^2); A ~ N(0, 1/d_in), i.e.
+standard deviations 1, 0.02 and 1/sqrt(d_in).  Draw order per linear is
+X, W, A, B, dY with numpy PCG64, each a float32 standard normal then scaled in
+float32.  The float32 draws are what the oracle consumes; the GPU consumes
+their bf16 round-to-nearest-even images (bf16 mode) or the float32 values
+themselves (fp32 debug mode).
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from statistics import NormalDist
+
+import numpy as np
+
+__all__ = [
+    "LinearShape", "Workload", "WORKLOADS", "make_linear_inputs", "codebook4_f32",
+    "quantize4", "workload",
+]
+
+
+@dataclasses.dataclass(frozen=True)
+class LinearShape:
+    """One LoRA linear: tokens M, d_in K, d_out N, rank r, lora_alpha, seed."""
+    name: str
+    M: int
+    K: int
+    N: int
+    r: int
+    alpha: float
+    seed: int
+    quant4: bool = False
+
+    @property
+    def scale(self) -> float:
+        """lora_alpha / r (the conventional LoRA scale)."""
+        return self.alpha / self.r
+
+    def flops(self) -> int:
+        """Algorithmic FLOPs of one forward + backward (no dW, no recompute)."""
+        M, K, N, r = self.M, self.K, self.N, self.r
+        return 4 * M * N * K + 6 * M * r * (K + N)
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    linears: tuple
+    description: str
+
+    def flops(self) -> int:
+        return sum(l.flops() for l in self.linears)
+
+    @property
+    def tokens(self) -> int:
+        return self.linears[0].M
+
+
+def _decoder_layer() -> tuple:
+    dims = [("q", 4096, 4096), ("k", 4096, 1024), ("v", 4096, 1024), ("o", 4096, 4096),
+            ("gate", 4096, 14336), ("up", 4096, 14336), ("down", 14336, 4096)]
+    return tuple(LinearShape(f"decoder_{n}", 4096, k, nn, 64, 16.0, 1300 + i)
+                 for i, (n, k, nn) in enumerate(dims))
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", (LinearShape("tiny", 64, 256, 256, 8, 32.0, 1000),),
+                     "M=64, d_in=d_out=256, r=8, alpha=32"),
+    "attn_proj_4096": Workload(
+        "attn_proj_4096", (LinearShape("attn_proj_4096", 4096, 4096, 4096, 8, 32.0, 1001),),
+        "M=4096 (batch 2 x seq 2048), d_in=d_out=4096, r=8, alpha=32"),
+    "mlp_11008": Workload(
+        "mlp_11008",
+        (LinearShape("mlp_gate", 8192, 4096, 11008, 16, 32.0, 1200),
+         LinearShape("mlp_up", 8192, 4096, 11008, 16, 32.0, 1201),
+         LinearShape("mlp_down", 8192, 11008, 4096, 16, 32.0, 1202)),
+        "gate/up 4096->11008 and down 11008->4096, M=8192, r=16, alpha=32"),
+    "decoder_layer_r64": Workload(
+        "decoder_layer_r64", _decoder_layer(),
+        "seven LoRA linears q,k,v,o,gate,up,down, M=4096, r=64, alpha=16"),
+    "qlora_28672": Workload(
+        "qlora_28672", (LinearShape("qlora_28672", 2048, 8192, 28672, 16, 32.0, 1004, True),),
+        "4-bit frozen W 8192->28672 (blocks of 64 along d_in, fp16 absmax), M=2048, r=16, alpha=32"),
+}
+
+
+def workload(name: str) -> Workload:
+    return WORKLOADS[name]
+
+
+def make_linear_inputs(shape: LinearShape, *, M: int | None = None) -> dict:
+    """Seeded float32 draws X[M,K], W[N,K], A[r,K], B[N,r], dY[M,N].
+
+    ``M`` may be lowered to draw only the first rows of X and dY; the draw
+    order then differs, so use it only for standalone small cases.
+    """
+    M = shape.M if M is None else M
+    K, N, r = shape.K, shape.N, shape.r
+    rng = np.random.Generator(np.random.PCG64(shape.seed))
+
+    def normal(rows, cols, std):
+        out = rng.standard_normal((rows, cols), dtype=np.float32)
+        out *= np.float32(std)
+        return out
+
+    X = normal(M, K, 1.0)
+    W = normal(N, K, 0.02)
+    A = normal(r, K, 1.0 / math.sqrt(K))
+    B = normal(N, r, 0.02)
+    dY = normal(M, N, 1.0)
+    return {"X": X, "W": W, "A": A, "B": B, "dY": dY}
+
+
+# ----------------------------------------------------------------------------
+# 4-bit weight format of the QLoRA workload (input preparation only).
+#
+# The frozen weight is stored as 4-bit codes in blocks of 64 along d_in with
+# one fp16 absmax per block; the 16-entry codebook holds the normal quantiles
+# Phi^-1((i + 0.5)/16) divided by Phi^-1(15.5/16), so that it spans [-1, 1].
+# The pages only say the frozen weights are int4 and that dequantisation is
+# fused into the matmul (page "Unsloth — 微调 2-5x 加速", section "核心要点",
+# item 3); the concrete format is this workload's.  The codebook is passed to
+# the library as an input array, like the codes and the absmax values.
+# ----------------------------------------------------------------------------
+
+QBLOCK = 64
+
+
+def codebook4_f32() -> np.ndarray:
+    """The 16 codebook values, float64 quantiles rounded once to float32."""
+    nd = NormalDist()
+    top = nd.inv_cdf(15.5 / 16.0)
+    return np.array([nd.inv_cdf((i + 0.5) / 16.0) / top for i in range(16)], dtype=np.float32)
+
+
+def quantize4(W: np.ndarray, codebook: np.ndarray | None = None):
+    """Quantise W[N,K] (K % 64 == 0) to (codes[N,K/2] u8, absmax[N,K/64] fp16).
+
+    absmax is the fp16 rounding of max|w| over each 64-block; each code is the
+    nearest codebook entry to w/absmax (computed in float64 with the rounded
+    absmax), ties to the lower index.  Element k even goes to the low nibble of
+    byte k/2, k odd to the high nibble.
+    """
+    N, K = W.shape
+    if K % QBLOCK:
+        raise ValueError("K must be a multiple of 64")
+    cb = (codebook4_f32() if codebook is None else codebook).astype(np.float64)
+    if np.any(np.diff(cb) <= 0):
+        raise ValueError("codebook must be strictly increasing")
+    # nearest entry with ties to the lower index == count of midpoints strictly below y
+    mids = (cb[:-1] + cb[1:]) * 0.5
+    codes = np.empty((N, K // 2), dtype=np.uint8)
+    absmax = np.empty((N, K // QBLOCK), dtype=np.float16)
+    step = max(1, (1 << 22) // K)
+    for r0 in range(0, N, step):
+        w = W[r0:r0 + step].astype(np.float64)
+        blocks = w.reshape(w.shape[0], K // QBLOCK, QBLOCK)
+        am = np.abs(blocks).max(axis=2).astype(np.float16)
+        absmax[r0:r0 + step] = am
+        scale = am.astype(np.float64)[:, :, None]
+        with np.errstate(invalid="ignore", divide="ignore"):
+            y = np.where(scale > 0, blocks / np.where(scale > 0, scale, 1.0), 0.0)
+        q = np.searchsorted(mids, y.reshape(w.shape[0], K), side="left").astype(np.uint8)
+        codes[r0:r0 + step] = q[:, 0::2] | (q[:, 1::2] << 4)
+    return codes, absmax
+
+
+def make_qlora_inputs(shape: LinearShape, *, M: int | None = None) -> dict:
+    """Draws as make_linear_inputs, plus the 4-bit encoding of W."""
+    d = make_linear_inputs(shape, M=M)
+    cb = codebook4_f32()
+    codes, absmax = quantize4(d["W"], cb)
+    d.update(codes=codes, absmax=absmax, codebook=cb)
+    return d
