@@ -1,0 +1,147 @@
+/*
+ * lora_linear.h -- C ABI of the fused LoRA linear layer for AMD MI355X (gfx950).
+ *
+ * The layer (page "UnSloth加速库集成：编译级优化带来的性能飞跃", section
+ * "为什么标准LoRA会慢？"): h = W x + B (A x), with A in R^{r x d_in},
+ * B in R^{d_out x r} and r << d.  The adapter term is multiplied by the scale
+ * s = alpha / r.  W is frozen: no gradient for W exists (page "ms-swift框架下
+ * UnSloth与Liger-Kernel优化实战", section "UnSloth：让LoRA真正“低秩”起来").
+ *
+ * Row-major convention used by every entry point (one token per row):
+ *   X  [M, K]  tokens x d_in          W  [N, K]  d_out x d_in (nn.Linear layout)
+ *   A  [r, K]                         B  [N, r]
+ *   H  [M, N] = X W^T + s (X A^T) B^T
+ *   dY [M, N] upstream gradient       dX [M, K] = dY W + s (dY B) A
+ *   dA [r, K] = s (dY B)^T X          dB [N, r] = s dY^T (X A^T)
+ *   U  [M, r] = X A^T (float32; saved by the forward for the backward)
+ * All matrices are dense with leading dimension equal to the row length.
+ *
+ * Memory: every pointer is caller-owned device memory (except `desc`, which is
+ * host memory).  The library allocates nothing, keeps no state between calls,
+ * never modifies an input, and enqueues all work on `stream` (a hipStream_t
+ * passed as void*; NULL means the null stream).  Calls return once the work is
+ * enqueued; device faults surface at the caller's next synchronisation.
+ * Outputs must not overlap inputs.  Device pointers must be 16-byte aligned.
+ *
+ * Errors: every function returns a lora_status.  Arguments are validated on
+ * the host before any HIP call, so an error other than LORA_ERR_HIP means
+ * nothing was enqueued.  lora_last_error() gives a text description of the
+ * last failure on the calling thread.  Nothing aborts or throws across the ABI.
+ */
+#ifndef LORA_LINEAR_H
+#define LORA_LINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum lora_status {
+    LORA_OK = 0,
+    LORA_ERR_INVALID_ARG = 1,        /* null pointer, non-positive size, bad dtype, aliasing, non-finite alpha */
+    LORA_ERR_UNSUPPORTED = 2,        /* shape outside the supported range (see below) */
+    LORA_ERR_MISALIGNED = 3,         /* a device pointer is not 16-byte aligned */
+    LORA_ERR_WORKSPACE_TOO_SMALL = 4,/* ws_bytes < lora_linear_workspace_size() */
+    LORA_ERR_HIP = 5                 /* a HIP launch failed; see lora_last_error() */
+} lora_status;
+
+typedef enum lora_dtype {
+    LORA_DTYPE_BF16 = 0,  /* bf16 storage, float32 accumulation (the hot path) */
+    LORA_DTYPE_F32 = 1    /* float32 storage and arithmetic (debug / checking mode) */
+} lora_dtype;
+
+/* flags */
+#define LORA_FLAG_ACCUM_GRADS 0x1u   /* backward adds into dA, dB instead of overwriting */
+
+/*
+ * Problem descriptor (host memory).
+ *   M tokens, K = d_in, N = d_out, r = rank, alpha = lora_alpha (s = alpha/r).
+ *   dtype applies to X, W, A, B, H, dY, dX, dA, dB.  U is always float32.
+ * Supported range: 1 <= r <= 128; M, K, N >= 1; K % 8 == 0 and N % 8 == 0;
+ * every matrix has fewer than 2^31 elements; the 4-bit entry points also need
+ * K % 64 == 0.  Outside it: LORA_ERR_UNSUPPORTED.
+ */
+typedef struct lora_linear_desc {
+    int64_t M, K, N, r;
+    float alpha;
+    int32_t dtype;    /* lora_dtype */
+    uint32_t flags;   /* LORA_FLAG_* */
+} lora_linear_desc;
+
+/* Bytes of device workspace any fwd/bwd call with this descriptor needs
+ * (the same figure for the plain and the 4-bit entry points).  May be 0. */
+lora_status lora_linear_workspace_size(const lora_linear_desc* desc, size_t* bytes);
+
+/*
+ * Forward, fused: H = X W^T + s (X A^T) B^T in one kernel (page "ms-swift高效
+ * 微调组合：LoRA+UnSloth提速实践", section 1.2 "算子融合": Linear, LoRA_A,
+ * LoRA_B and the add in a single launch).  The rank-r product U = X A^T is
+ * formed on chip, inside the main product's K loop, and never goes through HBM.
+ *   U_save: optional float32 [M, r]; when non-NULL receives U for the backward.
+ *   ws:     device workspace of ws_bytes bytes (NULL allowed when 0 is needed).
+ */
+lora_status lora_linear_fwd(const lora_linear_desc* desc,
+                            const void* X, const void* W, const void* A, const void* B,
+                            void* H, float* U_save,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Backward (page "Unsloth — 微调 2-5x 加速", section "核心要点", item 2: the
+ * product is re-associated as A(B dY) so that only [M, r] intermediates exist;
+ * page "ms-swift高效微调组合：LoRA+UnSloth提速实践", section 1.2: adapter
+ * gradients in closed form without autograd).
+ *   dX = dY W + s (dY B) A        (NULL: skipped)
+ *   dA = s (dY B)^T X,  dB = s dY^T U   (overwritten, or accumulated with
+ *                                        LORA_FLAG_ACCUM_GRADS)
+ *   U_saved: float32 [M, r] from lora_linear_fwd, or NULL to recompute it from X.
+ * Reductions over tokens run in a fixed order: results are bitwise
+ * reproducible from run to run.
+ */
+lora_status lora_linear_bwd(const lora_linear_desc* desc,
+                            const void* dY, const void* X, const void* W,
+                            const void* A, const void* B, const float* U_saved,
+                            void* dX, void* dA, void* dB,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * 4-bit frozen weight (page "Unsloth — 微调 2-5x 加速", section "核心要点",
+ * item 3: 4-bit weights are dequantised inside the matmul, not copied out
+ * first).  W is replaced by
+ *   Wq       [N, K/2] uint8: element k in the low nibble of byte k/2 when k is
+ *            even, in the high nibble when k is odd;
+ *   absmax   [N, K/64] IEEE fp16 bit patterns, one per 64 consecutive k;
+ *   codebook [16] float32 (device memory).
+ * Weight value: bf16_rne(float32(codebook[code] * float32(absmax))) in bf16
+ * mode; the float32 product itself in f32 mode.  Requires K % 64 == 0.
+ */
+lora_status lora_qlinear_fwd(const lora_linear_desc* desc,
+                             const void* X, const uint8_t* Wq, const uint16_t* absmax,
+                             const float* codebook, const void* A, const void* B,
+                             void* H, float* U_save,
+                             void* ws, size_t ws_bytes, void* stream);
+
+lora_status lora_qlinear_bwd(const lora_linear_desc* desc,
+                             const void* dY, const void* X, const uint8_t* Wq,
+                             const uint16_t* absmax, const float* codebook,
+                             const void* A, const void* B, const float* U_saved,
+                             void* dX, void* dA, void* dB,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* Standalone dequantisation of the 4-bit format above into a dense W_out [N, K]
+ * (out_dtype LORA_DTYPE_BF16 or LORA_DTYPE_F32).  Requires K % 64 == 0. */
+lora_status lora_dequant4(const uint8_t* Wq, const uint16_t* absmax, const float* codebook,
+                          int64_t N, int64_t K, int32_t out_dtype, void* W_out, void* stream);
+
+/* Static text for a status code. */
+const char* lora_status_string(lora_status status);
+
+/* Text of the last failure on the calling thread ("" if none). */
+const char* lora_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LORA_LINEAR_H */

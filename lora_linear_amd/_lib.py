@@ -1,0 +1,73 @@
+"""ctypes loader for liblora_linear.so (the C ABI in include/lora_linear.h).
+
+Loading fails loudly when the library has not been built: there is no
+fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liblora_linear.so")
+
+LORA_OK = 0
+LORA_ERR_INVALID_ARG = 1
+LORA_ERR_UNSUPPORTED = 2
+LORA_ERR_MISALIGNED = 3
+LORA_ERR_WORKSPACE_TOO_SMALL = 4
+LORA_ERR_HIP = 5
+
+LORA_DTYPE_BF16 = 0
+LORA_DTYPE_F32 = 1
+
+LORA_FLAG_ACCUM_GRADS = 0x1
+
+EXPORTED = (
+    "lora_linear_workspace_size", "lora_linear_fwd", "lora_linear_bwd",
+    "lora_qlinear_fwd", "lora_qlinear_bwd", "lora_dequant4",
+    "lora_status_string", "lora_last_error",
+)
+
+
+class LoraLinearDesc(ctypes.Structure):
+    """Mirror of struct lora_linear_desc."""
+    _fields_ = [
+        ("M", ctypes.c_int64), ("K", ctypes.c_int64), ("N", ctypes.c_int64), ("r", ctypes.c_int64),
+        ("alpha", ctypes.c_float), ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32),
+    ]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load the library once and declare the signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it first (python -m lora_linear_amd.build); "
+            "the LoRA layer has no non-HIP implementation")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, sz, i32, i64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64
+    dp = ctypes.POINTER(LoraLinearDesc)
+    sig = {
+        "lora_linear_workspace_size": [dp, ctypes.POINTER(sz)],
+        "lora_linear_fwd": [dp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "lora_linear_bwd": [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "lora_qlinear_fwd": [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "lora_qlinear_bwd": [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "lora_dequant4": [vp, vp, vp, i64, i64, i32, vp, vp],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    lib.lora_status_string.argtypes = [ctypes.c_int]
+    lib.lora_status_string.restype = ctypes.c_char_p
+    lib.lora_last_error.argtypes = []
+    lib.lora_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib

@@ -1,0 +1,142 @@
+"""Python binding of the C ABI: same names, argument marshalling only.
+
+Each function takes torch tensors (or raw integer device addresses, or None
+for optional arguments), passes their addresses and the current HIP stream to
+liblora_linear.so, and raises LoraError when the library returns a status
+other than LORA_OK.  All arithmetic happens in the library's kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+
+import torch
+
+from . import _lib
+from ._lib import (LORA_DTYPE_BF16, LORA_DTYPE_F32, LORA_FLAG_ACCUM_GRADS,  # noqa: F401
+                   LoraLinearDesc)
+
+
+class LoraError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        lib = _lib.load()
+        self.status = status
+        text = lib.lora_status_string(status).decode()
+        detail = lib.lora_last_error().decode()
+        super().__init__(f"{where}: {text} (status {status}){': ' + detail if detail else ''}")
+
+
+@dataclasses.dataclass(frozen=True)
+class Desc:
+    """Problem descriptor (mirrors struct lora_linear_desc)."""
+    M: int
+    K: int
+    N: int
+    r: int
+    alpha: float
+    dtype: int = LORA_DTYPE_BF16
+    flags: int = 0
+
+    def c(self) -> LoraLinearDesc:
+        return LoraLinearDesc(self.M, self.K, self.N, self.r, float(self.alpha), self.dtype, self.flags)
+
+    @property
+    def scale(self) -> float:
+        return self.alpha / self.r
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"expected a tensor, an int address or None, got {type(t)!r}")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous (dense row-major)")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int, where: str):
+    if status != _lib.LORA_OK:
+        raise LoraError(status, where)
+
+
+def _ws(desc: Desc, ws, device):
+    if ws is not None:
+        return ws, (ws.numel() * ws.element_size() if isinstance(ws, torch.Tensor) else None)
+    nbytes = lora_linear_workspace_size(desc)
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device), nbytes
+
+
+def lora_linear_workspace_size(desc: Desc) -> int:
+    out = ctypes.c_size_t(0)
+    d = desc.c()
+    _check(_lib.load().lora_linear_workspace_size(ctypes.byref(d), ctypes.byref(out)), "lora_linear_workspace_size")
+    return int(out.value)
+
+
+def lora_linear_fwd(desc: Desc, X, W, A, B, H, U_save=None, ws=None, ws_bytes=None, stream=None):
+    """H = X W^T + s (X A^T) B^T (see include/lora_linear.h)."""
+    if ws is None:
+        ws, ws_bytes = _ws(desc, None, X.device)
+    elif ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    d = desc.c()
+    st = _lib.load().lora_linear_fwd(ctypes.byref(d), _ptr(X), _ptr(W), _ptr(A), _ptr(B), _ptr(H), _ptr(U_save),
+                                     _ptr(ws), ws_bytes, _stream(stream))
+    _check(st, "lora_linear_fwd")
+
+
+def lora_linear_bwd(desc: Desc, dY, X, W, A, B, U_saved, dX, dA, dB, ws=None, ws_bytes=None, stream=None):
+    """dX = dY W + s (dY B) A; dA = s (dY B)^T X; dB = s dY^T U (see include/lora_linear.h)."""
+    if ws is None:
+        ws, ws_bytes = _ws(desc, None, dY.device)
+    elif ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    d = desc.c()
+    st = _lib.load().lora_linear_bwd(ctypes.byref(d), _ptr(dY), _ptr(X), _ptr(W), _ptr(A), _ptr(B), _ptr(U_saved),
+                                     _ptr(dX), _ptr(dA), _ptr(dB), _ptr(ws), ws_bytes, _stream(stream))
+    _check(st, "lora_linear_bwd")
+
+
+def lora_qlinear_fwd(desc: Desc, X, Wq, absmax, codebook, A, B, H, U_save=None, ws=None, ws_bytes=None,
+                     stream=None):
+    """Forward with the frozen weight in the 4-bit format (codes, fp16 absmax, codebook)."""
+    if ws is None:
+        ws, ws_bytes = _ws(desc, None, X.device)
+    elif ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    d = desc.c()
+    st = _lib.load().lora_qlinear_fwd(ctypes.byref(d), _ptr(X), _ptr(Wq), _ptr(absmax), _ptr(codebook), _ptr(A),
+                                      _ptr(B), _ptr(H), _ptr(U_save), _ptr(ws), ws_bytes, _stream(stream))
+    _check(st, "lora_qlinear_fwd")
+
+
+def lora_qlinear_bwd(desc: Desc, dY, X, Wq, absmax, codebook, A, B, U_saved, dX, dA, dB, ws=None, ws_bytes=None,
+                     stream=None):
+    """Backward with the frozen weight in the 4-bit format."""
+    if ws is None:
+        ws, ws_bytes = _ws(desc, None, dY.device)
+    elif ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    d = desc.c()
+    st = _lib.load().lora_qlinear_bwd(ctypes.byref(d), _ptr(dY), _ptr(X), _ptr(Wq), _ptr(absmax), _ptr(codebook),
+                                      _ptr(A), _ptr(B), _ptr(U_saved), _ptr(dX), _ptr(dA), _ptr(dB), _ptr(ws),
+                                      ws_bytes, _stream(stream))
+    _check(st, "lora_qlinear_bwd")
+
+
+def lora_dequant4(Wq, absmax, codebook, N: int, K: int, out_dtype: int, W_out, stream=None):
+    """Dense W_out [N, K] from the 4-bit format."""
+    st = _lib.load().lora_dequant4(_ptr(Wq), _ptr(absmax), _ptr(codebook), N, K, out_dtype, _ptr(W_out),
+                                   _stream(stream))
+    _check(st, "lora_dequant4")

@@ -1,0 +1,110 @@
+"""torch.autograd glue over the C ABI (a drop-in LoRA linear for training loops).
+
+The module mirrors the pages' description of the accelerated layer: the
+frozen linear is replaced by a module whose forward and backward call the
+fused kernels directly, without autograd tracing the adapter products (page
+"UnSloth加速库集成：编译级优化带来的性能飞跃", section "技术四：无缝兼容生态",
+and page "ms-swift高效微调组合：LoRA+UnSloth提速实践", section 1.2).
+Only memory allocation and stream handling come from PyTorch.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import api
+from ._lib import LORA_DTYPE_BF16, LORA_DTYPE_F32
+
+_DTYPES = {torch.bfloat16: LORA_DTYPE_BF16, torch.float32: LORA_DTYPE_F32}
+
+
+def _desc(M, K, N, r, alpha, dtype) -> api.Desc:
+    if dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dtype} (bfloat16 or float32)")
+    return api.Desc(M, K, N, r, float(alpha), _DTYPES[dtype])
+
+
+class LoraLinearFunction(torch.autograd.Function):
+    """H = X W^T + (alpha/r) (X A^T) B^T with W frozen (no gradient for W)."""
+
+    @staticmethod
+    def forward(ctx, x, W, A, B, alpha):
+        lead = x.shape[:-1]
+        K = x.shape[-1]
+        X = x.reshape(-1, K).contiguous()
+        N, r = B.shape
+        desc = _desc(X.shape[0], K, N, r, alpha, X.dtype)
+        H = torch.empty((X.shape[0], N), dtype=X.dtype, device=X.device)
+        U = torch.empty((X.shape[0], r), dtype=torch.float32, device=X.device)
+        ws = torch.empty(max(api.lora_linear_workspace_size(desc), 1), dtype=torch.uint8, device=X.device)
+        api.lora_linear_fwd(desc, X, W.contiguous(), A.contiguous(), B.contiguous(), H, U, ws=ws)
+        ctx.save_for_backward(X, W, A, B, U)
+        ctx.desc = desc
+        ctx.lead = lead
+        return H.reshape(*lead, N)
+
+    @staticmethod
+    def backward(ctx, dH):
+        X, W, A, B, U = ctx.saved_tensors
+        desc = ctx.desc
+        dY = dH.reshape(-1, desc.N).to(X.dtype).contiguous()
+        dX = torch.empty_like(X) if ctx.needs_input_grad[0] else None
+        dA = torch.empty_like(A)
+        dB = torch.empty_like(B)
+        ws = torch.empty(max(api.lora_linear_workspace_size(desc), 1), dtype=torch.uint8, device=X.device)
+        api.lora_linear_bwd(desc, dY, X, W.contiguous(), A.contiguous(), B.contiguous(), U, dX, dA, dB, ws=ws)
+        dx = dX.reshape(*ctx.lead, desc.K) if dX is not None else None
+        return dx, None, dA, dB, None
+
+
+class QLoraLinearFunction(torch.autograd.Function):
+    """As LoraLinearFunction with W given by 4-bit codes, fp16 absmax and a codebook."""
+
+    @staticmethod
+    def forward(ctx, x, Wq, absmax, codebook, A, B, alpha):
+        lead = x.shape[:-1]
+        K = x.shape[-1]
+        X = x.reshape(-1, K).contiguous()
+        N, r = B.shape
+        desc = _desc(X.shape[0], K, N, r, alpha, X.dtype)
+        H = torch.empty((X.shape[0], N), dtype=X.dtype, device=X.device)
+        U = torch.empty((X.shape[0], r), dtype=torch.float32, device=X.device)
+        ws = torch.empty(max(api.lora_linear_workspace_size(desc), 1), dtype=torch.uint8, device=X.device)
+        api.lora_qlinear_fwd(desc, X, Wq, absmax, codebook, A.contiguous(), B.contiguous(), H, U, ws=ws)
+        ctx.save_for_backward(X, Wq, absmax, codebook, A, B, U)
+        ctx.desc = desc
+        ctx.lead = lead
+        return H.reshape(*lead, N)
+
+    @staticmethod
+    def backward(ctx, dH):
+        X, Wq, absmax, codebook, A, B, U = ctx.saved_tensors
+        desc = ctx.desc
+        dY = dH.reshape(-1, desc.N).to(X.dtype).contiguous()
+        dX = torch.empty_like(X) if ctx.needs_input_grad[0] else None
+        dA = torch.empty_like(A)
+        dB = torch.empty_like(B)
+        ws = torch.empty(max(api.lora_linear_workspace_size(desc), 1), dtype=torch.uint8, device=X.device)
+        api.lora_qlinear_bwd(desc, dY, X, Wq, absmax, codebook, A.contiguous(), B.contiguous(), U, dX, dA, dB, ws=ws)
+        dx = dX.reshape(*ctx.lead, desc.K) if dX is not None else None
+        return dx, None, None, None, dA, dB, None
+
+
+class LoraLinear(torch.nn.Module):
+    """Frozen W [out, in] plus trainable A [r, in], B [out, r]; s = alpha / r.
+
+    B starts at zero, so the layer starts as the frozen linear.
+    """
+
+    def __init__(self, in_features, out_features, r, alpha, weight=None, dtype=torch.bfloat16, device=None):
+        super().__init__()
+        self.r, self.alpha = r, float(alpha)
+        w = weight if weight is not None else torch.empty(out_features, in_features, dtype=dtype, device=device)
+        self.weight = torch.nn.Parameter(w.to(dtype=dtype, device=device), requires_grad=False)
+        self.lora_A = torch.nn.Parameter(torch.empty(r, in_features, dtype=dtype, device=device))
+        self.lora_B = torch.nn.Parameter(torch.zeros(out_features, r, dtype=dtype, device=device))
+        torch.nn.init.normal_(self.lora_A, std=1.0 / math.sqrt(in_features))
+
+    def forward(self, x):
+        return LoraLinearFunction.apply(x, self.weight, self.lora_A, self.lora_B, self.alpha)

@@ -1,0 +1,97 @@
+"""Helpers for GPU parity tests: move seeded inputs to the device, call the C
+ABI through the Python binding, and compare with the oracle.
+
+Tolerance metric (per output T): max|T_gpu - T_ref| / max|T_ref|.  When the
+reference is identically zero the GPU output must be exactly zero.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import lora_linear_amd as lla
+
+BF16_TOL = 1e-2     # bf16 storage, fp32 accumulation
+F32_TOL = 1e-5      # float32 checking mode
+DTYPES = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+def rel_err(got, ref) -> float:
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    den = np.abs(ref).max() if ref.size else 0.0
+    if den == 0.0:
+        return 0.0 if not np.any(got) else float("inf")
+    return float(np.abs(got - ref).max() / den)
+
+
+def to_dev(a: np.ndarray, dtype) -> torch.Tensor:
+    """float32 numpy -> device tensor (bf16: round to nearest even on the host)."""
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to(dtype).to("cuda")
+
+
+def to_np(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to(torch.float32).cpu().numpy()
+
+
+def run_linear(inp: dict, r: int, alpha: float, dtype: str = "bf16", *, quant: bool = False,
+               save_u: bool = True, want_dx: bool = True, flags: int = 0, grads_init=None,
+               dev_inputs: dict | None = None) -> dict:
+    """One forward + backward through the C ABI; returns numpy float32 outputs."""
+    tdt = DTYPES[dtype]
+    dd = dev_inputs if dev_inputs is not None else device_inputs(inp, dtype, quant)
+    X, A, B, dY = dd["X"], dd["A"], dd["B"], dd["dY"]
+    M, K = X.shape
+    N = B.shape[0]
+    desc = lla.Desc(M, K, N, r, alpha, lla.LORA_DTYPE_BF16 if dtype == "bf16" else lla.LORA_DTYPE_F32, flags)
+    ws = torch.empty(max(lla.lora_linear_workspace_size(desc), 1), dtype=torch.uint8, device="cuda")
+    H = torch.empty((M, N), dtype=tdt, device="cuda")
+    U = torch.empty((M, r), dtype=torch.float32, device="cuda")
+    dX = torch.empty((M, K), dtype=tdt, device="cuda") if want_dx else None
+    if grads_init is not None:
+        dA = to_dev(grads_init[0], tdt)
+        dB = to_dev(grads_init[1], tdt)
+    else:
+        dA = torch.empty((r, K), dtype=tdt, device="cuda")
+        dB = torch.empty((N, r), dtype=tdt, device="cuda")
+    if quant:
+        lla.lora_qlinear_fwd(desc, X, dd["codes"], dd["absmax"], dd["codebook"], A, B, H,
+                             U if save_u else None, ws=ws)
+        lla.lora_qlinear_bwd(desc, dY, X, dd["codes"], dd["absmax"], dd["codebook"], A, B,
+                             U if save_u else None, dX, dA, dB, ws=ws)
+    else:
+        W = dd["W"]
+        lla.lora_linear_fwd(desc, X, W, A, B, H, U if save_u else None, ws=ws)
+        lla.lora_linear_bwd(desc, dY, X, W, A, B, U if save_u else None, dX, dA, dB, ws=ws)
+    torch.cuda.synchronize()
+    out = {"H": to_np(H), "dA": to_np(dA), "dB": to_np(dB)}
+    if save_u:
+        out["U"] = to_np(U)
+    if want_dx:
+        out["dX"] = to_np(dX)
+    return out
+
+
+def device_inputs(inp: dict, dtype: str, quant: bool = False) -> dict:
+    tdt = DTYPES[dtype]
+    d = {k: to_dev(inp[k], tdt) for k in ("X", "A", "B", "dY")}
+    if quant:
+        d["codes"] = torch.from_numpy(inp["codes"]).to("cuda")
+        d["absmax"] = torch.from_numpy(np.ascontiguousarray(inp["absmax"]).view(np.int16)).to("cuda")
+        d["codebook"] = torch.from_numpy(inp["codebook"]).to("cuda")
+    else:
+        d["W"] = to_dev(inp["W"], tdt)
+    return d
+
+
+def host_view(inp: dict, dtype: str) -> dict:
+    """The values the GPU actually received, as float32 numpy (bf16-rounded for bf16)."""
+    if dtype == "f32":
+        return dict(inp)
+    out = dict(inp)
+    for k in ("X", "W", "A", "B", "dY"):
+        if k in inp:
+            out[k] = torch.from_numpy(inp[k]).to(torch.bfloat16).to(torch.float32).numpy()
+    return out

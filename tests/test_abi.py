@@ -1,0 +1,161 @@
+"""C ABI contract tests that need no GPU.
+
+The library must load, export every function include/lora_linear.h declares,
+and reject bad arguments with the documented status before any HIP call.
+Every call below fails validation, so nothing is ever enqueued.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import lora_linear_amd as lla
+from lora_linear_amd import _lib
+from lora_linear_amd._lib import LoraLinearDesc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lora_linear.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="library not built")
+
+ALIGNED = 0x10000          # a fake, 16-byte aligned address; never dereferenced
+MISALIGNED = 0x10008
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lora_\w+)\s*\(", text)))
+
+
+def test_header_declares_expected_api():
+    names = header_functions()
+    for n in ("lora_linear_fwd", "lora_linear_bwd", "lora_qlinear_fwd", "lora_qlinear_bwd",
+              "lora_dequant4", "lora_linear_workspace_size", "lora_status_string", "lora_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    for name in header_functions():
+        assert hasattr(lib, name), name
+    assert set(header_functions()) == set(_lib.EXPORTED)
+
+
+def test_struct_layout_matches_header():
+    assert ctypes.sizeof(LoraLinearDesc) == 4 * 8 + 4 + 4 + 4 + 4  # 4 x int64, float, int32, uint32, pad
+    assert LoraLinearDesc.alpha.offset == 32 and LoraLinearDesc.flags.offset == 40
+
+
+def lib():
+    return _lib.load()
+
+
+def desc(**kw):
+    d = dict(M=64, K=256, N=256, r=8, alpha=32.0, dtype=0, flags=0)
+    d.update(kw)
+    return LoraLinearDesc(d["M"], d["K"], d["N"], d["r"], d["alpha"], d["dtype"], d["flags"])
+
+
+def ws_size(d):
+    out = ctypes.c_size_t()
+    st = lib().lora_linear_workspace_size(ctypes.byref(d), ctypes.byref(out))
+    return st, out.value
+
+
+def fwd(d, X=ALIGNED, W=ALIGNED + 0x100, A=ALIGNED + 0x200, B=ALIGNED + 0x300, H=ALIGNED + 0x400,
+        U=None, ws=None, ws_bytes=0):
+    return lib().lora_linear_fwd(ctypes.byref(d) if d is not None else None, X, W, A, B, H, U, ws, ws_bytes, None)
+
+
+def bwd(d, dY=ALIGNED, X=ALIGNED + 0x100, W=ALIGNED + 0x200, A=ALIGNED + 0x300, B=ALIGNED + 0x400,
+        U=None, dX=ALIGNED + 0x500, dA=ALIGNED + 0x600, dB=ALIGNED + 0x700, ws=None, ws_bytes=0):
+    return lib().lora_linear_bwd(ctypes.byref(d), dY, X, W, A, B, U, dX, dA, dB, ws, ws_bytes, None)
+
+
+def test_status_strings():
+    L = lib()
+    for code in range(6):
+        assert L.lora_status_string(code)
+    assert L.lora_status_string(99) == b"unknown status"
+
+
+@pytest.mark.parametrize("field,value", [("M", 0), ("K", -8), ("N", 0), ("r", 0)])
+def test_nonpositive_sizes(field, value):
+    d = desc(**{field: value})
+    assert fwd(d) == _lib.LORA_ERR_INVALID_ARG
+    assert ws_size(d)[0] == _lib.LORA_ERR_INVALID_ARG
+    assert b"positive" in lib().lora_last_error()
+
+
+def test_null_desc_and_bad_dtype_and_flags():
+    assert fwd(None) == _lib.LORA_ERR_INVALID_ARG
+    assert fwd(desc(dtype=7)) == _lib.LORA_ERR_INVALID_ARG
+    assert fwd(desc(flags=0x80)) == _lib.LORA_ERR_INVALID_ARG
+    assert fwd(desc(alpha=float("nan"))) == _lib.LORA_ERR_INVALID_ARG
+    assert fwd(desc(alpha=float("inf"))) == _lib.LORA_ERR_INVALID_ARG
+
+
+def test_unsupported_shapes():
+    assert fwd(desc(r=129)) == _lib.LORA_ERR_UNSUPPORTED
+    assert fwd(desc(K=260)) == _lib.LORA_ERR_UNSUPPORTED
+    assert fwd(desc(N=12)) == _lib.LORA_ERR_UNSUPPORTED
+    assert fwd(desc(M=1 << 20, K=1 << 12)) == _lib.LORA_ERR_UNSUPPORTED      # 2^32 elements
+    d = desc(K=96)
+    assert lib().lora_qlinear_fwd(ctypes.byref(d), ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED,
+                                  None, None, 0, None) == _lib.LORA_ERR_UNSUPPORTED
+
+
+def test_null_and_misaligned_pointers():
+    d = desc()
+    assert fwd(d, X=None) == _lib.LORA_ERR_INVALID_ARG
+    assert fwd(d, H=None) == _lib.LORA_ERR_INVALID_ARG
+    assert fwd(d, W=MISALIGNED) == _lib.LORA_ERR_MISALIGNED
+    assert fwd(d, U=MISALIGNED) == _lib.LORA_ERR_MISALIGNED
+    assert bwd(d, dA=None) == _lib.LORA_ERR_INVALID_ARG
+    assert bwd(d, dX=MISALIGNED) == _lib.LORA_ERR_MISALIGNED
+
+
+def test_aliasing_rejected():
+    d = desc()
+    assert fwd(d, H=ALIGNED) == _lib.LORA_ERR_INVALID_ARG          # H aliases X
+    assert b"aliases" in lib().lora_last_error()
+    assert bwd(d, dA=ALIGNED + 0x700) == _lib.LORA_ERR_INVALID_ARG  # dA aliases dB
+
+
+def test_workspace_checks():
+    d = desc()
+    st, need = ws_size(d)
+    assert st == _lib.LORA_OK and need > 0
+    assert fwd(d, ws=ALIGNED + 0x1000, ws_bytes=need - 1) == _lib.LORA_ERR_WORKSPACE_TOO_SMALL
+    assert bwd(d, ws=None, ws_bytes=0) == _lib.LORA_ERR_WORKSPACE_TOO_SMALL
+    assert bwd(d, ws=ALIGNED + 0x1008, ws_bytes=need) == _lib.LORA_ERR_MISALIGNED
+    assert bwd(d, ws=None, ws_bytes=need) == _lib.LORA_ERR_INVALID_ARG
+
+
+def test_workspace_grows_with_problem():
+    small = ws_size(desc())[1]
+    big = ws_size(desc(M=4096, K=4096, N=4096))[1]
+    f32 = ws_size(desc(M=4096, K=4096, N=4096, dtype=1))[1]
+    assert big > small and f32 < big
+
+
+def test_dequant4_validation():
+    L = lib()
+    assert L.lora_dequant4(ALIGNED, ALIGNED + 0x100, ALIGNED + 0x200, 0, 64, 0, ALIGNED + 0x300, None) == \
+        _lib.LORA_ERR_INVALID_ARG
+    assert L.lora_dequant4(ALIGNED, ALIGNED + 0x100, ALIGNED + 0x200, 8, 96, 0, ALIGNED + 0x300, None) == \
+        _lib.LORA_ERR_UNSUPPORTED
+    assert L.lora_dequant4(ALIGNED, ALIGNED + 0x100, ALIGNED + 0x200, 8, 64, 5, ALIGNED + 0x300, None) == \
+        _lib.LORA_ERR_INVALID_ARG
+    assert L.lora_dequant4(ALIGNED, ALIGNED + 0x100, None, 8, 64, 0, ALIGNED + 0x300, None) == \
+        _lib.LORA_ERR_INVALID_ARG
+    assert L.lora_dequant4(ALIGNED, ALIGNED + 0x100, ALIGNED + 0x200, 8, 64, 0, ALIGNED, None) == \
+        _lib.LORA_ERR_INVALID_ARG
+
+
+def test_python_binding_raises():
+    with pytest.raises(lla.LoraError) as ei:
+        lla.lora_linear_workspace_size(lla.Desc(0, 8, 8, 1, 1.0))
+    assert ei.value.status == _lib.LORA_ERR_INVALID_ARG

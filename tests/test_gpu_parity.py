@@ -1,0 +1,254 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle.
+
+Graded check: the oracle runs on the float32 draws, the GPU on their bf16
+images (bf16 mode) or on the draws themselves (float32 checking mode); the
+bound is max|err|/max|ref| <= 1e-2 (bf16) or 1e-5 (float32).  A diagnostic
+check runs the oracle on exactly the values the GPU received: then the only
+error left is the final bf16 rounding of each output: bf16 keeps 8
+significant bits, so that rounding costs at most 2^-8 of the output's own
+magnitude, hence <= 2^-8 * max|ref| (plus float32 accumulation error).
+The graded bound is asserted on the workload shapes; the ragged and
+degenerate shapes (e.g. one token, rank 1) use the diagnostic bound, because
+the bf16 rounding of a few inputs can by itself move a short sum by >1 %.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_harness import (BF16_TOL, F32_TOL, device_inputs, host_view, rel_err, run_linear, to_dev,
+                         to_np)
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": BF16_TOL, "f32": F32_TOL}
+DIAG = {"bf16": 4e-3, "f32": F32_TOL}   # 2^-8 = 3.906e-3
+
+
+def oracle_all(inp, s, rows=None):
+    X, W, A, B, dY = inp["X"], inp["W"], inp["A"], inp["B"], inp["dY"]
+    Xr = X if rows is None else X[rows]
+    dYr = dY if rows is None else dY[rows]
+    H, U = oracle.forward(Xr, W, A, B, s)
+    dX = oracle.backward_dx(dYr, W, A, B, s)
+    dA, dB = oracle.backward_lora(dY, X, A, B, s)
+    return {"H": H, "U": U, "dX": dX, "dA": dA, "dB": dB}
+
+
+def check(got, ref, tol, rows=None, keys=("H", "U", "dX", "dA", "dB"), label=""):
+    errs = {}
+    for k in keys:
+        if k not in got:
+            continue
+        g = got[k] if rows is None or k in ("dA", "dB") else got[k][rows]
+        errs[k] = rel_err(g, ref[k])
+    bad = {k: e for k, e in errs.items() if not e <= tol}
+    assert not bad, f"{label} errors {errs} exceed {tol}"
+    return errs
+
+
+def shape(M, K, N, r, alpha=32.0, seed=7):
+    return workloads.LinearShape("case", M, K, N, r, alpha, seed)
+
+
+# ----------------------------------------------------------------------------- tiny
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_tiny_workload(dtype):
+    sh = workloads.workload("tiny").linears[0]
+    inp = workloads.make_linear_inputs(sh)
+    got = run_linear(inp, sh.r, sh.alpha, dtype)
+    check(got, oracle_all(inp, sh.scale), TOL[dtype], label="graded")
+    check(got, oracle_all(host_view(inp, dtype), sh.scale), DIAG[dtype], label="diagnostic")
+
+
+# ---------------------------------------------------------------- ragged / rank sweep
+RAGGED = [
+    (300, 136, 264, 5), (1, 8, 8, 1), (257, 520, 72, 16), (130, 64, 1000, 24),
+    (513, 264, 256, 48), (64, 128, 128, 64), (200, 192, 136, 100), (96, 256, 264, 128),
+    (520, 72, 520, 8), (33, 2056, 40, 3),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("M,K,N,r", RAGGED)
+def test_ragged_shapes(M, K, N, r, dtype):
+    sh = shape(M, K, N, r, seed=M * 7 + K + N + r)
+    inp = workloads.make_linear_inputs(sh)
+    got = run_linear(inp, r, sh.alpha, dtype)
+    check(got, oracle_all(host_view(inp, dtype), sh.scale), DIAG[dtype], label=f"{(M, K, N, r)} diagnostic")
+
+
+# ------------------------------------------------------------------- special cases
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_b_zero_is_plain_linear(dtype):
+    sh = shape(192, 264, 320, 8)
+    inp = workloads.make_linear_inputs(sh)
+    inp["B"] = np.zeros_like(inp["B"])
+    got = run_linear(inp, sh.r, sh.alpha, dtype)
+    ref = oracle_all(host_view(inp, dtype), sh.scale)
+    assert not np.any(got["dA"]), "dA must be exactly zero when B = 0"
+    assert np.any(got["dB"])
+    check(got, ref, DIAG[dtype], keys=("H", "dX", "dB"))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_a_zero_and_s_zero(dtype):
+    sh = shape(160, 136, 200, 16)
+    inp = workloads.make_linear_inputs(sh)
+    a0 = dict(inp, A=np.zeros_like(inp["A"]))
+    got = run_linear(a0, sh.r, sh.alpha, dtype)
+    assert not np.any(got["dB"]) and not np.any(got["U"])
+    check(got, oracle_all(host_view(a0, dtype), sh.scale), DIAG[dtype], keys=("H", "dX", "dA"))
+    got0 = run_linear(inp, sh.r, 0.0, dtype)
+    assert not np.any(got0["dA"]) and not np.any(got0["dB"])
+    check(got0, oracle_all(host_view(inp, dtype), 0.0), DIAG[dtype], keys=("H", "dX"))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_one_hot_probes_are_exact(dtype):
+    """B = 0 and one-hot rows: each output is a single exact product, so bit-exact."""
+    M, K, N, r = 300, 520, 264, 8
+    sh = shape(M, K, N, r)
+    inp = workloads.make_linear_inputs(sh)
+    hv = host_view(inp, dtype)
+    rng = np.random.default_rng(5)
+    kk = rng.integers(0, K, size=M)
+    nn = rng.integers(0, N, size=M)
+    X = np.zeros((M, K), np.float32); X[np.arange(M), kk] = 1.0
+    dY = np.zeros((M, N), np.float32); dY[np.arange(M), nn] = 1.0
+    probe = dict(inp, X=X, dY=dY, B=np.zeros_like(inp["B"]))
+    got = run_linear(probe, r, sh.alpha, dtype)
+    W = hv["W"]
+    np.testing.assert_array_equal(got["H"], W[:, kk].T)           # H[m, n] = W[n, k(m)]
+    np.testing.assert_array_equal(got["dX"], W[nn, :])            # dX[m, k] = W[n(m), k]
+    np.testing.assert_array_equal(got["U"], hv["A"][:, kk].T)     # U[m, j] = A[j, k(m)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_deterministic(dtype):
+    sh = shape(1000, 392, 520, 16)
+    inp = workloads.make_linear_inputs(sh)
+    dev = device_inputs(inp, dtype)
+    a = run_linear(inp, sh.r, sh.alpha, dtype, dev_inputs=dev)
+    b = run_linear(inp, sh.r, sh.alpha, dtype, dev_inputs=dev)
+    for k in a:
+        np.testing.assert_array_equal(a[k].view(np.uint32), b[k].view(np.uint32), err_msg=k)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_accumulate_flag(dtype):
+    import lora_linear_amd as lla
+    sh = shape(200, 136, 144, 8)
+    inp = workloads.make_linear_inputs(sh)
+    rng = np.random.default_rng(9)
+    dA0 = rng.standard_normal(inp["A"].shape).astype(np.float32)
+    dB0 = rng.standard_normal(inp["B"].shape).astype(np.float32)
+    got = run_linear(inp, sh.r, sh.alpha, dtype, flags=lla.LORA_FLAG_ACCUM_GRADS, grads_init=(dA0, dB0))
+    ref = oracle_all(host_view(inp, dtype), sh.scale)
+    hv0 = host_view({"X": dA0, "W": dB0}, dtype)
+    ref["dA"] = ref["dA"] + hv0["X"]
+    ref["dB"] = ref["dB"] + hv0["W"]
+    check(got, ref, DIAG[dtype], keys=("dA", "dB"))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("r", [8, 100])
+def test_recompute_u_and_skip_dx(dtype, r):
+    sh = shape(264, 200, 136, r)
+    inp = workloads.make_linear_inputs(sh)
+    ref = oracle_all(host_view(inp, dtype), sh.scale)
+    got = run_linear(inp, r, sh.alpha, dtype, save_u=False)
+    check(got, ref, DIAG[dtype], keys=("H", "dX", "dA", "dB"))
+    got = run_linear(inp, r, sh.alpha, dtype, want_dx=False)
+    check(got, ref, DIAG[dtype], keys=("H", "dA", "dB"))
+
+
+# ---------------------------------------------------------------- full-size workloads
+def sample_rows(M, n=48, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, size=n)]))
+    return rows
+
+
+FULL = [("attn_proj_4096", 0)] + [("mlp_11008", i) for i in range(3)] + \
+       [("decoder_layer_r64", i) for i in range(7)]
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("wl,idx", FULL)
+def test_full_size(wl, idx, dtype):
+    sh = workloads.workload(wl).linears[idx]
+    inp = workloads.make_linear_inputs(sh)
+    print(f"full-size {sh.name} M={sh.M} K={sh.K} N={sh.N} r={sh.r} {dtype}", flush=True)
+    got = run_linear(inp, sh.r, sh.alpha, dtype)
+    rows = sample_rows(sh.M)
+    ref = oracle_all(inp, sh.scale, rows=rows)
+    errs = check(got, ref, TOL[dtype], rows=rows, label=f"{sh.name} graded")
+    print(f"  graded errors {errs}", flush=True)
+
+
+# ---------------------------------------------------------------------- 4-bit path
+def q_inputs(M, K, N, r, seed):
+    sh = workloads.LinearShape("q", M, K, N, r, 32.0, seed, True)
+    return sh, workloads.make_qlora_inputs(sh)
+
+
+def q_oracle_inputs(inp, dtype):
+    d = dict(inp)
+    d["W"] = oracle.dequant4(inp["codes"], inp["absmax"], oracle.codebook4(), out="bf16" if dtype == "bf16" else "f32")
+    return d
+
+
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+def test_dequant4_bit_exact(out):
+    import lora_linear_amd as lla
+    _, inp = q_inputs(8, 1024, 264, 4, 31)
+    N, K = 264, 1024
+    dev = device_inputs(inp, "bf16", quant=True)
+    tdt = torch.bfloat16 if out == "bf16" else torch.float32
+    W = torch.empty((N, K), dtype=tdt, device="cuda")
+    lla.lora_dequant4(dev["codes"], dev["absmax"], dev["codebook"], N, K,
+                      lla.LORA_DTYPE_BF16 if out == "bf16" else lla.LORA_DTYPE_F32, W)
+    torch.cuda.synchronize()
+    ref = oracle.dequant4(inp["codes"], inp["absmax"], oracle.codebook4(), out=out)
+    np.testing.assert_array_equal(to_np(W).view(np.uint32), ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("M,K,N,r", [(300, 256, 264, 16), (64, 1024, 136, 8), (130, 192, 520, 100)])
+def test_qlinear_parity(M, K, N, r, dtype):
+    sh, inp = q_inputs(M, K, N, r, M + K + N)
+    got = run_linear(inp, r, sh.alpha, dtype, quant=True)
+    ref_in = q_oracle_inputs(inp, dtype)
+    check(got, oracle_all(host_view(ref_in, dtype) | {"W": ref_in["W"]}, sh.scale), DIAG[dtype], label="diag")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_qlinear_one_hot_exact(dtype):
+    M, K, N, r = 200, 512, 264, 16
+    sh, inp = q_inputs(M, K, N, r, 41)
+    Wd = q_oracle_inputs(inp, dtype)["W"]
+    rng = np.random.default_rng(6)
+    kk = rng.integers(0, K, size=M)
+    nn = rng.integers(0, N, size=M)
+    X = np.zeros((M, K), np.float32); X[np.arange(M), kk] = 1.0
+    dY = np.zeros((M, N), np.float32); dY[np.arange(M), nn] = 1.0
+    probe = dict(inp, X=X, dY=dY, B=np.zeros_like(inp["B"]))
+    got = run_linear(probe, r, sh.alpha, dtype, quant=True)
+    np.testing.assert_array_equal(got["H"], Wd[:, kk].T)
+    np.testing.assert_array_equal(got["dX"], Wd[nn, :])
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_qlora_full_size(dtype):
+    sh = workloads.workload("qlora_28672").linears[0]
+    inp = workloads.make_qlora_inputs(sh)
+    print(f"full-size {sh.name} {dtype}", flush=True)
+    got = run_linear(inp, sh.r, sh.alpha, dtype, quant=True)
+    rows = sample_rows(sh.M)
+    ref_in = q_oracle_inputs(inp, dtype)
+    errs = check(got, oracle_all(ref_in, sh.scale, rows=rows), TOL[dtype], rows=rows, label="graded")
+    print(f"  graded errors {errs}", flush=True)

@@ -189,3 +189,42 @@ def make_qlora_inputs(shape: LinearShape, *, M: int | None = None) -> dict:
     codes, absmax = quantize4(d["W"], cb)
     d.update(codes=codes, absmax=absmax, codebook=cb)
     return d
+
+
+def device_inputs_torch(shape: LinearShape, device, dtype, seed: int):
+    """Seeded device-side draws with the same distributions (benchmark inputs).
+
+    Uses torch's generator on the device, so large workloads are drawn in
+    milliseconds; these draws are not the numpy ones above.
+    """
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    M, K, N, r = shape.M, shape.K, shape.N, shape.r
+
+    def normal(rows, cols, std):
+        t = torch.randn((rows, cols), generator=g, device=device, dtype=torch.float32)
+        return (t * std).to(dtype)
+
+    return {"X": normal(M, K, 1.0), "W": normal(N, K, 0.02), "A": normal(r, K, 1.0 / math.sqrt(K)),
+            "B": normal(N, r, 0.02), "dY": normal(M, N, 1.0)}
+
+
+def quantize4_torch(W):
+    """Device-side version of quantize4 for benchmark inputs (float32 arithmetic).
+
+    Returns codes [N, K/2] uint8, absmax [N, K/64] fp16 bit patterns as int16,
+    and the float32 codebook, all on W's device.
+    """
+    import torch
+    N, K = W.shape
+    cb = torch.from_numpy(codebook4_f32()).to(W.device)
+    mids = ((cb[:-1].double() + cb[1:].double()) * 0.5).float()
+    blocks = W.float().reshape(N, K // QBLOCK, QBLOCK)
+    am = blocks.abs().amax(dim=2).to(torch.float16)
+    scale = am.float().unsqueeze(2)
+    y = torch.where(scale > 0, blocks / torch.where(scale > 0, scale, torch.ones_like(scale)),
+                    torch.zeros_like(blocks))
+    q = torch.bucketize(y.reshape(N, K), mids).to(torch.uint8)
+    codes = (q[:, 0::2] | (q[:, 1::2] << 4)).contiguous()
+    return {"codes": codes, "absmax": am.view(torch.int16).contiguous(), "codebook": cb}
