@@ -87,7 +87,7 @@ def main():
         sys.exit(2)
 
     import torch
-    import lora_linear_amd as lla
+    import lora_linear_layer_amd as lla
     import workloads
 
     wl = workloads.workload(args.workload)

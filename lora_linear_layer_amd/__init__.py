@@ -1,7 +1,7 @@
 """Fused LoRA linear layer for AMD MI355X (gfx950): HIP kernels behind a C ABI.
 
 The Python names mirror the C entry points in include/lora_linear.h; the
-autograd wrappers live in lora_linear_amd.layer.
+autograd wrappers live in lora_linear_layer_amd.layer.
 """
 from ._lib import (LIB_PATH, LORA_DTYPE_BF16, LORA_DTYPE_F32, LORA_FLAG_ACCUM_GRADS,  # noqa: F401
                    load)

@@ -48,7 +48,7 @@ def load() -> ctypes.CDLL:
         return _lib
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(
-            f"{LIB_PATH} is missing: build it first (python -m lora_linear_amd.build); "
+            f"{LIB_PATH} is missing: build it first (python -m lora_linear_layer_amd.build); "
             "the LoRA layer has no non-HIP implementation")
     lib = ctypes.CDLL(LIB_PATH)
     vp, sz, i32, i64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64

@@ -1,6 +1,6 @@
 """Build liblora_linear.so in-tree with hipcc for gfx950.
 
-Usage: python -m lora_linear_amd.build
+Usage: python -m lora_linear_layer_amd.build
 """
 from __future__ import annotations
 

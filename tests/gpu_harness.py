@@ -9,7 +9,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-import lora_linear_amd as lla
+import lora_linear_layer_amd as lla
 
 BF16_TOL = 1e-2     # bf16 storage, fp32 accumulation
 F32_TOL = 1e-5      # float32 checking mode

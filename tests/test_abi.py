@@ -10,9 +10,9 @@ import re
 
 import pytest
 
-import lora_linear_amd as lla
-from lora_linear_amd import _lib
-from lora_linear_amd._lib import LoraLinearDesc
+import lora_linear_layer_amd as lla
+from lora_linear_layer_amd import _lib
+from lora_linear_layer_amd._lib import LoraLinearDesc
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "lora_linear.h")

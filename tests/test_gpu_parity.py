@@ -138,7 +138,7 @@ def test_deterministic(dtype):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_accumulate_flag(dtype):
-    import lora_linear_amd as lla
+    import lora_linear_layer_amd as lla
     sh = shape(200, 136, 144, 8)
     inp = workloads.make_linear_inputs(sh)
     rng = np.random.default_rng(9)
@@ -203,7 +203,7 @@ def q_oracle_inputs(inp, dtype):
 
 @pytest.mark.parametrize("out", ["bf16", "f32"])
 def test_dequant4_bit_exact(out):
-    import lora_linear_amd as lla
+    import lora_linear_layer_amd as lla
     _, inp = q_inputs(8, 1024, 264, 4, 31)
     N, K = 264, 1024
     dev = device_inputs(inp, "bf16", quant=True)
