@@ -1,0 +1,426 @@
+// Fused LoRA GEMM for gfx950: 8 waves, direct global->LDS staging, fragment
+// reads software-pipelined against the MFMAs, transposed LDS reads for the
+// input-gradient operand.
+//
+// One kernel computes
+//   Out[p][q] = sum_c L[p][c] R(q, c)  +  s * sum_j E(q, j) Z[p][j]
+//   Z[p][j]   = sum_c L[p][c] F(j, c)      (rank-r product, formed on chip)
+// which is both directions of the LoRA linear layer:
+//   forward (page "ms-swift高效微调组合：LoRA+UnSloth提速实践", section 1.2
+//     "算子融合": Linear, LoRA_A, LoRA_B and the add in one launch):
+//     P=M, Q=N, C=K, L=X, R(q,c)=W[q][c], F(j,c)=A[j][c], E(q,j)=B[q][j], Z=U.
+//   input gradient (page "Unsloth — 微调 2-5x 加速", section "核心要点",
+//     item 2: (A B) dY is evaluated as A (B dY), only rank-r intermediates):
+//     P=M, Q=K, C=N, L=dY, R(q,c)=W[c][q], F(j,c)=B[c][j], E(q,j)=A[j][q], Z=V.
+//
+// Work split: a 256 (p) x 256 (q) output tile per workgroup of 8 waves,
+// 2 (p) x 4 (q); each wave owns 128 p x 64 q = 8 x 4 MFMA 16x16x32 tiles
+// (128 fp32 accumulators per lane), two waves per SIMD.
+//
+// Pipeline: the contraction advances 64 at a time through two LDS stages
+// (L 32 KB, R 32 KB, F RPAD x 128 B).  Stage kt + 2 is fetched with
+// buffer_load ... lds (global memory straight into LDS, no VGPRs) into the slot
+// stage kt just vacated.  Each stage is two 32-wide steps; the fragments of the
+// next step are read from LDS while the MFMAs of the current step run, and the
+// workgroup barrier sits between the two steps of a stage, where every wave
+// still has a full step of MFMAs queued to cover the wait:
+//   [step kk0: MFMA(frags A) | read frags B for kk1]
+//   wait own loads of stage kt+1, barrier, issue loads of stage kt+2
+//   [step kk1: MFMA(frags B) | read frags A for kk0 of stage kt+1]
+// Out-of-range rows and contraction chunks get a buffer offset past the
+// descriptor's range, which the hardware answers with zeros.
+//
+// LDS layouts:
+//   contraction-contiguous tiles (L; R in forward; F in forward): rows of 64
+//     values (128 B); 16-byte chunk ch of row x stored at chunk ch ^ (x & 7),
+//     so the 8 lanes of each quarter of a fragment read hit distinct banks.
+//   R in the input gradient: W rows c (512 B = 256 q), 32-byte slot s of row
+//     c at slot s ^ sw512(c); fragments are gathered with ds_read_b64_tr_b16,
+//     which hands each lane 4 values down a column.
+//   F in the input gradient: B rows c of RPAD values, read with the same
+//     transposing load (needs r % 8 == 0 so rows are whole 16-byte chunks).
+// The rank-r product Z^T = F L^T reuses the L fragments already in registers:
+// the 4 waves that share a p half each form Z for 32 of its 128 rows.  In the
+// epilogue Z meets in LDS and s Z E^T is applied with MFMA, s Z split into
+// bf16 hi + lo halves that fill the two halves of the 32-long contraction.
+// ZIN = true takes a precomputed Z [P][r] float32 instead (large r).
+#pragma once
+#include <type_traits>
+
+#include "common.hpp"
+
+namespace lora {
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef __attribute__((address_space(3))) i16x4* lds_i16x4_ptr;
+
+constexpr uint32_t kOOB = 0x80000000u;        // buffer offset beyond every range -> zeros
+constexpr int32_t kRsrcWord3 = 0x00020000;    // raw buffer, 32-bit data format (gfx9 family)
+constexpr uint32_t kMaxRange = 0x7FFFFFFFu;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint64_t bytes) {
+    const uint32_t n = bytes > kMaxRange ? kMaxRange : (uint32_t)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, kRsrcWord3);
+}
+
+// 16 bytes per lane from global (rsrc + voff) into LDS at lds_wave_base + 16 * lane.
+__device__ __forceinline__ void g2lds16(__amdgpu_buffer_rsrc_t rs, void* lds_wave_base, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_ptr)lds_wave_base, 16, voff, 0, 0, 0);
+}
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane j receives element j % 4
+// of the 8-byte rows addressed by lanes j / 4, 4 + j / 4, 8 + j / 4, 12 + j / 4.
+__device__ __forceinline__ i16x4 lds_tr4(const void* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)p);
+}
+
+__device__ __forceinline__ bf16x8 cat_tr(const i16x4& lo, const i16x4& hi) {
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ bf16x8 lds_b128(const void* p) {
+    return as_bf16x8(*reinterpret_cast<const u32x4*>(p));
+}
+
+__device__ __forceinline__ int sw512(int row) { return (row & 3) | (((row >> 3) & 1) << 2); }
+
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void vmcnt_le() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+
+// Workgroup barrier that orders LDS traffic only (no wait on global loads).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+struct GemmArgs {
+    const uint16_t* L;      // [P][C] bf16
+    const uint16_t* R;      // forward: [Q][C]; input gradient: [C][Q]
+    const uint16_t* F;      // forward: A [r][C]; input gradient: B [C][r]
+    const uint16_t* E;      // forward: B [Q][r]; input gradient: A [r][Q]
+    const float* Zin;       // precomputed Z [P][r] (ZIN), else unused
+    uint16_t* Out;          // [P][Q] bf16
+    float* Zsave;           // [P][r] float32 or nullptr (written by the q-tile-0 workgroups)
+    int P, Q, C, r;
+    float s;
+};
+
+namespace g2 {
+constexpr int BP = 256, BQ = 256, BK = 64, NT = 512;
+constexpr int TILE = BP * BK * 2;             // 32 KB per operand per stage
+}  // namespace g2
+
+template <int RPAD, bool ZIN>
+struct GemmSmem {
+    static constexpr int F_BYTES = ZIN ? 0 : RPAD * g2::BK * 2;
+    static constexpr int STAGE = 2 * g2::TILE + F_BYTES;
+    static constexpr int TOTAL = 2 * STAGE;
+    static_assert(F_BYTES % 1024 == 0, "F tile is whole 1 KB wave loads");
+    static_assert(ZIN || g2::BP * RPAD * 4 <= TOTAL, "Z exchange must fit");
+    static_assert(TOTAL <= 160 * 1024, "LDS budget");
+};
+
+template <int JT>
+struct Frags {
+    bf16x8 r[4];      // R, 4 q blocks of 16
+    bf16x8 l[8];      // L, 8 p blocks of 16 (slot i = block (i + 2 wq) % 8)
+    bf16x8 f[JT];     // F, rank rows
+};
+
+template <bool TRANS, int RPAD, bool ZIN>
+__global__ __launch_bounds__(g2::NT) void lora_gemm(const GemmArgs a) {
+    using namespace g2;
+    using SM = GemmSmem<RPAD, ZIN>;
+    constexpr int JT = ZIN ? 1 : RPAD / 16;
+    constexpr int F_LOADS = SM::F_BYTES / 1024;   // done by waves 0 .. F_LOADS - 1
+    static_assert(F_LOADS <= 8, "F tile larger than one load per wave");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[SM::TOTAL];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wp = wave >> 2, wq = wave & 3;
+    const int l16 = lane & 15, g4 = lane >> 4;
+
+    const int P = a.P, Q = a.Q, C = a.C, r = a.r;
+    const int nPt = (P + BP - 1) / BP, nQt = (Q + BQ - 1) / BQ;
+    int pt, qt;
+    grouped_tile<4>(xcd_contiguous(blockIdx.x, nPt * nQt), nPt, nQt, pt, qt);
+    const int p0 = pt * BP, q0 = qt * BQ;
+
+    // ------------------------------------------------------------ load plan
+    // Row layout tiles: load i of wave w covers rows (4w + i) * 8 + lane / 8;
+    // lane's 16-byte chunk is (lane % 8) ^ (row % 8) = (lane % 8) ^ (lane / 8),
+    // the same for every i, so one base offset plus a uniform stride suffices.
+    const int kc_row0 = wave * 32 + (lane >> 3);
+    const int kc_ch = ((lane & 7) ^ (lane >> 3)) * 8;
+    const __amdgpu_buffer_rsrc_t rsL = make_rsrc(a.L + (size_t)p0 * C, (uint64_t)min(P - p0, BP) * C * 2);
+    const uint32_t offL = (uint32_t)(kc_row0 * C + kc_ch) * 2u;
+    __amdgpu_buffer_rsrc_t rsR;
+    uint32_t offR = 0;
+    int chR0 = 0, chR1 = 0;
+    if constexpr (!TRANS) {
+        rsR = make_rsrc(a.R + (size_t)q0 * C, (uint64_t)min(Q - q0, BQ) * C * 2);
+        offR = (uint32_t)(kc_row0 * C + kc_ch) * 2u;
+    } else {
+        // W rows c (512 bytes each), load i of wave w covers rows (4w + i) * 2 + lane / 32;
+        // the slot swizzle depends on i only through i % 2
+        const int pch = lane & 31;
+        const int rowe = wave * 8 + (lane >> 5), rowo = rowe + 2;
+        chR0 = (((pch >> 1) ^ sw512(rowe)) * 2 + (pch & 1)) * 8;   // q offset inside the tile
+        chR1 = (((pch >> 1) ^ sw512(rowo)) * 2 + (pch & 1)) * 8;
+        offR = (uint32_t)(rowe * Q) * 2u;
+    }
+    __amdgpu_buffer_rsrc_t rsF;
+    uint32_t offF = kOOB;
+    int fch = 0, frow = 0;
+    if constexpr (!ZIN) {
+        if constexpr (!TRANS) {
+            rsF = make_rsrc(a.F, (uint64_t)r * C * 2);
+            frow = wave * 8 + (lane >> 3);                   // j (waves 0 .. RPAD/8 - 1)
+            fch = kc_ch;
+            offF = (uint32_t)(frow * C + fch) * 2u;
+        } else {
+            rsF = make_rsrc(a.F, (uint64_t)C * r * 2);
+            const int idx = wave * 64 + lane;
+            frow = idx / (RPAD / 8);                         // c within the stage
+            fch = (idx % (RPAD / 8)) * 8;                    // j
+            offF = (uint32_t)(frow * r + fch) * 2u;
+        }
+    }
+
+    auto issue_stage = [&](int kt) {
+        const int c0 = kt * BK;
+        uint8_t* const Ls = smem + (kt & 1) * SM::STAGE;
+        uint8_t* const Rs = Ls + TILE;
+        uint8_t* const Fs = Rs + TILE;
+        const bool lok = c0 + kc_ch < C;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            g2lds16(rsL, Ls + (wave * 4 + i) * 1024, lok ? offL + (uint32_t)(i * 8 * C + c0) * 2u : kOOB);
+        if constexpr (!TRANS) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                g2lds16(rsR, Rs + (wave * 4 + i) * 1024, lok ? offR + (uint32_t)(i * 8 * C + c0) * 2u : kOOB);
+        } else {
+            const int rows_left = min(C - c0, BK);
+            const __amdgpu_buffer_rsrc_t rs =
+                make_rsrc(a.R + (size_t)c0 * Q + q0, (uint64_t)(rows_left - 1) * Q * 2 + (uint64_t)(Q - q0) * 2);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int ch = (i & 1) ? chR1 : chR0;
+                g2lds16(rs, Rs + (wave * 4 + i) * 1024,
+                        (q0 + ch < Q) ? offR + (uint32_t)(2 * i * Q + ch) * 2u : kOOB);
+            }
+        }
+        if constexpr (!ZIN) {
+            if (wave < F_LOADS) {
+                uint32_t v;
+                if constexpr (!TRANS) v = (frow < r && c0 + fch < C) ? offF + (uint32_t)c0 * 2u : kOOB;
+                else v = (c0 + frow < C && fch < r) ? offF + (uint32_t)(c0 * r) * 2u : kOOB;
+                g2lds16(rsF, Fs + wave * 1024, v);
+            }
+        }
+    };
+
+    // ------------------------------------------------------------ fragment reads
+    // row layout: row x of a 16-row block has x % 8 == l16 % 8, so the chunk
+    // (kk * 4 + g4) ^ (l16 % 8) is a per-lane constant for each kk
+    const int kc_lane = l16 * 128;
+    auto chunk_of = [&](int kk) { return (((kk * 4 + g4) ^ (l16 & 7)) << 4) + kc_lane; };
+    auto read_r = [&](const uint8_t* Ls, int kk, int i) -> bf16x8 {
+        const uint8_t* const Rs = Ls + TILE;
+        if constexpr (!TRANS) {
+            return lds_b128(Rs + (wq * 4 + i) * 2048 + chunk_of(kk));
+        } else {
+            const int rlo = kk * 32 + g4 * 8 + (l16 >> 2);            // rhi = rlo + 4: same swizzle
+            const uint8_t* const p = Rs + rlo * 512 + (l16 & 3) * 8 + (((wq * 4 + i) ^ sw512(rlo)) << 5);
+            return cat_tr(lds_tr4(p), lds_tr4(p + 4 * 512));
+        }
+    };
+    auto read_l = [&](const uint8_t* Ls, int kk, int i) -> bf16x8 {
+        return lds_b128(Ls + wp * 16384 + ((i + 2 * wq) & 7) * 2048 + chunk_of(kk));
+    };
+    auto read_f = [&](const uint8_t* Ls, int kk, int jt) -> bf16x8 {
+        const uint8_t* const Fs = Ls + 2 * TILE;
+        if constexpr (!TRANS) {
+            return lds_b128(Fs + jt * 2048 + chunk_of(kk));
+        } else {
+            const int rlo = kk * 32 + g4 * 8 + (l16 >> 2);
+            const uint8_t* const p = Fs + rlo * (RPAD * 2) + (jt * 16 + (l16 & 3) * 4) * 2;
+            return cat_tr(lds_tr4(p), lds_tr4(p + 4 * RPAD * 2));
+        }
+    };
+
+    f32x4 acc[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 zacc[JT][2];
+#pragma unroll
+    for (int i = 0; i < JT; ++i) zacc[i][0] = zacc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // One 32-wide step: the MFMAs of `cur`, p block by p block, with the reads
+    // of the next step's fragments slotted in as the current ones die: L block
+    // pi after its 4 MFMAs (blocks 0 and 1 after the rank-r MFMAs too), F after
+    // the rank-r MFMAs, and in the last two blocks the MFMAs run R fragment by
+    // R fragment so that each R fragment can be replaced as soon as it is dead.
+    auto step = [&](const Frags<JT>& cur, Frags<JT>& nxt, const uint8_t* nstage, int nkk, auto do_read) {
+        constexpr bool RD = decltype(do_read)::value;
+#pragma unroll
+        for (int pi = 0; pi < 6; ++pi) {
+#pragma unroll
+            for (int qi = 0; qi < 4; ++qi) acc[qi][pi] = mfma16(cur.r[qi], cur.l[pi], acc[qi][pi]);
+            if (pi == 1) {
+                if constexpr (!ZIN) {
+#pragma unroll
+                    for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+                        for (int z = 0; z < 2; ++z) zacc[jt][z] = mfma16(cur.f[jt], cur.l[z], zacc[jt][z]);
+                    if constexpr (RD) {
+#pragma unroll
+                        for (int jt = 0; jt < JT; ++jt) nxt.f[jt] = read_f(nstage, nkk, jt);
+                    }
+                }
+                if constexpr (RD) {
+                    nxt.l[0] = read_l(nstage, nkk, 0);
+                    nxt.l[1] = read_l(nstage, nkk, 1);
+                }
+            } else if (pi > 1) {
+                if constexpr (RD) nxt.l[pi] = read_l(nstage, nkk, pi);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int qi = 0; qi < 4; ++qi) {
+            acc[qi][6] = mfma16(cur.r[qi], cur.l[6], acc[qi][6]);
+            acc[qi][7] = mfma16(cur.r[qi], cur.l[7], acc[qi][7]);
+            if constexpr (RD) nxt.r[qi] = read_r(nstage, nkk, qi);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (RD) {
+            nxt.l[6] = read_l(nstage, nkk, 6);
+            nxt.l[7] = read_l(nstage, nkk, 7);
+        }
+    };
+    using Read = std::true_type;
+    using NoRead = std::false_type;
+
+    // ------------------------------------------------------------ main loop
+    const int nk = (C + BK - 1) / BK;
+    issue_stage(0);
+    if (nk > 1) {
+        issue_stage(1);
+        if (wave < F_LOADS) vmcnt_le<9>(); else vmcnt_le<8>();   // stage 0 landed, stage 1 in flight
+    } else {
+        vmcnt_le<0>();
+    }
+    lds_barrier();
+
+    Frags<JT> fa, fb;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa.r[i] = read_r(smem, 0, i);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) fa.l[i] = read_l(smem, 0, i);
+    if constexpr (!ZIN) {
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt) fa.f[jt] = read_f(smem, 0, jt);
+    }
+    for (int kt = 0; kt + 1 < nk; ++kt) {
+        const uint8_t* const cur = smem + (kt & 1) * SM::STAGE;
+        step(fa, fb, cur, 1, Read{});
+        vmcnt_le<0>();           // this wave's loads of stage kt + 1 have landed
+        lds_barrier();           // ... and everyone's; stage kt's slot is free
+        if (kt + 2 < nk) issue_stage(kt + 2);
+        step(fb, fa, smem + ((kt + 1) & 1) * SM::STAGE, 0, Read{});
+    }
+    step(fa, fb, smem + ((nk - 1) & 1) * SM::STAGE, 1, Read{});
+    step(fb, fa, smem, 0, NoRead{});
+    lds_barrier();   // every wave is done with the last stage before LDS is reused
+
+    // ------------------------------------------------------------ epilogue
+    float* const Zx = reinterpret_cast<float*>(smem);   // [256][RPAD] float32
+    if constexpr (!ZIN) {
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+            for (int z = 0; z < 2; ++z) {
+                const int pl = wp * 128 + (wq * 2 + z) * 16 + l16;
+                *reinterpret_cast<f32x4*>(Zx + pl * RPAD + jt * 16 + 4 * g4) = zacc[jt][z];
+            }
+        lds_barrier();
+        if (a.Zsave != nullptr && qt == 0) {
+            for (int e = tid; e < BP * r; e += NT) {
+                const int pl = e / r, j = e - pl * r;
+                if (p0 + pl < P) a.Zsave[(size_t)(p0 + pl) * r + j] = Zx[pl * RPAD + j];
+            }
+        }
+    }
+
+    const float s = a.s;
+#pragma unroll 1
+    for (int jt = 0; jt < RPAD / 16; ++jt) {
+        bf16x8 ef[4];
+#pragma unroll
+        for (int qi = 0; qi < 4; ++qi) {
+            const int q = q0 + wq * 64 + qi * 16 + l16;
+            uint32_t e4[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int j = jt * 16 + 4 * g4 + i;
+                uint32_t v = 0u;
+                if (q < Q && j < r) v = TRANS ? a.E[(size_t)j * Q + q] : a.E[(size_t)q * r + j];
+                e4[i] = v;
+            }
+            const uint32_t w0 = e4[0] | (e4[1] << 16), w1 = e4[2] | (e4[3] << 16);
+            ef[qi] = as_bf16x8(u32x4{w0, w1, w0, w1});
+        }
+#pragma unroll
+        for (int pi = 0; pi < 8; ++pi) {
+            const int pl = wp * 128 + ((pi + 2 * wq) & 7) * 16 + l16;
+            f32x4 z;
+            if constexpr (ZIN) {
+                const int p = p0 + pl;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int j = jt * 16 + 4 * g4 + i;
+                    z[i] = (p < P && j < r) ? a.Zin[(size_t)p * r + j] : 0.f;
+                }
+            } else {
+                z = *reinterpret_cast<const f32x4*>(Zx + pl * RPAD + jt * 16 + 4 * g4);
+            }
+            uint32_t hi[4], lo[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float zs = z[i] * s;
+                const __bf16 h = (__bf16)zs;
+                hi[i] = __builtin_bit_cast(uint16_t, h);
+                lo[i] = __builtin_bit_cast(uint16_t, (__bf16)(zs - (float)h));
+            }
+            const bf16x8 zf = as_bf16x8(u32x4{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16),
+                                              lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)});
+#pragma unroll
+            for (int qi = 0; qi < 4; ++qi) acc[qi][pi] = mfma16(ef[qi], zf, acc[qi][pi]);
+        }
+    }
+
+    // store: lane holds Out[p][q .. q+3], p = column l16, q = 4 consecutive rows
+#pragma unroll
+    for (int qi = 0; qi < 4; ++qi) {
+        const int q = q0 + wq * 64 + qi * 16 + 4 * g4;
+        if (q >= Q) continue;
+#pragma unroll
+        for (int pi = 0; pi < 8; ++pi) {
+            const int p = p0 + wp * 128 + ((pi + 2 * wq) & 7) * 16 + l16;
+            if (p < P) {
+                const f32x4 v = acc[qi][pi];
+                const u32x2 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+                *reinterpret_cast<u32x2*>(a.Out + (size_t)p * Q + q) = o;
+            }
+        }
+    }
+}
+
+}  // namespace lora

@@ -13,6 +13,8 @@
 
 #include "lora_linear.h"
 #include "fused_gemm.hpp"
+#include "lora_gemm.hpp"
+#include "lora_gemm_pp.hpp"
 #include "grad_splitm.hpp"
 #include "f32_kernels.hpp"
 
@@ -39,6 +41,7 @@ lora_status ok() {
 }
 
 constexpr int64_t kMaxElems = (int64_t(1) << 31) - 1;
+constexpr int64_t kMaxDim = int64_t(1) << 21;   // K, N bound: one 256-row tile stays under 2 GB
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -92,6 +95,9 @@ lora_status check_desc(const lora_linear_desc* d, bool quant) {
     if (d->r > 128) return fail(LORA_ERR_UNSUPPORTED, "r = %lld exceeds 128", (long long)d->r);
     if (d->K % 8 || d->N % 8)
         return fail(LORA_ERR_UNSUPPORTED, "K and N must be multiples of 8 (got K=%lld, N=%lld)",
+                    (long long)d->K, (long long)d->N);
+    if (d->K > kMaxDim || d->N > kMaxDim)
+        return fail(LORA_ERR_UNSUPPORTED, "K and N must not exceed %lld (got K=%lld, N=%lld)", (long long)kMaxDim,
                     (long long)d->K, (long long)d->N);
     if (quant && d->K % 64) return fail(LORA_ERR_UNSUPPORTED, "4-bit weights need K %% 64 == 0 (K=%lld)", (long long)d->K);
     const int64_t big[] = {d->M * d->K, d->N * d->K, d->M * d->N, d->M * d->r};
@@ -170,6 +176,41 @@ void launch_fused_mode(int mode, const FusedArgs& a, int rpad, bool zin, hipStre
     }
 }
 
+// Schedule per direction, chosen by measurement on the 4096 x 4096 layer: the
+// forward streams both operands as 128-byte row segments and runs best with
+// the software-pipelined kernel; the input gradient, whose W tile arrives as
+// whole 512-byte rows, runs best with the ping-pong kernel.
+#ifndef LORA_PINGPONG_FWD
+#define LORA_PINGPONG_FWD 0
+#endif
+#ifndef LORA_PINGPONG_DX
+#define LORA_PINGPONG_DX 1
+#endif
+
+template <bool TRANS, int RPAD, bool ZIN>
+void launch_gemm_t(const GemmArgs& a, hipStream_t st) {
+    const int tiles = (int)(cdiv(a.P, g2::BP) * cdiv(a.Q, g2::BQ));
+    if (TRANS ? LORA_PINGPONG_DX : LORA_PINGPONG_FWD)
+        hipLaunchKernelGGL((lora_gemm_pp<TRANS, RPAD, ZIN>), dim3(tiles), dim3(pp::NT), 0, st, a);
+    else
+        hipLaunchKernelGGL((lora_gemm<TRANS, RPAD, ZIN>), dim3(tiles), dim3(g2::NT), 0, st, a);
+}
+
+// In-tile rank-r product for r <= 16 (the input gradient also needs r % 8 == 0,
+// so that rows of B are whole 16-byte chunks); otherwise Z comes precomputed.
+bool gemm_in_tile(bool trans, int r) { return r <= 16 && (!trans || r % 8 == 0); }
+
+template <bool TRANS>
+void launch_gemm(const GemmArgs& a, hipStream_t st) {
+    if (gemm_in_tile(TRANS, a.r)) { launch_gemm_t<TRANS, 16, false>(a, st); return; }
+    switch (rpad_of(a.r)) {
+        case 16: launch_gemm_t<TRANS, 16, true>(a, st); break;
+        case 32: launch_gemm_t<TRANS, 32, true>(a, st); break;
+        case 64: launch_gemm_t<TRANS, 64, true>(a, st); break;
+        default: launch_gemm_t<TRANS, 128, true>(a, st); break;
+    }
+}
+
 void launch_skinny(const uint16_t* Y, const uint16_t* F, bool f_trans, float* Z, int P, int C, int r, hipStream_t st) {
     const dim3 grid((unsigned)cdiv(P, 64));
     const int rp = rpad_of(r);
@@ -202,6 +243,27 @@ lora_status fwd_bf16(const lora_linear_desc& d, int mode, const void* X, const v
                      float* U_save, void* ws, hipStream_t st) {
     const Plan plan = make_plan(d);
     const int r = (int)d.r, rpad = rpad_of(r);
+    if (mode == kFwd) {
+        GemmArgs g{};
+        g.L = static_cast<const uint16_t*>(X);
+        g.R = static_cast<const uint16_t*>(W);
+        g.F = static_cast<const uint16_t*>(A);
+        g.E = static_cast<const uint16_t*>(B);
+        g.Out = static_cast<uint16_t*>(H);
+        g.Zsave = U_save;
+        g.P = (int)d.M; g.Q = (int)d.N; g.C = (int)d.K; g.r = r;
+        g.s = d.alpha / (float)d.r;
+        if (!gemm_in_tile(false, r)) {
+            float* U = U_save ? U_save : reinterpret_cast<float*>(static_cast<char*>(ws) + plan.off_u);
+            launch_skinny(g.L, g.F, false, U, g.P, g.C, r, st);
+            LAUNCH_CHECK("skinny_rank(U)");
+            g.Zin = U;
+            g.Zsave = nullptr;
+        }
+        launch_gemm<false>(g, st);
+        LAUNCH_CHECK("lora_gemm(forward)");
+        return ok();
+    }
     const bool zin = rpad > 64;
     FusedArgs a{};
     a.L = static_cast<const uint16_t*>(X);
@@ -242,7 +304,25 @@ lora_status bwd_bf16(const lora_linear_desc& d, bool quant, const void* dY, cons
     const uint16_t* const B16 = static_cast<const uint16_t*>(B);
 
     // 1. dX = dY W + s V A with V = dY B formed on chip (and saved for dA)
-    if (dX) {
+    if (dX && !quant) {
+        GemmArgs g{};
+        g.L = dY16;
+        g.R = static_cast<const uint16_t*>(W);
+        g.F = B16;
+        g.E = A16;
+        g.Out = static_cast<uint16_t*>(dX);
+        g.Zsave = V;
+        g.P = (int)d.M; g.Q = (int)d.K; g.C = (int)d.N; g.r = r;
+        g.s = d.alpha / (float)d.r;
+        if (!gemm_in_tile(true, r)) {
+            launch_skinny(dY16, B16, true, V, g.P, g.C, r, st);
+            LAUNCH_CHECK("skinny_rank(V)");
+            g.Zin = V;
+            g.Zsave = nullptr;
+        }
+        launch_gemm<true>(g, st);
+        LAUNCH_CHECK("lora_gemm(dX)");
+    } else if (dX) {
         FusedArgs a{};
         a.L = dY16;
         a.R = static_cast<const uint16_t*>(W);
