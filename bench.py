@@ -5,18 +5,30 @@ One step = the whole hot path over one batch: the fused forward
 (H = X W^T + s (X A^T) B^T, U saved) followed by the backward (dX, dA, dB),
 for every linear of the workload (backward in reverse order).  Inputs are
 resident in HBM before timing starts; several input sets are rotated so the
-256 MB Infinity Cache cannot hold the whole working set between steps.
+256 MB Infinity Cache cannot serve the operands of one step from the previous
+one (cold operands, as in a training step where W was last touched a layer
+stack ago).
 
-Prints one JSON line (rank 0).  Timing: W warm-up steps, then K timed steps
-between device synchronisations, with HIP events on the stream the kernels are
-launched on.  The forward call of a rank <= 64 layer is exactly one kernel
+Prints one JSON line.  Timing: W warm-up steps, then K timed steps between
+device synchronisations, with HIP events recorded on the stream the library
+launches on.  For a rank <= 16 layer the forward call is exactly one kernel
 (the fused GEMM), so its event pair times that kernel alone: that is the
 roofline figure.  The CPU baseline times the float64 oracle on a bounded
 sample of the same workload on the host cores.
+
+Extra modes (used to produce the committed counter summaries):
+  --copy-calibration    run a plain device copy of known size (for scaling
+                        the FETCH_SIZE / WRITE_SIZE counters)
+  --traffic-from DIR    read rocprofv3 --pmc CSVs from DIR and write the
+                        measured HBM traffic of the dominant kernel to
+                        profiles/traffic_<workload>.json
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -28,6 +40,8 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0
 METRIC = "fused LoRA linear fwd+bwd TFLOP/s and tokens/s; % bf16 MFMA peak (1 GPU)"
+COPY_BYTES = 256 << 20             # calibration copy: 256 MiB read + 256 MiB written
+KERNEL_SOURCES = ("lora_linear_layer_amd/csrc/*.hpp", "lora_linear_layer_amd/csrc/*.hip")
 
 
 def parse():
@@ -38,45 +52,117 @@ def parse():
     ap.add_argument("--workload", default="attn_proj_4096")
     ap.add_argument("--input-sets", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-rows", type=int, default=512)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle time for the CPU baseline")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--traffic-from", default=None)
     return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for pat in KERNEL_SOURCES:
+        for p in sorted(glob.glob(os.path.join(ROOT, pat))):
+            h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def fwd_flops(l):
     return 2 * l.M * l.N * l.K + 2 * l.M * l.r * (l.K + l.N)
 
 
-def cpu_baseline(wl, rows):
-    """Oracle (numpy float64) forward + backward on the first `rows` tokens of the
-    workload's first linear; reported in TFLOP/s of algorithmic work."""
-    import numpy as np
+def bwd_flops(l):
+    return 2 * l.M * l.N * l.K + 4 * l.M * l.r * (l.K + l.N)
+
+
+def cpu_baseline(wl, min_seconds):
+    """The float64 oracle's forward + backward on the first linear of the
+    workload (all of its tokens), repeated until min_seconds have passed."""
+    import numpy as np  # noqa: F401
     import oracle
     import workloads
     try:
         from threadpoolctl import threadpool_info
-        threads = max(int(p.get("num_threads", 1)) for p in threadpool_info()) if threadpool_info() else 1
+        info = threadpool_info()
+        threads = max(int(p.get("num_threads", 1)) for p in info) if info else 1
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
     sh = wl.linears[0]
-    inp = workloads.make_linear_inputs(sh)
-    X, dY = inp["X"][:rows], inp["dY"][:rows]
-    s = sh.scale
-    t0 = time.perf_counter()
+    inp = workloads.make_qlora_inputs(sh) if sh.quant4 else workloads.make_linear_inputs(sh)
     if sh.quant4:
-        W = oracle.dequant4(*workloads.quantize4(inp["W"]), oracle.codebook4())
+        W = oracle.dequant4(inp["codes"], inp["absmax"], oracle.codebook4())
     else:
         W = inp["W"]
-    t_deq = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    oracle.forward(X, W, inp["A"], inp["B"], s)
-    oracle.backward(dY, X, W, inp["A"], inp["B"], s)
-    dt = time.perf_counter() - t0
-    sample_flops = 4 * rows * sh.N * sh.K + 6 * rows * sh.r * (sh.K + sh.N)
-    return {"value": sample_flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "seconds": round(dt, 3),
-            "sample": f"{sh.name}: first {rows} of {sh.M} tokens, K={sh.K}, N={sh.N}, r={sh.r}, float64 numpy "
-                      f"forward+backward ({sample_flops / 1e9:.1f} GFLOP)"
-                      + (f"; 4-bit dequant of W took {t_deq:.1f}s, not counted" if sh.quant4 else "")}
+    s = sh.scale
+    runs, t0 = 0, time.perf_counter()
+    while True:
+        oracle.forward(inp["X"], W, inp["A"], inp["B"], s)
+        oracle.backward(inp["dY"], inp["X"], W, inp["A"], inp["B"], s)
+        runs += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    flops = runs * sh.flops()
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "seconds": round(dt, 2), "tokens_per_s": round(runs * sh.M / dt, 1),
+            "sample": f"{sh.name}: all {sh.M} tokens, K={sh.K}, N={sh.N}, r={sh.r}, float64 numpy forward+backward, "
+                      f"{runs} run(s) ({sh.flops() / 1e9:.1f} GFLOP each)"
+                      + ("; 4-bit weights dequantised once beforehand, not timed" if sh.quant4 else "")}
+
+
+def traffic_path(workload):
+    return os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+
+
+def load_traffic(workload):
+    p = traffic_path(workload)
+    if not os.path.exists(p):
+        return None
+    t = json.load(open(p))
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None          # the kernels changed since the counters were taken
+    return t
+
+
+def write_traffic(args):
+    """Mean FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the dominant kernel and
+    of the calibration copy, from rocprofv3 --pmc counter_collection CSVs."""
+    def mean_counter(prefix, counter, pred):
+        vals = []
+        for f in glob.glob(os.path.join(args.traffic_from, prefix + "*counter_collection.csv")):
+            for row in csv.DictReader(open(f)):
+                if row["Counter_Name"] == counter and pred(row["Kernel_Name"]):
+                    vals.append(float(row["Counter_Value"]))
+        return sum(vals) / len(vals) if vals else None
+
+    # bench_* files: the forward GEMM (first template argument false); copy_* files: the neg kernel
+    is_gemm = lambda k: "lora_gemm" in k and k.split("<", 1)[-1].split(",")[0].strip() == "false"
+    is_copy = lambda k: "neg_kernel" in k
+    fetch_k, write_k = mean_counter("bench_", "FETCH_SIZE", is_gemm), mean_counter("bench_", "WRITE_SIZE", is_gemm)
+    cfetch_k, cwrite_k = mean_counter("copy_", "FETCH_SIZE", is_copy), mean_counter("copy_", "WRITE_SIZE", is_copy)
+    if None in (fetch_k, write_k, cfetch_k, cwrite_k):
+        raise SystemExit("missing counters: need FETCH_SIZE and WRITE_SIZE runs of both the bench and the copy")
+    f_fac = cfetch_k * 1024 / COPY_BYTES
+    w_fac = cwrite_k * 1024 / COPY_BYTES
+    out = {"workload": args.workload, "kernel": "lora_gemm forward", "kernel_source_hash": kernel_source_hash(),
+           "fetch_kib_per_dispatch": fetch_k, "write_kib_per_dispatch": write_k,
+           "copy_kib_fetch": cfetch_k, "copy_kib_write": cwrite_k, "copy_bytes": COPY_BYTES,
+           "copy_fetch_factor": round(f_fac, 4), "copy_write_factor": round(w_fac, 4),
+           "hbm_read_bytes_per_dispatch": round(fetch_k * 1024 / f_fac),
+           "hbm_write_bytes_per_dispatch": round(write_k * 1024 / w_fac),
+           "hbm_bytes_per_dispatch": round(fetch_k * 1024 / f_fac + write_k * 1024 / w_fac)}
+    os.makedirs(os.path.dirname(traffic_path(args.workload)), exist_ok=True)
+    json.dump(out, open(traffic_path(args.workload), "w"), indent=1)
+    print(json.dumps(out))
+
+
+def copy_calibration():
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.neg(src, out=dst)        # one elementwise kernel: reads and writes COPY_BYTES
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": COPY_BYTES}))
 
 
 def main():
@@ -85,6 +171,12 @@ def main():
         print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1 "
                                    "(data-parallel sharding is described in DESIGN.md, not built)"}))
         sys.exit(2)
+    if args.traffic_from:
+        write_traffic(args)
+        return
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import torch
     import lora_linear_layer_amd as lla
@@ -122,50 +214,56 @@ def main():
             layer.append(d)
         sets.append(layer)
     ws_bytes = max(lla.lora_linear_workspace_size(d["desc"]) for d in sets[0])
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     def fwd(d):
         if "codes" in d:
             lla.lora_qlinear_fwd(d["desc"], d["X"], d["codes"], d["absmax"], d["codebook"], d["A"], d["B"],
-                                 d["H"], d["U"], ws=ws, ws_bytes=ws_bytes)
+                                 d["H"], d["U"], ws=ws, ws_bytes=ws_bytes, stream=stream)
         else:
             lla.lora_linear_fwd(d["desc"], d["X"], d["W"], d["A"], d["B"], d["H"], d["U"], ws=ws,
-                                ws_bytes=ws_bytes)
+                                ws_bytes=ws_bytes, stream=stream)
 
     def bwd(d):
         if "codes" in d:
             lla.lora_qlinear_bwd(d["desc"], d["dY"], d["X"], d["codes"], d["absmax"], d["codebook"], d["A"],
-                                 d["B"], d["U"], d["dX"], d["dA"], d["dB"], ws=ws, ws_bytes=ws_bytes)
+                                 d["B"], d["U"], d["dX"], d["dA"], d["dB"], ws=ws, ws_bytes=ws_bytes, stream=stream)
         else:
             lla.lora_linear_bwd(d["desc"], d["dY"], d["X"], d["W"], d["A"], d["B"], d["U"], d["dX"], d["dA"],
-                                d["dB"], ws=ws, ws_bytes=ws_bytes)
+                                d["dB"], ws=ws, ws_bytes=ws_bytes, stream=stream)
 
     n_lin = len(wl.linears)
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_lin)]
-          for _ in range(args.steps)]
+    mk = lambda: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    ev_f = [[mk() for _ in range(n_lin)] for _ in range(args.steps)]
+    ev_b = [[mk() for _ in range(n_lin)] for _ in range(args.steps)]
 
     def step(i, timed):
         layer = sets[i % len(sets)]
         for li, d in enumerate(layer):
             if timed:
-                ev[i][li][0].record(stream)
+                ev_f[i][li][0].record(stream)
             fwd(d)
             if timed:
-                ev[i][li][1].record(stream)
-        for d in reversed(layer):
-            bwd(d)
+                ev_f[i][li][1].record(stream)
+        for li in reversed(range(n_lin)):
+            if timed:
+                ev_b[i][li][0].record(stream)
+            bwd(layer[li])
+            if timed:
+                ev_b[i][li][1].record(stream)
 
     for i in range(args.warmup):
         step(i, False)
     torch.cuda.synchronize()
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
+    t_start, t_end = mk()
+    wall0 = time.perf_counter()
     t_start.record(stream)
     for i in range(args.steps):
         step(i, True)
     t_end.record(stream)
     torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
     ms_total = t_start.elapsed_time(t_end)
     ms_step = ms_total / args.steps
 
@@ -173,15 +271,28 @@ def main():
     tflops = flops / (ms_step * 1e-3) / 1e12
     tokens_s = wl.tokens / (ms_step * 1e-3)
 
-    # dominant kernel: the fused forward GEMM of the largest linear (one launch per call)
+    def mean_ms(ev, li):
+        return sum(ev[i][li][0].elapsed_time(ev[i][li][1]) for i in range(args.steps)) / args.steps
+
+    per_linear = []
+    for li, l in enumerate(wl.linears):
+        f_ms, b_ms = mean_ms(ev_f, li), mean_ms(ev_b, li)
+        per_linear.append({"name": l.name, "fwd_us": round(f_ms * 1e3, 2), "bwd_us": round(b_ms * 1e3, 2),
+                           "fwd_tflops": round(fwd_flops(l) / (f_ms * 1e-3) / 1e12, 1),
+                           "bwd_tflops": round(bwd_flops(l) / (b_ms * 1e-3) / 1e12, 1)})
+
+    # dominant kernel: the fused forward GEMM of the largest linear
     big = max(range(n_lin), key=lambda i: fwd_flops(wl.linears[i]))
-    fwd_ms = sum(ev[i][big][0].elapsed_time(ev[i][big][1]) for i in range(args.steps)) / args.steps
     lb = wl.linears[big]
+    fwd_ms = mean_ms(ev_f, big)
     ach = fwd_flops(lb) / (fwd_ms * 1e-3) / 1e12
-    roofline = {"kernel": f"fused_lora_gemm forward ({lb.name})", "bound": "mfma", "achieved": round(ach, 2),
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-                "traffic": None, "avg_launch_us": round(fwd_ms * 1e3, 2),
-                "flops_per_launch": fwd_flops(lb)}
+    tr = load_traffic(wl.name)
+    roofline = {"kernel": f"lora_gemm forward ({lb.name})" + ("" if lb.r <= 16 else " + skinny U pass"),
+                "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                "traffic": tr["hbm_bytes_per_dispatch"] if tr else None,
+                "avg_launch_us": round(fwd_ms * 1e3, 2), "flops_per_launch": fwd_flops(lb),
+                "algorithmic_bytes_per_launch": 2 * (lb.M * lb.K + lb.N * lb.K + lb.M * lb.N)}
 
     out = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
@@ -191,11 +302,12 @@ def main():
         "config": {"workload": wl.name, "linears": [[l.name, l.M, l.K, l.N, l.r, l.alpha] for l in wl.linears],
                    "input_sets": args.input_sets, "description": wl.description},
         "tokens_per_s": round(tokens_s, 1), "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
-        "algorithmic_gflop_per_step": round(flops / 1e9, 3),
+        "algorithmic_gflop_per_step": round(flops / 1e9, 3), "wall_s_timed": round(wall, 3),
+        "per_linear": per_linear,
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, min(args.cpu_sample_rows, wl.linears[0].M))
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 
