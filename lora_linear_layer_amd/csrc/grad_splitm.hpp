@@ -190,13 +190,18 @@ __global__ __launch_bounds__(256) void grad_reduce(const ReduceArgs a) {
 }
 
 // Skinny rank-r product Z[p][j] = sum_c Y[p][c] * F(j, c) with float32 output,
-// used when the backward must rebuild U = X A^T (no saved U) or form
-// V = dY B without the dX product.  F_TRANS = false: F = A [r][C];
-// F_TRANS = true: F(j, c) = B[c][j] with B [C][r].
-// One workgroup (4 waves) owns 64 rows; each wave owns 16 rows.
+// used when U = X A^T or V = dY B is needed outside the fused GEMM (large r,
+// no saved U, no dX).  F_TRANS = false: F = A [r][C]; F_TRANS = true:
+// F(j, c) = B[c][j] with B [C][r].  HBM-bound on Y.
+// Workgroup (x, y) of 4 waves owns 64 rows and the contraction chunk
+// [y * chunk, (y + 1) * chunk); it writes its partial sums to
+// Z + y * P * r (gridDim.y == 1: the result itself), and skinny_sum adds the
+// chunks in a fixed order.
 template <int RPAD, bool F_TRANS>
 __global__ __launch_bounds__(256) void skinny_rank(const uint16_t* __restrict__ Y, const uint16_t* __restrict__ F,
-                                                  float* __restrict__ Z, int P, int C, int r) {
+                                                  float* __restrict__ Zall, int P, int C, int r, int chunk) {
+    float* const Z = Zall + (size_t)blockIdx.y * P * r;
+    const int c_begin = blockIdx.y * chunk, c_end = min(C, c_begin + chunk);
     constexpr int JT = RPAD / 16;
     __shared__ __attribute__((aligned(16))) uint8_t smem[64 * 128 + RPAD * 128];
     uint8_t* const Ys = smem;
@@ -208,7 +213,7 @@ __global__ __launch_bounds__(256) void skinny_rank(const uint16_t* __restrict__ 
 #pragma unroll
     for (int j = 0; j < JT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int c0 = 0; c0 < C; c0 += 64) {
+    for (int c0 = c_begin; c0 < c_end; c0 += 64) {
         // Y tile 64 x 64: 512 chunks, 2 per thread
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
@@ -216,7 +221,7 @@ __global__ __launch_bounds__(256) void skinny_rank(const uint16_t* __restrict__ 
             const int row = id >> 3, ch = id & 7;
             const int p = p0 + row, c = c0 + ch * 8;
             u32x4 v = {0u, 0u, 0u, 0u};
-            if (p < P && c < C) v = *reinterpret_cast<const u32x4*>(Y + (size_t)p * C + c);
+            if (p < P && c < c_end) v = *reinterpret_cast<const u32x4*>(Y + (size_t)p * C + c);
             *reinterpret_cast<u32x4*>(Ys + swz<128>(row, ch)) = v;
         }
         if constexpr (!F_TRANS) {
@@ -224,14 +229,14 @@ __global__ __launch_bounds__(256) void skinny_rank(const uint16_t* __restrict__ 
                 const int j = id >> 3, ch = id & 7;
                 const int c = c0 + ch * 8;
                 u32x4 v = {0u, 0u, 0u, 0u};
-                if (j < r && c < C) v = *reinterpret_cast<const u32x4*>(F + (size_t)j * C + c);
+                if (j < r && c < c_end) v = *reinterpret_cast<const u32x4*>(F + (size_t)j * C + c);
                 *reinterpret_cast<u32x4*>(Fs + swz<128>(j, ch)) = v;
             }
         } else {
             for (int e = tid; e < RPAD * 64; e += 256) {
                 const int j = e >> 6, cl = e & 63;
                 const int c = c0 + cl;
-                const uint16_t v = (j < r && c < C) ? F[(size_t)c * r + j] : (uint16_t)0;
+                const uint16_t v = (j < r && c < c_end) ? F[(size_t)c * r + j] : (uint16_t)0;
                 *reinterpret_cast<uint16_t*>(Fs + swz<128>(j, cl >> 3) + (cl & 7) * 2) = v;
             }
         }
@@ -259,6 +264,16 @@ __global__ __launch_bounds__(256) void skinny_rank(const uint16_t* __restrict__ 
                 if (j < r) Z[(size_t)p * r + j] = acc[jt][i];
             }
     }
+}
+
+// Z[e] = sum over the n_parts partials of skinny_rank, in increasing chunk order.
+__global__ __launch_bounds__(256) void skinny_sum(const float* __restrict__ part, float* __restrict__ Z, int64_t n,
+                                                 int n_parts) {
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= n) return;
+    float sum = 0.f;
+    for (int k = 0; k < n_parts; ++k) sum += part[(size_t)k * n + e];
+    Z[e] = sum;
 }
 
 // Standalone 4-bit dequantisation: W_out[n][k] for 16 consecutive k per thread.

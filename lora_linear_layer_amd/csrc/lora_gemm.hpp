@@ -37,10 +37,10 @@
 //   R in the input gradient: W rows c (512 B = 256 q), 32-byte slot s of row
 //     c at slot s ^ sw512(c); fragments are gathered with ds_read_b64_tr_b16,
 //     which hands each lane 4 values down a column.
-//   F in the input gradient: B rows c of RPAD values, read with the same
-//     transposing load (needs r % 8 == 0 so rows are whole 16-byte chunks).
-// The rank-r product Z^T = F L^T reuses the L fragments already in registers:
-// the 4 waves that share a p half each form Z for 32 of its 128 rows.  In the
+// Forward, r <= 16: the rank-r product Z^T = F L^T reuses the L fragments
+// already in registers; the 4 waves that share a p half each form Z for 32 of
+// its 128 rows.  (The input gradient takes V = dY B precomputed: forming it in
+// the tile too needs transposing reads of B and exceeds the register budget.)  In the
 // epilogue Z meets in LDS and s Z E^T is applied with MFMA, s Z split into
 // bf16 hi + lo halves that fill the two halves of the 32-long contraction.
 // ZIN = true takes a precomputed Z [P][r] float32 instead (large r).
@@ -132,6 +132,7 @@ template <bool TRANS, int RPAD, bool ZIN>
 __global__ __launch_bounds__(g2::NT) void lora_gemm(const GemmArgs a) {
     using namespace g2;
     using SM = GemmSmem<RPAD, ZIN>;
+    static_assert(ZIN || !TRANS, "the input gradient takes V precomputed");
     constexpr int JT = ZIN ? 1 : RPAD / 16;
     constexpr int F_LOADS = SM::F_BYTES / 1024;   // done by waves 0 .. F_LOADS - 1
     static_assert(F_LOADS <= 8, "F tile larger than one load per wave");
@@ -176,18 +177,10 @@ __global__ __launch_bounds__(g2::NT) void lora_gemm(const GemmArgs a) {
     uint32_t offF = kOOB;
     int fch = 0, frow = 0;
     if constexpr (!ZIN) {
-        if constexpr (!TRANS) {
-            rsF = make_rsrc(a.F, (uint64_t)r * C * 2);
-            frow = wave * 8 + (lane >> 3);                   // j (waves 0 .. RPAD/8 - 1)
-            fch = kc_ch;
-            offF = (uint32_t)(frow * C + fch) * 2u;
-        } else {
-            rsF = make_rsrc(a.F, (uint64_t)C * r * 2);
-            const int idx = wave * 64 + lane;
-            frow = idx / (RPAD / 8);                         // c within the stage
-            fch = (idx % (RPAD / 8)) * 8;                    // j
-            offF = (uint32_t)(frow * r + fch) * 2u;
-        }
+        rsF = make_rsrc(a.F, (uint64_t)r * C * 2);
+        frow = wave * 8 + (lane >> 3);                       // j (waves 0 .. RPAD/8 - 1)
+        fch = kc_ch;
+        offF = (uint32_t)(frow * C + fch) * 2u;
     }
 
     auto issue_stage = [&](int kt) {
@@ -215,12 +208,8 @@ __global__ __launch_bounds__(g2::NT) void lora_gemm(const GemmArgs a) {
             }
         }
         if constexpr (!ZIN) {
-            if (wave < F_LOADS) {
-                uint32_t v;
-                if constexpr (!TRANS) v = (frow < r && c0 + fch < C) ? offF + (uint32_t)c0 * 2u : kOOB;
-                else v = (c0 + frow < C && fch < r) ? offF + (uint32_t)(c0 * r) * 2u : kOOB;
-                g2lds16(rsF, Fs + wave * 1024, v);
-            }
+            if (wave < F_LOADS)
+                g2lds16(rsF, Fs + wave * 1024, (frow < r && c0 + fch < C) ? offF + (uint32_t)c0 * 2u : kOOB);
         }
     };
 
@@ -243,14 +232,7 @@ __global__ __launch_bounds__(g2::NT) void lora_gemm(const GemmArgs a) {
         return lds_b128(Ls + wp * 16384 + ((i + 2 * wq) & 7) * 2048 + chunk_of(kk));
     };
     auto read_f = [&](const uint8_t* Ls, int kk, int jt) -> bf16x8 {
-        const uint8_t* const Fs = Ls + 2 * TILE;
-        if constexpr (!TRANS) {
-            return lds_b128(Fs + jt * 2048 + chunk_of(kk));
-        } else {
-            const int rlo = kk * 32 + g4 * 8 + (l16 >> 2);
-            const uint8_t* const p = Fs + rlo * (RPAD * 2) + (jt * 16 + (l16 & 3) * 4) * 2;
-            return cat_tr(lds_tr4(p), lds_tr4(p + 4 * RPAD * 2));
-        }
+        return lds_b128(Ls + 2 * TILE + jt * 2048 + chunk_of(kk));
     };
 
     f32x4 acc[4][8];

@@ -14,7 +14,6 @@
 #include "lora_linear.h"
 #include "fused_gemm.hpp"
 #include "lora_gemm.hpp"
-#include "lora_gemm_pp.hpp"
 #include "grad_splitm.hpp"
 #include "f32_kernels.hpp"
 
@@ -53,9 +52,19 @@ int rpad_of(int64_t r) { return r <= 16 ? 16 : r <= 32 ? 32 : r <= 64 ? 64 : 128
 
 // Workspace layout for one descriptor (offsets in bytes from ws).
 struct Plan {
-    size_t off_v = 0, off_u = 0, off_pa = 0, off_pb = 0, total = 0;
+    size_t off_v = 0, off_u = 0, off_pa = 0, off_pb = 0, off_zp = 0, total = 0;
     int n_mblk = 1, mblk_rows = 128;
+    int max_zparts = 1;   // contraction chunks of the stand-alone rank-r products
 };
+
+// Chunks for a stand-alone rank-r product over C: enough workgroups (>= ~1024)
+// to cover the HBM stream of Y, each chunk a multiple of 64.
+int zparts_for(int64_t M, int64_t C) {
+    const int64_t rows = cdiv(M, 64);
+    int64_t n = cdiv(1024, rows);
+    n = std::max<int64_t>(1, std::min<int64_t>(n, cdiv(C, 256)));
+    return (int)n;
+}
 
 Plan make_plan(const lora_linear_desc& d) {
     Plan p;
@@ -77,6 +86,11 @@ Plan make_plan(const lora_linear_desc& d) {
         cur += align_up((size_t)p.n_mblk * d.K * d.r * sizeof(float));
         p.off_pb = cur;
         cur += align_up((size_t)p.n_mblk * d.N * d.r * sizeof(float));
+        p.max_zparts = std::max(zparts_for(d.M, d.K), zparts_for(d.M, d.N));
+        if (p.max_zparts > 1) {
+            p.off_zp = cur;
+            cur += align_up((size_t)p.max_zparts * d.M * d.r * sizeof(float));
+        }
     }
     p.total = cur;
     return p;
@@ -176,33 +190,26 @@ void launch_fused_mode(int mode, const FusedArgs& a, int rpad, bool zin, hipStre
     }
 }
 
-// Schedule per direction, chosen by measurement on the 4096 x 4096 layer: the
-// forward streams both operands as 128-byte row segments and runs best with
-// the software-pipelined kernel; the input gradient, whose W tile arrives as
-// whole 512-byte rows, runs best with the ping-pong kernel.
-#ifndef LORA_PINGPONG_FWD
-#define LORA_PINGPONG_FWD 0
-#endif
-#ifndef LORA_PINGPONG_DX
-#define LORA_PINGPONG_DX 1
-#endif
-
 template <bool TRANS, int RPAD, bool ZIN>
 void launch_gemm_t(const GemmArgs& a, hipStream_t st) {
     const int tiles = (int)(cdiv(a.P, g2::BP) * cdiv(a.Q, g2::BQ));
-    if (TRANS ? LORA_PINGPONG_DX : LORA_PINGPONG_FWD)
-        hipLaunchKernelGGL((lora_gemm_pp<TRANS, RPAD, ZIN>), dim3(tiles), dim3(pp::NT), 0, st, a);
-    else
-        hipLaunchKernelGGL((lora_gemm<TRANS, RPAD, ZIN>), dim3(tiles), dim3(g2::NT), 0, st, a);
+    hipLaunchKernelGGL((lora_gemm<TRANS, RPAD, ZIN>), dim3(tiles), dim3(g2::NT), 0, st, a);
 }
 
 // In-tile rank-r product for r <= 16 (the input gradient also needs r % 8 == 0,
 // so that rows of B are whole 16-byte chunks); otherwise Z comes precomputed.
-bool gemm_in_tile(bool trans, int r) { return r <= 16 && (!trans || r % 8 == 0); }
+// In-tile rank-r product: the forward forms U = X A^T inside the GEMM for
+// r <= 16.  The input gradient takes V = dY B from the stand-alone pass: its
+// in-tile form needs the transposing reads of B next to those of W, which
+// pushes the kernel past 256 VGPRs (measured: 197 us with V in-tile vs 174 us
+// for pass + GEMM + adapter gradients on the 4096 x 4096 r=8 layer).
+bool gemm_in_tile(bool trans, int r) { return r <= 16 && !trans; }
 
 template <bool TRANS>
 void launch_gemm(const GemmArgs& a, hipStream_t st) {
-    if (gemm_in_tile(TRANS, a.r)) { launch_gemm_t<TRANS, 16, false>(a, st); return; }
+    if constexpr (!TRANS) {
+        if (gemm_in_tile(TRANS, a.r)) { launch_gemm_t<TRANS, 16, false>(a, st); return; }
+    }
     switch (rpad_of(a.r)) {
         case 16: launch_gemm_t<TRANS, 16, true>(a, st); break;
         case 32: launch_gemm_t<TRANS, 32, true>(a, st); break;
@@ -211,12 +218,17 @@ void launch_gemm(const GemmArgs& a, hipStream_t st) {
     }
 }
 
-void launch_skinny(const uint16_t* Y, const uint16_t* F, bool f_trans, float* Z, int P, int C, int r, hipStream_t st) {
-    const dim3 grid((unsigned)cdiv(P, 64));
+void launch_skinny(const uint16_t* Y, const uint16_t* F, bool f_trans, float* Z, int P, int C, int r, hipStream_t st,
+                   float* zpart) {
+    const int parts = zpart ? zparts_for(P, C) : 1;
+    const int chunk = (int)(cdiv(cdiv(C, parts), 64) * 64);
+    const int n_parts = (int)cdiv(C, chunk);
+    float* const out = n_parts > 1 ? zpart : Z;
+    const dim3 grid((unsigned)cdiv(P, 64), (unsigned)n_parts);
     const int rp = rpad_of(r);
-#define SK(RP)                                                                                     \
-    if (f_trans) hipLaunchKernelGGL((skinny_rank<RP, true>), grid, dim3(256), 0, st, Y, F, Z, P, C, r); \
-    else hipLaunchKernelGGL((skinny_rank<RP, false>), grid, dim3(256), 0, st, Y, F, Z, P, C, r);
+#define SK(RP)                                                                                            \
+    if (f_trans) hipLaunchKernelGGL((skinny_rank<RP, true>), grid, dim3(256), 0, st, Y, F, out, P, C, r, chunk); \
+    else hipLaunchKernelGGL((skinny_rank<RP, false>), grid, dim3(256), 0, st, Y, F, out, P, C, r, chunk);
     switch (rp) {
         case 16: SK(16) break;
         case 32: SK(32) break;
@@ -224,6 +236,10 @@ void launch_skinny(const uint16_t* Y, const uint16_t* F, bool f_trans, float* Z,
         default: SK(128) break;
     }
 #undef SK
+    if (n_parts > 1) {
+        const int64_t n = (int64_t)P * r;
+        hipLaunchKernelGGL(skinny_sum, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, st, zpart, Z, n, n_parts);
+    }
 }
 
 void launch_grad_partials(const GradArgs& g, int rpad, hipStream_t st) {
@@ -243,6 +259,7 @@ lora_status fwd_bf16(const lora_linear_desc& d, int mode, const void* X, const v
                      float* U_save, void* ws, hipStream_t st) {
     const Plan plan = make_plan(d);
     const int r = (int)d.r, rpad = rpad_of(r);
+    float* const zpart = plan.max_zparts > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + plan.off_zp) : nullptr;
     if (mode == kFwd) {
         GemmArgs g{};
         g.L = static_cast<const uint16_t*>(X);
@@ -255,7 +272,7 @@ lora_status fwd_bf16(const lora_linear_desc& d, int mode, const void* X, const v
         g.s = d.alpha / (float)d.r;
         if (!gemm_in_tile(false, r)) {
             float* U = U_save ? U_save : reinterpret_cast<float*>(static_cast<char*>(ws) + plan.off_u);
-            launch_skinny(g.L, g.F, false, U, g.P, g.C, r, st);
+            launch_skinny(g.L, g.F, false, U, g.P, g.C, r, st, zpart);
             LAUNCH_CHECK("skinny_rank(U)");
             g.Zin = U;
             g.Zsave = nullptr;
@@ -279,7 +296,7 @@ lora_status fwd_bf16(const lora_linear_desc& d, int mode, const void* X, const v
     a.s = d.alpha / (float)d.r;
     if (zin) {
         float* U = U_save ? U_save : reinterpret_cast<float*>(static_cast<char*>(ws) + plan.off_u);
-        launch_skinny(a.L, a.F, false, U, a.P, a.C, r, st);
+        launch_skinny(a.L, a.F, false, U, a.P, a.C, r, st, zpart);
         LAUNCH_CHECK("skinny_rank(U)");
         a.Zin = U;
         a.Zsave = nullptr;
@@ -298,6 +315,7 @@ lora_status bwd_bf16(const lora_linear_desc& d, bool quant, const void* dY, cons
     const bool zin = rpad > 64;
     char* const wsb = static_cast<char*>(ws);
     float* const V = reinterpret_cast<float*>(wsb + plan.off_v);
+    float* const zpart = plan.max_zparts > 1 ? reinterpret_cast<float*>(wsb + plan.off_zp) : nullptr;
     const uint16_t* const dY16 = static_cast<const uint16_t*>(dY);
     const uint16_t* const X16 = static_cast<const uint16_t*>(X);
     const uint16_t* const A16 = static_cast<const uint16_t*>(A);
@@ -315,7 +333,7 @@ lora_status bwd_bf16(const lora_linear_desc& d, bool quant, const void* dY, cons
         g.P = (int)d.M; g.Q = (int)d.K; g.C = (int)d.N; g.r = r;
         g.s = d.alpha / (float)d.r;
         if (!gemm_in_tile(true, r)) {
-            launch_skinny(dY16, B16, true, V, g.P, g.C, r, st);
+            launch_skinny(dY16, B16, true, V, g.P, g.C, r, st, zpart);
             LAUNCH_CHECK("skinny_rank(V)");
             g.Zin = V;
             g.Zsave = nullptr;
@@ -334,7 +352,7 @@ lora_status bwd_bf16(const lora_linear_desc& d, bool quant, const void* dY, cons
         a.P = (int)d.M; a.Q = (int)d.K; a.C = (int)d.N; a.r = r;
         a.s = d.alpha / (float)d.r;
         if (zin) {
-            launch_skinny(dY16, B16, true, V, a.P, a.C, r, st);
+            launch_skinny(dY16, B16, true, V, a.P, a.C, r, st, zpart);
             LAUNCH_CHECK("skinny_rank(V)");
             a.Zin = V;
             a.Zsave = nullptr;
@@ -342,14 +360,14 @@ lora_status bwd_bf16(const lora_linear_desc& d, bool quant, const void* dY, cons
         launch_fused_mode(quant ? kQDx : kDx, a, rpad, zin, st);
         LAUNCH_CHECK("fused_lora_gemm(dX)");
     } else {
-        launch_skinny(dY16, B16, true, V, (int)d.M, (int)d.N, r, st);
+        launch_skinny(dY16, B16, true, V, (int)d.M, (int)d.N, r, st, zpart);
         LAUNCH_CHECK("skinny_rank(V)");
     }
     // 2. U (saved by the forward, or rebuilt from X)
     const float* U = U_saved;
     if (!U) {
         float* Uw = reinterpret_cast<float*>(wsb + plan.off_u);
-        launch_skinny(X16, A16, false, Uw, (int)d.M, (int)d.K, r, st);
+        launch_skinny(X16, A16, false, Uw, (int)d.M, (int)d.K, r, st, zpart);
         LAUNCH_CHECK("skinny_rank(U)");
         U = Uw;
     }
