@@ -22,8 +22,7 @@
 // buffer_load ... lds (global memory straight into LDS, no VGPRs) into the slot
 // stage kt just vacated.  Each stage is two 32-wide steps; the fragments of the
 // next step are read from LDS while the MFMAs of the current step run, and the
-// workgroup barrier sits between the two steps of a stage, where every wave
-// still has a full step of MFMAs queued to cover the wait:
+// workgroup barrier sits between the two steps of a stage:
 //   [step kk0: MFMA(frags A) | read frags B for kk1]
 //   wait own loads of stage kt+1, barrier, issue loads of stage kt+2
 //   [step kk1: MFMA(frags B) | read frags A for kk0 of stage kt+1]
@@ -244,47 +243,31 @@ __global__ __launch_bounds__(g2::NT) void lora_gemm(const GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < JT; ++i) zacc[i][0] = zacc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // One 32-wide step: the MFMAs of `cur`, p block by p block, with the reads
-    // of the next step's fragments slotted in as the current ones die: L block
-    // pi after its 4 MFMAs (blocks 0 and 1 after the rank-r MFMAs too), F after
-    // the rank-r MFMAs, and in the last two blocks the MFMAs run R fragment by
-    // R fragment so that each R fragment can be replaced as soon as it is dead.
+    // One 32-wide step: the MFMAs of `cur`, then the LDS reads of the next
+    // step's fragments.  The two waves of a SIMD and the hardware's in-order
+    // issue keep the MFMA pipe fed while the reads are in flight; the next
+    // step's first MFMAs wait only for the fragments they use.
     auto step = [&](const Frags<JT>& cur, Frags<JT>& nxt, const uint8_t* nstage, int nkk, auto do_read) {
         constexpr bool RD = decltype(do_read)::value;
 #pragma unroll
-        for (int pi = 0; pi < 6; ++pi) {
+        for (int pi = 0; pi < 8; ++pi)
 #pragma unroll
             for (int qi = 0; qi < 4; ++qi) acc[qi][pi] = mfma16(cur.r[qi], cur.l[pi], acc[qi][pi]);
-            if (pi == 1) {
-                if constexpr (!ZIN) {
+        if constexpr (!ZIN) {
 #pragma unroll
-                    for (int jt = 0; jt < JT; ++jt)
+            for (int jt = 0; jt < JT; ++jt)
 #pragma unroll
-                        for (int z = 0; z < 2; ++z) zacc[jt][z] = mfma16(cur.f[jt], cur.l[z], zacc[jt][z]);
-                    if constexpr (RD) {
-#pragma unroll
-                        for (int jt = 0; jt < JT; ++jt) nxt.f[jt] = read_f(nstage, nkk, jt);
-                    }
-                }
-                if constexpr (RD) {
-                    nxt.l[0] = read_l(nstage, nkk, 0);
-                    nxt.l[1] = read_l(nstage, nkk, 1);
-                }
-            } else if (pi > 1) {
-                if constexpr (RD) nxt.l[pi] = read_l(nstage, nkk, pi);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-#pragma unroll
-        for (int qi = 0; qi < 4; ++qi) {
-            acc[qi][6] = mfma16(cur.r[qi], cur.l[6], acc[qi][6]);
-            acc[qi][7] = mfma16(cur.r[qi], cur.l[7], acc[qi][7]);
-            if constexpr (RD) nxt.r[qi] = read_r(nstage, nkk, qi);
-            __builtin_amdgcn_sched_barrier(0);
+                for (int z = 0; z < 2; ++z) zacc[jt][z] = mfma16(cur.f[jt], cur.l[z], zacc[jt][z]);
         }
         if constexpr (RD) {
-            nxt.l[6] = read_l(nstage, nkk, 6);
-            nxt.l[7] = read_l(nstage, nkk, 7);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) nxt.r[i] = read_r(nstage, nkk, i);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) nxt.l[i] = read_l(nstage, nkk, i);
+            if constexpr (!ZIN) {
+#pragma unroll
+                for (int jt = 0; jt < JT; ++jt) nxt.f[jt] = read_f(nstage, nkk, jt);
+            }
         }
     };
     using Read = std::true_type;
@@ -388,20 +371,31 @@ __global__ __launch_bounds__(g2::NT) void lora_gemm(const GemmArgs a) {
         }
     }
 
-    // store: lane holds Out[p][q .. q+3], p = column l16, q = 4 consecutive rows
+    // store: the bf16 tile goes through LDS ([256 p][256 q], 16-byte chunk c of
+    // row p at c ^ (p % 32)) so that global stores are whole 512-byte row
+    // segments, 16 bytes per lane.  A lane holds Out[p][q .. q+3] of each
+    // accumulator (p = column l16, q = 4 consecutive rows).
+    static_assert(BP * BQ * 2 <= SM::TOTAL, "output tile must fit in LDS");
+    lds_barrier();                       // Zx reads are done
 #pragma unroll
     for (int qi = 0; qi < 4; ++qi) {
-        const int q = q0 + wq * 64 + qi * 16 + 4 * g4;
-        if (q >= Q) continue;
+        const int ql = wq * 64 + qi * 16 + 4 * g4;
 #pragma unroll
         for (int pi = 0; pi < 8; ++pi) {
-            const int p = p0 + wp * 128 + ((pi + 2 * wq) & 7) * 16 + l16;
-            if (p < P) {
-                const f32x4 v = acc[qi][pi];
-                const u32x2 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-                *reinterpret_cast<u32x2*>(a.Out + (size_t)p * Q + q) = o;
-            }
+            const int pl = wp * 128 + ((pi + 2 * wq) & 7) * 16 + l16;
+            const f32x4 v = acc[qi][pi];
+            const u32x2 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+            *reinterpret_cast<u32x2*>(smem + pl * 512 + (((ql >> 3) ^ (pl & 31)) << 4) + (ql & 7) * 2) = o;
         }
+    }
+    lds_barrier();
+    const int sc = tid & 31;             // 16-byte chunk of the row
+#pragma unroll 4
+    for (int pass = 0; pass < BP / 16; ++pass) {
+        const int pl = pass * 16 + (tid >> 5);
+        const int p = p0 + pl, q = q0 + sc * 8;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(smem + pl * 512 + ((sc ^ (pl & 31)) << 4));
+        if (p < P && q < Q) *reinterpret_cast<u32x4*>(a.Out + (size_t)p * Q + q) = v;
     }
 }
 
