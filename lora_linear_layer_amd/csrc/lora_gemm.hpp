@@ -303,9 +303,43 @@ __global__ __launch_bounds__(g2::NT) void lora_gemm(const GemmArgs a) {
     }
     step(fa, fb, smem + ((nk - 1) & 1) * SM::STAGE, 1, Read{});
     step(fb, fa, smem, 0, NoRead{});
-    lds_barrier();   // every wave is done with the last stage before LDS is reused
-
     // ------------------------------------------------------------ epilogue
+    // The E fragments (and Z itself when it comes precomputed) of the first 16
+    // rank columns are requested before the LDS exchange so that their global
+    // latency overlaps it.
+    auto load_e = [&](int jt, bf16x8 (&ef)[4]) {
+#pragma unroll
+        for (int qi = 0; qi < 4; ++qi) {
+            const int q = q0 + wq * 64 + qi * 16 + l16;
+            uint32_t e4[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int j = jt * 16 + 4 * g4 + i;
+                uint32_t v = 0u;
+                if (q < Q && j < r) v = TRANS ? a.E[(size_t)j * Q + q] : a.E[(size_t)q * r + j];
+                e4[i] = v;
+            }
+            const uint32_t w0 = e4[0] | (e4[1] << 16), w1 = e4[2] | (e4[3] << 16);
+            ef[qi] = as_bf16x8(u32x4{w0, w1, w0, w1});
+        }
+    };
+    auto load_zin = [&](int jt, f32x4 (&zv)[8]) {
+#pragma unroll
+        for (int pi = 0; pi < 8; ++pi) {
+            const int p = p0 + wp * 128 + ((pi + 2 * wq) & 7) * 16 + l16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int j = jt * 16 + 4 * g4 + i;
+                zv[pi][i] = (p < P && j < r) ? a.Zin[(size_t)p * r + j] : 0.f;
+            }
+        }
+    };
+    bf16x8 ef0[4];
+    load_e(0, ef0);
+    f32x4 zin0[ZIN ? 8 : 1];
+    if constexpr (ZIN) load_zin(0, zin0);
+
+    lds_barrier();   // every wave is done with the last stage before LDS is reused
     float* const Zx = reinterpret_cast<float*>(smem);   // [256][RPAD] float32
     if constexpr (!ZIN) {
 #pragma unroll
@@ -328,34 +362,24 @@ __global__ __launch_bounds__(g2::NT) void lora_gemm(const GemmArgs a) {
 #pragma unroll 1
     for (int jt = 0; jt < RPAD / 16; ++jt) {
         bf16x8 ef[4];
+        f32x4 zv[ZIN ? 8 : 1];
+        if (jt == 0) {
 #pragma unroll
-        for (int qi = 0; qi < 4; ++qi) {
-            const int q = q0 + wq * 64 + qi * 16 + l16;
-            uint32_t e4[4];
+            for (int qi = 0; qi < 4; ++qi) ef[qi] = ef0[qi];
+            if constexpr (ZIN) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int j = jt * 16 + 4 * g4 + i;
-                uint32_t v = 0u;
-                if (q < Q && j < r) v = TRANS ? a.E[(size_t)j * Q + q] : a.E[(size_t)q * r + j];
-                e4[i] = v;
+                for (int pi = 0; pi < 8; ++pi) zv[pi] = zin0[pi];
             }
-            const uint32_t w0 = e4[0] | (e4[1] << 16), w1 = e4[2] | (e4[3] << 16);
-            ef[qi] = as_bf16x8(u32x4{w0, w1, w0, w1});
+        } else {
+            load_e(jt, ef);
+            if constexpr (ZIN) load_zin(jt, zv);
         }
 #pragma unroll
         for (int pi = 0; pi < 8; ++pi) {
             const int pl = wp * 128 + ((pi + 2 * wq) & 7) * 16 + l16;
             f32x4 z;
-            if constexpr (ZIN) {
-                const int p = p0 + pl;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int j = jt * 16 + 4 * g4 + i;
-                    z[i] = (p < P && j < r) ? a.Zin[(size_t)p * r + j] : 0.f;
-                }
-            } else {
-                z = *reinterpret_cast<const f32x4*>(Zx + pl * RPAD + jt * 16 + 4 * g4);
-            }
+            if constexpr (ZIN) z = zv[pi];
+            else z = *reinterpret_cast<const f32x4*>(Zx + pl * RPAD + jt * 16 + 4 * g4);
             uint32_t hi[4], lo[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {

@@ -14,7 +14,8 @@
 #include "lora_linear.h"
 #include "fused_gemm.hpp"
 #include "lora_gemm.hpp"
-#include "grad_splitm.hpp"
+#include "rank_stream.hpp"
+#include "dequant4.hpp"
 #include "f32_kernels.hpp"
 
 using namespace lora;
@@ -50,21 +51,33 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 int rpad_of(int64_t r) { return r <= 16 ? 16 : r <= 32 ? 32 : r <= 64 ? 64 : 128; }
 
-// Workspace layout for one descriptor (offsets in bytes from ws).
-struct Plan {
-    size_t off_v = 0, off_u = 0, off_pa = 0, off_pb = 0, off_zp = 0, total = 0;
-    int n_mblk = 1, mblk_rows = 128;
-    int max_zparts = 1;   // contraction chunks of the stand-alone rank-r products
+// Chunking of a streamed rank-r product (rank_stream): out_tiles 128-wide
+// output tiles, n_ct 128-deep contraction tiles split into n_chunk chunks
+// (one float32 partial per chunk).
+struct RankSplit {
+    int chunk_tiles = 1, n_chunk = 1;
 };
 
-// Chunks for a stand-alone rank-r product over C: enough workgroups (>= ~1024)
-// to cover the HBM stream of Y, each chunk a multiple of 64.
-int zparts_for(int64_t M, int64_t C) {
-    const int64_t rows = cdiv(M, 64);
-    int64_t n = cdiv(1024, rows);
-    n = std::max<int64_t>(1, std::min<int64_t>(n, cdiv(C, 256)));
-    return (int)n;
+RankSplit rank_split(int64_t out_tiles, int64_t n_ct) {
+    // about 512 workgroups (two per CU), each walking at least two contraction
+    // tiles so that its double-buffered LDS ring has something to overlap
+    RankSplit sp;
+    int64_t n = cdiv(512, std::max<int64_t>(out_tiles, 1));
+    n = std::max<int64_t>(1, std::min<int64_t>(n, cdiv(n_ct, 2)));
+    sp.chunk_tiles = (int)cdiv(n_ct, n);
+    sp.n_chunk = (int)cdiv(n_ct, sp.chunk_tiles);
+    return sp;
 }
+
+// Splits of the three streamed products of one descriptor.
+RankSplit split_z(const lora_linear_desc& d, int64_t C) { return rank_split(cdiv(d.M, kRT), cdiv(C, kRT)); }
+RankSplit split_g(const lora_linear_desc& d) { return rank_split(cdiv(d.K, kRT) + cdiv(d.N, kRT), cdiv(d.M, kRT)); }
+
+// Workspace layout for one descriptor (offsets in bytes from ws).
+struct Plan {
+    size_t off_v = 0, off_u = 0, off_zp = 0, off_ga = 0, off_gb = 0, total = 0;
+    RankSplit g;
+};
 
 Plan make_plan(const lora_linear_desc& d) {
     Plan p;
@@ -73,24 +86,14 @@ Plan make_plan(const lora_linear_desc& d) {
     p.off_u = zbytes;
     size_t cur = 2 * zbytes;
     if (d.dtype == LORA_DTYPE_BF16) {
-        // enough m blocks that the two gradient problems give >= ~1024 workgroups
-        const int64_t cblocks = cdiv(d.K, kGradCB) + cdiv(d.N, kGradCB);
-        const int64_t max_mblk = cdiv(d.M, kGradMB);
-        int64_t want = cdiv(1024, cblocks);
-        if (want < 1) want = 1;
-        if (want > max_mblk) want = max_mblk;
-        const int64_t rows = cdiv(cdiv(d.M, want), kGradMB) * kGradMB;
-        p.mblk_rows = (int)rows;
-        p.n_mblk = (int)cdiv(d.M, rows);
-        p.off_pa = cur;
-        cur += align_up((size_t)p.n_mblk * d.K * d.r * sizeof(float));
-        p.off_pb = cur;
-        cur += align_up((size_t)p.n_mblk * d.N * d.r * sizeof(float));
-        p.max_zparts = std::max(zparts_for(d.M, d.K), zparts_for(d.M, d.N));
-        if (p.max_zparts > 1) {
-            p.off_zp = cur;
-            cur += align_up((size_t)p.max_zparts * d.M * d.r * sizeof(float));
-        }
+        const int zchunks = std::max(split_z(d, d.K).n_chunk, split_z(d, d.N).n_chunk);
+        p.off_zp = cur;
+        cur += align_up((size_t)zchunks * d.M * d.r * sizeof(float));
+        p.g = split_g(d);
+        p.off_ga = cur;
+        cur += align_up((size_t)p.g.n_chunk * d.K * d.r * sizeof(float));
+        p.off_gb = cur;
+        cur += align_up((size_t)p.g.n_chunk * d.N * d.r * sizeof(float));
     }
     p.total = cur;
     return p;
@@ -182,12 +185,8 @@ void launch_fused(const FusedArgs& a, int rpad, bool zin, hipStream_t st) {
 }
 
 void launch_fused_mode(int mode, const FusedArgs& a, int rpad, bool zin, hipStream_t st) {
-    switch (mode) {
-        case kFwd: launch_fused<kFwd>(a, rpad, zin, st); break;
-        case kDx: launch_fused<kDx>(a, rpad, zin, st); break;
-        case kQFwd: launch_fused<kQFwd>(a, rpad, zin, st); break;
-        default: launch_fused<kQDx>(a, rpad, zin, st); break;
-    }
+    if (mode == kQFwd) launch_fused<kQFwd>(a, rpad, zin, st);
+    else launch_fused<kQDx>(a, rpad, zin, st);
 }
 
 template <bool TRANS, int RPAD, bool ZIN>
@@ -196,8 +195,6 @@ void launch_gemm_t(const GemmArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((lora_gemm<TRANS, RPAD, ZIN>), dim3(tiles), dim3(g2::NT), 0, st, a);
 }
 
-// In-tile rank-r product for r <= 16 (the input gradient also needs r % 8 == 0,
-// so that rows of B are whole 16-byte chunks); otherwise Z comes precomputed.
 // In-tile rank-r product: the forward forms U = X A^T inside the GEMM for
 // r <= 16.  The input gradient takes V = dY B from the stand-alone pass: its
 // in-tile form needs the transposing reads of B next to those of W, which
@@ -218,180 +215,187 @@ void launch_gemm(const GemmArgs& a, hipStream_t st) {
     }
 }
 
-void launch_skinny(const uint16_t* Y, const uint16_t* F, bool f_trans, float* Z, int P, int C, int r, hipStream_t st,
-                   float* zpart) {
-    const int parts = zpart ? zparts_for(P, C) : 1;
-    const int chunk = (int)(cdiv(cdiv(C, parts), 64) * 64);
-    const int n_parts = (int)cdiv(C, chunk);
-    float* const out = n_parts > 1 ? zpart : Z;
-    const dim3 grid((unsigned)cdiv(P, 64), (unsigned)n_parts);
-    const int rp = rpad_of(r);
-#define SK(RP)                                                                                            \
-    if (f_trans) hipLaunchKernelGGL((skinny_rank<RP, true>), grid, dim3(256), 0, st, Y, F, out, P, C, r, chunk); \
-    else hipLaunchKernelGGL((skinny_rank<RP, false>), grid, dim3(256), 0, st, Y, F, out, P, C, r, chunk);
-    switch (rp) {
-        case 16: SK(16) break;
-        case 32: SK(32) break;
-        case 64: SK(64) break;
-        default: SK(128) break;
+// Z = Y F^T (Z [M][r] float32) streamed over Y [M][C]; f_trans: F = B [C][r],
+// else F = A [r][C].  Partials go to zpart and are summed into Z.
+void launch_rank_z(const lora_linear_desc& d, const uint16_t* Y, int64_t C, const uint16_t* F, bool f_trans, float* Z,
+                   float* zpart, hipStream_t st) {
+    const RankSplit sp = split_z(d, C);
+    RankArgs a{};
+    a.prob[0] = RankProblem{Y, F, nullptr, sp.n_chunk > 1 ? zpart : Z, (int)C, (int)cdiv(d.M, kRT)};
+    a.n_prob = 1;
+    a.M = (int)d.M;
+    a.r = (int)d.r;
+    a.chunk_tiles = sp.chunk_tiles;
+    a.n_chunk = sp.n_chunk;
+    const dim3 grid((unsigned)a.prob[0].n_tiles, (unsigned)sp.n_chunk, 1);
+#define RZ(RP)                                                                                 \
+    if (f_trans) hipLaunchKernelGGL((rank_stream<RP, false, true>), grid, dim3(256), 0, st, a); \
+    else hipLaunchKernelGGL((rank_stream<RP, false, false>), grid, dim3(256), 0, st, a);
+    for (int j0 = 0; j0 < d.r; j0 += 64) {        // ranks above 64: one launch per 64 columns
+        a.j0 = j0;
+        switch (rpad_of(std::min<int64_t>(d.r - j0, 64))) {
+            case 16: RZ(16) break;
+            case 32: RZ(32) break;
+            default: RZ(64) break;
+        }
     }
-#undef SK
-    if (n_parts > 1) {
-        const int64_t n = (int64_t)P * r;
-        hipLaunchKernelGGL(skinny_sum, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, st, zpart, Z, n, n_parts);
+#undef RZ
+    if (sp.n_chunk > 1) {
+        const int64_t n = d.M * d.r;
+        hipLaunchKernelGGL(partial_sum, dim3((unsigned)cdiv(n, 1024)), dim3(256), 0, st, zpart, Z, n, sp.n_chunk);
     }
 }
 
-void launch_grad_partials(const GradArgs& g, int rpad, hipStream_t st) {
-    const int cb = std::max(g.prob[0].n_cblk, g.n_prob > 1 ? g.prob[1].n_cblk : 0);
-    const dim3 grid((unsigned)cb, (unsigned)g.n_mblk, (unsigned)g.n_prob);
-    switch (rpad) {
-        case 16: hipLaunchKernelGGL((grad_partials<16>), grid, dim3(256), 0, st, g); break;
-        case 32: hipLaunchKernelGGL((grad_partials<32>), grid, dim3(256), 0, st, g); break;
-        case 64: hipLaunchKernelGGL((grad_partials<64>), grid, dim3(256), 0, st, g); break;
-        default: hipLaunchKernelGGL((grad_partials<128>), grid, dim3(256), 0, st, g); break;
+// dA and dB from X, V and dY, U: G-mode partials of both in one launch, then
+// the fixed-order final sum, scale, dtype and layout.
+lora_status launch_adapter_grads(const lora_linear_desc& d, const Plan& plan, char* wsb, const uint16_t* X,
+                                 const float* V, const uint16_t* dY, const float* U, void* dA, void* dB,
+                                 hipStream_t st) {
+    RankArgs a{};
+    float* const ga = reinterpret_cast<float*>(wsb + plan.off_ga);
+    float* const gb = reinterpret_cast<float*>(wsb + plan.off_gb);
+    a.prob[0] = RankProblem{X, nullptr, V, ga, (int)d.K, (int)cdiv(d.K, kRT)};
+    a.prob[1] = RankProblem{dY, nullptr, U, gb, (int)d.N, (int)cdiv(d.N, kRT)};
+    a.n_prob = 2;
+    a.M = (int)d.M;
+    a.r = (int)d.r;
+    a.chunk_tiles = plan.g.chunk_tiles;
+    a.n_chunk = plan.g.n_chunk;
+    const dim3 grid((unsigned)std::max(a.prob[0].n_tiles, a.prob[1].n_tiles), (unsigned)a.n_chunk, 2);
+    for (int j0 = 0; j0 < d.r; j0 += 64) {        // ranks above 64: one launch per 64 columns
+        a.j0 = j0;
+        switch (rpad_of(std::min<int64_t>(d.r - j0, 64))) {
+            case 16: hipLaunchKernelGGL((rank_stream<16, true, false>), grid, dim3(256), 0, st, a); break;
+            case 32: hipLaunchKernelGGL((rank_stream<32, true, false>), grid, dim3(256), 0, st, a); break;
+            default: hipLaunchKernelGGL((rank_stream<64, true, false>), grid, dim3(256), 0, st, a); break;
+        }
     }
+    LAUNCH_CHECK("rank_stream(dA, dB)");
+    GradFinalArgs f{};
+    f.ga = ga;
+    f.gb = gb;
+    f.dA = dA;
+    f.dB = dB;
+    f.K = (int)d.K;
+    f.N = (int)d.N;
+    f.r = (int)d.r;
+    f.n_chunk = plan.g.n_chunk;
+    f.s = d.alpha / (float)d.r;
+    f.f32_out = 0;
+    f.accumulate = (d.flags & LORA_FLAG_ACCUM_GRADS) ? 1 : 0;
+    hipLaunchKernelGGL(grad_final, dim3((unsigned)cdiv((d.K + d.N) * d.r, 256)), dim3(256), 0, st, f);
+    LAUNCH_CHECK("grad_final");
+    return LORA_OK;
 }
 
 // ---------------------------------------------------------------- forward
-lora_status fwd_bf16(const lora_linear_desc& d, int mode, const void* X, const void* W, const uint8_t* Wq,
+lora_status fwd_bf16(const lora_linear_desc& d, bool quant, const void* X, const void* W, const uint8_t* Wq,
                      const uint16_t* absmax, const float* codebook, const void* A, const void* B, void* H,
                      float* U_save, void* ws, hipStream_t st) {
     const Plan plan = make_plan(d);
+    char* const wsb = static_cast<char*>(ws);
     const int r = (int)d.r, rpad = rpad_of(r);
-    float* const zpart = plan.max_zparts > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + plan.off_zp) : nullptr;
-    if (mode == kFwd) {
+    const uint16_t* const X16 = static_cast<const uint16_t*>(X);
+    const uint16_t* const A16 = static_cast<const uint16_t*>(A);
+    float* const zpart = reinterpret_cast<float*>(wsb + plan.off_zp);
+    const bool in_tile = quant ? rpad <= 64 : gemm_in_tile(false, r);
+    float* U = U_save;
+    if (!in_tile) {
+        // U = X A^T by the streamed pass, read by the GEMM epilogue
+        if (!U) U = reinterpret_cast<float*>(wsb + plan.off_u);
+        launch_rank_z(d, X16, d.K, A16, false, U, zpart, st);
+        LAUNCH_CHECK("rank_stream(U)");
+    }
+    if (!quant) {
         GemmArgs g{};
-        g.L = static_cast<const uint16_t*>(X);
+        g.L = X16;
         g.R = static_cast<const uint16_t*>(W);
-        g.F = static_cast<const uint16_t*>(A);
+        g.F = A16;
         g.E = static_cast<const uint16_t*>(B);
         g.Out = static_cast<uint16_t*>(H);
-        g.Zsave = U_save;
+        g.Zsave = in_tile ? U_save : nullptr;
+        g.Zin = in_tile ? nullptr : U;
         g.P = (int)d.M; g.Q = (int)d.N; g.C = (int)d.K; g.r = r;
         g.s = d.alpha / (float)d.r;
-        if (!gemm_in_tile(false, r)) {
-            float* U = U_save ? U_save : reinterpret_cast<float*>(static_cast<char*>(ws) + plan.off_u);
-            launch_skinny(g.L, g.F, false, U, g.P, g.C, r, st, zpart);
-            LAUNCH_CHECK("skinny_rank(U)");
-            g.Zin = U;
-            g.Zsave = nullptr;
-        }
         launch_gemm<false>(g, st);
         LAUNCH_CHECK("lora_gemm(forward)");
         return ok();
     }
-    const bool zin = rpad > 64;
     FusedArgs a{};
-    a.L = static_cast<const uint16_t*>(X);
-    a.R = static_cast<const uint16_t*>(W);
+    a.L = X16;
     a.Rq = Wq;
     a.Rabs = absmax;
     a.codebook = codebook;
-    a.F = static_cast<const uint16_t*>(A);
+    a.F = A16;
     a.E = static_cast<const uint16_t*>(B);
     a.Out = static_cast<uint16_t*>(H);
-    a.Zsave = U_save;
+    a.Zsave = in_tile ? U_save : nullptr;
+    a.Zin = in_tile ? nullptr : U;
     a.P = (int)d.M; a.Q = (int)d.N; a.C = (int)d.K; a.r = r;
     a.s = d.alpha / (float)d.r;
-    if (zin) {
-        float* U = U_save ? U_save : reinterpret_cast<float*>(static_cast<char*>(ws) + plan.off_u);
-        launch_skinny(a.L, a.F, false, U, a.P, a.C, r, st, zpart);
-        LAUNCH_CHECK("skinny_rank(U)");
-        a.Zin = U;
-        a.Zsave = nullptr;
-    }
-    launch_fused_mode(mode, a, rpad, zin, st);
-    LAUNCH_CHECK("fused_lora_gemm(forward)");
+    launch_fused_mode(kQFwd, a, rpad, !in_tile, st);
+    LAUNCH_CHECK("fused_lora_gemm(4-bit forward)");
     return ok();
 }
 
 // ---------------------------------------------------------------- backward
+// Order on the stream: U (if not saved) -> V = dY B -> dX GEMM (V in the
+// epilogue) -> dA, dB partials (one pass over X and one over dY) -> final sum.
 lora_status bwd_bf16(const lora_linear_desc& d, bool quant, const void* dY, const void* X, const void* W,
                      const uint8_t* Wq, const uint16_t* absmax, const float* codebook, const void* A,
                      const void* B, const float* U_saved, void* dX, void* dA, void* dB, void* ws, hipStream_t st) {
     const Plan plan = make_plan(d);
     const int r = (int)d.r, rpad = rpad_of(r);
-    const bool zin = rpad > 64;
     char* const wsb = static_cast<char*>(ws);
     float* const V = reinterpret_cast<float*>(wsb + plan.off_v);
-    float* const zpart = plan.max_zparts > 1 ? reinterpret_cast<float*>(wsb + plan.off_zp) : nullptr;
+    float* const zpart = reinterpret_cast<float*>(wsb + plan.off_zp);
     const uint16_t* const dY16 = static_cast<const uint16_t*>(dY);
     const uint16_t* const X16 = static_cast<const uint16_t*>(X);
     const uint16_t* const A16 = static_cast<const uint16_t*>(A);
     const uint16_t* const B16 = static_cast<const uint16_t*>(B);
 
-    // 1. dX = dY W + s V A with V = dY B formed on chip (and saved for dA)
-    if (dX && !quant) {
-        GemmArgs g{};
-        g.L = dY16;
-        g.R = static_cast<const uint16_t*>(W);
-        g.F = B16;
-        g.E = A16;
-        g.Out = static_cast<uint16_t*>(dX);
-        g.Zsave = V;
-        g.P = (int)d.M; g.Q = (int)d.K; g.C = (int)d.N; g.r = r;
-        g.s = d.alpha / (float)d.r;
-        if (!gemm_in_tile(true, r)) {
-            launch_skinny(dY16, B16, true, V, g.P, g.C, r, st, zpart);
-            LAUNCH_CHECK("skinny_rank(V)");
-            g.Zin = V;
-            g.Zsave = nullptr;
-        }
-        launch_gemm<true>(g, st);
-        LAUNCH_CHECK("lora_gemm(dX)");
-    } else if (dX) {
-        FusedArgs a{};
-        a.L = dY16;
-        a.R = static_cast<const uint16_t*>(W);
-        a.Rq = Wq; a.Rabs = absmax; a.codebook = codebook;
-        a.F = B16;
-        a.E = A16;
-        a.Out = static_cast<uint16_t*>(dX);
-        a.Zsave = V;
-        a.P = (int)d.M; a.Q = (int)d.K; a.C = (int)d.N; a.r = r;
-        a.s = d.alpha / (float)d.r;
-        if (zin) {
-            launch_skinny(dY16, B16, true, V, a.P, a.C, r, st, zpart);
-            LAUNCH_CHECK("skinny_rank(V)");
-            a.Zin = V;
-            a.Zsave = nullptr;
-        }
-        launch_fused_mode(quant ? kQDx : kDx, a, rpad, zin, st);
-        LAUNCH_CHECK("fused_lora_gemm(dX)");
-    } else {
-        launch_skinny(dY16, B16, true, V, (int)d.M, (int)d.N, r, st, zpart);
-        LAUNCH_CHECK("skinny_rank(V)");
-    }
-    // 2. U (saved by the forward, or rebuilt from X)
+    // 1. U (saved by the forward, or rebuilt from X)
     const float* U = U_saved;
     if (!U) {
         float* Uw = reinterpret_cast<float*>(wsb + plan.off_u);
-        launch_skinny(X16, A16, false, Uw, (int)d.M, (int)d.K, r, st, zpart);
-        LAUNCH_CHECK("skinny_rank(U)");
+        launch_rank_z(d, X16, d.K, A16, false, Uw, zpart, st);
+        LAUNCH_CHECK("rank_stream(U)");
         U = Uw;
     }
-    // 3. split-M partials of dA (Y = X, Z = V) and dB (Y = dY, Z = U) in one launch
-    GradArgs g{};
-    g.prob[0] = GradProblem{X16, V, reinterpret_cast<float*>(wsb + plan.off_pa), (int)d.K, (int)cdiv(d.K, kGradCB)};
-    g.prob[1] = GradProblem{dY16, U, reinterpret_cast<float*>(wsb + plan.off_pb), (int)d.N, (int)cdiv(d.N, kGradCB)};
-    g.n_prob = 2;
-    g.M = (int)d.M; g.r = r;
-    g.mblk_rows = plan.mblk_rows; g.n_mblk = plan.n_mblk;
-    launch_grad_partials(g, rpad, st);
-    LAUNCH_CHECK("grad_partials");
-    // 4. fixed-order reduction, scale, dtype, layout
-    ReduceArgs ra{};
-    ra.prob[0] = ReduceProblem{g.prob[0].part, dA, (int)d.K, 1};
-    ra.prob[1] = ReduceProblem{g.prob[1].part, dB, (int)d.N, 0};
-    ra.n_prob = 2;
-    ra.r = r; ra.n_mblk = plan.n_mblk;
-    ra.s = d.alpha / (float)d.r;
-    ra.f32_out = 0;
-    ra.accumulate = (d.flags & LORA_FLAG_ACCUM_GRADS) ? 1 : 0;
-    const int64_t most = std::max(d.K, d.N) * d.r;
-    hipLaunchKernelGGL(grad_reduce, dim3((unsigned)cdiv(most, 256), 2), dim3(256), 0, st, ra);
-    LAUNCH_CHECK("grad_reduce");
+    // 2. V = dY B
+    launch_rank_z(d, dY16, d.N, B16, true, V, zpart, st);
+    LAUNCH_CHECK("rank_stream(V)");
+    // 3. dX = dY W + s V A
+    if (dX) {
+        if (!quant) {
+            GemmArgs g{};
+            g.L = dY16;
+            g.R = static_cast<const uint16_t*>(W);
+            g.F = B16;
+            g.E = A16;
+            g.Out = static_cast<uint16_t*>(dX);
+            g.Zin = V;
+            g.P = (int)d.M; g.Q = (int)d.K; g.C = (int)d.N; g.r = r;
+            g.s = d.alpha / (float)d.r;
+            launch_gemm<true>(g, st);
+            LAUNCH_CHECK("lora_gemm(dX)");
+        } else {
+            FusedArgs a{};
+            a.L = dY16;
+            a.Rq = Wq; a.Rabs = absmax; a.codebook = codebook;
+            a.F = B16;
+            a.E = A16;
+            a.Out = static_cast<uint16_t*>(dX);
+            a.Zin = V;
+            a.P = (int)d.M; a.Q = (int)d.K; a.C = (int)d.N; a.r = r;
+            a.s = d.alpha / (float)d.r;
+            launch_fused_mode(kQDx, a, rpad, true, st);
+            LAUNCH_CHECK("fused_lora_gemm(4-bit dX)");
+        }
+    }
+    // 4., 5. dA = s V^T X, dB = s dY^T U
+    const lora_status gst = launch_adapter_grads(d, plan, wsb, X16, V, dY16, U, dA, dB, st);
+    if (gst != LORA_OK) return gst;
     return ok();
 }
 
@@ -518,7 +522,7 @@ lora_status lora_linear_fwd(const lora_linear_desc* desc, const void* X, const v
     if (st != LORA_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (desc->dtype == LORA_DTYPE_F32) return fwd_f32(*desc, false, X, W, nullptr, nullptr, nullptr, A, B, H, U_save, ws, s);
-    return fwd_bf16(*desc, kFwd, X, W, nullptr, nullptr, nullptr, A, B, H, U_save, ws, s);
+    return fwd_bf16(*desc, false, X, W, nullptr, nullptr, nullptr, A, B, H, U_save, ws, s);
 }
 
 lora_status lora_linear_bwd(const lora_linear_desc* desc, const void* dY, const void* X, const void* W,
@@ -557,7 +561,7 @@ lora_status lora_qlinear_fwd(const lora_linear_desc* desc, const void* X, const 
     if (st != LORA_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (desc->dtype == LORA_DTYPE_F32) return fwd_f32(*desc, true, X, nullptr, Wq, absmax, codebook, A, B, H, U_save, ws, s);
-    return fwd_bf16(*desc, kQFwd, X, nullptr, Wq, absmax, codebook, A, B, H, U_save, ws, s);
+    return fwd_bf16(*desc, true, X, nullptr, Wq, absmax, codebook, A, B, H, U_save, ws, s);
 }
 
 lora_status lora_qlinear_bwd(const lora_linear_desc* desc, const void* dY, const void* X, const uint8_t* Wq,

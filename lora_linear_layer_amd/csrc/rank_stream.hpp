@@ -1,0 +1,302 @@
+// Rank-r products that stream a large bf16 matrix Y [M][C] from HBM once:
+//
+//   Z mode:  Z[m][j] = sum_c Y[m][c] F(j, c)          (U = X A^T, V = dY B)
+//   G mode:  G[c][j] = sum_m Y[m][c] Z2[m][j]         (dA^T = X^T V / s, dB = dY^T U / s)
+//
+// These are the adapter-gradient products of the backward (page "ms-swift高效微调
+// 组合：LoRA+UnSloth提速实践", section 1.2 "梯度计算绕过Autograd": closed-form
+// LoRA gradients; the printed formulas omit the input and the scale, the
+// forms here are the exact vector-Jacobian products) and the stand-alone
+// rank-r products U and V (page "Unsloth — 微调 2-5x 加速", section "核心要点",
+// item 2: only [M, r] intermediates are formed).
+//
+// Both modes are HBM-bound.  A workgroup (4 waves) owns one 128-wide tile of
+// the output's long dimension (m in Z mode, c in G mode) and a chunk of the
+// contraction, walks the chunk in 128 x 128 tiles of Y that arrive through a
+// double-buffered LDS ring straight from global memory (buffer_load ... lds,
+// rows of 256 bytes, 16-byte chunk ch of row x at ch ^ (x & 7)), and writes a
+// float32 partial per chunk; partial_sum adds the chunks in a fixed order, so
+// results are bitwise reproducible.  MFMA 16x16x32 bf16 with float32
+// accumulation; in G mode Z2 enters as a bf16 hi + lo pair and Y^T fragments
+// are gathered with ds_read_b64_tr_b16.
+#pragma once
+#include "lora_gemm.hpp"
+
+namespace lora {
+
+constexpr int kRT = 128;      // tile edge (rows of Y x columns of Y)
+
+struct RankProblem {
+    const uint16_t* Y;      // [M][C] bf16
+    const uint16_t* F;      // Z mode: F_TRANS ? [C][r] : [r][C] bf16
+    const float* Z2;        // G mode: [M][r] float32
+    float* part;            // Z mode: [n_chunk][M][r]; G mode: [n_chunk][C][r]
+    int C;
+    int n_tiles;            // 128-wide tiles of the output's long dimension
+};
+
+struct RankArgs {
+    RankProblem prob[2];
+    int n_prob;
+    int M, r;
+    int j0;                 // first rank column handled by this launch (ranks above 64 take two launches)
+    int chunk_tiles;        // contraction tiles per chunk
+    int n_chunk;
+};
+
+template <int RPAD>
+struct RankSmem {
+    static constexpr int YT = kRT * kRT * 2;          // 32 KB per Y tile
+    static constexpr int SIDE = RPAD * kRT * 2;       // F tile, or one of the Z2 hi / lo tiles
+    static constexpr int STAGE = YT + 2 * SIDE;
+    static constexpr int TOTAL = 2 * STAGE;
+    static_assert(RPAD <= 64 && TOTAL <= 160 * 1024, "LDS budget");
+};
+
+// Z mode when G == false, G mode when G == true.  Handles rank columns
+// j0 .. j0 + min(r - j0, RPAD) - 1.
+template <int RPAD, bool G, bool F_TRANS>
+__global__ __launch_bounds__(256) void rank_stream(const RankArgs a) {
+    using SM = RankSmem<RPAD>;
+    constexpr int JT = RPAD / 16;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[SM::TOTAL];
+
+    const int pidx = blockIdx.z;
+    if (pidx >= a.n_prob) return;
+    const RankProblem pr = a.prob[pidx];
+    if ((int)blockIdx.x >= pr.n_tiles) return;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const int M = a.M, C = pr.C, r = a.r, j0 = a.j0;
+    const int rl = min(r - j0, RPAD);                  // rank columns of this launch
+    // the output tile: m0 (Z mode) or c0 (G mode); contraction tiles [t_begin, t_end)
+    const int o0 = blockIdx.x * kRT;
+    const int n_ct = G ? (M + kRT - 1) / kRT : (C + kRT - 1) / kRT;
+    const int t_begin = blockIdx.y * a.chunk_tiles;
+    const int t_end = min(n_ct, t_begin + a.chunk_tiles);
+
+    // Y tile of contraction tile t: rows m, columns c (256 bytes per row); wave w
+    // issues loads b = 8 w .. 8 w + 7, each 4 rows: row = 4 b + lane / 16
+    const int ld_row0 = wave * 32 + (lane >> 4);
+    auto issue_y = [&](int t, uint8_t* Ys) {
+        const int m0 = G ? t * kRT : o0;
+        const int c0 = G ? o0 : t * kRT;
+        const __amdgpu_buffer_rsrc_t rs =
+            make_rsrc(pr.Y + (size_t)m0 * C + c0, (uint64_t)(min(M - m0, kRT) - 1) * C * 2 + (uint64_t)(C - c0) * 2);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int row = ld_row0 + 4 * i;
+            const int ch = ((lane & 15) ^ (row & 7)) * 8;
+            g2lds16(rs, Ys + (wave * 8 + i) * 1024, (c0 + ch < C) ? (uint32_t)(row * C + ch) * 2u : kOOB);
+        }
+    };
+    // side tiles (small, through VGPRs): F^T [RPAD][128 c] in Z mode, Z2^T hi / lo [RPAD][128 m] in G mode
+    auto side_off = [](int row, int col) -> int {      // byte offset in a [RPAD][128] bf16 tile
+        return row * 256 + ((((col >> 3) ^ (row & 7)) << 4)) + (col & 7) * 2;
+    };
+    constexpr int SIDE_E = RPAD * kRT / 256;          // elements per thread
+    uint32_t sreg[SIDE_E];
+    float zreg[G ? SIDE_E : 1];
+    auto load_side = [&](int t) {
+#pragma unroll
+        for (int i = 0; i < SIDE_E; ++i) {
+            const int e = tid + 256 * i;
+            if constexpr (!G) {
+                const int c0 = t * kRT;
+                if constexpr (F_TRANS) {                 // B [C][r]: element (j, c) at c * r + j
+                    const int c = e / RPAD, j = e % RPAD;
+                    sreg[i] = (j < rl && c0 + c < C) ? pr.F[(size_t)(c0 + c) * r + j0 + j] : 0u;
+                } else {                                 // A [r][C]
+                    const int j = e / kRT, c = e % kRT;
+                    sreg[i] = (j < rl && c0 + c < C) ? pr.F[(size_t)(j0 + j) * C + c0 + c] : 0u;
+                }
+            } else {
+                const int m0 = t * kRT;
+                const int m = e / RPAD, j = e % RPAD;
+                zreg[i] = (j < rl && m0 + m < M) ? pr.Z2[(size_t)(m0 + m) * r + j0 + j] : 0.f;
+            }
+        }
+    };
+    auto store_side = [&](uint8_t* Ss) {
+#pragma unroll
+        for (int i = 0; i < SIDE_E; ++i) {
+            const int e = tid + 256 * i;
+            if constexpr (!G) {
+                int j, c;
+                if constexpr (F_TRANS) { c = e / RPAD; j = e % RPAD; }
+                else { j = e / kRT; c = e % kRT; }
+                *reinterpret_cast<uint16_t*>(Ss + side_off(j, c)) = (uint16_t)sreg[i];
+            } else {
+                const int m = e / RPAD, j = e % RPAD;
+                const float z = zreg[i];
+                const __bf16 h = (__bf16)z;
+                const __bf16 l = (__bf16)(z - (float)h);
+                *reinterpret_cast<__bf16*>(Ss + side_off(j, m)) = h;
+                *reinterpret_cast<__bf16*>(Ss + SM::SIDE + side_off(j, m)) = l;
+            }
+        }
+    };
+
+    f32x4 acc[JT][2];
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt) acc[jt][0] = acc[jt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // prologue: tile t_begin in slot 0
+    if (t_begin < t_end) {
+        issue_y(t_begin, smem);
+        load_side(t_begin);
+        store_side(smem + SM::YT);
+    }
+    vmcnt_le<0>();
+    __syncthreads();
+    for (int t = t_begin; t < t_end; ++t) {
+        uint8_t* const cur = smem + ((t - t_begin) & 1) * SM::STAGE;
+        uint8_t* const nxt = smem + ((t - t_begin + 1) & 1) * SM::STAGE;
+        const bool more = t + 1 < t_end;
+        if (more) {
+            issue_y(t + 1, nxt);
+            load_side(t + 1);
+        }
+        const uint8_t* const Ys = cur;
+        const uint8_t* const Ss = cur + SM::YT;
+        // wave w owns output blocks 2w and 2w + 1 (16 rows each) of the 128-wide tile
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            bf16x8 yf[2];
+            if constexpr (!G) {
+                // B operand: Y rows m (contraction c): 16-byte chunk kk * 4 + g4 of row m
+#pragma unroll
+                for (int z = 0; z < 2; ++z) {
+                    const int m = (2 * wave + z) * 16 + l16;
+                    yf[z] = lds_b128(Ys + m * 256 + (((kk * 4 + g4) ^ (m & 7)) << 4));
+                }
+            } else {
+                // B operand: Y^T, columns c = l16 of block, 8 consecutive m from rows kk*32 + 8 g4 ..
+#pragma unroll
+                for (int z = 0; z < 2; ++z) {
+                    const int c = (2 * wave + z) * 16 + (l16 & 3) * 4;
+                    const int mlo = kk * 32 + g4 * 8 + (l16 >> 2);
+                    const int mhi = mlo + 4;
+                    const i16x4 lo = lds_tr4(Ys + mlo * 256 + ((((c >> 3) ^ (mlo & 7))) << 4) + (c & 7) * 2);
+                    const i16x4 hi = lds_tr4(Ys + mhi * 256 + ((((c >> 3) ^ (mhi & 7))) << 4) + (c & 7) * 2);
+                    yf[z] = cat_tr(lo, hi);
+                }
+            }
+#pragma unroll
+            for (int jt = 0; jt < JT; ++jt) {
+                const int j = jt * 16 + l16;
+                const int off = j * 256 + (((kk * 4 + g4) ^ (j & 7)) << 4);
+                const bf16x8 sa = lds_b128(Ss + off);
+#pragma unroll
+                for (int z = 0; z < 2; ++z) acc[jt][z] = mfma16(sa, yf[z], acc[jt][z]);
+                if constexpr (G) {
+                    const bf16x8 sl = lds_b128(Ss + SM::SIDE + off);
+#pragma unroll
+                    for (int z = 0; z < 2; ++z) acc[jt][z] = mfma16(sl, yf[z], acc[jt][z]);
+                }
+            }
+        }
+        if (more) store_side(nxt + SM::YT);
+        vmcnt_le<0>();
+        __syncthreads();
+    }
+
+    // lane holds out^T rows j = jt*16 + 4 g4 + i at column o = block*16 + l16
+    const int olim = G ? C : M;
+    float* const out = pr.part + (size_t)blockIdx.y * olim * r;
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+        for (int z = 0; z < 2; ++z) {
+            const int o = o0 + (2 * wave + z) * 16 + l16;
+            if (o >= olim) continue;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int j = jt * 16 + 4 * g4 + i;
+                if (j < rl) out[(size_t)o * r + j0 + j] = acc[jt][z][i];
+            }
+        }
+}
+
+// out[e] = sum over k < n_parts of part[k * n + e], added in increasing k.
+// Each thread owns 4 consecutive elements; the partial loads are issued 8 at a
+// time so that their latencies overlap (the additions keep the fixed order).
+__global__ __launch_bounds__(256) void partial_sum(const float* __restrict__ part, float* __restrict__ out, int64_t n,
+                                                   int n_parts) {
+    const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (e0 >= n) return;
+    const int cnt = (int)min<int64_t>(4, n - e0);
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    auto load4 = [&](int k) -> f32x4 {
+        const float* p = part + (size_t)k * n + e0;
+        if (cnt == 4 && (e0 & 3) == 0 && (n & 3) == 0) return *reinterpret_cast<const f32x4*>(p);
+        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < cnt; ++i) v[i] = p[i];
+        return v;
+    };
+    int k = 0;
+    for (; k + 8 <= n_parts; k += 8) {
+        f32x4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = load4(k + u);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    for (; k < n_parts; ++k) s += load4(k);
+    for (int i = 0; i < cnt; ++i) out[e0 + i] = s[i];
+}
+
+// Final adapter gradients from the G-mode partials:
+//   dA[j][k] = s * sum_chunk GA[chunk][k][j]   ([r][K] output)
+//   dB[n][j] = s * sum_chunk GB[chunk][n][j]   ([N][r] output)
+// in the tensor dtype, overwritten or accumulated.
+struct GradFinalArgs {
+    const float* ga;
+    const float* gb;
+    void* dA;
+    void* dB;
+    int K, N, r, n_chunk;
+    float s;
+    int f32_out, accumulate;
+};
+
+__global__ __launch_bounds__(256) void grad_final(const GradFinalArgs a) {
+    const int64_t na = (int64_t)a.K * a.r, nb = (int64_t)a.N * a.r;
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= na + nb) return;
+    const bool isA = e < na;
+    const int64_t f = isA ? e : e - na;
+    const int64_t n = isA ? na : nb;
+    const float* part = isA ? a.ga : a.gb;
+    float sum = 0.f;
+    int k = 0;
+    for (; k + 8 <= a.n_chunk; k += 8) {       // eight loads in flight, summed in chunk order
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = part[(size_t)(k + u) * n + f];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) sum += v[u];
+    }
+    for (; k < a.n_chunk; ++k) sum += part[(size_t)k * n + f];
+    float v = sum * a.s;
+    size_t o;
+    if (isA) {
+        const int kk = (int)(f / a.r), j = (int)(f % a.r);
+        o = (size_t)j * a.K + kk;
+    } else {
+        o = (size_t)f;
+    }
+    void* dst = isA ? a.dA : a.dB;
+    if (a.f32_out) {
+        float* p = reinterpret_cast<float*>(dst);
+        if (a.accumulate) v += p[o];
+        p[o] = v;
+    } else {
+        uint16_t* p = reinterpret_cast<uint16_t*>(dst);
+        if (a.accumulate) v += bf16_bits_to_f32(p[o]);
+        p[o] = __builtin_bit_cast(uint16_t, (__bf16)v);
+    }
+}
+
+}  // namespace lora
