@@ -3,7 +3,7 @@
 //   Z[p][j]   = sum_c Y[p][c] F(j, c)                       (f32_skinny)
 //   Out[p][q] = sum_c L[p][c] R(q, c) + s sum_j E(q, j) Z[p][j]   (f32_fused)
 //   G[c][j]   = sum_m Y[m][c] Z[m][j], scaled by s          (f32_grad)
-// Role mapping is the same as in the bf16 kernels (fused_gemm.hpp).
+// Role mapping is the same as in the bf16 GEMM (lora_gemm.hpp).
 #pragma once
 #include "common.hpp"
 

@@ -43,6 +43,16 @@
 // epilogue Z meets in LDS and s Z E^T is applied with MFMA, s Z split into
 // bf16 hi + lo halves that fill the two halves of the 32-long contraction.
 // ZIN = true takes a precomputed Z [P][r] float32 instead (large r).
+//
+// Q4 = true: R is a 4-bit weight matrix (page "Unsloth — 微调 2-5x 加速",
+// section "核心要点", item 3).  Its codes and absmax travel through registers
+// instead of the direct LDS path: each thread loads 16 code bytes (32 weights
+// of one row inside one 64-block) and that block's absmax when the stage is
+// issued, and one step later decodes them, codebook[code] * absmax in float32
+// rounded to bf16 (the standalone dequantisation's exact values), into the
+// stage's R tile in the same swizzled layout, before the barrier that
+// publishes the stage.  Every weight is decoded once per workgroup; the
+// reads, MFMAs and epilogue are the 16-bit kernel's.
 #pragma once
 #include <type_traits>
 
@@ -96,6 +106,9 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 struct GemmArgs {
     const uint16_t* L;      // [P][C] bf16
     const uint16_t* R;      // forward: [Q][C]; input gradient: [C][Q]
+    const uint8_t* Rq;      // 4-bit weights: codes, forward [Q][C/2], input gradient [C][Q/2]
+    const uint16_t* Rabs;   // 4-bit weights: fp16 absmax, forward [Q][C/64], input gradient [C][Q/64]
+    const float* codebook;  // 4-bit weights: 16 float32 values
     const uint16_t* F;      // forward: A [r][C]; input gradient: B [C][r]
     const uint16_t* E;      // forward: B [Q][r]; input gradient: A [r][Q]
     const float* Zin;       // precomputed Z [P][r] (ZIN), else unused
@@ -110,11 +123,12 @@ constexpr int BP = 256, BQ = 256, BK = 64, NT = 512;
 constexpr int TILE = BP * BK * 2;             // 32 KB per operand per stage
 }  // namespace g2
 
-template <int RPAD, bool ZIN>
+template <int RPAD, bool ZIN, bool Q4 = false>
 struct GemmSmem {
     static constexpr int F_BYTES = ZIN ? 0 : RPAD * g2::BK * 2;
     static constexpr int STAGE = 2 * g2::TILE + F_BYTES;
-    static constexpr int TOTAL = 2 * STAGE;
+    static constexpr int LUT = 2 * STAGE;                       // 4-bit codebook (16 float32)
+    static constexpr int TOTAL = 2 * STAGE + (Q4 ? 64 : 0);
     static_assert(F_BYTES % 1024 == 0, "F tile is whole 1 KB wave loads");
     static_assert(ZIN || g2::BP * RPAD * 4 <= TOTAL, "Z exchange must fit");
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
@@ -127,10 +141,10 @@ struct Frags {
     bf16x8 f[JT];     // F, rank rows
 };
 
-template <bool TRANS, int RPAD, bool ZIN>
+template <bool TRANS, int RPAD, bool ZIN, bool Q4 = false>
 __global__ __launch_bounds__(g2::NT) void lora_gemm(const GemmArgs a) {
     using namespace g2;
-    using SM = GemmSmem<RPAD, ZIN>;
+    using SM = GemmSmem<RPAD, ZIN, Q4>;
     static_assert(ZIN || !TRANS, "the input gradient takes V precomputed");
     constexpr int JT = ZIN ? 1 : RPAD / 16;
     constexpr int F_LOADS = SM::F_BYTES / 1024;   // done by waves 0 .. F_LOADS - 1
@@ -160,7 +174,9 @@ __global__ __launch_bounds__(g2::NT) void lora_gemm(const GemmArgs a) {
     __amdgpu_buffer_rsrc_t rsR;
     uint32_t offR = 0;
     int chR0 = 0, chR1 = 0;
-    if constexpr (!TRANS) {
+    if constexpr (Q4) {
+        // R tiles come through registers (load_q / decode_q)
+    } else if constexpr (!TRANS) {
         rsR = make_rsrc(a.R + (size_t)q0 * C, (uint64_t)min(Q - q0, BQ) * C * 2);
         offR = (uint32_t)(kc_row0 * C + kc_ch) * 2u;
     } else {
@@ -182,6 +198,57 @@ __global__ __launch_bounds__(g2::NT) void lora_gemm(const GemmArgs a) {
         offF = (uint32_t)(frow * C + fch) * 2u;
     }
 
+    // 4-bit weights: each thread fetches 16 bytes of codes (32 weights of one
+    // row, within one 64-block) and the block's absmax into registers when a
+    // stage is issued, and decodes them into the stage's bf16 R tile (same LDS
+    // layout as the 16-bit path) just before the barrier that publishes it.
+    u32x4 qreg = {0u, 0u, 0u, 0u};
+    float am_reg = 0.f;
+    if constexpr (Q4) {
+        if (tid < 16) reinterpret_cast<float*>(smem + SM::LUT)[tid] = a.codebook[tid];
+    }
+    auto load_q = [&](int kt) {
+        const int c0 = kt * BK;
+        if constexpr (!TRANS) {              // codes [Q][C/2]: row q = tid / 2, weights c0 + 32 (tid % 2) ..
+            const int q = tid >> 1, h = tid & 1;
+            const bool ok = q0 + q < Q;
+            qreg = ok ? *reinterpret_cast<const u32x4*>(a.Rq + (size_t)(q0 + q) * (C >> 1) + (c0 >> 1) + 16 * h)
+                      : u32x4{0u, 0u, 0u, 0u};
+            am_reg = ok ? f16_bits_to_f32(a.Rabs[(size_t)(q0 + q) * (C >> 6) + kt]) : 0.f;
+        } else {                             // codes [C][Q/2]: row c = tid / 8, weights q0 + 32 (tid % 8) ..
+            const int c = tid >> 3, pp = tid & 7;
+            const bool ok = c0 + c < C && q0 + 32 * pp < Q;
+            const size_t qq = (size_t)q0 + 32 * pp;
+            qreg = ok ? *reinterpret_cast<const u32x4*>(a.Rq + (size_t)(c0 + c) * (Q >> 1) + (qq >> 1))
+                      : u32x4{0u, 0u, 0u, 0u};
+            am_reg = ok ? f16_bits_to_f32(a.Rabs[(size_t)(c0 + c) * (Q >> 6) + (qq >> 6)]) : 0.f;
+        }
+    };
+    auto decode_q = [&](int kt) {
+        uint8_t* const Rs = smem + (kt & 1) * SM::STAGE + TILE;
+        const float* const lut = reinterpret_cast<const float*>(smem + SM::LUT);
+        u32x4 outv[4];
+#pragma unroll
+        for (int b = 0; b < 16; ++b) {       // byte b holds weights 2b (low nibble) and 2b + 1
+            const uint32_t byte = (qreg[b >> 2] >> (8 * (b & 3))) & 0xFFu;
+            const float lo = lut[byte & 15u] * am_reg, hi = lut[byte >> 4] * am_reg;
+            outv[b >> 2][b & 3] = pack_bf16x2(lo, hi);
+        }
+        if constexpr (!TRANS) {              // row q, 16-byte chunks 4h .. 4h + 3, chunk ch at ch ^ (q & 7)
+            const int q = tid >> 1, h = tid & 1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<u32x4*>(Rs + q * 128 + (((4 * h + i) ^ (q & 7)) << 4)) = outv[i];
+        } else {                             // row c, 32-byte slots 2 pp, 2 pp + 1 (swizzled by sw512)
+            const int c = tid >> 3, pp = tid & 7;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int slot = 2 * pp + (i >> 1);
+                *reinterpret_cast<u32x4*>(Rs + c * 512 + ((slot ^ sw512(c)) << 5) + (i & 1) * 16) = outv[i];
+            }
+        }
+    };
+
     auto issue_stage = [&](int kt) {
         const int c0 = kt * BK;
         uint8_t* const Ls = smem + (kt & 1) * SM::STAGE;
@@ -191,7 +258,9 @@ __global__ __launch_bounds__(g2::NT) void lora_gemm(const GemmArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             g2lds16(rsL, Ls + (wave * 4 + i) * 1024, lok ? offL + (uint32_t)(i * 8 * C + c0) * 2u : kOOB);
-        if constexpr (!TRANS) {
+        if constexpr (Q4) {
+            load_q(kt);
+        } else if constexpr (!TRANS) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 g2lds16(rsR, Rs + (wave * 4 + i) * 1024, lok ? offR + (uint32_t)(i * 8 * C + c0) * 2u : kOOB);
@@ -275,12 +344,20 @@ __global__ __launch_bounds__(g2::NT) void lora_gemm(const GemmArgs a) {
 
     // ------------------------------------------------------------ main loop
     const int nk = (C + BK - 1) / BK;
-    issue_stage(0);
-    if (nk > 1) {
-        issue_stage(1);
-        if (wave < F_LOADS) vmcnt_le<9>(); else vmcnt_le<8>();   // stage 0 landed, stage 1 in flight
-    } else {
+    if constexpr (Q4) {
+        lds_barrier();                       // codebook in LDS
+        issue_stage(0);
+        decode_q(0);
+        if (nk > 1) issue_stage(1);
         vmcnt_le<0>();
+    } else {
+        issue_stage(0);
+        if (nk > 1) {
+            issue_stage(1);
+            if (wave < F_LOADS) vmcnt_le<9>(); else vmcnt_le<8>();   // stage 0 landed, stage 1 in flight
+        } else {
+            vmcnt_le<0>();
+        }
     }
     lds_barrier();
 
@@ -296,6 +373,7 @@ __global__ __launch_bounds__(g2::NT) void lora_gemm(const GemmArgs a) {
     for (int kt = 0; kt + 1 < nk; ++kt) {
         const uint8_t* const cur = smem + (kt & 1) * SM::STAGE;
         step(fa, fb, cur, 1, Read{});
+        if constexpr (Q4) decode_q(kt + 1);  // R tile of stage kt + 1 from the registers loaded at its issue
         vmcnt_le<0>();           // this wave's loads of stage kt + 1 have landed
         lds_barrier();           // ... and everyone's; stage kt's slot is free
         if (kt + 2 < nk) issue_stage(kt + 2);

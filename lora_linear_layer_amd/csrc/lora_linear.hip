@@ -12,7 +12,7 @@
 #include <string>
 
 #include "lora_linear.h"
-#include "fused_gemm.hpp"
+
 #include "lora_gemm.hpp"
 #include "rank_stream.hpp"
 #include "dequant4.hpp"
@@ -168,31 +168,10 @@ lora_status launched(const char* what) {
     } while (0)
 
 // ---------------------------------------------------------------- bf16 launches
-template <int MODE, int RPAD, bool ZIN>
-void launch_fused_t(const FusedArgs& a, hipStream_t st) {
-    const int tiles = (int)(cdiv(a.P, kBP) * cdiv(a.Q, kBQ));
-    hipLaunchKernelGGL((fused_lora_gemm<MODE, RPAD, ZIN>), dim3(tiles), dim3(kThreads), 0, st, a);
-}
-
-template <int MODE>
-void launch_fused(const FusedArgs& a, int rpad, bool zin, hipStream_t st) {
-    if (zin) { launch_fused_t<MODE, 128, true>(a, st); return; }
-    switch (rpad) {
-        case 16: launch_fused_t<MODE, 16, false>(a, st); break;
-        case 32: launch_fused_t<MODE, 32, false>(a, st); break;
-        default: launch_fused_t<MODE, 64, false>(a, st); break;
-    }
-}
-
-void launch_fused_mode(int mode, const FusedArgs& a, int rpad, bool zin, hipStream_t st) {
-    if (mode == kQFwd) launch_fused<kQFwd>(a, rpad, zin, st);
-    else launch_fused<kQDx>(a, rpad, zin, st);
-}
-
-template <bool TRANS, int RPAD, bool ZIN>
+template <bool TRANS, int RPAD, bool ZIN, bool Q4>
 void launch_gemm_t(const GemmArgs& a, hipStream_t st) {
     const int tiles = (int)(cdiv(a.P, g2::BP) * cdiv(a.Q, g2::BQ));
-    hipLaunchKernelGGL((lora_gemm<TRANS, RPAD, ZIN>), dim3(tiles), dim3(g2::NT), 0, st, a);
+    hipLaunchKernelGGL((lora_gemm<TRANS, RPAD, ZIN, Q4>), dim3(tiles), dim3(g2::NT), 0, st, a);
 }
 
 // In-tile rank-r product: the forward forms U = X A^T inside the GEMM for
@@ -202,16 +181,16 @@ void launch_gemm_t(const GemmArgs& a, hipStream_t st) {
 // for pass + GEMM + adapter gradients on the 4096 x 4096 r=8 layer).
 bool gemm_in_tile(bool trans, int r) { return r <= 16 && !trans; }
 
-template <bool TRANS>
+template <bool TRANS, bool Q4>
 void launch_gemm(const GemmArgs& a, hipStream_t st) {
     if constexpr (!TRANS) {
-        if (gemm_in_tile(TRANS, a.r)) { launch_gemm_t<TRANS, 16, false>(a, st); return; }
+        if (gemm_in_tile(TRANS, a.r)) { launch_gemm_t<TRANS, 16, false, Q4>(a, st); return; }
     }
     switch (rpad_of(a.r)) {
-        case 16: launch_gemm_t<TRANS, 16, true>(a, st); break;
-        case 32: launch_gemm_t<TRANS, 32, true>(a, st); break;
-        case 64: launch_gemm_t<TRANS, 64, true>(a, st); break;
-        default: launch_gemm_t<TRANS, 128, true>(a, st); break;
+        case 16: launch_gemm_t<TRANS, 16, true, Q4>(a, st); break;
+        case 32: launch_gemm_t<TRANS, 32, true, Q4>(a, st); break;
+        case 64: launch_gemm_t<TRANS, 64, true, Q4>(a, st); break;
+        default: launch_gemm_t<TRANS, 128, true, Q4>(a, st); break;
     }
 }
 
@@ -294,11 +273,11 @@ lora_status fwd_bf16(const lora_linear_desc& d, bool quant, const void* X, const
                      float* U_save, void* ws, hipStream_t st) {
     const Plan plan = make_plan(d);
     char* const wsb = static_cast<char*>(ws);
-    const int r = (int)d.r, rpad = rpad_of(r);
+    const int r = (int)d.r;
     const uint16_t* const X16 = static_cast<const uint16_t*>(X);
     const uint16_t* const A16 = static_cast<const uint16_t*>(A);
     float* const zpart = reinterpret_cast<float*>(wsb + plan.off_zp);
-    const bool in_tile = quant ? rpad <= 64 : gemm_in_tile(false, r);
+    const bool in_tile = gemm_in_tile(false, r);
     float* U = U_save;
     if (!in_tile) {
         // U = X A^T by the streamed pass, read by the GEMM epilogue
@@ -306,35 +285,22 @@ lora_status fwd_bf16(const lora_linear_desc& d, bool quant, const void* X, const
         launch_rank_z(d, X16, d.K, A16, false, U, zpart, st);
         LAUNCH_CHECK("rank_stream(U)");
     }
-    if (!quant) {
-        GemmArgs g{};
-        g.L = X16;
-        g.R = static_cast<const uint16_t*>(W);
-        g.F = A16;
-        g.E = static_cast<const uint16_t*>(B);
-        g.Out = static_cast<uint16_t*>(H);
-        g.Zsave = in_tile ? U_save : nullptr;
-        g.Zin = in_tile ? nullptr : U;
-        g.P = (int)d.M; g.Q = (int)d.N; g.C = (int)d.K; g.r = r;
-        g.s = d.alpha / (float)d.r;
-        launch_gemm<false>(g, st);
-        LAUNCH_CHECK("lora_gemm(forward)");
-        return ok();
-    }
-    FusedArgs a{};
-    a.L = X16;
-    a.Rq = Wq;
-    a.Rabs = absmax;
-    a.codebook = codebook;
-    a.F = A16;
-    a.E = static_cast<const uint16_t*>(B);
-    a.Out = static_cast<uint16_t*>(H);
-    a.Zsave = in_tile ? U_save : nullptr;
-    a.Zin = in_tile ? nullptr : U;
-    a.P = (int)d.M; a.Q = (int)d.N; a.C = (int)d.K; a.r = r;
-    a.s = d.alpha / (float)d.r;
-    launch_fused_mode(kQFwd, a, rpad, !in_tile, st);
-    LAUNCH_CHECK("fused_lora_gemm(4-bit forward)");
+    GemmArgs g{};
+    g.L = X16;
+    g.R = static_cast<const uint16_t*>(W);
+    g.Rq = Wq;
+    g.Rabs = absmax;
+    g.codebook = codebook;
+    g.F = A16;
+    g.E = static_cast<const uint16_t*>(B);
+    g.Out = static_cast<uint16_t*>(H);
+    g.Zsave = in_tile ? U_save : nullptr;
+    g.Zin = in_tile ? nullptr : U;
+    g.P = (int)d.M; g.Q = (int)d.N; g.C = (int)d.K; g.r = r;
+    g.s = d.alpha / (float)d.r;
+    if (quant) launch_gemm<false, true>(g, st);
+    else launch_gemm<false, false>(g, st);
+    LAUNCH_CHECK(quant ? "lora_gemm(4-bit forward)" : "lora_gemm(forward)");
     return ok();
 }
 
@@ -345,7 +311,7 @@ lora_status bwd_bf16(const lora_linear_desc& d, bool quant, const void* dY, cons
                      const uint8_t* Wq, const uint16_t* absmax, const float* codebook, const void* A,
                      const void* B, const float* U_saved, void* dX, void* dA, void* dB, void* ws, hipStream_t st) {
     const Plan plan = make_plan(d);
-    const int r = (int)d.r, rpad = rpad_of(r);
+    const int r = (int)d.r;
     char* const wsb = static_cast<char*>(ws);
     float* const V = reinterpret_cast<float*>(wsb + plan.off_v);
     float* const zpart = reinterpret_cast<float*>(wsb + plan.off_zp);
@@ -367,31 +333,21 @@ lora_status bwd_bf16(const lora_linear_desc& d, bool quant, const void* dY, cons
     LAUNCH_CHECK("rank_stream(V)");
     // 3. dX = dY W + s V A
     if (dX) {
-        if (!quant) {
-            GemmArgs g{};
-            g.L = dY16;
-            g.R = static_cast<const uint16_t*>(W);
-            g.F = B16;
-            g.E = A16;
-            g.Out = static_cast<uint16_t*>(dX);
-            g.Zin = V;
-            g.P = (int)d.M; g.Q = (int)d.K; g.C = (int)d.N; g.r = r;
-            g.s = d.alpha / (float)d.r;
-            launch_gemm<true>(g, st);
-            LAUNCH_CHECK("lora_gemm(dX)");
-        } else {
-            FusedArgs a{};
-            a.L = dY16;
-            a.Rq = Wq; a.Rabs = absmax; a.codebook = codebook;
-            a.F = B16;
-            a.E = A16;
-            a.Out = static_cast<uint16_t*>(dX);
-            a.Zin = V;
-            a.P = (int)d.M; a.Q = (int)d.K; a.C = (int)d.N; a.r = r;
-            a.s = d.alpha / (float)d.r;
-            launch_fused_mode(kQDx, a, rpad, true, st);
-            LAUNCH_CHECK("fused_lora_gemm(4-bit dX)");
-        }
+        GemmArgs g{};
+        g.L = dY16;
+        g.R = static_cast<const uint16_t*>(W);
+        g.Rq = Wq;
+        g.Rabs = absmax;
+        g.codebook = codebook;
+        g.F = B16;
+        g.E = A16;
+        g.Out = static_cast<uint16_t*>(dX);
+        g.Zin = V;
+        g.P = (int)d.M; g.Q = (int)d.K; g.C = (int)d.N; g.r = r;
+        g.s = d.alpha / (float)d.r;
+        if (quant) launch_gemm<true, true>(g, st);
+        else launch_gemm<true, false>(g, st);
+        LAUNCH_CHECK(quant ? "lora_gemm(4-bit dX)" : "lora_gemm(dX)");
     }
     // 4., 5. dA = s V^T X, dB = s dY^T U
     const lora_status gst = launch_adapter_grads(d, plan, wsb, X16, V, dY16, U, dA, dB, st);
