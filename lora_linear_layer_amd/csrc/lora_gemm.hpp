@@ -74,8 +74,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 }
 
 // 16 bytes per lane from global (rsrc + voff) into LDS at lds_wave_base + 16 * lane.
+// UNTRACKED = true issues it as asm, hidden from the compiler's wait-count
+// bookkeeping: the compiler cannot tell a transposing LDS read
+// (ds_read_b64_tr_b16) from an in-flight load into another stage and would
+// put a full vmcnt(0) in front of every such read, exposing the next stage's
+// load latency on every step.  Callers wait for these loads themselves
+// (vmcnt_le) before the barrier that publishes a stage.  M0 carries the
+// wave's LDS base.
+template <bool UNTRACKED = false>
 __device__ __forceinline__ void g2lds16(__amdgpu_buffer_rsrc_t rs, void* lds_wave_base, uint32_t voff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_ptr)lds_wave_base, 16, voff, 0, 0, 0);
+    if constexpr (UNTRACKED) {
+        const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(lds_void_ptr)lds_wave_base);
+        asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "{m0}"(lds) : "memory");
+    } else {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_ptr)lds_wave_base, 16, voff, 0, 0, 0);
+    }
 }
 
 // ds_read_b64_tr_b16: within each 16-lane group, lane j receives element j % 4
@@ -119,9 +132,19 @@ struct GemmArgs {
 };
 
 namespace g2 {
-constexpr int BP = 256, BQ = 256, BK = 64, NT = 512;
+constexpr int BP = 256, BQ = 256, BK = 64;
 constexpr int TILE = BP * BK * 2;             // 32 KB per operand per stage
 }  // namespace g2
+
+// Wave layout of the 256 x 256 tile: 2 (p) x 4 (q) waves of 128 x 64, two
+// waves per SIMD.
+namespace g2w {
+constexpr int NT = 512;
+constexpr int WQN = 4;        // waves along q
+constexpr int QB = 4;         // q blocks of 16 per wave
+constexpr int ZB = 2;         // p blocks per wave in the rank-r product
+constexpr int LPW = 4;        // 1 KB loads per wave per operand per stage
+}  // namespace g2w
 
 template <int RPAD, bool ZIN, bool Q4 = false>
 struct GemmSmem {
@@ -134,16 +157,17 @@ struct GemmSmem {
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
 };
 
-template <int JT>
+template <int JT, int QB>
 struct Frags {
-    bf16x8 r[4];      // R, 4 q blocks of 16
-    bf16x8 l[8];      // L, 8 p blocks of 16 (slot i = block (i + 2 wq) % 8)
+    bf16x8 r[QB];     // R, QB q blocks of 16
+    bf16x8 l[8];      // L, 8 p blocks of 16 (slot i = block (i + ZB wq) % 8)
     bf16x8 f[JT];     // F, rank rows
 };
 
 template <bool TRANS, int RPAD, bool ZIN, bool Q4 = false>
-__global__ __launch_bounds__(g2::NT) void lora_gemm(const GemmArgs a) {
+__global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
     using namespace g2;
+    using namespace g2w;
     using SM = GemmSmem<RPAD, ZIN, Q4>;
     static_assert(ZIN || !TRANS, "the input gradient takes V precomputed");
     constexpr int JT = ZIN ? 1 : RPAD / 16;
@@ -154,7 +178,7 @@ __global__ __launch_bounds__(g2::NT) void lora_gemm(const GemmArgs a) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wp = wave >> 2, wq = wave & 3;
+    const int wp = wave / WQN, wq = wave % WQN;
     const int l16 = lane & 15, g4 = lane >> 4;
 
     const int P = a.P, Q = a.Q, C = a.C, r = a.r;
@@ -164,29 +188,33 @@ __global__ __launch_bounds__(g2::NT) void lora_gemm(const GemmArgs a) {
     const int p0 = pt * BP, q0 = qt * BQ;
 
     // ------------------------------------------------------------ load plan
-    // Row layout tiles: load i of wave w covers rows (4w + i) * 8 + lane / 8;
+    // Row layout tiles: load i of wave w covers rows (LPW w + i) * 8 + lane / 8;
     // lane's 16-byte chunk is (lane % 8) ^ (row % 8) = (lane % 8) ^ (lane / 8),
     // the same for every i, so one base offset plus a uniform stride suffices.
-    const int kc_row0 = wave * 32 + (lane >> 3);
+    const int kc_row0 = wave * LPW * 8 + (lane >> 3);
     const int kc_ch = ((lane & 7) ^ (lane >> 3)) * 8;
     const __amdgpu_buffer_rsrc_t rsL = make_rsrc(a.L + (size_t)p0 * C, (uint64_t)min(P - p0, BP) * C * 2);
     const uint32_t offL = (uint32_t)(kc_row0 * C + kc_ch) * 2u;
     __amdgpu_buffer_rsrc_t rsR;
     uint32_t offR = 0;
-    int chR0 = 0, chR1 = 0;
+    int chR[LPW == 8 ? 4 : 2] = {};
     if constexpr (Q4) {
         // R tiles come through registers (load_q / decode_q)
     } else if constexpr (!TRANS) {
         rsR = make_rsrc(a.R + (size_t)q0 * C, (uint64_t)min(Q - q0, BQ) * C * 2);
         offR = (uint32_t)(kc_row0 * C + kc_ch) * 2u;
     } else {
-        // W rows c (512 bytes each), load i of wave w covers rows (4w + i) * 2 + lane / 32;
-        // the slot swizzle depends on i only through i % 2
-        const int pch = lane & 31;
-        const int rowe = wave * 8 + (lane >> 5), rowo = rowe + 2;
-        chR0 = (((pch >> 1) ^ sw512(rowe)) * 2 + (pch & 1)) * 8;   // q offset inside the tile
-        chR1 = (((pch >> 1) ^ sw512(rowo)) * 2 + (pch & 1)) * 8;
-        offR = (uint32_t)(rowe * Q) * 2u;
+        // W rows c (512 bytes each); load i of wave w covers rows
+        // 2 (LPW w + i) + lane / 32.  The slot swizzle sw512 of those rows
+        // depends on i only through i % 2 (and i / 4 when LPW = 8).
+        const int pch = lane & 31, h = lane >> 5;
+        const int row0 = wave * 2 * LPW + h;
+#pragma unroll
+        for (int v = 0; v < (LPW == 8 ? 4 : 2); ++v) {
+            const int row = row0 + 2 * (v & 1) + 8 * (v >> 1);
+            chR[v] = (((pch >> 1) ^ sw512(row)) * 2 + (pch & 1)) * 8;   // q offset inside the tile
+        }
+        offR = (uint32_t)(row0 * Q) * 2u;
     }
     __amdgpu_buffer_rsrc_t rsF;
     uint32_t offF = kOOB;
@@ -199,85 +227,104 @@ __global__ __launch_bounds__(g2::NT) void lora_gemm(const GemmArgs a) {
     }
 
     // 4-bit weights: each thread fetches 16 bytes of codes (32 weights of one
-    // row, within one 64-block) and the block's absmax into registers when a
-    // stage is issued, and decodes them into the stage's bf16 R tile (same LDS
-    // layout as the 16-bit path) just before the barrier that publishes it.
-    u32x4 qreg = {0u, 0u, 0u, 0u};
-    float am_reg = 0.f;
+    // row, within one 64-block) and the block's absmax per unit into
+    // registers when a stage is issued, and decodes them into the stage's bf16
+    // R tile (same LDS layout as the 16-bit path) before the barrier that
+    // publishes it.  512 units per stage, 512 / NT per thread.
+    constexpr int QU = Q4 ? 512 / NT : 1;
+    u32x4 qreg[QU];
+    float am_reg[QU];
+#pragma unroll
+    for (int u = 0; u < QU; ++u) { qreg[u] = u32x4{0u, 0u, 0u, 0u}; am_reg[u] = 0.f; }
     if constexpr (Q4) {
         if (tid < 16) reinterpret_cast<float*>(smem + SM::LUT)[tid] = a.codebook[tid];
     }
     auto load_q = [&](int kt) {
         const int c0 = kt * BK;
-        if constexpr (!TRANS) {              // codes [Q][C/2]: row q = tid / 2, weights c0 + 32 (tid % 2) ..
-            const int q = tid >> 1, h = tid & 1;
-            const bool ok = q0 + q < Q;
-            qreg = ok ? *reinterpret_cast<const u32x4*>(a.Rq + (size_t)(q0 + q) * (C >> 1) + (c0 >> 1) + 16 * h)
-                      : u32x4{0u, 0u, 0u, 0u};
-            am_reg = ok ? f16_bits_to_f32(a.Rabs[(size_t)(q0 + q) * (C >> 6) + kt]) : 0.f;
-        } else {                             // codes [C][Q/2]: row c = tid / 8, weights q0 + 32 (tid % 8) ..
-            const int c = tid >> 3, pp = tid & 7;
-            const bool ok = c0 + c < C && q0 + 32 * pp < Q;
-            const size_t qq = (size_t)q0 + 32 * pp;
-            qreg = ok ? *reinterpret_cast<const u32x4*>(a.Rq + (size_t)(c0 + c) * (Q >> 1) + (qq >> 1))
-                      : u32x4{0u, 0u, 0u, 0u};
-            am_reg = ok ? f16_bits_to_f32(a.Rabs[(size_t)(c0 + c) * (Q >> 6) + (qq >> 6)]) : 0.f;
+#pragma unroll
+        for (int u = 0; u < QU; ++u) {
+            const int unit = tid + u * NT;
+            if constexpr (!TRANS) {          // codes [Q][C/2]: row q = unit / 2, weights c0 + 32 (unit % 2) ..
+                const int q = unit >> 1, hh = unit & 1;
+                const bool ok = q0 + q < Q;
+                qreg[u] = ok ? *reinterpret_cast<const u32x4*>(a.Rq + (size_t)(q0 + q) * (C >> 1) + (c0 >> 1) + 16 * hh)
+                             : u32x4{0u, 0u, 0u, 0u};
+                am_reg[u] = ok ? f16_bits_to_f32(a.Rabs[(size_t)(q0 + q) * (C >> 6) + kt]) : 0.f;
+            } else {                         // codes [C][Q/2]: row c = unit / 8, weights q0 + 32 (unit % 8) ..
+                const int c = unit >> 3, pp = unit & 7;
+                const bool ok = c0 + c < C && q0 + 32 * pp < Q;
+                const size_t qq = (size_t)q0 + 32 * pp;
+                qreg[u] = ok ? *reinterpret_cast<const u32x4*>(a.Rq + (size_t)(c0 + c) * (Q >> 1) + (qq >> 1))
+                             : u32x4{0u, 0u, 0u, 0u};
+                am_reg[u] = ok ? f16_bits_to_f32(a.Rabs[(size_t)(c0 + c) * (Q >> 6) + (qq >> 6)]) : 0.f;
+            }
         }
     };
     auto decode_q = [&](int kt) {
         uint8_t* const Rs = smem + (kt & 1) * SM::STAGE + TILE;
         const float* const lut = reinterpret_cast<const float*>(smem + SM::LUT);
-        u32x4 outv[4];
 #pragma unroll
-        for (int b = 0; b < 16; ++b) {       // byte b holds weights 2b (low nibble) and 2b + 1
-            const uint32_t byte = (qreg[b >> 2] >> (8 * (b & 3))) & 0xFFu;
-            const float lo = lut[byte & 15u] * am_reg, hi = lut[byte >> 4] * am_reg;
-            outv[b >> 2][b & 3] = pack_bf16x2(lo, hi);
-        }
-        if constexpr (!TRANS) {              // row q, 16-byte chunks 4h .. 4h + 3, chunk ch at ch ^ (q & 7)
-            const int q = tid >> 1, h = tid & 1;
+        for (int u = 0; u < QU; ++u) {
+            const int unit = tid + u * NT;
+            u32x4 outv[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                *reinterpret_cast<u32x4*>(Rs + q * 128 + (((4 * h + i) ^ (q & 7)) << 4)) = outv[i];
-        } else {                             // row c, 32-byte slots 2 pp, 2 pp + 1 (swizzled by sw512)
-            const int c = tid >> 3, pp = tid & 7;
+            for (int b = 0; b < 16; ++b) {   // byte b holds weights 2b (low nibble) and 2b + 1
+                const uint32_t byte = (qreg[u][b >> 2] >> (8 * (b & 3))) & 0xFFu;
+                const float lo = lut[byte & 15u] * am_reg[u], hi = lut[byte >> 4] * am_reg[u];
+                outv[b >> 2][b & 3] = pack_bf16x2(lo, hi);
+            }
+            if constexpr (!TRANS) {          // row q, 16-byte chunks 4h .. 4h + 3, chunk ch at ch ^ (q & 7)
+                const int q = unit >> 1, hh = unit & 1;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int slot = 2 * pp + (i >> 1);
-                *reinterpret_cast<u32x4*>(Rs + c * 512 + ((slot ^ sw512(c)) << 5) + (i & 1) * 16) = outv[i];
+                for (int i = 0; i < 4; ++i)
+                    *reinterpret_cast<u32x4*>(Rs + q * 128 + (((4 * hh + i) ^ (q & 7)) << 4)) = outv[i];
+            } else {                         // row c, 32-byte slots 2 pp, 2 pp + 1 (swizzled by sw512)
+                const int c = unit >> 3, pp = unit & 7;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int slot = 2 * pp + (i >> 1);
+                    *reinterpret_cast<u32x4*>(Rs + c * 512 + ((slot ^ sw512(c)) << 5) + (i & 1) * 16) = outv[i];
+                }
             }
         }
     };
 
-    auto issue_stage = [&](int kt) {
+    // L and R of stage kt (R from the codes when Q4).  With on = false every
+    // offset is out of range: the instructions still issue (keeping the loop
+    // free of branches) and write zeros into the slot of stage kt, which no
+    // later read uses.
+    auto issue_lr = [&](int kt, bool on) {
         const int c0 = kt * BK;
         uint8_t* const Ls = smem + (kt & 1) * SM::STAGE;
         uint8_t* const Rs = Ls + TILE;
-        uint8_t* const Fs = Rs + TILE;
-        const bool lok = c0 + kc_ch < C;
+        const bool lok = on && c0 + kc_ch < C;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            g2lds16(rsL, Ls + (wave * 4 + i) * 1024, lok ? offL + (uint32_t)(i * 8 * C + c0) * 2u : kOOB);
+        for (int i = 0; i < LPW; ++i)
+            g2lds16<TRANS>(rsL, Ls + (wave * LPW + i) * 1024, lok ? offL + (uint32_t)(i * 8 * C + c0) * 2u : kOOB);
         if constexpr (Q4) {
             load_q(kt);
         } else if constexpr (!TRANS) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                g2lds16(rsR, Rs + (wave * 4 + i) * 1024, lok ? offR + (uint32_t)(i * 8 * C + c0) * 2u : kOOB);
+            for (int i = 0; i < LPW; ++i)
+                g2lds16<TRANS>(rsR, Rs + (wave * LPW + i) * 1024, lok ? offR + (uint32_t)(i * 8 * C + c0) * 2u : kOOB);
         } else {
-            const int rows_left = min(C - c0, BK);
+            const int rows_left = max(1, min(C - c0, BK));
             const __amdgpu_buffer_rsrc_t rs =
                 make_rsrc(a.R + (size_t)c0 * Q + q0, (uint64_t)(rows_left - 1) * Q * 2 + (uint64_t)(Q - q0) * 2);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int ch = (i & 1) ? chR1 : chR0;
-                g2lds16(rs, Rs + (wave * 4 + i) * 1024,
-                        (q0 + ch < Q) ? offR + (uint32_t)(2 * i * Q + ch) * 2u : kOOB);
+            for (int i = 0; i < LPW; ++i) {
+                const int ch = chR[(i & 1) | (LPW == 8 ? ((i >> 2) & 1) << 1 : 0)];
+                g2lds16<TRANS>(rs, Rs + (wave * LPW + i) * 1024,
+                        (on && q0 + ch < Q) ? offR + (uint32_t)(2 * i * Q + ch) * 2u : kOOB);
             }
         }
+    };
+    auto issue_f = [&](int kt) {
         if constexpr (!ZIN) {
+            const int c0 = kt * BK;
+            uint8_t* const Fs = smem + (kt & 1) * SM::STAGE + 2 * TILE;
             if (wave < F_LOADS)
-                g2lds16(rsF, Fs + wave * 1024, (frow < r && c0 + fch < C) ? offF + (uint32_t)c0 * 2u : kOOB);
+                g2lds16<TRANS>(rsF, Fs + wave * 1024, (frow < r && c0 + fch < C) ? offF + (uint32_t)c0 * 2u : kOOB);
         }
     };
 
@@ -289,55 +336,103 @@ __global__ __launch_bounds__(g2::NT) void lora_gemm(const GemmArgs a) {
     auto read_r = [&](const uint8_t* Ls, int kk, int i) -> bf16x8 {
         const uint8_t* const Rs = Ls + TILE;
         if constexpr (!TRANS) {
-            return lds_b128(Rs + (wq * 4 + i) * 2048 + chunk_of(kk));
+            return lds_b128(Rs + (wq * QB + i) * 2048 + chunk_of(kk));
         } else {
             const int rlo = kk * 32 + g4 * 8 + (l16 >> 2);            // rhi = rlo + 4: same swizzle
-            const uint8_t* const p = Rs + rlo * 512 + (l16 & 3) * 8 + (((wq * 4 + i) ^ sw512(rlo)) << 5);
+            const uint8_t* const p = Rs + rlo * 512 + (l16 & 3) * 8 + (((wq * QB + i) ^ sw512(rlo)) << 5);
             return cat_tr(lds_tr4(p), lds_tr4(p + 4 * 512));
         }
     };
     auto read_l = [&](const uint8_t* Ls, int kk, int i) -> bf16x8 {
-        return lds_b128(Ls + wp * 16384 + ((i + 2 * wq) & 7) * 2048 + chunk_of(kk));
+        return lds_b128(Ls + wp * 16384 + ((i + ZB * wq) & 7) * 2048 + chunk_of(kk));
     };
     auto read_f = [&](const uint8_t* Ls, int kk, int jt) -> bf16x8 {
         return lds_b128(Ls + 2 * TILE + jt * 2048 + chunk_of(kk));
     };
 
-    f32x4 acc[4][8];
+    f32x4 acc[QB][8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < QB; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    f32x4 zacc[JT][2];
+    f32x4 zacc[JT][ZB];
 #pragma unroll
-    for (int i = 0; i < JT; ++i) zacc[i][0] = zacc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < JT; ++i)
+#pragma unroll
+        for (int z = 0; z < ZB; ++z) zacc[i][z] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // One 32-wide step: the MFMAs of `cur`, then the LDS reads of the next
-    // step's fragments.  The two waves of a SIMD and the hardware's in-order
-    // issue keep the MFMA pipe fed while the reads are in flight; the next
-    // step's first MFMAs wait only for the fragments they use.
-    auto step = [&](const Frags<JT>& cur, Frags<JT>& nxt, const uint8_t* nstage, int nkk, auto do_read) {
+    // One 32-wide step: `pre` (the next stage's DMA, or nothing), the LDS
+    // reads of the next step's fragments, and the MFMAs of `cur`.  The
+    // scheduling groups at the end place one DMA after each of the first MFMAs
+    // and then one fragment read after every RA MFMAs, so that neither the
+    // LDS queue nor the MFMA pipe runs dry and the last read is issued well
+    // before the next step needs it.
+    constexpr int NR_STEP = (TRANS ? 2 * QB : QB) + 8 + (ZIN ? 0 : JT);
+    constexpr int NM_STEP = 8 * QB + (ZIN ? 0 : ZB * JT);
+    auto step = [&](const Frags<JT, QB>& cur, Frags<JT, QB>& nxt, const uint8_t* nstage, int nkk, auto do_read,
+                    auto pre) {
         constexpr bool RD = decltype(do_read)::value;
+        auto reads = [&] {
+            if constexpr (RD) {
 #pragma unroll
-        for (int pi = 0; pi < 8; ++pi)
+                for (int i = 0; i < QB; ++i) nxt.r[i] = read_r(nstage, nkk, i);
 #pragma unroll
-            for (int qi = 0; qi < 4; ++qi) acc[qi][pi] = mfma16(cur.r[qi], cur.l[pi], acc[qi][pi]);
-        if constexpr (!ZIN) {
+                for (int i = 0; i < 8; ++i) nxt.l[i] = read_l(nstage, nkk, i);
+                if constexpr (!ZIN) {
 #pragma unroll
-            for (int jt = 0; jt < JT; ++jt)
+                    for (int jt = 0; jt < JT; ++jt) nxt.f[jt] = read_f(nstage, nkk, jt);
+                }
+            }
+        };
+        auto mfmas = [&] {
 #pragma unroll
-                for (int z = 0; z < 2; ++z) zacc[jt][z] = mfma16(cur.f[jt], cur.l[z], zacc[jt][z]);
-        }
-        if constexpr (RD) {
+            for (int pi = 0; pi < 8; ++pi)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) nxt.r[i] = read_r(nstage, nkk, i);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) nxt.l[i] = read_l(nstage, nkk, i);
+                for (int qi = 0; qi < QB; ++qi) acc[qi][pi] = mfma16(cur.r[qi], cur.l[pi], acc[qi][pi]);
             if constexpr (!ZIN) {
 #pragma unroll
-                for (int jt = 0; jt < JT; ++jt) nxt.f[jt] = read_f(nstage, nkk, jt);
+                for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+                    for (int z = 0; z < ZB; ++z) zacc[jt][z] = mfma16(cur.f[jt], cur.l[z], zacc[jt][z]);
             }
+        };
+        pre();
+        if constexpr (Q4) {
+            // the code registers leave no room for both fragment sets during
+            // the MFMAs: the reads follow them and the hardware's in-order
+            // issue with the second wave of the SIMD covers their latency
+            mfmas();
+            reads();
+            return;
         }
+        reads();
+        mfmas();
+        constexpr int NV = std::decay_t<decltype(pre)>::count();
+        constexpr int NR = RD ? NR_STEP : 0;
+        constexpr int RA_FIT = (NM_STEP - NV) / (NR == 0 ? 1 : NR);
+        constexpr int RA = RA_FIT > 2 ? RA_FIT : 2;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);    // VMEM read (global -> LDS)
+        }
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // DS read
+            __builtin_amdgcn_sched_group_barrier(0x008, RA - 1, 0);
+        }
+    };
+    struct NoPre {
+        static constexpr int count() { return 0; }
+        __device__ void operator()() const {}
+    };
+    struct StagePre {
+        static constexpr int count() { return 2 * LPW; }
+        decltype(issue_lr)* f;
+        int kt;
+        bool on;
+        __device__ void operator()() const { (*f)(kt, on); }
     };
     using Read = std::true_type;
     using NoRead = std::false_type;
@@ -346,24 +441,27 @@ __global__ __launch_bounds__(g2::NT) void lora_gemm(const GemmArgs a) {
     const int nk = (C + BK - 1) / BK;
     if constexpr (Q4) {
         lds_barrier();                       // codebook in LDS
-        issue_stage(0);
+        issue_lr(0, true);
+        issue_f(0);
         decode_q(0);
-        if (nk > 1) issue_stage(1);
+        if (nk > 1) { issue_lr(1, true); issue_f(1); }
         vmcnt_le<0>();
     } else {
-        issue_stage(0);
+        issue_lr(0, true);
+        issue_f(0);
         if (nk > 1) {
-            issue_stage(1);
-            if (wave < F_LOADS) vmcnt_le<9>(); else vmcnt_le<8>();   // stage 0 landed, stage 1 in flight
+            issue_lr(1, true);
+            issue_f(1);
+            if (wave < F_LOADS) vmcnt_le<2 * LPW + 1>(); else vmcnt_le<2 * LPW>();   // stage 0 landed
         } else {
             vmcnt_le<0>();
         }
     }
     lds_barrier();
 
-    Frags<JT> fa, fb;
+    Frags<JT, QB> fa, fb;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fa.r[i] = read_r(smem, 0, i);
+    for (int i = 0; i < QB; ++i) fa.r[i] = read_r(smem, 0, i);
 #pragma unroll
     for (int i = 0; i < 8; ++i) fa.l[i] = read_l(smem, 0, i);
     if constexpr (!ZIN) {
@@ -372,23 +470,31 @@ __global__ __launch_bounds__(g2::NT) void lora_gemm(const GemmArgs a) {
     }
     for (int kt = 0; kt + 1 < nk; ++kt) {
         const uint8_t* const cur = smem + (kt & 1) * SM::STAGE;
-        step(fa, fb, cur, 1, Read{});
+        const uint8_t* const nxt = smem + ((kt + 1) & 1) * SM::STAGE;
+        step(fa, fb, cur, 1, Read{}, NoPre{});
         if constexpr (Q4) decode_q(kt + 1);  // R tile of stage kt + 1 from the registers loaded at its issue
         vmcnt_le<0>();           // this wave's loads of stage kt + 1 have landed
         lds_barrier();           // ... and everyone's; stage kt's slot is free
-        if (kt + 2 < nk) issue_stage(kt + 2);
-        step(fb, fa, smem + ((kt + 1) & 1) * SM::STAGE, 0, Read{});
+        if constexpr (Q4) {
+            if (kt + 2 < nk) { issue_lr(kt + 2, true); issue_f(kt + 2); }
+            step(fb, fa, nxt, 0, Read{}, NoPre{});
+        } else {
+            if (kt + 2 < nk) issue_f(kt + 2);
+            step(fb, fa, nxt, 0, Read{}, StagePre{&issue_lr, kt + 2, kt + 2 < nk});
+        }
     }
-    step(fa, fb, smem + ((nk - 1) & 1) * SM::STAGE, 1, Read{});
-    step(fb, fa, smem, 0, NoRead{});
+    step(fa, fb, smem + ((nk - 1) & 1) * SM::STAGE, 1, Read{}, NoPre{});
+    step(fb, fa, smem, 0, NoRead{}, NoPre{});
+    vmcnt_le<0>();               // the last iteration's placeholder loads have written their zeros
+
     // ------------------------------------------------------------ epilogue
     // The E fragments (and Z itself when it comes precomputed) of the first 16
     // rank columns are requested before the LDS exchange so that their global
     // latency overlaps it.
-    auto load_e = [&](int jt, bf16x8 (&ef)[4]) {
+    auto load_e = [&](int jt, bf16x8 (&ef)[QB]) {
 #pragma unroll
-        for (int qi = 0; qi < 4; ++qi) {
-            const int q = q0 + wq * 64 + qi * 16 + l16;
+        for (int qi = 0; qi < QB; ++qi) {
+            const int q = q0 + wq * QB * 16 + qi * 16 + l16;
             uint32_t e4[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -404,7 +510,7 @@ __global__ __launch_bounds__(g2::NT) void lora_gemm(const GemmArgs a) {
     auto load_zin = [&](int jt, f32x4 (&zv)[8]) {
 #pragma unroll
         for (int pi = 0; pi < 8; ++pi) {
-            const int p = p0 + wp * 128 + ((pi + 2 * wq) & 7) * 16 + l16;
+            const int p = p0 + wp * 128 + ((pi + ZB * wq) & 7) * 16 + l16;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int j = jt * 16 + 4 * g4 + i;
@@ -412,7 +518,7 @@ __global__ __launch_bounds__(g2::NT) void lora_gemm(const GemmArgs a) {
             }
         }
     };
-    bf16x8 ef0[4];
+    bf16x8 ef0[QB];
     load_e(0, ef0);
     f32x4 zin0[ZIN ? 8 : 1];
     if constexpr (ZIN) load_zin(0, zin0);
@@ -423,8 +529,8 @@ __global__ __launch_bounds__(g2::NT) void lora_gemm(const GemmArgs a) {
 #pragma unroll
         for (int jt = 0; jt < JT; ++jt)
 #pragma unroll
-            for (int z = 0; z < 2; ++z) {
-                const int pl = wp * 128 + (wq * 2 + z) * 16 + l16;
+            for (int z = 0; z < ZB; ++z) {
+                const int pl = wp * 128 + (wq * ZB + z) * 16 + l16;
                 *reinterpret_cast<f32x4*>(Zx + pl * RPAD + jt * 16 + 4 * g4) = zacc[jt][z];
             }
         lds_barrier();
@@ -439,11 +545,11 @@ __global__ __launch_bounds__(g2::NT) void lora_gemm(const GemmArgs a) {
     const float s = a.s;
 #pragma unroll 1
     for (int jt = 0; jt < RPAD / 16; ++jt) {
-        bf16x8 ef[4];
+        bf16x8 ef[QB];
         f32x4 zv[ZIN ? 8 : 1];
         if (jt == 0) {
 #pragma unroll
-            for (int qi = 0; qi < 4; ++qi) ef[qi] = ef0[qi];
+            for (int qi = 0; qi < QB; ++qi) ef[qi] = ef0[qi];
             if constexpr (ZIN) {
 #pragma unroll
                 for (int pi = 0; pi < 8; ++pi) zv[pi] = zin0[pi];
@@ -454,7 +560,7 @@ __global__ __launch_bounds__(g2::NT) void lora_gemm(const GemmArgs a) {
         }
 #pragma unroll
         for (int pi = 0; pi < 8; ++pi) {
-            const int pl = wp * 128 + ((pi + 2 * wq) & 7) * 16 + l16;
+            const int pl = wp * 128 + ((pi + ZB * wq) & 7) * 16 + l16;
             f32x4 z;
             if constexpr (ZIN) z = zv[pi];
             else z = *reinterpret_cast<const f32x4*>(Zx + pl * RPAD + jt * 16 + 4 * g4);
@@ -469,7 +575,7 @@ __global__ __launch_bounds__(g2::NT) void lora_gemm(const GemmArgs a) {
             const bf16x8 zf = as_bf16x8(u32x4{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16),
                                               lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)});
 #pragma unroll
-            for (int qi = 0; qi < 4; ++qi) acc[qi][pi] = mfma16(ef[qi], zf, acc[qi][pi]);
+            for (int qi = 0; qi < QB; ++qi) acc[qi][pi] = mfma16(ef[qi], zf, acc[qi][pi]);
         }
     }
 
@@ -480,11 +586,11 @@ __global__ __launch_bounds__(g2::NT) void lora_gemm(const GemmArgs a) {
     static_assert(BP * BQ * 2 <= SM::TOTAL, "output tile must fit in LDS");
     lds_barrier();                       // Zx reads are done
 #pragma unroll
-    for (int qi = 0; qi < 4; ++qi) {
-        const int ql = wq * 64 + qi * 16 + 4 * g4;
+    for (int qi = 0; qi < QB; ++qi) {
+        const int ql = wq * QB * 16 + qi * 16 + 4 * g4;
 #pragma unroll
         for (int pi = 0; pi < 8; ++pi) {
-            const int pl = wp * 128 + ((pi + 2 * wq) & 7) * 16 + l16;
+            const int pl = wp * 128 + ((pi + ZB * wq) & 7) * 16 + l16;
             const f32x4 v = acc[qi][pi];
             const u32x2 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
             *reinterpret_cast<u32x2*>(smem + pl * 512 + (((ql >> 3) ^ (pl & 31)) << 4) + (ql & 7) * 2) = o;
@@ -493,8 +599,8 @@ __global__ __launch_bounds__(g2::NT) void lora_gemm(const GemmArgs a) {
     lds_barrier();
     const int sc = tid & 31;             // 16-byte chunk of the row
 #pragma unroll 4
-    for (int pass = 0; pass < BP / 16; ++pass) {
-        const int pl = pass * 16 + (tid >> 5);
+    for (int pass = 0; pass < BP / (NT / 32); ++pass) {
+        const int pl = pass * (NT / 32) + (tid >> 5);
         const int p = p0 + pl, q = q0 + sc * 8;
         const u32x4 v = *reinterpret_cast<const u32x4*>(smem + pl * 512 + ((sc ^ (pl & 31)) << 4));
         if (p < P && q < Q) *reinterpret_cast<u32x4*>(a.Out + (size_t)p * Q + q) = v;

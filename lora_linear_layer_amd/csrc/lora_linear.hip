@@ -171,7 +171,7 @@ lora_status launched(const char* what) {
 template <bool TRANS, int RPAD, bool ZIN, bool Q4>
 void launch_gemm_t(const GemmArgs& a, hipStream_t st) {
     const int tiles = (int)(cdiv(a.P, g2::BP) * cdiv(a.Q, g2::BQ));
-    hipLaunchKernelGGL((lora_gemm<TRANS, RPAD, ZIN, Q4>), dim3(tiles), dim3(g2::NT), 0, st, a);
+    hipLaunchKernelGGL((lora_gemm<TRANS, RPAD, ZIN, Q4>), dim3(tiles), dim3(g2w::NT), 0, st, a);
 }
 
 // In-tile rank-r product: the forward forms U = X A^T inside the GEMM for

@@ -88,7 +88,7 @@ __global__ __launch_bounds__(256) void rank_stream(const RankArgs a) {
         for (int i = 0; i < 8; ++i) {
             const int row = ld_row0 + 4 * i;
             const int ch = ((lane & 15) ^ (row & 7)) * 8;
-            g2lds16(rs, Ys + (wave * 8 + i) * 1024, (c0 + ch < C) ? (uint32_t)(row * C + ch) * 2u : kOOB);
+            g2lds16<true>(rs, Ys + (wave * 8 + i) * 1024, (c0 + ch < C) ? (uint32_t)(row * C + ch) * 2u : kOOB);
         }
     };
     // side tiles (small, through VGPRs): F^T [RPAD][128 c] in Z mode, Z2^T hi / lo [RPAD][128 m] in G mode
