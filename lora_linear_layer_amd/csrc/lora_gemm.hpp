@@ -36,11 +36,11 @@
 //   R in the input gradient: W rows c (512 B = 256 q), 32-byte slot s of row
 //     c at slot s ^ sw512(c); fragments are gathered with ds_read_b64_tr_b16,
 //     which hands each lane 4 values down a column.
-// Forward, r <= 16: the rank-r product Z^T = F L^T reuses the L fragments
-// already in registers; the 4 waves that share a p half each form Z for 32 of
-// its 128 rows.  (The input gradient takes V = dY B precomputed: forming it in
-// the tile too needs transposing reads of B and exceeds the register budget.)  In the
-// epilogue Z meets in LDS and s Z E^T is applied with MFMA, s Z split into
+// r <= 16: the rank-r product Z^T = F L^T reuses the L fragments already in
+// registers; the 4 waves that share a p half each form Z for 32 of its 128
+// rows.  The forward's F = A rows go to LDS like L; the input gradient's
+// F = B^T is staged through registers (B is [C][r]) into the same layout.  In
+// the epilogue Z meets in LDS and s Z E^T is applied with MFMA, s Z split into
 // bf16 hi + lo halves that fill the two halves of the 32-long contraction.
 // ZIN = true takes a precomputed Z [P][r] float32 instead (large r).
 //
@@ -169,7 +169,7 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
     using namespace g2;
     using namespace g2w;
     using SM = GemmSmem<RPAD, ZIN, Q4>;
-    static_assert(ZIN || !TRANS, "the input gradient takes V precomputed");
+    static_assert(ZIN || !(TRANS && Q4), "4-bit input gradient takes V precomputed");
     constexpr int JT = ZIN ? 1 : RPAD / 16;
     constexpr int F_LOADS = SM::F_BYTES / 1024;   // done by waves 0 .. F_LOADS - 1
     static_assert(F_LOADS <= 8, "F tile larger than one load per wave");
@@ -319,12 +319,34 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
             }
         }
     };
+    // F of the rank-r product.  Forward: A [r][C] rows are contiguous in c and
+    // go straight to LDS.  Input gradient: B [C][r] is contiguous in j, so each
+    // thread loads (c, j) and (c, j + 1) into registers when the stage is
+    // issued (c = tid / 8, j = 2 (tid % 8); out-of-range offsets read zero) and
+    // write_f stores them into the same [j][c] layout just before the barrier
+    // that publishes the stage.  The two halves stay in separate registers so
+    // that nothing waits for them before write_f.
+    uint32_t f_lo = 0u, f_hi = 0u;
     auto issue_f = [&](int kt) {
-        if constexpr (!ZIN) {
+        if constexpr (!ZIN && !TRANS) {
             const int c0 = kt * BK;
             uint8_t* const Fs = smem + (kt & 1) * SM::STAGE + 2 * TILE;
             if (wave < F_LOADS)
                 g2lds16<TRANS>(rsF, Fs + wave * 1024, (frow < r && c0 + fch < C) ? offF + (uint32_t)c0 * 2u : kOOB);
+        } else if constexpr (!ZIN) {
+            const int cc = kt * BK + (tid >> 3), j = (tid & 7) * 2;
+            const uint32_t o = (uint32_t)(cc * r + j) * 2u;
+            f_lo = __builtin_amdgcn_raw_buffer_load_b16(rsF, (cc < C && j < r) ? o : kOOB, 0, 0);
+            f_hi = __builtin_amdgcn_raw_buffer_load_b16(rsF, (cc < C && j + 1 < r) ? o + 2u : kOOB, 0, 0);
+        }
+    };
+    auto write_f = [&](int kt) {
+        if constexpr (!ZIN && TRANS) {
+            uint8_t* const Fs = smem + (kt & 1) * SM::STAGE + 2 * TILE;
+            const int c = tid >> 3, j = (tid & 7) * 2;
+            *reinterpret_cast<uint16_t*>(Fs + j * 128 + (((c >> 3) ^ (j & 7)) << 4) + (c & 7) * 2) = (uint16_t)f_lo;
+            *reinterpret_cast<uint16_t*>(Fs + (j + 1) * 128 + (((c >> 3) ^ ((j + 1) & 7)) << 4) + (c & 7) * 2) =
+                (uint16_t)f_hi;
         }
     };
 
@@ -449,10 +471,16 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
     } else {
         issue_lr(0, true);
         issue_f(0);
+        write_f(0);
         if (nk > 1) {
             issue_lr(1, true);
             issue_f(1);
-            if (wave < F_LOADS) vmcnt_le<2 * LPW + 1>(); else vmcnt_le<2 * LPW>();   // stage 0 landed
+            // stage 0 landed: newer than it are stage 1's L and R loads, plus its
+            // F (two register loads per thread in the input gradient's in-tile
+            // form, one load into LDS for waves 0 .. F_LOADS - 1 in the forward)
+            if constexpr (TRANS && !ZIN) vmcnt_le<2 * LPW + 2>();
+            else if (wave < F_LOADS) vmcnt_le<2 * LPW + 1>();
+            else vmcnt_le<2 * LPW>();
         } else {
             vmcnt_le<0>();
         }
@@ -473,6 +501,7 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
         const uint8_t* const nxt = smem + ((kt + 1) & 1) * SM::STAGE;
         step(fa, fb, cur, 1, Read{}, NoPre{});
         if constexpr (Q4) decode_q(kt + 1);  // R tile of stage kt + 1 from the registers loaded at its issue
+        write_f(kt + 1);                     // (input gradient) F of stage kt + 1 from its register
         vmcnt_le<0>();           // this wave's loads of stage kt + 1 have landed
         lds_barrier();           // ... and everyone's; stage kt's slot is free
         if constexpr (Q4) {

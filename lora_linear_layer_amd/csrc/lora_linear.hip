@@ -174,17 +174,17 @@ void launch_gemm_t(const GemmArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((lora_gemm<TRANS, RPAD, ZIN, Q4>), dim3(tiles), dim3(g2w::NT), 0, st, a);
 }
 
-// In-tile rank-r product: the forward forms U = X A^T inside the GEMM for
-// r <= 16.  The input gradient takes V = dY B from the stand-alone pass: its
-// in-tile form needs the transposing reads of B next to those of W, which
-// pushes the kernel past 256 VGPRs (measured: 197 us with V in-tile vs 174 us
-// for pass + GEMM + adapter gradients on the 4096 x 4096 r=8 layer).
-bool gemm_in_tile(bool trans, int r) { return r <= 16 && !trans; }
+// In-tile rank-r product for r <= 16: the forward forms U = X A^T and the
+// 16-bit input gradient forms V = dY B inside the GEMM (every q tile of a row
+// panel forms it; the first one saves it).  Larger ranks, and the 4-bit input
+// gradient (whose code registers leave no room), take Z from the stand-alone
+// streamed pass.
+bool gemm_in_tile(bool trans, bool quant, int r) { return r <= 16 && !(trans && quant); }
 
 template <bool TRANS, bool Q4>
 void launch_gemm(const GemmArgs& a, hipStream_t st) {
-    if constexpr (!TRANS) {
-        if (gemm_in_tile(TRANS, a.r)) { launch_gemm_t<TRANS, 16, false, Q4>(a, st); return; }
+    if constexpr (!(TRANS && Q4)) {
+        if (gemm_in_tile(TRANS, Q4, a.r)) { launch_gemm_t<TRANS, 16, false, Q4>(a, st); return; }
     }
     switch (rpad_of(a.r)) {
         case 16: launch_gemm_t<TRANS, 16, true, Q4>(a, st); break;
@@ -277,7 +277,7 @@ lora_status fwd_bf16(const lora_linear_desc& d, bool quant, const void* X, const
     const uint16_t* const X16 = static_cast<const uint16_t*>(X);
     const uint16_t* const A16 = static_cast<const uint16_t*>(A);
     float* const zpart = reinterpret_cast<float*>(wsb + plan.off_zp);
-    const bool in_tile = gemm_in_tile(false, r);
+    const bool in_tile = gemm_in_tile(false, quant, r);
     float* U = U_save;
     if (!in_tile) {
         // U = X A^T by the streamed pass, read by the GEMM epilogue
@@ -305,8 +305,9 @@ lora_status fwd_bf16(const lora_linear_desc& d, bool quant, const void* X, const
 }
 
 // ---------------------------------------------------------------- backward
-// Order on the stream: U (if not saved) -> V = dY B -> dX GEMM (V in the
-// epilogue) -> dA, dB partials (one pass over X and one over dY) -> final sum.
+// Order on the stream: U (if not saved) -> dX GEMM, which forms V = dY B in
+// the tile for r <= 16 (16-bit W) and saves it, or takes V from a streamed
+// pass -> dA, dB partials (one pass over X and one over dY) -> final sum.
 lora_status bwd_bf16(const lora_linear_desc& d, bool quant, const void* dY, const void* X, const void* W,
                      const uint8_t* Wq, const uint16_t* absmax, const float* codebook, const void* A,
                      const void* B, const float* U_saved, void* dX, void* dA, void* dB, void* ws, hipStream_t st) {
@@ -328,9 +329,13 @@ lora_status bwd_bf16(const lora_linear_desc& d, bool quant, const void* dY, cons
         LAUNCH_CHECK("rank_stream(U)");
         U = Uw;
     }
-    // 2. V = dY B
-    launch_rank_z(d, dY16, d.N, B16, true, V, zpart, st);
-    LAUNCH_CHECK("rank_stream(V)");
+    // 2. V = dY B: inside the dX GEMM when it runs in the in-tile form,
+    //    else the streamed pass
+    const bool v_in_tile = dX != nullptr && gemm_in_tile(true, quant, r);
+    if (!v_in_tile) {
+        launch_rank_z(d, dY16, d.N, B16, true, V, zpart, st);
+        LAUNCH_CHECK("rank_stream(V)");
+    }
     // 3. dX = dY W + s V A
     if (dX) {
         GemmArgs g{};
@@ -342,7 +347,8 @@ lora_status bwd_bf16(const lora_linear_desc& d, bool quant, const void* dY, cons
         g.F = B16;
         g.E = A16;
         g.Out = static_cast<uint16_t*>(dX);
-        g.Zin = V;
+        g.Zin = v_in_tile ? nullptr : V;
+        g.Zsave = v_in_tile ? V : nullptr;
         g.P = (int)d.M; g.Q = (int)d.K; g.C = (int)d.N; g.r = r;
         g.s = d.alpha / (float)d.r;
         if (quant) launch_gemm<true, true>(g, st);
