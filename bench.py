@@ -66,6 +66,14 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def fwd_bytes(l) -> int:
+    """HBM bytes a forward launch must move once: X and H in bf16, W in bf16
+    or as 4-bit codes plus one fp16 absmax per 64 weights, A, B and the saved
+    U (float32)."""
+    w = l.N * l.K // 2 + 2 * (l.N * l.K // 64) if l.quant4 else 2 * l.N * l.K
+    return 2 * l.M * l.K + w + 2 * l.M * l.N + 2 * l.r * (l.K + l.N) + 4 * l.M * l.r
+
+
 def fwd_flops(l):
     return 2 * l.M * l.N * l.K + 2 * l.M * l.r * (l.K + l.N)
 
@@ -292,7 +300,7 @@ def main():
                 "frac": round(ach / PEAK_BF16_TFLOPS, 4),
                 "traffic": tr["hbm_bytes_per_dispatch"] if tr else None,
                 "avg_launch_us": round(fwd_ms * 1e3, 2), "flops_per_launch": fwd_flops(lb),
-                "algorithmic_bytes_per_launch": 2 * (lb.M * lb.K + lb.N * lb.K + lb.M * lb.N)}
+                "algorithmic_bytes_per_launch": fwd_bytes(lb)}
 
     out = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,

@@ -60,8 +60,8 @@ typedef enum lora_dtype {
  *   M tokens, K = d_in, N = d_out, r = rank, alpha = lora_alpha (s = alpha/r).
  *   dtype applies to X, W, A, B, H, dY, dX, dA, dB.  U is always float32.
  * Supported range: 1 <= r <= 128; M, K, N >= 1; K % 8 == 0 and N % 8 == 0;
- * every matrix has fewer than 2^31 elements; the 4-bit entry points also need
- * K % 64 == 0.  Outside it: LORA_ERR_UNSUPPORTED.
+ * K, N <= 2^21; every matrix has fewer than 2^31 elements; the 4-bit entry
+ * points also need K % 64 == 0.  Outside it: LORA_ERR_UNSUPPORTED.
  */
 typedef struct lora_linear_desc {
     int64_t M, K, N, r;
