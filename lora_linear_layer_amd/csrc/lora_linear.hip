@@ -75,7 +75,8 @@ RankSplit split_g(const lora_linear_desc& d) { return rank_split(cdiv(d.K, kRT) 
 
 // Workspace layout for one descriptor (offsets in bytes from ws).
 struct Plan {
-    size_t off_v = 0, off_u = 0, off_zp = 0, off_ga = 0, off_gb = 0, total = 0;
+    size_t off_v = 0, off_u = 0, off_zp = 0, off_ga = 0, off_gb = 0, off_zt = 0, off_bt = 0, total = 0;
+    int64_t Mp = 0;         // tokens rounded up to a whole 128-token tile (side planes of the G pass)
     RankSplit g;
 };
 
@@ -94,6 +95,11 @@ Plan make_plan(const lora_linear_desc& d) {
         cur += align_up((size_t)p.g.n_chunk * d.K * d.r * sizeof(float));
         p.off_gb = cur;
         cur += align_up((size_t)p.g.n_chunk * d.N * d.r * sizeof(float));
+        p.Mp = cdiv(d.M, kRT) * kRT;
+        p.off_zt = cur;                                  // V^T hi, V^T lo, U^T hi, U^T lo: bf16 [r][Mp] each
+        cur += 4 * align_up((size_t)d.r * p.Mp * sizeof(uint16_t));
+        p.off_bt = cur;                                  // B^T: bf16 [r][N]
+        cur += align_up((size_t)d.r * d.N * sizeof(uint16_t));
     }
     p.total = cur;
     return p;
@@ -194,31 +200,28 @@ void launch_gemm(const GemmArgs& a, hipStream_t st) {
     }
 }
 
-// Z = Y F^T (Z [M][r] float32) streamed over Y [M][C]; f_trans: F = B [C][r],
-// else F = A [r][C].  Partials go to zpart and are summed into Z.
-void launch_rank_z(const lora_linear_desc& d, const uint16_t* Y, int64_t C, const uint16_t* F, bool f_trans, float* Z,
+// Z = Y F^T (Z [M][r] float32) streamed over Y [M][C]; F given as bf16 rows
+// [r][C] (A itself, or B^T from transpose_rank).  Partials go to zpart and
+// are summed into Z.
+void launch_rank_z(const lora_linear_desc& d, const uint16_t* Y, int64_t C, const uint16_t* F_rows, float* Z,
                    float* zpart, hipStream_t st) {
     const RankSplit sp = split_z(d, C);
     RankArgs a{};
-    a.prob[0] = RankProblem{Y, F, nullptr, sp.n_chunk > 1 ? zpart : Z, (int)C, (int)cdiv(d.M, kRT)};
+    a.prob[0] = RankProblem{Y, F_rows, nullptr, sp.n_chunk > 1 ? zpart : Z, (int)C, (int)C, (int)cdiv(d.M, kRT)};
     a.n_prob = 1;
     a.M = (int)d.M;
     a.r = (int)d.r;
     a.chunk_tiles = sp.chunk_tiles;
     a.n_chunk = sp.n_chunk;
     const dim3 grid((unsigned)a.prob[0].n_tiles, (unsigned)sp.n_chunk, 1);
-#define RZ(RP)                                                                                 \
-    if (f_trans) hipLaunchKernelGGL((rank_stream<RP, false, true>), grid, dim3(256), 0, st, a); \
-    else hipLaunchKernelGGL((rank_stream<RP, false, false>), grid, dim3(256), 0, st, a);
     for (int j0 = 0; j0 < d.r; j0 += 64) {        // ranks above 64: one launch per 64 columns
         a.j0 = j0;
         switch (rpad_of(std::min<int64_t>(d.r - j0, 64))) {
-            case 16: RZ(16) break;
-            case 32: RZ(32) break;
-            default: RZ(64) break;
+            case 16: hipLaunchKernelGGL((rank_stream<16, false>), grid, dim3(256), 0, st, a); break;
+            case 32: hipLaunchKernelGGL((rank_stream<32, false>), grid, dim3(256), 0, st, a); break;
+            default: hipLaunchKernelGGL((rank_stream<64, false>), grid, dim3(256), 0, st, a); break;
         }
     }
-#undef RZ
     if (sp.n_chunk > 1) {
         const int64_t n = d.M * d.r;
         hipLaunchKernelGGL(partial_sum, dim3((unsigned)cdiv(n, 1024)), dim3(256), 0, st, zpart, Z, n, sp.n_chunk);
@@ -233,8 +236,16 @@ lora_status launch_adapter_grads(const lora_linear_desc& d, const Plan& plan, ch
     RankArgs a{};
     float* const ga = reinterpret_cast<float*>(wsb + plan.off_ga);
     float* const gb = reinterpret_cast<float*>(wsb + plan.off_gb);
-    a.prob[0] = RankProblem{X, nullptr, V, ga, (int)d.K, (int)cdiv(d.K, kRT)};
-    a.prob[1] = RankProblem{dY, nullptr, U, gb, (int)d.N, (int)cdiv(d.N, kRT)};
+    const size_t plane = align_up((size_t)d.r * plan.Mp * sizeof(uint16_t));
+    uint16_t* const vt_hi = reinterpret_cast<uint16_t*>(wsb + plan.off_zt);
+    uint16_t* const vt_lo = reinterpret_cast<uint16_t*>(wsb + plan.off_zt + plane);
+    uint16_t* const ut_hi = reinterpret_cast<uint16_t*>(wsb + plan.off_zt + 2 * plane);
+    uint16_t* const ut_lo = reinterpret_cast<uint16_t*>(wsb + plan.off_zt + 3 * plane);
+    hipLaunchKernelGGL(zt_hilo, dim3((unsigned)cdiv(d.r * plan.Mp, 256), 2), dim3(256), 0, st, V, U, vt_hi, vt_lo,
+                       ut_hi, ut_lo, (int)d.M, (int)plan.Mp, (int)d.r);
+    LAUNCH_CHECK("zt_hilo");
+    a.prob[0] = RankProblem{X, vt_hi, vt_lo, ga, (int)d.K, (int)plan.Mp, (int)cdiv(d.K, kRT)};
+    a.prob[1] = RankProblem{dY, ut_hi, ut_lo, gb, (int)d.N, (int)plan.Mp, (int)cdiv(d.N, kRT)};
     a.n_prob = 2;
     a.M = (int)d.M;
     a.r = (int)d.r;
@@ -244,9 +255,9 @@ lora_status launch_adapter_grads(const lora_linear_desc& d, const Plan& plan, ch
     for (int j0 = 0; j0 < d.r; j0 += 64) {        // ranks above 64: one launch per 64 columns
         a.j0 = j0;
         switch (rpad_of(std::min<int64_t>(d.r - j0, 64))) {
-            case 16: hipLaunchKernelGGL((rank_stream<16, true, false>), grid, dim3(256), 0, st, a); break;
-            case 32: hipLaunchKernelGGL((rank_stream<32, true, false>), grid, dim3(256), 0, st, a); break;
-            default: hipLaunchKernelGGL((rank_stream<64, true, false>), grid, dim3(256), 0, st, a); break;
+            case 16: hipLaunchKernelGGL((rank_stream<16, true>), grid, dim3(256), 0, st, a); break;
+            case 32: hipLaunchKernelGGL((rank_stream<32, true>), grid, dim3(256), 0, st, a); break;
+            default: hipLaunchKernelGGL((rank_stream<64, true>), grid, dim3(256), 0, st, a); break;
         }
     }
     LAUNCH_CHECK("rank_stream(dA, dB)");
@@ -282,7 +293,7 @@ lora_status fwd_bf16(const lora_linear_desc& d, bool quant, const void* X, const
     if (!in_tile) {
         // U = X A^T by the streamed pass, read by the GEMM epilogue
         if (!U) U = reinterpret_cast<float*>(wsb + plan.off_u);
-        launch_rank_z(d, X16, d.K, A16, false, U, zpart, st);
+        launch_rank_z(d, X16, d.K, A16, U, zpart, st);
         LAUNCH_CHECK("rank_stream(U)");
     }
     GemmArgs g{};
@@ -325,7 +336,7 @@ lora_status bwd_bf16(const lora_linear_desc& d, bool quant, const void* dY, cons
     const float* U = U_saved;
     if (!U) {
         float* Uw = reinterpret_cast<float*>(wsb + plan.off_u);
-        launch_rank_z(d, X16, d.K, A16, false, Uw, zpart, st);
+        launch_rank_z(d, X16, d.K, A16, Uw, zpart, st);
         LAUNCH_CHECK("rank_stream(U)");
         U = Uw;
     }
@@ -333,7 +344,11 @@ lora_status bwd_bf16(const lora_linear_desc& d, bool quant, const void* dY, cons
     //    else the streamed pass
     const bool v_in_tile = dX != nullptr && gemm_in_tile(true, quant, r);
     if (!v_in_tile) {
-        launch_rank_z(d, dY16, d.N, B16, true, V, zpart, st);
+        uint16_t* const BT = reinterpret_cast<uint16_t*>(wsb + plan.off_bt);
+        hipLaunchKernelGGL(transpose_rank, dim3((unsigned)cdiv(d.r * d.N, 256)), dim3(256), 0, st, B16, BT,
+                           (int)d.N, (int)d.r);
+        LAUNCH_CHECK("transpose_rank");
+        launch_rank_z(d, dY16, d.N, BT, V, zpart, st);
         LAUNCH_CHECK("rank_stream(V)");
     }
     // 3. dX = dY W + s V A

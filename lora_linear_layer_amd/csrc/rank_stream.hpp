@@ -17,8 +17,12 @@
 // rows of 256 bytes, 16-byte chunk ch of row x at ch ^ (x & 7)), and writes a
 // float32 partial per chunk; partial_sum adds the chunks in a fixed order, so
 // results are bitwise reproducible.  MFMA 16x16x32 bf16 with float32
-// accumulation; in G mode Z2 enters as a bf16 hi + lo pair and Y^T fragments
-// are gathered with ds_read_b64_tr_b16.
+// accumulation; Y^T fragments (G mode) are gathered with ds_read_b64_tr_b16.
+//
+// The rank-side operand arrives the same way, as bf16 rows [r][len] read 128
+// columns at a time: F = A [r][C] or B^T in Z mode; in G mode the two planes
+// hi = bf16(Z2^T), lo = bf16(Z2^T - hi) of [r][Mp] (tokens padded with zeros
+// to a multiple of 128), which zt_hilo writes from Z2 [M][r] float32.
 #pragma once
 #include "lora_gemm.hpp"
 
@@ -28,10 +32,11 @@ constexpr int kRT = 128;      // tile edge (rows of Y x columns of Y)
 
 struct RankProblem {
     const uint16_t* Y;      // [M][C] bf16
-    const uint16_t* F;      // Z mode: F_TRANS ? [C][r] : [r][C] bf16
-    const float* Z2;        // G mode: [M][r] float32
+    const uint16_t* S;      // rank side, bf16 rows [r][s_len]: Z mode F, G mode the hi plane of Z2^T
+    const uint16_t* S_lo;   // G mode: the lo plane of Z2^T (same shape)
     float* part;            // Z mode: [n_chunk][M][r]; G mode: [n_chunk][C][r]
     int C;
+    int s_len;              // side row length: C (Z mode) or Mp (G mode)
     int n_tiles;            // 128-wide tiles of the output's long dimension
 };
 
@@ -55,7 +60,7 @@ struct RankSmem {
 
 // Z mode when G == false, G mode when G == true.  Handles rank columns
 // j0 .. j0 + min(r - j0, RPAD) - 1.
-template <int RPAD, bool G, bool F_TRANS>
+template <int RPAD, bool G>
 __global__ __launch_bounds__(256) void rank_stream(const RankArgs a) {
     using SM = RankSmem<RPAD>;
     constexpr int JT = RPAD / 16;
@@ -91,50 +96,24 @@ __global__ __launch_bounds__(256) void rank_stream(const RankArgs a) {
             g2lds16<true>(rs, Ys + (wave * 8 + i) * 1024, (c0 + ch < C) ? (uint32_t)(row * C + ch) * 2u : kOOB);
         }
     };
-    // side tiles (small, through VGPRs): F^T [RPAD][128 c] in Z mode, Z2^T hi / lo [RPAD][128 m] in G mode
-    auto side_off = [](int row, int col) -> int {      // byte offset in a [RPAD][128] bf16 tile
-        return row * 256 + ((((col >> 3) ^ (row & 7)) << 4)) + (col & 7) * 2;
-    };
-    constexpr int SIDE_E = RPAD * kRT / 256;          // elements per thread
-    uint32_t sreg[SIDE_E];
-    float zreg[G ? SIDE_E : 1];
-    auto load_side = [&](int t) {
+    // side tile(s) of contraction tile t: rows j0 .. j0 + RPAD - 1 of S (and S_lo),
+    // columns t * 128 .. + 127, same row layout as the Y tile; wave w issues
+    // loads b = RPAD/16 * w .. of each plane, each 4 rows: row = 4 b + lane / 16
+    constexpr int SLW = RPAD / 16;                    // side loads per wave per plane
+    const __amdgpu_buffer_rsrc_t rsS = make_rsrc(pr.S, (uint64_t)r * pr.s_len * 2);
+    __amdgpu_buffer_rsrc_t rsSl = rsS;
+    if constexpr (G) rsSl = make_rsrc(pr.S_lo, (uint64_t)r * pr.s_len * 2);
+    auto issue_side = [&](int t, uint8_t* Ss) {
+        const int col0 = t * kRT;
 #pragma unroll
-        for (int i = 0; i < SIDE_E; ++i) {
-            const int e = tid + 256 * i;
-            if constexpr (!G) {
-                const int c0 = t * kRT;
-                if constexpr (F_TRANS) {                 // B [C][r]: element (j, c) at c * r + j
-                    const int c = e / RPAD, j = e % RPAD;
-                    sreg[i] = (j < rl && c0 + c < C) ? pr.F[(size_t)(c0 + c) * r + j0 + j] : 0u;
-                } else {                                 // A [r][C]
-                    const int j = e / kRT, c = e % kRT;
-                    sreg[i] = (j < rl && c0 + c < C) ? pr.F[(size_t)(j0 + j) * C + c0 + c] : 0u;
-                }
-            } else {
-                const int m0 = t * kRT;
-                const int m = e / RPAD, j = e % RPAD;
-                zreg[i] = (j < rl && m0 + m < M) ? pr.Z2[(size_t)(m0 + m) * r + j0 + j] : 0.f;
-            }
-        }
-    };
-    auto store_side = [&](uint8_t* Ss) {
-#pragma unroll
-        for (int i = 0; i < SIDE_E; ++i) {
-            const int e = tid + 256 * i;
-            if constexpr (!G) {
-                int j, c;
-                if constexpr (F_TRANS) { c = e / RPAD; j = e % RPAD; }
-                else { j = e / kRT; c = e % kRT; }
-                *reinterpret_cast<uint16_t*>(Ss + side_off(j, c)) = (uint16_t)sreg[i];
-            } else {
-                const int m = e / RPAD, j = e % RPAD;
-                const float z = zreg[i];
-                const __bf16 h = (__bf16)z;
-                const __bf16 l = (__bf16)(z - (float)h);
-                *reinterpret_cast<__bf16*>(Ss + side_off(j, m)) = h;
-                *reinterpret_cast<__bf16*>(Ss + SM::SIDE + side_off(j, m)) = l;
-            }
+        for (int i = 0; i < SLW; ++i) {
+            const int b = wave * SLW + i;
+            const int row = 4 * b + (lane >> 4);
+            const int ch = ((lane & 15) ^ (row & 7)) * 8;
+            const uint32_t off = (row < rl && col0 + ch < pr.s_len)
+                                     ? (uint32_t)((size_t)(j0 + row) * pr.s_len + col0 + ch) * 2u : kOOB;
+            g2lds16<true>(rsS, Ss + b * 1024, off);
+            if constexpr (G) g2lds16<true>(rsSl, Ss + SM::SIDE + b * 1024, off);
         }
     };
 
@@ -145,8 +124,7 @@ __global__ __launch_bounds__(256) void rank_stream(const RankArgs a) {
     // prologue: tile t_begin in slot 0
     if (t_begin < t_end) {
         issue_y(t_begin, smem);
-        load_side(t_begin);
-        store_side(smem + SM::YT);
+        issue_side(t_begin, smem + SM::YT);
     }
     vmcnt_le<0>();
     __syncthreads();
@@ -156,7 +134,7 @@ __global__ __launch_bounds__(256) void rank_stream(const RankArgs a) {
         const bool more = t + 1 < t_end;
         if (more) {
             issue_y(t + 1, nxt);
-            load_side(t + 1);
+            issue_side(t + 1, nxt + SM::YT);
         }
         const uint8_t* const Ys = cur;
         const uint8_t* const Ss = cur + SM::YT;
@@ -197,7 +175,6 @@ __global__ __launch_bounds__(256) void rank_stream(const RankArgs a) {
                 }
             }
         }
-        if (more) store_side(nxt + SM::YT);
         vmcnt_le<0>();
         __syncthreads();
     }
@@ -217,6 +194,32 @@ __global__ __launch_bounds__(256) void rank_stream(const RankArgs a) {
                 if (j < rl) out[(size_t)o * r + j0 + j] = acc[jt][z][i];
             }
         }
+}
+
+// G-mode side planes: hi[j][m] = bf16(Z[m][j]), lo[j][m] = bf16(Z[m][j] - hi),
+// j < r, m < Mp (zero for m >= M); blockIdx.y selects one of two problems.
+__global__ __launch_bounds__(256) void zt_hilo(const float* __restrict__ z0, const float* __restrict__ z1,
+                                               uint16_t* __restrict__ hi0, uint16_t* __restrict__ lo0,
+                                               uint16_t* __restrict__ hi1, uint16_t* __restrict__ lo1, int M, int Mp,
+                                               int r) {
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= (int64_t)r * Mp) return;
+    const int j = (int)(e / Mp), m = (int)(e % Mp);
+    const float* z = blockIdx.y ? z1 : z0;
+    const float v = m < M ? z[(size_t)m * r + j] : 0.f;
+    const __bf16 h = (__bf16)v;
+    const __bf16 l = (__bf16)(v - (float)h);
+    (blockIdx.y ? hi1 : hi0)[e] = __builtin_bit_cast(uint16_t, h);
+    (blockIdx.y ? lo1 : lo0)[e] = __builtin_bit_cast(uint16_t, l);
+}
+
+// F^T rows for the Z-mode pass over dY: out[j][n] = B[n][j].
+__global__ __launch_bounds__(256) void transpose_rank(const uint16_t* __restrict__ B, uint16_t* __restrict__ out,
+                                                      int N, int r) {
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= (int64_t)r * N) return;
+    const int j = (int)(e / N), n = (int)(e % N);
+    out[e] = B[(size_t)n * r + j];
 }
 
 // out[e] = sum over k < n_parts of part[k * n + e], added in increasing k.
