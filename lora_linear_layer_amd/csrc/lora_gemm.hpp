@@ -127,7 +127,9 @@ struct GemmArgs {
     const float* Zin;       // precomputed Z [P][r] (ZIN), else unused
     uint16_t* Out;          // [P][Q] bf16
     float* Zsave;           // [P][r] float32 or nullptr (written by the q-tile-0 workgroups)
+    float* Part;            // split contraction: float32 partial tiles [split][P][Q]
     int P, Q, C, r;
+    int split, kc;          // split contraction: slices, 64-wide stages per slice
     float s;
 };
 
@@ -164,12 +166,18 @@ struct Frags {
     bf16x8 f[JT];     // F, rank rows
 };
 
-template <bool TRANS, int RPAD, bool ZIN, bool Q4 = false>
+// SPLIT = true (precomputed Z only): workgroup u covers tile u / split and the
+// contraction stages [kc (u % split), kc (u % split + 1)); it stores a float32
+// partial tile, slice 0 including the rank-r term, and split_finish adds the
+// slices in order and rounds to bf16.  For outputs with too few tiles to fill
+// the chip (e.g. d_out = 1024).
+template <bool TRANS, int RPAD, bool ZIN, bool Q4 = false, bool SPLIT = false>
 __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
     using namespace g2;
     using namespace g2w;
     using SM = GemmSmem<RPAD, ZIN, Q4>;
     static_assert(ZIN || !(TRANS && Q4), "4-bit input gradient takes V precomputed");
+    static_assert(!SPLIT || (ZIN && !Q4), "split contraction: 16-bit weights, precomputed Z");
     constexpr int JT = ZIN ? 1 : RPAD / 16;
     constexpr int F_LOADS = SM::F_BYTES / 1024;   // done by waves 0 .. F_LOADS - 1
     static_assert(F_LOADS <= 8, "F tile larger than one load per wave");
@@ -183,8 +191,15 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
 
     const int P = a.P, Q = a.Q, C = a.C, r = a.r;
     const int nPt = (P + BP - 1) / BP, nQt = (Q + BQ - 1) / BQ;
-    int pt, qt;
-    grouped_tile<4>(xcd_contiguous(blockIdx.x, nPt * nQt), nPt, nQt, pt, qt);
+    int pt, qt, kbase = 0, slice = 0;
+    if constexpr (SPLIT) {
+        const int u = xcd_contiguous(blockIdx.x, nPt * nQt * a.split);
+        slice = u % a.split;
+        kbase = slice * a.kc;
+        grouped_tile<4>(u / a.split, nPt, nQt, pt, qt);
+    } else {
+        grouped_tile<4>(xcd_contiguous(blockIdx.x, nPt * nQt), nPt, nQt, pt, qt);
+    }
     const int p0 = pt * BP, q0 = qt * BQ;
 
     // ------------------------------------------------------------ load plan
@@ -294,7 +309,7 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
     // free of branches) and write zeros into the slot of stage kt, which no
     // later read uses.
     auto issue_lr = [&](int kt, bool on) {
-        const int c0 = kt * BK;
+        const int c0 = (kbase + kt) * BK;
         uint8_t* const Ls = smem + (kt & 1) * SM::STAGE;
         uint8_t* const Rs = Ls + TILE;
         const bool lok = on && c0 + kc_ch < C;
@@ -460,7 +475,7 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
     using NoRead = std::false_type;
 
     // ------------------------------------------------------------ main loop
-    const int nk = (C + BK - 1) / BK;
+    const int nk = SPLIT ? min((C + BK - 1) / BK - kbase, a.kc) : (C + BK - 1) / BK;
     if constexpr (Q4) {
         lds_barrier();                       // codebook in LDS
         issue_lr(0, true);
@@ -572,8 +587,9 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
     }
 
     const float s = a.s;
+    const int n_jt = (SPLIT && slice != 0) ? 0 : RPAD / 16;   // the rank-r term goes into slice 0 only
 #pragma unroll 1
-    for (int jt = 0; jt < RPAD / 16; ++jt) {
+    for (int jt = 0; jt < n_jt; ++jt) {
         bf16x8 ef[QB];
         f32x4 zv[ZIN ? 8 : 1];
         if (jt == 0) {
@@ -608,6 +624,21 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
         }
     }
 
+    if constexpr (SPLIT) {
+        // float32 partial tile, straight from the accumulators: Part[slice][p][q .. q+3]
+        float* const out = a.Part + (size_t)slice * P * Q;
+#pragma unroll
+        for (int qi = 0; qi < QB; ++qi) {
+            const int q = q0 + wq * QB * 16 + qi * 16 + 4 * g4;
+#pragma unroll
+            for (int pi = 0; pi < 8; ++pi) {
+                const int p = p0 + wp * 128 + ((pi + ZB * wq) & 7) * 16 + l16;
+                if (p < P && q < Q) *reinterpret_cast<f32x4*>(out + (size_t)p * Q + q) = acc[qi][pi];
+            }
+        }
+        return;
+    }
+
     // store: the bf16 tile goes through LDS ([256 p][256 q], 16-byte chunk c of
     // row p at c ^ (p % 32)) so that global stores are whole 512-byte row
     // segments, 16 bytes per lane.  A lane holds Out[p][q .. q+3] of each
@@ -634,6 +665,16 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
         const u32x4 v = *reinterpret_cast<const u32x4*>(smem + pl * 512 + ((sc ^ (pl & 31)) << 4));
         if (p < P && q < Q) *reinterpret_cast<u32x4*>(a.Out + (size_t)p * Q + q) = v;
     }
+}
+
+// Out[e] = bf16(sum over slices k < n_slices of Part[k][e]), added in increasing k.
+__global__ __launch_bounds__(256) void split_finish(const float* __restrict__ part, uint16_t* __restrict__ out,
+                                                    int64_t n, int n_slices) {
+    const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;   // n % 4 == 0 (Q % 8 == 0)
+    if (e0 >= n) return;
+    f32x4 acc = *reinterpret_cast<const f32x4*>(part + e0);
+    for (int k = 1; k < n_slices; ++k) acc += *reinterpret_cast<const f32x4*>(part + (size_t)k * n + e0);
+    *reinterpret_cast<u32x2*>(out + e0) = u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
 }
 
 }  // namespace lora

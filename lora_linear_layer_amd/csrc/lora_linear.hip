@@ -51,6 +51,18 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 int rpad_of(int64_t r) { return r <= 16 ? 16 : r <= 32 ? 32 : r <= 64 ? 64 : 128; }
 
+// Contraction slices for a GEMM whose output has too few 256 x 256 tiles to
+// fill the 256 CUs (precomputed-Z form, 16-bit weights): about 256 workgroups,
+// at least two 64-wide stages per slice.  1 = no split.
+int gemm_split(int64_t P, int64_t Q, int64_t C) {
+    const int64_t tiles = cdiv(P, 256) * cdiv(Q, 256);
+    if (tiles >= 128) return 1;
+    const int64_t nk = cdiv(C, 64);
+    const int64_t want = std::min<int64_t>(cdiv(256, tiles), nk / 2);
+    if (want < 2) return 1;
+    return (int)cdiv(nk, cdiv(nk, want));
+}
+
 // Chunking of a streamed rank-r product (rank_stream): out_tiles 128-wide
 // output tiles, n_ct 128-deep contraction tiles split into n_chunk chunks
 // (one float32 partial per chunk).
@@ -75,7 +87,7 @@ RankSplit split_g(const lora_linear_desc& d) { return rank_split(cdiv(d.K, kRT) 
 
 // Workspace layout for one descriptor (offsets in bytes from ws).
 struct Plan {
-    size_t off_v = 0, off_u = 0, off_zp = 0, off_ga = 0, off_gb = 0, off_zt = 0, off_bt = 0, total = 0;
+    size_t off_v = 0, off_u = 0, off_zp = 0, off_ga = 0, off_gb = 0, off_zt = 0, off_bt = 0, off_split = 0, total = 0;
     int64_t Mp = 0;         // tokens rounded up to a whole 128-token tile (side planes of the G pass)
     RankSplit g;
 };
@@ -100,6 +112,12 @@ Plan make_plan(const lora_linear_desc& d) {
         cur += 4 * align_up((size_t)d.r * p.Mp * sizeof(uint16_t));
         p.off_bt = cur;                                  // B^T: bf16 [r][N]
         cur += align_up((size_t)d.r * d.N * sizeof(uint16_t));
+        p.off_split = cur;                               // float32 partial tiles of a split contraction
+        if (d.r > 16) {                                  // the split runs in the precomputed-Z form only
+            const int sf = gemm_split(d.M, d.N, d.K), sx = gemm_split(d.M, d.K, d.N);
+            const size_t n_split = std::max(sf > 1 ? (size_t)sf * d.M * d.N : 0, sx > 1 ? (size_t)sx * d.M * d.K : 0);
+            cur += align_up(n_split * sizeof(float));
+        }
     }
     p.total = cur;
     return p;
@@ -187,16 +205,35 @@ void launch_gemm_t(const GemmArgs& a, hipStream_t st) {
 // streamed pass.
 bool gemm_in_tile(bool trans, bool quant, int r) { return r <= 16 && !(trans && quant); }
 
+// Precomputed-Z form; outputs with too few tiles run as a split contraction
+// into a.Part (workspace) plus split_finish.
+template <bool TRANS, int RPAD, bool Q4>
+void launch_gemm_zin(GemmArgs a, hipStream_t st) {
+    if constexpr (!Q4) {
+        const int sp = gemm_split(a.P, a.Q, a.C);
+        if (sp > 1 && a.Part != nullptr) {
+            a.split = sp;
+            a.kc = (int)cdiv(cdiv(a.C, g2::BK), sp);     // every slice gets at least one stage
+            const int tiles = (int)(cdiv(a.P, g2::BP) * cdiv(a.Q, g2::BQ));
+            hipLaunchKernelGGL((lora_gemm<TRANS, RPAD, true, false, true>), dim3(tiles * sp), dim3(g2w::NT), 0, st, a);
+            const int64_t n = (int64_t)a.P * a.Q;
+            hipLaunchKernelGGL(split_finish, dim3((unsigned)cdiv(n, 1024)), dim3(256), 0, st, a.Part, a.Out, n, sp);
+            return;
+        }
+    }
+    launch_gemm_t<TRANS, RPAD, true, Q4>(a, st);
+}
+
 template <bool TRANS, bool Q4>
 void launch_gemm(const GemmArgs& a, hipStream_t st) {
     if constexpr (!(TRANS && Q4)) {
         if (gemm_in_tile(TRANS, Q4, a.r)) { launch_gemm_t<TRANS, 16, false, Q4>(a, st); return; }
     }
     switch (rpad_of(a.r)) {
-        case 16: launch_gemm_t<TRANS, 16, true, Q4>(a, st); break;
-        case 32: launch_gemm_t<TRANS, 32, true, Q4>(a, st); break;
-        case 64: launch_gemm_t<TRANS, 64, true, Q4>(a, st); break;
-        default: launch_gemm_t<TRANS, 128, true, Q4>(a, st); break;
+        case 16: launch_gemm_zin<TRANS, 16, Q4>(a, st); break;
+        case 32: launch_gemm_zin<TRANS, 32, Q4>(a, st); break;
+        case 64: launch_gemm_zin<TRANS, 64, Q4>(a, st); break;
+        default: launch_gemm_zin<TRANS, 128, Q4>(a, st); break;
     }
 }
 
@@ -307,6 +344,7 @@ lora_status fwd_bf16(const lora_linear_desc& d, bool quant, const void* X, const
     g.Out = static_cast<uint16_t*>(H);
     g.Zsave = in_tile ? U_save : nullptr;
     g.Zin = in_tile ? nullptr : U;
+    g.Part = reinterpret_cast<float*>(wsb + plan.off_split);
     g.P = (int)d.M; g.Q = (int)d.N; g.C = (int)d.K; g.r = r;
     g.s = d.alpha / (float)d.r;
     if (quant) launch_gemm<false, true>(g, st);
@@ -364,6 +402,7 @@ lora_status bwd_bf16(const lora_linear_desc& d, bool quant, const void* dY, cons
         g.Out = static_cast<uint16_t*>(dX);
         g.Zin = v_in_tile ? nullptr : V;
         g.Zsave = v_in_tile ? V : nullptr;
+        g.Part = reinterpret_cast<float*>(wsb + plan.off_split);
         g.P = (int)d.M; g.Q = (int)d.K; g.C = (int)d.N; g.r = r;
         g.s = d.alpha / (float)d.r;
         if (quant) launch_gemm<true, true>(g, st);

@@ -67,6 +67,7 @@ RAGGED = [
     (300, 136, 264, 5), (1, 8, 8, 1), (257, 520, 72, 16), (130, 64, 1000, 24),
     (513, 264, 256, 48), (64, 128, 128, 64), (200, 192, 136, 100), (96, 256, 264, 128),
     (520, 72, 520, 8), (33, 2056, 40, 3),
+    (300, 200, 1000, 24),    # r > 16 with few output tiles: forward in 2 and dX in 8 contraction slices
 ]
 
 
