@@ -312,26 +312,32 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
         const int c0 = (kbase + kt) * BK;
         uint8_t* const Ls = smem + (kt & 1) * SM::STAGE;
         uint8_t* const Rs = Ls + TILE;
+        // one per-lane base per operand and stage (or the out-of-range marker,
+        // which stays out of range with any of the row increments added: they
+        // are below 2^31), plus a uniform row increment per load
         const bool lok = on && c0 + kc_ch < C;
+        const uint32_t vL = lok ? offL + (uint32_t)c0 * 2u : kOOB;
 #pragma unroll
-        for (int i = 0; i < LPW; ++i)
-            g2lds16<TRANS>(rsL, Ls + (wave * LPW + i) * 1024, lok ? offL + (uint32_t)(i * 8 * C + c0) * 2u : kOOB);
+        for (int i = 0; i < LPW; ++i) g2lds16<TRANS>(rsL, Ls + (wave * LPW + i) * 1024, vL + (uint32_t)(i * 8 * C) * 2u);
         if constexpr (Q4) {
             load_q(kt);
         } else if constexpr (!TRANS) {
+            const uint32_t vR = lok ? offR + (uint32_t)c0 * 2u : kOOB;
 #pragma unroll
             for (int i = 0; i < LPW; ++i)
-                g2lds16<TRANS>(rsR, Rs + (wave * LPW + i) * 1024, lok ? offR + (uint32_t)(i * 8 * C + c0) * 2u : kOOB);
+                g2lds16<TRANS>(rsR, Rs + (wave * LPW + i) * 1024, vR + (uint32_t)(i * 8 * C) * 2u);
         } else {
             const int rows_left = max(1, min(C - c0, BK));
             const __amdgpu_buffer_rsrc_t rs =
                 make_rsrc(a.R + (size_t)c0 * Q + q0, (uint64_t)(rows_left - 1) * Q * 2 + (uint64_t)(Q - q0) * 2);
+            uint32_t vR[LPW == 8 ? 4 : 2];
 #pragma unroll
-            for (int i = 0; i < LPW; ++i) {
-                const int ch = chR[(i & 1) | (LPW == 8 ? ((i >> 2) & 1) << 1 : 0)];
+            for (int v = 0; v < (LPW == 8 ? 4 : 2); ++v)
+                vR[v] = (on && q0 + chR[v] < Q) ? offR + (uint32_t)chR[v] * 2u : kOOB;
+#pragma unroll
+            for (int i = 0; i < LPW; ++i)
                 g2lds16<TRANS>(rs, Rs + (wave * LPW + i) * 1024,
-                        (on && q0 + ch < Q) ? offR + (uint32_t)(2 * i * Q + ch) * 2u : kOOB);
-            }
+                               vR[(i & 1) | (LPW == 8 ? ((i >> 2) & 1) << 1 : 0)] + (uint32_t)(2 * i * Q) * 2u);
         }
     };
     // F of the rank-r product.  Forward: A [r][C] rows are contiguous in c and
@@ -535,10 +541,20 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
     // The E fragments (and Z itself when it comes precomputed) of the first 16
     // rank columns are requested before the LDS exchange so that their global
     // latency overlaps it.
+    // r % 4 == 0: the four rank columns a lane needs are contiguous (16 bytes of
+    // Z, 8 bytes of the forward's E = B), one load each
+    const bool r4 = (r & 3) == 0;
     auto load_e = [&](int jt, bf16x8 (&ef)[QB]) {
 #pragma unroll
         for (int qi = 0; qi < QB; ++qi) {
             const int q = q0 + wq * QB * 16 + qi * 16 + l16;
+            if (!TRANS && r4) {
+                const int j = jt * 16 + 4 * g4;
+                u32x2 v = {0u, 0u};
+                if (q < Q && j < r) v = *reinterpret_cast<const u32x2*>(a.E + (size_t)q * r + j);
+                ef[qi] = as_bf16x8(u32x4{v[0], v[1], v[0], v[1]});
+                continue;
+            }
             uint32_t e4[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -555,6 +571,12 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
 #pragma unroll
         for (int pi = 0; pi < 8; ++pi) {
             const int p = p0 + wp * 128 + ((pi + ZB * wq) & 7) * 16 + l16;
+            if (r4) {
+                const int j = jt * 16 + 4 * g4;
+                zv[pi] = (p < P && j < r) ? *reinterpret_cast<const f32x4*>(a.Zin + (size_t)p * r + j)
+                                          : f32x4{0.f, 0.f, 0.f, 0.f};
+                continue;
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int j = jt * 16 + 4 * g4 + i;
