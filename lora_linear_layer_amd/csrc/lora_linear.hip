@@ -82,7 +82,12 @@ RankSplit rank_split(int64_t out_tiles, int64_t n_ct) {
 }
 
 // Splits of the three streamed products of one descriptor.
-RankSplit split_z(const lora_linear_desc& d, int64_t C) { return rank_split(cdiv(d.M, kRT), cdiv(C, kRT)); }
+// Contraction chunks of the register-streamed Z pass (rank_z_direct): about
+// 256 workgroups of 128 rows, at least 256 columns per chunk.
+int z_chunks(const lora_linear_desc& d, int64_t C) {
+    const int64_t rows = cdiv(d.M, 128);
+    return (int)std::max<int64_t>(1, std::min<int64_t>(cdiv(256, rows), cdiv(C, 256)));
+}
 RankSplit split_g(const lora_linear_desc& d) { return rank_split(cdiv(d.K, kRT) + cdiv(d.N, kRT), cdiv(d.M, kRT)); }
 
 // Workspace layout for one descriptor (offsets in bytes from ws).
@@ -99,7 +104,7 @@ Plan make_plan(const lora_linear_desc& d) {
     p.off_u = zbytes;
     size_t cur = 2 * zbytes;
     if (d.dtype == LORA_DTYPE_BF16) {
-        const int zchunks = std::max(split_z(d, d.K).n_chunk, split_z(d, d.N).n_chunk);
+        const int zchunks = std::max(z_chunks(d, d.K), z_chunks(d, d.N));
         p.off_zp = cur;
         cur += align_up((size_t)zchunks * d.M * d.r * sizeof(float));
         p.g = split_g(d);
@@ -237,31 +242,33 @@ void launch_gemm(const GemmArgs& a, hipStream_t st) {
     }
 }
 
-// Z = Y F^T (Z [M][r] float32) streamed over Y [M][C]; F given as bf16 rows
-// [r][C] (A itself, or B^T from transpose_rank).  Partials go to zpart and
-// are summed into Z.
+// Z = Y F^T (Z [M][r] float32) streamed over Y [M][C] through registers
+// (rank_z_direct); F given as bf16 rows [r][C] (A itself, or B^T from
+// transpose_rank).  The contraction is split into z_chunks chunks whose
+// float32 partials partial_sum adds in a fixed order.
+
 void launch_rank_z(const lora_linear_desc& d, const uint16_t* Y, int64_t C, const uint16_t* F_rows, float* Z,
                    float* zpart, hipStream_t st) {
-    const RankSplit sp = split_z(d, C);
-    RankArgs a{};
-    a.prob[0] = RankProblem{Y, F_rows, nullptr, sp.n_chunk > 1 ? zpart : Z, (int)C, (int)C, (int)cdiv(d.M, kRT)};
-    a.n_prob = 1;
-    a.M = (int)d.M;
-    a.r = (int)d.r;
-    a.chunk_tiles = sp.chunk_tiles;
-    a.n_chunk = sp.n_chunk;
-    const dim3 grid((unsigned)a.prob[0].n_tiles, (unsigned)sp.n_chunk, 1);
-    for (int j0 = 0; j0 < d.r; j0 += 64) {        // ranks above 64: one launch per 64 columns
-        a.j0 = j0;
-        switch (rpad_of(std::min<int64_t>(d.r - j0, 64))) {
-            case 16: hipLaunchKernelGGL((rank_stream<16, false>), grid, dim3(256), 0, st, a); break;
-            case 32: hipLaunchKernelGGL((rank_stream<32, false>), grid, dim3(256), 0, st, a); break;
-            default: hipLaunchKernelGGL((rank_stream<64, false>), grid, dim3(256), 0, st, a); break;
+    const int n_chunk = z_chunks(d, C);
+    const int chunk_c = (int)(cdiv(cdiv(C, n_chunk), 32) * 32);
+    const int n_used = (int)cdiv(C, chunk_c);
+    float* const out = n_used > 1 ? zpart : Z;
+    const dim3 grid((unsigned)cdiv(d.M, 128), (unsigned)n_used, 1);
+    for (int j0 = 0; j0 < d.r; j0 += 64) {        // 64 rank columns per launch
+        const int jb = (int)cdiv(std::min<int64_t>(d.r - j0, 64), 16);
+#define RZD(J) hipLaunchKernelGGL((rank_z_direct<J>), grid, dim3(256), 0, st, Y, F_rows, out, (int)d.M, (int)C, \
+                                  (int)d.r, j0, chunk_c)
+        switch (jb) {
+            case 1: RZD(1); break;
+            case 2: RZD(2); break;
+            case 3: RZD(3); break;
+            default: RZD(4); break;
         }
+#undef RZD
     }
-    if (sp.n_chunk > 1) {
+    if (n_used > 1) {
         const int64_t n = d.M * d.r;
-        hipLaunchKernelGGL(partial_sum, dim3((unsigned)cdiv(n, 1024)), dim3(256), 0, st, zpart, Z, n, sp.n_chunk);
+        hipLaunchKernelGGL(partial_sum, dim3((unsigned)cdiv(n, 1024)), dim3(256), 0, st, zpart, Z, n, n_used);
     }
 }
 

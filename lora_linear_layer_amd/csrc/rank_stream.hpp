@@ -196,6 +196,88 @@ __global__ __launch_bounds__(256) void rank_stream(const RankArgs a) {
         }
 }
 
+// Z mode streamed through registers (no LDS): Z[m][j] = sum_c Y[m][c] F[j][c],
+// F as bf16 rows [r][C].  Wave w of workgroup (x, y) owns rows
+// m0 = (4 x + w) * 32 .. + 31 (two MFMA row blocks) and the contraction chunk
+// y (chunk_c columns, a multiple of 32); every lane loads its operand
+// fragments (16 bytes: 8 consecutive c of one row) straight from global
+// memory in MFMA layout, D steps of 32 c ahead of the MFMAs.  Rows, columns
+// and rank rows out of range read zero (buffer bounds).  Writes the float32
+// partial part[y][m][j0 + j] for j < min(r - j0, 16 JB).
+template <int JB>
+__global__ __launch_bounds__(256) void rank_z_direct(const uint16_t* __restrict__ Y, const uint16_t* __restrict__ F,
+                                                     float* __restrict__ part, int M, int C, int r, int j0,
+                                                     int chunk_c) {
+    constexpr int D = 4;                              // k-steps in flight
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const int m0 = ((int)blockIdx.x * 4 + wave) * 32;
+    const int cb = (int)blockIdx.y * chunk_c;
+    const int ce = min(C, cb + chunk_c);
+    const int nsteps = (ce - cb + 31) / 32;
+    const int rl = min(r - j0, 16 * JB);
+    const __amdgpu_buffer_rsrc_t rsY = make_rsrc(Y, (uint64_t)M * C * 2);
+    const __amdgpu_buffer_rsrc_t rsF = make_rsrc(F, (uint64_t)r * C * 2);
+    // per-lane row bases; a step adds its column offset
+    uint32_t yoff[2], foff[JB];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int m = m0 + 16 * i + l16;
+        yoff[i] = m < M ? (uint32_t)((size_t)m * C + cb + 8 * g4) * 2u : kOOB;
+    }
+#pragma unroll
+    for (int jb = 0; jb < JB; ++jb) {
+        const int j = 16 * jb + l16;
+        foff[jb] = j < rl ? (uint32_t)((size_t)(j0 + j) * C + cb + 8 * g4) * 2u : kOOB;
+    }
+    auto ld = [&](__amdgpu_buffer_rsrc_t rs, uint32_t base, int step) -> bf16x8 {
+        const int c = cb + 32 * step + 8 * g4;        // this lane's first column
+        const uint32_t o = (base == kOOB || c >= ce) ? kOOB : base + (uint32_t)(32 * step) * 2u;
+        return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, o, 0, 0));
+    };
+    bf16x8 yr[D][2], fr[D][JB];
+    f32x4 acc[2][JB];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int jb = 0; jb < JB; ++jb) acc[i][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) yr[u][i] = ld(rsY, yoff[i], u);
+#pragma unroll
+        for (int jb = 0; jb < JB; ++jb) fr[u][jb] = ld(rsF, foff[jb], u);
+    }
+    for (int s0 = 0; s0 < nsteps; s0 += D) {
+#pragma unroll
+        for (int u = 0; u < D; ++u) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int jb = 0; jb < JB; ++jb) acc[i][jb] = mfma16(fr[u][jb], yr[u][i], acc[i][jb]);
+            const int nx = s0 + u + D;                 // refill this slot D steps ahead (zeros past the chunk)
+#pragma unroll
+            for (int i = 0; i < 2; ++i) yr[u][i] = ld(rsY, yoff[i], nx);
+#pragma unroll
+            for (int jb = 0; jb < JB; ++jb) fr[u][jb] = ld(rsF, foff[jb], nx);
+        }
+    }
+    // lane holds Z^T rows j = 16 jb + 4 g4 + e at column m = m0 + 16 i + l16
+    float* const out = part + (size_t)blockIdx.y * M * r;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int m = m0 + 16 * i + l16;
+        if (m >= M) continue;
+#pragma unroll
+        for (int jb = 0; jb < JB; ++jb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = 16 * jb + 4 * g4 + e;
+                if (j < rl) out[(size_t)m * r + j0 + j] = acc[i][jb][e];
+            }
+    }
+}
+
 // G-mode side planes: hi[j][m] = bf16(Z[m][j]), lo[j][m] = bf16(Z[m][j] - hi),
 // j < r, m < Mp (zero for m >= M); blockIdx.y selects one of two problems.
 __global__ __launch_bounds__(256) void zt_hilo(const float* __restrict__ z0, const float* __restrict__ z1,
