@@ -127,9 +127,9 @@ struct GemmArgs {
     const float* Zin;       // precomputed Z [P][r] (ZIN), else unused
     uint16_t* Out;          // [P][Q] bf16
     float* Zsave;           // [P][r] float32 or nullptr (written by the q-tile-0 workgroups)
-    float* Part;            // split contraction: float32 partial tiles [split][P][Q]
+    float* Part;            // split contraction: float32 partial tiles [split][tile - first_split][256][256]
     int P, Q, C, r;
-    int split, kc;          // split contraction: slices, 64-wide stages per slice
+    int first_split, split, kc;   // split contraction: first split tile, slices, 64-wide stages per slice
     float s;
 };
 
@@ -166,18 +166,19 @@ struct Frags {
     bf16x8 f[JT];     // F, rank rows
 };
 
-// SPLIT = true (precomputed Z only): workgroup u covers tile u / split and the
-// contraction stages [kc (u % split), kc (u % split + 1)); it stores a float32
-// partial tile, slice 0 including the rank-r term, and split_finish adds the
-// slices in order and rounds to bf16.  For outputs with too few tiles to fill
-// the chip (e.g. d_out = 1024).
+// SPLIT = true (precomputed Z only): tiles below first_split run whole; the
+// others run as `split` workgroups each, slice v covering the contraction
+// stages [kc v, kc (v + 1)), storing a float32 partial tile (slice 0 with the
+// rank-r term) that split_finish adds in order and rounds to bf16.  Used when
+// the output has too few tiles to fill the chip (e.g. d_out = 1024: all tiles
+// split) and for the tiles of a last, partly empty round.
 template <bool TRANS, int RPAD, bool ZIN, bool Q4 = false, bool SPLIT = false>
 __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
     using namespace g2;
     using namespace g2w;
     using SM = GemmSmem<RPAD, ZIN, Q4>;
-    static_assert(ZIN || !(TRANS && Q4), "4-bit input gradient takes V precomputed");
-    static_assert(!SPLIT || (ZIN && !Q4), "split contraction: 16-bit weights, precomputed Z");
+    static_assert(ZIN || !Q4, "4-bit GEMMs take Z precomputed");
+    static_assert(!SPLIT || ZIN, "split contraction: precomputed Z");
     constexpr int JT = ZIN ? 1 : RPAD / 16;
     constexpr int F_LOADS = SM::F_BYTES / 1024;   // done by waves 0 .. F_LOADS - 1
     static_assert(F_LOADS <= 8, "F tile larger than one load per wave");
@@ -191,12 +192,19 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
 
     const int P = a.P, Q = a.Q, C = a.C, r = a.r;
     const int nPt = (P + BP - 1) / BP, nQt = (Q + BQ - 1) / BQ;
-    int pt, qt, kbase = 0, slice = 0;
+    int pt, qt, kbase = 0, slice = -1, stile = 0;   // slice -1: whole tile
     if constexpr (SPLIT) {
-        const int u = xcd_contiguous(blockIdx.x, nPt * nQt * a.split);
-        slice = u % a.split;
-        kbase = slice * a.kc;
-        grouped_tile<4>(u / a.split, nPt, nQt, pt, qt);
+        const int T = nPt * nQt;
+        const int u = xcd_contiguous(blockIdx.x, a.first_split + (T - a.first_split) * a.split);
+        int tile = u;
+        if (u >= a.first_split) {
+            const int v = u - a.first_split;
+            stile = v / a.split;
+            slice = v % a.split;
+            kbase = slice * a.kc;
+            tile = a.first_split + stile;
+        }
+        grouped_tile<4>(tile, nPt, nQt, pt, qt);
     } else {
         grouped_tile<4>(xcd_contiguous(blockIdx.x, nPt * nQt), nPt, nQt, pt, qt);
     }
@@ -254,7 +262,8 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
     if constexpr (Q4) {
         if (tid < 16) reinterpret_cast<float*>(smem + SM::LUT)[tid] = a.codebook[tid];
     }
-    auto load_q = [&](int kt) {
+    auto load_q = [&](int kt0) {
+        const int kt = kbase + kt0;              // stage of the whole contraction
         const int c0 = kt * BK;
 #pragma unroll
         for (int u = 0; u < QU; ++u) {
@@ -481,7 +490,7 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
     using NoRead = std::false_type;
 
     // ------------------------------------------------------------ main loop
-    const int nk = SPLIT ? min((C + BK - 1) / BK - kbase, a.kc) : (C + BK - 1) / BK;
+    const int nk = (SPLIT && slice >= 0) ? min((C + BK - 1) / BK - kbase, a.kc) : (C + BK - 1) / BK;
     if constexpr (Q4) {
         lds_barrier();                       // codebook in LDS
         issue_lr(0, true);
@@ -609,7 +618,7 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
     }
 
     const float s = a.s;
-    const int n_jt = (SPLIT && slice != 0) ? 0 : RPAD / 16;   // the rank-r term goes into slice 0 only
+    const int n_jt = (SPLIT && slice > 0) ? 0 : RPAD / 16;    // the rank-r term goes into slice 0 only
 #pragma unroll 1
     for (int jt = 0; jt < n_jt; ++jt) {
         bf16x8 ef[QB];
@@ -646,16 +655,17 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
         }
     }
 
-    if constexpr (SPLIT) {
-        // float32 partial tile, straight from the accumulators: Part[slice][p][q .. q+3]
-        float* const out = a.Part + (size_t)slice * P * Q;
+    if (SPLIT && slice >= 0) {
+        // float32 partial tile, straight from the accumulators: [slice][stile][pl][ql .. ql+3]
+        const int n_stiles = nPt * nQt - a.first_split;
+        float* const out = a.Part + ((size_t)slice * n_stiles + stile) * (BP * BQ);
 #pragma unroll
         for (int qi = 0; qi < QB; ++qi) {
-            const int q = q0 + wq * QB * 16 + qi * 16 + 4 * g4;
+            const int ql = wq * QB * 16 + qi * 16 + 4 * g4;
 #pragma unroll
             for (int pi = 0; pi < 8; ++pi) {
-                const int p = p0 + wp * 128 + ((pi + ZB * wq) & 7) * 16 + l16;
-                if (p < P && q < Q) *reinterpret_cast<f32x4*>(out + (size_t)p * Q + q) = acc[qi][pi];
+                const int pl = wp * 128 + ((pi + ZB * wq) & 7) * 16 + l16;
+                *reinterpret_cast<f32x4*>(out + pl * BQ + ql) = acc[qi][pi];
             }
         }
         return;
@@ -689,14 +699,29 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
     }
 }
 
-// Out[e] = bf16(sum over slices k < n_slices of Part[k][e]), added in increasing k.
-__global__ __launch_bounds__(256) void split_finish(const float* __restrict__ part, uint16_t* __restrict__ out,
-                                                    int64_t n, int n_slices) {
-    const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;   // n % 4 == 0 (Q % 8 == 0)
-    if (e0 >= n) return;
-    f32x4 acc = *reinterpret_cast<const f32x4*>(part + e0);
-    for (int k = 1; k < n_slices; ++k) acc += *reinterpret_cast<const f32x4*>(part + (size_t)k * n + e0);
-    *reinterpret_cast<u32x2*>(out + e0) = u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+// Split tiles: Out[p][q] = bf16(sum over slices k < split of Part[k][stile][pl][ql]),
+// added in increasing k; each thread finishes 4 consecutive q of one tile row.
+struct SplitFinishArgs {
+    const float* part;
+    uint16_t* out;
+    int P, Q, nPt, nQt, first_split, n_stiles, split;
+};
+
+__global__ __launch_bounds__(256) void split_finish(const SplitFinishArgs a) {
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;        // one per 4 outputs
+    if (e >= (int64_t)a.n_stiles * (g2::BP * g2::BQ / 4)) return;
+    const int stile = (int)(e / (g2::BP * g2::BQ / 4));
+    const int w = (int)(e % (g2::BP * g2::BQ / 4));
+    const int pl = w / (g2::BQ / 4), ql = (w % (g2::BQ / 4)) * 4;
+    int pt, qt;
+    grouped_tile<4>(a.first_split + stile, a.nPt, a.nQt, pt, qt);
+    const int p = pt * g2::BP + pl, q = qt * g2::BQ + ql;
+    if (p >= a.P || q >= a.Q) return;                                 // Q % 8 == 0: q .. q+3 all valid
+    const size_t ts = (size_t)g2::BP * g2::BQ;
+    const float* src = a.part + (size_t)stile * ts + pl * g2::BQ + ql;
+    f32x4 acc = *reinterpret_cast<const f32x4*>(src);
+    for (int k = 1; k < a.split; ++k) acc += *reinterpret_cast<const f32x4*>(src + (size_t)k * a.n_stiles * ts);
+    *reinterpret_cast<u32x2*>(a.out + (size_t)p * a.Q + q) = u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
 }
 
 }  // namespace lora

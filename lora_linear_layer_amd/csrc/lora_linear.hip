@@ -51,16 +51,35 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 int rpad_of(int64_t r) { return r <= 16 ? 16 : r <= 32 ? 32 : r <= 64 ? 64 : 128; }
 
-// Contraction slices for a GEMM whose output has too few 256 x 256 tiles to
-// fill the 256 CUs (precomputed-Z form, 16-bit weights): about 256 workgroups,
-// at least two 64-wide stages per slice.  1 = no split.
-int gemm_split(int64_t P, int64_t Q, int64_t C) {
-    const int64_t tiles = cdiv(P, 256) * cdiv(Q, 256);
-    if (tiles >= 128) return 1;
-    const int64_t nk = cdiv(C, 64);
-    const int64_t want = std::min<int64_t>(cdiv(256, tiles), nk / 2);
-    if (want < 2) return 1;
-    return (int)cdiv(nk, cdiv(nk, want));
+// Contraction slices of a GEMM (precomputed-Z form).  An output with under
+// 128 tiles of 256 x 256 splits every tile (about 256 workgroups).  With
+// 4-bit weights, an output of more than 256 tiles whose last round is at most
+// half full also splits the tiles of that round, so it runs as a full round
+// of shorter work (measured on 2048 x 8192 -> 28672: 1226 -> 1205 us; the
+// same split of bf16 GEMMs measured slower, 477 -> 498 us on
+// 4096 x 4096 -> 14336, so they keep whole tiles).  Every slice gets at least
+// one 64-wide stage, and at least two when the contraction allows.
+struct SplitPlan {
+    int first = 0, split = 1, kc = 0;
+    size_t part_floats = 0;          // float32 partial tiles in the workspace
+};
+
+SplitPlan gemm_split_plan(int64_t P, int64_t Q, int64_t C, bool quant) {
+    SplitPlan sp;
+    const int64_t T = cdiv(P, 256) * cdiv(Q, 256), nk = cdiv(C, 64);
+    int64_t first = 0, want = 1;
+    if (T < 128) {
+        want = std::min<int64_t>(cdiv(256, T), nk / 2);
+    } else if (quant && T > 256 && T % 256 != 0 && T % 256 <= 128) {
+        first = T - T % 256;
+        want = std::min<int64_t>(256 / (T % 256), nk / 2);
+    }
+    if (want < 2) return sp;
+    sp.first = (int)first;
+    sp.split = (int)cdiv(nk, cdiv(nk, want));
+    sp.kc = (int)cdiv(nk, sp.split);
+    sp.part_floats = (size_t)sp.split * (size_t)(T - first) * 256 * 256;
+    return sp;
 }
 
 // Chunking of a streamed rank-r product (rank_stream): out_tiles 128-wide
@@ -118,11 +137,10 @@ Plan make_plan(const lora_linear_desc& d) {
         p.off_bt = cur;                                  // B^T: bf16 [r][N]
         cur += align_up((size_t)d.r * d.N * sizeof(uint16_t));
         p.off_split = cur;                               // float32 partial tiles of a split contraction
-        if (d.r > 16) {                                  // the split runs in the precomputed-Z form only
-            const int sf = gemm_split(d.M, d.N, d.K), sx = gemm_split(d.M, d.K, d.N);
-            const size_t n_split = std::max(sf > 1 ? (size_t)sf * d.M * d.N : 0, sx > 1 ? (size_t)sx * d.M * d.K : 0);
-            cur += align_up(n_split * sizeof(float));
-        }
+        // sized for the 4-bit plans, which split a superset of the bf16 ones
+        const size_t n_split = std::max(gemm_split_plan(d.M, d.N, d.K, true).part_floats,
+                                        gemm_split_plan(d.M, d.K, d.N, true).part_floats);
+        cur += align_up(n_split * sizeof(float));
     }
     p.total = cur;
     return p;
@@ -203,42 +221,47 @@ void launch_gemm_t(const GemmArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((lora_gemm<TRANS, RPAD, ZIN, Q4>), dim3(tiles), dim3(g2w::NT), 0, st, a);
 }
 
-// In-tile rank-r product for r <= 16: the forward forms U = X A^T and the
-// 16-bit input gradient forms V = dY B inside the GEMM (every q tile of a row
-// panel forms it; the first one saves it).  Larger ranks, and the 4-bit input
-// gradient (whose code registers leave no room), take Z from the stand-alone
-// streamed pass.
-bool gemm_in_tile(bool trans, bool quant, int r) { return r <= 16 && !(trans && quant); }
+// In-tile rank-r product for r <= 16 with 16-bit weights: the forward forms
+// U = X A^T and the input gradient V = dY B inside the GEMM (every q tile of
+// a row panel forms it; the first one saves it).  Larger ranks, GEMMs that
+// run with a split contraction and 4-bit weights take Z from the stand-alone
+// streamed pass: next to the code registers and the dequantisation the
+// in-tile product slows the 4-bit GEMM more than the separate pass costs
+// (2048 x 8192 -> 28672, r = 16: 1403 us in-tile, 1226 us with the pass).
+bool gemm_in_tile(bool quant, int r, const SplitPlan& sp) {
+    return r <= 16 && !quant && sp.split == 1;
+}
 
-// Precomputed-Z form; outputs with too few tiles run as a split contraction
-// into a.Part (workspace) plus split_finish.
+// Precomputed-Z form, with the split contraction of gemm_split_plan into
+// a.Part (workspace) plus split_finish when it applies.
 template <bool TRANS, int RPAD, bool Q4>
-void launch_gemm_zin(GemmArgs a, hipStream_t st) {
-    if constexpr (!Q4) {
-        const int sp = gemm_split(a.P, a.Q, a.C);
-        if (sp > 1 && a.Part != nullptr) {
-            a.split = sp;
-            a.kc = (int)cdiv(cdiv(a.C, g2::BK), sp);     // every slice gets at least one stage
-            const int tiles = (int)(cdiv(a.P, g2::BP) * cdiv(a.Q, g2::BQ));
-            hipLaunchKernelGGL((lora_gemm<TRANS, RPAD, true, false, true>), dim3(tiles * sp), dim3(g2w::NT), 0, st, a);
-            const int64_t n = (int64_t)a.P * a.Q;
-            hipLaunchKernelGGL(split_finish, dim3((unsigned)cdiv(n, 1024)), dim3(256), 0, st, a.Part, a.Out, n, sp);
-            return;
-        }
+void launch_gemm_zin(GemmArgs a, const SplitPlan& sp, hipStream_t st) {
+    if (sp.split > 1 && a.Part != nullptr) {
+        a.first_split = sp.first;
+        a.split = sp.split;
+        a.kc = sp.kc;
+        const int T = (int)(cdiv(a.P, g2::BP) * cdiv(a.Q, g2::BQ));
+        const int units = sp.first + (T - sp.first) * sp.split;
+        hipLaunchKernelGGL((lora_gemm<TRANS, RPAD, true, Q4, true>), dim3(units), dim3(g2w::NT), 0, st, a);
+        SplitFinishArgs f{a.Part, a.Out, a.P, a.Q, (int)cdiv(a.P, g2::BP), (int)cdiv(a.Q, g2::BQ), sp.first,
+                          T - sp.first, sp.split};
+        const int64_t n = (int64_t)(T - sp.first) * (g2::BP * g2::BQ / 4);
+        hipLaunchKernelGGL(split_finish, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, st, f);
+        return;
     }
     launch_gemm_t<TRANS, RPAD, true, Q4>(a, st);
 }
 
 template <bool TRANS, bool Q4>
-void launch_gemm(const GemmArgs& a, hipStream_t st) {
-    if constexpr (!(TRANS && Q4)) {
-        if (gemm_in_tile(TRANS, Q4, a.r)) { launch_gemm_t<TRANS, 16, false, Q4>(a, st); return; }
+void launch_gemm(const GemmArgs& a, bool in_tile, const SplitPlan& sp, hipStream_t st) {
+    if constexpr (!Q4) {
+        if (in_tile) { launch_gemm_t<TRANS, 16, false, false>(a, st); return; }
     }
     switch (rpad_of(a.r)) {
-        case 16: launch_gemm_zin<TRANS, 16, Q4>(a, st); break;
-        case 32: launch_gemm_zin<TRANS, 32, Q4>(a, st); break;
-        case 64: launch_gemm_zin<TRANS, 64, Q4>(a, st); break;
-        default: launch_gemm_zin<TRANS, 128, Q4>(a, st); break;
+        case 16: launch_gemm_zin<TRANS, 16, Q4>(a, sp, st); break;
+        case 32: launch_gemm_zin<TRANS, 32, Q4>(a, sp, st); break;
+        case 64: launch_gemm_zin<TRANS, 64, Q4>(a, sp, st); break;
+        default: launch_gemm_zin<TRANS, 128, Q4>(a, sp, st); break;
     }
 }
 
@@ -332,7 +355,8 @@ lora_status fwd_bf16(const lora_linear_desc& d, bool quant, const void* X, const
     const uint16_t* const X16 = static_cast<const uint16_t*>(X);
     const uint16_t* const A16 = static_cast<const uint16_t*>(A);
     float* const zpart = reinterpret_cast<float*>(wsb + plan.off_zp);
-    const bool in_tile = gemm_in_tile(false, quant, r);
+    const SplitPlan sp = gemm_split_plan(d.M, d.N, d.K, quant);
+    const bool in_tile = gemm_in_tile(quant, r, sp);
     float* U = U_save;
     if (!in_tile) {
         // U = X A^T by the streamed pass, read by the GEMM epilogue
@@ -354,8 +378,8 @@ lora_status fwd_bf16(const lora_linear_desc& d, bool quant, const void* X, const
     g.Part = reinterpret_cast<float*>(wsb + plan.off_split);
     g.P = (int)d.M; g.Q = (int)d.N; g.C = (int)d.K; g.r = r;
     g.s = d.alpha / (float)d.r;
-    if (quant) launch_gemm<false, true>(g, st);
-    else launch_gemm<false, false>(g, st);
+    if (quant) launch_gemm<false, true>(g, in_tile, sp, st);
+    else launch_gemm<false, false>(g, in_tile, sp, st);
     LAUNCH_CHECK(quant ? "lora_gemm(4-bit forward)" : "lora_gemm(forward)");
     return ok();
 }
@@ -387,7 +411,8 @@ lora_status bwd_bf16(const lora_linear_desc& d, bool quant, const void* dY, cons
     }
     // 2. V = dY B: inside the dX GEMM when it runs in the in-tile form,
     //    else the streamed pass
-    const bool v_in_tile = dX != nullptr && gemm_in_tile(true, quant, r);
+    const SplitPlan sp = gemm_split_plan(d.M, d.K, d.N, quant);
+    const bool v_in_tile = dX != nullptr && gemm_in_tile(quant, r, sp);
     if (!v_in_tile) {
         uint16_t* const BT = reinterpret_cast<uint16_t*>(wsb + plan.off_bt);
         hipLaunchKernelGGL(transpose_rank, dim3((unsigned)cdiv(d.r * d.N, 256)), dim3(256), 0, st, B16, BT,
@@ -412,8 +437,8 @@ lora_status bwd_bf16(const lora_linear_desc& d, bool quant, const void* dY, cons
         g.Part = reinterpret_cast<float*>(wsb + plan.off_split);
         g.P = (int)d.M; g.Q = (int)d.K; g.C = (int)d.N; g.r = r;
         g.s = d.alpha / (float)d.r;
-        if (quant) launch_gemm<true, true>(g, st);
-        else launch_gemm<true, false>(g, st);
+        if (quant) launch_gemm<true, true>(g, v_in_tile, sp, st);
+        else launch_gemm<true, false>(g, v_in_tile, sp, st);
         LAUNCH_CHECK(quant ? "lora_gemm(4-bit dX)" : "lora_gemm(dX)");
     }
     // 4., 5. dA = s V^T X, dB = s dY^T U

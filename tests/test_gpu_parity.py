@@ -68,6 +68,7 @@ RAGGED = [
     (513, 264, 256, 48), (64, 128, 128, 64), (200, 192, 136, 100), (96, 256, 264, 128),
     (520, 72, 520, 8), (33, 2056, 40, 3),
     (300, 200, 1000, 24),    # r > 16 with few output tiles: forward in 2 and dX in 8 contraction slices
+    (4352, 320, 4136, 24),   # 289 forward tiles: the last 33 in 2 contraction slices; dX (34 tiles) in 8
 ]
 
 
