@@ -295,7 +295,7 @@ void launch_rank_z(const lora_linear_desc& d, const uint16_t* Y, int64_t C, cons
     }
 }
 
-// dA and dB from X, V and dY, U: G-mode partials of both in one launch, then
+// dA and dB from X, V and dY, U: rank_stream partials of both in one launch, then
 // the fixed-order final sum, scale, dtype and layout.
 lora_status launch_adapter_grads(const lora_linear_desc& d, const Plan& plan, char* wsb, const uint16_t* X,
                                  const float* V, const uint16_t* dY, const float* U, void* dA, void* dB,
@@ -322,9 +322,9 @@ lora_status launch_adapter_grads(const lora_linear_desc& d, const Plan& plan, ch
     for (int j0 = 0; j0 < d.r; j0 += 64) {        // ranks above 64: one launch per 64 columns
         a.j0 = j0;
         switch (rpad_of(std::min<int64_t>(d.r - j0, 64))) {
-            case 16: hipLaunchKernelGGL((rank_stream<16, true>), grid, dim3(256), 0, st, a); break;
-            case 32: hipLaunchKernelGGL((rank_stream<32, true>), grid, dim3(256), 0, st, a); break;
-            default: hipLaunchKernelGGL((rank_stream<64, true>), grid, dim3(256), 0, st, a); break;
+            case 16: hipLaunchKernelGGL((rank_stream<16>), grid, dim3(256), 0, st, a); break;
+            case 32: hipLaunchKernelGGL((rank_stream<32>), grid, dim3(256), 0, st, a); break;
+            default: hipLaunchKernelGGL((rank_stream<64>), grid, dim3(256), 0, st, a); break;
         }
     }
     LAUNCH_CHECK("rank_stream(dA, dB)");
@@ -362,7 +362,7 @@ lora_status fwd_bf16(const lora_linear_desc& d, bool quant, const void* X, const
         // U = X A^T by the streamed pass, read by the GEMM epilogue
         if (!U) U = reinterpret_cast<float*>(wsb + plan.off_u);
         launch_rank_z(d, X16, d.K, A16, U, zpart, st);
-        LAUNCH_CHECK("rank_stream(U)");
+        LAUNCH_CHECK("rank_z_direct(U)");
     }
     GemmArgs g{};
     g.L = X16;
@@ -406,7 +406,7 @@ lora_status bwd_bf16(const lora_linear_desc& d, bool quant, const void* dY, cons
     if (!U) {
         float* Uw = reinterpret_cast<float*>(wsb + plan.off_u);
         launch_rank_z(d, X16, d.K, A16, Uw, zpart, st);
-        LAUNCH_CHECK("rank_stream(U)");
+        LAUNCH_CHECK("rank_z_direct(U)");
         U = Uw;
     }
     // 2. V = dY B: inside the dX GEMM when it runs in the in-tile form,
@@ -419,7 +419,7 @@ lora_status bwd_bf16(const lora_linear_desc& d, bool quant, const void* dY, cons
                            (int)d.N, (int)d.r);
         LAUNCH_CHECK("transpose_rank");
         launch_rank_z(d, dY16, d.N, BT, V, zpart, st);
-        LAUNCH_CHECK("rank_stream(V)");
+        LAUNCH_CHECK("rank_z_direct(V)");
     }
     // 3. dX = dY W + s V A
     if (dX) {

@@ -1,7 +1,7 @@
 // Rank-r products that stream a large bf16 matrix Y [M][C] from HBM once:
 //
-//   Z mode:  Z[m][j] = sum_c Y[m][c] F(j, c)          (U = X A^T, V = dY B)
-//   G mode:  G[c][j] = sum_m Y[m][c] Z2[m][j]         (dA^T = X^T V / s, dB = dY^T U / s)
+//   rank_stream:    G[c][j] = sum_m Y[m][c] Z2[m][j]   (dA^T = X^T V / s, dB = dY^T U / s)
+//   rank_z_direct:  Z[m][j] = sum_c Y[m][c] F(j, c)    (U = X A^T, V = dY B)
 //
 // These are the adapter-gradient products of the backward (page "ms-swift高效微调
 // 组合：LoRA+UnSloth提速实践", section 1.2 "梯度计算绕过Autograd": closed-form
@@ -10,19 +10,16 @@
 // rank-r products U and V (page "Unsloth — 微调 2-5x 加速", section "核心要点",
 // item 2: only [M, r] intermediates are formed).
 //
-// Both modes are HBM-bound.  A workgroup (4 waves) owns one 128-wide tile of
-// the output's long dimension (m in Z mode, c in G mode) and a chunk of the
-// contraction, walks the chunk in 128 x 128 tiles of Y that arrive through a
-// double-buffered LDS ring straight from global memory (buffer_load ... lds,
-// rows of 256 bytes, 16-byte chunk ch of row x at ch ^ (x & 7)), and writes a
-// float32 partial per chunk; partial_sum adds the chunks in a fixed order, so
-// results are bitwise reproducible.  MFMA 16x16x32 bf16 with float32
-// accumulation; Y^T fragments (G mode) are gathered with ds_read_b64_tr_b16.
-//
-// The rank-side operand arrives the same way, as bf16 rows [r][len] read 128
-// columns at a time: F = A [r][C] or B^T in Z mode; in G mode the two planes
-// hi = bf16(Z2^T), lo = bf16(Z2^T - hi) of [r][Mp] (tokens padded with zeros
-// to a multiple of 128), which zt_hilo writes from Z2 [M][r] float32.
+// Both are HBM-bound.  A rank_stream workgroup (4 waves) owns one 128-wide
+// tile of c and a chunk of the tokens m, walks the chunk in 128 x 128 tiles of
+// Y that arrive through a double-buffered LDS ring straight from global memory
+// (buffer_load ... lds, rows of 256 bytes, 16-byte chunk ch of row x at
+// ch ^ (x & 7)), and writes a float32 partial per chunk; grad_final adds the
+// chunks in a fixed order, so results are bitwise reproducible.  MFMA
+// 16x16x32 bf16 with float32 accumulation; Y^T fragments are gathered with
+// ds_read_b64_tr_b16.  The rank-side operand arrives the same way, as the two
+// bf16 planes hi = bf16(Z2^T), lo = bf16(Z2^T - hi) of [r][Mp] (tokens padded
+// with zeros to a multiple of 128), which zt_hilo writes from Z2 [M][r] float32.
 #pragma once
 #include "lora_gemm.hpp"
 
@@ -32,12 +29,12 @@ constexpr int kRT = 128;      // tile edge (rows of Y x columns of Y)
 
 struct RankProblem {
     const uint16_t* Y;      // [M][C] bf16
-    const uint16_t* S;      // rank side, bf16 rows [r][s_len]: Z mode F, G mode the hi plane of Z2^T
-    const uint16_t* S_lo;   // G mode: the lo plane of Z2^T (same shape)
-    float* part;            // Z mode: [n_chunk][M][r]; G mode: [n_chunk][C][r]
+    const uint16_t* S;      // hi plane of Z2^T, bf16 rows [r][s_len]
+    const uint16_t* S_lo;   // lo plane of Z2^T (same shape)
+    float* part;            // [n_chunk][C][r]
     int C;
-    int s_len;              // side row length: C (Z mode) or Mp (G mode)
-    int n_tiles;            // 128-wide tiles of the output's long dimension
+    int s_len;              // side row length Mp (tokens padded to a multiple of 128)
+    int n_tiles;            // 128-wide tiles of c
 };
 
 struct RankArgs {
@@ -52,15 +49,14 @@ struct RankArgs {
 template <int RPAD>
 struct RankSmem {
     static constexpr int YT = kRT * kRT * 2;          // 32 KB per Y tile
-    static constexpr int SIDE = RPAD * kRT * 2;       // F tile, or one of the Z2 hi / lo tiles
+    static constexpr int SIDE = RPAD * kRT * 2;       // one of the Z2 hi / lo tiles
     static constexpr int STAGE = YT + 2 * SIDE;
     static constexpr int TOTAL = 2 * STAGE;
     static_assert(RPAD <= 64 && TOTAL <= 160 * 1024, "LDS budget");
 };
 
-// Z mode when G == false, G mode when G == true.  Handles rank columns
-// j0 .. j0 + min(r - j0, RPAD) - 1.
-template <int RPAD, bool G>
+// Handles rank columns j0 .. j0 + min(r - j0, RPAD) - 1.
+template <int RPAD>
 __global__ __launch_bounds__(256) void rank_stream(const RankArgs a) {
     using SM = RankSmem<RPAD>;
     constexpr int JT = RPAD / 16;
@@ -75,9 +71,9 @@ __global__ __launch_bounds__(256) void rank_stream(const RankArgs a) {
     const int l16 = lane & 15, g4 = lane >> 4;
     const int M = a.M, C = pr.C, r = a.r, j0 = a.j0;
     const int rl = min(r - j0, RPAD);                  // rank columns of this launch
-    // the output tile: m0 (Z mode) or c0 (G mode); contraction tiles [t_begin, t_end)
+    // the output tile c0 = o0; token tiles [t_begin, t_end)
     const int o0 = blockIdx.x * kRT;
-    const int n_ct = G ? (M + kRT - 1) / kRT : (C + kRT - 1) / kRT;
+    const int n_ct = (M + kRT - 1) / kRT;
     const int t_begin = blockIdx.y * a.chunk_tiles;
     const int t_end = min(n_ct, t_begin + a.chunk_tiles);
 
@@ -85,8 +81,8 @@ __global__ __launch_bounds__(256) void rank_stream(const RankArgs a) {
     // issues loads b = 8 w .. 8 w + 7, each 4 rows: row = 4 b + lane / 16
     const int ld_row0 = wave * 32 + (lane >> 4);
     auto issue_y = [&](int t, uint8_t* Ys) {
-        const int m0 = G ? t * kRT : o0;
-        const int c0 = G ? o0 : t * kRT;
+        const int m0 = t * kRT;
+        const int c0 = o0;
         const __amdgpu_buffer_rsrc_t rs =
             make_rsrc(pr.Y + (size_t)m0 * C + c0, (uint64_t)(min(M - m0, kRT) - 1) * C * 2 + (uint64_t)(C - c0) * 2);
 #pragma unroll
@@ -101,8 +97,7 @@ __global__ __launch_bounds__(256) void rank_stream(const RankArgs a) {
     // loads b = RPAD/16 * w .. of each plane, each 4 rows: row = 4 b + lane / 16
     constexpr int SLW = RPAD / 16;                    // side loads per wave per plane
     const __amdgpu_buffer_rsrc_t rsS = make_rsrc(pr.S, (uint64_t)r * pr.s_len * 2);
-    __amdgpu_buffer_rsrc_t rsSl = rsS;
-    if constexpr (G) rsSl = make_rsrc(pr.S_lo, (uint64_t)r * pr.s_len * 2);
+    const __amdgpu_buffer_rsrc_t rsSl = make_rsrc(pr.S_lo, (uint64_t)r * pr.s_len * 2);
     auto issue_side = [&](int t, uint8_t* Ss) {
         const int col0 = t * kRT;
 #pragma unroll
@@ -113,7 +108,7 @@ __global__ __launch_bounds__(256) void rank_stream(const RankArgs a) {
             const uint32_t off = (row < rl && col0 + ch < pr.s_len)
                                      ? (uint32_t)((size_t)(j0 + row) * pr.s_len + col0 + ch) * 2u : kOOB;
             g2lds16<true>(rsS, Ss + b * 1024, off);
-            if constexpr (G) g2lds16<true>(rsSl, Ss + SM::SIDE + b * 1024, off);
+            g2lds16<true>(rsSl, Ss + SM::SIDE + b * 1024, off);
         }
     };
 
@@ -141,38 +136,27 @@ __global__ __launch_bounds__(256) void rank_stream(const RankArgs a) {
         // wave w owns output blocks 2w and 2w + 1 (16 rows each) of the 128-wide tile
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
+            // B operand: Y^T, columns c = l16 of block, 8 consecutive m from rows kk*32 + 8 g4 ..
             bf16x8 yf[2];
-            if constexpr (!G) {
-                // B operand: Y rows m (contraction c): 16-byte chunk kk * 4 + g4 of row m
 #pragma unroll
-                for (int z = 0; z < 2; ++z) {
-                    const int m = (2 * wave + z) * 16 + l16;
-                    yf[z] = lds_b128(Ys + m * 256 + (((kk * 4 + g4) ^ (m & 7)) << 4));
-                }
-            } else {
-                // B operand: Y^T, columns c = l16 of block, 8 consecutive m from rows kk*32 + 8 g4 ..
-#pragma unroll
-                for (int z = 0; z < 2; ++z) {
-                    const int c = (2 * wave + z) * 16 + (l16 & 3) * 4;
-                    const int mlo = kk * 32 + g4 * 8 + (l16 >> 2);
-                    const int mhi = mlo + 4;
-                    const i16x4 lo = lds_tr4(Ys + mlo * 256 + ((((c >> 3) ^ (mlo & 7))) << 4) + (c & 7) * 2);
-                    const i16x4 hi = lds_tr4(Ys + mhi * 256 + ((((c >> 3) ^ (mhi & 7))) << 4) + (c & 7) * 2);
-                    yf[z] = cat_tr(lo, hi);
-                }
+            for (int z = 0; z < 2; ++z) {
+                const int c = (2 * wave + z) * 16 + (l16 & 3) * 4;
+                const int mlo = kk * 32 + g4 * 8 + (l16 >> 2);
+                const int mhi = mlo + 4;
+                const i16x4 lo = lds_tr4(Ys + mlo * 256 + ((((c >> 3) ^ (mlo & 7))) << 4) + (c & 7) * 2);
+                const i16x4 hi = lds_tr4(Ys + mhi * 256 + ((((c >> 3) ^ (mhi & 7))) << 4) + (c & 7) * 2);
+                yf[z] = cat_tr(lo, hi);
             }
 #pragma unroll
             for (int jt = 0; jt < JT; ++jt) {
                 const int j = jt * 16 + l16;
                 const int off = j * 256 + (((kk * 4 + g4) ^ (j & 7)) << 4);
                 const bf16x8 sa = lds_b128(Ss + off);
+                const bf16x8 sl = lds_b128(Ss + SM::SIDE + off);
 #pragma unroll
                 for (int z = 0; z < 2; ++z) acc[jt][z] = mfma16(sa, yf[z], acc[jt][z]);
-                if constexpr (G) {
-                    const bf16x8 sl = lds_b128(Ss + SM::SIDE + off);
 #pragma unroll
-                    for (int z = 0; z < 2; ++z) acc[jt][z] = mfma16(sl, yf[z], acc[jt][z]);
-                }
+                for (int z = 0; z < 2; ++z) acc[jt][z] = mfma16(sl, yf[z], acc[jt][z]);
             }
         }
         vmcnt_le<0>();
@@ -180,7 +164,7 @@ __global__ __launch_bounds__(256) void rank_stream(const RankArgs a) {
     }
 
     // lane holds out^T rows j = jt*16 + 4 g4 + i at column o = block*16 + l16
-    const int olim = G ? C : M;
+    const int olim = C;
     float* const out = pr.part + (size_t)blockIdx.y * olim * r;
 #pragma unroll
     for (int jt = 0; jt < JT; ++jt)
@@ -196,7 +180,7 @@ __global__ __launch_bounds__(256) void rank_stream(const RankArgs a) {
         }
 }
 
-// Z mode streamed through registers (no LDS): Z[m][j] = sum_c Y[m][c] F[j][c],
+// Z streamed through registers (no LDS): Z[m][j] = sum_c Y[m][c] F[j][c],
 // F as bf16 rows [r][C].  Wave w of workgroup (x, y) owns rows
 // m0 = (4 x + w) * 32 .. + 31 (two MFMA row blocks) and the contraction chunk
 // y (chunk_c columns, a multiple of 32); every lane loads its operand
@@ -278,7 +262,7 @@ __global__ __launch_bounds__(256) void rank_z_direct(const uint16_t* __restrict_
     }
 }
 
-// G-mode side planes: hi[j][m] = bf16(Z[m][j]), lo[j][m] = bf16(Z[m][j] - hi),
+// rank_stream side planes: hi[j][m] = bf16(Z[m][j]), lo[j][m] = bf16(Z[m][j] - hi),
 // j < r, m < Mp (zero for m >= M); blockIdx.y selects one of two problems.
 __global__ __launch_bounds__(256) void zt_hilo(const float* __restrict__ z0, const float* __restrict__ z1,
                                                uint16_t* __restrict__ hi0, uint16_t* __restrict__ lo0,
@@ -332,7 +316,7 @@ __global__ __launch_bounds__(256) void partial_sum(const float* __restrict__ par
     for (int i = 0; i < cnt; ++i) out[e0 + i] = s[i];
 }
 
-// Final adapter gradients from the G-mode partials:
+// Final adapter gradients from the rank_stream partials:
 //   dA[j][k] = s * sum_chunk GA[chunk][k][j]   ([r][K] output)
 //   dB[n][j] = s * sum_chunk GB[chunk][n][j]   ([N][r] output)
 // in the tensor dtype, overwritten or accumulated.

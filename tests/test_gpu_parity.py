@@ -68,7 +68,7 @@ RAGGED = [
     (513, 264, 256, 48), (64, 128, 128, 64), (200, 192, 136, 100), (96, 256, 264, 128),
     (520, 72, 520, 8), (33, 2056, 40, 3),
     (300, 200, 1000, 24),    # r > 16 with few output tiles: forward in 2 and dX in 8 contraction slices
-    (4352, 320, 4136, 24),   # 289 forward tiles: the last 33 in 2 contraction slices; dX (34 tiles) in 8
+    (4352, 320, 4136, 24),   # 289 forward tiles, ragged in both directions; dX (34 tiles) in 8 slices
 ]
 
 
@@ -219,7 +219,8 @@ def test_dequant4_bit_exact(out):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("M,K,N,r", [(300, 256, 264, 16), (64, 1024, 136, 8), (130, 192, 520, 100)])
+@pytest.mark.parametrize("M,K,N,r", [(300, 256, 264, 16), (64, 1024, 136, 8), (130, 192, 520, 100),
+                                     (4352, 320, 4136, 24)])   # 289 forward tiles: the last 33 in 2 slices
 def test_qlinear_parity(M, K, N, r, dtype):
     sh, inp = q_inputs(M, K, N, r, M + K + N)
     got = run_linear(inp, r, sh.alpha, dtype, quant=True)
