@@ -101,8 +101,8 @@ RankSplit rank_split(int64_t out_tiles, int64_t n_ct) {
 }
 
 // Splits of the three streamed products of one descriptor.
-// Contraction chunks of the register-streamed Z pass (rank_z_direct): about
-// 256 workgroups of 128 rows, at least 256 columns per chunk.
+// Contraction chunks of the Z pass (rank_z_lds): about 256 workgroups of 128
+// rows, at least 256 columns (one F slice) per chunk.
 int z_chunks(const lora_linear_desc& d, int64_t C) {
     const int64_t rows = cdiv(d.M, 128);
     return (int)std::max<int64_t>(1, std::min<int64_t>(cdiv(256, rows), cdiv(C, 256)));
@@ -265,29 +265,29 @@ void launch_gemm(const GemmArgs& a, bool in_tile, const SplitPlan& sp, hipStream
     }
 }
 
-// Z = Y F^T (Z [M][r] float32) streamed over Y [M][C] through registers
-// (rank_z_direct); F given as bf16 rows [r][C] (A itself, or B^T from
-// transpose_rank).  The contraction is split into z_chunks chunks whose
-// float32 partials partial_sum adds in a fixed order.
+// Z = Y F^T (Z [M][r] float32) streamed over Y [M][C] (rank_z_lds); F given as
+// bf16 rows [r][C] (A itself, or B^T from transpose_rank).  The contraction is
+// split into z_chunks chunks whose float32 partials partial_sum adds in a
+// fixed order.
 
 void launch_rank_z(const lora_linear_desc& d, const uint16_t* Y, int64_t C, const uint16_t* F_rows, float* Z,
                    float* zpart, hipStream_t st) {
     const int n_chunk = z_chunks(d, C);
-    const int chunk_c = (int)(cdiv(cdiv(C, n_chunk), 32) * 32);
+    const int chunk_c = (int)(cdiv(cdiv(C, n_chunk), 256) * 256);     // whole 256-column F slices
     const int n_used = (int)cdiv(C, chunk_c);
     float* const out = n_used > 1 ? zpart : Z;
     const dim3 grid((unsigned)cdiv(d.M, 128), (unsigned)n_used, 1);
     for (int j0 = 0; j0 < d.r; j0 += 64) {        // 64 rank columns per launch
         const int jb = (int)cdiv(std::min<int64_t>(d.r - j0, 64), 16);
-#define RZD(J) hipLaunchKernelGGL((rank_z_direct<J>), grid, dim3(256), 0, st, Y, F_rows, out, (int)d.M, (int)C, \
-                                  (int)d.r, j0, chunk_c)
+#define RZ(J) hipLaunchKernelGGL((rank_z_lds<J>), grid, dim3(512), 0, st, Y, F_rows, out, (int)d.M, (int)C, \
+                                 (int)d.r, j0, chunk_c)
         switch (jb) {
-            case 1: RZD(1); break;
-            case 2: RZD(2); break;
-            case 3: RZD(3); break;
-            default: RZD(4); break;
+            case 1: RZ(1); break;
+            case 2: RZ(2); break;
+            case 3: RZ(3); break;
+            default: RZ(4); break;
         }
-#undef RZD
+#undef RZ
     }
     if (n_used > 1) {
         const int64_t n = d.M * d.r;
@@ -362,7 +362,7 @@ lora_status fwd_bf16(const lora_linear_desc& d, bool quant, const void* X, const
         // U = X A^T by the streamed pass, read by the GEMM epilogue
         if (!U) U = reinterpret_cast<float*>(wsb + plan.off_u);
         launch_rank_z(d, X16, d.K, A16, U, zpart, st);
-        LAUNCH_CHECK("rank_z_direct(U)");
+        LAUNCH_CHECK("rank_z_lds(U)");
     }
     GemmArgs g{};
     g.L = X16;
@@ -406,7 +406,7 @@ lora_status bwd_bf16(const lora_linear_desc& d, bool quant, const void* dY, cons
     if (!U) {
         float* Uw = reinterpret_cast<float*>(wsb + plan.off_u);
         launch_rank_z(d, X16, d.K, A16, Uw, zpart, st);
-        LAUNCH_CHECK("rank_z_direct(U)");
+        LAUNCH_CHECK("rank_z_lds(U)");
         U = Uw;
     }
     // 2. V = dY B: inside the dX GEMM when it runs in the in-tile form,
@@ -419,7 +419,7 @@ lora_status bwd_bf16(const lora_linear_desc& d, bool quant, const void* dY, cons
                            (int)d.N, (int)d.r);
         LAUNCH_CHECK("transpose_rank");
         launch_rank_z(d, dY16, d.N, BT, V, zpart, st);
-        LAUNCH_CHECK("rank_z_direct(V)");
+        LAUNCH_CHECK("rank_z_lds(V)");
     }
     // 3. dX = dY W + s V A
     if (dX) {

@@ -1,7 +1,7 @@
 // Rank-r products that stream a large bf16 matrix Y [M][C] from HBM once:
 //
 //   rank_stream:    G[c][j] = sum_m Y[m][c] Z2[m][j]   (dA^T = X^T V / s, dB = dY^T U / s)
-//   rank_z_direct:  Z[m][j] = sum_c Y[m][c] F(j, c)    (U = X A^T, V = dY B)
+//   rank_z_lds:     Z[m][j] = sum_c Y[m][c] F(j, c)    (U = X A^T, V = dY B)
 //
 // These are the adapter-gradient products of the backward (page "ms-swift高效微调
 // 组合：LoRA+UnSloth提速实践", section 1.2 "梯度计算绕过Autograd": closed-form
@@ -180,85 +180,91 @@ __global__ __launch_bounds__(256) void rank_stream(const RankArgs a) {
         }
 }
 
-// Z streamed through registers (no LDS): Z[m][j] = sum_c Y[m][c] F[j][c],
-// F as bf16 rows [r][C].  Wave w of workgroup (x, y) owns rows
-// m0 = (4 x + w) * 32 .. + 31 (two MFMA row blocks) and the contraction chunk
-// y (chunk_c columns, a multiple of 32); every lane loads its operand
-// fragments (16 bytes: 8 consecutive c of one row) straight from global
-// memory in MFMA layout, D steps of 32 c ahead of the MFMAs.  Rows, columns
-// and rank rows out of range read zero (buffer bounds).  Writes the float32
-// partial part[y][m][j0 + j] for j < min(r - j0, 16 JB).
+// Z with the rank side in LDS: Z[m][j] = sum_c Y[m][c] F[j][c] (F bf16 rows [r][C]).
+// Workgroup (x, y): 8 waves; wave w owns rows m = 128 x + 16 w + (0 .. 15) (one MFMA
+// row block) and the workgroup the contraction chunk y, [cb, ce), chunk_c columns (a
+// multiple of 256).  F comes in 256-column slices through a double-buffered LDS pair
+// (row j of a slice: 512 bytes, 16-byte chunk ch stored at ch ^ (j % 16), so the 16
+// rows one fragment read touches hit distinct banks); each lane loads its Y fragment
+// (8 consecutive c of one row, 16 bytes) straight from global memory into registers,
+// D = 8 steps of 32 columns ahead.  Out-of-range rows, columns and rank rows read
+// zero.  Writes the float32 partial part[y][m][j0 + j] for j < min(r - j0, 16 JB).
 template <int JB>
-__global__ __launch_bounds__(256) void rank_z_direct(const uint16_t* __restrict__ Y, const uint16_t* __restrict__ F,
-                                                     float* __restrict__ part, int M, int C, int r, int j0,
-                                                     int chunk_c) {
-    constexpr int D = 4;                              // k-steps in flight
+__global__ __launch_bounds__(512) void rank_z_lds(const uint16_t* __restrict__ Y, const uint16_t* __restrict__ F,
+                                                  float* __restrict__ part, int M, int C, int r, int j0,
+                                                  int chunk_c) {
+    constexpr int D = 8;                               // steps in flight = steps per slice
+    constexpr int SC = 256;                            // slice columns
+    constexpr int FBYTES = 16 * JB * SC * 2;           // one F slice
+    __shared__ __attribute__((aligned(1024))) uint8_t fs[2 * FBYTES];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int l16 = lane & 15, g4 = lane >> 4;
-    const int m0 = ((int)blockIdx.x * 4 + wave) * 32;
+    const int m = (int)blockIdx.x * 128 + wave * 16 + l16;
     const int cb = (int)blockIdx.y * chunk_c;
     const int ce = min(C, cb + chunk_c);
-    const int nsteps = (ce - cb + 31) / 32;
+    const int nsl = (ce - cb + SC - 1) / SC;
     const int rl = min(r - j0, 16 * JB);
     const __amdgpu_buffer_rsrc_t rsY = make_rsrc(Y, (uint64_t)M * C * 2);
     const __amdgpu_buffer_rsrc_t rsF = make_rsrc(F, (uint64_t)r * C * 2);
-    // per-lane row bases; a step adds its column offset
-    uint32_t yoff[2], foff[JB];
+    const uint32_t yoff = m < M ? (uint32_t)((size_t)m * C + cb + 8 * g4) * 2u : kOOB;
+    // F slice: load i (1 KB) covers rows 2 i and 2 i + 1; wave w issues i = JB w .. JB w + JB - 1
+    auto issue_f = [&](int sl, uint8_t* buf) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int m = m0 + 16 * i + l16;
-        yoff[i] = m < M ? (uint32_t)((size_t)m * C + cb + 8 * g4) * 2u : kOOB;
-    }
-#pragma unroll
-    for (int jb = 0; jb < JB; ++jb) {
-        const int j = 16 * jb + l16;
-        foff[jb] = j < rl ? (uint32_t)((size_t)(j0 + j) * C + cb + 8 * g4) * 2u : kOOB;
-    }
-    auto ld = [&](__amdgpu_buffer_rsrc_t rs, uint32_t base, int step) -> bf16x8 {
-        const int c = cb + 32 * step + 8 * g4;        // this lane's first column
-        const uint32_t o = (base == kOOB || c >= ce) ? kOOB : base + (uint32_t)(32 * step) * 2u;
-        return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, o, 0, 0));
+        for (int t = 0; t < JB; ++t) {
+            const int i = wave * JB + t;
+            const int row = 2 * i + (lane >> 5);
+            const int col = cb + sl * SC + (((lane & 31) ^ (row & 15)) << 3);
+            const uint32_t off = (row < rl && col < ce) ? (uint32_t)((size_t)(j0 + row) * C + col) * 2u : kOOB;
+            g2lds16<true>(rsF, buf + i * 1024, off);
+        }
     };
-    bf16x8 yr[D][2], fr[D][JB];
-    f32x4 acc[2][JB];
+    auto ld = [&](int step) -> bf16x8 {
+        const int c = cb + 32 * step + 8 * g4;
+        const uint32_t o = (yoff == kOOB || c >= ce) ? kOOB : yoff + (uint32_t)(64 * step);
+        return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rsY, o, 0, 0));
+    };
+    f32x4 acc[JB];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int jb = 0; jb < JB; ++jb) acc[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 yr[D];
+    issue_f(0, fs);
 #pragma unroll
-        for (int jb = 0; jb < JB; ++jb) acc[i][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int u = 0; u < D; ++u) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) yr[u][i] = ld(rsY, yoff[i], u);
-#pragma unroll
-        for (int jb = 0; jb < JB; ++jb) fr[u][jb] = ld(rsF, foff[jb], u);
-    }
-    for (int s0 = 0; s0 < nsteps; s0 += D) {
+    for (int u = 0; u < D; ++u) yr[u] = ld(u);
+    vmcnt_le<D>();                                     // this wave's part of slice 0 (older than the D Y loads)
+    __syncthreads();
+    for (int sl = 0; sl < nsl; ++sl) {
+        const uint8_t* const fb = fs + (sl & 1) * FBYTES;
+        if (sl + 1 < nsl) issue_f(sl + 1, fs + ((sl + 1) & 1) * FBYTES);
 #pragma unroll
         for (int u = 0; u < D; ++u) {
+            bf16x8 ff[JB];
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int jb = 0; jb < JB; ++jb)
+                ff[jb] = lds_b128(fb + (jb * 16 + l16) * (SC * 2) + (((u * 4 + g4) ^ l16) << 4));
 #pragma unroll
-                for (int jb = 0; jb < JB; ++jb) acc[i][jb] = mfma16(fr[u][jb], yr[u][i], acc[i][jb]);
-            const int nx = s0 + u + D;                 // refill this slot D steps ahead (zeros past the chunk)
-#pragma unroll
-            for (int i = 0; i < 2; ++i) yr[u][i] = ld(rsY, yoff[i], nx);
-#pragma unroll
-            for (int jb = 0; jb < JB; ++jb) fr[u][jb] = ld(rsF, foff[jb], nx);
+            for (int jb = 0; jb < JB; ++jb) acc[jb] = mfma16(ff[jb], yr[u], acc[jb]);
+            yr[u] = ld(sl * D + u + D);                // zeros past the chunk
+        }
+        if (sl + 1 < nsl) {
+            vmcnt_le<D>();                             // slice sl + 1 (older than this slice's D Y loads)
+            __syncthreads();
         }
     }
-    // lane holds Z^T rows j = 16 jb + 4 g4 + e at column m = m0 + 16 i + l16
-    float* const out = part + (size_t)blockIdx.y * M * r;
+    vmcnt_le<0>();
+    // lane holds Z^T rows j = 16 jb + 4 g4 + e at column m
+    if (m < M) {
+        float* const out = part + (size_t)blockIdx.y * M * r + (size_t)m * r + j0;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int m = m0 + 16 * i + l16;
-        if (m >= M) continue;
+        for (int jb = 0; jb < JB; ++jb) {
+            const int j = 16 * jb + 4 * g4;
+            if ((r & 3) == 0 && j + 3 < rl) {
+                *reinterpret_cast<f32x4*>(out + j) = acc[jb];
+            } else {
 #pragma unroll
-        for (int jb = 0; jb < JB; ++jb)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int j = 16 * jb + 4 * g4 + e;
-                if (j < rl) out[(size_t)m * r + j0 + j] = acc[i][jb][e];
+                for (int e = 0; e < 4; ++e)
+                    if (j + e < rl) out[j + e] = acc[jb][e];
             }
+        }
     }
 }
 
