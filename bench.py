@@ -38,6 +38,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA (published)
+PEAK_HBM_GBPS = 8000.0             # MI355X HBM3E (published)
+DEQUANT_SHAPE = (28672, 8192)      # the 4-bit layer's frozen weight, d_out x d_in
 PEAK_HBM_GBS = 8000.0
 METRIC = "fused LoRA linear fwd+bwd TFLOP/s and tokens/s; % bf16 MFMA peak (1 GPU)"
 COPY_BYTES = 256 << 20             # calibration copy: 256 MiB read + 256 MiB written
@@ -52,6 +54,7 @@ def parse():
     ap.add_argument("--workload", default="attn_proj_4096")
     ap.add_argument("--input-sets", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dequant", action="store_true", help="skip the stand-alone 4-bit dequantisation timing")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle time for the CPU baseline")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--traffic-from", default=None)
@@ -161,6 +164,36 @@ def write_traffic(args):
     os.makedirs(os.path.dirname(traffic_path(args.workload)), exist_ok=True)
     json.dump(out, open(traffic_path(args.workload), "w"), indent=1)
     print(json.dumps(out))
+
+
+def dequant_rate(lla, workloads, torch, dev, stream, reps=20):
+    """The stand-alone 4-bit dequantisation (lora_dequant4, bf16 output) on the
+    4-bit layer's weight shape: HIP events on the library's stream around each
+    launch; bytes = codes (0.5 B) + fp16 absmax (2 B per 64) + bf16 out (2 B)
+    per weight, each moved once."""
+    N, K = DEQUANT_SHAPE
+    g = torch.Generator(device=dev)
+    g.manual_seed(4004)
+    codes = torch.randint(0, 256, (N, K // 2), dtype=torch.uint8, device=dev, generator=g)
+    absmax = (torch.rand((N, K // 64), device=dev, generator=g) * 0.08 + 0.01).to(torch.float16).view(torch.int16)
+    cb = torch.from_numpy(workloads.codebook4_f32()).to(dev)
+    out = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    run = lambda: lla.lora_dequant4(codes, absmax, cb, N, K, lla.LORA_DTYPE_BF16, out, stream=stream)
+    for _ in range(3):
+        run()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record(stream)
+        run()
+        b.record(stream)
+    torch.cuda.synchronize()
+    us = sum(a.elapsed_time(b) for a, b in ev) / reps * 1e3
+    nbytes = N * K // 2 + 2 * (N * K // 64) + 2 * N * K
+    gbps = nbytes / (us * 1e-6) / 1e9
+    del codes, absmax, out
+    return {"kernel": "dequant4_kernel (lora_dequant4, bf16 out)", "shape": [N, K], "bound": "hbm",
+            "bytes_per_launch": nbytes, "avg_launch_us": round(us, 2), "achieved": round(gbps, 1),
+            "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4)}
 
 
 def copy_calibration():
@@ -314,6 +347,8 @@ def main():
         "per_linear": per_linear,
         "roofline": roofline,
     }
+    if not args.no_dequant:
+        out["hbm_kernels"] = [dequant_rate(lla, workloads, torch, dev, stream)]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -128,6 +128,12 @@ struct GemmArgs {
     uint16_t* Out;          // [P][Q] bf16
     float* Zsave;           // [P][r] float32 or nullptr (written by the q-tile-0 workgroups)
     float* Part;            // split contraction: float32 partial tiles [split][tile - first_split][256][256]
+    // Input gradient, in-tile Z only: the bf16 planes hi = bf16(Z^T), lo = bf16(Z^T - hi) of
+    // Z = V and of U (read from Uin [P][r] float32), rows [r][Mp], tokens p >= P zero; written by
+    // the q-tile-0 workgroups for the adapter-gradient pass, or not at all when Zt_hi is nullptr
+    uint16_t *Zt_hi, *Zt_lo, *Ut_hi, *Ut_lo;
+    const float* Uin;
+    int Mp;
     int P, Q, C, r;
     int first_split, split, kc;   // split contraction: first split tile, slices, 64-wide stages per slice
     float s;
@@ -613,6 +619,23 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
             for (int e = tid; e < BP * r; e += NT) {
                 const int pl = e / r, j = e - pl * r;
                 if (p0 + pl < P) a.Zsave[(size_t)(p0 + pl) * r + j] = Zx[pl * RPAD + j];
+            }
+        }
+        if constexpr (TRANS) {
+            if (a.Zt_hi != nullptr && qt == 0) {
+                // element (j, pl), pl fastest: each wave stores 128 contiguous bytes per plane
+                for (int e = tid; e < BP * r; e += NT) {
+                    const int j = e / BP, pl = e - j * BP, p = p0 + pl;
+                    if (p >= a.Mp) continue;
+                    const float v = p < P ? Zx[pl * RPAD + j] : 0.f;
+                    const float u = p < P ? a.Uin[(size_t)p * r + j] : 0.f;
+                    const __bf16 vh = (__bf16)v, uh = (__bf16)u;
+                    const size_t o = (size_t)j * a.Mp + p;
+                    a.Zt_hi[o] = __builtin_bit_cast(uint16_t, vh);
+                    a.Zt_lo[o] = __builtin_bit_cast(uint16_t, (__bf16)(v - (float)vh));
+                    a.Ut_hi[o] = __builtin_bit_cast(uint16_t, uh);
+                    a.Ut_lo[o] = __builtin_bit_cast(uint16_t, (__bf16)(u - (float)uh));
+                }
             }
         }
     }

@@ -295,22 +295,31 @@ void launch_rank_z(const lora_linear_desc& d, const uint16_t* Y, int64_t C, cons
     }
 }
 
+// bf16 planes [r][Mp] of V^T and U^T in the workspace: V^T hi, V^T lo, U^T hi, U^T lo.
+uint16_t* zt_plane(const Plan& plan, char* wsb, int64_t r, int i) {
+    const size_t plane = align_up((size_t)r * plan.Mp * sizeof(uint16_t));
+    return reinterpret_cast<uint16_t*>(wsb + plan.off_zt + i * plane);
+}
+
 // dA and dB from X, V and dY, U: rank_stream partials of both in one launch, then
-// the fixed-order final sum, scale, dtype and layout.
+// the fixed-order final sum, scale, dtype and layout.  planes_ready: the dX GEMM
+// has already written the hi / lo planes of V^T and U^T (V is then not read);
+// otherwise zt_hilo writes them.
 lora_status launch_adapter_grads(const lora_linear_desc& d, const Plan& plan, char* wsb, const uint16_t* X,
                                  const float* V, const uint16_t* dY, const float* U, void* dA, void* dB,
-                                 hipStream_t st) {
+                                 bool planes_ready, hipStream_t st) {
     RankArgs a{};
     float* const ga = reinterpret_cast<float*>(wsb + plan.off_ga);
     float* const gb = reinterpret_cast<float*>(wsb + plan.off_gb);
-    const size_t plane = align_up((size_t)d.r * plan.Mp * sizeof(uint16_t));
-    uint16_t* const vt_hi = reinterpret_cast<uint16_t*>(wsb + plan.off_zt);
-    uint16_t* const vt_lo = reinterpret_cast<uint16_t*>(wsb + plan.off_zt + plane);
-    uint16_t* const ut_hi = reinterpret_cast<uint16_t*>(wsb + plan.off_zt + 2 * plane);
-    uint16_t* const ut_lo = reinterpret_cast<uint16_t*>(wsb + plan.off_zt + 3 * plane);
-    hipLaunchKernelGGL(zt_hilo, dim3((unsigned)cdiv(d.r * plan.Mp, 256), 2), dim3(256), 0, st, V, U, vt_hi, vt_lo,
-                       ut_hi, ut_lo, (int)d.M, (int)plan.Mp, (int)d.r);
-    LAUNCH_CHECK("zt_hilo");
+    uint16_t* const vt_hi = zt_plane(plan, wsb, d.r, 0);
+    uint16_t* const vt_lo = zt_plane(plan, wsb, d.r, 1);
+    uint16_t* const ut_hi = zt_plane(plan, wsb, d.r, 2);
+    uint16_t* const ut_lo = zt_plane(plan, wsb, d.r, 3);
+    if (!planes_ready) {
+        hipLaunchKernelGGL(zt_hilo, dim3((unsigned)cdiv(d.r * plan.Mp, 256), 2), dim3(256), 0, st, V, U, vt_hi,
+                           vt_lo, ut_hi, ut_lo, (int)d.M, (int)plan.Mp, (int)d.r);
+        LAUNCH_CHECK("zt_hilo");
+    }
     a.prob[0] = RankProblem{X, vt_hi, vt_lo, ga, (int)d.K, (int)plan.Mp, (int)cdiv(d.K, kRT)};
     a.prob[1] = RankProblem{dY, ut_hi, ut_lo, gb, (int)d.N, (int)plan.Mp, (int)cdiv(d.N, kRT)};
     a.n_prob = 2;
@@ -433,7 +442,15 @@ lora_status bwd_bf16(const lora_linear_desc& d, bool quant, const void* dY, cons
         g.E = A16;
         g.Out = static_cast<uint16_t*>(dX);
         g.Zin = v_in_tile ? nullptr : V;
-        g.Zsave = v_in_tile ? V : nullptr;
+        if (v_in_tile) {
+            // V goes straight into the adapter-gradient planes (with U's), not to V [M][r]
+            g.Zt_hi = zt_plane(plan, wsb, d.r, 0);
+            g.Zt_lo = zt_plane(plan, wsb, d.r, 1);
+            g.Ut_hi = zt_plane(plan, wsb, d.r, 2);
+            g.Ut_lo = zt_plane(plan, wsb, d.r, 3);
+            g.Uin = U;
+            g.Mp = (int)plan.Mp;
+        }
         g.Part = reinterpret_cast<float*>(wsb + plan.off_split);
         g.P = (int)d.M; g.Q = (int)d.K; g.C = (int)d.N; g.r = r;
         g.s = d.alpha / (float)d.r;
@@ -442,7 +459,7 @@ lora_status bwd_bf16(const lora_linear_desc& d, bool quant, const void* dY, cons
         LAUNCH_CHECK(quant ? "lora_gemm(4-bit dX)" : "lora_gemm(dX)");
     }
     // 4., 5. dA = s V^T X, dB = s dY^T U
-    const lora_status gst = launch_adapter_grads(d, plan, wsb, X16, V, dY16, U, dA, dB, st);
+    const lora_status gst = launch_adapter_grads(d, plan, wsb, X16, V, dY16, U, dA, dB, v_in_tile, st);
     if (gst != LORA_OK) return gst;
     return ok();
 }
@@ -646,11 +663,13 @@ lora_status lora_dequant4(const uint8_t* Wq, const uint16_t* absmax, const float
     st = check_no_alias({{W_out, "W_out"}}, {{Wq, "Wq"}, {absmax, "absmax"}, {codebook, "codebook"}, {W_out, "W_out"}});
     if (st != LORA_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const dim3 grid((unsigned)cdiv(N * (K / 16), 256));
+    // groups of 8 weights; at most 16 workgroups per CU, grid-stride beyond that
+    const int n_groups = (int)(N * K / 8);
+    const dim3 grid((unsigned)std::min<int64_t>(cdiv(n_groups, 256), 256 * 16));
     if (out_dtype == LORA_DTYPE_F32)
-        hipLaunchKernelGGL((dequant4_kernel<true>), grid, dim3(256), 0, s, Wq, absmax, codebook, W_out, N, K);
+        hipLaunchKernelGGL((dequant4_kernel<true>), grid, dim3(256), 0, s, Wq, absmax, codebook, W_out, n_groups);
     else
-        hipLaunchKernelGGL((dequant4_kernel<false>), grid, dim3(256), 0, s, Wq, absmax, codebook, W_out, N, K);
+        hipLaunchKernelGGL((dequant4_kernel<false>), grid, dim3(256), 0, s, Wq, absmax, codebook, W_out, n_groups);
     LAUNCH_CHECK("dequant4");
     return ok();
 }

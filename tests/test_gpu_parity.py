@@ -255,3 +255,34 @@ def test_qlora_full_size(dtype):
     ref_in = q_oracle_inputs(inp, dtype)
     errs = check(got, oracle_all(ref_in, sh.scale, rows=rows), TOL[dtype], rows=rows, label="graded")
     print(f"  graded errors {errs}", flush=True)
+
+
+@pytest.mark.parametrize("r,want_dx", [(8, True), (100, False)])
+def test_workspace_garbage_and_reuse(r, want_dx):
+    """The adapter-gradient pass keeps per-tile counters in the workspace: the
+    backward clears them itself, so a workspace full of 0xFF bytes and a second
+    backward on the same workspace give the oracle's gradients, bit-identical
+    between the two calls.  r = 8 with dX: V formed in the dX GEMM, which writes
+    the rank planes and clears the counters; r = 100 without dX: the streamed V
+    pass, two adapter-gradient launches (64 rank columns each)."""
+    import lora_linear_layer_amd as lla
+    sh = shape(520, 392, 264, r)
+    inp = workloads.make_linear_inputs(sh)
+    dd = device_inputs(inp, "bf16")
+    desc = lla.Desc(sh.M, sh.K, sh.N, r, sh.alpha)
+    ws = torch.full((lla.lora_linear_workspace_size(desc),), 0xFF, dtype=torch.uint8, device="cuda")
+    H = torch.empty((sh.M, sh.N), dtype=torch.bfloat16, device="cuda")
+    U = torch.empty((sh.M, r), dtype=torch.float32, device="cuda")
+    lla.lora_linear_fwd(desc, dd["X"], dd["W"], dd["A"], dd["B"], H, U, ws=ws)
+    outs = []
+    for _ in range(2):
+        dX = torch.empty((sh.M, sh.K), dtype=torch.bfloat16, device="cuda") if want_dx else None
+        dA = torch.empty((r, sh.K), dtype=torch.bfloat16, device="cuda")
+        dB = torch.empty((sh.N, r), dtype=torch.bfloat16, device="cuda")
+        lla.lora_linear_bwd(desc, dd["dY"], dd["X"], dd["W"], dd["A"], dd["B"], U, dX, dA, dB, ws=ws)
+        torch.cuda.synchronize()
+        outs.append({"dA": to_np(dA), "dB": to_np(dB)} | ({"dX": to_np(dX)} if want_dx else {}))
+    ref = oracle_all(host_view(inp, "bf16"), sh.scale)
+    check(outs[1], ref, DIAG["bf16"], keys=("dX", "dA", "dB"))
+    for k in outs[0]:
+        np.testing.assert_array_equal(outs[0][k].view(np.uint32), outs[1][k].view(np.uint32), err_msg=k)
