@@ -43,7 +43,8 @@ DEQUANT_SHAPE = (28672, 8192)      # the 4-bit layer's frozen weight, d_out x d_
 PEAK_HBM_GBS = 8000.0
 METRIC = "fused LoRA linear fwd+bwd TFLOP/s and tokens/s; % bf16 MFMA peak (1 GPU)"
 COPY_BYTES = 256 << 20             # calibration copy: 256 MiB read + 256 MiB written
-KERNEL_SOURCES = ("lora_linear_layer_amd/csrc/*.hpp", "lora_linear_layer_amd/csrc/*.hip")
+# the sources of the kernel whose HBM traffic the counters measured (the fused GEMM)
+KERNEL_SOURCES = ("lora_linear_layer_amd/csrc/lora_gemm.hpp", "lora_linear_layer_amd/csrc/common.hpp")
 
 
 def parse():
