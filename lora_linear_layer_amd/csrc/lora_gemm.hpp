@@ -39,7 +39,8 @@
 // r <= 16: the rank-r product Z^T = F L^T reuses the L fragments already in
 // registers; the 4 waves that share a p half each form Z for 32 of its 128
 // rows.  The forward's F = A rows go to LDS like L; the input gradient's
-// F = B^T is staged through registers (B is [C][r]) into the same layout.  In
+// F (r = 8 or 16) arrives as B's own [c][j] rows and is read with the
+// transposing LDS load, like the W tile.  In
 // the epilogue Z meets in LDS and s Z E^T is applied with MFMA, s Z split into
 // bf16 hi + lo halves that fill the two halves of the 32-long contraction.
 // ZIN = true takes a precomputed Z [P][r] float32 instead (large r).
@@ -355,14 +356,14 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
                                vR[(i & 1) | (LPW == 8 ? ((i >> 2) & 1) << 1 : 0)] + (uint32_t)(2 * i * Q) * 2u);
         }
     };
-    // F of the rank-r product.  Forward: A [r][C] rows are contiguous in c and
-    // go straight to LDS.  Input gradient: B [C][r] is contiguous in j, so each
-    // thread loads (c, j) and (c, j + 1) into registers when the stage is
-    // issued (c = tid / 8, j = 2 (tid % 8); out-of-range offsets read zero) and
-    // write_f stores them into the same [j][c] layout just before the barrier
-    // that publishes the stage.  The two halves stay in separate registers so
-    // that nothing waits for them before write_f.
-    uint32_t f_lo = 0u, f_hi = 0u;
+    // F of the rank-r product, straight from global memory into LDS in both
+    // directions (waves 0 .. F_LOADS - 1, one 1 KB load each per stage).
+    // Forward: A [r][C] rows are contiguous in c: rows j of 64 c, swizzled like L.
+    // Input gradient (r = 8 or 16): B [C][r] rows are contiguous in j and land
+    // as they are, [64 c][16 j] rows of 32 bytes; lane l of wave w carries row
+    // c = 32 w + l / 2, half l % 2 (j 8 h .. 8 h + 7; zeros when r = 8 and
+    // h = 1), and the fragments are gathered down the columns with
+    // ds_read_b64_tr_b16 like the W tile.
     auto issue_f = [&](int kt) {
         if constexpr (!ZIN && !TRANS) {
             const int c0 = kt * BK;
@@ -370,19 +371,14 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
             if (wave < F_LOADS)
                 g2lds16<TRANS>(rsF, Fs + wave * 1024, (frow < r && c0 + fch < C) ? offF + (uint32_t)c0 * 2u : kOOB);
         } else if constexpr (!ZIN) {
-            const int cc = kt * BK + (tid >> 3), j = (tid & 7) * 2;
-            const uint32_t o = (uint32_t)(cc * r + j) * 2u;
-            f_lo = __builtin_amdgcn_raw_buffer_load_b16(rsF, (cc < C && j < r) ? o : kOOB, 0, 0);
-            f_hi = __builtin_amdgcn_raw_buffer_load_b16(rsF, (cc < C && j + 1 < r) ? o + 2u : kOOB, 0, 0);
-        }
-    };
-    auto write_f = [&](int kt) {
-        if constexpr (!ZIN && TRANS) {
+            static_assert(RPAD == 16, "input-gradient in-tile F is 16 rank columns");
+            const int c0 = kt * BK;
             uint8_t* const Fs = smem + (kt & 1) * SM::STAGE + 2 * TILE;
-            const int c = tid >> 3, j = (tid & 7) * 2;
-            *reinterpret_cast<uint16_t*>(Fs + j * 128 + (((c >> 3) ^ (j & 7)) << 4) + (c & 7) * 2) = (uint16_t)f_lo;
-            *reinterpret_cast<uint16_t*>(Fs + (j + 1) * 128 + (((c >> 3) ^ ((j + 1) & 7)) << 4) + (c & 7) * 2) =
-                (uint16_t)f_hi;
+            if (wave < F_LOADS) {
+                const int c = wave * 32 + (lane >> 1), h = lane & 1;
+                const bool ok = c0 + c < C && 8 * h < r;
+                g2lds16<TRANS>(rsF, Fs + wave * 1024, ok ? (uint32_t)((c0 + c) * r + 8 * h) * 2u : kOOB);
+            }
         }
     };
 
@@ -405,7 +401,13 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
         return lds_b128(Ls + wp * 16384 + ((i + ZB * wq) & 7) * 2048 + chunk_of(kk));
     };
     auto read_f = [&](const uint8_t* Ls, int kk, int jt) -> bf16x8 {
-        return lds_b128(Ls + 2 * TILE + jt * 2048 + chunk_of(kk));
+        if constexpr (!TRANS) {
+            return lds_b128(Ls + 2 * TILE + jt * 2048 + chunk_of(kk));
+        } else {
+            const int rlo = kk * 32 + g4 * 8 + (l16 >> 2);            // as read_r, 32-byte rows
+            const uint8_t* const p = Ls + 2 * TILE + rlo * 32 + (l16 & 3) * 8;
+            return cat_tr(lds_tr4(p), lds_tr4(p + 4 * 32));
+        }
     };
 
     f32x4 acc[QB][8];
@@ -425,7 +427,7 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
     // and then one fragment read after every RA MFMAs, so that neither the
     // LDS queue nor the MFMA pipe runs dry and the last read is issued well
     // before the next step needs it.
-    constexpr int NR_STEP = (TRANS ? 2 * QB : QB) + 8 + (ZIN ? 0 : JT);
+    constexpr int NR_STEP = (TRANS ? 2 * QB : QB) + 8 + (ZIN ? 0 : (TRANS ? 2 * JT : JT));
     constexpr int NM_STEP = 8 * QB + (ZIN ? 0 : ZB * JT);
     auto step = [&](const Frags<JT, QB>& cur, Frags<JT, QB>& nxt, const uint8_t* nstage, int nkk, auto do_read,
                     auto pre) {
@@ -507,15 +509,12 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
     } else {
         issue_lr(0, true);
         issue_f(0);
-        write_f(0);
         if (nk > 1) {
             issue_lr(1, true);
             issue_f(1);
             // stage 0 landed: newer than it are stage 1's L and R loads, plus its
-            // F (two register loads per thread in the input gradient's in-tile
-            // form, one load into LDS for waves 0 .. F_LOADS - 1 in the forward)
-            if constexpr (TRANS && !ZIN) vmcnt_le<2 * LPW + 2>();
-            else if (wave < F_LOADS) vmcnt_le<2 * LPW + 1>();
+            // F (one load into LDS for waves 0 .. F_LOADS - 1)
+            if (wave < F_LOADS) vmcnt_le<2 * LPW + 1>();
             else vmcnt_le<2 * LPW>();
         } else {
             vmcnt_le<0>();
@@ -537,7 +536,6 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
         const uint8_t* const nxt = smem + ((kt + 1) & 1) * SM::STAGE;
         step(fa, fb, cur, 1, Read{}, NoPre{});
         if constexpr (Q4) decode_q(kt + 1);  // R tile of stage kt + 1 from the registers loaded at its issue
-        write_f(kt + 1);                     // (input gradient) F of stage kt + 1 from its register
         vmcnt_le<0>();           // this wave's loads of stage kt + 1 have landed
         lds_barrier();           // ... and everyone's; stage kt's slot is free
         if constexpr (Q4) {

@@ -232,6 +232,12 @@ bool gemm_in_tile(bool quant, int r, const SplitPlan& sp) {
     return r <= 16 && !quant && sp.split == 1;
 }
 
+// The input gradient's in-tile form loads B [N][r] rows whole into LDS: 16-byte
+// pieces that never straddle a row, so r is 8 or 16.
+bool dx_in_tile(bool quant, int r, const SplitPlan& sp) {
+    return gemm_in_tile(quant, r, sp) && r % 8 == 0;
+}
+
 // Precomputed-Z form, with the split contraction of gemm_split_plan into
 // a.Part (workspace) plus split_finish when it applies.
 template <bool TRANS, int RPAD, bool Q4>
@@ -421,7 +427,7 @@ lora_status bwd_bf16(const lora_linear_desc& d, bool quant, const void* dY, cons
     // 2. V = dY B: inside the dX GEMM when it runs in the in-tile form,
     //    else the streamed pass
     const SplitPlan sp = gemm_split_plan(d.M, d.K, d.N, quant);
-    const bool v_in_tile = dX != nullptr && gemm_in_tile(quant, r, sp);
+    const bool v_in_tile = dX != nullptr && dx_in_tile(quant, r, sp);
     if (!v_in_tile) {
         uint16_t* const BT = reinterpret_cast<uint16_t*>(wsb + plan.off_bt);
         hipLaunchKernelGGL(transpose_rank, dim3((unsigned)cdiv(d.r * d.N, 256)), dim3(256), 0, st, B16, BT,
