@@ -56,6 +56,8 @@ def parse():
     ap.add_argument("--input-sets", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dequant", action="store_true", help="skip the stand-alone 4-bit dequantisation timing")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of a HIP graph of each step (captured once per input set)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle time for the CPU baseline")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--traffic-from", default=None)
@@ -259,21 +261,23 @@ def main():
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
+    # the library launches on the stream torch reports as current (the capture
+    # stream while a graph is being recorded)
     def fwd(d):
         if "codes" in d:
             lla.lora_qlinear_fwd(d["desc"], d["X"], d["codes"], d["absmax"], d["codebook"], d["A"], d["B"],
-                                 d["H"], d["U"], ws=ws, ws_bytes=ws_bytes, stream=stream)
+                                 d["H"], d["U"], ws=ws, ws_bytes=ws_bytes)
         else:
             lla.lora_linear_fwd(d["desc"], d["X"], d["W"], d["A"], d["B"], d["H"], d["U"], ws=ws,
-                                ws_bytes=ws_bytes, stream=stream)
+                                ws_bytes=ws_bytes)
 
     def bwd(d):
         if "codes" in d:
             lla.lora_qlinear_bwd(d["desc"], d["dY"], d["X"], d["codes"], d["absmax"], d["codebook"], d["A"],
-                                 d["B"], d["U"], d["dX"], d["dA"], d["dB"], ws=ws, ws_bytes=ws_bytes, stream=stream)
+                                 d["B"], d["U"], d["dX"], d["dA"], d["dB"], ws=ws, ws_bytes=ws_bytes)
         else:
             lla.lora_linear_bwd(d["desc"], d["dY"], d["X"], d["W"], d["A"], d["B"], d["U"], d["dX"], d["dA"],
-                                d["dB"], ws=ws, ws_bytes=ws_bytes, stream=stream)
+                                d["dB"], ws=ws, ws_bytes=ws_bytes)
 
     n_lin = len(wl.linears)
     mk = lambda: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -298,16 +302,35 @@ def main():
     for i in range(args.warmup):
         step(i, False)
     torch.cuda.synchronize()
+    run = lambda i: step(i, False)
+    if args.graph:
+        graphs = []
+        for si in range(len(sets)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(si, False)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        run = lambda i: graphs[i % len(graphs)].replay()
+        for i in range(args.warmup):
+            run(i)
+        torch.cuda.synchronize()
+    # the timed region holds only the steps themselves (no per-call events)
     t_start, t_end = mk()
     wall0 = time.perf_counter()
     t_start.record(stream)
     for i in range(args.steps):
-        step(i, True)
+        run(i)
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_total = t_start.elapsed_time(t_end)
     ms_step = ms_total / args.steps
+    # per-call durations (per-linear table, roofline) from a second pass of the
+    # same steps with HIP events around every library call
+    for i in range(args.steps):
+        step(i, True)
+    torch.cuda.synchronize()
 
     flops = wl.flops()
     tflops = flops / (ms_step * 1e-3) / 1e12
@@ -340,6 +363,7 @@ def main():
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "launch": "hip_graph_replay" if args.graph else "eager",
         "data": "synthetic (seeded on-device normal draws; no dataset or checkpoint)",
         "config": {"workload": wl.name, "linears": [[l.name, l.M, l.K, l.N, l.r, l.alpha] for l in wl.linears],
                    "input_sets": args.input_sets, "description": wl.description},
