@@ -218,6 +218,25 @@ def test_dequant4_bit_exact(out):
     np.testing.assert_array_equal(to_np(W).view(np.uint32), ref.view(np.uint32))
 
 
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+def test_dequant4_bit_exact_grid_stride(out):
+    """4104 x 8192 weights (4.2 M groups of 8): every thread takes the four-groups-in-flight
+    path of the grid-stride loop once and some take the remainder path after it."""
+    import lora_linear_layer_amd as lla
+    N, K = 4104, 8192
+    rng = np.random.default_rng(4104)
+    codes = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    absmax = (rng.random((N, K // 64)) * 0.08 + 0.01).astype(np.float16)
+    cb = workloads.codebook4_f32()
+    tdt = torch.bfloat16 if out == "bf16" else torch.float32
+    W = torch.empty((N, K), dtype=tdt, device="cuda")
+    lla.lora_dequant4(torch.from_numpy(codes).cuda(), torch.from_numpy(absmax.view(np.int16)).cuda(),
+                      torch.from_numpy(cb).cuda(), N, K, lla.LORA_DTYPE_BF16 if out == "bf16" else lla.LORA_DTYPE_F32, W)
+    torch.cuda.synchronize()
+    ref = oracle.dequant4(codes, absmax, cb, out=out)
+    np.testing.assert_array_equal(to_np(W).view(np.uint32), ref.view(np.uint32))
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("M,K,N,r", [(300, 256, 264, 16), (64, 1024, 136, 8), (130, 192, 520, 100),
                                      (4352, 320, 4136, 24)])   # 289 forward tiles: the last 33 in 2 slices
