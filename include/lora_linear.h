@@ -71,14 +71,19 @@ typedef struct lora_linear_desc {
 } lora_linear_desc;
 
 /* Bytes of device workspace any fwd/bwd call with this descriptor needs
- * (the same figure for the plain and the 4-bit entry points).  May be 0. */
+ * (the same figure for the plain and the 4-bit entry points).  May be 0.
+ * The workspace holds the intermediates passed between the kernels of one
+ * call (rank-r products, split partial sums); its contents on entry do not
+ * matter, and calls that share one workspace must be ordered on one stream. */
 lora_status lora_linear_workspace_size(const lora_linear_desc* desc, size_t* bytes);
 
 /*
  * Forward, fused: H = X W^T + s (X A^T) B^T in one kernel (page "ms-swift高效
  * 微调组合：LoRA+UnSloth提速实践", section 1.2 "算子融合": Linear, LoRA_A,
- * LoRA_B and the add in a single launch).  The rank-r product U = X A^T is
- * formed on chip, inside the main product's K loop, and never goes through HBM.
+ * LoRA_B and the add in a single launch).  For r <= 16 with 16-bit W the
+ * rank-r product U = X A^T is formed on chip, inside the main product's K loop
+ * (U_save is its only trip to HBM); for larger r and for 4-bit W a streamed
+ * pass over X forms U first and the GEMM epilogue reads it.
  *   U_save: optional float32 [M, r]; when non-NULL receives U for the backward.
  *   ws:     device workspace of ws_bytes bytes (NULL allowed when 0 is needed).
  */
