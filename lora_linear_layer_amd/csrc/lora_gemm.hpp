@@ -193,7 +193,9 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    // uniform per wave: keeps the wave-dependent parts of the LDS and global
+    // offsets in scalar registers (fewer VGPRs, no spills in most variants)
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wp = wave / WQN, wq = wave % WQN;
     const int l16 = lane & 15, g4 = lane >> 4;
 
