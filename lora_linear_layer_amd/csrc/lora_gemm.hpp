@@ -559,12 +559,17 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
     // r % 4 == 0: the four rank columns a lane needs are contiguous (16 bytes of
     // Z, 8 bytes of the forward's E = B), one load each
     const bool r4 = (r & 3) == 0;
+    // fresh copies of the lane indices: the epilogue's row and column offsets
+    // are then not shared with the main loop's LDS offsets, which would keep
+    // them live (and spilled) across the loop
+    int l16e = l16, g4e = g4;
+    asm volatile("" : "+v"(l16e), "+v"(g4e));
     auto load_e = [&](int jt, bf16x8 (&ef)[QB]) {
 #pragma unroll
         for (int qi = 0; qi < QB; ++qi) {
-            const int q = q0 + wq * QB * 16 + qi * 16 + l16;
+            const int q = q0 + wq * QB * 16 + qi * 16 + l16e;
             if (!TRANS && r4) {
-                const int j = jt * 16 + 4 * g4;
+                const int j = jt * 16 + 4 * g4e;
                 u32x2 v = {0u, 0u};
                 if (q < Q && j < r) v = *reinterpret_cast<const u32x2*>(a.E + (size_t)q * r + j);
                 ef[qi] = as_bf16x8(u32x4{v[0], v[1], v[0], v[1]});
@@ -573,7 +578,7 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
             uint32_t e4[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int j = jt * 16 + 4 * g4 + i;
+                const int j = jt * 16 + 4 * g4e + i;
                 uint32_t v = 0u;
                 if (q < Q && j < r) v = TRANS ? a.E[(size_t)j * Q + q] : a.E[(size_t)q * r + j];
                 e4[i] = v;
@@ -585,24 +590,29 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
     auto load_zin = [&](int jt, f32x4 (&zv)[8]) {
 #pragma unroll
         for (int pi = 0; pi < 8; ++pi) {
-            const int p = p0 + wp * 128 + ((pi + ZB * wq) & 7) * 16 + l16;
+            const int p = p0 + wp * 128 + ((pi + ZB * wq) & 7) * 16 + l16e;
             if (r4) {
-                const int j = jt * 16 + 4 * g4;
+                const int j = jt * 16 + 4 * g4e;
                 zv[pi] = (p < P && j < r) ? *reinterpret_cast<const f32x4*>(a.Zin + (size_t)p * r + j)
                                           : f32x4{0.f, 0.f, 0.f, 0.f};
                 continue;
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int j = jt * 16 + 4 * g4 + i;
+                const int j = jt * 16 + 4 * g4e + i;
                 zv[pi][i] = (p < P && j < r) ? a.Zin[(size_t)p * r + j] : 0.f;
             }
         }
     };
+    // (one rank block only: with several, the prefetched block stays live
+    // next to the loop-carried values and the main loop spills)
+    constexpr bool PREF = RPAD == 16;
     bf16x8 ef0[QB];
-    load_e(0, ef0);
     f32x4 zin0[ZIN ? 8 : 1];
-    if constexpr (ZIN) load_zin(0, zin0);
+    if constexpr (PREF) {
+        load_e(0, ef0);
+        if constexpr (ZIN) load_zin(0, zin0);
+    }
 
     lds_barrier();   // every wave is done with the last stage before LDS is reused
     float* const Zx = reinterpret_cast<float*>(smem);   // [256][RPAD] float32
@@ -611,8 +621,8 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
         for (int jt = 0; jt < JT; ++jt)
 #pragma unroll
             for (int z = 0; z < ZB; ++z) {
-                const int pl = wp * 128 + (wq * ZB + z) * 16 + l16;
-                *reinterpret_cast<f32x4*>(Zx + pl * RPAD + jt * 16 + 4 * g4) = zacc[jt][z];
+                const int pl = wp * 128 + (wq * ZB + z) * 16 + l16e;
+                *reinterpret_cast<f32x4*>(Zx + pl * RPAD + jt * 16 + 4 * g4e) = zacc[jt][z];
             }
         lds_barrier();
         if (a.Zsave != nullptr && qt == 0) {
@@ -646,7 +656,7 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
     for (int jt = 0; jt < n_jt; ++jt) {
         bf16x8 ef[QB];
         f32x4 zv[ZIN ? 8 : 1];
-        if (jt == 0) {
+        if (PREF && jt == 0) {
 #pragma unroll
             for (int qi = 0; qi < QB; ++qi) ef[qi] = ef0[qi];
             if constexpr (ZIN) {
@@ -659,10 +669,10 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
         }
 #pragma unroll
         for (int pi = 0; pi < 8; ++pi) {
-            const int pl = wp * 128 + ((pi + ZB * wq) & 7) * 16 + l16;
+            const int pl = wp * 128 + ((pi + ZB * wq) & 7) * 16 + l16e;
             f32x4 z;
             if constexpr (ZIN) z = zv[pi];
-            else z = *reinterpret_cast<const f32x4*>(Zx + pl * RPAD + jt * 16 + 4 * g4);
+            else z = *reinterpret_cast<const f32x4*>(Zx + pl * RPAD + jt * 16 + 4 * g4e);
             uint32_t hi[4], lo[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -684,10 +694,10 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
         float* const out = a.Part + ((size_t)slice * n_stiles + stile) * (BP * BQ);
 #pragma unroll
         for (int qi = 0; qi < QB; ++qi) {
-            const int ql = wq * QB * 16 + qi * 16 + 4 * g4;
+            const int ql = wq * QB * 16 + qi * 16 + 4 * g4e;
 #pragma unroll
             for (int pi = 0; pi < 8; ++pi) {
-                const int pl = wp * 128 + ((pi + ZB * wq) & 7) * 16 + l16;
+                const int pl = wp * 128 + ((pi + ZB * wq) & 7) * 16 + l16e;
                 *reinterpret_cast<f32x4*>(out + pl * BQ + ql) = acc[qi][pi];
             }
         }
@@ -697,15 +707,15 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
     // store: the bf16 tile goes through LDS ([256 p][256 q], 16-byte chunk c of
     // row p at c ^ (p % 32)) so that global stores are whole 512-byte row
     // segments, 16 bytes per lane.  A lane holds Out[p][q .. q+3] of each
-    // accumulator (p = column l16, q = 4 consecutive rows).
+    // accumulator (p = column l16e, q = 4 consecutive rows).
     static_assert(BP * BQ * 2 <= SM::TOTAL, "output tile must fit in LDS");
     lds_barrier();                       // Zx reads are done
 #pragma unroll
     for (int qi = 0; qi < QB; ++qi) {
-        const int ql = wq * QB * 16 + qi * 16 + 4 * g4;
+        const int ql = wq * QB * 16 + qi * 16 + 4 * g4e;
 #pragma unroll
         for (int pi = 0; pi < 8; ++pi) {
-            const int pl = wp * 128 + ((pi + ZB * wq) & 7) * 16 + l16;
+            const int pl = wp * 128 + ((pi + ZB * wq) & 7) * 16 + l16e;
             const f32x4 v = acc[qi][pi];
             const u32x2 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
             *reinterpret_cast<u32x2*>(smem + pl * 512 + (((ql >> 3) ^ (pl & 31)) << 4) + (ql & 7) * 2) = o;
