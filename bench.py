@@ -55,7 +55,8 @@ def parse():
     ap.add_argument("--workload", default="attn_proj_4096")
     ap.add_argument("--input-sets", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-dequant", action="store_true", help="skip the stand-alone 4-bit dequantisation timing")
+    ap.add_argument("--no-dequant", action="store_true",
+                    help="skip the stand-alone timings of the dequantisation and merge kernels")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of a HIP graph of each step (captured once per input set)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle time for the CPU baseline")
@@ -195,6 +196,35 @@ def dequant_rate(lla, workloads, torch, dev, stream, reps=20):
     gbps = nbytes / (us * 1e-6) / 1e9
     del codes, absmax, out
     return {"kernel": "dequant4_kernel (lora_dequant4, bf16 out)", "shape": [N, K], "bound": "hbm",
+            "bytes_per_launch": nbytes, "avg_launch_us": round(us, 2), "achieved": round(gbps, 1),
+            "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4)}
+
+
+def merge_rate(lla, torch, dev, stream, l, reps=20):
+    """lora_merge (W_out = W + s B A, bf16, out of place) on the weight shape of
+    linear l: HIP events on the library's stream around each launch; bytes =
+    W read and W_out written once (2 + 2 bytes per weight) plus A and B."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(5005)
+    W = (torch.randn((l.N, l.K), device=dev, generator=g) * 0.02).to(torch.bfloat16)
+    A = (torch.randn((l.r, l.K), device=dev, generator=g) * l.K ** -0.5).to(torch.bfloat16)
+    B = (torch.randn((l.N, l.r), device=dev, generator=g) * 0.02).to(torch.bfloat16)
+    out = torch.empty_like(W)
+    desc = lla.Desc(1, l.K, l.N, l.r, l.alpha)
+    run = lambda: lla.lora_merge(desc, W, A, B, out, 1, stream=stream)
+    for _ in range(3):
+        run()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record(stream)
+        run()
+        b.record(stream)
+    torch.cuda.synchronize()
+    us = sum(a.elapsed_time(b) for a, b in ev) / reps * 1e3
+    nbytes = 4 * l.N * l.K + 2 * l.r * (l.K + l.N)
+    gbps = nbytes / (us * 1e-6) / 1e9
+    del W, A, B, out
+    return {"kernel": "lora_merge_kernel (lora_merge, bf16)", "shape": [l.N, l.K, l.r], "bound": "hbm",
             "bytes_per_launch": nbytes, "avg_launch_us": round(us, 2), "achieved": round(gbps, 1),
             "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4)}
 
@@ -373,7 +403,8 @@ def main():
         "roofline": roofline,
     }
     if not args.no_dequant:
-        out["hbm_kernels"] = [dequant_rate(lla, workloads, torch, dev, stream)]
+        out["hbm_kernels"] = [dequant_rate(lla, workloads, torch, dev, stream),
+                              merge_rate(lla, torch, dev, stream, lb)]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)

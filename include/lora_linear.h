@@ -139,6 +139,19 @@ lora_status lora_qlinear_bwd(const lora_linear_desc* desc,
 lora_status lora_dequant4(const uint8_t* Wq, const uint16_t* absmax, const float* codebook,
                           int64_t N, int64_t K, int32_t out_dtype, void* W_out, void* stream);
 
+/*
+ * Merge / unmerge (page "ms-swift框架下UnSloth与Liger-Kernel优化实战", section
+ * "设计权衡与最佳实践", item 4: before deployment the adapter is folded into
+ * the base weight, so that inference engines see a plain linear layer):
+ *   W_out = W + sign * s * B A        sign = +1 merge, -1 unmerge; s = alpha / r
+ * from desc (K, N, r, alpha, dtype; M is not used).  W, W_out [N, K], A [r, K],
+ * B [N, r] in desc->dtype; float32 arithmetic, one rounding to the dtype.
+ * W_out may be W itself (in place); it must not be A or B.  Requires
+ * 1 <= r <= 128 and K % 8 == 0; invalid arguments as for the other entry points.
+ */
+lora_status lora_merge(const lora_linear_desc* desc, const void* W, const void* A, const void* B,
+                       void* W_out, int32_t sign, void* stream);
+
 /* Static text for a status code. */
 const char* lora_status_string(lora_status status);
 

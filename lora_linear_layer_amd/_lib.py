@@ -25,7 +25,7 @@ LORA_FLAG_ACCUM_GRADS = 0x1
 
 EXPORTED = (
     "lora_linear_workspace_size", "lora_linear_fwd", "lora_linear_bwd",
-    "lora_qlinear_fwd", "lora_qlinear_bwd", "lora_dequant4",
+    "lora_qlinear_fwd", "lora_qlinear_bwd", "lora_dequant4", "lora_merge",
     "lora_status_string", "lora_last_error",
 )
 
@@ -60,6 +60,7 @@ def load() -> ctypes.CDLL:
         "lora_qlinear_fwd": [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "lora_qlinear_bwd": [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "lora_dequant4": [vp, vp, vp, i64, i64, i32, vp, vp],
+        "lora_merge": [dp, vp, vp, vp, vp, i32, vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)

@@ -140,3 +140,10 @@ def lora_dequant4(Wq, absmax, codebook, N: int, K: int, out_dtype: int, W_out, s
     st = _lib.load().lora_dequant4(_ptr(Wq), _ptr(absmax), _ptr(codebook), N, K, out_dtype, _ptr(W_out),
                                    _stream(stream))
     _check(st, "lora_dequant4")
+
+
+def lora_merge(desc: Desc, W, A, B, W_out, sign: int = 1, stream=None):
+    """W_out = W + sign * s * B A (sign +1 merge, -1 unmerge); W_out may be W (in place)."""
+    d = desc.c()
+    st = _lib.load().lora_merge(ctypes.byref(d), _ptr(W), _ptr(A), _ptr(B), _ptr(W_out), int(sign), _stream(stream))
+    _check(st, "lora_merge")

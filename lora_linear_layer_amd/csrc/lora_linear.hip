@@ -16,6 +16,7 @@
 #include "lora_gemm.hpp"
 #include "rank_stream.hpp"
 #include "dequant4.hpp"
+#include "merge.hpp"
 #include "f32_kernels.hpp"
 
 using namespace lora;
@@ -655,6 +656,41 @@ lora_status lora_qlinear_bwd(const lora_linear_desc* desc, const void* dY, const
     if (desc->dtype == LORA_DTYPE_F32)
         return bwd_f32(*desc, true, dY, X, nullptr, Wq, absmax, codebook, A, B, U_saved, dX, dA, dB, ws, s);
     return bwd_bf16(*desc, true, dY, X, nullptr, Wq, absmax, codebook, A, B, U_saved, dX, dA, dB, ws, s);
+}
+
+lora_status lora_merge(const lora_linear_desc* desc, const void* W, const void* A, const void* B, void* W_out,
+                       int32_t sign, void* stream) {
+    if (!desc) return fail(LORA_ERR_INVALID_ARG, "desc is NULL");
+    const lora_linear_desc& d = *desc;
+    if (d.K <= 0 || d.N <= 0 || d.r <= 0)
+        return fail(LORA_ERR_INVALID_ARG, "K, N, r must be positive (got %lld, %lld, %lld)", (long long)d.K,
+                    (long long)d.N, (long long)d.r);
+    if (d.dtype != LORA_DTYPE_BF16 && d.dtype != LORA_DTYPE_F32)
+        return fail(LORA_ERR_INVALID_ARG, "unknown dtype %d", (int)d.dtype);
+    if (!std::isfinite(d.alpha)) return fail(LORA_ERR_INVALID_ARG, "alpha is not finite");
+    if (sign != 1 && sign != -1) return fail(LORA_ERR_INVALID_ARG, "sign must be +1 (merge) or -1 (unmerge), got %d", (int)sign);
+    if (d.r > kMergeMaxR) return fail(LORA_ERR_UNSUPPORTED, "r = %lld exceeds %d", (long long)d.r, kMergeMaxR);
+    if (d.K % 8) return fail(LORA_ERR_UNSUPPORTED, "K must be a multiple of 8 (K=%lld)", (long long)d.K);
+    if (d.N * d.K > kMaxElems || d.r * d.K > kMaxElems || d.N * d.r > kMaxElems)
+        return fail(LORA_ERR_UNSUPPORTED, "a matrix has 2^31 or more elements");
+    if (cdiv(d.N, kMergeRows) > 65535) return fail(LORA_ERR_UNSUPPORTED, "N = %lld is too large", (long long)d.N);
+    lora_status st = check_ptrs({{W, "W"}, {A, "A"}, {B, "B"}, {W_out, "W_out"}}, {});
+    if (st != LORA_OK) return st;
+    // in place (W_out == W) is allowed; W_out must not be A or B
+    st = check_no_alias({{W_out, "W_out"}}, {{A, "A"}, {B, "B"}, {W_out, "W_out"}});
+    if (st != LORA_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const dim3 grid((unsigned)cdiv(d.K, kMergeCols), (unsigned)cdiv(d.N, kMergeRows));
+    const float scale = (float)sign * (d.alpha / (float)d.r);
+    if (d.dtype == LORA_DTYPE_F32)
+        hipLaunchKernelGGL((lora_merge_kernel<true>), grid, dim3(256), 0, s, W, A, B, W_out, (int)d.N, (int)d.K,
+                           (int)d.r, scale);
+    else
+        hipLaunchKernelGGL((lora_merge_kernel<false>), grid, dim3(256),
+                           (size_t)d.r * (kMergeCols + kMergeRows) * sizeof(uint16_t), s, W, A, B, W_out, (int)d.N,
+                           (int)d.K, (int)d.r, scale);
+    LAUNCH_CHECK("lora_merge");
+    return ok();
 }
 
 lora_status lora_dequant4(const uint8_t* Wq, const uint16_t* absmax, const float* codebook, int64_t N, int64_t K,

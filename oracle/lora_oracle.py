@@ -96,7 +96,10 @@ def backward(dY, X, W, A, B, s):
 
 
 def merged_weight(W, A, B, s):
-    """W' = W + s B A  (fold the adapter into the frozen weight; tiny shapes only)."""
+    """W' = W + s B A: the adapter folded into the frozen weight before
+    deployment ([P2] section "设计权衡与最佳实践", item 4, merge-and-unload
+    for inference engines); with -s it removes the adapter again (unmerge).
+    Forms the N x K product B A, so only for test shapes."""
     return _f64(W) + float(s) * (_f64(B) @ _f64(A))
 
 

@@ -32,7 +32,8 @@ def header_functions():
 def test_header_declares_expected_api():
     names = header_functions()
     for n in ("lora_linear_fwd", "lora_linear_bwd", "lora_qlinear_fwd", "lora_qlinear_bwd",
-              "lora_dequant4", "lora_linear_workspace_size", "lora_status_string", "lora_last_error"):
+              "lora_dequant4", "lora_merge", "lora_linear_workspace_size", "lora_status_string",
+              "lora_last_error"):
         assert n in names
 
 
@@ -152,6 +153,27 @@ def test_dequant4_validation():
     assert L.lora_dequant4(ALIGNED, ALIGNED + 0x100, None, 8, 64, 0, ALIGNED + 0x300, None) == \
         _lib.LORA_ERR_INVALID_ARG
     assert L.lora_dequant4(ALIGNED, ALIGNED + 0x100, ALIGNED + 0x200, 8, 64, 0, ALIGNED, None) == \
+        _lib.LORA_ERR_INVALID_ARG
+
+
+def test_merge_validation():
+    """lora_merge: W_out may equal W (in place, not checked here: that call would
+    launch), but not A or B; sign is +1 or -1; r <= 128, K % 8 == 0."""
+    L = lib()
+    W, A, B, O = ALIGNED, ALIGNED + 0x1000, ALIGNED + 0x2000, ALIGNED + 0x3000
+    d = desc(M=1, K=64, N=32, r=8)
+    ok_args = (W, A, B, O)
+    assert L.lora_merge(None, *ok_args, 1, None) == _lib.LORA_ERR_INVALID_ARG
+    assert L.lora_merge(ctypes.byref(d), *ok_args, 0, None) == _lib.LORA_ERR_INVALID_ARG
+    assert L.lora_merge(ctypes.byref(d), *ok_args, 2, None) == _lib.LORA_ERR_INVALID_ARG
+    assert L.lora_merge(ctypes.byref(d), W, A, B, A, 1, None) == _lib.LORA_ERR_INVALID_ARG      # W_out is A
+    assert L.lora_merge(ctypes.byref(d), W, A, B, B, -1, None) == _lib.LORA_ERR_INVALID_ARG     # W_out is B
+    assert L.lora_merge(ctypes.byref(d), W, None, B, O, 1, None) == _lib.LORA_ERR_INVALID_ARG
+    assert L.lora_merge(ctypes.byref(d), W, A, B, MISALIGNED, 1, None) == _lib.LORA_ERR_MISALIGNED
+    assert L.lora_merge(ctypes.byref(desc(M=1, K=60, N=32, r=8)), *ok_args, 1, None) == _lib.LORA_ERR_UNSUPPORTED
+    assert L.lora_merge(ctypes.byref(desc(M=1, K=64, N=32, r=129)), *ok_args, 1, None) == _lib.LORA_ERR_UNSUPPORTED
+    assert L.lora_merge(ctypes.byref(desc(M=1, K=64, N=0, r=8)), *ok_args, 1, None) == _lib.LORA_ERR_INVALID_ARG
+    assert L.lora_merge(ctypes.byref(desc(M=1, K=64, N=32, r=8, dtype=7)), *ok_args, 1, None) == \
         _lib.LORA_ERR_INVALID_ARG
 
 

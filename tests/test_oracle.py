@@ -65,6 +65,17 @@ def test_forward_merged_weight_identity():
                         rel_tol=1e-13)
 
 
+def test_merged_weight_unmerge_and_zero_b():
+    """Unmerging with -s restores W (up to float64 rounding); B = 0 merges to W
+    exactly; the merged weight is linear in s."""
+    _, W, A, B, _, s = rand_case(5)
+    Wm = oracle.merged_weight(W, A, B, s)
+    np.testing.assert_allclose(oracle.merged_weight(Wm, A, B, -s), W, rtol=0, atol=1e-14)
+    np.testing.assert_array_equal(oracle.merged_weight(W, A, np.zeros_like(B), s), W)
+    np.testing.assert_allclose(oracle.merged_weight(W, A, B, 2 * s) - W, 2 * (Wm - W), rtol=1e-13, atol=1e-15)
+    assert not np.allclose(Wm, W)
+
+
 def test_forward_special_cases():
     X, W, A, B, _, s = rand_case(4)
     H0, _ = oracle.forward(X, W, A, np.zeros_like(B), s)            # B = 0 -> plain linear
