@@ -108,3 +108,14 @@ class LoraLinear(torch.nn.Module):
 
     def forward(self, x):
         return LoraLinearFunction.apply(x, self.weight, self.lora_A, self.lora_B, self.alpha)
+
+    @torch.no_grad()
+    def merged_weight(self, sign: int = 1) -> torch.Tensor:
+        """W + sign * s * B A as a new tensor (sign +1: the adapter folded in for
+        deployment, page "ms-swift框架下UnSloth与Liger-Kernel优化实战", section
+        "设计权衡与最佳实践", item 4; sign -1 removes it again)."""
+        W = self.weight.contiguous()
+        desc = _desc(1, W.shape[1], W.shape[0], self.r, self.alpha, W.dtype)
+        out = torch.empty_like(W)
+        api.lora_merge(desc, W, self.lora_A.contiguous(), self.lora_B.contiguous(), out, sign)
+        return out
