@@ -81,6 +81,17 @@ def test_ragged_shapes(M, K, N, r, dtype):
     check(got, oracle_all(host_view(inp, dtype), sh.scale), DIAG[dtype], label=f"{(M, K, N, r)} diagnostic")
 
 
+@pytest.mark.parametrize("M,K,N,r", [(64, 1 << 21, 64, 8), (64, 64, 1 << 21, 8), (72, (1 << 21) - 8, 40, 16)])
+def test_maximum_dims(M, K, N, r):
+    """K or N at the descriptor's bound 2^21 (the largest per-tile buffer offsets;
+    with one output tile the contraction runs split into slices), bf16."""
+    sh = shape(M, K, N, r, seed=M + r + (K >> 10) + (N >> 10))
+    print(f"max dims M={M} K={K} N={N} r={r}", flush=True)
+    inp = workloads.make_linear_inputs(sh)
+    got = run_linear(inp, r, sh.alpha, "bf16")
+    check(got, oracle_all(host_view(inp, "bf16"), sh.scale), DIAG["bf16"], label=f"{(M, K, N, r)} diagnostic")
+
+
 # ------------------------------------------------------------------- special cases
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_b_zero_is_plain_linear(dtype):
