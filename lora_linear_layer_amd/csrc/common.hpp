@@ -12,8 +12,6 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWave = 64;
-
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
     return __uint_as_float(b16 << 16);
 }
@@ -39,31 +37,6 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const 
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) {
     return __builtin_bit_cast(bf16x8, v);
-}
-
-// Swizzled byte offset of 16-byte chunk `ch` of row `row` in an LDS tile whose
-// rows are `row_bytes` long.  XOR with the row's low 3 bits spreads 8
-// consecutive rows over 8 distinct 16-byte bank groups.
-template <int ROW_BYTES>
-__device__ __forceinline__ uint32_t swz(int row, int ch) {
-    return (uint32_t)(row * ROW_BYTES + ((ch ^ (row & 7)) << 4));
-}
-
-// 8x8 transpose of 16-bit elements held as 8 rows x 4 dwords.
-// in[i].dword[h] = (row i, col 2h) | (row i, col 2h+1) << 16.
-// out[j].dword[h] = (row 2h, col j) | (row 2h+1, col j) << 16.
-__device__ __forceinline__ void transpose8x8_b16(const u32x4 (&in)[8], u32x4 (&out)[8]) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-            const uint32_t a = in[2 * h][j >> 1];
-            const uint32_t b = in[2 * h + 1][j >> 1];
-            // even j: low halves of a and b; odd j: high halves
-            out[j][h] = (j & 1) ? __builtin_amdgcn_perm(b, a, 0x07060302u)
-                                : __builtin_amdgcn_perm(b, a, 0x05040100u);
-        }
-    }
 }
 
 // Workgroup -> tile index such that the tiles one XCD runs are contiguous.
