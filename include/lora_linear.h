@@ -146,8 +146,9 @@ lora_status lora_dequant4(const uint8_t* Wq, const uint16_t* absmax, const float
  *   W_out = W + sign * s * B A        sign = +1 merge, -1 unmerge; s = alpha / r
  * from desc (K, N, r, alpha, dtype; M is not used).  W, W_out [N, K], A [r, K],
  * B [N, r] in desc->dtype; float32 arithmetic, one rounding to the dtype.
- * W_out may be W itself (in place); it must not be A or B.  Requires
- * 1 <= r <= 128 and K % 8 == 0; invalid arguments as for the other entry points.
+ * W_out may be W itself (in place); otherwise its bytes must not overlap W, A
+ * or B (LORA_ERR_INVALID_ARG).  Requires 1 <= r <= 128 and K % 8 == 0
+ * (LORA_ERR_UNSUPPORTED); other invalid arguments as for the entry points above.
  */
 lora_status lora_merge(const lora_linear_desc* desc, const void* W, const void* A, const void* B,
                        void* W_out, int32_t sign, void* stream);

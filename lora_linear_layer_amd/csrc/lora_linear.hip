@@ -676,9 +676,16 @@ lora_status lora_merge(const lora_linear_desc* desc, const void* W, const void* 
     if (cdiv(d.N, kMergeRows) > 65535) return fail(LORA_ERR_UNSUPPORTED, "N = %lld is too large", (long long)d.N);
     lora_status st = check_ptrs({{W, "W"}, {A, "A"}, {B, "B"}, {W_out, "W_out"}}, {});
     if (st != LORA_OK) return st;
-    // in place (W_out == W) is allowed; W_out must not be A or B
-    st = check_no_alias({{W_out, "W_out"}}, {{A, "A"}, {B, "B"}, {W_out, "W_out"}});
-    if (st != LORA_OK) return st;
+    // in place (W_out == W) is allowed; otherwise W_out's bytes must not overlap W, A or B
+    const size_t es = d.dtype == LORA_DTYPE_F32 ? 4 : 2;
+    auto overlaps = [](const void* p, size_t pn, const void* q, size_t qn) {
+        const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+        return a < b + qn && b < a + pn;
+    };
+    const size_t wn = (size_t)d.N * d.K * es;
+    if (W_out != W && overlaps(W_out, wn, W, wn)) return fail(LORA_ERR_INVALID_ARG, "W_out overlaps W (not in place)");
+    if (overlaps(W_out, wn, A, (size_t)d.r * d.K * es)) return fail(LORA_ERR_INVALID_ARG, "W_out overlaps A");
+    if (overlaps(W_out, wn, B, (size_t)d.N * d.r * es)) return fail(LORA_ERR_INVALID_ARG, "W_out overlaps B");
     hipStream_t s = static_cast<hipStream_t>(stream);
     const dim3 grid((unsigned)cdiv(d.K, kMergeCols), (unsigned)cdiv(d.N, kMergeRows));
     const float scale = (float)sign * (d.alpha / (float)d.r);

@@ -158,7 +158,8 @@ def test_dequant4_validation():
 
 def test_merge_validation():
     """lora_merge: W_out may equal W (in place, not checked here: that call would
-    launch), but not A or B; sign is +1 or -1; r <= 128, K % 8 == 0."""
+    launch), but must not overlap W otherwise, nor A or B; sign is +1 or -1;
+    r <= 128, K % 8 == 0."""
     L = lib()
     W, A, B, O = ALIGNED, ALIGNED + 0x1000, ALIGNED + 0x2000, ALIGNED + 0x3000
     d = desc(M=1, K=64, N=32, r=8)
@@ -175,6 +176,10 @@ def test_merge_validation():
     assert L.lora_merge(ctypes.byref(desc(M=1, K=64, N=0, r=8)), *ok_args, 1, None) == _lib.LORA_ERR_INVALID_ARG
     assert L.lora_merge(ctypes.byref(desc(M=1, K=64, N=32, r=8, dtype=7)), *ok_args, 1, None) == \
         _lib.LORA_ERR_INVALID_ARG
+    # W is 32 x 64 bf16 = 4 KB: a W_out 16 bytes past W overlaps it, as does one inside A's range
+    assert L.lora_merge(ctypes.byref(d), W, A, B, W + 16, 1, None) == _lib.LORA_ERR_INVALID_ARG
+    assert L.lora_merge(ctypes.byref(d), W, A, B, A - 0x800, 1, None) == _lib.LORA_ERR_INVALID_ARG
+    assert L.lora_merge(ctypes.byref(d), W, A, B, B + 0x100, 1, None) == _lib.LORA_ERR_INVALID_ARG
 
 
 def test_python_binding_raises():
