@@ -243,7 +243,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1 "
-                                   "(data-parallel sharding is described in DESIGN.md, not built)"}))
+                                   "(data-parallel sharding across GPUs is not built)"}))
         sys.exit(2)
     if args.traffic_from:
         write_traffic(args)
