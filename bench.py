@@ -242,7 +242,7 @@ def copy_calibration():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1 "
+        print(json.dumps({"error": "bench.py runs on exactly one GPU; --gpus must be 1 "
                                    "(data-parallel sharding across GPUs is not built)"}))
         sys.exit(2)
     if args.traffic_from:
