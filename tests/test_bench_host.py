@@ -1,0 +1,83 @@
+"""Host logic of bench.py (no GPU): the one-GPU contract, the FLOP and byte
+counts behind `value` and `roofline`, and the counter-CSV arithmetic behind
+`roofline.traffic`."""
+import argparse
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+import bench
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, cwd=ROOT)
+    assert p.returncode == 2
+    assert "exactly one GPU" in json.loads(p.stdout.strip().splitlines()[-1])["error"]
+
+
+@pytest.mark.parametrize("name", ["attn_proj_4096", "mlp_11008", "decoder_layer_r64", "qlora_28672"])
+def test_fwd_plus_bwd_flops_are_the_algorithmic_count(name):
+    """fwd (2MNK + 2Mr(K+N)) + bwd (2MNK + 4Mr(K+N)) = 4MNK + 6Mr(K+N) per linear."""
+    wl = workloads.workload(name)
+    assert sum(bench.fwd_flops(l) + bench.bwd_flops(l) for l in wl.linears) == wl.flops()
+    for l in wl.linears:
+        assert l.flops() == 4 * l.M * l.N * l.K + 6 * l.M * l.r * (l.K + l.N)
+
+
+def test_forward_bytes():
+    l = workloads.workload("attn_proj_4096").linears[0]
+    M, K, N, r = l.M, l.K, l.N, l.r
+    assert bench.fwd_bytes(l) == 2 * M * K + 2 * N * K + 2 * M * N + 2 * r * (K + N) + 4 * M * r
+    q = workloads.workload("qlora_28672").linears[0]
+    # 4-bit W: half a byte per code plus one fp16 absmax per 64 weights
+    w4 = q.N * q.K // 2 + 2 * (q.N * q.K // 64)
+    assert bench.fwd_bytes(q) == 2 * q.M * q.K + w4 + 2 * q.M * q.N + 2 * q.r * (q.K + q.N) + 4 * q.M * q.r
+
+
+def _write_counters(path, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for k, c, v in rows:
+            w.writerow({"Kernel_Name": k, "Counter_Name": c, "Counter_Value": v})
+
+
+def test_traffic_from_counter_csvs(tmp_path, monkeypatch):
+    """Counters are averaged over the forward GEMM's dispatches only and scaled
+    by what the same counter reads for the calibration copy of known size."""
+    fwd = "void lora::lora_gemm<false, 16, false, false, false>(lora::GemmArgs)"
+    bwd = "void lora::lora_gemm<true, 16, false, false, false>(lora::GemmArgs)"
+    neg = "void at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel_cuda(...)>"
+    copy_kib = bench.COPY_BYTES / 1024
+    _write_counters(tmp_path / "bench_FETCH_SIZE_counter_collection.csv",
+                    [(fwd, "FETCH_SIZE", 1000.0), (fwd, "FETCH_SIZE", 3000.0), (bwd, "FETCH_SIZE", 9e9)])
+    _write_counters(tmp_path / "bench_WRITE_SIZE_counter_collection.csv",
+                    [(fwd, "WRITE_SIZE", 500.0), (bwd, "WRITE_SIZE", 9e9)])
+    _write_counters(tmp_path / "copy_FETCH_SIZE_counter_collection.csv", [(neg, "FETCH_SIZE", copy_kib / 2)])
+    _write_counters(tmp_path / "copy_WRITE_SIZE_counter_collection.csv", [(neg, "WRITE_SIZE", copy_kib)])
+    out = tmp_path / "traffic.json"
+    monkeypatch.setattr(bench, "traffic_path", lambda workload: str(out))
+    bench.write_traffic(argparse.Namespace(traffic_from=str(tmp_path), workload="attn_proj_4096"))
+    t = json.load(open(out))
+    assert t["fetch_kib_per_dispatch"] == 2000.0 and t["write_kib_per_dispatch"] == 500.0
+    assert t["copy_fetch_factor"] == 0.5 and t["copy_write_factor"] == 1.0
+    assert t["hbm_read_bytes_per_dispatch"] == 2000 * 1024 * 2
+    assert t["hbm_write_bytes_per_dispatch"] == 500 * 1024
+    assert t["kernel_source_hash"] == bench.kernel_source_hash()
+    # the stored figures are used only while the GEMM's sources are unchanged
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 16)
+    assert bench.load_traffic("attn_proj_4096") is None
+
+
+def test_missing_counters_are_an_error(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "traffic_path", lambda workload: str(tmp_path / "t.json"))
+    with pytest.raises(SystemExit):
+        bench.write_traffic(argparse.Namespace(traffic_from=str(tmp_path), workload="attn_proj_4096"))
