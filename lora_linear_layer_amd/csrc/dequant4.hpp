@@ -6,6 +6,7 @@
 // float32, then rounded to bf16 for a bf16 output.  HBM-bound.
 #pragma once
 #include "common.hpp"
+#include "stream_store.hpp"
 
 namespace lora {
 
@@ -37,12 +38,12 @@ __global__ __launch_bounds__(256) void dequant4_kernel(const uint8_t* __restrict
         }
         if constexpr (F32_OUT) {
             f32x4* o = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + (size_t)g * 8);
-            o[0] = f32x4{v[0], v[1], v[2], v[3]};
-            o[1] = f32x4{v[4], v[5], v[6], v[7]};
+            store_stream(o, f32x4{v[0], v[1], v[2], v[3]});
+            store_stream(o + 1, f32x4{v[4], v[5], v[6], v[7]});
         } else {
-            *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(out) + (size_t)g * 8) =
-                u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
-                      pack_bf16x2(v[6], v[7])};
+            store_stream(reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(out) + (size_t)g * 8),
+                         u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                               pack_bf16x2(v[6], v[7])});
         }
     };
     int g = (int)blockIdx.x * 256 + tid;

@@ -18,6 +18,7 @@
 #include <type_traits>
 
 #include "common.hpp"
+#include "stream_store.hpp"
 
 namespace lora {
 
@@ -131,12 +132,12 @@ __global__ __launch_bounds__(256) void lora_merge_kernel(const void* W, const vo
         for (int e = 0; e < 8; ++e) out[e] = wv[e] + scale * acc[i][e];
         if constexpr (F32) {
             float* const p = reinterpret_cast<float*>(Wout) + (size_t)n * K + k;
-            *reinterpret_cast<f32x4*>(p) = f32x4{out[0], out[1], out[2], out[3]};
-            *reinterpret_cast<f32x4*>(p + 4) = f32x4{out[4], out[5], out[6], out[7]};
+            store_stream(reinterpret_cast<f32x4*>(p), f32x4{out[0], out[1], out[2], out[3]});
+            store_stream(reinterpret_cast<f32x4*>(p + 4), f32x4{out[4], out[5], out[6], out[7]});
         } else {
-            *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(Wout) + (size_t)n * K + k) =
-                u32x4{pack_bf16x2(out[0], out[1]), pack_bf16x2(out[2], out[3]), pack_bf16x2(out[4], out[5]),
-                      pack_bf16x2(out[6], out[7])};
+            store_stream(reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(Wout) + (size_t)n * K + k),
+                         u32x4{pack_bf16x2(out[0], out[1]), pack_bf16x2(out[2], out[3]), pack_bf16x2(out[4], out[5]),
+                               pack_bf16x2(out[6], out[7])});
         }
     }
 }
