@@ -362,9 +362,11 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
     // directions (waves 0 .. F_LOADS - 1, one 1 KB load each per stage).
     // Forward: A [r][C] rows are contiguous in c: rows j of 64 c, swizzled like L.
     // Input gradient (r = 8 or 16): B [C][r] rows are contiguous in j and land
-    // as they are, [64 c][16 j] rows of 32 bytes; lane l of wave w carries row
-    // c = 32 w + l / 2, half l % 2 (j 8 h .. 8 h + 7; zeros when r = 8 and
-    // h = 1), and the fragments are gathered down the columns with
+    // as they are, [64 c][16 j] rows of 32 bytes, row c at physical row
+    // c ^ 4 (c & 8 ? 1 : 0) so that the two 16-lane groups of a transposing
+    // read (rows 8 apart) use different banks; lane l of wave w carries
+    // physical row 32 w + l / 2, half l % 2 (j 8 h .. 8 h + 7; zeros when r = 8
+    // and h = 1), and the fragments are gathered down the columns with
     // ds_read_b64_tr_b16 like the W tile.
     auto issue_f = [&](int kt) {
         if constexpr (!ZIN && !TRANS) {
@@ -377,7 +379,7 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
             const int c0 = kt * BK;
             uint8_t* const Fs = smem + (kt & 1) * SM::STAGE + 2 * TILE;
             if (wave < F_LOADS) {
-                const int c = wave * 32 + (lane >> 1), h = lane & 1;
+                const int c = (wave * 32 + (lane >> 1)) ^ (((lane >> 4) & 1) << 2), h = lane & 1;
                 const bool ok = c0 + c < C && 8 * h < r;
                 g2lds16<TRANS>(rsF, Fs + wave * 1024, ok ? (uint32_t)((c0 + c) * r + 8 * h) * 2u : kOOB);
             }
@@ -407,8 +409,9 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
             return lds_b128(Ls + 2 * TILE + jt * 2048 + chunk_of(kk));
         } else {
             const int rlo = kk * 32 + g4 * 8 + (l16 >> 2);            // as read_r, 32-byte rows
-            const uint8_t* const p = Ls + 2 * TILE + rlo * 32 + (l16 & 3) * 8;
-            return cat_tr(lds_tr4(p), lds_tr4(p + 4 * 32));
+            const int sw = (g4 & 1) << 2;                              // (rlo / 8) % 2 == g4 % 2
+            const uint8_t* const f = Ls + 2 * TILE + (l16 & 3) * 8;
+            return cat_tr(lds_tr4(f + (rlo ^ sw) * 32), lds_tr4(f + ((rlo + 4) ^ sw) * 32));
         }
     };
 
