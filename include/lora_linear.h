@@ -145,7 +145,9 @@ lora_status lora_dequant4(const uint8_t* Wq, const uint16_t* absmax, const float
  * the base weight, so that inference engines see a plain linear layer):
  *   W_out = W + sign * s * B A        sign = +1 merge, -1 unmerge; s = alpha / r
  * from desc (K, N, r, alpha, dtype; M is not used).  W, W_out [N, K], A [r, K],
- * B [N, r] in desc->dtype; float32 arithmetic, one rounding to the dtype.
+ * B [N, r] in desc->dtype; float32 arithmetic, one rounding to the dtype
+ * (bf16 with r >= 16 forms the rank-r sum on the matrix cores, float32
+ * accumulation; otherwise fused multiply-adds in increasing j).
  * W_out may be W itself (in place); otherwise its bytes must not overlap W, A
  * or B (LORA_ERR_INVALID_ARG).  Requires 1 <= r <= 128 and K % 8 == 0
  * (LORA_ERR_UNSUPPORTED); other invalid arguments as for the entry points above.

@@ -689,7 +689,21 @@ lora_status lora_merge(const lora_linear_desc* desc, const void* W, const void* 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const dim3 grid((unsigned)cdiv(d.K, kMergeCols), (unsigned)cdiv(d.N, kMergeRows));
     const float scale = (float)sign * (d.alpha / (float)d.r);
-    if (d.dtype == LORA_DTYPE_F32)
+    if (d.dtype == LORA_DTYPE_BF16 && d.r >= 16) {
+        // MFMA form: from r ~ 16 the rank-r sum costs the VALU form more than its 4 bytes per weight
+        const uint16_t *W16 = static_cast<const uint16_t*>(W), *A16 = static_cast<const uint16_t*>(A),
+                       *B16 = static_cast<const uint16_t*>(B);
+        uint16_t* const O16 = static_cast<uint16_t*>(W_out);
+#define MERGE_MFMA(RP) hipLaunchKernelGGL((lora_merge_mfma<RP>), grid, dim3(256), 0, s, W16, A16, B16, O16, \
+                                          (int)d.N, (int)d.K, (int)d.r, scale)
+        switch ((d.r + 31) / 32) {
+            case 1: MERGE_MFMA(32); break;
+            case 2: MERGE_MFMA(64); break;
+            case 3: MERGE_MFMA(96); break;
+            default: MERGE_MFMA(128); break;
+        }
+#undef MERGE_MFMA
+    } else if (d.dtype == LORA_DTYPE_F32)
         hipLaunchKernelGGL((lora_merge_kernel<true>), grid, dim3(256), 0, s, W, A, B, W_out, (int)d.N, (int)d.K,
                            (int)d.r, scale);
     else

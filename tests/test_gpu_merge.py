@@ -49,7 +49,11 @@ def check_merge(got, inp, sh, dtype, sign):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("N,K,r", [(264, 392, 8), (33, 8, 1), (1000, 136, 100), (64, 4104, 128),
-                                   (4096, 4096, 8), (14336, 4096, 64)])
+                                   (4096, 4096, 8), (14336, 4096, 64),
+                                   # bf16 ranks r >= 16 take the MFMA form (B rows unaligned when r % 8 != 0):
+                                   # every rank padding (32, 64, 96, 128) with ragged rows and columns
+                                   (520, 264, 16), (1030, 96, 24), (200, 392, 32), (130, 72, 40),
+                                   (4100, 520, 96), (77, 8, 120), (300, 136, 17), (260, 200, 60)])
 @pytest.mark.parametrize("sign", [1, -1])
 def test_merge_parity(N, K, r, sign, dtype):
     sh, inp = merge_inputs(N, K, r, N + K + r)
