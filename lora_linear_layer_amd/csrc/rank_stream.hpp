@@ -11,8 +11,9 @@
 // item 2: only [M, r] intermediates are formed).
 //
 // Both are HBM-bound.  A rank_stream workgroup (4 waves) owns one 128-wide
-// tile of c and a chunk of the tokens m, walks the chunk in 128 x 128 tiles of
-// Y that arrive through a double-buffered LDS ring straight from global memory
+// tile of c and a chunk of the tokens m, walks the chunk in steps of TM x 128 of
+// Y (TM = 128 tokens for r <= 16, else 64) that arrive through a
+// double-buffered LDS ring straight from global memory
 // (buffer_load ... lds, rows of 256 bytes, 16-byte chunk ch of row x at
 // ch ^ (x & 7)), and writes a float32 partial per chunk; grad_final adds the
 // chunks in a fixed order, so results are bitwise reproducible.  MFMA
@@ -46,13 +47,17 @@ struct RankArgs {
     int n_chunk;
 };
 
+// A ring step covers TM tokens: 128 for r <= 16, 64 above, where the
+// Z2 hi / lo tiles grow with the rank and 128-token stages would leave one
+// workgroup (one stage in flight) per CU; with 64-token steps two or three fit.
 template <int RPAD>
 struct RankSmem {
-    static constexpr int YT = kRT * kRT * 2;          // 32 KB per Y tile
-    static constexpr int SIDE = RPAD * kRT * 2;       // one of the Z2 hi / lo tiles
+    static constexpr int TM = RPAD <= 16 ? kRT : kRT / 2;
+    static constexpr int YT = TM * kRT * 2;           // Y tile: TM rows of 256 bytes
+    static constexpr int SIDE = RPAD * TM * 2;        // one of the Z2 hi / lo tiles: RPAD rows of 2 TM bytes
     static constexpr int STAGE = YT + 2 * SIDE;
     static constexpr int TOTAL = 2 * STAGE;
-    static_assert(RPAD <= 64 && TOTAL <= 160 * 1024, "LDS budget");
+    static_assert(RPAD <= 64 && TOTAL <= 80 * 1024, "LDS budget: two workgroups per CU");
 };
 
 // Handles rank columns j0 .. j0 + min(r - j0, RPAD) - 1.
@@ -60,6 +65,7 @@ template <int RPAD>
 __global__ __launch_bounds__(256) void rank_stream(const RankArgs a) {
     using SM = RankSmem<RPAD>;
     constexpr int JT = RPAD / 16;
+    constexpr int TM = SM::TM;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[SM::TOTAL];
 
     const int pidx = blockIdx.z;
@@ -71,40 +77,47 @@ __global__ __launch_bounds__(256) void rank_stream(const RankArgs a) {
     const int l16 = lane & 15, g4 = lane >> 4;
     const int M = a.M, C = pr.C, r = a.r, j0 = a.j0;
     const int rl = min(r - j0, RPAD);                  // rank columns of this launch
-    // the output tile c0 = o0; token tiles [t_begin, t_end)
+    // the output tile c0 = o0; token tiles [t_begin, t_end) of 128, walked in
+    // steps of TM tokens: [s_begin, s_end)
     const int o0 = blockIdx.x * kRT;
     const int n_ct = (M + kRT - 1) / kRT;
     const int t_begin = blockIdx.y * a.chunk_tiles;
     const int t_end = min(n_ct, t_begin + a.chunk_tiles);
+    const int s_begin = t_begin * (kRT / TM);
+    const int s_end = min((M + TM - 1) / TM, t_end * (kRT / TM));
 
-    // Y tile of contraction tile t: rows m, columns c (256 bytes per row); wave w
-    // issues loads b = 8 w .. 8 w + 7, each 4 rows: row = 4 b + lane / 16
-    const int ld_row0 = wave * 32 + (lane >> 4);
+    // Y tile of step t: TM rows m, columns c (256 bytes per row); wave w issues
+    // loads b = TM/16 w .. + TM/16 - 1, each 4 rows: row = 4 b + lane / 16
+    constexpr int YLW = TM / 16;                      // Y loads per wave
     auto issue_y = [&](int t, uint8_t* Ys) {
-        const int m0 = t * kRT;
+        const int m0 = t * TM;
         const int c0 = o0;
         const __amdgpu_buffer_rsrc_t rs =
-            make_rsrc(pr.Y + (size_t)m0 * C + c0, (uint64_t)(min(M - m0, kRT) - 1) * C * 2 + (uint64_t)(C - c0) * 2);
+            make_rsrc(pr.Y + (size_t)m0 * C + c0, (uint64_t)(min(M - m0, TM) - 1) * C * 2 + (uint64_t)(C - c0) * 2);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int row = ld_row0 + 4 * i;
+        for (int i = 0; i < YLW; ++i) {
+            const int b = wave * YLW + i;
+            const int row = 4 * b + (lane >> 4);
             const int ch = ((lane & 15) ^ (row & 7)) * 8;
-            g2lds16<true>(rs, Ys + (wave * 8 + i) * 1024, (c0 + ch < C) ? (uint32_t)(row * C + ch) * 2u : kOOB);
+            g2lds16<true>(rs, Ys + b * 1024, (c0 + ch < C) ? (uint32_t)(row * C + ch) * 2u : kOOB);
         }
     };
-    // side tile(s) of contraction tile t: rows j0 .. j0 + RPAD - 1 of S (and S_lo),
-    // columns t * 128 .. + 127, same row layout as the Y tile; wave w issues
-    // loads b = RPAD/16 * w .. of each plane, each 4 rows: row = 4 b + lane / 16
-    constexpr int SLW = RPAD / 16;                    // side loads per wave per plane
+    // side tile(s) of step t: rows j0 .. j0 + RPAD - 1 of S (and S_lo), columns
+    // t TM .. + TM - 1, rows of 2 TM bytes whose 16-byte chunk ch of row x sits
+    // at ch ^ (x & 7); wave w issues loads b = SLW w .. of each plane, each
+    // SRL rows: row = SRL b + lane / (TM / 8)
+    constexpr int SLW = RPAD * TM / 2048;             // side loads per wave per plane
+    constexpr int SRL = 1024 / (2 * TM);              // side rows per 1 KB load
+    static_assert(SLW >= 1, "side tile smaller than one load per wave");
     const __amdgpu_buffer_rsrc_t rsS = make_rsrc(pr.S, (uint64_t)r * pr.s_len * 2);
     const __amdgpu_buffer_rsrc_t rsSl = make_rsrc(pr.S_lo, (uint64_t)r * pr.s_len * 2);
     auto issue_side = [&](int t, uint8_t* Ss) {
-        const int col0 = t * kRT;
+        const int col0 = t * TM;
 #pragma unroll
         for (int i = 0; i < SLW; ++i) {
             const int b = wave * SLW + i;
-            const int row = 4 * b + (lane >> 4);
-            const int ch = ((lane & 15) ^ (row & 7)) * 8;
+            const int row = SRL * b + lane / (TM / 8);
+            const int ch = ((lane % (TM / 8)) ^ (row & 7)) * 8;
             const uint32_t off = (row < rl && col0 + ch < pr.s_len)
                                      ? (uint32_t)((size_t)(j0 + row) * pr.s_len + col0 + ch) * 2u : kOOB;
             g2lds16<true>(rsS, Ss + b * 1024, off);
@@ -116,17 +129,17 @@ __global__ __launch_bounds__(256) void rank_stream(const RankArgs a) {
 #pragma unroll
     for (int jt = 0; jt < JT; ++jt) acc[jt][0] = acc[jt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // prologue: tile t_begin in slot 0
-    if (t_begin < t_end) {
-        issue_y(t_begin, smem);
-        issue_side(t_begin, smem + SM::YT);
+    // prologue: step s_begin in slot 0
+    if (s_begin < s_end) {
+        issue_y(s_begin, smem);
+        issue_side(s_begin, smem + SM::YT);
     }
     vmcnt_le<0>();
     __syncthreads();
-    for (int t = t_begin; t < t_end; ++t) {
-        uint8_t* const cur = smem + ((t - t_begin) & 1) * SM::STAGE;
-        uint8_t* const nxt = smem + ((t - t_begin + 1) & 1) * SM::STAGE;
-        const bool more = t + 1 < t_end;
+    for (int t = s_begin; t < s_end; ++t) {
+        uint8_t* const cur = smem + ((t - s_begin) & 1) * SM::STAGE;
+        uint8_t* const nxt = smem + ((t - s_begin + 1) & 1) * SM::STAGE;
+        const bool more = t + 1 < s_end;
         if (more) {
             issue_y(t + 1, nxt);
             issue_side(t + 1, nxt + SM::YT);
@@ -135,7 +148,7 @@ __global__ __launch_bounds__(256) void rank_stream(const RankArgs a) {
         const uint8_t* const Ss = cur + SM::YT;
         // wave w owns output blocks 2w and 2w + 1 (16 rows each) of the 128-wide tile
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
+        for (int kk = 0; kk < TM / 32; ++kk) {
             // B operand: Y^T, columns c = l16 of block, 8 consecutive m from rows kk*32 + 8 g4 ..
             bf16x8 yf[2];
 #pragma unroll
@@ -150,7 +163,7 @@ __global__ __launch_bounds__(256) void rank_stream(const RankArgs a) {
 #pragma unroll
             for (int jt = 0; jt < JT; ++jt) {
                 const int j = jt * 16 + l16;
-                const int off = j * 256 + (((kk * 4 + g4) ^ (j & 7)) << 4);
+                const int off = j * (2 * TM) + (((kk * 4 + g4) ^ (j & 7)) << 4);
                 const bf16x8 sa = lds_b128(Ss + off);
                 const bf16x8 sl = lds_b128(Ss + SM::SIDE + off);
 #pragma unroll
