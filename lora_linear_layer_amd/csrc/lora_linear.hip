@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -90,15 +91,35 @@ struct RankSplit {
     int chunk_tiles = 1, n_chunk = 1;
 };
 
-RankSplit rank_split(int64_t out_tiles, int64_t n_ct) {
-    // about 512 workgroups (two per CU), each walking at least two contraction
-    // tiles so that its double-buffered LDS ring has something to overlap
-    RankSplit sp;
-    int64_t n = cdiv(512, std::max<int64_t>(out_tiles, 1));
-    n = std::max<int64_t>(1, std::min<int64_t>(n, cdiv(n_ct, 2)));
-    sp.chunk_tiles = (int)cdiv(n_ct, n);
-    sp.n_chunk = (int)cdiv(n_ct, sp.chunk_tiles);
-    return sp;
+constexpr int64_t kCUs = 256;          // compute units of an MI355X
+
+RankSplit rank_split(int64_t out_tiles, int64_t n_ct, int64_t r) {
+    // Workgroups run in rounds of two per CU (rank_stream<32> fits three, but
+    // counting them made its chunks shorter and the launch slower: 4096 tokens,
+    // 4096 + 4096 columns, r = 32, 17.3 -> 18.9 us), so the streaming takes about
+    // rounds x (contraction tiles per chunk) x (one 32 KB Y tile per slot);
+    // each chunk adds a float32 partial of 128 r floats per output tile,
+    // written here and read again by grad_final.  The chunk count with the
+    // least bytes-equivalent cost wins, the fewest chunks on a tie.  Each chunk
+    // walks at least two contraction tiles so that the double-buffered LDS
+    // ring has something to overlap; at most 4 x 512 chunks are tried.
+    // (Rounding the chunk count up to fill 512 slots exactly left e.g. 576
+    // workgroups: a second round of 64.)
+    RankSplit best;
+    int64_t best_cost = INT64_MAX;
+    const int64_t slots = 2 * kCUs, nmax = std::max<int64_t>(1, std::min<int64_t>(cdiv(n_ct, 2), 4 * slots));
+    const int64_t tiles = std::max<int64_t>(out_tiles, 1);
+    for (int64_t n = 1; n <= nmax; ++n) {
+        const int64_t chunk = cdiv(n_ct, n), nc = cdiv(n_ct, chunk);
+        const int64_t cost = cdiv(tiles * nc, slots) * chunk * (int64_t)(kRT * kRT * 2) * slots +
+                             nc * tiles * kRT * r * 8;
+        if (cost < best_cost) {
+            best_cost = cost;
+            best.chunk_tiles = (int)chunk;
+            best.n_chunk = (int)nc;
+        }
+    }
+    return best;
 }
 
 // Splits of the three streamed products of one descriptor.
@@ -108,7 +129,9 @@ int z_chunks(const lora_linear_desc& d, int64_t C) {
     const int64_t rows = cdiv(d.M, 128);
     return (int)std::max<int64_t>(1, std::min<int64_t>(cdiv(256, rows), cdiv(C, 256)));
 }
-RankSplit split_g(const lora_linear_desc& d) { return rank_split(cdiv(d.K, kRT) + cdiv(d.N, kRT), cdiv(d.M, kRT)); }
+RankSplit split_g(const lora_linear_desc& d) {
+    return rank_split(cdiv(d.K, kRT) + cdiv(d.N, kRT), cdiv(d.M, kRT), d.r);
+}
 
 // Workspace layout for one descriptor (offsets in bytes from ws).
 struct Plan {
