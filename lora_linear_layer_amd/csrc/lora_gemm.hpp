@@ -299,10 +299,18 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
 #pragma unroll
         for (int u = 0; u < QU; ++u) {
             const int unit = tid + u * NT;
+            // code dword d = 8 weights = 16-byte output chunk d.  Input gradient:
+            // lanes with pp & 4 take their chunks in the order 1, 0, 3, 2, so that
+            // each 16-byte store instruction of a row's 8 lanes covers both
+            // halves of 4 slots (8 distinct bank groups) instead of one half of
+            // 8 slots, of which the swizzle leaves 4 distinct
+            u32x4 qv = qreg[u];
+            const int sh = TRANS ? (unit >> 2) & 1 : 0;
+            if (TRANS && sh) qv = u32x4{qv[1], qv[0], qv[3], qv[2]};
             u32x4 outv[4];
 #pragma unroll
             for (int b = 0; b < 16; ++b) {   // byte b holds weights 2b (low nibble) and 2b + 1
-                const uint32_t byte = (qreg[u][b >> 2] >> (8 * (b & 3))) & 0xFFu;
+                const uint32_t byte = (qv[b >> 2] >> (8 * (b & 3))) & 0xFFu;
                 const float lo = lut[byte & 15u] * am_reg[u], hi = lut[byte >> 4] * am_reg[u];
                 outv[b >> 2][b & 3] = pack_bf16x2(lo, hi);
             }
@@ -314,9 +322,10 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
             } else {                         // row c, 32-byte slots 2 pp, 2 pp + 1 (swizzled by sw512)
                 const int c = unit >> 3, pp = unit & 7;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
+                for (int i = 0; i < 4; ++i) {   // outv[i] is chunk i ^ sh: slot 2 pp + i / 2, half (i & 1) ^ sh
                     const int slot = 2 * pp + (i >> 1);
-                    *reinterpret_cast<u32x4*>(Rs + c * 512 + ((slot ^ sw512(c)) << 5) + (i & 1) * 16) = outv[i];
+                    *reinterpret_cast<u32x4*>(Rs + c * 512 + ((slot ^ sw512(c)) << 5) + ((i & 1) ^ sh) * 16) =
+                        outv[i];
                 }
             }
         }
