@@ -15,7 +15,7 @@
 // Y (TM = 128 tokens for r <= 16, else 64) that arrive through a
 // double-buffered LDS ring straight from global memory
 // (buffer_load ... lds, rows of 256 bytes, 16-byte chunk ch of row x at
-// ch ^ (x & 7)), and writes a float32 partial per chunk; grad_final adds the
+// ch ^ y_swz(x)), and writes a float32 partial per chunk; grad_final adds the
 // chunks in a fixed order, so results are bitwise reproducible.  MFMA
 // 16x16x32 bf16 with float32 accumulation; Y^T fragments are gathered with
 // ds_read_b64_tr_b16.  The rank-side operand arrives the same way, as the two
@@ -60,6 +60,23 @@ struct RankSmem {
     static_assert(RPAD <= 64 && TOTAL <= 80 * 1024, "LDS budget: two workgroups per CU");
 };
 
+// LDS chunk swizzles (16-byte chunk ch of a row stored at ch ^ swz(row)),
+// chosen so that the fragment reads hit distinct banks:
+//  - Y rows (256 bytes): one transposing read's 32 lanes of a bank window read
+//    rows m0 + y and m0 + 8 + y (y < 4), two chunks of each; row bits 0-1 and 3
+//    spread them over all 16 chunks.  (row & 7 left rows 8 apart on the same
+//    chunks: 4-way conflicts.)
+//  - side rows of 2 TM bytes: one 16-byte read's 16 lanes read rows j .. j + 15
+//    at one chunk; 256-byte rows use j & 15, 128-byte rows (two per bank window)
+//    (j >> 1) & 7.  (j & 7 paired rows 8 apart: 2-way.)
+__device__ __forceinline__ int y_swz(int row) { return ((row & 3) << 1) | (((row >> 3) & 1) << 3); }
+template <int TM>
+__device__ __forceinline__ int side_swz(int row) {
+    static_assert(TM == 128 || TM == 64, "side rows of 256 or 128 bytes");
+    if constexpr (TM == 128) return row & 15;
+    else return (row >> 1) & 7;
+}
+
 // Handles rank columns j0 .. j0 + min(r - j0, RPAD) - 1.
 template <int RPAD>
 __global__ __launch_bounds__(256) void rank_stream(const RankArgs a) {
@@ -98,13 +115,13 @@ __global__ __launch_bounds__(256) void rank_stream(const RankArgs a) {
         for (int i = 0; i < YLW; ++i) {
             const int b = wave * YLW + i;
             const int row = 4 * b + (lane >> 4);
-            const int ch = ((lane & 15) ^ (row & 7)) * 8;
+            const int ch = ((lane & 15) ^ y_swz(row)) * 8;
             g2lds16<true>(rs, Ys + b * 1024, (c0 + ch < C) ? (uint32_t)(row * C + ch) * 2u : kOOB);
         }
     };
     // side tile(s) of step t: rows j0 .. j0 + RPAD - 1 of S (and S_lo), columns
     // t TM .. + TM - 1, rows of 2 TM bytes whose 16-byte chunk ch of row x sits
-    // at ch ^ (x & 7); wave w issues loads b = SLW w .. of each plane, each
+    // at ch ^ side_swz(x); wave w issues loads b = SLW w .. of each plane, each
     // SRL rows: row = SRL b + lane / (TM / 8)
     constexpr int SLW = RPAD * TM / 2048;             // side loads per wave per plane
     constexpr int SRL = 1024 / (2 * TM);              // side rows per 1 KB load
@@ -117,7 +134,7 @@ __global__ __launch_bounds__(256) void rank_stream(const RankArgs a) {
         for (int i = 0; i < SLW; ++i) {
             const int b = wave * SLW + i;
             const int row = SRL * b + lane / (TM / 8);
-            const int ch = ((lane % (TM / 8)) ^ (row & 7)) * 8;
+            const int ch = ((lane % (TM / 8)) ^ side_swz<TM>(row)) * 8;
             const uint32_t off = (row < rl && col0 + ch < pr.s_len)
                                      ? (uint32_t)((size_t)(j0 + row) * pr.s_len + col0 + ch) * 2u : kOOB;
             g2lds16<true>(rsS, Ss + b * 1024, off);
@@ -156,14 +173,14 @@ __global__ __launch_bounds__(256) void rank_stream(const RankArgs a) {
                 const int c = (2 * wave + z) * 16 + (l16 & 3) * 4;
                 const int mlo = kk * 32 + g4 * 8 + (l16 >> 2);
                 const int mhi = mlo + 4;
-                const i16x4 lo = lds_tr4(Ys + mlo * 256 + ((((c >> 3) ^ (mlo & 7))) << 4) + (c & 7) * 2);
-                const i16x4 hi = lds_tr4(Ys + mhi * 256 + ((((c >> 3) ^ (mhi & 7))) << 4) + (c & 7) * 2);
+                const i16x4 lo = lds_tr4(Ys + mlo * 256 + (((c >> 3) ^ y_swz(mlo)) << 4) + (c & 7) * 2);
+                const i16x4 hi = lds_tr4(Ys + mhi * 256 + (((c >> 3) ^ y_swz(mhi)) << 4) + (c & 7) * 2);
                 yf[z] = cat_tr(lo, hi);
             }
 #pragma unroll
             for (int jt = 0; jt < JT; ++jt) {
                 const int j = jt * 16 + l16;
-                const int off = j * (2 * TM) + (((kk * 4 + g4) ^ (j & 7)) << 4);
+                const int off = j * (2 * TM) + (((kk * 4 + g4) ^ side_swz<TM>(j)) << 4);
                 const bf16x8 sa = lds_b128(Ss + off);
                 const bf16x8 sl = lds_b128(Ss + SM::SIDE + off);
 #pragma unroll
