@@ -3,24 +3,29 @@
 
 One step = the whole hot path over one batch: the fused forward
 (H = X W^T + s (X A^T) B^T, U saved) followed by the backward (dX, dA, dB),
-for every linear of the workload (backward in reverse order).  Inputs are
-resident in HBM before timing starts; several input sets are rotated so the
-256 MB Infinity Cache cannot serve the operands of one step from the previous
-one (cold operands, as in a training step where W was last touched a layer
-stack ago).
+for every linear of the workload (forwards in order, backwards in reverse,
+one shared workspace).  Inputs are resident in HBM before timing starts;
+several input sets are rotated so the 256 MB Infinity Cache cannot serve the
+operands of one step from the previous one (cold operands, as in a training
+step where W was last touched a layer stack ago).
 
-Prints one JSON line.  Timing: W warm-up steps, then K timed steps between
-device synchronisations, with HIP events recorded on the stream the library
-launches on.  For a rank <= 16 layer the forward call is exactly one kernel
-(the fused GEMM), so its event pair times that kernel alone: that is the
-roofline figure.  The CPU baseline times the float64 oracle on a bounded
-sample of the same workload on the host cores.
+Prints one JSON line.  Timing passes, all on the stream the library launches on:
+  1. the timed region: W warm-up steps, then K steps between two HIP events,
+     device-synchronised on both sides, nothing else inside (`value`);
+  2. the same K steps with one HIP event at every step boundary: the spread of
+     the step time (p10 / p50 / p90);
+  3. the same K steps with HIP events around every kernel the library
+     enqueues (through its launch observer): per-kernel mean durations, from
+     which the roofline entries of the GEMMs are computed.  The dominant
+     kernel (`roofline`) is the GEMM with the largest measured time per step.
+The CPU baseline times the float64 oracle on a bounded sample of the same
+workload on the host cores.
 
 Extra modes (used to produce the committed counter summaries):
   --copy-calibration    run a plain device copy of known size (for scaling
                         the FETCH_SIZE / WRITE_SIZE counters)
   --traffic-from DIR    read rocprofv3 --pmc CSVs from DIR and write the
-                        measured HBM traffic of the dominant kernel to
+                        measured HBM traffic of both GEMMs to
                         profiles/traffic_<workload>.json
 """
 from __future__ import annotations
@@ -40,14 +45,17 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBPS = 8000.0             # MI355X HBM3E (published)
 DEQUANT_SHAPE = (28672, 8192)      # the 4-bit layer's frozen weight, d_out x d_in
-PEAK_HBM_GBS = 8000.0
 METRIC = "fused LoRA linear fwd+bwd TFLOP/s and tokens/s; % bf16 MFMA peak (1 GPU)"
 COPY_BYTES = 256 << 20             # calibration copy: 256 MiB read + 256 MiB written
-# the sources of the kernel whose HBM traffic the counters measured (the fused GEMM)
-KERNEL_SOURCES = ("lora_linear_layer_amd/csrc/lora_gemm.hpp", "lora_linear_layer_amd/csrc/common.hpp")
+# the sources of the kernels whose HBM traffic the counters measured (the fused GEMMs)
+KERNEL_SOURCES = ("lora_linear_layer_amd/csrc/lora_gemm.hpp", "lora_linear_layer_amd/csrc/common.hpp",
+                  "lora_linear_layer_amd/csrc/ranges.hpp")
+GEMM_FWD, GEMM_DX = "lora_gemm forward", "lora_gemm dX"
+# linears that read the same input (decoder layer): q/k/v share X, gate/up share X
+SHARED_INPUT = {"q": "qkv", "k": "qkv", "v": "qkv", "gate": "gu", "up": "gu"}
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
@@ -62,7 +70,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle time for the CPU baseline")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--traffic-from", default=None)
-    return ap.parse_args()
+    return ap.parse_args(argv)
 
 
 def kernel_source_hash() -> str:
@@ -73,12 +81,16 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+# ------------------------------------------------------------------ counts
+def w_bytes(l) -> int:
+    """The frozen weight once: bf16, or 4-bit codes plus one fp16 absmax per 64 weights."""
+    return l.N * l.K // 2 + 2 * (l.N * l.K // 64) if l.quant4 else 2 * l.N * l.K
+
+
 def fwd_bytes(l) -> int:
-    """HBM bytes a forward launch must move once: X and H in bf16, W in bf16
-    or as 4-bit codes plus one fp16 absmax per 64 weights, A, B and the saved
-    U (float32)."""
-    w = l.N * l.K // 2 + 2 * (l.N * l.K // 64) if l.quant4 else 2 * l.N * l.K
-    return 2 * l.M * l.K + w + 2 * l.M * l.N + 2 * l.r * (l.K + l.N) + 4 * l.M * l.r
+    """HBM bytes a forward launch must move once: X and H in bf16, W, A, B and
+    the saved U (float32)."""
+    return 2 * l.M * l.K + w_bytes(l) + 2 * l.M * l.N + 2 * l.r * (l.K + l.N) + 4 * l.M * l.r
 
 
 def fwd_flops(l):
@@ -89,6 +101,42 @@ def bwd_flops(l):
     return 2 * l.M * l.N * l.K + 4 * l.M * l.r * (l.K + l.N)
 
 
+def in_tile(l, split: bool, dx: bool) -> bool:
+    """Whether the GEMM forms its rank-r product itself (the library's rule:
+    r <= 16, 16-bit W, whole tiles; the input gradient also needs r % 8 == 0)."""
+    return l.r <= 16 and not l.quant4 and not split and (not dx or l.r % 8 == 0)
+
+
+def gemm_flops(l, label: str) -> int:
+    """Algorithmic FLOPs of one launch of a fused GEMM: the dense product,
+    the rank-r term of the epilogue and, when formed in the tile, the rank-r
+    product U = X A^T (forward) or V = dY B (input gradient)."""
+    dx = label.startswith(GEMM_DX)
+    P, Q, C = (l.M, l.K, l.N) if dx else (l.M, l.N, l.K)
+    f = 2 * P * Q * C + 2 * P * Q * l.r
+    if in_tile(l, "(split)" in label, dx):
+        f += 2 * P * l.r * C
+    return f
+
+
+def gemm_bytes(l, label: str) -> int:
+    """Algorithmic HBM bytes of one launch of a fused GEMM, each operand once.
+    Forward: X, W, A, B, H, and U (written, or read when precomputed).
+    Input gradient: dY, W, A, B, dX, and U read; in the in-tile form also the
+    four bf16 rank planes (V^T and U^T, hi and lo, r x M each) it writes,
+    otherwise V read."""
+    M, K, N, r = l.M, l.K, l.N, l.r
+    if not label.startswith(GEMM_DX):
+        return fwd_bytes(l)
+    b = 2 * M * N + w_bytes(l) + 2 * M * K + 2 * r * (K + N) + 4 * M * r
+    if in_tile(l, "(split)" in label, True):
+        b += 4 * 2 * r * (-(-M // 128) * 128)
+    else:
+        b += 4 * M * r
+    return b
+
+
+# ------------------------------------------------------------------ oracle baseline
 def cpu_baseline(wl, min_seconds):
     """The float64 oracle's forward + backward on the first linear of the
     workload (all of its tokens), repeated until min_seconds have passed."""
@@ -124,23 +172,26 @@ def cpu_baseline(wl, min_seconds):
                       + ("; 4-bit weights dequantised once beforehand, not timed" if sh.quant4 else "")}
 
 
+# ------------------------------------------------------------------ traffic counters
 def traffic_path(workload):
     return os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
 
 
 def load_traffic(workload):
+    """Measured HBM bytes per dispatch of each GEMM, {label: bytes}, or None
+    when no counters were taken for the current kernel sources."""
     p = traffic_path(workload)
     if not os.path.exists(p):
         return None
     t = json.load(open(p))
     if t.get("kernel_source_hash") != kernel_source_hash():
         return None          # the kernels changed since the counters were taken
-    return t
+    return {k: v["hbm_bytes_per_dispatch"] for k, v in t.get("kernels", {}).items()}
 
 
 def write_traffic(args):
-    """Mean FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the dominant kernel and
-    of the calibration copy, from rocprofv3 --pmc counter_collection CSVs."""
+    """Mean FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of both GEMMs and of the
+    calibration copy, from rocprofv3 --pmc counter_collection CSVs."""
     def mean_counter(prefix, counter, pred):
         vals = []
         for f in glob.glob(os.path.join(args.traffic_from, prefix + "*counter_collection.csv")):
@@ -149,28 +200,122 @@ def write_traffic(args):
                     vals.append(float(row["Counter_Value"]))
         return sum(vals) / len(vals) if vals else None
 
-    # bench_* files: the forward GEMM (first template argument false); copy_* files: the neg kernel
-    is_gemm = lambda k: "lora_gemm" in k and k.split("<", 1)[-1].split(",")[0].strip() == "false"
+    # bench_* files: the GEMMs (first template argument false: forward, true: input
+    # gradient); copy_* files: the neg kernel
+    def is_gemm(trans):
+        def pred(k):
+            if "lora_gemm<" not in k:
+                return False
+            targs = [a.strip() for a in k.split("lora_gemm<", 1)[1].split(">", 1)[0].split(",")]
+            return targs[0] == trans
+        return pred
     is_copy = lambda k: "neg_kernel" in k
-    fetch_k, write_k = mean_counter("bench_", "FETCH_SIZE", is_gemm), mean_counter("bench_", "WRITE_SIZE", is_gemm)
     cfetch_k, cwrite_k = mean_counter("copy_", "FETCH_SIZE", is_copy), mean_counter("copy_", "WRITE_SIZE", is_copy)
-    if None in (fetch_k, write_k, cfetch_k, cwrite_k):
-        raise SystemExit("missing counters: need FETCH_SIZE and WRITE_SIZE runs of both the bench and the copy")
+    if None in (cfetch_k, cwrite_k):
+        raise SystemExit("missing counters: need FETCH_SIZE and WRITE_SIZE runs of the copy")
     f_fac = cfetch_k * 1024 / COPY_BYTES
     w_fac = cwrite_k * 1024 / COPY_BYTES
-    out = {"workload": args.workload, "kernel": "lora_gemm forward", "kernel_source_hash": kernel_source_hash(),
-           "fetch_kib_per_dispatch": fetch_k, "write_kib_per_dispatch": write_k,
+    kernels = {}
+    for label, trans in ((GEMM_FWD, "false"), (GEMM_DX, "true")):
+        fetch_k = mean_counter("bench_", "FETCH_SIZE", is_gemm(trans))
+        write_k = mean_counter("bench_", "WRITE_SIZE", is_gemm(trans))
+        if None in (fetch_k, write_k):
+            continue
+        kernels[label] = {"fetch_kib_per_dispatch": fetch_k, "write_kib_per_dispatch": write_k,
+                          "hbm_read_bytes_per_dispatch": round(fetch_k * 1024 / f_fac),
+                          "hbm_write_bytes_per_dispatch": round(write_k * 1024 / w_fac),
+                          "hbm_bytes_per_dispatch": round(fetch_k * 1024 / f_fac + write_k * 1024 / w_fac)}
+    if not kernels:
+        raise SystemExit("missing counters: need FETCH_SIZE and WRITE_SIZE runs of the bench")
+    out = {"workload": args.workload, "kernel_source_hash": kernel_source_hash(),
            "copy_kib_fetch": cfetch_k, "copy_kib_write": cwrite_k, "copy_bytes": COPY_BYTES,
-           "copy_fetch_factor": round(f_fac, 4), "copy_write_factor": round(w_fac, 4),
-           "hbm_read_bytes_per_dispatch": round(fetch_k * 1024 / f_fac),
-           "hbm_write_bytes_per_dispatch": round(write_k * 1024 / w_fac),
-           "hbm_bytes_per_dispatch": round(fetch_k * 1024 / f_fac + write_k * 1024 / w_fac)}
+           "copy_fetch_factor": round(f_fac, 4), "copy_write_factor": round(w_fac, 4), "kernels": kernels}
     os.makedirs(os.path.dirname(traffic_path(args.workload)), exist_ok=True)
     json.dump(out, open(traffic_path(args.workload), "w"), indent=1)
     print(json.dumps(out))
 
 
-def dequant_rate(lla, workloads, torch, dev, stream, reps=20):
+# ------------------------------------------------------------------ the step
+def share_inputs(wl, layer):
+    """Linears that read the same activations get the same X tensor: the first
+    member of each group (q of q/k/v, gate of gate/up) provides it."""
+    first = {}
+    for sh, d in zip(wl.linears, layer):
+        group = SHARED_INPUT.get(sh.name.split("_")[-1])
+        if group is None:
+            continue
+        if group in first:
+            d["X"] = first[group]
+        else:
+            first[group] = d["X"]
+    return layer
+
+
+def add_outputs(lla, torch, wl, layer, dev):
+    """Descriptor and output buffers (H, U, dX, dA, dB) for each linear."""
+    for sh, d in zip(wl.linears, layer):
+        d["desc"] = lla.Desc(sh.M, sh.K, sh.N, sh.r, sh.alpha)
+        d["H"] = torch.empty((sh.M, sh.N), dtype=torch.bfloat16, device=dev)
+        d["U"] = torch.empty((sh.M, sh.r), dtype=torch.float32, device=dev)
+        d["dX"] = torch.empty((sh.M, sh.K), dtype=torch.bfloat16, device=dev)
+        d["dA"] = torch.empty((sh.r, sh.K), dtype=torch.bfloat16, device=dev)
+        d["dB"] = torch.empty((sh.N, sh.r), dtype=torch.bfloat16, device=dev)
+    return layer
+
+
+class Stepper:
+    """Runs one step of a workload through the C ABI: every linear's fused
+    forward in order, then every backward in reverse order, all on torch's
+    current stream, with one workspace sized for the largest descriptor
+    shared by all calls (and by all input sets)."""
+
+    def __init__(self, lla, torch, layers, dev):
+        self.lla = lla
+        self.ws_bytes = max(lla.lora_linear_workspace_size(d["desc"]) for layer in layers for d in layer)
+        self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=dev)
+        self.current = None          # index of the linear being run (for the per-kernel timing pass)
+
+    def fwd(self, d):
+        lla = self.lla
+        if "codes" in d:
+            lla.lora_qlinear_fwd(d["desc"], d["X"], d["codes"], d["absmax"], d["codebook"], d["A"], d["B"],
+                                 d["H"], d["U"], ws=self.ws, ws_bytes=self.ws_bytes)
+        else:
+            lla.lora_linear_fwd(d["desc"], d["X"], d["W"], d["A"], d["B"], d["H"], d["U"], ws=self.ws,
+                                ws_bytes=self.ws_bytes)
+
+    def bwd(self, d):
+        lla = self.lla
+        if "codes" in d:
+            lla.lora_qlinear_bwd(d["desc"], d["dY"], d["X"], d["codes"], d["absmax"], d["codebook"], d["A"],
+                                 d["B"], d["U"], d["dX"], d["dA"], d["dB"], ws=self.ws, ws_bytes=self.ws_bytes)
+        else:
+            lla.lora_linear_bwd(d["desc"], d["dY"], d["X"], d["W"], d["A"], d["B"], d["U"], d["dX"], d["dA"],
+                                d["dB"], ws=self.ws, ws_bytes=self.ws_bytes)
+
+    def step(self, layer):
+        for li, d in enumerate(layer):
+            self.current = li
+            self.fwd(d)
+        for li in reversed(range(len(layer))):
+            self.current = li
+            self.bwd(layer[li])
+
+
+# ------------------------------------------------------------------ stand-alone HBM kernels
+def event_time_us(torch, stream, run, reps=20):
+    for _ in range(3):
+        run()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record(stream)
+        run()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in ev) / reps * 1e3
+
+
+def dequant_rate(lla, workloads, torch, dev, stream):
     """The stand-alone 4-bit dequantisation (lora_dequant4, bf16 output) on the
     4-bit layer's weight shape: HIP events on the library's stream around each
     launch; bytes = codes (0.5 B) + fp16 absmax (2 B per 64) + bf16 out (2 B)
@@ -182,16 +327,8 @@ def dequant_rate(lla, workloads, torch, dev, stream, reps=20):
     absmax = (torch.rand((N, K // 64), device=dev, generator=g) * 0.08 + 0.01).to(torch.float16).view(torch.int16)
     cb = torch.from_numpy(workloads.codebook4_f32()).to(dev)
     out = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
-    run = lambda: lla.lora_dequant4(codes, absmax, cb, N, K, lla.LORA_DTYPE_BF16, out, stream=stream)
-    for _ in range(3):
-        run()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for a, b in ev:
-        a.record(stream)
-        run()
-        b.record(stream)
-    torch.cuda.synchronize()
-    us = sum(a.elapsed_time(b) for a, b in ev) / reps * 1e3
+    us = event_time_us(torch, stream,
+                       lambda: lla.lora_dequant4(codes, absmax, cb, N, K, lla.LORA_DTYPE_BF16, out, stream=stream))
     nbytes = N * K // 2 + 2 * (N * K // 64) + 2 * N * K
     gbps = nbytes / (us * 1e-6) / 1e9
     del codes, absmax, out
@@ -200,7 +337,7 @@ def dequant_rate(lla, workloads, torch, dev, stream, reps=20):
             "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4)}
 
 
-def merge_rate(lla, torch, dev, stream, l, reps=20):
+def merge_rate(lla, torch, dev, stream, l):
     """lora_merge (W_out = W + s B A, bf16, out of place) on the weight shape of
     linear l: HIP events on the library's stream around each launch; bytes =
     W read and W_out written once (2 + 2 bytes per weight) plus A and B."""
@@ -211,20 +348,11 @@ def merge_rate(lla, torch, dev, stream, l, reps=20):
     B = (torch.randn((l.N, l.r), device=dev, generator=g) * 0.02).to(torch.bfloat16)
     out = torch.empty_like(W)
     desc = lla.Desc(1, l.K, l.N, l.r, l.alpha)
-    run = lambda: lla.lora_merge(desc, W, A, B, out, 1, stream=stream)
-    for _ in range(3):
-        run()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for a, b in ev:
-        a.record(stream)
-        run()
-        b.record(stream)
-    torch.cuda.synchronize()
-    us = sum(a.elapsed_time(b) for a, b in ev) / reps * 1e3
+    us = event_time_us(torch, stream, lambda: lla.lora_merge(desc, W, A, B, out, 1, stream=stream))
     nbytes = 4 * l.N * l.K + 2 * l.r * (l.K + l.N)
     gbps = nbytes / (us * 1e-6) / 1e9
     del W, A, B, out
-    return {"kernel": "lora_merge_kernel (lora_merge, bf16)", "shape": [l.N, l.K, l.r], "bound": "hbm",
+    return {"kernel": "lora_merge (bf16)", "shape": [l.N, l.K, l.r], "bound": "hbm",
             "bytes_per_launch": nbytes, "avg_launch_us": round(us, 2), "achieved": round(gbps, 1),
             "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4)}
 
@@ -239,8 +367,37 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": COPY_BYTES}))
 
 
-def main():
-    args = parse()
+def percentile(vals, q):
+    v = sorted(vals)
+    if not v:
+        return None
+    x = (len(v) - 1) * q
+    lo, hi = int(x), min(int(x) + 1, len(v) - 1)
+    return v[lo] + (v[hi] - v[lo]) * (x - lo)
+
+
+def gemm_rooflines(wl, kernel_us, traffic):
+    """Roofline entries of the fused GEMMs from their measured mean durations
+    (kernel_us: {(linear index, label): [launch durations in us]})."""
+    out = []
+    for (li, label), durs in sorted(kernel_us.items()):
+        if not label.startswith("lora_gemm"):
+            continue
+        l = wl.linears[li]
+        us = sum(durs) / len(durs)
+        fl = gemm_flops(l, label)
+        ach = fl / (us * 1e-6) / 1e12
+        base = label.replace(" (split)", "")
+        tr = traffic.get(base) if (traffic and len(wl.linears) == 1) else None
+        out.append({"kernel": f"{label} ({l.name})", "bound": "mfma", "achieved": round(ach, 2),
+                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                    "traffic": tr, "avg_launch_us": round(us, 2), "launches_per_step": len(durs),
+                    "flops_per_launch": fl, "algorithmic_bytes_per_launch": gemm_bytes(l, label)})
+    return out
+
+
+def main(argv=None):
+    args = parse(argv)
     if args.gpus != 1:
         print(json.dumps({"error": "bench.py runs on exactly one GPU; --gpus must be 1 "
                                    "(data-parallel sharding across GPUs is not built)"}))
@@ -265,88 +422,38 @@ def main():
     sets = []
     for si in range(args.input_sets):
         layer = []
-        shared_x = {}
-        for li, sh in enumerate(wl.linears):
+        for sh in wl.linears:
             d = workloads.device_inputs_torch(sh, dev, torch.bfloat16, seed=sh.seed * 100 + si)
             if sh.quant4:
                 d.update(workloads.quantize4_torch(d.pop("W").float()))
-            # q/k/v share one input, gate/up share one input (decoder layer)
-            key = sh.name.split("_")[-1]
-            group = {"q": "qkv", "k": "qkv", "v": "qkv", "gate": "gu", "up": "gu"}.get(key)
-            if group:
-                if group in shared_x:
-                    d["X"] = shared_x[group]
-                else:
-                    shared_x[group] = d["X"]
-            desc = lla.Desc(sh.M, sh.K, sh.N, sh.r, sh.alpha)
-            d["desc"] = desc
-            d["H"] = torch.empty((sh.M, sh.N), dtype=torch.bfloat16, device=dev)
-            d["U"] = torch.empty((sh.M, sh.r), dtype=torch.float32, device=dev)
-            d["dX"] = torch.empty((sh.M, sh.K), dtype=torch.bfloat16, device=dev)
-            d["dA"] = torch.empty((sh.r, sh.K), dtype=torch.bfloat16, device=dev)
-            d["dB"] = torch.empty((sh.N, sh.r), dtype=torch.bfloat16, device=dev)
             layer.append(d)
-        sets.append(layer)
-    ws_bytes = max(lla.lora_linear_workspace_size(d["desc"]) for d in sets[0])
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+        sets.append(add_outputs(lla, torch, wl, share_inputs(wl, layer), dev))
+    stepper = Stepper(lla, torch, sets, dev)
     torch.cuda.synchronize()
-
-    # the library launches on the stream torch reports as current (the capture
-    # stream while a graph is being recorded)
-    def fwd(d):
-        if "codes" in d:
-            lla.lora_qlinear_fwd(d["desc"], d["X"], d["codes"], d["absmax"], d["codebook"], d["A"], d["B"],
-                                 d["H"], d["U"], ws=ws, ws_bytes=ws_bytes)
-        else:
-            lla.lora_linear_fwd(d["desc"], d["X"], d["W"], d["A"], d["B"], d["H"], d["U"], ws=ws,
-                                ws_bytes=ws_bytes)
-
-    def bwd(d):
-        if "codes" in d:
-            lla.lora_qlinear_bwd(d["desc"], d["dY"], d["X"], d["codes"], d["absmax"], d["codebook"], d["A"],
-                                 d["B"], d["U"], d["dX"], d["dA"], d["dB"], ws=ws, ws_bytes=ws_bytes)
-        else:
-            lla.lora_linear_bwd(d["desc"], d["dY"], d["X"], d["W"], d["A"], d["B"], d["U"], d["dX"], d["dA"],
-                                d["dB"], ws=ws, ws_bytes=ws_bytes)
-
     n_lin = len(wl.linears)
-    mk = lambda: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-    ev_f = [[mk() for _ in range(n_lin)] for _ in range(args.steps)]
-    ev_b = [[mk() for _ in range(n_lin)] for _ in range(args.steps)]
-
-    def step(i, timed):
-        layer = sets[i % len(sets)]
-        for li, d in enumerate(layer):
-            if timed:
-                ev_f[i][li][0].record(stream)
-            fwd(d)
-            if timed:
-                ev_f[i][li][1].record(stream)
-        for li in reversed(range(n_lin)):
-            if timed:
-                ev_b[i][li][0].record(stream)
-            bwd(layer[li])
-            if timed:
-                ev_b[i][li][1].record(stream)
+    step = lambda i: stepper.step(sets[i % len(sets)])
 
     for i in range(args.warmup):
-        step(i, False)
+        step(i)
     torch.cuda.synchronize()
-    run = lambda i: step(i, False)
+    run = step
     if args.graph:
         graphs = []
         for si in range(len(sets)):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                step(si, False)
+                step(si)
             graphs.append(g)
         torch.cuda.synchronize()
         run = lambda i: graphs[i % len(graphs)].replay()
         for i in range(args.warmup):
             run(i)
         torch.cuda.synchronize()
-    # the timed region holds only the steps themselves (no per-call events)
-    t_start, t_end = mk()
+    mk = lambda: torch.cuda.Event(enable_timing=True)
+
+    # 1. the timed region holds only the steps themselves
+    t_start, t_end = mk(), mk()
+    torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record(stream)
     for i in range(args.steps):
@@ -354,40 +461,54 @@ def main():
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms_total = t_start.elapsed_time(t_end)
-    ms_step = ms_total / args.steps
-    # per-call durations (per-linear table, roofline) from a second pass of the
-    # same steps with HIP events around every library call
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+
+    # 2. step-time spread: one event at every step boundary
+    bounds = [mk() for _ in range(args.steps + 1)]
+    bounds[0].record(stream)
     for i in range(args.steps):
-        step(i, True)
+        run(i)
+        bounds[i + 1].record(stream)
     torch.cuda.synchronize()
+    step_ms = [bounds[i].elapsed_time(bounds[i + 1]) for i in range(args.steps)]
+
+    # 3. per-kernel durations: events around every kernel the library enqueues
+    records, pending = [], {}
+
+    def observer(kernel, _stream, phase):
+        if phase == 0:
+            e = mk()
+            e.record(stream)
+            pending[kernel] = e
+        else:
+            e = mk()
+            e.record(stream)
+            records.append((stepper.current, kernel, pending.pop(kernel), e))
+
+    lla.lora_set_launch_observer(observer)
+    try:
+        for i in range(args.steps):
+            step(i)
+        torch.cuda.synchronize()
+    finally:
+        lla.lora_set_launch_observer(None)
+    kernel_us = {}
+    for li, kernel, a, b in records:
+        kernel_us.setdefault((li, kernel), []).append(a.elapsed_time(b) * 1e3)
 
     flops = wl.flops()
     tflops = flops / (ms_step * 1e-3) / 1e12
     tokens_s = wl.tokens / (ms_step * 1e-3)
 
-    def mean_ms(ev, li):
-        return sum(ev[i][li][0].elapsed_time(ev[i][li][1]) for i in range(args.steps)) / args.steps
-
     per_linear = []
     for li, l in enumerate(wl.linears):
-        f_ms, b_ms = mean_ms(ev_f, li), mean_ms(ev_b, li)
-        per_linear.append({"name": l.name, "fwd_us": round(f_ms * 1e3, 2), "bwd_us": round(b_ms * 1e3, 2),
-                           "fwd_tflops": round(fwd_flops(l) / (f_ms * 1e-3) / 1e12, 1),
-                           "bwd_tflops": round(bwd_flops(l) / (b_ms * 1e-3) / 1e12, 1)})
+        ks = {k: round(sum(v) / len(v), 2) for (i, k), v in kernel_us.items() if i == li}
+        per_linear.append({"name": l.name, "kernel_us": ks})
 
-    # dominant kernel: the fused forward GEMM of the largest linear
-    big = max(range(n_lin), key=lambda i: fwd_flops(wl.linears[i]))
-    lb = wl.linears[big]
-    fwd_ms = mean_ms(ev_f, big)
-    ach = fwd_flops(lb) / (fwd_ms * 1e-3) / 1e12
-    tr = load_traffic(wl.name)
-    roofline = {"kernel": f"lora_gemm forward ({lb.name})" + ("" if lb.r <= 16 else " + skinny U pass"),
-                "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-                "traffic": tr["hbm_bytes_per_dispatch"] if tr else None,
-                "avg_launch_us": round(fwd_ms * 1e3, 2), "flops_per_launch": fwd_flops(lb),
-                "algorithmic_bytes_per_launch": fwd_bytes(lb)}
+    gemms = gemm_rooflines(wl, kernel_us, load_traffic(wl.name))
+    # dominant kernel: the GEMM with the largest measured time per step
+    dominant = max(gemms, key=lambda g: g["avg_launch_us"] * g["launches_per_step"] / args.steps)
+    p10, p50, p90 = (percentile(step_ms, q) for q in (0.1, 0.5, 0.9))
 
     out = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
@@ -398,13 +519,15 @@ def main():
         "config": {"workload": wl.name, "linears": [[l.name, l.M, l.K, l.N, l.r, l.alpha] for l in wl.linears],
                    "input_sets": args.input_sets, "description": wl.description},
         "tokens_per_s": round(tokens_s, 1), "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "step_ms_p10_p50_p90": [round(p10, 4), round(p50, 4), round(p90, 4)],
         "algorithmic_gflop_per_step": round(flops / 1e9, 3), "wall_s_timed": round(wall, 3),
         "per_linear": per_linear,
-        "roofline": roofline,
+        "roofline": dict(dominant),
+        "gemm_rooflines": gemms,
     }
     if not args.no_dequant:
         out["hbm_kernels"] = [dequant_rate(lla, workloads, torch, dev, stream),
-                              merge_rate(lla, torch, dev, stream, lb)]
+                              merge_rate(lla, torch, dev, stream, max(wl.linears, key=lambda l: l.N * l.K))]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -17,7 +17,8 @@
  * All matrices are dense with leading dimension equal to the row length.
  *
  * Memory: every pointer is caller-owned device memory (except `desc`, which is
- * host memory).  The library allocates nothing, keeps no state between calls,
+ * host memory).  The library allocates nothing, keeps no state between calls
+ * (apart from the optional launch observer below),
  * never modifies an input, and enqueues all work on `stream` (a hipStream_t
  * passed as void*; NULL means the null stream).  Calls return once the work is
  * enqueued; device faults surface at the caller's next synchronisation.
@@ -154,6 +155,45 @@ lora_status lora_dequant4(const uint8_t* Wq, const uint16_t* absmax, const float
  */
 lora_status lora_merge(const lora_linear_desc* desc, const void* W, const void* A, const void* B,
                        void* W_out, int32_t sign, void* stream);
+
+/*
+ * Buffer ranges (a check of the library's own addressing, host only; no HIP
+ * call).  The bf16 kernels read their large operands through buffer resources,
+ * whose range field holds at most 2^31 - 1 bytes; each resource is therefore
+ * based near the rows one workgroup or one pipeline step reads.  This lists,
+ * for the plain (quant = 0) or 4-bit (quant = 1) entry points and this
+ * descriptor, every resource a forward or backward call may build: the kernel,
+ * the operand and the largest range in bytes it asks for.  The range of every
+ * entry stays at or below 2^31 - 1 for every descriptor the entry points
+ * accept.  The float32 mode builds none (count 0).
+ *   out:      caller-owned host array of `capacity` entries (may be NULL when
+ *             capacity is 0); the strings are static.
+ *   count:    receives the number of entries (also when it exceeds capacity;
+ *             then only the first `capacity` are written).
+ * Errors as for the descriptor checks of the entry points.
+ */
+typedef struct lora_buffer_range {
+    const char* kernel;
+    const char* operand;
+    uint64_t bytes;
+} lora_buffer_range;
+
+lora_status lora_linear_buffer_ranges(const lora_linear_desc* desc, int32_t quant, lora_buffer_range* out,
+                                      int32_t capacity, int32_t* count);
+
+/*
+ * Launch observer (a profiling aid for callers that time the kernels inside
+ * one call with events on the call's stream).  When set, every entry point
+ * calls fn(user, kernel, stream, 0) right before it enqueues each kernel and
+ * fn(user, kernel, stream, 1) right after, on the calling thread, with a
+ * static kernel label ("lora_gemm forward", "lora_gemm dX", "rank_stream",
+ * "grad_final", ...) and the stream passed to the entry point.  NULL removes
+ * the observer.  It is the library's only process-wide setting: set or clear
+ * it while no other thread is inside the library.
+ */
+typedef void (*lora_launch_observer)(void* user, const char* kernel, void* stream, int32_t phase);
+
+void lora_set_launch_observer(lora_launch_observer fn, void* user);
 
 /* Static text for a status code. */
 const char* lora_status_string(lora_status status);

@@ -26,8 +26,11 @@ LORA_FLAG_ACCUM_GRADS = 0x1
 EXPORTED = (
     "lora_linear_workspace_size", "lora_linear_fwd", "lora_linear_bwd",
     "lora_qlinear_fwd", "lora_qlinear_bwd", "lora_dequant4", "lora_merge",
-    "lora_status_string", "lora_last_error",
+    "lora_linear_buffer_ranges", "lora_set_launch_observer", "lora_status_string", "lora_last_error",
 )
+
+# void (*)(void* user, const char* kernel, void* stream, int32_t phase)
+LAUNCH_OBSERVER = ctypes.CFUNCTYPE(None, ctypes.c_void_p, ctypes.c_char_p, ctypes.c_void_p, ctypes.c_int32)
 
 
 class LoraLinearDesc(ctypes.Structure):
@@ -36,6 +39,11 @@ class LoraLinearDesc(ctypes.Structure):
         ("M", ctypes.c_int64), ("K", ctypes.c_int64), ("N", ctypes.c_int64), ("r", ctypes.c_int64),
         ("alpha", ctypes.c_float), ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32),
     ]
+
+
+class LoraBufferRange(ctypes.Structure):
+    """Mirror of struct lora_buffer_range."""
+    _fields_ = [("kernel", ctypes.c_char_p), ("operand", ctypes.c_char_p), ("bytes", ctypes.c_uint64)]
 
 
 _lib = None
@@ -61,11 +69,14 @@ def load() -> ctypes.CDLL:
         "lora_qlinear_bwd": [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "lora_dequant4": [vp, vp, vp, i64, i64, i32, vp, vp],
         "lora_merge": [dp, vp, vp, vp, vp, i32, vp],
+        "lora_linear_buffer_ranges": [dp, i32, ctypes.POINTER(LoraBufferRange), i32, ctypes.POINTER(i32)],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = ctypes.c_int
+    lib.lora_set_launch_observer.argtypes = [LAUNCH_OBSERVER, ctypes.c_void_p]
+    lib.lora_set_launch_observer.restype = None
     lib.lora_status_string.argtypes = [ctypes.c_int]
     lib.lora_status_string.restype = ctypes.c_char_p
     lib.lora_last_error.argtypes = []

@@ -14,7 +14,7 @@ import torch
 
 from . import _lib
 from ._lib import (LORA_DTYPE_BF16, LORA_DTYPE_F32, LORA_FLAG_ACCUM_GRADS,  # noqa: F401
-                   LoraLinearDesc)
+                   LoraBufferRange, LoraLinearDesc)
 
 
 class LoraError(RuntimeError):
@@ -57,6 +57,51 @@ def _ptr(t):
     return t.data_ptr()
 
 
+_TORCH_DTYPE = {LORA_DTYPE_BF16: torch.bfloat16, LORA_DTYPE_F32: torch.float32}
+
+
+def _expect(t, name, shape, dtypes):
+    """Shape and dtype of a tensor argument (raw integer addresses and None
+    pass unchecked)."""
+    if t is None or isinstance(t, int):
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a tensor, an int address or None, got {type(t)!r}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {' or '.join(str(d) for d in dtypes)}")
+
+
+def _same_gpu(**ts):
+    """All tensor arguments on one GPU (checked after their shapes and dtypes)."""
+    dev = None
+    for name, t in ts.items():
+        if not isinstance(t, torch.Tensor):
+            continue
+        if t.device.type != "cuda":
+            raise ValueError(f"{name}: tensor on {t.device}, expected a GPU tensor")
+        if dev is not None and t.device != dev:
+            raise ValueError(f"{name}: tensor on {t.device}, the other operands are on {dev}")
+        dev = t.device
+
+
+def _check_dense(desc: "Desc", **ts):
+    """Operands of a forward or backward call against the descriptor, before
+    their addresses go to the library."""
+    M, K, N, r = desc.M, desc.K, desc.N, desc.r
+    dt = (_TORCH_DTYPE[desc.dtype],) if desc.dtype in _TORCH_DTYPE else ()
+    spec = {"X": ((M, K), dt), "W": ((N, K), dt), "A": ((r, K), dt), "B": ((N, r), dt), "H": ((M, N), dt),
+            "dY": ((M, N), dt), "dX": ((M, K), dt), "dA": ((r, K), dt), "dB": ((N, r), dt),
+            "U_save": ((M, r), (torch.float32,)), "U_saved": ((M, r), (torch.float32,)),
+            "Wq": ((N, K // 2), (torch.uint8,)),
+            "absmax": ((N, K // 64), (torch.int16, torch.float16, torch.uint16)),
+            "codebook": ((16,), (torch.float32,))}
+    for name, t in ts.items():
+        _expect(t, name, *spec[name])
+    _same_gpu(**ts)
+
+
 def _stream(stream):
     if stream is None:
         return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
@@ -84,8 +129,41 @@ def lora_linear_workspace_size(desc: Desc) -> int:
     return int(out.value)
 
 
+def lora_linear_buffer_ranges(desc: Desc, quant: bool = False) -> list:
+    """Every buffer resource the kernels may build for this descriptor, as
+    (kernel, operand, largest range in bytes) tuples (host only, no HIP call)."""
+    d = desc.c()
+    n = ctypes.c_int32(0)
+    lib = _lib.load()
+    _check(lib.lora_linear_buffer_ranges(ctypes.byref(d), int(quant), None, 0, ctypes.byref(n)),
+           "lora_linear_buffer_ranges")
+    arr = (LoraBufferRange * max(n.value, 1))()
+    _check(lib.lora_linear_buffer_ranges(ctypes.byref(d), int(quant), arr, n.value, ctypes.byref(n)),
+           "lora_linear_buffer_ranges")
+    return [(arr[i].kernel.decode(), arr[i].operand.decode(), int(arr[i].bytes)) for i in range(n.value)]
+
+
+_observer_ref = None      # keeps the ctypes callback alive while the library holds it
+
+
+def lora_set_launch_observer(fn) -> None:
+    """fn(kernel: str, stream: int, phase: int) is called right before (phase
+    0) and right after (phase 1) each kernel the library enqueues; None
+    removes it (see include/lora_linear.h)."""
+    global _observer_ref
+    lib = _lib.load()
+    if fn is None:
+        lib.lora_set_launch_observer(_lib.LAUNCH_OBSERVER(), None)
+        _observer_ref = None
+        return
+    cb = _lib.LAUNCH_OBSERVER(lambda user, kernel, stream, phase: fn(kernel.decode(), stream or 0, int(phase)))
+    lib.lora_set_launch_observer(cb, None)
+    _observer_ref = cb
+
+
 def lora_linear_fwd(desc: Desc, X, W, A, B, H, U_save=None, ws=None, ws_bytes=None, stream=None):
     """H = X W^T + s (X A^T) B^T (see include/lora_linear.h)."""
+    _check_dense(desc, X=X, W=W, A=A, B=B, H=H, U_save=U_save)
     if ws is None:
         ws, ws_bytes = _ws(desc, None, X.device)
     elif ws_bytes is None:
@@ -98,6 +176,7 @@ def lora_linear_fwd(desc: Desc, X, W, A, B, H, U_save=None, ws=None, ws_bytes=No
 
 def lora_linear_bwd(desc: Desc, dY, X, W, A, B, U_saved, dX, dA, dB, ws=None, ws_bytes=None, stream=None):
     """dX = dY W + s (dY B) A; dA = s (dY B)^T X; dB = s dY^T U (see include/lora_linear.h)."""
+    _check_dense(desc, dY=dY, X=X, W=W, A=A, B=B, U_saved=U_saved, dX=dX, dA=dA, dB=dB)
     if ws is None:
         ws, ws_bytes = _ws(desc, None, dY.device)
     elif ws_bytes is None:
@@ -111,6 +190,7 @@ def lora_linear_bwd(desc: Desc, dY, X, W, A, B, U_saved, dX, dA, dB, ws=None, ws
 def lora_qlinear_fwd(desc: Desc, X, Wq, absmax, codebook, A, B, H, U_save=None, ws=None, ws_bytes=None,
                      stream=None):
     """Forward with the frozen weight in the 4-bit format (codes, fp16 absmax, codebook)."""
+    _check_dense(desc, X=X, Wq=Wq, absmax=absmax, codebook=codebook, A=A, B=B, H=H, U_save=U_save)
     if ws is None:
         ws, ws_bytes = _ws(desc, None, X.device)
     elif ws_bytes is None:
@@ -124,6 +204,8 @@ def lora_qlinear_fwd(desc: Desc, X, Wq, absmax, codebook, A, B, H, U_save=None, 
 def lora_qlinear_bwd(desc: Desc, dY, X, Wq, absmax, codebook, A, B, U_saved, dX, dA, dB, ws=None, ws_bytes=None,
                      stream=None):
     """Backward with the frozen weight in the 4-bit format."""
+    _check_dense(desc, dY=dY, X=X, Wq=Wq, absmax=absmax, codebook=codebook, A=A, B=B,
+                 U_saved=U_saved, dX=dX, dA=dA, dB=dB)
     if ws is None:
         ws, ws_bytes = _ws(desc, None, dY.device)
     elif ws_bytes is None:
@@ -137,6 +219,11 @@ def lora_qlinear_bwd(desc: Desc, dY, X, Wq, absmax, codebook, A, B, U_saved, dX,
 
 def lora_dequant4(Wq, absmax, codebook, N: int, K: int, out_dtype: int, W_out, stream=None):
     """Dense W_out [N, K] from the 4-bit format."""
+    _expect(Wq, "Wq", (N, K // 2), (torch.uint8,))
+    _expect(absmax, "absmax", (N, K // 64), (torch.int16, torch.float16, torch.uint16))
+    _expect(codebook, "codebook", (16,), (torch.float32,))
+    _expect(W_out, "W_out", (N, K), (_TORCH_DTYPE.get(out_dtype, torch.bfloat16),))
+    _same_gpu(Wq=Wq, absmax=absmax, codebook=codebook, W_out=W_out)
     st = _lib.load().lora_dequant4(_ptr(Wq), _ptr(absmax), _ptr(codebook), N, K, out_dtype, _ptr(W_out),
                                    _stream(stream))
     _check(st, "lora_dequant4")
@@ -144,6 +231,12 @@ def lora_dequant4(Wq, absmax, codebook, N: int, K: int, out_dtype: int, W_out, s
 
 def lora_merge(desc: Desc, W, A, B, W_out, sign: int = 1, stream=None):
     """W_out = W + sign * s * B A (sign +1 merge, -1 unmerge); W_out may be W (in place)."""
+    dt = (_TORCH_DTYPE[desc.dtype],) if desc.dtype in _TORCH_DTYPE else ()
+    _expect(W, "W", (desc.N, desc.K), dt)
+    _expect(A, "A", (desc.r, desc.K), dt)
+    _expect(B, "B", (desc.N, desc.r), dt)
+    _expect(W_out, "W_out", (desc.N, desc.K), dt)
+    _same_gpu(W=W, A=A, B=B, W_out=W_out)
     d = desc.c()
     st = _lib.load().lora_merge(ctypes.byref(d), _ptr(W), _ptr(A), _ptr(B), _ptr(W_out), int(sign), _stream(stream))
     _check(st, "lora_merge")

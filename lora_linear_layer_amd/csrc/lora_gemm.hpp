@@ -58,6 +58,7 @@
 #include <type_traits>
 
 #include "common.hpp"
+#include "ranges.hpp"
 
 namespace lora {
 
@@ -67,7 +68,6 @@ typedef __attribute__((address_space(3))) i16x4* lds_i16x4_ptr;
 
 constexpr uint32_t kOOB = 0x80000000u;        // buffer offset beyond every range -> zeros
 constexpr int32_t kRsrcWord3 = 0x00020000;    // raw buffer, 32-bit data format (gfx9 family)
-constexpr uint32_t kMaxRange = 0x7FFFFFFFu;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint64_t bytes) {
     const uint32_t n = bytes > kMaxRange ? kMaxRange : (uint32_t)bytes;
@@ -130,7 +130,8 @@ struct GemmArgs {
     float* Zsave;           // [P][r] float32 or nullptr (written by the q-tile-0 workgroups)
     float* Part;            // split contraction: float32 partial tiles [split][tile - first_split][256][256]
     // Input gradient, in-tile Z only: the bf16 planes hi = bf16(Z^T), lo = bf16(Z^T - hi) of
-    // Z = V and of U (read from Uin [P][r] float32), rows [r][Mp], tokens p >= P zero; written by
+    // Z = V and of U (read from Uin [P][r] float32), [r][Mp] in the token-block-major order of
+    // zt_index, tokens p >= P zero; written by
     // the q-tile-0 workgroups for the adapter-gradient pass, or not at all when Zt_hi is nullptr
     uint16_t *Zt_hi, *Zt_lo, *Ut_hi, *Ut_lo;
     const float* Uin;
@@ -225,7 +226,7 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
     // the same for every i, so one base offset plus a uniform stride suffices.
     const int kc_row0 = wave * LPW * 8 + (lane >> 3);
     const int kc_ch = ((lane & 7) ^ (lane >> 3)) * 8;
-    const __amdgpu_buffer_rsrc_t rsL = make_rsrc(a.L + (size_t)p0 * C, (uint64_t)min(P - p0, BP) * C * 2);
+    const __amdgpu_buffer_rsrc_t rsL = make_rsrc(a.L + (size_t)p0 * C, panel_bytes(P, p0, BP, C));
     const uint32_t offL = (uint32_t)(kc_row0 * C + kc_ch) * 2u;
     __amdgpu_buffer_rsrc_t rsR;
     uint32_t offR = 0;
@@ -233,7 +234,7 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
     if constexpr (Q4) {
         // R tiles come through registers (load_q / decode_q)
     } else if constexpr (!TRANS) {
-        rsR = make_rsrc(a.R + (size_t)q0 * C, (uint64_t)min(Q - q0, BQ) * C * 2);
+        rsR = make_rsrc(a.R + (size_t)q0 * C, panel_bytes(Q, q0, BQ, C));
         offR = (uint32_t)(kc_row0 * C + kc_ch) * 2u;
     } else {
         // W rows c (512 bytes each); load i of wave w covers rows
@@ -252,7 +253,7 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
     uint32_t offF = kOOB;
     int fch = 0, frow = 0;
     if constexpr (!ZIN) {
-        rsF = make_rsrc(a.F, (uint64_t)r * C * 2);
+        rsF = make_rsrc(a.F, TRANS ? whole_bytes(C, r) : whole_bytes(r, C));   // B [C][r] or A [r][C]
         frow = wave * 8 + (lane >> 3);                       // j (waves 0 .. RPAD/8 - 1)
         fch = kc_ch;
         offF = (uint32_t)(frow * C + fch) * 2u;
@@ -354,9 +355,7 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
             for (int i = 0; i < LPW; ++i)
                 g2lds16<TRANS>(rsR, Rs + (wave * LPW + i) * 1024, vR + (uint32_t)(i * 8 * C) * 2u);
         } else {
-            const int rows_left = max(1, min(C - c0, BK));
-            const __amdgpu_buffer_rsrc_t rs =
-                make_rsrc(a.R + (size_t)c0 * Q + q0, (uint64_t)(rows_left - 1) * Q * 2 + (uint64_t)(Q - q0) * 2);
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.R + (size_t)c0 * Q + q0, gemm_wt_stage_bytes(C, Q, c0, q0));
             uint32_t vR[LPW == 8 ? 4 : 2];
 #pragma unroll
             for (int v = 0; v < (LPW == 8 ? 4 : 2); ++v)
@@ -646,13 +645,14 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
         if constexpr (TRANS) {
             if (a.Zt_hi != nullptr && qt == 0) {
                 // element (j, pl), pl fastest: each wave stores 128 contiguous bytes per plane
+                // (planes token-block major, zt_index: p0 is a multiple of the 128-token block)
                 for (int e = tid; e < BP * r; e += NT) {
                     const int j = e / BP, pl = e - j * BP, p = p0 + pl;
                     if (p >= a.Mp) continue;
                     const float v = p < P ? Zx[pl * RPAD + j] : 0.f;
                     const float u = p < P ? a.Uin[(size_t)p * r + j] : 0.f;
                     const __bf16 vh = (__bf16)v, uh = (__bf16)u;
-                    const size_t o = (size_t)j * a.Mp + p;
+                    const size_t o = zt_index(j, p, r);
                     a.Zt_hi[o] = __builtin_bit_cast(uint16_t, vh);
                     a.Zt_lo[o] = __builtin_bit_cast(uint16_t, (__bf16)(v - (float)vh));
                     a.Ut_hi[o] = __builtin_bit_cast(uint16_t, uh);

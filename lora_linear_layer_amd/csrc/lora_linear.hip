@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <climits>
 #include <cmath>
 #include <cstdarg>
@@ -15,6 +16,7 @@
 #include "lora_linear.h"
 
 #include "lora_gemm.hpp"
+#include "ranges.hpp"
 #include "rank_stream.hpp"
 #include "dequant4.hpp"
 #include "merge.hpp"
@@ -40,6 +42,16 @@ lora_status fail(lora_status st, const char* fmt, ...) {
 lora_status ok() {
     g_last_error.clear();
     return LORA_OK;
+}
+
+// Launch observer (lora_set_launch_observer): called right before and right
+// after each kernel is enqueued.
+std::atomic<lora_launch_observer> g_observer{nullptr};
+std::atomic<void*> g_observer_user{nullptr};
+
+void observe(const char* kernel, hipStream_t st, int phase) {
+    const lora_launch_observer fn = g_observer.load(std::memory_order_acquire);
+    if (fn) fn(g_observer_user.load(std::memory_order_relaxed), kernel, static_cast<void*>(st), phase);
 }
 
 constexpr int64_t kMaxElems = (int64_t(1) << 31) - 1;
@@ -242,7 +254,7 @@ lora_status launched(const char* what) {
 template <bool TRANS, int RPAD, bool ZIN, bool Q4>
 void launch_gemm_t(const GemmArgs& a, hipStream_t st) {
     const int tiles = (int)(cdiv(a.P, g2::BP) * cdiv(a.Q, g2::BQ));
-    hipLaunchKernelGGL((lora_gemm<TRANS, RPAD, ZIN, Q4>), dim3(tiles), dim3(g2w::NT), 0, st, a);
+    { observe(TRANS ? "lora_gemm dX" : "lora_gemm forward", st, 0); hipLaunchKernelGGL((lora_gemm<TRANS, RPAD, ZIN, Q4>), dim3(tiles), dim3(g2w::NT), 0, st, a); observe(TRANS ? "lora_gemm dX" : "lora_gemm forward", st, 1); }
 }
 
 // In-tile rank-r product for r <= 16 with 16-bit weights: the forward forms
@@ -272,11 +284,11 @@ void launch_gemm_zin(GemmArgs a, const SplitPlan& sp, hipStream_t st) {
         a.kc = sp.kc;
         const int T = (int)(cdiv(a.P, g2::BP) * cdiv(a.Q, g2::BQ));
         const int units = sp.first + (T - sp.first) * sp.split;
-        hipLaunchKernelGGL((lora_gemm<TRANS, RPAD, true, Q4, true>), dim3(units), dim3(g2w::NT), 0, st, a);
+        { observe(TRANS ? "lora_gemm dX (split)" : "lora_gemm forward (split)", st, 0); hipLaunchKernelGGL((lora_gemm<TRANS, RPAD, true, Q4, true>), dim3(units), dim3(g2w::NT), 0, st, a); observe(TRANS ? "lora_gemm dX (split)" : "lora_gemm forward (split)", st, 1); }
         SplitFinishArgs f{a.Part, a.Out, a.P, a.Q, (int)cdiv(a.P, g2::BP), (int)cdiv(a.Q, g2::BQ), sp.first,
                           T - sp.first, sp.split};
         const int64_t n = (int64_t)(T - sp.first) * (g2::BP * g2::BQ / 4);
-        hipLaunchKernelGGL(split_finish, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, st, f);
+        { observe("split_finish", st, 0); hipLaunchKernelGGL(split_finish, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, st, f); observe("split_finish", st, 1); }
         return;
     }
     launch_gemm_t<TRANS, RPAD, true, Q4>(a, st);
@@ -309,8 +321,8 @@ void launch_rank_z(const lora_linear_desc& d, const uint16_t* Y, int64_t C, cons
     const dim3 grid((unsigned)cdiv(d.M, 128), (unsigned)n_used, 1);
     for (int j0 = 0; j0 < d.r; j0 += 64) {        // 64 rank columns per launch
         const int jb = (int)cdiv(std::min<int64_t>(d.r - j0, 64), 16);
-#define RZ(J) hipLaunchKernelGGL((rank_z_lds<J>), grid, dim3(512), 0, st, Y, F_rows, out, (int)d.M, (int)C, \
-                                 (int)d.r, j0, chunk_c)
+#define RZ(J) do { observe("rank_z_lds", st, 0); hipLaunchKernelGGL((rank_z_lds<J>), grid, dim3(512), 0, st, Y, F_rows, out, (int)d.M, (int)C, \
+                                 (int)d.r, j0, chunk_c); observe("rank_z_lds", st, 1); } while (0)
         switch (jb) {
             case 1: RZ(1); break;
             case 2: RZ(2); break;
@@ -321,7 +333,7 @@ void launch_rank_z(const lora_linear_desc& d, const uint16_t* Y, int64_t C, cons
     }
     if (n_used > 1) {
         const int64_t n = d.M * d.r;
-        hipLaunchKernelGGL(partial_sum, dim3((unsigned)cdiv(n, 1024)), dim3(256), 0, st, zpart, Z, n, n_used);
+        { observe("partial_sum", st, 0); hipLaunchKernelGGL(partial_sum, dim3((unsigned)cdiv(n, 1024)), dim3(256), 0, st, zpart, Z, n, n_used); observe("partial_sum", st, 1); }
     }
 }
 
@@ -346,12 +358,12 @@ lora_status launch_adapter_grads(const lora_linear_desc& d, const Plan& plan, ch
     uint16_t* const ut_hi = zt_plane(plan, wsb, d.r, 2);
     uint16_t* const ut_lo = zt_plane(plan, wsb, d.r, 3);
     if (!planes_ready) {
-        hipLaunchKernelGGL(zt_hilo, dim3((unsigned)cdiv(d.r * plan.Mp, 256), 2), dim3(256), 0, st, V, U, vt_hi,
-                           vt_lo, ut_hi, ut_lo, (int)d.M, (int)plan.Mp, (int)d.r);
+        { observe("zt_hilo", st, 0); hipLaunchKernelGGL(zt_hilo, dim3((unsigned)cdiv(d.r * plan.Mp, 256), 2), dim3(256), 0, st, V, U, vt_hi,
+                           vt_lo, ut_hi, ut_lo, (int)d.M, (int)plan.Mp, (int)d.r); observe("zt_hilo", st, 1); }
         LAUNCH_CHECK("zt_hilo");
     }
-    a.prob[0] = RankProblem{X, vt_hi, vt_lo, ga, (int)d.K, (int)plan.Mp, (int)cdiv(d.K, kRT)};
-    a.prob[1] = RankProblem{dY, ut_hi, ut_lo, gb, (int)d.N, (int)plan.Mp, (int)cdiv(d.N, kRT)};
+    a.prob[0] = RankProblem{X, vt_hi, vt_lo, ga, (int)d.K, (int)cdiv(d.K, kRT)};
+    a.prob[1] = RankProblem{dY, ut_hi, ut_lo, gb, (int)d.N, (int)cdiv(d.N, kRT)};
     a.n_prob = 2;
     a.M = (int)d.M;
     a.r = (int)d.r;
@@ -361,9 +373,9 @@ lora_status launch_adapter_grads(const lora_linear_desc& d, const Plan& plan, ch
     for (int j0 = 0; j0 < d.r; j0 += 64) {        // ranks above 64: one launch per 64 columns
         a.j0 = j0;
         switch (rpad_of(std::min<int64_t>(d.r - j0, 64))) {
-            case 16: hipLaunchKernelGGL((rank_stream<16>), grid, dim3(256), 0, st, a); break;
-            case 32: hipLaunchKernelGGL((rank_stream<32>), grid, dim3(256), 0, st, a); break;
-            default: hipLaunchKernelGGL((rank_stream<64>), grid, dim3(256), 0, st, a); break;
+            case 16: { observe("rank_stream", st, 0); hipLaunchKernelGGL((rank_stream<16>), grid, dim3(256), 0, st, a); observe("rank_stream", st, 1); } break;
+            case 32: { observe("rank_stream", st, 0); hipLaunchKernelGGL((rank_stream<32>), grid, dim3(256), 0, st, a); observe("rank_stream", st, 1); } break;
+            default: { observe("rank_stream", st, 0); hipLaunchKernelGGL((rank_stream<64>), grid, dim3(256), 0, st, a); observe("rank_stream", st, 1); } break;
         }
     }
     LAUNCH_CHECK("rank_stream(dA, dB)");
@@ -379,7 +391,7 @@ lora_status launch_adapter_grads(const lora_linear_desc& d, const Plan& plan, ch
     f.s = d.alpha / (float)d.r;
     f.f32_out = 0;
     f.accumulate = (d.flags & LORA_FLAG_ACCUM_GRADS) ? 1 : 0;
-    hipLaunchKernelGGL(grad_final, dim3((unsigned)cdiv((d.K + d.N) * d.r, 256)), dim3(256), 0, st, f);
+    { observe("grad_final", st, 0); hipLaunchKernelGGL(grad_final, dim3((unsigned)cdiv((d.K + d.N) * d.r, 256)), dim3(256), 0, st, f); observe("grad_final", st, 1); }
     LAUNCH_CHECK("grad_final");
     return LORA_OK;
 }
@@ -454,8 +466,8 @@ lora_status bwd_bf16(const lora_linear_desc& d, bool quant, const void* dY, cons
     const bool v_in_tile = dX != nullptr && dx_in_tile(quant, r, sp);
     if (!v_in_tile) {
         uint16_t* const BT = reinterpret_cast<uint16_t*>(wsb + plan.off_bt);
-        hipLaunchKernelGGL(transpose_rank, dim3((unsigned)cdiv(d.r * d.N, 256)), dim3(256), 0, st, B16, BT,
-                           (int)d.N, (int)d.r);
+        { observe("transpose_rank", st, 0); hipLaunchKernelGGL(transpose_rank, dim3((unsigned)cdiv(d.r * d.N, 256)), dim3(256), 0, st, B16, BT,
+                           (int)d.N, (int)d.r); observe("transpose_rank", st, 1); }
         LAUNCH_CHECK("transpose_rank");
         launch_rank_z(d, dY16, d.N, BT, V, zpart, st);
         LAUNCH_CHECK("rank_z_lds(V)");
@@ -498,7 +510,7 @@ lora_status bwd_bf16(const lora_linear_desc& d, bool quant, const void* dY, cons
 template <int RMODE>
 void launch_f32_fused(const F32FusedArgs& a, hipStream_t st) {
     const dim3 grid((unsigned)cdiv(a.Q, 64), (unsigned)cdiv(a.P, 64));
-    hipLaunchKernelGGL((f32_fused<RMODE>), grid, dim3(256), 0, st, a);
+    { observe("f32_fused", st, 0); hipLaunchKernelGGL((f32_fused<RMODE>), grid, dim3(256), 0, st, a); observe("f32_fused", st, 1); }
 }
 
 void launch_f32_fused_mode(int rmode, const F32FusedArgs& a, hipStream_t st) {
@@ -516,8 +528,8 @@ lora_status fwd_f32(const lora_linear_desc& d, bool quant, const void* X, const 
     const Plan plan = make_plan(d);
     float* U = U_save ? U_save : reinterpret_cast<float*>(static_cast<char*>(ws) + plan.off_u);
     const int M = (int)d.M, K = (int)d.K, N = (int)d.N, r = (int)d.r;
-    hipLaunchKernelGGL(f32_skinny, dim3((unsigned)cdiv((int64_t)M * r, 256)), dim3(256), 0, st,
-                       static_cast<const float*>(X), static_cast<const float*>(A), U, M, K, r, 0);
+    { observe("f32_skinny", st, 0); hipLaunchKernelGGL(f32_skinny, dim3((unsigned)cdiv((int64_t)M * r, 256)), dim3(256), 0, st,
+                       static_cast<const float*>(X), static_cast<const float*>(A), U, M, K, r, 0); observe("f32_skinny", st, 1); }
     LAUNCH_CHECK("f32_skinny(U)");
     F32FusedArgs a{};
     a.L = static_cast<const float*>(X);
@@ -543,14 +555,14 @@ lora_status bwd_f32(const lora_linear_desc& d, bool quant, const void* dY, const
     const float s = d.alpha / (float)d.r;
     const float* dYf = static_cast<const float*>(dY);
     const float* Xf = static_cast<const float*>(X);
-    hipLaunchKernelGGL(f32_skinny, dim3((unsigned)cdiv((int64_t)M * r, 256)), dim3(256), 0, st,
-                       dYf, static_cast<const float*>(B), V, M, N, r, 1);
+    { observe("f32_skinny", st, 0); hipLaunchKernelGGL(f32_skinny, dim3((unsigned)cdiv((int64_t)M * r, 256)), dim3(256), 0, st,
+                       dYf, static_cast<const float*>(B), V, M, N, r, 1); observe("f32_skinny", st, 1); }
     LAUNCH_CHECK("f32_skinny(V)");
     const float* U = U_saved;
     if (!U) {
         float* Uw = reinterpret_cast<float*>(wsb + plan.off_u);
-        hipLaunchKernelGGL(f32_skinny, dim3((unsigned)cdiv((int64_t)M * r, 256)), dim3(256), 0, st,
-                           Xf, static_cast<const float*>(A), Uw, M, K, r, 0);
+        { observe("f32_skinny", st, 0); hipLaunchKernelGGL(f32_skinny, dim3((unsigned)cdiv((int64_t)M * r, 256)), dim3(256), 0, st,
+                           Xf, static_cast<const float*>(A), Uw, M, K, r, 0); observe("f32_skinny", st, 1); }
         LAUNCH_CHECK("f32_skinny(U)");
         U = Uw;
     }
@@ -568,13 +580,65 @@ lora_status bwd_f32(const lora_linear_desc& d, bool quant, const void* dY, const
         LAUNCH_CHECK("f32_fused(dX)");
     }
     const int acc = (d.flags & LORA_FLAG_ACCUM_GRADS) ? 1 : 0;
-    hipLaunchKernelGGL(f32_grad, dim3((unsigned)cdiv((int64_t)K * r, 256)), dim3(256), 0, st,
-                       Xf, (const float*)V, static_cast<float*>(dA), M, K, r, s, 1, acc);
+    { observe("f32_grad", st, 0); hipLaunchKernelGGL(f32_grad, dim3((unsigned)cdiv((int64_t)K * r, 256)), dim3(256), 0, st,
+                       Xf, (const float*)V, static_cast<float*>(dA), M, K, r, s, 1, acc); observe("f32_grad", st, 1); }
     LAUNCH_CHECK("f32_grad(dA)");
-    hipLaunchKernelGGL(f32_grad, dim3((unsigned)cdiv((int64_t)N * r, 256)), dim3(256), 0, st,
-                       dYf, U, static_cast<float*>(dB), M, N, r, s, 0, acc);
+    { observe("f32_grad", st, 0); hipLaunchKernelGGL(f32_grad, dim3((unsigned)cdiv((int64_t)N * r, 256)), dim3(256), 0, st,
+                       dYf, U, static_cast<float*>(dB), M, N, r, s, 0, acc); observe("f32_grad", st, 1); }
     LAUNCH_CHECK("f32_grad(dB)");
     return ok();
+}
+
+// ---------------------------------------------------------------- buffer ranges
+// Every buffer resource the bf16 kernels of one descriptor may build, with the
+// largest range it asks for (the first workgroup and step, where the clipping
+// to the matrix ends has not yet shortened it).  The kernels build their
+// resources with the same functions (ranges.hpp); a call that skips dX or does
+// not pass U builds a subset.
+struct RangeList {
+    lora_buffer_range* out;
+    int cap, n;
+    void add(const char* kernel, const char* operand, uint64_t bytes) {
+        if (out && n < cap) out[n] = lora_buffer_range{kernel, operand, bytes};
+        ++n;
+    }
+};
+
+void gemm_ranges(RangeList& L, const char* name, bool trans, bool quant, bool in_tile, int64_t P, int64_t Q,
+                 int64_t C, int64_t r) {
+    L.add(name, trans ? "dY panel" : "X panel", panel_bytes(P, 0, g2::BP, C));
+    if (!quant) {
+        if (trans) L.add(name, "W stage (rows c0 .. c0 + 63)", gemm_wt_stage_bytes(C, Q, 0, 0));
+        else L.add(name, "W panel", panel_bytes(Q, 0, g2::BQ, C));
+    }
+    if (in_tile) L.add(name, trans ? "B" : "A", trans ? whole_bytes(C, r) : whole_bytes(r, C));
+}
+
+void rank_z_ranges(RangeList& L, const char* name, int64_t M, int64_t C, int64_t r) {
+    L.add(name, "Y block (128 rows)", panel_bytes(M, 0, 128, C));
+    L.add(name, "F rows", whole_bytes(r, C));
+}
+
+void buffer_ranges(const lora_linear_desc& d, bool quant, RangeList& L) {
+    if (d.dtype != LORA_DTYPE_BF16) return;          // the float32 mode uses plain loads only
+    const int r = (int)d.r;
+    const SplitPlan spf = gemm_split_plan(d.M, d.N, d.K, quant);
+    const SplitPlan spb = gemm_split_plan(d.M, d.K, d.N, quant);
+    // forward (U by the streamed pass when it is not formed in the tile)
+    const bool fwd_in_tile = gemm_in_tile(quant, r, spf);
+    if (!fwd_in_tile) rank_z_ranges(L, "rank_z_lds (U = X A^T)", d.M, d.K, d.r);
+    gemm_ranges(L, "lora_gemm (forward)", false, quant, fwd_in_tile, d.M, d.N, d.K, d.r);
+    // backward: U recomputed when not saved, V streamed unless the dX GEMM forms it
+    if (fwd_in_tile) rank_z_ranges(L, "rank_z_lds (U = X A^T)", d.M, d.K, d.r);
+    rank_z_ranges(L, "rank_z_lds (V = dY B)", d.M, d.N, d.r);
+    gemm_ranges(L, "lora_gemm (dX)", true, quant, dx_in_tile(quant, r, spb), d.M, d.K, d.N, d.r);
+    for (int64_t j0 = 0; j0 < d.r; j0 += 64) {
+        const int64_t rl = std::min<int64_t>(d.r - j0, 64);
+        const int64_t TM = rpad_of(rl) <= 16 ? kRT : kRT / 2;
+        L.add("rank_stream (dA partials)", "X step", stream_y_bytes(d.M, d.K, 0, 0, TM));
+        L.add("rank_stream (dB partials)", "dY step", stream_y_bytes(d.M, d.N, 0, 0, TM));
+        L.add("rank_stream (dA, dB partials)", "rank plane block (hi, lo)", stream_side_bytes(rl, TM));
+    }
 }
 
 }  // namespace
@@ -596,11 +660,28 @@ const char* lora_status_string(lora_status s) {
 
 const char* lora_last_error(void) { return g_last_error.c_str(); }
 
+void lora_set_launch_observer(lora_launch_observer fn, void* user) {
+    g_observer_user.store(user, std::memory_order_relaxed);
+    g_observer.store(fn, std::memory_order_release);
+}
+
 lora_status lora_linear_workspace_size(const lora_linear_desc* desc, size_t* bytes) {
     if (!bytes) return fail(LORA_ERR_INVALID_ARG, "bytes is NULL");
     lora_status st = check_desc(desc, false);
     if (st != LORA_OK) return st;
     *bytes = make_plan(*desc).total;
+    return ok();
+}
+
+lora_status lora_linear_buffer_ranges(const lora_linear_desc* desc, int32_t quant, lora_buffer_range* out,
+                                      int32_t capacity, int32_t* count) {
+    if (!count) return fail(LORA_ERR_INVALID_ARG, "count is NULL");
+    if (capacity < 0 || (capacity > 0 && !out)) return fail(LORA_ERR_INVALID_ARG, "out is NULL or capacity < 0");
+    lora_status st = check_desc(desc, quant != 0);
+    if (st != LORA_OK) return st;
+    RangeList L{out, capacity, 0};
+    buffer_ranges(*desc, quant != 0, L);
+    *count = L.n;
     return ok();
 }
 
@@ -717,8 +798,8 @@ lora_status lora_merge(const lora_linear_desc* desc, const void* W, const void* 
         const uint16_t *W16 = static_cast<const uint16_t*>(W), *A16 = static_cast<const uint16_t*>(A),
                        *B16 = static_cast<const uint16_t*>(B);
         uint16_t* const O16 = static_cast<uint16_t*>(W_out);
-#define MERGE_MFMA(RP) hipLaunchKernelGGL((lora_merge_mfma<RP>), grid, dim3(256), 0, s, W16, A16, B16, O16, \
-                                          (int)d.N, (int)d.K, (int)d.r, scale)
+#define MERGE_MFMA(RP) do { observe("lora_merge", s, 0); hipLaunchKernelGGL((lora_merge_mfma<RP>), grid, dim3(256), 0, s, W16, A16, B16, O16, \
+                                          (int)d.N, (int)d.K, (int)d.r, scale); observe("lora_merge", s, 1); } while (0)
         switch ((d.r + 31) / 32) {
             case 1: MERGE_MFMA(32); break;
             case 2: MERGE_MFMA(64); break;
@@ -727,12 +808,12 @@ lora_status lora_merge(const lora_linear_desc* desc, const void* W, const void* 
         }
 #undef MERGE_MFMA
     } else if (d.dtype == LORA_DTYPE_F32)
-        hipLaunchKernelGGL((lora_merge_kernel<true>), grid, dim3(256), 0, s, W, A, B, W_out, (int)d.N, (int)d.K,
-                           (int)d.r, scale);
+        { observe("lora_merge", s, 0); hipLaunchKernelGGL((lora_merge_kernel<true>), grid, dim3(256), 0, s, W, A, B, W_out, (int)d.N, (int)d.K,
+                           (int)d.r, scale); observe("lora_merge", s, 1); }
     else
-        hipLaunchKernelGGL((lora_merge_kernel<false>), grid, dim3(256),
+        { observe("lora_merge", s, 0); hipLaunchKernelGGL((lora_merge_kernel<false>), grid, dim3(256),
                            (size_t)d.r * (kMergeCols + kMergeRows) * sizeof(uint16_t), s, W, A, B, W_out, (int)d.N,
-                           (int)d.K, (int)d.r, scale);
+                           (int)d.K, (int)d.r, scale); observe("lora_merge", s, 1); }
     LAUNCH_CHECK("lora_merge");
     return ok();
 }
@@ -753,9 +834,9 @@ lora_status lora_dequant4(const uint8_t* Wq, const uint16_t* absmax, const float
     const int n_groups = (int)(N * K / 8);
     const dim3 grid((unsigned)std::min<int64_t>(cdiv(n_groups, 256), 256 * 16));
     if (out_dtype == LORA_DTYPE_F32)
-        hipLaunchKernelGGL((dequant4_kernel<true>), grid, dim3(256), 0, s, Wq, absmax, codebook, W_out, n_groups);
+        { observe("dequant4", s, 0); hipLaunchKernelGGL((dequant4_kernel<true>), grid, dim3(256), 0, s, Wq, absmax, codebook, W_out, n_groups); observe("dequant4", s, 1); }
     else
-        hipLaunchKernelGGL((dequant4_kernel<false>), grid, dim3(256), 0, s, Wq, absmax, codebook, W_out, n_groups);
+        { observe("dequant4", s, 0); hipLaunchKernelGGL((dequant4_kernel<false>), grid, dim3(256), 0, s, Wq, absmax, codebook, W_out, n_groups); observe("dequant4", s, 1); }
     LAUNCH_CHECK("dequant4");
     return ok();
 }

@@ -1,0 +1,63 @@
+// Byte ranges of the buffer resources the kernels build.
+//
+// A buffer resource describes [base, base + range) with a 32-bit range, and a
+// load whose offset lands past it returns zeros.  Every kernel therefore
+// builds its resources from a base near the data one workgroup (or one step)
+// touches, so that the range stays below 2^31 bytes for every descriptor the
+// C ABI accepts, and the out-of-range marker offset 2^31 can never be a valid
+// offset.  The same functions are used by the kernels when they build the
+// resources and by lora_linear_buffer_ranges, which lists the worst case of
+// each one for a descriptor (host tests check them against 2^31 - 1).
+#pragma once
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+namespace lora {
+
+constexpr uint64_t kMaxRange = 0x7FFFFFFFu;          // largest range a resource can describe
+constexpr int kSideBlock = 128;                      // token block of the rank planes (see zt_index)
+
+__host__ __device__ inline int64_t rmin64(int64_t a, int64_t b) { return a < b ? a : b; }
+
+// Rows [row0, row0 + rows) of a row-major bf16 matrix with C columns, clipped
+// to its `total` rows: the GEMM's operand panels (rows = 256), rank_z_lds's Y
+// block (128) and one rank_stream step (TM).
+__host__ __device__ inline uint64_t panel_bytes(int64_t total, int64_t row0, int64_t rows, int64_t C) {
+    return (uint64_t)rmin64(total - row0, rows) * (uint64_t)C * 2u;
+}
+
+// Input-gradient GEMM, W tile of one stage: rows c0 .. c0 + 63 of W [C][Q]
+// from column q0 on (the last row only up to Q).
+__host__ __device__ inline uint64_t gemm_wt_stage_bytes(int64_t C, int64_t Q, int64_t c0, int64_t q0) {
+    const int64_t rows_left = rmin64(C - c0, 64) < 1 ? 1 : rmin64(C - c0, 64);
+    return (uint64_t)(rows_left - 1) * (uint64_t)Q * 2u + (uint64_t)(Q - q0) * 2u;
+}
+
+// rank_stream, Y tile of one step: rows m0 .. m0 + TM - 1 of Y [M][C] from
+// column c0 on (the last row only up to C).
+__host__ __device__ inline uint64_t stream_y_bytes(int64_t M, int64_t C, int64_t m0, int64_t c0, int64_t TM) {
+    return (uint64_t)(rmin64(M - m0, TM) - 1) * (uint64_t)C * 2u + (uint64_t)(C - c0) * 2u;
+}
+
+// Rank planes (bf16 hi / lo of Z^T for the adapter gradients), token-block
+// major: element (j, m) of an [r][Mp] plane sits at zt_index(j, m, r), i.e.
+// blocks of 128 tokens, each holding its r rows of 128 consecutive tokens.
+// One rank_stream step then reads one contiguous block, whatever M is.
+__host__ __device__ inline size_t zt_index(int64_t j, int64_t m, int64_t r) {
+    return ((size_t)(m / kSideBlock) * (size_t)r + (size_t)j) * kSideBlock + (size_t)(m % kSideBlock);
+}
+
+// rank_stream, side tile of one step: rank rows j0 .. j0 + rl - 1 of one token
+// block, the first row from token offset `col` (0, or 64 for the second half
+// of a block with 64-token steps), each row TM tokens.
+__host__ __device__ inline uint64_t stream_side_bytes(int64_t rl, int64_t TM) {
+    return ((uint64_t)(rl - 1) * kSideBlock + (uint64_t)TM) * 2u;
+}
+
+// Small whole operands: A [r][K], B [N][r], B^T [r][N] (bf16).
+__host__ __device__ inline uint64_t whole_bytes(int64_t rows, int64_t cols) {
+    return (uint64_t)rows * (uint64_t)cols * 2u;
+}
+
+}  // namespace lora

@@ -20,7 +20,8 @@
 // 16x16x32 bf16 with float32 accumulation; Y^T fragments are gathered with
 // ds_read_b64_tr_b16.  The rank-side operand arrives the same way, as the two
 // bf16 planes hi = bf16(Z2^T), lo = bf16(Z2^T - hi) of [r][Mp] (tokens padded
-// with zeros to a multiple of 128), which zt_hilo writes from Z2 [M][r] float32.
+// with zeros to a multiple of 128, stored token-block major as zt_index gives),
+// which zt_hilo writes from Z2 [M][r] float32.
 #pragma once
 #include "lora_gemm.hpp"
 
@@ -30,11 +31,10 @@ constexpr int kRT = 128;      // tile edge (rows of Y x columns of Y)
 
 struct RankProblem {
     const uint16_t* Y;      // [M][C] bf16
-    const uint16_t* S;      // hi plane of Z2^T, bf16 rows [r][s_len]
+    const uint16_t* S;      // hi plane of Z2^T, bf16 [r][Mp] in zt_index order
     const uint16_t* S_lo;   // lo plane of Z2^T (same shape)
     float* part;            // [n_chunk][C][r]
     int C;
-    int s_len;              // side row length Mp (tokens padded to a multiple of 128)
     int n_tiles;            // 128-wide tiles of c
 };
 
@@ -109,8 +109,7 @@ __global__ __launch_bounds__(256) void rank_stream(const RankArgs a) {
     auto issue_y = [&](int t, uint8_t* Ys) {
         const int m0 = t * TM;
         const int c0 = o0;
-        const __amdgpu_buffer_rsrc_t rs =
-            make_rsrc(pr.Y + (size_t)m0 * C + c0, (uint64_t)(min(M - m0, TM) - 1) * C * 2 + (uint64_t)(C - c0) * 2);
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(pr.Y + (size_t)m0 * C + c0, stream_y_bytes(M, C, m0, c0, TM));
 #pragma unroll
         for (int i = 0; i < YLW; ++i) {
             const int b = wave * YLW + i;
@@ -119,24 +118,28 @@ __global__ __launch_bounds__(256) void rank_stream(const RankArgs a) {
             g2lds16<true>(rs, Ys + b * 1024, (c0 + ch < C) ? (uint32_t)(row * C + ch) * 2u : kOOB);
         }
     };
-    // side tile(s) of step t: rows j0 .. j0 + RPAD - 1 of S (and S_lo), columns
-    // t TM .. + TM - 1, rows of 2 TM bytes whose 16-byte chunk ch of row x sits
-    // at ch ^ side_swz(x); wave w issues loads b = SLW w .. of each plane, each
-    // SRL rows: row = SRL b + lane / (TM / 8)
+    // side tile(s) of step t: rank rows j0 .. j0 + RPAD - 1 of S (and S_lo), tokens
+    // t TM .. + TM - 1, which lie in one 128-token block of the planes (rows
+    // 256 bytes apart there); in LDS rows of 2 TM bytes whose 16-byte chunk ch of
+    // row x sits at ch ^ side_swz(x).  The resources start at row j0 of the
+    // step's block, so their range is a few KB whatever M is.  Wave w issues
+    // loads b = SLW w .. of each plane, each SRL rows: row = SRL b + lane / (TM / 8)
     constexpr int SLW = RPAD * TM / 2048;             // side loads per wave per plane
     constexpr int SRL = 1024 / (2 * TM);              // side rows per 1 KB load
     static_assert(SLW >= 1, "side tile smaller than one load per wave");
-    const __amdgpu_buffer_rsrc_t rsS = make_rsrc(pr.S, (uint64_t)r * pr.s_len * 2);
-    const __amdgpu_buffer_rsrc_t rsSl = make_rsrc(pr.S_lo, (uint64_t)r * pr.s_len * 2);
+    static_assert(kSideBlock % TM == 0, "a step stays inside one token block");
+    const uint64_t side_range = stream_side_bytes(rl, TM);
     auto issue_side = [&](int t, uint8_t* Ss) {
-        const int col0 = t * TM;
+        const int64_t m0 = (int64_t)t * TM;
+        const size_t base = zt_index(j0, m0, r);
+        const __amdgpu_buffer_rsrc_t rsS = make_rsrc(pr.S + base, side_range);
+        const __amdgpu_buffer_rsrc_t rsSl = make_rsrc(pr.S_lo + base, side_range);
 #pragma unroll
         for (int i = 0; i < SLW; ++i) {
             const int b = wave * SLW + i;
             const int row = SRL * b + lane / (TM / 8);
             const int ch = ((lane % (TM / 8)) ^ side_swz<TM>(row)) * 8;
-            const uint32_t off = (row < rl && col0 + ch < pr.s_len)
-                                     ? (uint32_t)((size_t)(j0 + row) * pr.s_len + col0 + ch) * 2u : kOOB;
+            const uint32_t off = row < rl ? (uint32_t)(row * kSideBlock + ch) * 2u : kOOB;
             g2lds16<true>(rsS, Ss + b * 1024, off);
             g2lds16<true>(rsSl, Ss + SM::SIDE + b * 1024, off);
         }
@@ -213,7 +216,8 @@ __global__ __launch_bounds__(256) void rank_stream(const RankArgs a) {
 // Z with the rank side in LDS: Z[m][j] = sum_c Y[m][c] F[j][c] (F bf16 rows [r][C]).
 // Workgroup (x, y): 8 waves; wave w owns rows m = 128 x + 16 w + (0 .. 15) (one MFMA
 // row block) and the workgroup the contraction chunk y, [cb, ce), chunk_c columns (a
-// multiple of 256).  F comes in 256-column slices through a double-buffered LDS pair
+// multiple of 256).  Y is addressed from the workgroup's first row (a 128-row
+// block stays below 2^29 bytes), so Y itself may exceed 2 GB.  F comes in 256-column slices through a double-buffered LDS pair
 // (row j of a slice: 512 bytes, 16-byte chunk ch stored at ch ^ (j % 16), so the 16
 // rows one fragment read touches hit distinct banks); each lane loads its Y fragment
 // (8 consecutive c of one row, 16 bytes) straight from global memory into registers,
@@ -229,14 +233,15 @@ __global__ __launch_bounds__(512) void rank_z_lds(const uint16_t* __restrict__ Y
     __shared__ __attribute__((aligned(1024))) uint8_t fs[2 * FBYTES];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int l16 = lane & 15, g4 = lane >> 4;
-    const int m = (int)blockIdx.x * 128 + wave * 16 + l16;
+    const int m0 = (int)blockIdx.x * 128;
+    const int m = m0 + wave * 16 + l16;
     const int cb = (int)blockIdx.y * chunk_c;
     const int ce = min(C, cb + chunk_c);
     const int nsl = (ce - cb + SC - 1) / SC;
     const int rl = min(r - j0, 16 * JB);
-    const __amdgpu_buffer_rsrc_t rsY = make_rsrc(Y, (uint64_t)M * C * 2);
-    const __amdgpu_buffer_rsrc_t rsF = make_rsrc(F, (uint64_t)r * C * 2);
-    const uint32_t yoff = m < M ? (uint32_t)((size_t)m * C + cb + 8 * g4) * 2u : kOOB;
+    const __amdgpu_buffer_rsrc_t rsY = make_rsrc(Y + (size_t)m0 * C, panel_bytes(M, m0, 128, C));
+    const __amdgpu_buffer_rsrc_t rsF = make_rsrc(F, whole_bytes(r, C));
+    const uint32_t yoff = m < M ? (uint32_t)((m - m0) * C + cb + 8 * g4) * 2u : kOOB;
     // F slice: load i (1 KB) covers rows 2 i and 2 i + 1; wave w issues i = JB w .. JB w + JB - 1
     auto issue_f = [&](int sl, uint8_t* buf) {
 #pragma unroll
@@ -298,15 +303,19 @@ __global__ __launch_bounds__(512) void rank_z_lds(const uint16_t* __restrict__ Y
     }
 }
 
-// rank_stream side planes: hi[j][m] = bf16(Z[m][j]), lo[j][m] = bf16(Z[m][j] - hi),
-// j < r, m < Mp (zero for m >= M); blockIdx.y selects one of two problems.
+// rank_stream side planes: hi(j, m) = bf16(Z[m][j]), lo(j, m) = bf16(Z[m][j] - hi),
+// j < r, m < Mp (zero for m >= M), stored at e = zt_index(j, m, r); blockIdx.y
+// selects one of two problems.
 __global__ __launch_bounds__(256) void zt_hilo(const float* __restrict__ z0, const float* __restrict__ z1,
                                                uint16_t* __restrict__ hi0, uint16_t* __restrict__ lo0,
                                                uint16_t* __restrict__ hi1, uint16_t* __restrict__ lo1, int M, int Mp,
                                                int r) {
     const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (e >= (int64_t)r * Mp) return;
-    const int j = (int)(e / Mp), m = (int)(e % Mp);
+    const int64_t blk = e / ((int64_t)r * kSideBlock);
+    const int rem = (int)(e - blk * r * kSideBlock);
+    const int j = rem / kSideBlock;
+    const int64_t m = blk * kSideBlock + rem % kSideBlock;
     const float* z = blockIdx.y ? z1 : z0;
     const float v = m < M ? z[(size_t)m * r + j] : 0.f;
     const __bf16 h = (__bf16)v;

@@ -25,6 +25,16 @@ def _desc(M, K, N, r, alpha, dtype) -> api.Desc:
     return api.Desc(M, K, N, r, float(alpha), _DTYPES[dtype])
 
 
+def _same(x, **ts):
+    """x and the adapter (and 16-bit weight) tensors share x's dtype and device."""
+    for name, t in ts.items():
+        if t.dtype != x.dtype:
+            raise TypeError(f"{name} has dtype {t.dtype} but the input has {x.dtype}; the layer computes in one "
+                            "dtype (cast the input, or build the layer in the input's dtype)")
+        if t.device != x.device:
+            raise ValueError(f"{name} is on {t.device} but the input is on {x.device}")
+
+
 class LoraLinearFunction(torch.autograd.Function):
     """H = X W^T + (alpha/r) (X A^T) B^T with W frozen (no gradient for W)."""
 
@@ -34,6 +44,7 @@ class LoraLinearFunction(torch.autograd.Function):
         K = x.shape[-1]
         X = x.reshape(-1, K).contiguous()
         N, r = B.shape
+        _same(X, W=W, A=A, B=B)
         desc = _desc(X.shape[0], K, N, r, alpha, X.dtype)
         H = torch.empty((X.shape[0], N), dtype=X.dtype, device=X.device)
         U = torch.empty((X.shape[0], r), dtype=torch.float32, device=X.device)
@@ -67,6 +78,7 @@ class QLoraLinearFunction(torch.autograd.Function):
         K = x.shape[-1]
         X = x.reshape(-1, K).contiguous()
         N, r = B.shape
+        _same(X, A=A, B=B)
         desc = _desc(X.shape[0], K, N, r, alpha, X.dtype)
         H = torch.empty((X.shape[0], N), dtype=X.dtype, device=X.device)
         U = torch.empty((X.shape[0], r), dtype=torch.float32, device=X.device)
@@ -107,6 +119,10 @@ class LoraLinear(torch.nn.Module):
         torch.nn.init.normal_(self.lora_A, std=1.0 / math.sqrt(in_features))
 
     def forward(self, x):
+        # the layer computes in its parameters' dtype (e.g. float32 activations
+        # from an autocast region are converted to bf16 here)
+        if x.dtype != self.weight.dtype:
+            x = x.to(self.weight.dtype)
         return LoraLinearFunction.apply(x, self.weight, self.lora_A, self.lora_B, self.alpha)
 
     @torch.no_grad()

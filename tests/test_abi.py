@@ -186,3 +186,71 @@ def test_python_binding_raises():
     with pytest.raises(lla.LoraError) as ei:
         lla.lora_linear_workspace_size(lla.Desc(0, 8, 8, 1, 1.0))
     assert ei.value.status == _lib.LORA_ERR_INVALID_ARG
+
+
+# ------------------------------------------------------------ buffer ranges
+MAX_RANGE = (1 << 31) - 1
+
+# descriptors at the edges of the supported range: 16-bit inputs above 2 GB,
+# the largest K and N, the largest rank, tiny K with many tokens
+EDGE_DESCS = [
+    dict(M=(1 << 30) // 4096 + 64, K=4096, N=64, r=32),          # X just over 2 GB (2^30 + 2^18 elements)
+    dict(M=(1 << 31) // 4096 - 1, K=4096, N=4096, r=128),        # X and dY just under 4 GB
+    dict(M=(1 << 31) // 4096 - 1, K=4096, N=4096, r=8),
+    dict(M=1023, K=1 << 21, N=1000, r=128),                      # K at 2^21
+    dict(M=1000, K=960, N=1 << 21, r=128),                       # N at 2^21
+    dict(M=(1 << 28) - 8, K=8, N=8, r=7),                        # 2^28 tokens: M r just under 2^31
+    dict(M=(1 << 24) - 1, K=128, N=128, r=128),                  # M r just under 2^31 at the top rank
+    dict(M=(1 << 25) - 1, K=64, N=64, r=64),
+    dict(M=65, K=(1 << 21) - 64, N=1000, r=100),
+]
+
+
+@pytest.mark.parametrize("quant", [False, True])
+@pytest.mark.parametrize("kw", EDGE_DESCS)
+def test_buffer_ranges_fit_32_bits(kw, quant):
+    """Every buffer resource the bf16 kernels build stays within the 2^31 - 1
+    bytes its range field can describe, so no valid load reads zeros."""
+    if quant and kw["K"] % 64:
+        pytest.skip("4-bit entry points need K % 64 == 0")
+    d = lla.Desc(kw["M"], kw["K"], kw["N"], kw["r"], 16.0)
+    ranges = lla.lora_linear_buffer_ranges(d, quant)
+    assert ranges, "no resources listed"
+    kernels = {k for k, _, _ in ranges}
+    assert any("lora_gemm (forward)" in k for k in kernels) and any("lora_gemm (dX)" in k for k in kernels)
+    assert any("rank_stream" in k for k in kernels) and any("rank_z_lds" in k for k in kernels)
+    too_big = [(k, o, b) for k, o, b in ranges if not 0 < b <= MAX_RANGE]
+    assert not too_big, too_big
+
+
+def test_buffer_ranges_x_over_2gb_is_blockwise():
+    """X of 2^30 + 2^18 bf16 elements (2.15 GB): the streamed U pass addresses
+    it in 128-row blocks (1 MB each), not as one resource over all of X."""
+    M, K = (1 << 30) // 4096 + 64, 4096
+    ranges = lla.lora_linear_buffer_ranges(lla.Desc(M, K, 64, 32, 16.0))
+    y = [b for k, o, b in ranges if k.startswith("rank_z_lds (U") and o.startswith("Y block")]
+    assert y == [128 * K * 2]
+    assert 2 * M * K > MAX_RANGE
+
+
+def test_buffer_ranges_f32_mode_builds_none():
+    assert lla.lora_linear_buffer_ranges(lla.Desc(64, 256, 256, 8, 32.0, lla.LORA_DTYPE_F32)) == []
+
+
+def test_buffer_ranges_rejects_bad_descriptor():
+    with pytest.raises(lla.LoraError):
+        lla.lora_linear_buffer_ranges(lla.Desc(64, 250, 256, 8, 32.0))
+    with pytest.raises(lla.LoraError):
+        lla.lora_linear_buffer_ranges(lla.Desc(64, 96, 256, 8, 32.0), quant=True)
+
+
+def test_launch_observer_set_and_clear():
+    """The observer can be set and removed; a call refused by validation
+    enqueues nothing, so the observer is never called."""
+    seen = []
+    lla.lora_set_launch_observer(lambda k, s, p: seen.append((k, p)))
+    try:
+        assert fwd(desc(K=250)) == _lib.LORA_ERR_UNSUPPORTED
+    finally:
+        lla.lora_set_launch_observer(None)
+    assert seen == []

@@ -51,30 +51,67 @@ def _write_counters(path, rows):
 
 
 def test_traffic_from_counter_csvs(tmp_path, monkeypatch):
-    """Counters are averaged over the forward GEMM's dispatches only and scaled
-    by what the same counter reads for the calibration copy of known size."""
+    """Counters are averaged over each GEMM's dispatches and scaled by what the
+    same counter reads for the calibration copy of known size."""
     fwd = "void lora::lora_gemm<false, 16, false, false, false>(lora::GemmArgs)"
     bwd = "void lora::lora_gemm<true, 16, false, false, false>(lora::GemmArgs)"
     neg = "void at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel_cuda(...)>"
     copy_kib = bench.COPY_BYTES / 1024
     _write_counters(tmp_path / "bench_FETCH_SIZE_counter_collection.csv",
-                    [(fwd, "FETCH_SIZE", 1000.0), (fwd, "FETCH_SIZE", 3000.0), (bwd, "FETCH_SIZE", 9e9)])
+                    [(fwd, "FETCH_SIZE", 1000.0), (fwd, "FETCH_SIZE", 3000.0), (bwd, "FETCH_SIZE", 5000.0)])
     _write_counters(tmp_path / "bench_WRITE_SIZE_counter_collection.csv",
-                    [(fwd, "WRITE_SIZE", 500.0), (bwd, "WRITE_SIZE", 9e9)])
+                    [(fwd, "WRITE_SIZE", 500.0), (bwd, "WRITE_SIZE", 700.0), ("grad_final", "WRITE_SIZE", 9e9)])
     _write_counters(tmp_path / "copy_FETCH_SIZE_counter_collection.csv", [(neg, "FETCH_SIZE", copy_kib / 2)])
     _write_counters(tmp_path / "copy_WRITE_SIZE_counter_collection.csv", [(neg, "WRITE_SIZE", copy_kib)])
     out = tmp_path / "traffic.json"
     monkeypatch.setattr(bench, "traffic_path", lambda workload: str(out))
     bench.write_traffic(argparse.Namespace(traffic_from=str(tmp_path), workload="attn_proj_4096"))
     t = json.load(open(out))
-    assert t["fetch_kib_per_dispatch"] == 2000.0 and t["write_kib_per_dispatch"] == 500.0
+    f, b = t["kernels"][bench.GEMM_FWD], t["kernels"][bench.GEMM_DX]
+    assert f["fetch_kib_per_dispatch"] == 2000.0 and f["write_kib_per_dispatch"] == 500.0
+    assert b["fetch_kib_per_dispatch"] == 5000.0 and b["write_kib_per_dispatch"] == 700.0
     assert t["copy_fetch_factor"] == 0.5 and t["copy_write_factor"] == 1.0
-    assert t["hbm_read_bytes_per_dispatch"] == 2000 * 1024 * 2
-    assert t["hbm_write_bytes_per_dispatch"] == 500 * 1024
+    assert f["hbm_read_bytes_per_dispatch"] == 2000 * 1024 * 2
+    assert f["hbm_write_bytes_per_dispatch"] == 500 * 1024
     assert t["kernel_source_hash"] == bench.kernel_source_hash()
+    assert bench.load_traffic("attn_proj_4096") == {bench.GEMM_FWD: 2000 * 2048 + 500 * 1024,
+                                                   bench.GEMM_DX: 5000 * 2048 + 700 * 1024}
     # the stored figures are used only while the GEMM's sources are unchanged
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 16)
     assert bench.load_traffic("attn_proj_4096") is None
+
+
+def test_gemm_flops_and_bytes():
+    """Per-launch algorithmic counts of the two GEMMs: the in-tile forms also
+    carry the rank-r product (U = X A^T, V = dY B); their sum with the
+    adapter-gradient products is the layer's 4MNK + 6Mr(K+N)."""
+    l = workloads.workload("attn_proj_4096").linears[0]
+    M, K, N, r = l.M, l.K, l.N, l.r
+    assert bench.gemm_flops(l, bench.GEMM_FWD) == 2 * M * N * K + 2 * M * N * r + 2 * M * r * K
+    assert bench.gemm_flops(l, bench.GEMM_DX) == 2 * M * N * K + 2 * M * K * r + 2 * M * r * N
+    grads = 2 * M * r * K + 2 * M * N * r      # dA = s V^T X, dB = s dY^T U
+    assert bench.gemm_flops(l, bench.GEMM_FWD) + bench.gemm_flops(l, bench.GEMM_DX) + grads == l.flops()
+    # r > 16: the rank-r product comes from the streamed pass, not the GEMM
+    d = workloads.workload("decoder_layer_r64").linears[0]
+    assert bench.gemm_flops(d, bench.GEMM_FWD) == 2 * d.M * d.N * d.K + 2 * d.M * d.N * d.r
+    assert bench.gemm_flops(d, bench.GEMM_DX + " (split)") == 2 * d.M * d.K * d.N + 2 * d.M * d.K * d.r
+    assert bench.gemm_bytes(l, bench.GEMM_FWD) == bench.fwd_bytes(l)
+    assert bench.gemm_bytes(l, bench.GEMM_DX) == (2 * M * N + 2 * N * K + 2 * M * K + 2 * r * (K + N) + 4 * M * r
+                                                  + 8 * r * M)
+
+
+def test_percentile_and_input_sharing():
+    assert bench.percentile([4.0, 1.0, 3.0, 2.0, 5.0], 0.5) == 3.0
+    assert bench.percentile([1.0, 2.0], 0.1) == 1.1
+    wl = workloads.workload("decoder_layer_r64")
+    layer = [{"X": object()} for _ in wl.linears]
+    xs = [d["X"] for d in layer]
+    bench.share_inputs(wl, layer)
+    names = [l.name.split("_")[-1] for l in wl.linears]
+    got = dict(zip(names, (d["X"] for d in layer)))
+    assert got["q"] is got["k"] is got["v"] is xs[0]
+    assert got["gate"] is got["up"] is xs[names.index("gate")]
+    assert got["o"] is xs[names.index("o")] and got["down"] is xs[names.index("down")]
 
 
 def test_missing_counters_are_an_error(tmp_path, monkeypatch):
