@@ -9,15 +9,17 @@ several input sets are rotated so the 256 MB Infinity Cache cannot serve the
 operands of one step from the previous one (cold operands, as in a training
 step where W was last touched a layer stack ago).
 
-Prints one JSON line.  Timing passes, all on the stream the library launches on:
+Prints one JSON line.  Timing passes, both on the stream the library launches on:
   1. the timed region: W warm-up steps, then K steps between two HIP events,
      device-synchronised on both sides, nothing else inside (`value`);
-  2. the same K steps with one HIP event at every step boundary: the spread of
-     the step time (p10 / p50 / p90);
-  3. the same K steps with HIP events around every kernel the library
-     enqueues (through its launch observer): per-kernel mean durations, from
-     which the roofline entries of the GEMMs are computed.  The dominant
-     kernel (`roofline`) is the GEMM with the largest measured time per step.
+  2. the same K steps again with the library's kernel timer set: HIP events
+     attached to every kernel's dispatch (hipExtLaunchKernel) record its start
+     and end without adding commands between the kernels, so the kernels run
+     back to back as in the timed region.  They give each kernel's mean
+     duration (the roofline entries of the GEMMs; the dominant kernel,
+     `roofline`, is the GEMM with the largest measured time per step) and the
+     spread of the step time, first kernel start to last kernel end
+     (p10 / p50 / p90).
 The CPU baseline times the float64 oracle on a bounded sample of the same
 workload on the host cores.
 
@@ -31,6 +33,7 @@ Extra modes (used to produce the committed counter summaries):
 from __future__ import annotations
 
 import argparse
+import ctypes
 import csv
 import glob
 import hashlib
@@ -367,6 +370,36 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": COPY_BYTES}))
 
 
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime the library itself uses (its
+    symbols resolved through the library's handle)."""
+
+    def __init__(self, lib):
+        self.lib = lib
+        self.made = []
+
+    def _ok(self, err, what):
+        if err != 0:
+            raise RuntimeError(f"{what} failed with HIP error {err}")
+
+    def create(self) -> int:
+        ev = ctypes.c_void_p()
+        self._ok(self.lib.hipEventCreate(ctypes.byref(ev)), "hipEventCreate")
+        self.made.append(ev.value)
+        return ev.value
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        ms = ctypes.c_float()
+        self._ok(self.lib.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)),
+                 "hipEventElapsedTime")
+        return ms.value
+
+    def destroy_all(self):
+        for e in self.made:
+            self.lib.hipEventDestroy(ctypes.c_void_p(e))
+        self.made = []
+
+
 def percentile(vals, q):
     v = sorted(vals)
     if not v:
@@ -463,38 +496,36 @@ def main(argv=None):
     wall = time.perf_counter() - wall0
     ms_step = t_start.elapsed_time(t_end) / args.steps
 
-    # 2. step-time spread: one event at every step boundary
-    bounds = [mk() for _ in range(args.steps + 1)]
-    bounds[0].record(stream)
-    for i in range(args.steps):
-        run(i)
-        bounds[i + 1].record(stream)
-    torch.cuda.synchronize()
-    step_ms = [bounds[i].elapsed_time(bounds[i + 1]) for i in range(args.steps)]
+    # 2. the same steps with events attached to every kernel's dispatch
+    hev = HipEvents(lla.load())
+    records = []          # (step, linear index, kernel label, start event, stop event)
+    cur_step = [0]
 
-    # 3. per-kernel durations: events around every kernel the library enqueues
-    records, pending = [], {}
+    def timer(kernel, _stream):
+        a, b = hev.create(), hev.create()
+        records.append((cur_step[0], stepper.current, kernel, a, b))
+        return a, b
 
-    def observer(kernel, _stream, phase):
-        if phase == 0:
-            e = mk()
-            e.record(stream)
-            pending[kernel] = e
-        else:
-            e = mk()
-            e.record(stream)
-            records.append((stepper.current, kernel, pending.pop(kernel), e))
-
-    lla.lora_set_launch_observer(observer)
+    lla.lora_set_kernel_timer(timer)
     try:
+        torch.cuda.synchronize()
         for i in range(args.steps):
+            cur_step[0] = i
             step(i)
         torch.cuda.synchronize()
     finally:
-        lla.lora_set_launch_observer(None)
+        lla.lora_set_kernel_timer(None)
     kernel_us = {}
-    for li, kernel, a, b in records:
-        kernel_us.setdefault((li, kernel), []).append(a.elapsed_time(b) * 1e3)
+    first = {}
+    for si, li, kernel, a, b in records:
+        kernel_us.setdefault((li, kernel), []).append(hev.elapsed_ms(a, b) * 1e3)
+        first.setdefault(si, (a, b))
+    last = {}
+    for si, li, kernel, a, b in records:
+        last[si] = b
+    step_ms = [hev.elapsed_ms(first[i][0], last[i]) for i in range(args.steps)]
+    timer_ms_step = hev.elapsed_ms(first[0][0], last[args.steps - 1]) / args.steps
+    hev.destroy_all()
 
     flops = wl.flops()
     tflops = flops / (ms_step * 1e-3) / 1e12
@@ -520,6 +551,7 @@ def main(argv=None):
                    "input_sets": args.input_sets, "description": wl.description},
         "tokens_per_s": round(tokens_s, 1), "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "step_ms_p10_p50_p90": [round(p10, 4), round(p50, 4), round(p90, 4)],
+        "timed_kernels_ms_per_step": round(timer_ms_step, 4),
         "algorithmic_gflop_per_step": round(flops / 1e9, 3), "wall_s_timed": round(wall, 3),
         "per_linear": per_linear,
         "roofline": dict(dominant),

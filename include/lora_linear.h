@@ -18,7 +18,7 @@
  *
  * Memory: every pointer is caller-owned device memory (except `desc`, which is
  * host memory).  The library allocates nothing, keeps no state between calls
- * (apart from the optional launch observer below),
+ * (apart from the optional kernel timer below),
  * never modifies an input, and enqueues all work on `stream` (a hipStream_t
  * passed as void*; NULL means the null stream).  Calls return once the work is
  * enqueued; device faults surface at the caller's next synchronisation.
@@ -182,18 +182,23 @@ lora_status lora_linear_buffer_ranges(const lora_linear_desc* desc, int32_t quan
                                       int32_t capacity, int32_t* count);
 
 /*
- * Launch observer (a profiling aid for callers that time the kernels inside
- * one call with events on the call's stream).  When set, every entry point
- * calls fn(user, kernel, stream, 0) right before it enqueues each kernel and
- * fn(user, kernel, stream, 1) right after, on the calling thread, with a
- * static kernel label ("lora_gemm forward", "lora_gemm dX", "rank_stream",
- * "grad_final", ...) and the stream passed to the entry point.  NULL removes
- * the observer.  It is the library's only process-wide setting: set or clear
- * it while no other thread is inside the library.
+ * Kernel timer (a profiling aid for callers that time the kernels inside one
+ * call).  When set, every entry point calls
+ *   fn(user, kernel, stream, &start, &stop)
+ * on the calling thread right before it enqueues each kernel, with a static
+ * kernel label ("lora_gemm forward", "lora_gemm dX", "rank_stream",
+ * "grad_final", ...) and the stream passed to the entry point.  fn may set
+ * start and stop to events (hipEvent_t, created by the caller, as void*); the
+ * library attaches them to that kernel's dispatch (hipExtLaunchKernel), so
+ * they record the kernel's own start and end and add no commands between the
+ * kernels.  Left NULL, the kernel launches untimed.  fn(NULL) removes the
+ * timer.  It is the library's only process-wide setting: set or clear it
+ * while no other thread is inside the library.
  */
-typedef void (*lora_launch_observer)(void* user, const char* kernel, void* stream, int32_t phase);
+typedef void (*lora_kernel_timer)(void* user, const char* kernel, void* stream, void** start_event,
+                                  void** stop_event);
 
-void lora_set_launch_observer(lora_launch_observer fn, void* user);
+void lora_set_kernel_timer(lora_kernel_timer fn, void* user);
 
 /* Static text for a status code. */
 const char* lora_status_string(lora_status status);

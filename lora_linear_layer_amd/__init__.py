@@ -7,11 +7,11 @@ from ._lib import (LIB_PATH, LORA_DTYPE_BF16, LORA_DTYPE_F32, LORA_FLAG_ACCUM_GR
                    load)
 from .api import (Desc, LoraError, lora_dequant4, lora_linear_buffer_ranges, lora_linear_bwd,  # noqa: F401
                   lora_linear_fwd, lora_linear_workspace_size, lora_merge, lora_qlinear_bwd, lora_qlinear_fwd,
-                  lora_set_launch_observer)
+                  lora_set_kernel_timer)
 
 __all__ = [
     "Desc", "LoraError", "lora_linear_workspace_size", "lora_linear_fwd", "lora_linear_bwd",
     "lora_qlinear_fwd", "lora_qlinear_bwd", "lora_dequant4", "lora_merge", "lora_linear_buffer_ranges",
-    "lora_set_launch_observer", "load", "LIB_PATH",
+    "lora_set_kernel_timer", "load", "LIB_PATH",
     "LORA_DTYPE_BF16", "LORA_DTYPE_F32", "LORA_FLAG_ACCUM_GRADS",
 ]

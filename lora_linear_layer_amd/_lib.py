@@ -26,11 +26,12 @@ LORA_FLAG_ACCUM_GRADS = 0x1
 EXPORTED = (
     "lora_linear_workspace_size", "lora_linear_fwd", "lora_linear_bwd",
     "lora_qlinear_fwd", "lora_qlinear_bwd", "lora_dequant4", "lora_merge",
-    "lora_linear_buffer_ranges", "lora_set_launch_observer", "lora_status_string", "lora_last_error",
+    "lora_linear_buffer_ranges", "lora_set_kernel_timer", "lora_status_string", "lora_last_error",
 )
 
-# void (*)(void* user, const char* kernel, void* stream, int32_t phase)
-LAUNCH_OBSERVER = ctypes.CFUNCTYPE(None, ctypes.c_void_p, ctypes.c_char_p, ctypes.c_void_p, ctypes.c_int32)
+# void (*)(void* user, const char* kernel, void* stream, void** start_event, void** stop_event)
+KERNEL_TIMER = ctypes.CFUNCTYPE(None, ctypes.c_void_p, ctypes.c_char_p, ctypes.c_void_p,
+                                ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p))
 
 
 class LoraLinearDesc(ctypes.Structure):
@@ -75,8 +76,8 @@ def load() -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = ctypes.c_int
-    lib.lora_set_launch_observer.argtypes = [LAUNCH_OBSERVER, ctypes.c_void_p]
-    lib.lora_set_launch_observer.restype = None
+    lib.lora_set_kernel_timer.argtypes = [KERNEL_TIMER, ctypes.c_void_p]
+    lib.lora_set_kernel_timer.restype = None
     lib.lora_status_string.argtypes = [ctypes.c_int]
     lib.lora_status_string.restype = ctypes.c_char_p
     lib.lora_last_error.argtypes = []

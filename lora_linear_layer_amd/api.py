@@ -143,22 +143,30 @@ def lora_linear_buffer_ranges(desc: Desc, quant: bool = False) -> list:
     return [(arr[i].kernel.decode(), arr[i].operand.decode(), int(arr[i].bytes)) for i in range(n.value)]
 
 
-_observer_ref = None      # keeps the ctypes callback alive while the library holds it
+_timer_ref = None      # keeps the ctypes callback alive while the library holds it
 
 
-def lora_set_launch_observer(fn) -> None:
-    """fn(kernel: str, stream: int, phase: int) is called right before (phase
-    0) and right after (phase 1) each kernel the library enqueues; None
-    removes it (see include/lora_linear.h)."""
-    global _observer_ref
+def lora_set_kernel_timer(fn) -> None:
+    """fn(kernel: str, stream: int) -> (start_event, stop_event) or None is
+    asked before each kernel the library enqueues; the events (hipEvent_t
+    handles as ints, created by the caller) are attached to that kernel's
+    dispatch and record its start and end.  None removes the timer (see
+    include/lora_linear.h)."""
+    global _timer_ref
     lib = _lib.load()
     if fn is None:
-        lib.lora_set_launch_observer(_lib.LAUNCH_OBSERVER(), None)
-        _observer_ref = None
+        lib.lora_set_kernel_timer(_lib.KERNEL_TIMER(), None)
+        _timer_ref = None
         return
-    cb = _lib.LAUNCH_OBSERVER(lambda user, kernel, stream, phase: fn(kernel.decode(), stream or 0, int(phase)))
-    lib.lora_set_launch_observer(cb, None)
-    _observer_ref = cb
+
+    def cb(user, kernel, stream, start, stop):
+        ev = fn(kernel.decode(), stream or 0)
+        if ev is not None:
+            start[0], stop[0] = ev[0], ev[1]
+
+    c = _lib.KERNEL_TIMER(cb)
+    lib.lora_set_kernel_timer(c, None)
+    _timer_ref = c
 
 
 def lora_linear_fwd(desc: Desc, X, W, A, B, H, U_save=None, ws=None, ws_bytes=None, stream=None):

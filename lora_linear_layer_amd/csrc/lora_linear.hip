@@ -3,6 +3,7 @@
 // call), workspace planning, kernel selection and launches on the caller's
 // stream.  No allocation, no state, no synchronisation.
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <algorithm>
 #include <atomic>
@@ -44,15 +45,34 @@ lora_status ok() {
     return LORA_OK;
 }
 
-// Launch observer (lora_set_launch_observer): called right before and right
-// after each kernel is enqueued.
-std::atomic<lora_launch_observer> g_observer{nullptr};
-std::atomic<void*> g_observer_user{nullptr};
+// Kernel timer (lora_set_kernel_timer): asked for a start and a stop event
+// before each kernel is enqueued; events it returns are attached to that
+// kernel's dispatch (hipExtLaunchKernel), so they record the kernel itself
+// without adding commands between the kernels.
+std::atomic<lora_kernel_timer> g_timer{nullptr};
+std::atomic<void*> g_timer_user{nullptr};
 
-void observe(const char* kernel, hipStream_t st, int phase) {
-    const lora_launch_observer fn = g_observer.load(std::memory_order_acquire);
-    if (fn) fn(g_observer_user.load(std::memory_order_relaxed), kernel, static_cast<void*>(st), phase);
+void kernel_events(const char* kernel, hipStream_t st, hipEvent_t* start, hipEvent_t* stop) {
+    *start = *stop = nullptr;
+    const lora_kernel_timer fn = g_timer.load(std::memory_order_acquire);
+    if (!fn) return;
+    void *a = nullptr, *b = nullptr;
+    fn(g_timer_user.load(std::memory_order_relaxed), kernel, static_cast<void*>(st), &a, &b);
+    *start = static_cast<hipEvent_t>(a);
+    *stop = static_cast<hipEvent_t>(b);
 }
+
+// Every kernel of the library is enqueued through this: a plain launch, or,
+// while a kernel timer is set, a launch with the timer's events attached.
+#define LAUNCH(label, kernel, grid, block, shmem, stream, ...)                                          \
+    do {                                                                                                \
+        hipEvent_t ev0_, ev1_;                                                                          \
+        kernel_events(label, stream, &ev0_, &ev1_);                                                     \
+        if (ev0_ || ev1_)                                                                               \
+            hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, ev0_, ev1_, 0u, __VA_ARGS__);     \
+        else                                                                                            \
+            hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);                        \
+    } while (0)
 
 constexpr int64_t kMaxElems = (int64_t(1) << 31) - 1;
 constexpr int64_t kMaxDim = int64_t(1) << 21;   // K, N bound: one 256-row tile stays under 2 GB
@@ -254,7 +274,7 @@ lora_status launched(const char* what) {
 template <bool TRANS, int RPAD, bool ZIN, bool Q4>
 void launch_gemm_t(const GemmArgs& a, hipStream_t st) {
     const int tiles = (int)(cdiv(a.P, g2::BP) * cdiv(a.Q, g2::BQ));
-    { observe(TRANS ? "lora_gemm dX" : "lora_gemm forward", st, 0); hipLaunchKernelGGL((lora_gemm<TRANS, RPAD, ZIN, Q4>), dim3(tiles), dim3(g2w::NT), 0, st, a); observe(TRANS ? "lora_gemm dX" : "lora_gemm forward", st, 1); }
+    LAUNCH(TRANS ? "lora_gemm dX" : "lora_gemm forward", (lora_gemm<TRANS, RPAD, ZIN, Q4>), dim3(tiles), dim3(g2w::NT), 0, st, a);
 }
 
 // In-tile rank-r product for r <= 16 with 16-bit weights: the forward forms
@@ -284,11 +304,11 @@ void launch_gemm_zin(GemmArgs a, const SplitPlan& sp, hipStream_t st) {
         a.kc = sp.kc;
         const int T = (int)(cdiv(a.P, g2::BP) * cdiv(a.Q, g2::BQ));
         const int units = sp.first + (T - sp.first) * sp.split;
-        { observe(TRANS ? "lora_gemm dX (split)" : "lora_gemm forward (split)", st, 0); hipLaunchKernelGGL((lora_gemm<TRANS, RPAD, true, Q4, true>), dim3(units), dim3(g2w::NT), 0, st, a); observe(TRANS ? "lora_gemm dX (split)" : "lora_gemm forward (split)", st, 1); }
+        LAUNCH(TRANS ? "lora_gemm dX (split)" : "lora_gemm forward (split)", (lora_gemm<TRANS, RPAD, true, Q4, true>), dim3(units), dim3(g2w::NT), 0, st, a);
         SplitFinishArgs f{a.Part, a.Out, a.P, a.Q, (int)cdiv(a.P, g2::BP), (int)cdiv(a.Q, g2::BQ), sp.first,
                           T - sp.first, sp.split};
         const int64_t n = (int64_t)(T - sp.first) * (g2::BP * g2::BQ / 4);
-        { observe("split_finish", st, 0); hipLaunchKernelGGL(split_finish, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, st, f); observe("split_finish", st, 1); }
+        LAUNCH("split_finish", split_finish, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, st, f);
         return;
     }
     launch_gemm_t<TRANS, RPAD, true, Q4>(a, st);
@@ -321,8 +341,8 @@ void launch_rank_z(const lora_linear_desc& d, const uint16_t* Y, int64_t C, cons
     const dim3 grid((unsigned)cdiv(d.M, 128), (unsigned)n_used, 1);
     for (int j0 = 0; j0 < d.r; j0 += 64) {        // 64 rank columns per launch
         const int jb = (int)cdiv(std::min<int64_t>(d.r - j0, 64), 16);
-#define RZ(J) do { observe("rank_z_lds", st, 0); hipLaunchKernelGGL((rank_z_lds<J>), grid, dim3(512), 0, st, Y, F_rows, out, (int)d.M, (int)C, \
-                                 (int)d.r, j0, chunk_c); observe("rank_z_lds", st, 1); } while (0)
+#define RZ(J) LAUNCH("rank_z_lds", (rank_z_lds<J>), grid, dim3(512), 0, st, Y, F_rows, out, (int)d.M, (int)C, \
+                    (int)d.r, j0, chunk_c)
         switch (jb) {
             case 1: RZ(1); break;
             case 2: RZ(2); break;
@@ -333,7 +353,7 @@ void launch_rank_z(const lora_linear_desc& d, const uint16_t* Y, int64_t C, cons
     }
     if (n_used > 1) {
         const int64_t n = d.M * d.r;
-        { observe("partial_sum", st, 0); hipLaunchKernelGGL(partial_sum, dim3((unsigned)cdiv(n, 1024)), dim3(256), 0, st, zpart, Z, n, n_used); observe("partial_sum", st, 1); }
+        LAUNCH("partial_sum", partial_sum, dim3((unsigned)cdiv(n, 1024)), dim3(256), 0, st, zpart, Z, n, n_used);
     }
 }
 
@@ -358,8 +378,8 @@ lora_status launch_adapter_grads(const lora_linear_desc& d, const Plan& plan, ch
     uint16_t* const ut_hi = zt_plane(plan, wsb, d.r, 2);
     uint16_t* const ut_lo = zt_plane(plan, wsb, d.r, 3);
     if (!planes_ready) {
-        { observe("zt_hilo", st, 0); hipLaunchKernelGGL(zt_hilo, dim3((unsigned)cdiv(d.r * plan.Mp, 256), 2), dim3(256), 0, st, V, U, vt_hi,
-                           vt_lo, ut_hi, ut_lo, (int)d.M, (int)plan.Mp, (int)d.r); observe("zt_hilo", st, 1); }
+        LAUNCH("zt_hilo", zt_hilo, dim3((unsigned)cdiv(d.r * plan.Mp, 256), 2), dim3(256), 0, st, V, U, vt_hi,
+                           vt_lo, ut_hi, ut_lo, (int)d.M, (int)plan.Mp, (int)d.r);
         LAUNCH_CHECK("zt_hilo");
     }
     a.prob[0] = RankProblem{X, vt_hi, vt_lo, ga, (int)d.K, (int)cdiv(d.K, kRT)};
@@ -373,9 +393,9 @@ lora_status launch_adapter_grads(const lora_linear_desc& d, const Plan& plan, ch
     for (int j0 = 0; j0 < d.r; j0 += 64) {        // ranks above 64: one launch per 64 columns
         a.j0 = j0;
         switch (rpad_of(std::min<int64_t>(d.r - j0, 64))) {
-            case 16: { observe("rank_stream", st, 0); hipLaunchKernelGGL((rank_stream<16>), grid, dim3(256), 0, st, a); observe("rank_stream", st, 1); } break;
-            case 32: { observe("rank_stream", st, 0); hipLaunchKernelGGL((rank_stream<32>), grid, dim3(256), 0, st, a); observe("rank_stream", st, 1); } break;
-            default: { observe("rank_stream", st, 0); hipLaunchKernelGGL((rank_stream<64>), grid, dim3(256), 0, st, a); observe("rank_stream", st, 1); } break;
+            case 16: LAUNCH("rank_stream", (rank_stream<16>), grid, dim3(256), 0, st, a); break;
+            case 32: LAUNCH("rank_stream", (rank_stream<32>), grid, dim3(256), 0, st, a); break;
+            default: LAUNCH("rank_stream", (rank_stream<64>), grid, dim3(256), 0, st, a); break;
         }
     }
     LAUNCH_CHECK("rank_stream(dA, dB)");
@@ -391,7 +411,7 @@ lora_status launch_adapter_grads(const lora_linear_desc& d, const Plan& plan, ch
     f.s = d.alpha / (float)d.r;
     f.f32_out = 0;
     f.accumulate = (d.flags & LORA_FLAG_ACCUM_GRADS) ? 1 : 0;
-    { observe("grad_final", st, 0); hipLaunchKernelGGL(grad_final, dim3((unsigned)cdiv((d.K + d.N) * d.r, 256)), dim3(256), 0, st, f); observe("grad_final", st, 1); }
+    LAUNCH("grad_final", grad_final, dim3((unsigned)cdiv((d.K + d.N) * d.r, 256)), dim3(256), 0, st, f);
     LAUNCH_CHECK("grad_final");
     return LORA_OK;
 }
@@ -466,8 +486,8 @@ lora_status bwd_bf16(const lora_linear_desc& d, bool quant, const void* dY, cons
     const bool v_in_tile = dX != nullptr && dx_in_tile(quant, r, sp);
     if (!v_in_tile) {
         uint16_t* const BT = reinterpret_cast<uint16_t*>(wsb + plan.off_bt);
-        { observe("transpose_rank", st, 0); hipLaunchKernelGGL(transpose_rank, dim3((unsigned)cdiv(d.r * d.N, 256)), dim3(256), 0, st, B16, BT,
-                           (int)d.N, (int)d.r); observe("transpose_rank", st, 1); }
+        LAUNCH("transpose_rank", transpose_rank, dim3((unsigned)cdiv(d.r * d.N, 256)), dim3(256), 0, st, B16, BT,
+                           (int)d.N, (int)d.r);
         LAUNCH_CHECK("transpose_rank");
         launch_rank_z(d, dY16, d.N, BT, V, zpart, st);
         LAUNCH_CHECK("rank_z_lds(V)");
@@ -510,7 +530,7 @@ lora_status bwd_bf16(const lora_linear_desc& d, bool quant, const void* dY, cons
 template <int RMODE>
 void launch_f32_fused(const F32FusedArgs& a, hipStream_t st) {
     const dim3 grid((unsigned)cdiv(a.Q, 64), (unsigned)cdiv(a.P, 64));
-    { observe("f32_fused", st, 0); hipLaunchKernelGGL((f32_fused<RMODE>), grid, dim3(256), 0, st, a); observe("f32_fused", st, 1); }
+    LAUNCH("f32_fused", (f32_fused<RMODE>), grid, dim3(256), 0, st, a);
 }
 
 void launch_f32_fused_mode(int rmode, const F32FusedArgs& a, hipStream_t st) {
@@ -528,8 +548,8 @@ lora_status fwd_f32(const lora_linear_desc& d, bool quant, const void* X, const 
     const Plan plan = make_plan(d);
     float* U = U_save ? U_save : reinterpret_cast<float*>(static_cast<char*>(ws) + plan.off_u);
     const int M = (int)d.M, K = (int)d.K, N = (int)d.N, r = (int)d.r;
-    { observe("f32_skinny", st, 0); hipLaunchKernelGGL(f32_skinny, dim3((unsigned)cdiv((int64_t)M * r, 256)), dim3(256), 0, st,
-                       static_cast<const float*>(X), static_cast<const float*>(A), U, M, K, r, 0); observe("f32_skinny", st, 1); }
+    LAUNCH("f32_skinny", f32_skinny, dim3((unsigned)cdiv((int64_t)M * r, 256)), dim3(256), 0, st,
+                       static_cast<const float*>(X), static_cast<const float*>(A), U, M, K, r, 0);
     LAUNCH_CHECK("f32_skinny(U)");
     F32FusedArgs a{};
     a.L = static_cast<const float*>(X);
@@ -555,14 +575,14 @@ lora_status bwd_f32(const lora_linear_desc& d, bool quant, const void* dY, const
     const float s = d.alpha / (float)d.r;
     const float* dYf = static_cast<const float*>(dY);
     const float* Xf = static_cast<const float*>(X);
-    { observe("f32_skinny", st, 0); hipLaunchKernelGGL(f32_skinny, dim3((unsigned)cdiv((int64_t)M * r, 256)), dim3(256), 0, st,
-                       dYf, static_cast<const float*>(B), V, M, N, r, 1); observe("f32_skinny", st, 1); }
+    LAUNCH("f32_skinny", f32_skinny, dim3((unsigned)cdiv((int64_t)M * r, 256)), dim3(256), 0, st,
+                       dYf, static_cast<const float*>(B), V, M, N, r, 1);
     LAUNCH_CHECK("f32_skinny(V)");
     const float* U = U_saved;
     if (!U) {
         float* Uw = reinterpret_cast<float*>(wsb + plan.off_u);
-        { observe("f32_skinny", st, 0); hipLaunchKernelGGL(f32_skinny, dim3((unsigned)cdiv((int64_t)M * r, 256)), dim3(256), 0, st,
-                           Xf, static_cast<const float*>(A), Uw, M, K, r, 0); observe("f32_skinny", st, 1); }
+        LAUNCH("f32_skinny", f32_skinny, dim3((unsigned)cdiv((int64_t)M * r, 256)), dim3(256), 0, st,
+                           Xf, static_cast<const float*>(A), Uw, M, K, r, 0);
         LAUNCH_CHECK("f32_skinny(U)");
         U = Uw;
     }
@@ -580,11 +600,11 @@ lora_status bwd_f32(const lora_linear_desc& d, bool quant, const void* dY, const
         LAUNCH_CHECK("f32_fused(dX)");
     }
     const int acc = (d.flags & LORA_FLAG_ACCUM_GRADS) ? 1 : 0;
-    { observe("f32_grad", st, 0); hipLaunchKernelGGL(f32_grad, dim3((unsigned)cdiv((int64_t)K * r, 256)), dim3(256), 0, st,
-                       Xf, (const float*)V, static_cast<float*>(dA), M, K, r, s, 1, acc); observe("f32_grad", st, 1); }
+    LAUNCH("f32_grad", f32_grad, dim3((unsigned)cdiv((int64_t)K * r, 256)), dim3(256), 0, st,
+                       Xf, (const float*)V, static_cast<float*>(dA), M, K, r, s, 1, acc);
     LAUNCH_CHECK("f32_grad(dA)");
-    { observe("f32_grad", st, 0); hipLaunchKernelGGL(f32_grad, dim3((unsigned)cdiv((int64_t)N * r, 256)), dim3(256), 0, st,
-                       dYf, U, static_cast<float*>(dB), M, N, r, s, 0, acc); observe("f32_grad", st, 1); }
+    LAUNCH("f32_grad", f32_grad, dim3((unsigned)cdiv((int64_t)N * r, 256)), dim3(256), 0, st,
+                       dYf, U, static_cast<float*>(dB), M, N, r, s, 0, acc);
     LAUNCH_CHECK("f32_grad(dB)");
     return ok();
 }
@@ -660,9 +680,9 @@ const char* lora_status_string(lora_status s) {
 
 const char* lora_last_error(void) { return g_last_error.c_str(); }
 
-void lora_set_launch_observer(lora_launch_observer fn, void* user) {
-    g_observer_user.store(user, std::memory_order_relaxed);
-    g_observer.store(fn, std::memory_order_release);
+void lora_set_kernel_timer(lora_kernel_timer fn, void* user) {
+    g_timer_user.store(user, std::memory_order_relaxed);
+    g_timer.store(fn, std::memory_order_release);
 }
 
 lora_status lora_linear_workspace_size(const lora_linear_desc* desc, size_t* bytes) {
@@ -798,8 +818,8 @@ lora_status lora_merge(const lora_linear_desc* desc, const void* W, const void* 
         const uint16_t *W16 = static_cast<const uint16_t*>(W), *A16 = static_cast<const uint16_t*>(A),
                        *B16 = static_cast<const uint16_t*>(B);
         uint16_t* const O16 = static_cast<uint16_t*>(W_out);
-#define MERGE_MFMA(RP) do { observe("lora_merge", s, 0); hipLaunchKernelGGL((lora_merge_mfma<RP>), grid, dim3(256), 0, s, W16, A16, B16, O16, \
-                                          (int)d.N, (int)d.K, (int)d.r, scale); observe("lora_merge", s, 1); } while (0)
+#define MERGE_MFMA(RP) LAUNCH("lora_merge", (lora_merge_mfma<RP>), grid, dim3(256), 0, s, W16, A16, B16, O16, \
+                             (int)d.N, (int)d.K, (int)d.r, scale)
         switch ((d.r + 31) / 32) {
             case 1: MERGE_MFMA(32); break;
             case 2: MERGE_MFMA(64); break;
@@ -808,12 +828,12 @@ lora_status lora_merge(const lora_linear_desc* desc, const void* W, const void* 
         }
 #undef MERGE_MFMA
     } else if (d.dtype == LORA_DTYPE_F32)
-        { observe("lora_merge", s, 0); hipLaunchKernelGGL((lora_merge_kernel<true>), grid, dim3(256), 0, s, W, A, B, W_out, (int)d.N, (int)d.K,
-                           (int)d.r, scale); observe("lora_merge", s, 1); }
+        LAUNCH("lora_merge", (lora_merge_kernel<true>), grid, dim3(256), 0, s, W, A, B, W_out, (int)d.N, (int)d.K,
+                           (int)d.r, scale);
     else
-        { observe("lora_merge", s, 0); hipLaunchKernelGGL((lora_merge_kernel<false>), grid, dim3(256),
+        LAUNCH("lora_merge", (lora_merge_kernel<false>), grid, dim3(256),
                            (size_t)d.r * (kMergeCols + kMergeRows) * sizeof(uint16_t), s, W, A, B, W_out, (int)d.N,
-                           (int)d.K, (int)d.r, scale); observe("lora_merge", s, 1); }
+                           (int)d.K, (int)d.r, scale);
     LAUNCH_CHECK("lora_merge");
     return ok();
 }
@@ -834,9 +854,9 @@ lora_status lora_dequant4(const uint8_t* Wq, const uint16_t* absmax, const float
     const int n_groups = (int)(N * K / 8);
     const dim3 grid((unsigned)std::min<int64_t>(cdiv(n_groups, 256), 256 * 16));
     if (out_dtype == LORA_DTYPE_F32)
-        { observe("dequant4", s, 0); hipLaunchKernelGGL((dequant4_kernel<true>), grid, dim3(256), 0, s, Wq, absmax, codebook, W_out, n_groups); observe("dequant4", s, 1); }
+        LAUNCH("dequant4", (dequant4_kernel<true>), grid, dim3(256), 0, s, Wq, absmax, codebook, W_out, n_groups);
     else
-        { observe("dequant4", s, 0); hipLaunchKernelGGL((dequant4_kernel<false>), grid, dim3(256), 0, s, Wq, absmax, codebook, W_out, n_groups); observe("dequant4", s, 1); }
+        LAUNCH("dequant4", (dequant4_kernel<false>), grid, dim3(256), 0, s, Wq, absmax, codebook, W_out, n_groups);
     LAUNCH_CHECK("dequant4");
     return ok();
 }

@@ -244,13 +244,13 @@ def test_buffer_ranges_rejects_bad_descriptor():
         lla.lora_linear_buffer_ranges(lla.Desc(64, 96, 256, 8, 32.0), quant=True)
 
 
-def test_launch_observer_set_and_clear():
-    """The observer can be set and removed; a call refused by validation
-    enqueues nothing, so the observer is never called."""
+def test_kernel_timer_set_and_clear():
+    """The timer can be set and removed; a call refused by validation enqueues
+    nothing, so the timer is never asked for events."""
     seen = []
-    lla.lora_set_launch_observer(lambda k, s, p: seen.append((k, p)))
+    lla.lora_set_kernel_timer(lambda k, s: seen.append(k))
     try:
         assert fwd(desc(K=250)) == _lib.LORA_ERR_UNSUPPORTED
     finally:
-        lla.lora_set_launch_observer(None)
+        lla.lora_set_kernel_timer(None)
     assert seen == []
