@@ -112,6 +112,27 @@ lora_status lora_linear_bwd(const lora_linear_desc* desc,
                             void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Backward without a workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving or training loops, harnesses
+ * that forbid allocation).  Same arguments, results and errors as
+ * lora_linear_bwd (bitwise the same outputs), except that the intermediates
+ * live in a static device array of LORA_NOALLOC_SCRATCH_BYTES inside the
+ * library, one per device, held until the process ends.  Nothing is
+ * allocated.  The array's contents on entry do not matter (nothing in it has
+ * to start at zero); every call on a device shares that device's array, so
+ * calls that overlap on one device race: order them on one stream.  The
+ * stream must belong to the current device.  A descriptor whose backward
+ * needs more than LORA_NOALLOC_SCRATCH_BYTES of intermediates (large M x r, or
+ * many split-M partials) gets LORA_ERR_UNSUPPORTED before anything is enqueued.
+ */
+#define LORA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+lora_status lora_linear_bwd_noalloc(const lora_linear_desc* desc,
+                                    const void* dY, const void* X, const void* W,
+                                    const void* A, const void* B, const float* U_saved,
+                                    void* dX, void* dA, void* dB, void* stream);
+
+/*
  * 4-bit frozen weight (page "Unsloth — 微调 2-5x 加速", section "核心要点",
  * item 3: 4-bit weights are dequantised inside the matmul, not copied out
  * first).  W is replaced by

@@ -22,9 +22,10 @@ LORA_DTYPE_BF16 = 0
 LORA_DTYPE_F32 = 1
 
 LORA_FLAG_ACCUM_GRADS = 0x1
+LORA_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 EXPORTED = (
-    "lora_linear_workspace_size", "lora_linear_fwd", "lora_linear_bwd",
+    "lora_linear_workspace_size", "lora_linear_fwd", "lora_linear_bwd", "lora_linear_bwd_noalloc",
     "lora_qlinear_fwd", "lora_qlinear_bwd", "lora_dequant4", "lora_merge",
     "lora_linear_buffer_ranges", "lora_set_kernel_timer", "lora_status_string", "lora_last_error",
 )
@@ -66,6 +67,7 @@ def load() -> ctypes.CDLL:
         "lora_linear_workspace_size": [dp, ctypes.POINTER(sz)],
         "lora_linear_fwd": [dp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "lora_linear_bwd": [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "lora_linear_bwd_noalloc": [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
         "lora_qlinear_fwd": [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "lora_qlinear_bwd": [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "lora_dequant4": [vp, vp, vp, i64, i64, i32, vp, vp],

@@ -195,6 +195,16 @@ def lora_linear_bwd(desc: Desc, dY, X, W, A, B, U_saved, dX, dA, dB, ws=None, ws
     _check(st, "lora_linear_bwd")
 
 
+def lora_linear_bwd_noalloc(desc: Desc, dY, X, W, A, B, U_saved, dX, dA, dB, stream=None):
+    """lora_linear_bwd with the intermediates in the library's static device
+    array instead of a workspace (for callers that cannot allocate)."""
+    _check_dense(desc, dY=dY, X=X, W=W, A=A, B=B, U_saved=U_saved, dX=dX, dA=dA, dB=dB)
+    d = desc.c()
+    st = _lib.load().lora_linear_bwd_noalloc(ctypes.byref(d), _ptr(dY), _ptr(X), _ptr(W), _ptr(A), _ptr(B),
+                                             _ptr(U_saved), _ptr(dX), _ptr(dA), _ptr(dB), _stream(stream))
+    _check(st, "lora_linear_bwd_noalloc")
+
+
 def lora_qlinear_fwd(desc: Desc, X, Wq, absmax, codebook, A, B, H, U_save=None, ws=None, ws_bytes=None,
                      stream=None):
     """Forward with the frozen weight in the 4-bit format (codes, fp16 absmax, codebook)."""

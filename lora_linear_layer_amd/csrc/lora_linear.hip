@@ -7,6 +7,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <climits>
 #include <cmath>
 #include <cstdarg>
@@ -609,6 +610,50 @@ lora_status bwd_f32(const lora_linear_desc& d, bool quant, const void* dY, const
     return ok();
 }
 
+// ---------------------------------------------------------------- allocation-free backward
+// The backward's intermediates (V, U, the rank planes, the split-M partials)
+// live in this array when the caller cannot provide a workspace.  Its address
+// differs on every device: the host looks it up once per device with
+// hipGetSymbolAddress and never uses the name itself as an address.
+constexpr size_t kScratchBytes = LORA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the current device (looked up on the first
+// call on that device, with that device current).
+lora_status scratch_on_current_device(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(LORA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(LORA_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess || !p)
+                return fail(LORA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return LORA_OK;
+}
+
+// Bytes of the backward's intermediates for a 16-bit weight: the workspace
+// layout up to its last region, plus the float32 slices of the input
+// gradient's own split contraction (the workspace is sized for the 4-bit
+// plans too, whose forward splits more).
+size_t bwd_scratch_bytes(const lora_linear_desc& d) {
+    const Plan p = make_plan(d);
+    if (d.dtype != LORA_DTYPE_BF16) return p.total;
+    return p.off_split + align_up(gemm_split_plan(d.M, d.K, d.N, false).part_floats * sizeof(float));
+}
+
 // ---------------------------------------------------------------- buffer ranges
 // Every buffer resource the bf16 kernels of one descriptor may build, with the
 // largest range it asks for (the first workgroup and step, where the clipping
@@ -703,6 +748,38 @@ lora_status lora_linear_buffer_ranges(const lora_linear_desc* desc, int32_t quan
     buffer_ranges(*desc, quant != 0, L);
     *count = L.n;
     return ok();
+}
+
+lora_status lora_linear_bwd_noalloc(const lora_linear_desc* desc, const void* dY, const void* X, const void* W,
+                                    const void* A, const void* B, const float* U_saved, void* dX, void* dA, void* dB,
+                                    void* stream) {
+    lora_status st = check_desc(desc, false);
+    if (st != LORA_OK) return st;
+    st = check_ptrs({{dY, "dY"}, {X, "X"}, {W, "W"}, {A, "A"}, {B, "B"}, {dA, "dA"}, {dB, "dB"}},
+                    {{U_saved, "U_saved"}, {dX, "dX"}});
+    if (st != LORA_OK) return st;
+    st = check_no_alias({{dX, "dX"}, {dA, "dA"}, {dB, "dB"}},
+                        {{dY, "dY"}, {X, "X"}, {W, "W"}, {A, "A"}, {B, "B"}, {U_saved, "U_saved"},
+                         {dX, "dX"}, {dA, "dA"}, {dB, "dB"}});
+    if (st != LORA_OK) return st;
+    const size_t need = bwd_scratch_bytes(*desc);
+    if (need > kScratchBytes)
+        return fail(LORA_ERR_UNSUPPORTED,
+                    "this backward needs %zu bytes of intermediates; the allocation-free entry point holds %zu "
+                    "(use lora_linear_bwd with a workspace)", need, kScratchBytes);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void* ws = nullptr;
+    st = scratch_on_current_device(&ws);
+    if (st != LORA_OK) return st;
+    if (s) {
+        hipDevice_t sd = -1;
+        int cur = -1;
+        if (hipStreamGetDevice(s, &sd) == hipSuccess && hipGetDevice(&cur) == hipSuccess && sd != cur)
+            return fail(LORA_ERR_INVALID_ARG, "stream belongs to device %d but device %d is current", (int)sd, cur);
+    }
+    if (desc->dtype == LORA_DTYPE_F32)
+        return bwd_f32(*desc, false, dY, X, W, nullptr, nullptr, nullptr, A, B, U_saved, dX, dA, dB, ws, s);
+    return bwd_bf16(*desc, false, dY, X, W, nullptr, nullptr, nullptr, A, B, U_saved, dX, dA, dB, ws, s);
 }
 
 lora_status lora_linear_fwd(const lora_linear_desc* desc, const void* X, const void* W, const void* A,
