@@ -41,7 +41,7 @@ import numpy as np
 
 __all__ = [
     "lora_scale", "forward", "backward", "backward_dx", "backward_lora",
-    "merged_weight", "bf16_round", "f16_to_f64", "codebook4", "dequant4",
+    "merged_weight", "group_forward", "group_backward", "bf16_round", "f16_to_f64", "codebook4", "dequant4",
 ]
 
 
@@ -101,6 +101,32 @@ def merged_weight(W, A, B, s):
     for inference engines); with -s it removes the adapter again (unmerge).
     Forms the N x K product B A, so only for test shapes."""
     return _f64(W) + float(s) * (_f64(B) @ _f64(A))
+
+
+# ----------------------------------------------------------------------------
+# Linears that read the same input
+# ----------------------------------------------------------------------------
+
+def group_forward(X, Ws, As, Bs, s):
+    """Several LoRA linears applied to one input X (the attention projections
+    q, k, v, or the MLP's gate and up: [P4] section 1.2, the fused q_proj
+    example, and section 2.3, LoRA on all linear layers).  Each member i is
+    its own layer: H_i = X W_i^T + s (X A_i^T) B_i^T.  Returns [(H_i, U_i)]."""
+    return [forward(X, W, A, B, s) for W, A, B in zip(Ws, As, Bs)]
+
+
+def group_backward(dYs, X, Ws, As, Bs, s):
+    """Vector-Jacobian products of L = sum_i <dY_i, H_i> for group_forward.
+    X feeds every member, so its gradient is the sum of the members' input
+    gradients; each member keeps its own dA_i, dB_i.  Returns (dX, [dA_i], [dB_i])."""
+    dX = None
+    dAs, dBs = [], []
+    for dY, W, A, B in zip(dYs, Ws, As, Bs):
+        dXi, dAi, dBi = backward(dY, X, W, A, B, s)
+        dX = dXi if dX is None else dX + dXi
+        dAs.append(dAi)
+        dBs.append(dBi)
+    return dX, dAs, dBs
 
 
 # ----------------------------------------------------------------------------

@@ -321,3 +321,85 @@ def test_workload_flops():
     wl = workloads.workload("attn_proj_4096")
     assert wl.flops() == 4 * 4096 ** 3 + 6 * 4096 * 8 * 8192
     assert abs(wl.flops() / 1e9 - 276.49) < 0.01
+
+
+# ---------------------------------------------------------------- linears sharing one input
+def group_case(seed, M=4, K=6, Ns=(5, 3, 4), r=2):
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal((M, K))
+    Ws = [rng.standard_normal((n, K)) for n in Ns]
+    As = [rng.standard_normal((r, K)) for _ in Ns]
+    Bs = [rng.standard_normal((n, r)) for n in Ns]
+    dYs = [rng.standard_normal((M, n)) for n in Ns]
+    return X, Ws, As, Bs, dYs, float(rng.uniform(0.25, 4.0))
+
+
+def test_group_backward_finite_differences():
+    """dX of a group is the gradient of L = sum_i <dY_i, H_i> with respect to
+    the shared X (central differences; L is linear in X, so they are exact up
+    to rounding), and each member's dA_i, dB_i that of its own parameters."""
+    X, Ws, As, Bs, dYs, s = group_case(11)
+
+    def loss(X_, As_, Bs_):
+        outs = oracle.group_forward(X_, Ws, As_, Bs_, s)
+        return sum(float(np.sum(dY * H)) for dY, (H, _) in zip(dYs, outs))
+
+    dX, dAs, dBs = oracle.group_backward(dYs, X, Ws, As, Bs, s)
+    h = 1e-3
+    for idx in itertools.product(range(X.shape[0]), range(X.shape[1])):
+        Xp, Xm = X.copy(), X.copy()
+        Xp[idx] += h
+        Xm[idx] -= h
+        assert abs((loss(Xp, As, Bs) - loss(Xm, As, Bs)) / (2 * h) - dX[idx]) <= 1e-9 * max(1.0, abs(dX[idx]))
+    for i in range(len(Ws)):
+        for idx in itertools.product(range(As[i].shape[0]), range(As[i].shape[1])):
+            Ap = [a.copy() for a in As]; Am = [a.copy() for a in As]
+            Ap[i][idx] += h; Am[i][idx] -= h
+            fd = (loss(X, Ap, Bs) - loss(X, Am, Bs)) / (2 * h)
+            assert abs(fd - dAs[i][idx]) <= 1e-9 * max(1.0, abs(fd))
+        for idx in itertools.product(range(Bs[i].shape[0]), range(Bs[i].shape[1])):
+            Bp = [b.copy() for b in Bs]; Bm = [b.copy() for b in Bs]
+            Bp[i][idx] += h; Bm[i][idx] -= h
+            fd = (loss(X, As, Bp) - loss(X, As, Bm)) / (2 * h)
+            assert abs(fd - dBs[i][idx]) <= 1e-9 * max(1.0, abs(fd))
+
+
+def test_group_is_one_layer_with_block_diagonal_b():
+    """A group equals one LoRA layer over the stacked weights: W = [W_1; ..; W_G],
+    A = [A_1; ..; A_G] (rank G r), B block-diagonal diag(B_1, .., B_G).  Its
+    output is the members' outputs side by side, its dX the group's dX, its
+    dA the members' dA stacked, and the diagonal blocks of its dB the
+    members' dB (the off-diagonal blocks belong to no parameter)."""
+    X, Ws, As, Bs, dYs, s = group_case(12)
+    Ns = [w.shape[0] for w in Ws]
+    r = As[0].shape[0]
+    Bbd = np.zeros((sum(Ns), r * len(Ns)))
+    n0 = 0
+    for i, B in enumerate(Bs):
+        Bbd[n0:n0 + Ns[i], i * r:(i + 1) * r] = B
+        n0 += Ns[i]
+    Wst, Ast, dYst = np.vstack(Ws), np.vstack(As), np.hstack(dYs)
+    H, U = oracle.forward(X, Wst, Ast, Bbd, s)
+    outs = oracle.group_forward(X, Ws, As, Bs, s)
+    np.testing.assert_allclose(H, np.hstack([h for h, _ in outs]), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(U, np.hstack([u for _, u in outs]), rtol=1e-12, atol=1e-12)
+    dX, dA, dB = oracle.backward(dYst, X, Wst, Ast, Bbd, s)
+    gdX, gdAs, gdBs = oracle.group_backward(dYs, X, Ws, As, Bs, s)
+    np.testing.assert_allclose(dX, gdX, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dA, np.vstack(gdAs), rtol=1e-12, atol=1e-12)
+    n0 = 0
+    for i, g in enumerate(gdBs):
+        np.testing.assert_allclose(dB[n0:n0 + Ns[i], i * r:(i + 1) * r], g, rtol=1e-12, atol=1e-12)
+        n0 += Ns[i]
+
+
+def test_group_of_one_is_the_layer():
+    X, Ws, As, Bs, dYs, s = group_case(13, Ns=(5,))
+    (H, U), = oracle.group_forward(X, Ws, As, Bs, s)
+    H1, U1 = oracle.forward(X, Ws[0], As[0], Bs[0], s)
+    np.testing.assert_array_equal(H, H1)
+    dX, (dA,), (dB,) = oracle.group_backward(dYs, X, Ws, As, Bs, s)
+    dX1, dA1, dB1 = oracle.backward(dYs[0], X, Ws[0], As[0], Bs[0], s)
+    np.testing.assert_array_equal(dX, dX1)
+    np.testing.assert_array_equal(dA, dA1)
+    np.testing.assert_array_equal(dB, dB1)
