@@ -133,6 +133,58 @@ lora_status lora_linear_bwd_noalloc(const lora_linear_desc* desc,
                                     void* dX, void* dA, void* dB, void* stream);
 
 /*
+ * Linears that share one input (page "ms-swift高效微调组合：LoRA+UnSloth提速实践",
+ * section 1.2, the fused q_proj example, and section 2.3, LoRA on all linear
+ * layers: the attention projections q, k, v read the same hidden states, and
+ * so do the MLP's gate and up).  The members are stored stacked, in member
+ * order: member m has N[m] output columns, and with n0 = N[0] + .. + N[m-1]
+ *   X  [M, K]             the shared input
+ *   W  [sum N, K]         rows n0 .. n0 + N[m] - 1: member m's frozen weight
+ *   A  [n_members r, K]   rows m r .. m r + r - 1: member m's A
+ *   B  [sum N, r]         rows n0 .. : member m's B
+ *   H, dY [M, sum N]      columns n0 .. : member m's output / its gradient
+ *   U  [M, n_members r]   columns m r .. : member m's U = X A_m^T (float32)
+ *   dA, dB                as A, B
+ * Forward: H_m = X W_m^T + s (X A_m^T) B_m^T for every member, in one GEMM over
+ * the stacked W whose epilogue adds each member's own rank-r term, after one
+ * streamed pass over X that forms all members' U.  Backward: the input
+ * gradient of the shared X is the sum over the members,
+ *   dX = sum_m (dY_m W_m + s (dY_m B_m) A_m)     (one GEMM contracting over all
+ *                                                 sum N columns; NULL: skipped),
+ * and dA_m = s (dY_m B_m)^T X, dB_m = s dY_m^T U_m per member (overwritten, or
+ * accumulated with LORA_FLAG_ACCUM_GRADS).  s = alpha / r for every member.
+ * Requirements: 1 <= n_members <= LORA_MAX_MEMBERS; every N[m] >= 8 and a
+ * multiple of 8; 1 <= r <= 128 and n_members r <= LORA_MAX_GROUP_RANK; K % 8 == 0;
+ * K, sum N <= 2^21; every matrix under 2^31 elements; dtype LORA_DTYPE_BF16
+ * (LORA_ERR_UNSUPPORTED otherwise).  Memory, errors and the workspace as for
+ * lora_linear_fwd / lora_linear_bwd (lora_group_workspace_size).
+ */
+#define LORA_MAX_MEMBERS 8
+#define LORA_MAX_GROUP_RANK 192
+
+typedef struct lora_group_desc {
+    int64_t M, K, r;
+    float alpha;
+    int32_t dtype;                   /* lora_dtype: LORA_DTYPE_BF16 */
+    uint32_t flags;                  /* LORA_FLAG_* */
+    int32_t n_members;
+    int64_t N[LORA_MAX_MEMBERS];     /* output columns of each member (the first n_members entries) */
+} lora_group_desc;
+
+lora_status lora_group_workspace_size(const lora_group_desc* desc, size_t* bytes);
+
+lora_status lora_group_fwd(const lora_group_desc* desc,
+                           const void* X, const void* W, const void* A, const void* B,
+                           void* H, float* U_save,
+                           void* ws, size_t ws_bytes, void* stream);
+
+lora_status lora_group_bwd(const lora_group_desc* desc,
+                           const void* dY, const void* X, const void* W,
+                           const void* A, const void* B, const float* U_saved,
+                           void* dX, void* dA, void* dB,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/*
  * 4-bit frozen weight (page "Unsloth — 微调 2-5x 加速", section "核心要点",
  * item 3: 4-bit weights are dequantised inside the matmul, not copied out
  * first).  W is replaced by

@@ -5,13 +5,15 @@ autograd wrappers live in lora_linear_layer_amd.layer.
 """
 from ._lib import (LIB_PATH, LORA_DTYPE_BF16, LORA_DTYPE_F32, LORA_FLAG_ACCUM_GRADS,  # noqa: F401
                    LORA_NOALLOC_SCRATCH_BYTES, load)
-from .api import (Desc, LoraError, lora_dequant4, lora_linear_buffer_ranges, lora_linear_bwd,  # noqa: F401
+from .api import (Desc, GroupDesc, LoraError, lora_dequant4, lora_group_bwd, lora_group_fwd,  # noqa: F401
+                  lora_group_workspace_size, lora_linear_buffer_ranges, lora_linear_bwd,
                   lora_linear_bwd_noalloc,
                   lora_linear_fwd, lora_linear_workspace_size, lora_merge, lora_qlinear_bwd, lora_qlinear_fwd,
                   lora_set_kernel_timer)
 
 __all__ = [
-    "Desc", "LoraError", "lora_linear_workspace_size", "lora_linear_fwd", "lora_linear_bwd",
+    "Desc", "GroupDesc", "LoraError", "lora_linear_workspace_size", "lora_linear_fwd", "lora_linear_bwd",
+    "lora_group_workspace_size", "lora_group_fwd", "lora_group_bwd",
     "lora_linear_bwd_noalloc", "LORA_NOALLOC_SCRATCH_BYTES",
     "lora_qlinear_fwd", "lora_qlinear_bwd", "lora_dequant4", "lora_merge", "lora_linear_buffer_ranges",
     "lora_set_kernel_timer", "load", "LIB_PATH",

@@ -23,11 +23,13 @@ LORA_DTYPE_F32 = 1
 
 LORA_FLAG_ACCUM_GRADS = 0x1
 LORA_NOALLOC_SCRATCH_BYTES = 32 << 20
+LORA_MAX_MEMBERS = 8
+LORA_MAX_GROUP_RANK = 192
 
 EXPORTED = (
     "lora_linear_workspace_size", "lora_linear_fwd", "lora_linear_bwd", "lora_linear_bwd_noalloc",
     "lora_qlinear_fwd", "lora_qlinear_bwd", "lora_dequant4", "lora_merge",
-    "lora_linear_buffer_ranges", "lora_set_kernel_timer", "lora_status_string", "lora_last_error",
+    "lora_linear_buffer_ranges", "lora_group_workspace_size", "lora_group_fwd", "lora_group_bwd", "lora_set_kernel_timer", "lora_status_string", "lora_last_error",
 )
 
 # void (*)(void* user, const char* kernel, void* stream, void** start_event, void** stop_event)
@@ -40,6 +42,15 @@ class LoraLinearDesc(ctypes.Structure):
     _fields_ = [
         ("M", ctypes.c_int64), ("K", ctypes.c_int64), ("N", ctypes.c_int64), ("r", ctypes.c_int64),
         ("alpha", ctypes.c_float), ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32),
+    ]
+
+
+class LoraGroupDesc(ctypes.Structure):
+    """Mirror of struct lora_group_desc."""
+    _fields_ = [
+        ("M", ctypes.c_int64), ("K", ctypes.c_int64), ("r", ctypes.c_int64), ("alpha", ctypes.c_float),
+        ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32), ("n_members", ctypes.c_int32),
+        ("N", ctypes.c_int64 * LORA_MAX_MEMBERS),
     ]
 
 
@@ -63,6 +74,7 @@ def load() -> ctypes.CDLL:
     lib = ctypes.CDLL(LIB_PATH)
     vp, sz, i32, i64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64
     dp = ctypes.POINTER(LoraLinearDesc)
+    gp = ctypes.POINTER(LoraGroupDesc)
     sig = {
         "lora_linear_workspace_size": [dp, ctypes.POINTER(sz)],
         "lora_linear_fwd": [dp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
@@ -73,6 +85,9 @@ def load() -> ctypes.CDLL:
         "lora_dequant4": [vp, vp, vp, i64, i64, i32, vp, vp],
         "lora_merge": [dp, vp, vp, vp, vp, i32, vp],
         "lora_linear_buffer_ranges": [dp, i32, ctypes.POINTER(LoraBufferRange), i32, ctypes.POINTER(i32)],
+        "lora_group_workspace_size": [gp, ctypes.POINTER(sz)],
+        "lora_group_fwd": [gp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "lora_group_bwd": [gp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)

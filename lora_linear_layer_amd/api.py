@@ -13,8 +13,8 @@ import dataclasses
 import torch
 
 from . import _lib
-from ._lib import (LORA_DTYPE_BF16, LORA_DTYPE_F32, LORA_FLAG_ACCUM_GRADS,  # noqa: F401
-                   LoraBufferRange, LoraLinearDesc)
+from ._lib import (LORA_DTYPE_BF16, LORA_DTYPE_F32, LORA_FLAG_ACCUM_GRADS, LORA_MAX_MEMBERS,  # noqa: F401
+                   LoraBufferRange, LoraGroupDesc, LoraLinearDesc)
 
 
 class LoraError(RuntimeError):
@@ -39,6 +39,39 @@ class Desc:
 
     def c(self) -> LoraLinearDesc:
         return LoraLinearDesc(self.M, self.K, self.N, self.r, float(self.alpha), self.dtype, self.flags)
+
+    @property
+    def scale(self) -> float:
+        return self.alpha / self.r
+
+
+@dataclasses.dataclass(frozen=True)
+class GroupDesc:
+    """Linears sharing one input (mirrors struct lora_group_desc): member m has
+    N[m] output columns; W, B, H, dY are stacked by output columns and A, U, V
+    by rank rows (m r .. m r + r - 1)."""
+    M: int
+    K: int
+    N: tuple
+    r: int
+    alpha: float
+    dtype: int = LORA_DTYPE_BF16
+    flags: int = 0
+
+    def c(self) -> LoraGroupDesc:
+        Ns = list(self.N)
+        if not 1 <= len(Ns) <= LORA_MAX_MEMBERS:
+            raise ValueError(f"a group has 1 .. {LORA_MAX_MEMBERS} members, got {len(Ns)}")
+        arr = (ctypes.c_int64 * LORA_MAX_MEMBERS)(*(Ns + [0] * (LORA_MAX_MEMBERS - len(Ns))))
+        return LoraGroupDesc(self.M, self.K, self.r, float(self.alpha), self.dtype, self.flags, len(Ns), arr)
+
+    @property
+    def N_total(self) -> int:
+        return int(sum(self.N))
+
+    @property
+    def rank_total(self) -> int:
+        return len(self.N) * self.r
 
     @property
     def scale(self) -> float:
@@ -203,6 +236,53 @@ def lora_linear_bwd_noalloc(desc: Desc, dY, X, W, A, B, U_saved, dX, dA, dB, str
     st = _lib.load().lora_linear_bwd_noalloc(ctypes.byref(d), _ptr(dY), _ptr(X), _ptr(W), _ptr(A), _ptr(B),
                                              _ptr(U_saved), _ptr(dX), _ptr(dA), _ptr(dB), _stream(stream))
     _check(st, "lora_linear_bwd_noalloc")
+
+
+def _check_group(g: GroupDesc, **ts):
+    M, K, N, R, r = g.M, g.K, g.N_total, g.rank_total, g.r
+    dt = (_TORCH_DTYPE[g.dtype],) if g.dtype in _TORCH_DTYPE else ()
+    spec = {"X": ((M, K), dt), "W": ((N, K), dt), "A": ((R, K), dt), "B": ((N, r), dt), "H": ((M, N), dt),
+            "dY": ((M, N), dt), "dX": ((M, K), dt), "dA": ((R, K), dt), "dB": ((N, r), dt),
+            "U_save": ((M, R), (torch.float32,)), "U_saved": ((M, R), (torch.float32,))}
+    for name, t in ts.items():
+        _expect(t, name, *spec[name])
+    _same_gpu(**ts)
+
+
+def lora_group_workspace_size(desc: GroupDesc) -> int:
+    out = ctypes.c_size_t(0)
+    d = desc.c()
+    _check(_lib.load().lora_group_workspace_size(ctypes.byref(d), ctypes.byref(out)), "lora_group_workspace_size")
+    return int(out.value)
+
+
+def _group_ws(desc, ws, ws_bytes, device):
+    if ws is None:
+        nbytes = lora_group_workspace_size(desc)
+        return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device), nbytes
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    return ws, ws_bytes
+
+
+def lora_group_fwd(desc: GroupDesc, X, W, A, B, H, U_save=None, ws=None, ws_bytes=None, stream=None):
+    """H_m = X W_m^T + s (X A_m^T) B_m^T for every member (stacked layout, see include/lora_linear.h)."""
+    _check_group(desc, X=X, W=W, A=A, B=B, H=H, U_save=U_save)
+    ws, ws_bytes = _group_ws(desc, ws, ws_bytes, X.device)
+    d = desc.c()
+    st = _lib.load().lora_group_fwd(ctypes.byref(d), _ptr(X), _ptr(W), _ptr(A), _ptr(B), _ptr(H), _ptr(U_save),
+                                    _ptr(ws), ws_bytes, _stream(stream))
+    _check(st, "lora_group_fwd")
+
+
+def lora_group_bwd(desc: GroupDesc, dY, X, W, A, B, U_saved, dX, dA, dB, ws=None, ws_bytes=None, stream=None):
+    """dX = sum_m (dY_m W_m + s V_m A_m); dA_m, dB_m per member (stacked layout)."""
+    _check_group(desc, dY=dY, X=X, W=W, A=A, B=B, U_saved=U_saved, dX=dX, dA=dA, dB=dB)
+    ws, ws_bytes = _group_ws(desc, ws, ws_bytes, dY.device)
+    d = desc.c()
+    st = _lib.load().lora_group_bwd(ctypes.byref(d), _ptr(dY), _ptr(X), _ptr(W), _ptr(A), _ptr(B), _ptr(U_saved),
+                                    _ptr(dX), _ptr(dA), _ptr(dB), _ptr(ws), ws_bytes, _stream(stream))
+    _check(st, "lora_group_bwd")
 
 
 def lora_qlinear_fwd(desc: Desc, X, Wq, absmax, codebook, A, B, H, U_save=None, ws=None, ws_bytes=None,

@@ -63,6 +63,8 @@
 namespace lora {
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kMaxMembers = 8;      // linears sharing one input in one grouped call
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 typedef __attribute__((address_space(3))) i16x4* lds_i16x4_ptr;
 
@@ -139,6 +141,12 @@ struct GemmArgs {
     int P, Q, C, r;
     int first_split, split, kc;   // split contraction: first split tile, slices, 64-wide stages per slice
     float s;
+    // Precomputed Z: its rows are z_ld floats.  Output columns q in [member_q0[i],
+    // member_q0[i + 1]) belong to member i, whose rank term uses Z columns i r ..
+    // i r + r - 1 (linears sharing one input, forward); a plain layer is one member.
+    int z_ld;
+    int n_members;
+    int member_q0[kMaxMembers + 1];
 };
 
 namespace g2 {
@@ -575,14 +583,16 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
     // them live (and spilled) across the loop
     int l16e = l16, g4e = g4;
     asm volatile("" : "+v"(l16e), "+v"(g4e));
-    auto load_e = [&](int jt, bf16x8 (&ef)[QB]) {
+    // E rows of output columns q in [qlo, qhi) (the member's; zeros elsewhere)
+    auto load_e = [&](int jt, bf16x8 (&ef)[QB], int qlo, int qhi) {
 #pragma unroll
         for (int qi = 0; qi < QB; ++qi) {
             const int q = q0 + wq * QB * 16 + qi * 16 + l16e;
+            const bool qok = q >= qlo && q < qhi;
             if (!TRANS && r4) {
                 const int j = jt * 16 + 4 * g4e;
                 u32x2 v = {0u, 0u};
-                if (q < Q && j < r) v = *reinterpret_cast<const u32x2*>(a.E + (size_t)q * r + j);
+                if (qok && j < r) v = *reinterpret_cast<const u32x2*>(a.E + (size_t)q * r + j);
                 ef[qi] = as_bf16x8(u32x4{v[0], v[1], v[0], v[1]});
                 continue;
             }
@@ -591,38 +601,60 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
             for (int i = 0; i < 4; ++i) {
                 const int j = jt * 16 + 4 * g4e + i;
                 uint32_t v = 0u;
-                if (q < Q && j < r) v = TRANS ? a.E[(size_t)j * Q + q] : a.E[(size_t)q * r + j];
+                if (qok && j < r) v = TRANS ? a.E[(size_t)j * Q + q] : a.E[(size_t)q * r + j];
                 e4[i] = v;
             }
             const uint32_t w0 = e4[0] | (e4[1] << 16), w1 = e4[2] | (e4[3] << 16);
             ef[qi] = as_bf16x8(u32x4{w0, w1, w0, w1});
         }
     };
-    auto load_zin = [&](int jt, f32x4 (&zv)[8]) {
+    // Z columns zc + j of the precomputed Z (rows of z_ld floats)
+    const bool z4 = ((a.z_ld | r) & 3) == 0;
+    auto load_zin = [&](int jt, f32x4 (&zv)[8], int zc) {
 #pragma unroll
         for (int pi = 0; pi < 8; ++pi) {
             const int p = p0 + wp * 128 + ((pi + ZB * wq) & 7) * 16 + l16e;
-            if (r4) {
+            const float* const zrow = a.Zin + (size_t)p * a.z_ld + zc;
+            if (z4) {
                 const int j = jt * 16 + 4 * g4e;
-                zv[pi] = (p < P && j < r) ? *reinterpret_cast<const f32x4*>(a.Zin + (size_t)p * r + j)
-                                          : f32x4{0.f, 0.f, 0.f, 0.f};
+                zv[pi] = (p < P && j < r) ? *reinterpret_cast<const f32x4*>(zrow + j) : f32x4{0.f, 0.f, 0.f, 0.f};
                 continue;
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int j = jt * 16 + 4 * g4e + i;
-                zv[pi][i] = (p < P && j < r) ? a.Zin[(size_t)p * r + j] : 0.f;
+                zv[pi][i] = (p < P && j < r) ? zrow[j] : 0.f;
             }
         }
     };
+    // member boundary i (a wave-uniform select chain: indexing the argument
+    // array with a run-time value would copy the arguments to scratch memory)
+    auto member_q0 = [&](int i) {
+        int v = 0;
+#pragma unroll
+        for (int k = 0; k <= kMaxMembers; ++k) v = (k == i) ? a.member_q0[k] : v;
+        return v;
+    };
+    // members whose output columns meet this tile (one, unless a member boundary lies inside it)
+    int m_lo = 0, m_hi = 0;
+    if constexpr (ZIN) {
+        m_lo = kMaxMembers;
+#pragma unroll
+        for (int i = 0; i < kMaxMembers; ++i) {
+            if (i < a.n_members && a.member_q0[i] < q0 + BQ && a.member_q0[i + 1] > q0) {
+                m_lo = min(m_lo, i);
+                m_hi = i;
+            }
+        }
+    }
     // (one rank block only: with several, the prefetched block stays live
     // next to the loop-carried values and the main loop spills)
     constexpr bool PREF = RPAD == 16;
     bf16x8 ef0[QB];
     f32x4 zin0[ZIN ? 8 : 1];
     if constexpr (PREF) {
-        load_e(0, ef0);
-        if constexpr (ZIN) load_zin(0, zin0);
+        load_e(0, ef0, ZIN ? member_q0(m_lo) : 0, ZIN ? member_q0(m_lo + 1) : Q);
+        if constexpr (ZIN) load_zin(0, zin0, m_lo * r);
     }
 
     lds_barrier();   // every wave is done with the last stage before LDS is reused
@@ -663,12 +695,19 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
     }
 
     const float s = a.s;
-    const int n_jt = (SPLIT && slice > 0) ? 0 : RPAD / 16;    // the rank-r term goes into slice 0 only
+    // rank blocks of 16: the in-tile Z has RPAD columns; a precomputed one any r
+    // (up to the 192 of grouped input gradients); the rank-r term goes into slice 0 only
+    const int n_jt = (SPLIT && slice > 0) ? 0 : (ZIN ? (r + 15) / 16 : RPAD / 16);
+    // one flat loop over (member, rank block) pairs: a nested loop here keeps
+    // the accumulators live across two loop levels and spills them
+    const int n_it = (m_hi - m_lo + 1) * n_jt;
 #pragma unroll 1
-    for (int jt = 0; jt < n_jt; ++jt) {
+    for (int it = 0; it < n_it; ++it) {
+        const int mi = m_lo + it / max(n_jt, 1), jt = it - (mi - m_lo) * n_jt;
+        const int qlo = ZIN ? member_q0(mi) : 0, qhi = ZIN ? member_q0(mi + 1) : Q, zc = mi * r;
         bf16x8 ef[QB];
         f32x4 zv[ZIN ? 8 : 1];
-        if (PREF && jt == 0) {
+        if (PREF && jt == 0 && mi == m_lo) {
 #pragma unroll
             for (int qi = 0; qi < QB; ++qi) ef[qi] = ef0[qi];
             if constexpr (ZIN) {
@@ -676,8 +715,8 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
                 for (int pi = 0; pi < 8; ++pi) zv[pi] = zin0[pi];
             }
         } else {
-            load_e(jt, ef);
-            if constexpr (ZIN) load_zin(jt, zv);
+            load_e(jt, ef, qlo, qhi);
+            if constexpr (ZIN) load_zin(jt, zv, zc);
         }
 #pragma unroll
         for (int pi = 0; pi < 8; ++pi) {

@@ -26,6 +26,8 @@
 
 using namespace lora;
 
+static_assert(kMaxMembers == LORA_MAX_MEMBERS, "member table of the GEMM arguments");
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -155,48 +157,81 @@ RankSplit rank_split(int64_t out_tiles, int64_t n_ct, int64_t r) {
     return best;
 }
 
-// Splits of the three streamed products of one descriptor.
-// Contraction chunks of the Z pass (rank_z_lds): about 256 workgroups of 128
-// rows, at least 256 columns (one F slice) per chunk.
-int z_chunks(const lora_linear_desc& d, int64_t C) {
-    const int64_t rows = cdiv(d.M, 128);
-    return (int)std::max<int64_t>(1, std::min<int64_t>(cdiv(256, rows), cdiv(C, 256)));
-}
-RankSplit split_g(const lora_linear_desc& d) {
-    return rank_split(cdiv(d.K, kRT) + cdiv(d.N, kRT), cdiv(d.M, kRT), d.r);
+// One layer as the bf16 path sees it: M tokens, K inputs, N output columns,
+// rank r, and G members that share the input X (linears such as q, k and v,
+// stored stacked: W [N][K], A [G r][K], B [N][r], H and dY [M][N]); member m
+// owns output columns [n0[m], n0[m + 1]) and rank rows m r .. m r + r - 1 of A,
+// U and V.  A plain layer is the one-member case.
+struct Shape {
+    int64_t M = 0, K = 0, N = 0, r = 0;
+    int G = 1;
+    int64_t n0[kMaxMembers + 1] = {};
+    float alpha = 0.f;
+    int32_t dtype = LORA_DTYPE_BF16;
+    uint32_t flags = 0;
+    bool quant_capable = true;      // workspace also sized for the 4-bit entry points (plain layers)
+    int64_t rg() const { return (int64_t)G * r; }      // rank of the stacked A, U and V
+    int64_t Nm(int m) const { return n0[m + 1] - n0[m]; }
+};
+
+Shape shape_of(const lora_linear_desc& d) {
+    Shape s;
+    s.M = d.M; s.K = d.K; s.N = d.N; s.r = d.r;
+    s.G = 1;
+    s.n0[0] = 0;
+    s.n0[1] = d.N;
+    s.alpha = d.alpha;
+    s.dtype = d.dtype;
+    s.flags = d.flags;
+    return s;
 }
 
-// Workspace layout for one descriptor (offsets in bytes from ws).
+constexpr int64_t kMaxZCols = 192;     // rank columns one rank_z_lds pass forms
+
+// Contraction chunks of the Z pass (rank_z_lds): about 256 workgroups of 128
+// rows, at least 256 columns (one F slice) per chunk.
+int z_chunks(int64_t M, int64_t C) {
+    const int64_t rows = cdiv(M, 128);
+    return (int)std::max<int64_t>(1, std::min<int64_t>(cdiv(256, rows), cdiv(C, 256)));
+}
+RankSplit split_g(const Shape& d) {
+    return rank_split(cdiv(d.K, kRT) + cdiv(d.N, kRT), cdiv(d.M, kRT), d.rg());
+}
+
+// Workspace layout for one shape (offsets in bytes from ws).
 struct Plan {
     size_t off_v = 0, off_u = 0, off_zp = 0, off_ga = 0, off_gb = 0, off_zt = 0, off_bt = 0, off_split = 0, total = 0;
     int64_t Mp = 0;         // tokens rounded up to a whole 128-token tile (side planes of the G pass)
     RankSplit g;
 };
 
-Plan make_plan(const lora_linear_desc& d) {
+Plan make_plan(const Shape& d) {
     Plan p;
-    const size_t zbytes = align_up((size_t)d.M * d.r * sizeof(float));
-    p.off_v = 0;
-    p.off_u = zbytes;
+    const int64_t rg = d.rg();
+    const size_t zbytes = align_up((size_t)d.M * rg * sizeof(float));
+    p.off_v = 0;                                         // V [M][G r]
+    p.off_u = zbytes;                                    // U [M][G r]
     size_t cur = 2 * zbytes;
     if (d.dtype == LORA_DTYPE_BF16) {
-        const int zchunks = std::max(z_chunks(d, d.K), z_chunks(d, d.N));
-        p.off_zp = cur;
-        cur += align_up((size_t)zchunks * d.M * d.r * sizeof(float));
+        const int zchunks = std::max(z_chunks(d.M, d.K), z_chunks(d.M, d.N));
+        p.off_zp = cur;                                  // rank_z_lds chunk partials (one pass at a time)
+        cur += align_up((size_t)zchunks * d.M * std::min(rg, kMaxZCols) * sizeof(float));
         p.g = split_g(d);
-        p.off_ga = cur;
-        cur += align_up((size_t)p.g.n_chunk * d.K * d.r * sizeof(float));
-        p.off_gb = cur;
+        p.off_ga = cur;                                  // dA partials [chunk][K][G r]
+        cur += align_up((size_t)p.g.n_chunk * d.K * rg * sizeof(float));
+        p.off_gb = cur;                                  // dB partials [chunk][N][r]
         cur += align_up((size_t)p.g.n_chunk * d.N * d.r * sizeof(float));
         p.Mp = cdiv(d.M, kRT) * kRT;
-        p.off_zt = cur;                                  // V^T hi, V^T lo, U^T hi, U^T lo: bf16 [r][Mp] each
-        cur += 4 * align_up((size_t)d.r * p.Mp * sizeof(uint16_t));
-        p.off_bt = cur;                                  // B^T: bf16 [r][N]
+        p.off_zt = cur;                                  // V^T hi, V^T lo, U^T hi, U^T lo: bf16 [G r][Mp] each
+        cur += 4 * align_up((size_t)rg * p.Mp * sizeof(uint16_t));
+        p.off_bt = cur;                                  // B^T per member: bf16 [r][N_m], members side by side
         cur += align_up((size_t)d.r * d.N * sizeof(uint16_t));
         p.off_split = cur;                               // float32 partial tiles of a split contraction
-        // sized for the 4-bit plans, which split a superset of the bf16 ones
-        const size_t n_split = std::max(gemm_split_plan(d.M, d.N, d.K, true).part_floats,
-                                        gemm_split_plan(d.M, d.K, d.N, true).part_floats);
+        // sized for the 4-bit plans, which split a superset of the bf16 ones, when
+        // the 4-bit entry points share the descriptor
+        const bool q = d.quant_capable;
+        const size_t n_split = std::max(gemm_split_plan(d.M, d.N, d.K, q).part_floats,
+                                        gemm_split_plan(d.M, d.K, d.N, q).part_floats);
         cur += align_up(n_split * sizeof(float));
     }
     p.total = cur;
@@ -227,6 +262,54 @@ lora_status check_desc(const lora_linear_desc* d, bool quant) {
     return LORA_OK;
 }
 
+// A group descriptor as a shape (after check_group).
+Shape shape_of(const lora_group_desc& g) {
+    Shape s;
+    s.M = g.M; s.K = g.K; s.r = g.r;
+    s.G = g.n_members;
+    s.n0[0] = 0;
+    for (int m = 0; m < g.n_members; ++m) s.n0[m + 1] = s.n0[m] + g.N[m];
+    s.N = s.n0[g.n_members];
+    s.alpha = g.alpha;
+    s.dtype = g.dtype;
+    s.flags = g.flags;
+    s.quant_capable = false;
+    return s;
+}
+
+lora_status check_group(const lora_group_desc* g) {
+    if (!g) return fail(LORA_ERR_INVALID_ARG, "desc is NULL");
+    if (g->n_members < 1 || g->n_members > LORA_MAX_MEMBERS)
+        return fail(LORA_ERR_INVALID_ARG, "n_members = %d (1 .. %d)", (int)g->n_members, LORA_MAX_MEMBERS);
+    if (g->M <= 0 || g->K <= 0 || g->r <= 0)
+        return fail(LORA_ERR_INVALID_ARG, "M, K, r must be positive (got %lld, %lld, %lld)", (long long)g->M,
+                    (long long)g->K, (long long)g->r);
+    int64_t N = 0;
+    for (int m = 0; m < g->n_members; ++m) {
+        if (g->N[m] <= 0) return fail(LORA_ERR_INVALID_ARG, "member %d has N = %lld", m, (long long)g->N[m]);
+        if (g->N[m] % 8) return fail(LORA_ERR_UNSUPPORTED, "member %d: N = %lld is not a multiple of 8", m,
+                                     (long long)g->N[m]);
+        N += g->N[m];
+    }
+    if (g->dtype != LORA_DTYPE_BF16 && g->dtype != LORA_DTYPE_F32)
+        return fail(LORA_ERR_INVALID_ARG, "unknown dtype %d", (int)g->dtype);
+    if (g->dtype != LORA_DTYPE_BF16) return fail(LORA_ERR_UNSUPPORTED, "grouped linears are bf16 only");
+    if (!std::isfinite(g->alpha)) return fail(LORA_ERR_INVALID_ARG, "alpha is not finite");
+    if ((g->flags & ~LORA_FLAG_ACCUM_GRADS) != 0)
+        return fail(LORA_ERR_INVALID_ARG, "unknown flag bits 0x%x", (unsigned)g->flags);
+    if (g->r > 128) return fail(LORA_ERR_UNSUPPORTED, "r = %lld exceeds 128", (long long)g->r);
+    if (g->r * g->n_members > LORA_MAX_GROUP_RANK)
+        return fail(LORA_ERR_UNSUPPORTED, "n_members x r = %lld exceeds %d", (long long)(g->r * g->n_members),
+                    LORA_MAX_GROUP_RANK);
+    if (g->K % 8) return fail(LORA_ERR_UNSUPPORTED, "K must be a multiple of 8 (K=%lld)", (long long)g->K);
+    if (g->K > kMaxDim || N > kMaxDim)
+        return fail(LORA_ERR_UNSUPPORTED, "K and the members' total N must not exceed %lld", (long long)kMaxDim);
+    const int64_t big[] = {g->M * g->K, N * g->K, g->M * N, g->M * g->r * g->n_members};
+    for (int64_t v : big)
+        if (v > kMaxElems || v < 0) return fail(LORA_ERR_UNSUPPORTED, "a matrix has 2^31 or more elements");
+    return LORA_OK;
+}
+
 lora_status check_ptrs(std::initializer_list<std::pair<const void*, const char*>> required,
                        std::initializer_list<std::pair<const void*, const char*>> optional) {
     for (auto& pr : required) {
@@ -250,7 +333,7 @@ lora_status check_no_alias(std::initializer_list<std::pair<const void*, const ch
     return LORA_OK;
 }
 
-lora_status check_ws(const lora_linear_desc& d, void* ws, size_t ws_bytes) {
+lora_status check_ws(const Shape& d, void* ws, size_t ws_bytes) {
     const size_t need = make_plan(d).total;
     if (ws_bytes < need)
         return fail(LORA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", ws_bytes, need);
@@ -258,6 +341,8 @@ lora_status check_ws(const lora_linear_desc& d, void* ws, size_t ws_bytes) {
     if (ws && !aligned16(ws)) return fail(LORA_ERR_MISALIGNED, "ws is not 16-byte aligned");
     return LORA_OK;
 }
+
+lora_status check_ws(const lora_linear_desc& d, void* ws, size_t ws_bytes) { return check_ws(shape_of(d), ws, ws_bytes); }
 
 lora_status launched(const char* what) {
     const hipError_t e = hipGetLastError();
@@ -316,7 +401,13 @@ void launch_gemm_zin(GemmArgs a, const SplitPlan& sp, hipStream_t st) {
 }
 
 template <bool TRANS, bool Q4>
-void launch_gemm(const GemmArgs& a, bool in_tile, const SplitPlan& sp, hipStream_t st) {
+void launch_gemm(GemmArgs a, bool in_tile, const SplitPlan& sp, hipStream_t st) {
+    if (a.n_members == 0) {              // a plain layer: one member over all output columns
+        a.n_members = 1;
+        a.member_q0[0] = 0;
+        a.member_q0[1] = a.Q;
+    }
+    if (a.z_ld == 0) a.z_ld = a.r;
     if constexpr (!Q4) {
         if (in_tile) { launch_gemm_t<TRANS, 16, false, false>(a, st); return; }
     }
@@ -328,75 +419,125 @@ void launch_gemm(const GemmArgs& a, bool in_tile, const SplitPlan& sp, hipStream
     }
 }
 
-// Z = Y F^T (Z [M][r] float32) streamed over Y [M][C] (rank_z_lds); F given as
-// bf16 rows [r][C] (A itself, or B^T from transpose_rank).  The contraction is
-// split into z_chunks chunks whose float32 partials partial_sum adds in a
-// fixed order.
+// Z[m][z_j0 + j] = sum_c Y[m][c] F[j][c] for j < f_rows (Z float32 rows of z_ld;
+// Y bf16 [M][C] with row stride ldy; F bf16 rows [f_rows][C]: A itself, or
+// B^T from transpose_rank), streamed over Y by rank_z_lds, up to 192 rank
+// columns per pass.  The contraction is split into z_chunks chunks whose
+// float32 partials partial_sum adds in a fixed order.
+template <int JB, int SC>
+void launch_rank_z_t(const RankZArgs& a, dim3 grid, hipStream_t st) {
+    LAUNCH("rank_z_lds", (rank_z_lds<JB, SC>), grid, dim3(512), 0, st, a);
+}
 
-void launch_rank_z(const lora_linear_desc& d, const uint16_t* Y, int64_t C, const uint16_t* F_rows, float* Z,
-                   float* zpart, hipStream_t st) {
-    const int n_chunk = z_chunks(d, C);
-    const int chunk_c = (int)(cdiv(cdiv(C, n_chunk), 256) * 256);     // whole 256-column F slices
-    const int n_used = (int)cdiv(C, chunk_c);
-    float* const out = n_used > 1 ? zpart : Z;
-    const dim3 grid((unsigned)cdiv(d.M, 128), (unsigned)n_used, 1);
-    for (int j0 = 0; j0 < d.r; j0 += 64) {        // 64 rank columns per launch
-        const int jb = (int)cdiv(std::min<int64_t>(d.r - j0, 64), 16);
-#define RZ(J) LAUNCH("rank_z_lds", (rank_z_lds<J>), grid, dim3(512), 0, st, Y, F_rows, out, (int)d.M, (int)C, \
-                    (int)d.r, j0, chunk_c)
-        switch (jb) {
-            case 1: RZ(1); break;
-            case 2: RZ(2); break;
-            case 3: RZ(3); break;
-            default: RZ(4); break;
+void launch_rank_z(int64_t M, const uint16_t* Y, int64_t ldy, int64_t C, const uint16_t* F, int64_t f_rows,
+                   float* Z, int64_t z_ld, int64_t z_j0, float* zpart, hipStream_t st) {
+    const int n_chunk = z_chunks(M, C);
+    for (int64_t j0 = 0; j0 < f_rows; j0 += kMaxZCols) {
+        const int rl = (int)std::min<int64_t>(f_rows - j0, kMaxZCols);
+        const int jb = (int)cdiv(rl, 16);
+        const int sc = jb > 8 ? 128 : 256;                // F slices of 16 jb rows must fit twice in LDS
+        const int chunk_c = (int)(cdiv(cdiv(C, n_chunk), sc) * sc);
+        const int n_used = (int)cdiv(C, chunk_c);
+        RankZArgs a{};
+        a.Y = Y;
+        a.F = F;
+        a.ldy = (int)ldy;
+        a.M = (int)M;
+        a.C = (int)C;
+        a.f_j0 = (int)j0;
+        a.rl = rl;
+        a.chunk_c = chunk_c;
+        if (n_used > 1) {                                 // compact partials [chunk][M][rl]
+            a.out = zpart;
+            a.z_ld = rl;
+            a.z_j0 = 0;
+            a.chunk_stride = (size_t)M * rl;
+        } else {
+            a.out = Z;
+            a.z_ld = (int)z_ld;
+            a.z_j0 = (int)(z_j0 + j0);
+            a.chunk_stride = 0;
         }
-#undef RZ
-    }
-    if (n_used > 1) {
-        const int64_t n = d.M * d.r;
-        LAUNCH("partial_sum", partial_sum, dim3((unsigned)cdiv(n, 1024)), dim3(256), 0, st, zpart, Z, n, n_used);
+        const dim3 grid((unsigned)cdiv(M, 128), (unsigned)n_used, 1);
+        switch (jb) {
+            case 1: launch_rank_z_t<1, 256>(a, grid, st); break;
+            case 2: launch_rank_z_t<2, 256>(a, grid, st); break;
+            case 3: launch_rank_z_t<3, 256>(a, grid, st); break;
+            case 4: launch_rank_z_t<4, 256>(a, grid, st); break;
+            case 5: case 6: case 7: case 8: launch_rank_z_t<8, 256>(a, grid, st); break;
+            default: launch_rank_z_t<12, 128>(a, grid, st); break;
+        }
+        if (n_used > 1) {
+            const int64_t n = M * rl;
+            LAUNCH("partial_sum", partial_sum, dim3((unsigned)cdiv(n, 1024)), dim3(256), 0, st, zpart, Z, (int)M,
+                   rl, (int)z_ld, (int)(z_j0 + j0), n_used);
+        }
     }
 }
 
-// bf16 planes [r][Mp] of V^T and U^T in the workspace: V^T hi, V^T lo, U^T hi, U^T lo.
-uint16_t* zt_plane(const Plan& plan, char* wsb, int64_t r, int i) {
-    const size_t plane = align_up((size_t)r * plan.Mp * sizeof(uint16_t));
+// bf16 planes [G r][Mp] of V^T and U^T in the workspace: V^T hi, V^T lo, U^T hi, U^T lo.
+uint16_t* zt_plane(const Plan& plan, char* wsb, int64_t rows, int i) {
+    const size_t plane = align_up((size_t)rows * plan.Mp * sizeof(uint16_t));
     return reinterpret_cast<uint16_t*>(wsb + plan.off_zt + i * plane);
 }
 
-// dA and dB from X, V and dY, U: rank_stream partials of both in one launch, then
-// the fixed-order final sum, scale, dtype and layout.  planes_ready: the dX GEMM
+// dA and dB from X, V and dY, U: rank_stream partials (dA = s V^T X over the
+// stacked rank in 64-column problems; dB = s dY_m^T U_m per member), then the
+// fixed-order final sum, scale, dtype and layout.  planes_ready: the dX GEMM
 // has already written the hi / lo planes of V^T and U^T (V is then not read);
-// otherwise zt_hilo writes them.
-lora_status launch_adapter_grads(const lora_linear_desc& d, const Plan& plan, char* wsb, const uint16_t* X,
-                                 const float* V, const uint16_t* dY, const float* U, void* dA, void* dB,
-                                 bool planes_ready, hipStream_t st) {
-    RankArgs a{};
+// otherwise zt_hilo writes them.  Problems of one rank width share a launch.
+lora_status launch_adapter_grads(const Shape& d, const Plan& plan, char* wsb, const uint16_t* X, const float* V,
+                                 const uint16_t* dY, const float* U, void* dA, void* dB, bool planes_ready,
+                                 hipStream_t st) {
+    const int64_t rg = d.rg();
     float* const ga = reinterpret_cast<float*>(wsb + plan.off_ga);
     float* const gb = reinterpret_cast<float*>(wsb + plan.off_gb);
-    uint16_t* const vt_hi = zt_plane(plan, wsb, d.r, 0);
-    uint16_t* const vt_lo = zt_plane(plan, wsb, d.r, 1);
-    uint16_t* const ut_hi = zt_plane(plan, wsb, d.r, 2);
-    uint16_t* const ut_lo = zt_plane(plan, wsb, d.r, 3);
+    uint16_t* const vt_hi = zt_plane(plan, wsb, rg, 0);
+    uint16_t* const vt_lo = zt_plane(plan, wsb, rg, 1);
+    uint16_t* const ut_hi = zt_plane(plan, wsb, rg, 2);
+    uint16_t* const ut_lo = zt_plane(plan, wsb, rg, 3);
     if (!planes_ready) {
-        LAUNCH("zt_hilo", zt_hilo, dim3((unsigned)cdiv(d.r * plan.Mp, 256), 2), dim3(256), 0, st, V, U, vt_hi,
-                           vt_lo, ut_hi, ut_lo, (int)d.M, (int)plan.Mp, (int)d.r);
+        LAUNCH("zt_hilo", zt_hilo, dim3((unsigned)cdiv(rg * plan.Mp, 256), 2), dim3(256), 0, st, V, U, vt_hi,
+               vt_lo, ut_hi, ut_lo, (int)d.M, (int)plan.Mp, (int)rg);
         LAUNCH_CHECK("zt_hilo");
     }
-    a.prob[0] = RankProblem{X, vt_hi, vt_lo, ga, (int)d.K, (int)cdiv(d.K, kRT)};
-    a.prob[1] = RankProblem{dY, ut_hi, ut_lo, gb, (int)d.N, (int)cdiv(d.N, kRT)};
-    a.n_prob = 2;
-    a.M = (int)d.M;
-    a.r = (int)d.r;
-    a.chunk_tiles = plan.g.chunk_tiles;
-    a.n_chunk = plan.g.n_chunk;
-    const dim3 grid((unsigned)std::max(a.prob[0].n_tiles, a.prob[1].n_tiles), (unsigned)a.n_chunk, 2);
-    for (int j0 = 0; j0 < d.r; j0 += 64) {        // ranks above 64: one launch per 64 columns
-        a.j0 = j0;
-        switch (rpad_of(std::min<int64_t>(d.r - j0, 64))) {
-            case 16: LAUNCH("rank_stream", (rank_stream<16>), grid, dim3(256), 0, st, a); break;
-            case 32: LAUNCH("rank_stream", (rank_stream<32>), grid, dim3(256), 0, st, a); break;
-            default: LAUNCH("rank_stream", (rank_stream<64>), grid, dim3(256), 0, st, a); break;
+    // the problems, by rank padding (16, 32 or 64 columns)
+    RankProblem probs[3][4 * kMaxMembers];
+    int np[3] = {0, 0, 0};
+    auto pad_slot = [](int64_t rl) { return rl <= 16 ? 0 : rl <= 32 ? 1 : 2; };
+    for (int64_t j0 = 0; j0 < rg; j0 += 64) {            // dA^T [K][G r]: 64 rank columns per problem
+        const int64_t rl = std::min<int64_t>(rg - j0, 64);
+        const int sl = pad_slot(rl);
+        probs[sl][np[sl]++] = RankProblem{X, vt_hi, vt_lo, ga, (int)d.K, (int)d.K, (int)cdiv(d.K, kRT),
+                                          (int)rg, (int)j0, (int)rl, (int)rg, (int)j0, (size_t)d.K * rg};
+    }
+    for (int m = 0; m < d.G; ++m) {                       // dB [N][r]: member m's rows from its dY columns
+        for (int64_t j0 = 0; j0 < d.r; j0 += 64) {
+            const int64_t rl = std::min<int64_t>(d.r - j0, 64);
+            const int sl = pad_slot(rl);
+            probs[sl][np[sl]++] = RankProblem{dY + d.n0[m], ut_hi, ut_lo, gb + (size_t)d.n0[m] * d.r, (int)d.Nm(m),
+                                              (int)d.N, (int)cdiv(d.Nm(m), kRT), (int)rg, (int)(m * d.r + j0),
+                                              (int)rl, (int)d.r, (int)j0, (size_t)d.N * d.r};
+        }
+    }
+    for (int sl = 0; sl < 3; ++sl) {
+        for (int p0 = 0; p0 < np[sl]; p0 += kMaxRankProblems) {
+            RankArgs a{};
+            a.n_prob = std::min(np[sl] - p0, kMaxRankProblems);
+            int tiles = 1;
+            for (int i = 0; i < a.n_prob; ++i) {
+                a.prob[i] = probs[sl][p0 + i];
+                tiles = std::max(tiles, a.prob[i].n_tiles);
+            }
+            a.M = (int)d.M;
+            a.chunk_tiles = plan.g.chunk_tiles;
+            a.n_chunk = plan.g.n_chunk;
+            const dim3 grid((unsigned)tiles, (unsigned)a.n_chunk, (unsigned)a.n_prob);
+            switch (sl) {
+                case 0: LAUNCH("rank_stream", (rank_stream<16>), grid, dim3(256), 0, st, a); break;
+                case 1: LAUNCH("rank_stream", (rank_stream<32>), grid, dim3(256), 0, st, a); break;
+                default: LAUNCH("rank_stream", (rank_stream<64>), grid, dim3(256), 0, st, a); break;
+            }
         }
     }
     LAUNCH_CHECK("rank_stream(dA, dB)");
@@ -407,18 +548,25 @@ lora_status launch_adapter_grads(const lora_linear_desc& d, const Plan& plan, ch
     f.dB = dB;
     f.K = (int)d.K;
     f.N = (int)d.N;
-    f.r = (int)d.r;
+    f.ra = (int)rg;
+    f.rb = (int)d.r;
     f.n_chunk = plan.g.n_chunk;
     f.s = d.alpha / (float)d.r;
     f.f32_out = 0;
     f.accumulate = (d.flags & LORA_FLAG_ACCUM_GRADS) ? 1 : 0;
-    LAUNCH("grad_final", grad_final, dim3((unsigned)cdiv((d.K + d.N) * d.r, 256)), dim3(256), 0, st, f);
+    LAUNCH("grad_final", grad_final, dim3((unsigned)cdiv(d.K * rg + d.N * d.r, 256)), dim3(256), 0, st, f);
     LAUNCH_CHECK("grad_final");
     return LORA_OK;
 }
 
+// member boundaries of the forward GEMM's epilogue
+void set_members(GemmArgs& g, const Shape& d) {
+    g.n_members = d.G;
+    for (int m = 0; m <= d.G; ++m) g.member_q0[m] = (int)d.n0[m];
+}
+
 // ---------------------------------------------------------------- forward
-lora_status fwd_bf16(const lora_linear_desc& d, bool quant, const void* X, const void* W, const uint8_t* Wq,
+lora_status fwd_bf16(const Shape& d, bool quant, const void* X, const void* W, const uint8_t* Wq,
                      const uint16_t* absmax, const float* codebook, const void* A, const void* B, void* H,
                      float* U_save, void* ws, hipStream_t st) {
     const Plan plan = make_plan(d);
@@ -428,12 +576,12 @@ lora_status fwd_bf16(const lora_linear_desc& d, bool quant, const void* X, const
     const uint16_t* const A16 = static_cast<const uint16_t*>(A);
     float* const zpart = reinterpret_cast<float*>(wsb + plan.off_zp);
     const SplitPlan sp = gemm_split_plan(d.M, d.N, d.K, quant);
-    const bool in_tile = gemm_in_tile(quant, r, sp);
+    const bool in_tile = d.G == 1 && gemm_in_tile(quant, r, sp);
     float* U = U_save;
     if (!in_tile) {
-        // U = X A^T by the streamed pass, read by the GEMM epilogue
+        // U = X A^T (all members in one pass over X), read by the GEMM epilogue
         if (!U) U = reinterpret_cast<float*>(wsb + plan.off_u);
-        launch_rank_z(d, X16, d.K, A16, U, zpart, st);
+        launch_rank_z(d.M, X16, d.K, d.K, A16, d.rg(), U, d.rg(), 0, zpart, st);
         LAUNCH_CHECK("rank_z_lds(U)");
     }
     GemmArgs g{};
@@ -447,6 +595,8 @@ lora_status fwd_bf16(const lora_linear_desc& d, bool quant, const void* X, const
     g.Out = static_cast<uint16_t*>(H);
     g.Zsave = in_tile ? U_save : nullptr;
     g.Zin = in_tile ? nullptr : U;
+    g.z_ld = (int)d.rg();
+    set_members(g, d);
     g.Part = reinterpret_cast<float*>(wsb + plan.off_split);
     g.P = (int)d.M; g.Q = (int)d.N; g.C = (int)d.K; g.r = r;
     g.s = d.alpha / (float)d.r;
@@ -458,13 +608,16 @@ lora_status fwd_bf16(const lora_linear_desc& d, bool quant, const void* X, const
 
 // ---------------------------------------------------------------- backward
 // Order on the stream: U (if not saved) -> dX GEMM, which forms V = dY B in
-// the tile for r <= 16 (16-bit W) and saves it, or takes V from a streamed
-// pass -> dA, dB partials (one pass over X and one over dY) -> final sum.
-lora_status bwd_bf16(const lora_linear_desc& d, bool quant, const void* dY, const void* X, const void* W,
+// the tile for a plain layer with r = 8 or 16 (16-bit W) and saves it, or takes
+// V from streamed passes (one per member, over the member's dY columns) ->
+// dA, dB partials -> final sum.  With several members the dX GEMM contracts
+// over all their output columns at once: dX = sum_m (dY_m W_m + s V_m A_m).
+lora_status bwd_bf16(const Shape& d, bool quant, const void* dY, const void* X, const void* W,
                      const uint8_t* Wq, const uint16_t* absmax, const float* codebook, const void* A,
                      const void* B, const float* U_saved, void* dX, void* dA, void* dB, void* ws, hipStream_t st) {
     const Plan plan = make_plan(d);
     const int r = (int)d.r;
+    const int64_t rg = d.rg();
     char* const wsb = static_cast<char*>(ws);
     float* const V = reinterpret_cast<float*>(wsb + plan.off_v);
     float* const zpart = reinterpret_cast<float*>(wsb + plan.off_zp);
@@ -477,23 +630,25 @@ lora_status bwd_bf16(const lora_linear_desc& d, bool quant, const void* dY, cons
     const float* U = U_saved;
     if (!U) {
         float* Uw = reinterpret_cast<float*>(wsb + plan.off_u);
-        launch_rank_z(d, X16, d.K, A16, Uw, zpart, st);
+        launch_rank_z(d.M, X16, d.K, d.K, A16, rg, Uw, rg, 0, zpart, st);
         LAUNCH_CHECK("rank_z_lds(U)");
         U = Uw;
     }
     // 2. V = dY B: inside the dX GEMM when it runs in the in-tile form,
-    //    else the streamed pass
+    //    else the streamed pass of each member over its columns of dY
     const SplitPlan sp = gemm_split_plan(d.M, d.K, d.N, quant);
-    const bool v_in_tile = dX != nullptr && dx_in_tile(quant, r, sp);
+    const bool v_in_tile = dX != nullptr && d.G == 1 && dx_in_tile(quant, r, sp);
     if (!v_in_tile) {
         uint16_t* const BT = reinterpret_cast<uint16_t*>(wsb + plan.off_bt);
-        LAUNCH("transpose_rank", transpose_rank, dim3((unsigned)cdiv(d.r * d.N, 256)), dim3(256), 0, st, B16, BT,
-                           (int)d.N, (int)d.r);
-        LAUNCH_CHECK("transpose_rank");
-        launch_rank_z(d, dY16, d.N, BT, V, zpart, st);
+        for (int m = 0; m < d.G; ++m) {
+            uint16_t* const BTm = BT + (size_t)d.r * d.n0[m];
+            LAUNCH("transpose_rank", transpose_rank, dim3((unsigned)cdiv(d.r * d.Nm(m), 256)), dim3(256), 0, st,
+                   B16 + (size_t)d.n0[m] * d.r, BTm, (int)d.Nm(m), r);
+            launch_rank_z(d.M, dY16 + d.n0[m], d.N, d.Nm(m), BTm, d.r, V, rg, (int64_t)m * d.r, zpart, st);
+        }
         LAUNCH_CHECK("rank_z_lds(V)");
     }
-    // 3. dX = dY W + s V A
+    // 3. dX = dY W + s V A  (summed over the members: one contraction over all N columns)
     if (dX) {
         GemmArgs g{};
         g.L = dY16;
@@ -505,17 +660,18 @@ lora_status bwd_bf16(const lora_linear_desc& d, bool quant, const void* dY, cons
         g.E = A16;
         g.Out = static_cast<uint16_t*>(dX);
         g.Zin = v_in_tile ? nullptr : V;
+        g.z_ld = (int)rg;
         if (v_in_tile) {
             // V goes straight into the adapter-gradient planes (with U's), not to V [M][r]
-            g.Zt_hi = zt_plane(plan, wsb, d.r, 0);
-            g.Zt_lo = zt_plane(plan, wsb, d.r, 1);
-            g.Ut_hi = zt_plane(plan, wsb, d.r, 2);
-            g.Ut_lo = zt_plane(plan, wsb, d.r, 3);
+            g.Zt_hi = zt_plane(plan, wsb, rg, 0);
+            g.Zt_lo = zt_plane(plan, wsb, rg, 1);
+            g.Ut_hi = zt_plane(plan, wsb, rg, 2);
+            g.Ut_lo = zt_plane(plan, wsb, rg, 3);
             g.Uin = U;
             g.Mp = (int)plan.Mp;
         }
         g.Part = reinterpret_cast<float*>(wsb + plan.off_split);
-        g.P = (int)d.M; g.Q = (int)d.K; g.C = (int)d.N; g.r = r;
+        g.P = (int)d.M; g.Q = (int)d.K; g.C = (int)d.N; g.r = (int)rg;
         g.s = d.alpha / (float)d.r;
         if (quant) launch_gemm<true, true>(g, v_in_tile, sp, st);
         else launch_gemm<true, false>(g, v_in_tile, sp, st);
@@ -546,7 +702,7 @@ void launch_f32_fused_mode(int rmode, const F32FusedArgs& a, hipStream_t st) {
 lora_status fwd_f32(const lora_linear_desc& d, bool quant, const void* X, const void* W, const uint8_t* Wq,
                     const uint16_t* absmax, const float* codebook, const void* A, const void* B, void* H,
                     float* U_save, void* ws, hipStream_t st) {
-    const Plan plan = make_plan(d);
+    const Plan plan = make_plan(shape_of(d));
     float* U = U_save ? U_save : reinterpret_cast<float*>(static_cast<char*>(ws) + plan.off_u);
     const int M = (int)d.M, K = (int)d.K, N = (int)d.N, r = (int)d.r;
     LAUNCH("f32_skinny", f32_skinny, dim3((unsigned)cdiv((int64_t)M * r, 256)), dim3(256), 0, st,
@@ -569,7 +725,7 @@ lora_status fwd_f32(const lora_linear_desc& d, bool quant, const void* X, const 
 lora_status bwd_f32(const lora_linear_desc& d, bool quant, const void* dY, const void* X, const void* W,
                     const uint8_t* Wq, const uint16_t* absmax, const float* codebook, const void* A, const void* B,
                     const float* U_saved, void* dX, void* dA, void* dB, void* ws, hipStream_t st) {
-    const Plan plan = make_plan(d);
+    const Plan plan = make_plan(shape_of(d));
     char* const wsb = static_cast<char*>(ws);
     float* const V = reinterpret_cast<float*>(wsb + plan.off_v);
     const int M = (int)d.M, K = (int)d.K, N = (int)d.N, r = (int)d.r;
@@ -648,7 +804,7 @@ lora_status scratch_on_current_device(void** out) {
 // layout up to its last region, plus the float32 slices of the input
 // gradient's own split contraction (the workspace is sized for the 4-bit
 // plans too, whose forward splits more).
-size_t bwd_scratch_bytes(const lora_linear_desc& d) {
+size_t bwd_scratch_bytes(const Shape& d) {
     const Plan p = make_plan(d);
     if (d.dtype != LORA_DTYPE_BF16) return p.total;
     return p.off_split + align_up(gemm_split_plan(d.M, d.K, d.N, false).part_floats * sizeof(float));
@@ -679,30 +835,37 @@ void gemm_ranges(RangeList& L, const char* name, bool trans, bool quant, bool in
     if (in_tile) L.add(name, trans ? "B" : "A", trans ? whole_bytes(C, r) : whole_bytes(r, C));
 }
 
-void rank_z_ranges(RangeList& L, const char* name, int64_t M, int64_t C, int64_t r) {
-    L.add(name, "Y block (128 rows)", panel_bytes(M, 0, 128, C));
-    L.add(name, "F rows", whole_bytes(r, C));
+void rank_z_ranges(RangeList& L, const char* name, int64_t M, int64_t C, int64_t ldy, int64_t f_rows) {
+    L.add(name, "Y block (128 rows)", strided_panel_bytes(M, 0, 128, C, ldy));
+    L.add(name, "F rows", whole_bytes(std::min(f_rows, kMaxZCols), C));
 }
 
-void buffer_ranges(const lora_linear_desc& d, bool quant, RangeList& L) {
+void buffer_ranges(const Shape& d, bool quant, RangeList& L) {
     if (d.dtype != LORA_DTYPE_BF16) return;          // the float32 mode uses plain loads only
     const int r = (int)d.r;
+    const int64_t rg = d.rg();
     const SplitPlan spf = gemm_split_plan(d.M, d.N, d.K, quant);
     const SplitPlan spb = gemm_split_plan(d.M, d.K, d.N, quant);
     // forward (U by the streamed pass when it is not formed in the tile)
-    const bool fwd_in_tile = gemm_in_tile(quant, r, spf);
-    if (!fwd_in_tile) rank_z_ranges(L, "rank_z_lds (U = X A^T)", d.M, d.K, d.r);
+    const bool fwd_in_tile = d.G == 1 && gemm_in_tile(quant, r, spf);
+    rank_z_ranges(L, "rank_z_lds (U = X A^T)", d.M, d.K, d.K, rg);   // forward, or a backward without U
     gemm_ranges(L, "lora_gemm (forward)", false, quant, fwd_in_tile, d.M, d.N, d.K, d.r);
-    // backward: U recomputed when not saved, V streamed unless the dX GEMM forms it
-    if (fwd_in_tile) rank_z_ranges(L, "rank_z_lds (U = X A^T)", d.M, d.K, d.r);
-    rank_z_ranges(L, "rank_z_lds (V = dY B)", d.M, d.N, d.r);
-    gemm_ranges(L, "lora_gemm (dX)", true, quant, dx_in_tile(quant, r, spb), d.M, d.K, d.N, d.r);
-    for (int64_t j0 = 0; j0 < d.r; j0 += 64) {
-        const int64_t rl = std::min<int64_t>(d.r - j0, 64);
+    // backward: V streamed per member unless the dX GEMM forms it
+    for (int m = 0; m < d.G; ++m) rank_z_ranges(L, "rank_z_lds (V = dY B)", d.M, d.Nm(m), d.N, d.r);
+    gemm_ranges(L, "lora_gemm (dX)", true, quant, d.G == 1 && dx_in_tile(quant, r, spb), d.M, d.K, d.N, d.r);
+    for (int64_t j0 = 0; j0 < rg; j0 += 64) {
+        const int64_t rl = std::min<int64_t>(rg - j0, 64);
         const int64_t TM = rpad_of(rl) <= 16 ? kRT : kRT / 2;
-        L.add("rank_stream (dA partials)", "X step", stream_y_bytes(d.M, d.K, 0, 0, TM));
-        L.add("rank_stream (dB partials)", "dY step", stream_y_bytes(d.M, d.N, 0, 0, TM));
-        L.add("rank_stream (dA, dB partials)", "rank plane block (hi, lo)", stream_side_bytes(rl, TM));
+        L.add("rank_stream (dA partials)", "X step", stream_y_bytes(d.M, d.K, 0, 0, TM, d.K));
+        L.add("rank_stream (dA partials)", "rank plane block (hi, lo)", stream_side_bytes(rl, TM));
+    }
+    for (int m = 0; m < d.G; ++m) {
+        for (int64_t j0 = 0; j0 < d.r; j0 += 64) {
+            const int64_t rl = std::min<int64_t>(d.r - j0, 64);
+            const int64_t TM = rpad_of(rl) <= 16 ? kRT : kRT / 2;
+            L.add("rank_stream (dB partials)", "dY step", stream_y_bytes(d.M, d.Nm(m), 0, 0, TM, d.N));
+            L.add("rank_stream (dB partials)", "rank plane block (hi, lo)", stream_side_bytes(rl, TM));
+        }
     }
 }
 
@@ -734,7 +897,7 @@ lora_status lora_linear_workspace_size(const lora_linear_desc* desc, size_t* byt
     if (!bytes) return fail(LORA_ERR_INVALID_ARG, "bytes is NULL");
     lora_status st = check_desc(desc, false);
     if (st != LORA_OK) return st;
-    *bytes = make_plan(*desc).total;
+    *bytes = make_plan(shape_of(*desc)).total;
     return ok();
 }
 
@@ -745,7 +908,7 @@ lora_status lora_linear_buffer_ranges(const lora_linear_desc* desc, int32_t quan
     lora_status st = check_desc(desc, quant != 0);
     if (st != LORA_OK) return st;
     RangeList L{out, capacity, 0};
-    buffer_ranges(*desc, quant != 0, L);
+    buffer_ranges(shape_of(*desc), quant != 0, L);
     *count = L.n;
     return ok();
 }
@@ -762,7 +925,7 @@ lora_status lora_linear_bwd_noalloc(const lora_linear_desc* desc, const void* dY
                         {{dY, "dY"}, {X, "X"}, {W, "W"}, {A, "A"}, {B, "B"}, {U_saved, "U_saved"},
                          {dX, "dX"}, {dA, "dA"}, {dB, "dB"}});
     if (st != LORA_OK) return st;
-    const size_t need = bwd_scratch_bytes(*desc);
+    const size_t need = bwd_scratch_bytes(shape_of(*desc));
     if (need > kScratchBytes)
         return fail(LORA_ERR_UNSUPPORTED,
                     "this backward needs %zu bytes of intermediates; the allocation-free entry point holds %zu "
@@ -779,7 +942,49 @@ lora_status lora_linear_bwd_noalloc(const lora_linear_desc* desc, const void* dY
     }
     if (desc->dtype == LORA_DTYPE_F32)
         return bwd_f32(*desc, false, dY, X, W, nullptr, nullptr, nullptr, A, B, U_saved, dX, dA, dB, ws, s);
-    return bwd_bf16(*desc, false, dY, X, W, nullptr, nullptr, nullptr, A, B, U_saved, dX, dA, dB, ws, s);
+    return bwd_bf16(shape_of(*desc), false, dY, X, W, nullptr, nullptr, nullptr, A, B, U_saved, dX, dA, dB, ws, s);
+}
+
+lora_status lora_group_workspace_size(const lora_group_desc* desc, size_t* bytes) {
+    if (!bytes) return fail(LORA_ERR_INVALID_ARG, "bytes is NULL");
+    lora_status st = check_group(desc);
+    if (st != LORA_OK) return st;
+    *bytes = make_plan(shape_of(*desc)).total;
+    return ok();
+}
+
+lora_status lora_group_fwd(const lora_group_desc* desc, const void* X, const void* W, const void* A, const void* B,
+                           void* H, float* U_save, void* ws, size_t ws_bytes, void* stream) {
+    lora_status st = check_group(desc);
+    if (st != LORA_OK) return st;
+    st = check_ptrs({{X, "X"}, {W, "W"}, {A, "A"}, {B, "B"}, {H, "H"}}, {{U_save, "U_save"}});
+    if (st != LORA_OK) return st;
+    st = check_no_alias({{H, "H"}, {U_save, "U_save"}},
+                        {{X, "X"}, {W, "W"}, {A, "A"}, {B, "B"}, {H, "H"}, {U_save, "U_save"}, {ws, "ws"}});
+    if (st != LORA_OK) return st;
+    const Shape d = shape_of(*desc);
+    st = check_ws(d, ws, ws_bytes);
+    if (st != LORA_OK) return st;
+    return fwd_bf16(d, false, X, W, nullptr, nullptr, nullptr, A, B, H, U_save, ws, static_cast<hipStream_t>(stream));
+}
+
+lora_status lora_group_bwd(const lora_group_desc* desc, const void* dY, const void* X, const void* W, const void* A,
+                           const void* B, const float* U_saved, void* dX, void* dA, void* dB, void* ws,
+                           size_t ws_bytes, void* stream) {
+    lora_status st = check_group(desc);
+    if (st != LORA_OK) return st;
+    st = check_ptrs({{dY, "dY"}, {X, "X"}, {W, "W"}, {A, "A"}, {B, "B"}, {dA, "dA"}, {dB, "dB"}},
+                    {{U_saved, "U_saved"}, {dX, "dX"}});
+    if (st != LORA_OK) return st;
+    st = check_no_alias({{dX, "dX"}, {dA, "dA"}, {dB, "dB"}},
+                        {{dY, "dY"}, {X, "X"}, {W, "W"}, {A, "A"}, {B, "B"}, {U_saved, "U_saved"},
+                         {dX, "dX"}, {dA, "dA"}, {dB, "dB"}, {ws, "ws"}});
+    if (st != LORA_OK) return st;
+    const Shape d = shape_of(*desc);
+    st = check_ws(d, ws, ws_bytes);
+    if (st != LORA_OK) return st;
+    return bwd_bf16(d, false, dY, X, W, nullptr, nullptr, nullptr, A, B, U_saved, dX, dA, dB, ws,
+                    static_cast<hipStream_t>(stream));
 }
 
 lora_status lora_linear_fwd(const lora_linear_desc* desc, const void* X, const void* W, const void* A,
@@ -795,7 +1000,7 @@ lora_status lora_linear_fwd(const lora_linear_desc* desc, const void* X, const v
     if (st != LORA_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (desc->dtype == LORA_DTYPE_F32) return fwd_f32(*desc, false, X, W, nullptr, nullptr, nullptr, A, B, H, U_save, ws, s);
-    return fwd_bf16(*desc, false, X, W, nullptr, nullptr, nullptr, A, B, H, U_save, ws, s);
+    return fwd_bf16(shape_of(*desc), false, X, W, nullptr, nullptr, nullptr, A, B, H, U_save, ws, s);
 }
 
 lora_status lora_linear_bwd(const lora_linear_desc* desc, const void* dY, const void* X, const void* W,
@@ -815,7 +1020,7 @@ lora_status lora_linear_bwd(const lora_linear_desc* desc, const void* dY, const 
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (desc->dtype == LORA_DTYPE_F32)
         return bwd_f32(*desc, false, dY, X, W, nullptr, nullptr, nullptr, A, B, U_saved, dX, dA, dB, ws, s);
-    return bwd_bf16(*desc, false, dY, X, W, nullptr, nullptr, nullptr, A, B, U_saved, dX, dA, dB, ws, s);
+    return bwd_bf16(shape_of(*desc), false, dY, X, W, nullptr, nullptr, nullptr, A, B, U_saved, dX, dA, dB, ws, s);
 }
 
 lora_status lora_qlinear_fwd(const lora_linear_desc* desc, const void* X, const uint8_t* Wq, const uint16_t* absmax,
@@ -834,7 +1039,7 @@ lora_status lora_qlinear_fwd(const lora_linear_desc* desc, const void* X, const 
     if (st != LORA_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (desc->dtype == LORA_DTYPE_F32) return fwd_f32(*desc, true, X, nullptr, Wq, absmax, codebook, A, B, H, U_save, ws, s);
-    return fwd_bf16(*desc, true, X, nullptr, Wq, absmax, codebook, A, B, H, U_save, ws, s);
+    return fwd_bf16(shape_of(*desc), true, X, nullptr, Wq, absmax, codebook, A, B, H, U_save, ws, s);
 }
 
 lora_status lora_qlinear_bwd(const lora_linear_desc* desc, const void* dY, const void* X, const uint8_t* Wq,
@@ -856,7 +1061,7 @@ lora_status lora_qlinear_bwd(const lora_linear_desc* desc, const void* dY, const
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (desc->dtype == LORA_DTYPE_F32)
         return bwd_f32(*desc, true, dY, X, nullptr, Wq, absmax, codebook, A, B, U_saved, dX, dA, dB, ws, s);
-    return bwd_bf16(*desc, true, dY, X, nullptr, Wq, absmax, codebook, A, B, U_saved, dX, dA, dB, ws, s);
+    return bwd_bf16(shape_of(*desc), true, dY, X, nullptr, Wq, absmax, codebook, A, B, U_saved, dX, dA, dB, ws, s);
 }
 
 lora_status lora_merge(const lora_linear_desc* desc, const void* W, const void* A, const void* B, void* W_out,

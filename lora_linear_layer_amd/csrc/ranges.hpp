@@ -27,6 +27,13 @@ __host__ __device__ inline uint64_t panel_bytes(int64_t total, int64_t row0, int
     return (uint64_t)rmin64(total - row0, rows) * (uint64_t)C * 2u;
 }
 
+// Rows [row0, row0 + rows) of a bf16 matrix with C used columns and row stride
+// ld, clipped to its `total` rows (the last row only up to C).
+__host__ __device__ inline uint64_t strided_panel_bytes(int64_t total, int64_t row0, int64_t rows, int64_t C,
+                                                        int64_t ld) {
+    return ((uint64_t)(rmin64(total - row0, rows) - 1) * (uint64_t)ld + (uint64_t)C) * 2u;
+}
+
 // Input-gradient GEMM, W tile of one stage: rows c0 .. c0 + 63 of W [C][Q]
 // from column q0 on (the last row only up to Q).
 __host__ __device__ inline uint64_t gemm_wt_stage_bytes(int64_t C, int64_t Q, int64_t c0, int64_t q0) {
@@ -34,10 +41,11 @@ __host__ __device__ inline uint64_t gemm_wt_stage_bytes(int64_t C, int64_t Q, in
     return (uint64_t)(rows_left - 1) * (uint64_t)Q * 2u + (uint64_t)(Q - q0) * 2u;
 }
 
-// rank_stream, Y tile of one step: rows m0 .. m0 + TM - 1 of Y [M][C] from
-// column c0 on (the last row only up to C).
-__host__ __device__ inline uint64_t stream_y_bytes(int64_t M, int64_t C, int64_t m0, int64_t c0, int64_t TM) {
-    return (uint64_t)(rmin64(M - m0, TM) - 1) * (uint64_t)C * 2u + (uint64_t)(C - c0) * 2u;
+// rank_stream, Y tile of one step: rows m0 .. m0 + TM - 1 of Y [M][C] (row
+// stride ld) from column c0 on (the last row only up to C).
+__host__ __device__ inline uint64_t stream_y_bytes(int64_t M, int64_t C, int64_t m0, int64_t c0, int64_t TM,
+                                                   int64_t ld) {
+    return (uint64_t)(rmin64(M - m0, TM) - 1) * (uint64_t)ld * 2u + (uint64_t)(C - c0) * 2u;
 }
 
 // Rank planes (bf16 hi / lo of Z^T for the adapter gradients), token-block

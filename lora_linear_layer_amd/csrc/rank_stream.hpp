@@ -29,20 +29,27 @@ namespace lora {
 
 constexpr int kRT = 128;      // tile edge (rows of Y x columns of Y)
 
+// One product G[c][j] = sum_m Y[m][c] Z2[m][s_j0 + j], c < C, j < rl (at most RPAD),
+// into part[chunk * chunk_stride + c * out_r + out_j0 + j].
 struct RankProblem {
-    const uint16_t* Y;      // [M][C] bf16
-    const uint16_t* S;      // hi plane of Z2^T, bf16 [r][Mp] in zt_index order
+    const uint16_t* Y;      // [M][C] bf16, row stride ldy
+    const uint16_t* S;      // hi plane of Z2^T, bf16 [s_rows][Mp] in zt_index order
     const uint16_t* S_lo;   // lo plane of Z2^T (same shape)
-    float* part;            // [n_chunk][C][r]
-    int C;
+    float* part;            // token-chunk partials, chunk_stride floats apart
+    int C, ldy;
     int n_tiles;            // 128-wide tiles of c
+    int s_rows, s_j0;       // rows of the planes, first plane row used
+    int rl;                 // rank columns of this problem
+    int out_r, out_j0;
+    size_t chunk_stride;
 };
 
+constexpr int kMaxRankProblems = 8;
+
 struct RankArgs {
-    RankProblem prob[2];
+    RankProblem prob[kMaxRankProblems];
     int n_prob;
-    int M, r;
-    int j0;                 // first rank column handled by this launch (ranks above 64 take two launches)
+    int M;
     int chunk_tiles;        // contraction tiles per chunk
     int n_chunk;
 };
@@ -77,7 +84,7 @@ __device__ __forceinline__ int side_swz(int row) {
     else return (row >> 1) & 7;
 }
 
-// Handles rank columns j0 .. j0 + min(r - j0, RPAD) - 1.
+// Problem blockIdx.z, output tile blockIdx.x, token chunk blockIdx.y.
 template <int RPAD>
 __global__ __launch_bounds__(256) void rank_stream(const RankArgs a) {
     using SM = RankSmem<RPAD>;
@@ -92,8 +99,8 @@ __global__ __launch_bounds__(256) void rank_stream(const RankArgs a) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, g4 = lane >> 4;
-    const int M = a.M, C = pr.C, r = a.r, j0 = a.j0;
-    const int rl = min(r - j0, RPAD);                  // rank columns of this launch
+    const int M = a.M, C = pr.C, ldy = pr.ldy;
+    const int rl = min(pr.rl, RPAD);                   // rank columns of this problem
     // the output tile c0 = o0; token tiles [t_begin, t_end) of 128, walked in
     // steps of TM tokens: [s_begin, s_end)
     const int o0 = blockIdx.x * kRT;
@@ -109,19 +116,20 @@ __global__ __launch_bounds__(256) void rank_stream(const RankArgs a) {
     auto issue_y = [&](int t, uint8_t* Ys) {
         const int m0 = t * TM;
         const int c0 = o0;
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(pr.Y + (size_t)m0 * C + c0, stream_y_bytes(M, C, m0, c0, TM));
+        const __amdgpu_buffer_rsrc_t rs =
+            make_rsrc(pr.Y + (size_t)m0 * ldy + c0, stream_y_bytes(M, C, m0, c0, TM, ldy));
 #pragma unroll
         for (int i = 0; i < YLW; ++i) {
             const int b = wave * YLW + i;
             const int row = 4 * b + (lane >> 4);
             const int ch = ((lane & 15) ^ y_swz(row)) * 8;
-            g2lds16<true>(rs, Ys + b * 1024, (c0 + ch < C) ? (uint32_t)(row * C + ch) * 2u : kOOB);
+            g2lds16<true>(rs, Ys + b * 1024, (c0 + ch < C) ? (uint32_t)(row * ldy + ch) * 2u : kOOB);
         }
     };
-    // side tile(s) of step t: rank rows j0 .. j0 + RPAD - 1 of S (and S_lo), tokens
+    // side tile(s) of step t: plane rows s_j0 .. s_j0 + RPAD - 1 of S (and S_lo), tokens
     // t TM .. + TM - 1, which lie in one 128-token block of the planes (rows
     // 256 bytes apart there); in LDS rows of 2 TM bytes whose 16-byte chunk ch of
-    // row x sits at ch ^ side_swz(x).  The resources start at row j0 of the
+    // row x sits at ch ^ side_swz(x).  The resources start at row s_j0 of the
     // step's block, so their range is a few KB whatever M is.  Wave w issues
     // loads b = SLW w .. of each plane, each SRL rows: row = SRL b + lane / (TM / 8)
     constexpr int SLW = RPAD * TM / 2048;             // side loads per wave per plane
@@ -131,7 +139,7 @@ __global__ __launch_bounds__(256) void rank_stream(const RankArgs a) {
     const uint64_t side_range = stream_side_bytes(rl, TM);
     auto issue_side = [&](int t, uint8_t* Ss) {
         const int64_t m0 = (int64_t)t * TM;
-        const size_t base = zt_index(j0, m0, r);
+        const size_t base = zt_index(pr.s_j0, m0, pr.s_rows);
         const __amdgpu_buffer_rsrc_t rsS = make_rsrc(pr.S + base, side_range);
         const __amdgpu_buffer_rsrc_t rsSl = make_rsrc(pr.S_lo + base, side_range);
 #pragma unroll
@@ -198,7 +206,7 @@ __global__ __launch_bounds__(256) void rank_stream(const RankArgs a) {
 
     // lane holds out^T rows j = jt*16 + 4 g4 + i at column o = block*16 + l16
     const int olim = C;
-    float* const out = pr.part + (size_t)blockIdx.y * olim * r;
+    float* const out = pr.part + (size_t)blockIdx.y * pr.chunk_stride;
 #pragma unroll
     for (int jt = 0; jt < JT; ++jt)
 #pragma unroll
@@ -208,48 +216,63 @@ __global__ __launch_bounds__(256) void rank_stream(const RankArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int j = jt * 16 + 4 * g4 + i;
-                if (j < rl) out[(size_t)o * r + j0 + j] = acc[jt][z][i];
+                if (j < rl) out[(size_t)o * pr.out_r + pr.out_j0 + j] = acc[jt][z][i];
             }
         }
 }
 
-// Z with the rank side in LDS: Z[m][j] = sum_c Y[m][c] F[j][c] (F bf16 rows [r][C]).
+// Z with the rank side in LDS: Z[m][z_j0 + j] = sum_c Y[m][c] F[f_j0 + j][c] for
+// j < rl (F bf16 rows [f_rows][C], row stride C; Y [M][C] with row stride ldy).
 // Workgroup (x, y): 8 waves; wave w owns rows m = 128 x + 16 w + (0 .. 15) (one MFMA
 // row block) and the workgroup the contraction chunk y, [cb, ce), chunk_c columns (a
-// multiple of 256).  Y is addressed from the workgroup's first row (a 128-row
-// block stays below 2^29 bytes), so Y itself may exceed 2 GB.  F comes in 256-column slices through a double-buffered LDS pair
-// (row j of a slice: 512 bytes, 16-byte chunk ch stored at ch ^ (j % 16), so the 16
-// rows one fragment read touches hit distinct banks); each lane loads its Y fragment
-// (8 consecutive c of one row, 16 bytes) straight from global memory into registers,
-// D = 8 steps of 32 columns ahead.  Out-of-range rows, columns and rank rows read
-// zero.  Writes the float32 partial part[y][m][j0 + j] for j < min(r - j0, 16 JB).
-template <int JB>
-__global__ __launch_bounds__(512) void rank_z_lds(const uint16_t* __restrict__ Y, const uint16_t* __restrict__ F,
-                                                  float* __restrict__ part, int M, int C, int r, int j0,
-                                                  int chunk_c) {
-    constexpr int D = 8;                               // steps in flight = steps per slice
-    constexpr int SC = 256;                            // slice columns
+// multiple of SC).  Y is addressed from the workgroup's first row (a 128-row
+// block stays below 2^29 bytes), so Y itself may exceed 2 GB.  F comes in
+// SC-column slices (16 JB rows each) through a double-buffered LDS pair (row j
+// of a slice: 2 SC bytes, 16-byte chunk ch stored at ch ^ (j % 16), so the 16
+// rows one fragment read touches hit distinct banks); each lane loads its Y
+// fragment (8 consecutive c of one row, 16 bytes) straight from global memory
+// into registers, D = SC / 32 steps of 32 columns ahead.  Every Y fragment
+// feeds JB MFMAs, so one pass over Y forms up to 16 JB rank columns (JB = 12:
+// 192, with 128-column slices to stay within LDS).  Out-of-range rows, columns
+// and rank rows read zero.  Writes out[y * chunk_stride + m * z_ld + z_j0 + j].
+struct RankZArgs {
+    const uint16_t* Y;
+    const uint16_t* F;
+    float* out;
+    size_t chunk_stride;      // floats between the partials of two contraction chunks
+    int ldy, z_ld;
+    int M, C, f_j0, rl, z_j0, chunk_c;
+};
+
+template <int JB, int SC>
+__global__ __launch_bounds__(512) void rank_z_lds(const RankZArgs a) {
+    constexpr int D = SC / 32;                         // steps in flight = steps per slice
     constexpr int FBYTES = 16 * JB * SC * 2;           // one F slice
+    constexpr int RPL = 1024 / (2 * SC);               // F rows per 1 KB load (2 or 4)
+    constexpr int FLW = 16 * JB / RPL / 8;             // F loads per wave per slice
+    static_assert(FLW >= 1 && 16 * JB == FLW * 8 * RPL, "F slice is whole loads for 8 waves");
+    static_assert(2 * FBYTES <= 160 * 1024, "LDS budget");
     __shared__ __attribute__((aligned(1024))) uint8_t fs[2 * FBYTES];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int l16 = lane & 15, g4 = lane >> 4;
+    const int M = a.M, C = a.C;
     const int m0 = (int)blockIdx.x * 128;
     const int m = m0 + wave * 16 + l16;
-    const int cb = (int)blockIdx.y * chunk_c;
-    const int ce = min(C, cb + chunk_c);
+    const int cb = (int)blockIdx.y * a.chunk_c;
+    const int ce = min(C, cb + a.chunk_c);
     const int nsl = (ce - cb + SC - 1) / SC;
-    const int rl = min(r - j0, 16 * JB);
-    const __amdgpu_buffer_rsrc_t rsY = make_rsrc(Y + (size_t)m0 * C, panel_bytes(M, m0, 128, C));
-    const __amdgpu_buffer_rsrc_t rsF = make_rsrc(F, whole_bytes(r, C));
-    const uint32_t yoff = m < M ? (uint32_t)((m - m0) * C + cb + 8 * g4) * 2u : kOOB;
-    // F slice: load i (1 KB) covers rows 2 i and 2 i + 1; wave w issues i = JB w .. JB w + JB - 1
+    const int rl = a.rl;
+    const __amdgpu_buffer_rsrc_t rsY = make_rsrc(a.Y + (size_t)m0 * a.ldy, strided_panel_bytes(M, m0, 128, C, a.ldy));
+    const __amdgpu_buffer_rsrc_t rsF = make_rsrc(a.F + (size_t)a.f_j0 * C, whole_bytes(rl, C));
+    const uint32_t yoff = m < M ? (uint32_t)((m - m0) * a.ldy + cb + 8 * g4) * 2u : kOOB;
+    // F slice: load i (1 KB) covers rows RPL i .. RPL i + RPL - 1; wave w issues i = FLW w ..
     auto issue_f = [&](int sl, uint8_t* buf) {
 #pragma unroll
-        for (int t = 0; t < JB; ++t) {
-            const int i = wave * JB + t;
-            const int row = 2 * i + (lane >> 5);
-            const int col = cb + sl * SC + (((lane & 31) ^ (row & 15)) << 3);
-            const uint32_t off = (row < rl && col < ce) ? (uint32_t)((size_t)(j0 + row) * C + col) * 2u : kOOB;
+        for (int t = 0; t < FLW; ++t) {
+            const int i = wave * FLW + t;
+            const int row = RPL * i + lane / (SC / 8);
+            const int col = cb + sl * SC + (((lane % (SC / 8)) ^ (row & 15)) << 3);
+            const uint32_t off = (row < rl && col < ce) ? (uint32_t)(row * C + col) * 2u : kOOB;
             g2lds16<true>(rsF, buf + i * 1024, off);
         }
     };
@@ -288,11 +311,12 @@ __global__ __launch_bounds__(512) void rank_z_lds(const uint16_t* __restrict__ Y
     vmcnt_le<0>();
     // lane holds Z^T rows j = 16 jb + 4 g4 + e at column m
     if (m < M) {
-        float* const out = part + (size_t)blockIdx.y * M * r + (size_t)m * r + j0;
+        float* const out = a.out + (size_t)blockIdx.y * a.chunk_stride + (size_t)m * a.z_ld + a.z_j0;
+        const bool vec = ((a.z_ld | a.z_j0) & 3) == 0;
 #pragma unroll
         for (int jb = 0; jb < JB; ++jb) {
             const int j = 16 * jb + 4 * g4;
-            if ((r & 3) == 0 && j + 3 < rl) {
+            if (vec && j + 3 < rl) {
                 *reinterpret_cast<f32x4*>(out + j) = acc[jb];
             } else {
 #pragma unroll
@@ -333,18 +357,21 @@ __global__ __launch_bounds__(256) void transpose_rank(const uint16_t* __restrict
     out[e] = B[(size_t)n * r + j];
 }
 
-// out[e] = sum over k < n_parts of part[k * n + e], added in increasing k.
-// Each thread owns 4 consecutive elements; the partial loads are issued 8 at a
-// time so that their latencies overlap (the additions keep the fixed order).
-__global__ __launch_bounds__(256) void partial_sum(const float* __restrict__ part, float* __restrict__ out, int64_t n,
-                                                   int n_parts) {
+// out[m * out_ld + out_j0 + j] = sum over k < n_parts of part[k * M * w + m * w + j]
+// (j < w), added in increasing k: the contraction-chunk partials of one
+// rank_z_lds launch (compact rows of w columns) into its columns of Z.  Each
+// thread owns 4 consecutive partial elements; the partial loads are issued 8
+// at a time so that their latencies overlap (the additions keep the fixed order).
+__global__ __launch_bounds__(256) void partial_sum(const float* __restrict__ part, float* __restrict__ out, int M,
+                                                   int w, int out_ld, int out_j0, int n_parts) {
+    const int64_t n = (int64_t)M * w;
     const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
     if (e0 >= n) return;
     const int cnt = (int)min<int64_t>(4, n - e0);
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
     auto load4 = [&](int k) -> f32x4 {
         const float* p = part + (size_t)k * n + e0;
-        if (cnt == 4 && (e0 & 3) == 0 && (n & 3) == 0) return *reinterpret_cast<const f32x4*>(p);
+        if (cnt == 4 && (n & 3) == 0) return *reinterpret_cast<const f32x4*>(p);
         f32x4 v = {0.f, 0.f, 0.f, 0.f};
         for (int i = 0; i < cnt; ++i) v[i] = p[i];
         return v;
@@ -358,25 +385,29 @@ __global__ __launch_bounds__(256) void partial_sum(const float* __restrict__ par
         for (int u = 0; u < 8; ++u) s += v[u];
     }
     for (; k < n_parts; ++k) s += load4(k);
-    for (int i = 0; i < cnt; ++i) out[e0 + i] = s[i];
+    for (int i = 0; i < cnt; ++i) {
+        const int64_t e = e0 + i;
+        const int64_t mm = e / w;
+        out[mm * out_ld + out_j0 + (e - mm * w)] = s[i];
+    }
 }
 
 // Final adapter gradients from the rank_stream partials:
-//   dA[j][k] = s * sum_chunk GA[chunk][k][j]   ([r][K] output)
-//   dB[n][j] = s * sum_chunk GB[chunk][n][j]   ([N][r] output)
+//   dA[j][k] = s * sum_chunk GA[chunk][k][j]   ([ra][K] output; ra = G r for a group)
+//   dB[n][j] = s * sum_chunk GB[chunk][n][j]   ([N][rb] output)
 // in the tensor dtype, overwritten or accumulated.
 struct GradFinalArgs {
-    const float* ga;
-    const float* gb;
-    void* dA;
-    void* dB;
-    int K, N, r, n_chunk;
+    const float* ga;        // [n_chunk][K][ra]
+    const float* gb;        // [n_chunk][N][rb]
+    void* dA;               // [ra][K]
+    void* dB;               // [N][rb]
+    int K, N, ra, rb, n_chunk;
     float s;
     int f32_out, accumulate;
 };
 
 __global__ __launch_bounds__(256) void grad_final(const GradFinalArgs a) {
-    const int64_t na = (int64_t)a.K * a.r, nb = (int64_t)a.N * a.r;
+    const int64_t na = (int64_t)a.K * a.ra, nb = (int64_t)a.N * a.rb;
     const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (e >= na + nb) return;
     const bool isA = e < na;
@@ -396,7 +427,7 @@ __global__ __launch_bounds__(256) void grad_final(const GradFinalArgs a) {
     float v = sum * a.s;
     size_t o;
     if (isA) {
-        const int kk = (int)(f / a.r), j = (int)(f % a.r);
+        const int kk = (int)(f / a.ra), j = (int)(f % a.ra);
         o = (size_t)j * a.K + kk;
     } else {
         o = (size_t)f;

@@ -254,3 +254,39 @@ def test_kernel_timer_set_and_clear():
     finally:
         lla.lora_set_kernel_timer(None)
     assert seen == []
+
+
+# ------------------------------------------------------------ grouped linears
+def test_group_desc_layout_and_checks():
+    from lora_linear_layer_amd._lib import LoraGroupDesc
+    assert ctypes.sizeof(LoraGroupDesc) == 3 * 8 + 4 + 4 + 4 + 4 + 8 * 8     # pad after n_members
+    assert LoraGroupDesc.N.offset == 40
+    ok = lla.GroupDesc(64, 256, (256, 64, 64), 16, 32.0)
+    assert lla.lora_group_workspace_size(ok) > 0
+    for bad, status in ((lla.GroupDesc(64, 256, (256, 64), 100, 16.0), _lib.LORA_ERR_UNSUPPORTED),   # rank 200
+                        (lla.GroupDesc(64, 256, (256, 60), 16, 16.0), _lib.LORA_ERR_UNSUPPORTED),    # N % 8
+                        (lla.GroupDesc(64, 250, (256,), 16, 16.0), _lib.LORA_ERR_UNSUPPORTED),       # K % 8
+                        (lla.GroupDesc(64, 256, (256, 0), 16, 16.0), _lib.LORA_ERR_INVALID_ARG),
+                        (lla.GroupDesc(64, 256, (256,), 16, 16.0, lla.LORA_DTYPE_F32), _lib.LORA_ERR_UNSUPPORTED)):
+        with pytest.raises(lla.LoraError) as e:
+            lla.lora_group_workspace_size(bad)
+        assert e.value.status == status
+    d = lla.GroupDesc(64, 256, (256,), 16, 16.0).c()
+    d.n_members = 9
+    out = ctypes.c_size_t()
+    assert lib().lora_group_workspace_size(ctypes.byref(d), ctypes.byref(out)) == _lib.LORA_ERR_INVALID_ARG
+
+
+def test_group_calls_validate_before_any_hip_call():
+    d = lla.GroupDesc(64, 256, (256, 64), 16, 32.0).c()
+    need = lla.lora_group_workspace_size(lla.GroupDesc(64, 256, (256, 64), 16, 32.0))
+    L = lib()
+    assert L.lora_group_fwd(ctypes.byref(d), ALIGNED, ALIGNED + 0x100, ALIGNED + 0x200, ALIGNED + 0x300, None, None,
+                            ALIGNED + 0x500, need, None) == _lib.LORA_ERR_INVALID_ARG              # H NULL
+    assert L.lora_group_fwd(ctypes.byref(d), MISALIGNED, ALIGNED + 0x100, ALIGNED + 0x200, ALIGNED + 0x300,
+                            ALIGNED + 0x400, None, ALIGNED + 0x500, need, None) == _lib.LORA_ERR_MISALIGNED
+    assert L.lora_group_fwd(ctypes.byref(d), ALIGNED, ALIGNED + 0x100, ALIGNED + 0x200, ALIGNED + 0x300,
+                            ALIGNED + 0x400, None, ALIGNED + 0x500, need - 1, None) == _lib.LORA_ERR_WORKSPACE_TOO_SMALL
+    assert L.lora_group_bwd(ctypes.byref(d), ALIGNED, ALIGNED + 0x100, ALIGNED + 0x200, ALIGNED + 0x300,
+                            ALIGNED + 0x400, None, ALIGNED, ALIGNED + 0x600, ALIGNED + 0x700, ALIGNED + 0x800, need,
+                            None) == _lib.LORA_ERR_INVALID_ARG                                       # dX aliases dY
