@@ -29,12 +29,18 @@ Extra modes (used to produce the committed counter summaries):
   --traffic-from DIR    read rocprofv3 --pmc CSVs from DIR and write the
                         measured HBM traffic of both GEMMs to
                         profiles/traffic_<workload>.json
+  --grouped             run the linears that read the same input (q/k/v,
+                        gate/up) as one grouped call each (lora_group_fwd /
+                        lora_group_bwd: one pass over X for all their U, one
+                        GEMM over the stacked weights, the shared input's
+                        gradient summed over them)
 """
 from __future__ import annotations
 
 import argparse
 import ctypes
 import csv
+import dataclasses
 import glob
 import hashlib
 import json
@@ -71,6 +77,8 @@ def parse(argv=None):
     ap.add_argument("--graph", action="store_true",
                     help="time replays of a HIP graph of each step (captured once per input set)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle time for the CPU baseline")
+    ap.add_argument("--grouped", action="store_true",
+                    help="linears sharing an input run as one grouped call (q/k/v, gate/up)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--traffic-from", default=None)
     return ap.parse_args(argv)
@@ -106,17 +114,21 @@ def bwd_flops(l):
 
 def in_tile(l, split: bool, dx: bool) -> bool:
     """Whether the GEMM forms its rank-r product itself (the library's rule:
-    r <= 16, 16-bit W, whole tiles; the input gradient also needs r % 8 == 0)."""
-    return l.r <= 16 and not l.quant4 and not split and (not dx or l.r % 8 == 0)
+    a plain layer, r <= 16, 16-bit W, whole tiles; the input gradient also
+    needs r % 8 == 0)."""
+    G = getattr(l, "G", 1)
+    return G == 1 and l.r <= 16 and not l.quant4 and not split and (not dx or l.r % 8 == 0)
 
 
 def gemm_flops(l, label: str) -> int:
     """Algorithmic FLOPs of one launch of a fused GEMM: the dense product,
-    the rank-r term of the epilogue and, when formed in the tile, the rank-r
-    product U = X A^T (forward) or V = dY B (input gradient)."""
+    the rank-r term of the epilogue (a group: each output column's member
+    rank r forward, the stacked rank G r in the input gradient) and, when
+    formed in the tile, the rank-r product U = X A^T or V = dY B."""
     dx = label.startswith(GEMM_DX)
+    G = getattr(l, "G", 1)
     P, Q, C = (l.M, l.K, l.N) if dx else (l.M, l.N, l.K)
-    f = 2 * P * Q * C + 2 * P * Q * l.r
+    f = 2 * P * Q * C + 2 * P * Q * (G * l.r if dx else l.r)
     if in_tile(l, "(split)" in label, dx):
         f += 2 * P * l.r * C
     return f
@@ -128,15 +140,53 @@ def gemm_bytes(l, label: str) -> int:
     Input gradient: dY, W, A, B, dX, and U read; in the in-tile form also the
     four bf16 rank planes (V^T and U^T, hi and lo, r x M each) it writes,
     otherwise V read."""
-    M, K, N, r = l.M, l.K, l.N, l.r
+    G = getattr(l, "G", 1)
+    M, K, N, r, R = l.M, l.K, l.N, l.r, getattr(l, "G", 1) * l.r
     if not label.startswith(GEMM_DX):
-        return fwd_bytes(l)
-    b = 2 * M * N + w_bytes(l) + 2 * M * K + 2 * r * (K + N) + 4 * M * r
+        return 2 * M * K + w_bytes(l) + 2 * M * N + 2 * R * K + 2 * N * r + 4 * M * R
+    b = 2 * M * N + w_bytes(l) + 2 * M * K + 2 * R * K + 2 * N * r + 4 * M * R
     if in_tile(l, "(split)" in label, True):
         b += 4 * 2 * r * (-(-M // 128) * 128)
     else:
-        b += 4 * M * r
+        b += 4 * M * R
     return b
+
+
+@dataclasses.dataclass(frozen=True)
+class Unit:
+    """What one library call of a step covers: a single linear (G = 1), or
+    G linears that share their input, run as one group (N = their total)."""
+    name: str
+    M: int
+    K: int
+    N: int
+    r: int
+    alpha: float
+    G: int = 1
+    quant4: bool = False
+    members: tuple = ()
+
+
+def step_units(wl, grouped: bool):
+    """The workload's linears as the calls of one step: consecutive linears of
+    one shared-input set form a group when grouped is set."""
+    units, i = [], 0
+    lins = wl.linears
+    while i < len(lins):
+        l = lins[i]
+        grp = SHARED_INPUT.get(l.name.split("_")[-1])
+        j = i + 1
+        if grouped and grp:
+            while j < len(lins) and SHARED_INPUT.get(lins[j].name.split("_")[-1]) == grp:
+                j += 1
+        mem = lins[i:j]
+        if len(mem) == 1:
+            units.append(Unit(l.name, l.M, l.K, l.N, l.r, l.alpha, 1, l.quant4, (i,)))
+        else:
+            units.append(Unit("+".join(m.name for m in mem), l.M, l.K, sum(m.N for m in mem), l.r, l.alpha,
+                              len(mem), False, tuple(range(i, j))))
+        i = j
+    return units
 
 
 # ------------------------------------------------------------------ oracle baseline
@@ -266,6 +316,32 @@ def add_outputs(lla, torch, wl, layer, dev):
     return layer
 
 
+def group_layer(lla, torch, wl, layer, units, dev):
+    """The per-linear inputs of one step regrouped as units: a group's W, A, B
+    and dY stacked (copies made once, before any timing), its outputs H
+    [M][sum N], U [M][G r], dX [M][K] (the shared input's gradient, summed
+    over the members), dA [G r][K], dB [sum N][r]."""
+    out = []
+    for u in units:
+        if u.G == 1:
+            out.append(layer[u.members[0]])
+            continue
+        ds = [layer[i] for i in u.members]
+        g = {"gdesc": lla.GroupDesc(u.M, u.K, tuple(wl.linears[i].N for i in u.members), u.r, u.alpha),
+             "X": ds[0]["X"],
+             "W": torch.cat([d["W"] for d in ds]).contiguous(), "A": torch.cat([d["A"] for d in ds]).contiguous(),
+             "B": torch.cat([d["B"] for d in ds]).contiguous(),
+             "dY": torch.cat([d["dY"] for d in ds], dim=1).contiguous()}
+        R = u.G * u.r
+        g["H"] = torch.empty((u.M, u.N), dtype=torch.bfloat16, device=dev)
+        g["U"] = torch.empty((u.M, R), dtype=torch.float32, device=dev)
+        g["dX"] = torch.empty((u.M, u.K), dtype=torch.bfloat16, device=dev)
+        g["dA"] = torch.empty((R, u.K), dtype=torch.bfloat16, device=dev)
+        g["dB"] = torch.empty((u.N, u.r), dtype=torch.bfloat16, device=dev)
+        out.append(g)
+    return out
+
+
 class Stepper:
     """Runs one step of a workload through the C ABI: every linear's fused
     forward in order, then every backward in reverse order, all on torch's
@@ -274,13 +350,17 @@ class Stepper:
 
     def __init__(self, lla, torch, layers, dev):
         self.lla = lla
-        self.ws_bytes = max(lla.lora_linear_workspace_size(d["desc"]) for layer in layers for d in layer)
+        self.ws_bytes = max(lla.lora_group_workspace_size(d["gdesc"]) if "gdesc" in d
+                            else lla.lora_linear_workspace_size(d["desc"]) for layer in layers for d in layer)
         self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=dev)
         self.current = None          # index of the linear being run (for the per-kernel timing pass)
 
     def fwd(self, d):
         lla = self.lla
-        if "codes" in d:
+        if "gdesc" in d:
+            lla.lora_group_fwd(d["gdesc"], d["X"], d["W"], d["A"], d["B"], d["H"], d["U"], ws=self.ws,
+                               ws_bytes=self.ws_bytes)
+        elif "codes" in d:
             lla.lora_qlinear_fwd(d["desc"], d["X"], d["codes"], d["absmax"], d["codebook"], d["A"], d["B"],
                                  d["H"], d["U"], ws=self.ws, ws_bytes=self.ws_bytes)
         else:
@@ -289,7 +369,10 @@ class Stepper:
 
     def bwd(self, d):
         lla = self.lla
-        if "codes" in d:
+        if "gdesc" in d:
+            lla.lora_group_bwd(d["gdesc"], d["dY"], d["X"], d["W"], d["A"], d["B"], d["U"], d["dX"], d["dA"],
+                               d["dB"], ws=self.ws, ws_bytes=self.ws_bytes)
+        elif "codes" in d:
             lla.lora_qlinear_bwd(d["desc"], d["dY"], d["X"], d["codes"], d["absmax"], d["codebook"], d["A"],
                                  d["B"], d["U"], d["dX"], d["dA"], d["dB"], ws=self.ws, ws_bytes=self.ws_bytes)
         else:
@@ -409,19 +492,19 @@ def percentile(vals, q):
     return v[lo] + (v[hi] - v[lo]) * (x - lo)
 
 
-def gemm_rooflines(wl, kernel_us, traffic):
+def gemm_rooflines(units, kernel_us, traffic):
     """Roofline entries of the fused GEMMs from their measured mean durations
-    (kernel_us: {(linear index, label): [launch durations in us]})."""
+    (kernel_us: {(unit index, label): [launch durations in us]})."""
     out = []
     for (li, label), durs in sorted(kernel_us.items()):
         if not label.startswith("lora_gemm"):
             continue
-        l = wl.linears[li]
+        l = units[li]
         us = sum(durs) / len(durs)
         fl = gemm_flops(l, label)
         ach = fl / (us * 1e-6) / 1e12
         base = label.replace(" (split)", "")
-        tr = traffic.get(base) if (traffic and len(wl.linears) == 1) else None
+        tr = traffic.get(base) if (traffic and len(units) == 1) else None
         out.append({"kernel": f"{label} ({l.name})", "bound": "mfma", "achieved": round(ach, 2),
                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
                     "traffic": tr, "avg_launch_us": round(us, 2), "launches_per_step": len(durs),
@@ -461,9 +544,11 @@ def main(argv=None):
                 d.update(workloads.quantize4_torch(d.pop("W").float()))
             layer.append(d)
         sets.append(add_outputs(lla, torch, wl, share_inputs(wl, layer), dev))
+    units = step_units(wl, args.grouped)
+    if args.grouped:
+        sets = [group_layer(lla, torch, wl, layer, units, dev) for layer in sets]
     stepper = Stepper(lla, torch, sets, dev)
     torch.cuda.synchronize()
-    n_lin = len(wl.linears)
     step = lambda i: stepper.step(sets[i % len(sets)])
 
     for i in range(args.warmup):
@@ -532,11 +617,11 @@ def main(argv=None):
     tokens_s = wl.tokens / (ms_step * 1e-3)
 
     per_linear = []
-    for li, l in enumerate(wl.linears):
+    for li, u in enumerate(units):
         ks = {k: round(sum(v) / len(v), 2) for (i, k), v in kernel_us.items() if i == li}
-        per_linear.append({"name": l.name, "kernel_us": ks})
+        per_linear.append({"name": u.name, "kernel_us": ks})
 
-    gemms = gemm_rooflines(wl, kernel_us, load_traffic(wl.name))
+    gemms = gemm_rooflines(units, kernel_us, load_traffic(wl.name))
     # dominant kernel: the GEMM with the largest measured time per step
     dominant = max(gemms, key=lambda g: g["avg_launch_us"] * g["launches_per_step"] / args.steps)
     p10, p50, p90 = (percentile(step_ms, q) for q in (0.1, 0.5, 0.9))
@@ -548,7 +633,8 @@ def main(argv=None):
         "launch": "hip_graph_replay" if args.graph else "eager",
         "data": "synthetic (seeded on-device normal draws; no dataset or checkpoint)",
         "config": {"workload": wl.name, "linears": [[l.name, l.M, l.K, l.N, l.r, l.alpha] for l in wl.linears],
-                   "input_sets": args.input_sets, "description": wl.description},
+                   "input_sets": args.input_sets, "description": wl.description,
+                   "calls": [u.name for u in units]},
         "tokens_per_s": round(tokens_s, 1), "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "step_ms_p10_p50_p90": [round(p10, 4), round(p50, 4), round(p90, 4)],
         "timed_kernels_ms_per_step": round(timer_ms_step, 4),

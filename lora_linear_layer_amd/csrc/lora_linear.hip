@@ -128,18 +128,19 @@ struct RankSplit {
 
 constexpr int64_t kCUs = 256;          // compute units of an MI355X
 
-RankSplit rank_split(int64_t out_tiles, int64_t n_ct, int64_t r) {
+RankSplit rank_split(int64_t out_tiles, int64_t n_ct, int64_t part_cols) {
     // Workgroups run in rounds of two per CU (rank_stream<32> fits three, but
     // counting them made its chunks shorter and the launch slower: 4096 tokens,
     // 4096 + 4096 columns, r = 32, 17.3 -> 18.9 us), so the streaming takes about
     // rounds x (contraction tiles per chunk) x (one 32 KB Y tile per slot);
-    // each chunk adds a float32 partial of 128 r floats per output tile,
-    // written here and read again by grad_final.  The chunk count with the
-    // least bytes-equivalent cost wins, the fewest chunks on a tie.  Each chunk
-    // walks at least two contraction tiles so that the double-buffered LDS
-    // ring has something to overlap; at most 4 x 512 chunks are tried.
-    // (Rounding the chunk count up to fill 512 slots exactly left e.g. 576
-    // workgroups: a second round of 64.)
+    // each chunk adds a float32 partial of part_cols floats per 128 output
+    // columns (the problems' rank columns summed over their tiles), written
+    // here and read again by grad_final.  The chunk count with the least
+    // bytes-equivalent cost wins, the fewest chunks on a tie.  Each chunk walks
+    // at least two contraction tiles so that the double-buffered LDS ring has
+    // something to overlap; at most 4 x 512 chunks are tried.  (Rounding the
+    // chunk count up to fill 512 slots exactly left e.g. 576 workgroups: a
+    // second round of 64.)
     RankSplit best;
     int64_t best_cost = INT64_MAX;
     const int64_t slots = 2 * kCUs, nmax = std::max<int64_t>(1, std::min<int64_t>(cdiv(n_ct, 2), 4 * slots));
@@ -147,7 +148,7 @@ RankSplit rank_split(int64_t out_tiles, int64_t n_ct, int64_t r) {
     for (int64_t n = 1; n <= nmax; ++n) {
         const int64_t chunk = cdiv(n_ct, n), nc = cdiv(n_ct, chunk);
         const int64_t cost = cdiv(tiles * nc, slots) * chunk * (int64_t)(kRT * kRT * 2) * slots +
-                             nc * tiles * kRT * r * 8;
+                             nc * part_cols * kRT * 8;
         if (cost < best_cost) {
             best_cost = cost;
             best.chunk_tiles = (int)chunk;
@@ -194,8 +195,21 @@ int z_chunks(int64_t M, int64_t C) {
     const int64_t rows = cdiv(M, 128);
     return (int)std::max<int64_t>(1, std::min<int64_t>(cdiv(256, rows), cdiv(C, 256)));
 }
+// The adapter-gradient problems: dA^T over X in 64-rank-column slices of the
+// stacked rank, dB over each member's dY columns in 64-column slices of r.
+// Their output tiles (128 columns each) and rank columns set the chunking.
 RankSplit split_g(const Shape& d) {
-    return rank_split(cdiv(d.K, kRT) + cdiv(d.N, kRT), cdiv(d.M, kRT), d.rg());
+    int64_t tiles = 0, part_cols = 0;
+    for (int64_t j0 = 0; j0 < d.rg(); j0 += 64) {
+        tiles += cdiv(d.K, kRT);
+        part_cols += cdiv(d.K, kRT) * std::min<int64_t>(d.rg() - j0, 64);
+    }
+    for (int m = 0; m < d.G; ++m)
+        for (int64_t j0 = 0; j0 < d.r; j0 += 64) {
+            tiles += cdiv(d.Nm(m), kRT);
+            part_cols += cdiv(d.Nm(m), kRT) * std::min<int64_t>(d.r - j0, 64);
+        }
+    return rank_split(tiles, cdiv(d.M, kRT), part_cols);
 }
 
 // Workspace layout for one shape (offsets in bytes from ws).

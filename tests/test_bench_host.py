@@ -118,3 +118,18 @@ def test_missing_counters_are_an_error(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "traffic_path", lambda workload: str(tmp_path / "t.json"))
     with pytest.raises(SystemExit):
         bench.write_traffic(argparse.Namespace(traffic_from=str(tmp_path), workload="attn_proj_4096"))
+
+
+def test_grouped_units_and_counts():
+    """--grouped: q/k/v and gate/up become one call each; the GEMM counts of a
+    group add up to its members' (the same dense and rank-r products)."""
+    wl = workloads.workload("decoder_layer_r64")
+    units = bench.step_units(wl, True)
+    assert [u.name for u in units] == ["decoder_q+decoder_k+decoder_v", "decoder_o", "decoder_gate+decoder_up",
+                                       "decoder_down"]
+    assert [u.G for u in units] == [3, 1, 2, 1] and units[0].N == 4096 + 1024 + 1024
+    assert [u.name for u in bench.step_units(wl, False)] == [l.name for l in wl.linears]
+    for u in units:
+        mem = [wl.linears[i] for i in u.members]
+        for label in (bench.GEMM_FWD, bench.GEMM_DX):
+            assert bench.gemm_flops(u, label) == sum(bench.gemm_flops(m, label) for m in mem)

@@ -52,3 +52,45 @@ def test_decoder_layer_as_benched():
         print(f"  {sh.name}: graded errors {errs}", flush=True)
         bad = {k: e for k, e in errs.items() if not e <= BF16_TOL}
         assert not bad, f"{sh.name}: {errs} exceed {BF16_TOL}"
+
+
+def test_decoder_layer_grouped_as_benched():
+    """The same layer as bench.py --grouped runs it: q/k/v one grouped call and
+    gate/up one grouped call (stacked operands, one pass over X for all their
+    U, dX of the shared input summed over the members), o and down alone.
+    Every member's H, U, dA, dB and every call's dX against the oracle
+    (group_forward / group_backward for the groups), graded bound."""
+    import lora_linear_layer_amd as lla
+    wl = workloads.workload("decoder_layer_r64")
+    dev = torch.device("cuda:0")
+    inps = [workloads.make_linear_inputs(sh) for sh in wl.linears]
+    bench.share_inputs(wl, inps)
+    layer = [device_inputs(inp, "bf16") for inp in inps]
+    bench.share_inputs(wl, layer)
+    bench.add_outputs(lla, torch, wl, layer, dev)
+    units = bench.step_units(wl, True)
+    glayer = bench.group_layer(lla, torch, wl, layer, units, dev)
+    stepper = bench.Stepper(lla, torch, [glayer], dev)
+    print(f"grouped decoder layer: calls {[u.name for u in units]}, workspace {stepper.ws_bytes} bytes", flush=True)
+    stepper.step(glayer)
+    torch.cuda.synchronize()
+    for u, d in zip(units, glayer):
+        got = {k: to_np(d[k]) for k in OUTPUTS}
+        mem = [wl.linears[i] for i in u.members]
+        mi = [inps[i] for i in u.members]
+        s = mem[0].scale
+        X = mi[0]["X"]
+        outs = oracle.group_forward(X, [m["W"] for m in mi], [m["A"] for m in mi], [m["B"] for m in mi], s)
+        dX, dAs, dBs = oracle.group_backward([m["dY"] for m in mi], X, [m["W"] for m in mi],
+                                             [m["A"] for m in mi], [m["B"] for m in mi], s)
+        errs = {"dX": rel_err(got["dX"], dX)}
+        n0, r = 0, u.r
+        for k, (sh, (H, U), dA, dB) in enumerate(zip(mem, outs, dAs, dBs)):
+            errs[f"{sh.name} H"] = rel_err(got["H"][:, n0:n0 + sh.N], H)
+            errs[f"{sh.name} U"] = rel_err(got["U"][:, k * r:(k + 1) * r], U)
+            errs[f"{sh.name} dA"] = rel_err(got["dA"][k * r:(k + 1) * r], dA)
+            errs[f"{sh.name} dB"] = rel_err(got["dB"][n0:n0 + sh.N], dB)
+            n0 += sh.N
+        print(f"  {u.name}: graded errors {errs}", flush=True)
+        bad = {k: e for k, e in errs.items() if not e <= BF16_TOL}
+        assert not bad, f"{u.name}: {bad} exceed {BF16_TOL}"
