@@ -77,6 +77,9 @@ def parse(argv=None):
     ap.add_argument("--graph", action="store_true",
                     help="time replays of a HIP graph of each step (captured once per input set)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle time for the CPU baseline")
+    ap.add_argument("--tune", action="store_true",
+                    help="probe and cache the launch parameters of every single-linear call before timing "
+                         "(lora_tune_linear; the probing is outside the timed region)")
     ap.add_argument("--grouped", action="store_true",
                     help="linears sharing an input run as one grouped call (q/k/v, gate/up)")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -549,6 +552,16 @@ def main(argv=None):
         sets = [group_layer(lla, torch, wl, layer, units, dev) for layer in sets]
     stepper = Stepper(lla, torch, sets, dev)
     torch.cuda.synchronize()
+    tuned = {}
+    if args.tune:
+        for u, d in zip(units, sets[0]):
+            if "gdesc" in d:
+                continue                      # grouped calls keep the built-in rules
+            wargs = (dict(Wq=d["codes"], absmax=d["absmax"], codebook=d["codebook"]) if "codes" in d
+                     else dict(W=d["W"]))
+            tuned[u.name] = lla.lora_tune_linear(d["desc"], d["X"], d["A"], d["B"], d["H"], d["U"], d["dY"], d["dX"],
+                                                 d["dA"], d["dB"], ws=stepper.ws, ws_bytes=stepper.ws_bytes, **wargs)
+        torch.cuda.synchronize()
     step = lambda i: stepper.step(sets[i % len(sets)])
 
     for i in range(args.warmup):
@@ -640,6 +653,7 @@ def main(argv=None):
         "timed_kernels_ms_per_step": round(timer_ms_step, 4),
         "algorithmic_gflop_per_step": round(flops / 1e9, 3), "wall_s_timed": round(wall, 3),
         "per_linear": per_linear,
+        "tuned": tuned if args.tune else None,
         "roofline": dict(dominant),
         "gemm_rooflines": gemms,
     }

@@ -18,7 +18,7 @@
  *
  * Memory: every pointer is caller-owned device memory (except `desc`, which is
  * host memory).  The library allocates nothing, keeps no state between calls
- * (apart from the optional kernel timer below),
+ * (apart from the optional kernel timer and the tuning cache below),
  * never modifies an input, and enqueues all work on `stream` (a hipStream_t
  * passed as void*; NULL means the null stream).  Calls return once the work is
  * enqueued; device faults surface at the caller's next synchronisation.
@@ -253,6 +253,63 @@ typedef struct lora_buffer_range {
 
 lora_status lora_linear_buffer_ranges(const lora_linear_desc* desc, int32_t quant, lora_buffer_range* out,
                                       int32_t capacity, int32_t* count);
+
+/*
+ * Auto-tuning (page "UnSloth加速库集成：编译级优化带来的性能飞跃", section
+ * "技术三：自动调优引擎（Auto-tuning）": the best launch configuration differs
+ * with the GPU, the sequence length and the rank, so it is probed on the first
+ * run and cached for reuse).  The tuned parameters of the bf16 path are
+ *   fwd_split, bwd_split  contraction split of the forward / input-gradient
+ *                         GEMM: 0 the built-in rule for the weight format, 1 no
+ *                         split, 2 split outputs of under 128 tiles only, 3 also
+ *                         split the tiles of a partly filled last round;
+ *   rank_div              the adapter-gradient pass's token chunks: the
+ *                         built-in count divided by 1, 2 or 4;
+ *   z_div_fwd, z_div_bwd  the streamed U (forward) / V and U (backward) passes'
+ *                         contraction chunks, divided likewise.
+ * Every choice fits the workspace lora_linear_workspace_size gives, and every
+ * choice computes the same result up to the order of float32 additions.
+ *
+ * lora_tune_linear runs the forward and the backward of a plain layer (quant 0:
+ * W; quant 1: Wq, absmax, codebook) with every candidate, round-robin, reps
+ * rounds after one warm-up round (HIP events on `stream`; the call blocks until
+ * they finish), keeps per direction the candidate with the least median time
+ * if it beats the built-in rules by at least 2 % (else the built-in rules),
+ * and stores the choice in the process-wide cache
+ * under (device architecture, compute units, M, K, N, r, quant).  From then on
+ * lora_linear_fwd / _bwd and lora_qlinear_fwd / _bwd on such a device with
+ * such a descriptor use it (the grouped and allocation-free entry points keep
+ * the built-in rules).  It overwrites H, U, dX, dA and dB (dA, dB are
+ * overwritten even with LORA_FLAG_ACCUM_GRADS).  `chosen` (optional) receives
+ * the choice and the median times in µs of it and of the built-in rules.
+ * dtype must be LORA_DTYPE_BF16.
+ *
+ * lora_tuner_save writes the cache as text (one line per entry: arch cus M K N
+ * r quant fwd_split bwd_split rank_div z_div_fwd z_div_bwd; '#' starts a
+ * comment); lora_tuner_load merges such a file into it (LORA_ERR_INVALID_ARG
+ * names the first malformed line; nothing is merged then); lora_tuner_clear
+ * empties it; lora_tuner_lookup reports the entry for a descriptor on the
+ * named architecture and compute-unit count (arch NULL: the current device).
+ * The cache is shared by all threads; tuning and calls that use it may
+ * overlap.
+ */
+typedef struct lora_tuned_config {
+    int32_t fwd_split, bwd_split, rank_div, z_div_fwd, z_div_bwd;
+    float fwd_us, bwd_us;                   /* chosen configuration, median */
+    float default_fwd_us, default_bwd_us;   /* built-in rules, median */
+} lora_tuned_config;
+
+lora_status lora_tune_linear(const lora_linear_desc* desc, int32_t quant,
+                             const void* X, const void* W, const uint8_t* Wq, const uint16_t* absmax,
+                             const float* codebook, const void* A, const void* B,
+                             void* H, float* U, const void* dY, void* dX, void* dA, void* dB,
+                             void* ws, size_t ws_bytes, void* stream, int32_t reps,
+                             lora_tuned_config* chosen);
+lora_status lora_tuner_lookup(const char* arch, int32_t cus, const lora_linear_desc* desc, int32_t quant,
+                              lora_tuned_config* out, int32_t* found);
+lora_status lora_tuner_save(const char* path);
+lora_status lora_tuner_load(const char* path);
+void lora_tuner_clear(void);
 
 /*
  * Kernel timer (a profiling aid for callers that time the kernels inside one

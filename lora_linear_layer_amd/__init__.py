@@ -9,13 +9,15 @@ from .api import (Desc, GroupDesc, LoraError, lora_dequant4, lora_group_bwd, lor
                   lora_group_workspace_size, lora_linear_buffer_ranges, lora_linear_bwd,
                   lora_linear_bwd_noalloc,
                   lora_linear_fwd, lora_linear_workspace_size, lora_merge, lora_qlinear_bwd, lora_qlinear_fwd,
-                  lora_set_kernel_timer)
+                  lora_set_kernel_timer, lora_tune_linear, lora_tuner_clear, lora_tuner_load,
+                  lora_tuner_lookup, lora_tuner_save)
 
 __all__ = [
     "Desc", "GroupDesc", "LoraError", "lora_linear_workspace_size", "lora_linear_fwd", "lora_linear_bwd",
     "lora_group_workspace_size", "lora_group_fwd", "lora_group_bwd",
     "lora_linear_bwd_noalloc", "LORA_NOALLOC_SCRATCH_BYTES",
     "lora_qlinear_fwd", "lora_qlinear_bwd", "lora_dequant4", "lora_merge", "lora_linear_buffer_ranges",
-    "lora_set_kernel_timer", "load", "LIB_PATH",
+    "lora_set_kernel_timer", "lora_tune_linear", "lora_tuner_lookup", "lora_tuner_save", "lora_tuner_load",
+    "lora_tuner_clear", "load", "LIB_PATH",
     "LORA_DTYPE_BF16", "LORA_DTYPE_F32", "LORA_FLAG_ACCUM_GRADS",
 ]

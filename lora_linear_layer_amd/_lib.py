@@ -29,7 +29,8 @@ LORA_MAX_GROUP_RANK = 192
 EXPORTED = (
     "lora_linear_workspace_size", "lora_linear_fwd", "lora_linear_bwd", "lora_linear_bwd_noalloc",
     "lora_qlinear_fwd", "lora_qlinear_bwd", "lora_dequant4", "lora_merge",
-    "lora_linear_buffer_ranges", "lora_group_workspace_size", "lora_group_fwd", "lora_group_bwd", "lora_set_kernel_timer", "lora_status_string", "lora_last_error",
+    "lora_linear_buffer_ranges", "lora_group_workspace_size", "lora_group_fwd", "lora_group_bwd",
+    "lora_tune_linear", "lora_tuner_lookup", "lora_tuner_save", "lora_tuner_load", "lora_tuner_clear", "lora_set_kernel_timer", "lora_status_string", "lora_last_error",
 )
 
 # void (*)(void* user, const char* kernel, void* stream, void** start_event, void** stop_event)
@@ -52,6 +53,13 @@ class LoraGroupDesc(ctypes.Structure):
         ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32), ("n_members", ctypes.c_int32),
         ("N", ctypes.c_int64 * LORA_MAX_MEMBERS),
     ]
+
+
+class LoraTunedConfig(ctypes.Structure):
+    """Mirror of struct lora_tuned_config."""
+    _fields_ = [("fwd_split", ctypes.c_int32), ("bwd_split", ctypes.c_int32), ("rank_div", ctypes.c_int32),
+                ("z_div_fwd", ctypes.c_int32), ("z_div_bwd", ctypes.c_int32), ("fwd_us", ctypes.c_float),
+                ("bwd_us", ctypes.c_float), ("default_fwd_us", ctypes.c_float), ("default_bwd_us", ctypes.c_float)]
 
 
 class LoraBufferRange(ctypes.Structure):
@@ -86,6 +94,11 @@ def load() -> ctypes.CDLL:
         "lora_merge": [dp, vp, vp, vp, vp, i32, vp],
         "lora_linear_buffer_ranges": [dp, i32, ctypes.POINTER(LoraBufferRange), i32, ctypes.POINTER(i32)],
         "lora_group_workspace_size": [gp, ctypes.POINTER(sz)],
+        "lora_tune_linear": [dp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, i32,
+                             ctypes.POINTER(LoraTunedConfig)],
+        "lora_tuner_lookup": [ctypes.c_char_p, i32, dp, i32, ctypes.POINTER(LoraTunedConfig), ctypes.POINTER(i32)],
+        "lora_tuner_save": [ctypes.c_char_p],
+        "lora_tuner_load": [ctypes.c_char_p],
         "lora_group_fwd": [gp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "lora_group_bwd": [gp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
     }
@@ -95,6 +108,8 @@ def load() -> ctypes.CDLL:
         fn.restype = ctypes.c_int
     lib.lora_set_kernel_timer.argtypes = [KERNEL_TIMER, ctypes.c_void_p]
     lib.lora_set_kernel_timer.restype = None
+    lib.lora_tuner_clear.argtypes = []
+    lib.lora_tuner_clear.restype = None
     lib.lora_status_string.argtypes = [ctypes.c_int]
     lib.lora_status_string.restype = ctypes.c_char_p
     lib.lora_last_error.argtypes = []

@@ -14,7 +14,7 @@ import torch
 
 from . import _lib
 from ._lib import (LORA_DTYPE_BF16, LORA_DTYPE_F32, LORA_FLAG_ACCUM_GRADS, LORA_MAX_MEMBERS,  # noqa: F401
-                   LoraBufferRange, LoraGroupDesc, LoraLinearDesc)
+                   LoraBufferRange, LoraGroupDesc, LoraLinearDesc, LoraTunedConfig)
 
 
 class LoraError(RuntimeError):
@@ -283,6 +283,63 @@ def lora_group_bwd(desc: GroupDesc, dY, X, W, A, B, U_saved, dX, dA, dB, ws=None
     st = _lib.load().lora_group_bwd(ctypes.byref(d), _ptr(dY), _ptr(X), _ptr(W), _ptr(A), _ptr(B), _ptr(U_saved),
                                     _ptr(dX), _ptr(dA), _ptr(dB), _ptr(ws), ws_bytes, _stream(stream))
     _check(st, "lora_group_bwd")
+
+
+_TUNED_FIELDS = ("fwd_split", "bwd_split", "rank_div", "z_div_fwd", "z_div_bwd", "fwd_us", "bwd_us",
+                 "default_fwd_us", "default_bwd_us")
+
+
+def _tuned_dict(c: LoraTunedConfig) -> dict:
+    return {k: (round(getattr(c, k), 2) if k.endswith("_us") else int(getattr(c, k))) for k in _TUNED_FIELDS}
+
+
+def lora_tune_linear(desc: Desc, X, A, B, H, U, dY, dX, dA, dB, W=None, Wq=None, absmax=None, codebook=None,
+                     ws=None, ws_bytes=None, stream=None, reps: int = 5) -> dict:
+    """Probe the launch parameters of this layer shape on the current device
+    (forward and backward, each candidate timed reps times), cache the fastest
+    and return it with the median times (see include/lora_linear.h).  With W
+    the plain layer is tuned, with Wq, absmax, codebook the 4-bit one."""
+    quant = W is None
+    _check_dense(desc, X=X, A=A, B=B, H=H, U_save=U, dY=dY, dX=dX, dA=dA, dB=dB,
+                 **({"Wq": Wq, "absmax": absmax, "codebook": codebook} if quant else {"W": W}))
+    if ws is None:
+        ws, ws_bytes = _ws(desc, None, X.device)
+    elif ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    d = desc.c()
+    out = LoraTunedConfig()
+    st = _lib.load().lora_tune_linear(ctypes.byref(d), int(quant), _ptr(X), _ptr(W), _ptr(Wq), _ptr(absmax),
+                                      _ptr(codebook), _ptr(A), _ptr(B), _ptr(H), _ptr(U), _ptr(dY), _ptr(dX),
+                                      _ptr(dA), _ptr(dB), _ptr(ws), ws_bytes, _stream(stream), int(reps),
+                                      ctypes.byref(out))
+    _check(st, "lora_tune_linear")
+    return _tuned_dict(out)
+
+
+def lora_tuner_lookup(desc: Desc, quant: bool = False, arch: str | None = None, cus: int = 0):
+    """The cached choice for this descriptor (on the named architecture and
+    compute-unit count, or the current device), or None."""
+    d = desc.c()
+    out = LoraTunedConfig()
+    found = ctypes.c_int32(0)
+    st = _lib.load().lora_tuner_lookup(arch.encode() if arch else None, int(cus), ctypes.byref(d), int(quant),
+                                       ctypes.byref(out), ctypes.byref(found))
+    _check(st, "lora_tuner_lookup")
+    if not found.value:
+        return None
+    return {k: v for k, v in _tuned_dict(out).items() if not k.endswith("_us")}
+
+
+def lora_tuner_save(path: str) -> None:
+    _check(_lib.load().lora_tuner_save(str(path).encode()), "lora_tuner_save")
+
+
+def lora_tuner_load(path: str) -> None:
+    _check(_lib.load().lora_tuner_load(str(path).encode()), "lora_tuner_load")
+
+
+def lora_tuner_clear() -> None:
+    _lib.load().lora_tuner_clear()
 
 
 def lora_qlinear_fwd(desc: Desc, X, Wq, absmax, codebook, A, B, H, U_save=None, ws=None, ws_bytes=None,

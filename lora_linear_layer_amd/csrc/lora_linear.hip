@@ -7,7 +7,10 @@
 
 #include <algorithm>
 #include <atomic>
+#include <map>
 #include <mutex>
+#include <tuple>
+#include <vector>
 #include <climits>
 #include <cmath>
 #include <cstdarg>
@@ -117,6 +120,27 @@ SplitPlan gemm_split_plan(int64_t P, int64_t Q, int64_t C, bool quant) {
     sp.kc = (int)cdiv(nk, sp.split);
     sp.part_floats = (size_t)sp.split * (size_t)(T - first) * 256 * 256;
     return sp;
+}
+
+// Launch parameters the auto-tuner may change (lora_tune_linear).  Every
+// choice stays within the workspace the plan sizes: the split modes use the
+// contraction-split rules whose partial tiles it already holds, and the chunk
+// counts are the model's divided by a power of two.
+struct Tuning {
+    int fwd_split = 0;      // forward GEMM: 0 the rule for the weight format, 1 no split,
+    int bwd_split = 0;      //   2 few-tile outputs only, 3 also the last partial round (input gradient: bwd_split)
+    int rank_div = 1;       // rank_stream token chunks: the model's count / rank_div
+    int z_div_f = 1;        // rank_z_lds contraction chunks (forward U pass): the model's / z_div_f
+    int z_div_b = 1;        // (backward V and U passes)
+};
+
+SplitPlan split_for(int mode, int64_t P, int64_t Q, int64_t C, bool quant) {
+    switch (mode) {
+        case 1: return SplitPlan{};
+        case 2: return gemm_split_plan(P, Q, C, false);
+        case 3: return gemm_split_plan(P, Q, C, true);
+        default: return gemm_split_plan(P, Q, C, quant);
+    }
 }
 
 // Chunking of a streamed rank-r product (rank_stream): out_tiles 128-wide
@@ -444,8 +468,8 @@ void launch_rank_z_t(const RankZArgs& a, dim3 grid, hipStream_t st) {
 }
 
 void launch_rank_z(int64_t M, const uint16_t* Y, int64_t ldy, int64_t C, const uint16_t* F, int64_t f_rows,
-                   float* Z, int64_t z_ld, int64_t z_j0, float* zpart, hipStream_t st) {
-    const int n_chunk = z_chunks(M, C);
+                   float* Z, int64_t z_ld, int64_t z_j0, float* zpart, hipStream_t st, int z_div = 1) {
+    const int n_chunk = std::max(1, z_chunks(M, C) / std::max(z_div, 1));
     for (int64_t j0 = 0; j0 < f_rows; j0 += kMaxZCols) {
         const int rl = (int)std::min<int64_t>(f_rows - j0, kMaxZCols);
         const int jb = (int)cdiv(rl, 16);
@@ -502,8 +526,15 @@ uint16_t* zt_plane(const Plan& plan, char* wsb, int64_t rows, int i) {
 // otherwise zt_hilo writes them.  Problems of one rank width share a launch.
 lora_status launch_adapter_grads(const Shape& d, const Plan& plan, char* wsb, const uint16_t* X, const float* V,
                                  const uint16_t* dY, const float* U, void* dA, void* dB, bool planes_ready,
-                                 hipStream_t st) {
+                                 hipStream_t st, int rank_div = 1) {
     const int64_t rg = d.rg();
+    // token chunks: the model's count, or fewer (tuned); the partials fit either way
+    RankSplit g = plan.g;
+    if (rank_div > 1) {
+        const int64_t n_ct = cdiv(d.M, kRT);
+        g.chunk_tiles = (int)cdiv(n_ct, std::max<int64_t>(1, plan.g.n_chunk / rank_div));
+        g.n_chunk = (int)cdiv(n_ct, g.chunk_tiles);
+    }
     float* const ga = reinterpret_cast<float*>(wsb + plan.off_ga);
     float* const gb = reinterpret_cast<float*>(wsb + plan.off_gb);
     uint16_t* const vt_hi = zt_plane(plan, wsb, rg, 0);
@@ -544,8 +575,8 @@ lora_status launch_adapter_grads(const Shape& d, const Plan& plan, char* wsb, co
                 tiles = std::max(tiles, a.prob[i].n_tiles);
             }
             a.M = (int)d.M;
-            a.chunk_tiles = plan.g.chunk_tiles;
-            a.n_chunk = plan.g.n_chunk;
+            a.chunk_tiles = g.chunk_tiles;
+            a.n_chunk = g.n_chunk;
             const dim3 grid((unsigned)tiles, (unsigned)a.n_chunk, (unsigned)a.n_prob);
             switch (sl) {
                 case 0: LAUNCH("rank_stream", (rank_stream<16>), grid, dim3(256), 0, st, a); break;
@@ -564,7 +595,7 @@ lora_status launch_adapter_grads(const Shape& d, const Plan& plan, char* wsb, co
     f.N = (int)d.N;
     f.ra = (int)rg;
     f.rb = (int)d.r;
-    f.n_chunk = plan.g.n_chunk;
+    f.n_chunk = g.n_chunk;
     f.s = d.alpha / (float)d.r;
     f.f32_out = 0;
     f.accumulate = (d.flags & LORA_FLAG_ACCUM_GRADS) ? 1 : 0;
@@ -582,20 +613,20 @@ void set_members(GemmArgs& g, const Shape& d) {
 // ---------------------------------------------------------------- forward
 lora_status fwd_bf16(const Shape& d, bool quant, const void* X, const void* W, const uint8_t* Wq,
                      const uint16_t* absmax, const float* codebook, const void* A, const void* B, void* H,
-                     float* U_save, void* ws, hipStream_t st) {
+                     float* U_save, void* ws, hipStream_t st, const Tuning& tn = Tuning{}) {
     const Plan plan = make_plan(d);
     char* const wsb = static_cast<char*>(ws);
     const int r = (int)d.r;
     const uint16_t* const X16 = static_cast<const uint16_t*>(X);
     const uint16_t* const A16 = static_cast<const uint16_t*>(A);
     float* const zpart = reinterpret_cast<float*>(wsb + plan.off_zp);
-    const SplitPlan sp = gemm_split_plan(d.M, d.N, d.K, quant);
+    const SplitPlan sp = split_for(tn.fwd_split, d.M, d.N, d.K, quant);
     const bool in_tile = d.G == 1 && gemm_in_tile(quant, r, sp);
     float* U = U_save;
     if (!in_tile) {
         // U = X A^T (all members in one pass over X), read by the GEMM epilogue
         if (!U) U = reinterpret_cast<float*>(wsb + plan.off_u);
-        launch_rank_z(d.M, X16, d.K, d.K, A16, d.rg(), U, d.rg(), 0, zpart, st);
+        launch_rank_z(d.M, X16, d.K, d.K, A16, d.rg(), U, d.rg(), 0, zpart, st, tn.z_div_f);
         LAUNCH_CHECK("rank_z_lds(U)");
     }
     GemmArgs g{};
@@ -628,7 +659,8 @@ lora_status fwd_bf16(const Shape& d, bool quant, const void* X, const void* W, c
 // over all their output columns at once: dX = sum_m (dY_m W_m + s V_m A_m).
 lora_status bwd_bf16(const Shape& d, bool quant, const void* dY, const void* X, const void* W,
                      const uint8_t* Wq, const uint16_t* absmax, const float* codebook, const void* A,
-                     const void* B, const float* U_saved, void* dX, void* dA, void* dB, void* ws, hipStream_t st) {
+                     const void* B, const float* U_saved, void* dX, void* dA, void* dB, void* ws, hipStream_t st,
+                     const Tuning& tn = Tuning{}) {
     const Plan plan = make_plan(d);
     const int r = (int)d.r;
     const int64_t rg = d.rg();
@@ -644,13 +676,13 @@ lora_status bwd_bf16(const Shape& d, bool quant, const void* dY, const void* X, 
     const float* U = U_saved;
     if (!U) {
         float* Uw = reinterpret_cast<float*>(wsb + plan.off_u);
-        launch_rank_z(d.M, X16, d.K, d.K, A16, rg, Uw, rg, 0, zpart, st);
+        launch_rank_z(d.M, X16, d.K, d.K, A16, rg, Uw, rg, 0, zpart, st, tn.z_div_b);
         LAUNCH_CHECK("rank_z_lds(U)");
         U = Uw;
     }
     // 2. V = dY B: inside the dX GEMM when it runs in the in-tile form,
     //    else the streamed pass of each member over its columns of dY
-    const SplitPlan sp = gemm_split_plan(d.M, d.K, d.N, quant);
+    const SplitPlan sp = split_for(tn.bwd_split, d.M, d.K, d.N, quant);
     const bool v_in_tile = dX != nullptr && d.G == 1 && dx_in_tile(quant, r, sp);
     if (!v_in_tile) {
         uint16_t* const BT = reinterpret_cast<uint16_t*>(wsb + plan.off_bt);
@@ -658,7 +690,8 @@ lora_status bwd_bf16(const Shape& d, bool quant, const void* dY, const void* X, 
             uint16_t* const BTm = BT + (size_t)d.r * d.n0[m];
             LAUNCH("transpose_rank", transpose_rank, dim3((unsigned)cdiv(d.r * d.Nm(m), 256)), dim3(256), 0, st,
                    B16 + (size_t)d.n0[m] * d.r, BTm, (int)d.Nm(m), r);
-            launch_rank_z(d.M, dY16 + d.n0[m], d.N, d.Nm(m), BTm, d.r, V, rg, (int64_t)m * d.r, zpart, st);
+            launch_rank_z(d.M, dY16 + d.n0[m], d.N, d.Nm(m), BTm, d.r, V, rg, (int64_t)m * d.r, zpart, st,
+                          tn.z_div_b);
         }
         LAUNCH_CHECK("rank_z_lds(V)");
     }
@@ -692,7 +725,7 @@ lora_status bwd_bf16(const Shape& d, bool quant, const void* dY, const void* X, 
         LAUNCH_CHECK(quant ? "lora_gemm(4-bit dX)" : "lora_gemm(dX)");
     }
     // 4., 5. dA = s V^T X, dB = s dY^T U
-    const lora_status gst = launch_adapter_grads(d, plan, wsb, X16, V, dY16, U, dA, dB, v_in_tile, st);
+    const lora_status gst = launch_adapter_grads(d, plan, wsb, X16, V, dY16, U, dA, dB, v_in_tile, st, tn.rank_div);
     if (gst != LORA_OK) return gst;
     return ok();
 }
@@ -822,6 +855,73 @@ size_t bwd_scratch_bytes(const Shape& d) {
     const Plan p = make_plan(d);
     if (d.dtype != LORA_DTYPE_BF16) return p.total;
     return p.off_split + align_up(gemm_split_plan(d.M, d.K, d.N, false).part_floats * sizeof(float));
+}
+
+// ---------------------------------------------------------------- auto-tuner
+// Tuned launch parameters per (device, shape): chosen by lora_tune_linear from
+// timed runs, kept for the process, saved to and loaded from a text file.
+struct TuneKey {
+    std::string arch;
+    int cus;
+    int64_t M, K, N, r;
+    int quant;
+    bool operator<(const TuneKey& o) const {
+        return std::tie(arch, cus, M, K, N, r, quant) < std::tie(o.arch, o.cus, o.M, o.K, o.N, o.r, o.quant);
+    }
+};
+
+std::mutex g_tune_mu;
+std::map<TuneKey, Tuning> g_tuned;
+std::atomic<bool> g_tune_any{false};
+
+struct DevInfo {
+    std::string arch;
+    int cus = 0;
+    bool ok = false;
+};
+DevInfo g_devinfo[kMaxDevices];
+std::mutex g_dev_mu;
+
+// Architecture name (without feature suffixes) and compute-unit count of the
+// current device, looked up once per device.
+bool current_device_info(std::string& arch, int& cus) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return false;
+    std::lock_guard<std::mutex> lock(g_dev_mu);
+    DevInfo& di = g_devinfo[dev];
+    if (!di.ok) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return false;
+        std::string a = prop.gcnArchName;
+        di.arch = a.substr(0, a.find(':'));
+        di.cus = prop.multiProcessorCount;
+        di.ok = true;
+    }
+    arch = di.arch;
+    cus = di.cus;
+    return true;
+}
+
+TuneKey tune_key(const std::string& arch, int cus, const lora_linear_desc& d, bool quant) {
+    return TuneKey{arch, cus, d.M, d.K, d.N, d.r, quant ? 1 : 0};
+}
+
+// The tuned parameters for a plain bf16 layer on the current device, or the
+// built-in rules when the cache holds none (no lookup at all while it is empty).
+Tuning tuned_for(const lora_linear_desc& d, bool quant) {
+    if (!g_tune_any.load(std::memory_order_acquire) || d.dtype != LORA_DTYPE_BF16) return Tuning{};
+    std::string arch;
+    int cus = 0;
+    if (!current_device_info(arch, cus)) return Tuning{};
+    std::lock_guard<std::mutex> lock(g_tune_mu);
+    const auto it = g_tuned.find(tune_key(arch, cus, d, quant));
+    return it == g_tuned.end() ? Tuning{} : it->second;
+}
+
+bool valid_tuning(const Tuning& t) {
+    auto pow2 = [](int v) { return v == 1 || v == 2 || v == 4 || v == 8; };
+    return t.fwd_split >= 0 && t.fwd_split <= 3 && t.bwd_split >= 0 && t.bwd_split <= 3 && pow2(t.rank_div) &&
+           pow2(t.z_div_f) && pow2(t.z_div_b);
 }
 
 // ---------------------------------------------------------------- buffer ranges
@@ -1014,7 +1114,8 @@ lora_status lora_linear_fwd(const lora_linear_desc* desc, const void* X, const v
     if (st != LORA_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (desc->dtype == LORA_DTYPE_F32) return fwd_f32(*desc, false, X, W, nullptr, nullptr, nullptr, A, B, H, U_save, ws, s);
-    return fwd_bf16(shape_of(*desc), false, X, W, nullptr, nullptr, nullptr, A, B, H, U_save, ws, s);
+    return fwd_bf16(shape_of(*desc), false, X, W, nullptr, nullptr, nullptr, A, B, H, U_save, ws, s,
+                    tuned_for(*desc, false));
 }
 
 lora_status lora_linear_bwd(const lora_linear_desc* desc, const void* dY, const void* X, const void* W,
@@ -1034,7 +1135,8 @@ lora_status lora_linear_bwd(const lora_linear_desc* desc, const void* dY, const 
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (desc->dtype == LORA_DTYPE_F32)
         return bwd_f32(*desc, false, dY, X, W, nullptr, nullptr, nullptr, A, B, U_saved, dX, dA, dB, ws, s);
-    return bwd_bf16(shape_of(*desc), false, dY, X, W, nullptr, nullptr, nullptr, A, B, U_saved, dX, dA, dB, ws, s);
+    return bwd_bf16(shape_of(*desc), false, dY, X, W, nullptr, nullptr, nullptr, A, B, U_saved, dX, dA, dB, ws, s,
+                    tuned_for(*desc, false));
 }
 
 lora_status lora_qlinear_fwd(const lora_linear_desc* desc, const void* X, const uint8_t* Wq, const uint16_t* absmax,
@@ -1053,7 +1155,8 @@ lora_status lora_qlinear_fwd(const lora_linear_desc* desc, const void* X, const 
     if (st != LORA_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (desc->dtype == LORA_DTYPE_F32) return fwd_f32(*desc, true, X, nullptr, Wq, absmax, codebook, A, B, H, U_save, ws, s);
-    return fwd_bf16(shape_of(*desc), true, X, nullptr, Wq, absmax, codebook, A, B, H, U_save, ws, s);
+    return fwd_bf16(shape_of(*desc), true, X, nullptr, Wq, absmax, codebook, A, B, H, U_save, ws, s,
+                    tuned_for(*desc, true));
 }
 
 lora_status lora_qlinear_bwd(const lora_linear_desc* desc, const void* dY, const void* X, const uint8_t* Wq,
@@ -1075,7 +1178,226 @@ lora_status lora_qlinear_bwd(const lora_linear_desc* desc, const void* dY, const
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (desc->dtype == LORA_DTYPE_F32)
         return bwd_f32(*desc, true, dY, X, nullptr, Wq, absmax, codebook, A, B, U_saved, dX, dA, dB, ws, s);
-    return bwd_bf16(shape_of(*desc), true, dY, X, nullptr, Wq, absmax, codebook, A, B, U_saved, dX, dA, dB, ws, s);
+    return bwd_bf16(shape_of(*desc), true, dY, X, nullptr, Wq, absmax, codebook, A, B, U_saved, dX, dA, dB, ws, s,
+                    tuned_for(*desc, true));
+}
+
+lora_status lora_tune_linear(const lora_linear_desc* desc, int32_t quant, const void* X, const void* W,
+                             const uint8_t* Wq, const uint16_t* absmax, const float* codebook, const void* A,
+                             const void* B, void* H, float* U, const void* dY, void* dX, void* dA, void* dB, void* ws,
+                             size_t ws_bytes, void* stream, int32_t reps, lora_tuned_config* chosen) {
+    const bool q = quant != 0;
+    lora_status st = check_desc(desc, q);
+    if (st != LORA_OK) return st;
+    if (desc->dtype != LORA_DTYPE_BF16) return fail(LORA_ERR_UNSUPPORTED, "only the bf16 path has launch parameters");
+    if (reps < 1 || reps > 100) return fail(LORA_ERR_INVALID_ARG, "reps = %d (1 .. 100)", (int)reps);
+    st = check_ptrs({{X, "X"}, {A, "A"}, {B, "B"}, {H, "H"}, {U, "U"}, {dY, "dY"}, {dX, "dX"}, {dA, "dA"}, {dB, "dB"}},
+                    {{W, "W"}, {Wq, "Wq"}, {absmax, "absmax"}, {codebook, "codebook"}});
+    if (st != LORA_OK) return st;
+    if (q ? (!Wq || !absmax || !codebook) : !W)
+        return fail(LORA_ERR_INVALID_ARG, q ? "Wq, absmax and codebook are needed" : "W is NULL");
+    st = check_no_alias({{H, "H"}, {U, "U"}, {dX, "dX"}, {dA, "dA"}, {dB, "dB"}},
+                        {{X, "X"}, {W, "W"}, {Wq, "Wq"}, {absmax, "absmax"}, {codebook, "codebook"}, {A, "A"},
+                         {B, "B"}, {H, "H"}, {U, "U"}, {dY, "dY"}, {dX, "dX"}, {dA, "dA"}, {dB, "dB"}, {ws, "ws"}});
+    if (st != LORA_OK) return st;
+    st = check_ws(*desc, ws, ws_bytes);
+    if (st != LORA_OK) return st;
+    std::string arch;
+    int cus = 0;
+    if (!current_device_info(arch, cus)) return fail(LORA_ERR_HIP, "no current HIP device");
+    Shape d = shape_of(*desc);
+    d.flags &= ~LORA_FLAG_ACCUM_GRADS;          // repeated runs must not accumulate
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+        if (e0) hipEventDestroy(e0);
+        return fail(LORA_ERR_HIP, "hipEventCreate failed");
+    }
+    lora_status err = LORA_OK;
+    auto fwd = [&](const Tuning& tn) {
+        return fwd_bf16(d, q, X, W, Wq, absmax, codebook, A, B, H, U, ws, s, tn);
+    };
+    auto bwd = [&](const Tuning& tn) {
+        return bwd_bf16(d, q, dY, X, W, Wq, absmax, codebook, A, B, U, dX, dA, dB, ws, s, tn);
+    };
+    // Median times (us) of the candidates, measured round-robin (one run of each
+    // per round, after a warm-up round) so that the clock's drift under load
+    // affects all of them alike; candidate 0 is the built-in rules.
+    auto medians = [&](const std::vector<Tuning>& cand, auto&& run) {
+        std::vector<std::vector<float>> t(cand.size());
+        for (int round = 0; round <= reps && err == LORA_OK; ++round) {
+            for (size_t i = 0; i < cand.size() && err == LORA_OK; ++i) {
+                hipEventRecord(e0, s);
+                err = run(cand[i]);
+                hipEventRecord(e1, s);
+                if (err != LORA_OK) break;
+                if (hipEventSynchronize(e1) != hipSuccess) {
+                    err = fail(LORA_ERR_HIP, "hipEventSynchronize failed");
+                    break;
+                }
+                float ms = 0.f;
+                hipEventElapsedTime(&ms, e0, e1);
+                if (round > 0) t[i].push_back(ms * 1e3f);
+            }
+        }
+        std::vector<float> med(cand.size(), 0.f);
+        for (size_t i = 0; i < cand.size(); ++i) {
+            if (t[i].empty()) continue;
+            std::sort(t[i].begin(), t[i].end());
+            med[i] = t[i][t[i].size() / 2];
+        }
+        return med;
+    };
+    // the candidate with the least median, unless it beats the built-in rules by less than 2 %
+    auto pick = [](const std::vector<float>& med) {
+        size_t b = 0;
+        for (size_t i = 1; i < med.size(); ++i)
+            if (med[i] < med[b]) b = i;
+        return med[b] < 0.98f * med[0] ? b : 0;
+    };
+    auto same_split = [](const SplitPlan& a, const SplitPlan& b) {
+        return a.first == b.first && a.split == b.split && a.kc == b.kc;
+    };
+    // distinct split modes of a GEMM (modes giving the same plan are one candidate)
+    auto split_modes = [&](int64_t P, int64_t Qd, int64_t C) {
+        std::vector<int> modes{0};
+        std::vector<SplitPlan> seen{split_for(0, P, Qd, C, q)};
+        for (int mode = 1; mode <= 3; ++mode) {
+            const SplitPlan sp = split_for(mode, P, Qd, C, q);
+            if (std::none_of(seen.begin(), seen.end(), [&](const SplitPlan& o) { return same_split(o, sp); })) {
+                seen.push_back(sp);
+                modes.push_back(mode);
+            }
+        }
+        return modes;
+    };
+    // distinct divisors of a chunk count (1 first)
+    auto divisors = [](int n) {
+        std::vector<int> out{1};
+        for (int div = 2; div <= 4; div *= 2)
+            if (n / div >= 1 && n / div != n / (div / 2)) out.push_back(div);
+        return out;
+    };
+    // forward: contraction split x the U pass's chunks (when U is streamed)
+    std::vector<Tuning> fc;
+    for (int mode : split_modes(d.M, d.N, d.K)) {
+        const bool u_streamed = !gemm_in_tile(q, (int)d.r, split_for(mode, d.M, d.N, d.K, q));
+        for (int zd : u_streamed ? divisors(z_chunks(d.M, d.K)) : std::vector<int>{1}) {
+            Tuning c;
+            c.fwd_split = mode;
+            c.z_div_f = zd;
+            fc.push_back(c);
+        }
+    }
+    const std::vector<float> mf = medians(fc, fwd);
+    const size_t bf = err == LORA_OK ? pick(mf) : 0;
+    Tuning best = fc[bf];
+    // backward: contraction split x adapter-gradient chunks x the V pass's chunks (when V is streamed)
+    std::vector<Tuning> bc;
+    for (int mode : split_modes(d.M, d.K, d.N)) {
+        const bool v_streamed = !dx_in_tile(q, (int)d.r, split_for(mode, d.M, d.K, d.N, q));
+        for (int rd : divisors(split_g(d).n_chunk))
+            for (int zd : v_streamed ? divisors(z_chunks(d.M, d.N)) : std::vector<int>{1}) {
+                Tuning c = best;
+                c.bwd_split = mode;
+                c.rank_div = rd;
+                c.z_div_b = zd;
+                bc.push_back(c);
+            }
+    }
+    const std::vector<float> mb = err == LORA_OK ? medians(bc, bwd) : std::vector<float>(bc.size(), 0.f);
+    const size_t bb = err == LORA_OK ? pick(mb) : 0;
+    best = bc[bb];
+    const float t_fwd = mf[bf], t_fwd_default = mf[0], t_bwd = mb[bb], t_bwd_default = mb[0];
+    hipEventDestroy(e0);
+    hipEventDestroy(e1);
+    if (err != LORA_OK) return err;
+    {
+        std::lock_guard<std::mutex> lock(g_tune_mu);
+        g_tuned[tune_key(arch, cus, *desc, q)] = best;
+        g_tune_any.store(true, std::memory_order_release);
+    }
+    if (chosen) {
+        *chosen = lora_tuned_config{best.fwd_split, best.bwd_split, best.rank_div, best.z_div_f, best.z_div_b,
+                                    t_fwd, t_bwd, t_fwd_default, t_bwd_default};
+    }
+    return ok();
+}
+
+lora_status lora_tuner_lookup(const char* arch, int32_t cus, const lora_linear_desc* desc, int32_t quant,
+                              lora_tuned_config* out, int32_t* found) {
+    if (!desc || !out || !found) return fail(LORA_ERR_INVALID_ARG, "desc, out and found must not be NULL");
+    std::string a;
+    int c = cus;
+    if (arch) {
+        a = arch;
+    } else if (!current_device_info(a, c)) {
+        return fail(LORA_ERR_HIP, "no current HIP device");
+    }
+    std::lock_guard<std::mutex> lock(g_tune_mu);
+    const auto it = g_tuned.find(tune_key(a, c, *desc, quant != 0));
+    *found = it != g_tuned.end();
+    const Tuning t = *found ? it->second : Tuning{};
+    *out = lora_tuned_config{t.fwd_split, t.bwd_split, t.rank_div, t.z_div_f, t.z_div_b, 0.f, 0.f, 0.f, 0.f};
+    return ok();
+}
+
+lora_status lora_tuner_save(const char* path) {
+    if (!path) return fail(LORA_ERR_INVALID_ARG, "path is NULL");
+    FILE* f = std::fopen(path, "w");
+    if (!f) return fail(LORA_ERR_INVALID_ARG, "cannot write %s", path);
+    std::fprintf(f, "# lora tuning cache v1: arch cus M K N r quant fwd_split bwd_split rank_div z_div_fwd z_div_bwd\n");
+    {
+        std::lock_guard<std::mutex> lock(g_tune_mu);
+        for (const auto& kv : g_tuned) {
+            const TuneKey& k = kv.first;
+            const Tuning& t = kv.second;
+            std::fprintf(f, "%s %d %lld %lld %lld %lld %d %d %d %d %d %d\n", k.arch.c_str(), k.cus, (long long)k.M,
+                         (long long)k.K, (long long)k.N, (long long)k.r, k.quant, t.fwd_split, t.bwd_split, t.rank_div,
+                         t.z_div_f, t.z_div_b);
+        }
+    }
+    const bool bad = std::ferror(f) != 0;
+    std::fclose(f);
+    return bad ? fail(LORA_ERR_INVALID_ARG, "write error on %s", path) : ok();
+}
+
+lora_status lora_tuner_load(const char* path) {
+    if (!path) return fail(LORA_ERR_INVALID_ARG, "path is NULL");
+    FILE* f = std::fopen(path, "r");
+    if (!f) return fail(LORA_ERR_INVALID_ARG, "cannot read %s", path);
+    std::map<TuneKey, Tuning> read;
+    char line[512];
+    int lineno = 0;
+    while (std::fgets(line, sizeof line, f)) {
+        ++lineno;
+        const char* p = line;
+        while (*p == ' ' || *p == '\t') ++p;
+        if (*p == '#' || *p == '\n' || *p == '\0') continue;
+        char arch[64];
+        int cus = 0, quant = 0;
+        long long M = 0, K = 0, N = 0, r = 0;
+        Tuning t;
+        const int n = std::sscanf(p, "%63s %d %lld %lld %lld %lld %d %d %d %d %d %d", arch, &cus, &M, &K, &N, &r, &quant,
+                                  &t.fwd_split, &t.bwd_split, &t.rank_div, &t.z_div_f, &t.z_div_b);
+        if (n != 12 || cus <= 0 || M <= 0 || K <= 0 || N <= 0 || r <= 0 || (quant != 0 && quant != 1) ||
+            !valid_tuning(t)) {
+            std::fclose(f);
+            return fail(LORA_ERR_INVALID_ARG, "%s:%d: not a tuning entry", path, lineno);
+        }
+        read[TuneKey{arch, cus, M, K, N, r, quant}] = t;
+    }
+    std::fclose(f);
+    std::lock_guard<std::mutex> lock(g_tune_mu);
+    for (const auto& kv : read) g_tuned[kv.first] = kv.second;
+    g_tune_any.store(!g_tuned.empty(), std::memory_order_release);
+    return ok();
+}
+
+void lora_tuner_clear(void) {
+    std::lock_guard<std::mutex> lock(g_tune_mu);
+    g_tuned.clear();
+    g_tune_any.store(false, std::memory_order_release);
 }
 
 lora_status lora_merge(const lora_linear_desc* desc, const void* W, const void* A, const void* B, void* W_out,

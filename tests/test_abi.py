@@ -290,3 +290,45 @@ def test_group_calls_validate_before_any_hip_call():
     assert L.lora_group_bwd(ctypes.byref(d), ALIGNED, ALIGNED + 0x100, ALIGNED + 0x200, ALIGNED + 0x300,
                             ALIGNED + 0x400, None, ALIGNED, ALIGNED + 0x600, ALIGNED + 0x700, ALIGNED + 0x800, need,
                             None) == _lib.LORA_ERR_INVALID_ARG                                       # dX aliases dY
+
+
+# ------------------------------------------------------------ tuning cache (host only)
+def test_tuner_cache_file_round_trip(tmp_path):
+    """Entries loaded from a cache file are found for their (architecture,
+    compute units, shape, weight format) and nowhere else; saving writes them
+    back; clearing empties the cache."""
+    lla.lora_tuner_clear()
+    f = tmp_path / "tune.txt"
+    f.write_text("# comment line\n"
+                 "gfx950 256 4096 4096 4096 8 0 0 3 2 1 1\n"
+                 "gfx950 256 2048 8192 28672 16 1 1 2 4 2 2\n")
+    lla.lora_tuner_load(f)
+    d = lla.Desc(4096, 4096, 4096, 8, 32.0)
+    assert lla.lora_tuner_lookup(d, False, "gfx950", 256) == {"fwd_split": 0, "bwd_split": 3, "rank_div": 2,
+                                                              "z_div_fwd": 1, "z_div_bwd": 1}
+    assert lla.lora_tuner_lookup(d, True, "gfx950", 256) is None            # the 4-bit layer is another entry
+    assert lla.lora_tuner_lookup(d, False, "gfx950", 304) is None            # another compute-unit count
+    assert lla.lora_tuner_lookup(lla.Desc(2048, 8192, 28672, 16, 32.0), True, "gfx950", 256)["rank_div"] == 4
+    out = tmp_path / "saved.txt"
+    lla.lora_tuner_save(out)
+    lines = [l for l in out.read_text().splitlines() if not l.startswith("#")]
+    assert sorted(lines) == sorted(["gfx950 256 4096 4096 4096 8 0 0 3 2 1 1",
+                                    "gfx950 256 2048 8192 28672 16 1 1 2 4 2 2"])
+    lla.lora_tuner_clear()
+    assert lla.lora_tuner_lookup(d, False, "gfx950", 256) is None
+
+
+def test_tuner_load_rejects_malformed_files(tmp_path):
+    lla.lora_tuner_clear()
+    for bad in ("gfx950 256 4096 4096 4096 8 0 0 3 2 1\n",          # a field missing
+                "gfx950 256 4096 4096 4096 8 0 5 0 1 1 1\n",         # split mode 5
+                "gfx950 256 4096 4096 4096 8 0 0 0 3 1 1\n",         # divisor 3
+                "gfx950 0 4096 4096 4096 8 0 0 0 1 1 1\n"):          # no compute units
+        f = tmp_path / "bad.txt"
+        f.write_text("gfx950 256 64 256 256 8 0 0 0 1 1 1\n" + bad)
+        with pytest.raises(lla.LoraError, match="bad.txt:2"):
+            lla.lora_tuner_load(f)
+        # nothing of a rejected file is merged
+        assert lla.lora_tuner_lookup(lla.Desc(64, 256, 256, 8, 32.0), False, "gfx950", 256) is None
+    with pytest.raises(lla.LoraError):
+        lla.lora_tuner_load(tmp_path / "missing.txt")
