@@ -41,7 +41,8 @@ import numpy as np
 
 __all__ = [
     "lora_scale", "forward", "backward", "backward_dx", "backward_lora",
-    "merged_weight", "group_forward", "group_backward", "bf16_round", "f16_to_f64", "codebook4", "dequant4",
+    "merged_weight", "group_forward", "group_backward", "rms_norm", "norm_forward", "norm_backward",
+    "bf16_round", "f16_to_f64", "codebook4", "dequant4",
 ]
 
 
@@ -127,6 +128,46 @@ def group_backward(dYs, X, Ws, As, Bs, s):
         dAs.append(dAi)
         dBs.append(dBi)
     return dX, dAs, dBs
+
+
+# ----------------------------------------------------------------------------
+# RMSNorm in front of the layer
+# ----------------------------------------------------------------------------
+
+def rms_norm(X, g, eps):
+    """RMSNorm over the last axis ([P2] section "关键融合策略解析", RMSNorm +
+    Linear: the norm that feeds the attention projections):
+    Xn[m, k] = X[m, k] / sqrt(mean_k X[m, k]^2 + eps) * g[k].  Returns (Xn, inv)
+    with inv[m] = 1 / sqrt(mean_k X[m, k]^2 + eps)."""
+    X, g = _f64(X), _f64(g)
+    inv = 1.0 / np.sqrt(np.mean(X * X, axis=1) + float(eps))
+    return X * inv[:, None] * g[None, :], inv
+
+
+def norm_forward(X, g, eps, W, A, B, s):
+    """The LoRA linear applied to RMSNorm(X): H = Xn W^T + s (Xn A^T) B^T.
+    Returns (H, U, inv) with U = Xn A^T."""
+    Xn, inv = rms_norm(X, g, eps)
+    H, U = forward(Xn, W, A, B, s)
+    return H, U, inv
+
+
+def norm_backward(dY, X, g, eps, W, A, B, s):
+    """Vector-Jacobian products of L = <dY, H> for norm_forward, with respect to
+    the raw input X and the adapter (the norm's g is part of the frozen
+    backbone, like W: no gradient).  The layer gives dXn = dY W + s (dY B) A and
+    dA = s (dY B)^T Xn, dB = s dY^T (Xn A^T); the norm's Jacobian, for one row
+    with inv = 1 / sqrt(mean(x^2) + eps), is
+        dx = inv * g * dxn - x * inv^3 / K * sum_k g[k] dxn[k] x[k].
+    Returns (dX, dA, dB)."""
+    X, g = _f64(X), _f64(g)
+    Xn, inv = rms_norm(X, g, eps)
+    dXn = backward_dx(dY, W, A, B, s)
+    dA, dB = backward_lora(dY, Xn, A, B, s)
+    K = X.shape[1]
+    dot = np.sum(g[None, :] * dXn * X, axis=1)
+    dX = inv[:, None] * g[None, :] * dXn - X * (inv ** 3 / K * dot)[:, None]
+    return dX, dA, dB
 
 
 # ----------------------------------------------------------------------------

@@ -403,3 +403,72 @@ def test_group_of_one_is_the_layer():
     np.testing.assert_array_equal(dX, dX1)
     np.testing.assert_array_equal(dA, dA1)
     np.testing.assert_array_equal(dB, dB1)
+
+
+# ---------------------------------------------------------------- RMSNorm in front of the layer
+def norm_case(seed, M=4, K=6, N=5, r=2):
+    X, W, A, B, dY, s = rand_case(seed, M, K, N, r)
+    rng = np.random.default_rng(seed + 100)
+    g = rng.uniform(0.5, 1.5, size=K)
+    return X, g, 1e-3, W, A, B, dY, s
+
+
+def test_rms_norm_brute_force():
+    X, g, eps, *_ = norm_case(21)
+    Xn, inv = oracle.rms_norm(X, g, eps)
+    for m in range(X.shape[0]):
+        ms = sum(float(v) * float(v) for v in X[m]) / X.shape[1]
+        i = 1.0 / math.sqrt(ms + eps)
+        assert abs(inv[m] - i) <= 1e-15 * i
+        for k in range(X.shape[1]):
+            assert abs(Xn[m, k] - X[m, k] * i * g[k]) <= 1e-14 * max(1.0, abs(Xn[m, k]))
+
+
+def test_norm_backward_finite_differences():
+    """dX of the norm + layer is the gradient of L = <dY, H> with respect to the
+    raw X (central differences with h = 1e-6: the norm is not linear in X, so
+    agreement is to ~1e-8), dA and dB those of the adapter."""
+    X, g, eps, W, A, B, dY, s = norm_case(22)
+    loss = lambda X_, A_, B_: float(np.sum(dY * oracle.norm_forward(X_, g, eps, W, A_, B_, s)[0]))
+    dX, dA, dB = oracle.norm_backward(dY, X, g, eps, W, A, B, s)
+    h = 1e-6
+    for idx in itertools.product(range(X.shape[0]), range(X.shape[1])):
+        Xp, Xm = X.copy(), X.copy()
+        Xp[idx] += h
+        Xm[idx] -= h
+        fd = (loss(Xp, A, B) - loss(Xm, A, B)) / (2 * h)
+        assert abs(fd - dX[idx]) <= 1e-6 * max(1.0, abs(dX[idx])), (idx, fd, dX[idx])
+    for P, G, which in ((A, dA, "A"), (B, dB, "B")):
+        for idx in itertools.product(*map(range, P.shape)):
+            Pp, Pm = P.copy(), P.copy()
+            Pp[idx] += h
+            Pm[idx] -= h
+            args_p = (Pp, B) if which == "A" else (A, Pp)
+            args_m = (Pm, B) if which == "A" else (A, Pm)
+            fd = (loss(X, *args_p) - loss(X, *args_m)) / (2 * h)
+            assert abs(fd - G[idx]) <= 1e-6 * max(1.0, abs(G[idx]))
+
+
+def test_norm_scale_invariance():
+    """With eps = 0, RMSNorm(c X) = RMSNorm(X) for c > 0: H does not change and
+    the input gradient scales by 1 / c (the adapter gradients do not change)."""
+    X, g, _, W, A, B, dY, s = norm_case(23)
+    c = 3.7
+    H1, U1, _ = oracle.norm_forward(X, g, 0.0, W, A, B, s)
+    H2, U2, _ = oracle.norm_forward(c * X, g, 0.0, W, A, B, s)
+    np.testing.assert_allclose(H2, H1, rtol=1e-12, atol=1e-12)
+    dX1, dA1, dB1 = oracle.norm_backward(dY, X, g, 0.0, W, A, B, s)
+    dX2, dA2, dB2 = oracle.norm_backward(dY, c * X, g, 0.0, W, A, B, s)
+    np.testing.assert_allclose(dX2, dX1 / c, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dA2, dA1, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dB2, dB1, rtol=1e-11, atol=1e-12)
+
+
+def test_norm_input_gradient_is_orthogonal_to_the_input():
+    """With eps = 0 the rows of RMSNorm(X) do not change along X's own rows, so
+    every row of dX is orthogonal to the same row of X (a property of the
+    norm's Jacobian that the closed form must keep)."""
+    X, g, _, W, A, B, dY, s = norm_case(24)
+    dX, _, _ = oracle.norm_backward(dY, X, g, 0.0, W, A, B, s)
+    dots = np.sum(dX * X, axis=1)
+    assert np.all(np.abs(dots) <= 1e-11 * np.abs(dX).max() * np.abs(X).max() * X.shape[1])
