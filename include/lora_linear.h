@@ -185,6 +185,39 @@ lora_status lora_group_bwd(const lora_group_desc* desc,
                            void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * RMSNorm in front of the layer (page "ms-swift框架下UnSloth与Liger-Kernel优化
+ * 实战", section "关键融合策略解析", RMSNorm + Linear: the normalised input is
+ * never written out and read back).  The layer is applied to
+ *   Xn[m, k] = X[m, k] inv[m] g[k],   inv[m] = 1 / sqrt(mean_k X[m, k]^2 + eps),
+ * with the norm weight g [K] (bf16) frozen like W.  g is folded into the frozen
+ * weight once: lora_fold_norm_weight writes W_g = bf16(W diag(g)) ([N, K]; W_out
+ * may be W itself).  The entry points then read the raw X:
+ *   forward:  H = Xn W^T + s (Xn A^T) B^T, computed as inv (X W_g^T + s X (A diag g)^T B^T);
+ *             U_save (optional) receives U = Xn A^T, inv_rms_save (optional,
+ *             float32 [M]) receives inv for the backward;
+ *   backward: dX = the gradient with respect to the raw X (through the norm),
+ *             dA = s (dY B)^T Xn, dB = s dY^T U; U_saved / inv_rms_saved NULL:
+ *             recomputed from X.  No gradient for g (frozen).
+ * Shapes, flags, errors and ownership as for lora_linear_fwd / _bwd, with the
+ * workspace of lora_norm_linear_workspace_size; eps >= 0; bf16 only
+ * (LORA_ERR_UNSUPPORTED otherwise).
+ */
+lora_status lora_fold_norm_weight(const void* W, const void* g, int64_t N, int64_t K, void* W_out, void* stream);
+
+lora_status lora_norm_linear_workspace_size(const lora_linear_desc* desc, size_t* bytes);
+
+lora_status lora_norm_linear_fwd(const lora_linear_desc* desc, float eps,
+                                 const void* X, const void* g, const void* W_g, const void* A, const void* B,
+                                 void* H, float* U_save, float* inv_rms_save,
+                                 void* ws, size_t ws_bytes, void* stream);
+
+lora_status lora_norm_linear_bwd(const lora_linear_desc* desc, float eps,
+                                 const void* dY, const void* X, const void* g, const void* W_g,
+                                 const void* A, const void* B, const float* U_saved, const float* inv_rms_saved,
+                                 void* dX, void* dA, void* dB,
+                                 void* ws, size_t ws_bytes, void* stream);
+
+/*
  * 4-bit frozen weight (page "Unsloth — 微调 2-5x 加速", section "核心要点",
  * item 3: 4-bit weights are dequantised inside the matmul, not copied out
  * first).  W is replaced by

@@ -30,7 +30,9 @@ EXPORTED = (
     "lora_linear_workspace_size", "lora_linear_fwd", "lora_linear_bwd", "lora_linear_bwd_noalloc",
     "lora_qlinear_fwd", "lora_qlinear_bwd", "lora_dequant4", "lora_merge",
     "lora_linear_buffer_ranges", "lora_group_workspace_size", "lora_group_fwd", "lora_group_bwd",
-    "lora_tune_linear", "lora_tuner_lookup", "lora_tuner_save", "lora_tuner_load", "lora_tuner_clear", "lora_set_kernel_timer", "lora_status_string", "lora_last_error",
+    "lora_fold_norm_weight", "lora_norm_linear_workspace_size", "lora_norm_linear_fwd", "lora_norm_linear_bwd",
+    "lora_tune_linear", "lora_tuner_lookup", "lora_tuner_save", "lora_tuner_load", "lora_tuner_clear",
+    "lora_set_kernel_timer", "lora_status_string", "lora_last_error",
 )
 
 # void (*)(void* user, const char* kernel, void* stream, void** start_event, void** stop_event)
@@ -80,7 +82,7 @@ def load() -> ctypes.CDLL:
             f"{LIB_PATH} is missing: build it first (python -m lora_linear_layer_amd.build); "
             "the LoRA layer has no non-HIP implementation")
     lib = ctypes.CDLL(LIB_PATH)
-    vp, sz, i32, i64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64
+    vp, sz, i32, i64, f32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
     dp = ctypes.POINTER(LoraLinearDesc)
     gp = ctypes.POINTER(LoraGroupDesc)
     sig = {
@@ -101,6 +103,10 @@ def load() -> ctypes.CDLL:
         "lora_tuner_load": [ctypes.c_char_p],
         "lora_group_fwd": [gp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "lora_group_bwd": [gp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "lora_fold_norm_weight": [vp, vp, i64, i64, vp, vp],
+        "lora_norm_linear_workspace_size": [dp, ctypes.POINTER(sz)],
+        "lora_norm_linear_fwd": [dp, f32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "lora_norm_linear_bwd": [dp, f32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)

@@ -285,6 +285,72 @@ def lora_group_bwd(desc: GroupDesc, dY, X, W, A, B, U_saved, dX, dA, dB, ws=None
     _check(st, "lora_group_bwd")
 
 
+def _check_norm(desc: Desc, **ts):
+    M, K, N, r = desc.M, desc.K, desc.N, desc.r
+    bf = (torch.bfloat16,)
+    spec = {"X": ((M, K), bf), "g": ((K,), bf), "W": ((N, K), bf), "W_g": ((N, K), bf), "A": ((r, K), bf),
+            "B": ((N, r), bf), "H": ((M, N), bf), "dY": ((M, N), bf), "dX": ((M, K), bf), "dA": ((r, K), bf),
+            "dB": ((N, r), bf), "U_save": ((M, r), (torch.float32,)), "U_saved": ((M, r), (torch.float32,)),
+            "inv_rms_save": ((M,), (torch.float32,)), "inv_rms_saved": ((M,), (torch.float32,))}
+    for name, t in ts.items():
+        _expect(t, name, *spec[name])
+    _same_gpu(**ts)
+
+
+def lora_norm_linear_workspace_size(desc: Desc) -> int:
+    out = ctypes.c_size_t(0)
+    d = desc.c()
+    _check(_lib.load().lora_norm_linear_workspace_size(ctypes.byref(d), ctypes.byref(out)),
+           "lora_norm_linear_workspace_size")
+    return int(out.value)
+
+
+def lora_fold_norm_weight(W, g, W_out, stream=None):
+    """W_out = bf16(W diag(g)): the frozen RMSNorm weight folded into the frozen
+    linear weight once (W_out may be W)."""
+    N, K = W.shape
+    for name, t, shape in (("W", W, (N, K)), ("g", g, (K,)), ("W_out", W_out, (N, K))):
+        _expect(t, name, shape, (torch.bfloat16,))
+    _same_gpu(W=W, g=g, W_out=W_out)
+    st = _lib.load().lora_fold_norm_weight(_ptr(W), _ptr(g), N, K, _ptr(W_out), _stream(stream))
+    _check(st, "lora_fold_norm_weight")
+
+
+def _norm_ws(desc, ws, ws_bytes, device):
+    if ws is None:
+        nbytes = lora_norm_linear_workspace_size(desc)
+        return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device), nbytes
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    return ws, ws_bytes
+
+
+def lora_norm_linear_fwd(desc: Desc, eps: float, X, g, W_g, A, B, H, U_save=None, inv_rms_save=None, ws=None,
+                         ws_bytes=None, stream=None):
+    """H = Xn W^T + s (Xn A^T) B^T with Xn = RMSNorm(X) g, from the raw X and
+    the folded W_g (see include/lora_linear.h)."""
+    _check_norm(desc, X=X, g=g, W_g=W_g, A=A, B=B, H=H, U_save=U_save, inv_rms_save=inv_rms_save)
+    ws, ws_bytes = _norm_ws(desc, ws, ws_bytes, X.device)
+    d = desc.c()
+    st = _lib.load().lora_norm_linear_fwd(ctypes.byref(d), float(eps), _ptr(X), _ptr(g), _ptr(W_g), _ptr(A),
+                                          _ptr(B), _ptr(H), _ptr(U_save), _ptr(inv_rms_save), _ptr(ws), ws_bytes,
+                                          _stream(stream))
+    _check(st, "lora_norm_linear_fwd")
+
+
+def lora_norm_linear_bwd(desc: Desc, eps: float, dY, X, g, W_g, A, B, U_saved, inv_rms_saved, dX, dA, dB,
+                         ws=None, ws_bytes=None, stream=None):
+    """dX through the norm to the raw X; dA = s (dY B)^T Xn; dB = s dY^T U."""
+    _check_norm(desc, dY=dY, X=X, g=g, W_g=W_g, A=A, B=B, U_saved=U_saved, inv_rms_saved=inv_rms_saved, dX=dX,
+                dA=dA, dB=dB)
+    ws, ws_bytes = _norm_ws(desc, ws, ws_bytes, dY.device)
+    d = desc.c()
+    st = _lib.load().lora_norm_linear_bwd(ctypes.byref(d), float(eps), _ptr(dY), _ptr(X), _ptr(g), _ptr(W_g),
+                                          _ptr(A), _ptr(B), _ptr(U_saved), _ptr(inv_rms_saved), _ptr(dX), _ptr(dA),
+                                          _ptr(dB), _ptr(ws), ws_bytes, _stream(stream))
+    _check(st, "lora_norm_linear_bwd")
+
+
 _TUNED_FIELDS = ("fwd_split", "bwd_split", "rank_div", "z_div_fwd", "z_div_bwd", "fwd_us", "bwd_us",
                  "default_fwd_us", "default_bwd_us")
 

@@ -147,6 +147,12 @@ struct GemmArgs {
     int z_ld;
     int n_members;
     int member_q0[kMaxMembers + 1];
+    // Optional per-row scale (RMSNorm in front of the layer: 1 / rms of each
+    // input row).  Forward: every output row after the rank-r term and the
+    // saved Z.  Input gradient: only the V planes written for the adapter
+    // gradients (the output is scaled by the row kernel that follows).
+    // nullptr: none.
+    const float* row_scale;
 };
 
 namespace g2 {
@@ -671,7 +677,9 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
         if (a.Zsave != nullptr && qt == 0) {
             for (int e = tid; e < BP * r; e += NT) {
                 const int pl = e / r, j = e - pl * r;
-                if (p0 + pl < P) a.Zsave[(size_t)(p0 + pl) * r + j] = Zx[pl * RPAD + j];
+                if (p0 + pl < P)
+                    a.Zsave[(size_t)(p0 + pl) * r + j] =
+                        Zx[pl * RPAD + j] * (a.row_scale ? a.row_scale[p0 + pl] : 1.f);
             }
         }
         if constexpr (TRANS) {
@@ -681,7 +689,7 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
                 for (int e = tid; e < BP * r; e += NT) {
                     const int j = e / BP, pl = e - j * BP, p = p0 + pl;
                     if (p >= a.Mp) continue;
-                    const float v = p < P ? Zx[pl * RPAD + j] : 0.f;
+                    const float v = p < P ? Zx[pl * RPAD + j] * (a.row_scale ? a.row_scale[p] : 1.f) : 0.f;
                     const float u = p < P ? a.Uin[(size_t)p * r + j] : 0.f;
                     const __bf16 vh = (__bf16)v, uh = (__bf16)u;
                     const size_t o = zt_index(j, p, r);
@@ -694,6 +702,18 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
         }
     }
 
+    // precomputed Z saved row-scaled (RMSNorm in front: Zin is the product with
+    // the raw input, the saved U the one with the normalised input; forward only)
+    if constexpr (ZIN && !TRANS) {
+        if (a.Zsave != nullptr && qt == 0 && slice <= 0) {
+            for (int e = tid; e < BP * a.z_ld; e += NT) {
+                const int pl = e / a.z_ld, j = e - pl * a.z_ld, p = p0 + pl;
+                if (p < P)
+                    a.Zsave[(size_t)p * a.z_ld + j] =
+                        a.Zin[(size_t)p * a.z_ld + j] * (a.row_scale ? a.row_scale[p] : 1.f);
+            }
+        }
+    }
     const float s = a.s;
     // rank blocks of 16: the in-tile Z has RPAD columns; a precomputed one any r
     // (up to the 192 of grouped input gradients); the rank-r term goes into slice 0 only
@@ -736,6 +756,16 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
                                               lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)});
 #pragma unroll
             for (int qi = 0; qi < QB; ++qi) acc[qi][pi] = mfma16(ef[qi], zf, acc[qi][pi]);
+        }
+    }
+
+    if (!TRANS && a.row_scale != nullptr && !(SPLIT && slice >= 0)) {   // split tiles: in split_finish
+#pragma unroll
+        for (int pi = 0; pi < 8; ++pi) {
+            const int p = p0 + wp * 128 + ((pi + ZB * wq) & 7) * 16 + l16e;
+            const float rsc = p < P ? a.row_scale[p] : 0.f;
+#pragma unroll
+            for (int qi = 0; qi < QB; ++qi) acc[qi][pi] *= rsc;
         }
     }
 
@@ -789,6 +819,7 @@ struct SplitFinishArgs {
     const float* part;
     uint16_t* out;
     int P, Q, nPt, nQt, first_split, n_stiles, split;
+    const float* row_scale;     // optional per-row scale of the sum (see GemmArgs)
 };
 
 __global__ __launch_bounds__(256) void split_finish(const SplitFinishArgs a) {
@@ -805,6 +836,7 @@ __global__ __launch_bounds__(256) void split_finish(const SplitFinishArgs a) {
     const float* src = a.part + (size_t)stile * ts + pl * g2::BQ + ql;
     f32x4 acc = *reinterpret_cast<const f32x4*>(src);
     for (int k = 1; k < a.split; ++k) acc += *reinterpret_cast<const f32x4*>(src + (size_t)k * a.n_stiles * ts);
+    if (a.row_scale) acc *= a.row_scale[p];
     *reinterpret_cast<u32x2*>(a.out + (size_t)p * a.Q + q) = u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
 }
 

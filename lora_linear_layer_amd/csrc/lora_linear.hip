@@ -25,6 +25,7 @@
 #include "rank_stream.hpp"
 #include "dequant4.hpp"
 #include "merge.hpp"
+#include "norm.hpp"
 #include "f32_kernels.hpp"
 
 using namespace lora;
@@ -195,6 +196,7 @@ struct Shape {
     int32_t dtype = LORA_DTYPE_BF16;
     uint32_t flags = 0;
     bool quant_capable = true;      // workspace also sized for the 4-bit entry points (plain layers)
+    bool norm = false;              // RMSNorm in front (1 / rms per row and A diag(g) in the workspace)
     int64_t rg() const { return (int64_t)G * r; }      // rank of the stacked A, U and V
     int64_t Nm(int m) const { return n0[m + 1] - n0[m]; }
 };
@@ -239,6 +241,7 @@ RankSplit split_g(const Shape& d) {
 // Workspace layout for one shape (offsets in bytes from ws).
 struct Plan {
     size_t off_v = 0, off_u = 0, off_zp = 0, off_ga = 0, off_gb = 0, off_zt = 0, off_bt = 0, off_split = 0, total = 0;
+    size_t off_inv = 0, off_ag = 0;     // RMSNorm in front: 1 / rms [M] float32, A diag(g) [r][K] bf16
     int64_t Mp = 0;         // tokens rounded up to a whole 128-token tile (side planes of the G pass)
     RankSplit g;
 };
@@ -271,6 +274,12 @@ Plan make_plan(const Shape& d) {
         const size_t n_split = std::max(gemm_split_plan(d.M, d.N, d.K, q).part_floats,
                                         gemm_split_plan(d.M, d.K, d.N, q).part_floats);
         cur += align_up(n_split * sizeof(float));
+        if (d.norm) {
+            p.off_inv = cur;
+            cur += align_up((size_t)d.M * sizeof(float));
+            p.off_ag = cur;
+            cur += align_up((size_t)rg * d.K * sizeof(uint16_t));
+        }
     }
     p.total = cur;
     return p;
@@ -430,7 +439,7 @@ void launch_gemm_zin(GemmArgs a, const SplitPlan& sp, hipStream_t st) {
         const int units = sp.first + (T - sp.first) * sp.split;
         LAUNCH(TRANS ? "lora_gemm dX (split)" : "lora_gemm forward (split)", (lora_gemm<TRANS, RPAD, true, Q4, true>), dim3(units), dim3(g2w::NT), 0, st, a);
         SplitFinishArgs f{a.Part, a.Out, a.P, a.Q, (int)cdiv(a.P, g2::BP), (int)cdiv(a.Q, g2::BQ), sp.first,
-                          T - sp.first, sp.split};
+                          T - sp.first, sp.split, TRANS ? nullptr : a.row_scale};
         const int64_t n = (int64_t)(T - sp.first) * (g2::BP * g2::BQ / 4);
         LAUNCH("split_finish", split_finish, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, st, f);
         return;
@@ -468,7 +477,8 @@ void launch_rank_z_t(const RankZArgs& a, dim3 grid, hipStream_t st) {
 }
 
 void launch_rank_z(int64_t M, const uint16_t* Y, int64_t ldy, int64_t C, const uint16_t* F, int64_t f_rows,
-                   float* Z, int64_t z_ld, int64_t z_j0, float* zpart, hipStream_t st, int z_div = 1) {
+                   float* Z, int64_t z_ld, int64_t z_j0, float* zpart, hipStream_t st, int z_div = 1,
+                   const float* row_scale = nullptr) {
     const int n_chunk = std::max(1, z_chunks(M, C) / std::max(z_div, 1));
     for (int64_t j0 = 0; j0 < f_rows; j0 += kMaxZCols) {
         const int rl = (int)std::min<int64_t>(f_rows - j0, kMaxZCols);
@@ -495,6 +505,7 @@ void launch_rank_z(int64_t M, const uint16_t* Y, int64_t ldy, int64_t C, const u
             a.z_ld = (int)z_ld;
             a.z_j0 = (int)(z_j0 + j0);
             a.chunk_stride = 0;
+            a.row_scale = row_scale;
         }
         const dim3 grid((unsigned)cdiv(M, 128), (unsigned)n_used, 1);
         switch (jb) {
@@ -508,7 +519,7 @@ void launch_rank_z(int64_t M, const uint16_t* Y, int64_t ldy, int64_t C, const u
         if (n_used > 1) {
             const int64_t n = M * rl;
             LAUNCH("partial_sum", partial_sum, dim3((unsigned)cdiv(n, 1024)), dim3(256), 0, st, zpart, Z, (int)M,
-                   rl, (int)z_ld, (int)(z_j0 + j0), n_used);
+                   rl, (int)z_ld, (int)(z_j0 + j0), n_used, row_scale);
         }
     }
 }
@@ -526,7 +537,8 @@ uint16_t* zt_plane(const Plan& plan, char* wsb, int64_t rows, int i) {
 // otherwise zt_hilo writes them.  Problems of one rank width share a launch.
 lora_status launch_adapter_grads(const Shape& d, const Plan& plan, char* wsb, const uint16_t* X, const float* V,
                                  const uint16_t* dY, const float* U, void* dA, void* dB, bool planes_ready,
-                                 hipStream_t st, int rank_div = 1) {
+                                 hipStream_t st, int rank_div = 1, const float* v_row_scale = nullptr,
+                                 const uint16_t* a_col_scale = nullptr) {
     const int64_t rg = d.rg();
     // token chunks: the model's count, or fewer (tuned); the partials fit either way
     RankSplit g = plan.g;
@@ -543,7 +555,7 @@ lora_status launch_adapter_grads(const Shape& d, const Plan& plan, char* wsb, co
     uint16_t* const ut_lo = zt_plane(plan, wsb, rg, 3);
     if (!planes_ready) {
         LAUNCH("zt_hilo", zt_hilo, dim3((unsigned)cdiv(rg * plan.Mp, 256), 2), dim3(256), 0, st, V, U, vt_hi,
-               vt_lo, ut_hi, ut_lo, (int)d.M, (int)plan.Mp, (int)rg);
+               vt_lo, ut_hi, ut_lo, (int)d.M, (int)plan.Mp, (int)rg, v_row_scale);
         LAUNCH_CHECK("zt_hilo");
     }
     // the problems, by rank padding (16, 32 or 64 columns)
@@ -599,6 +611,7 @@ lora_status launch_adapter_grads(const Shape& d, const Plan& plan, char* wsb, co
     f.s = d.alpha / (float)d.r;
     f.f32_out = 0;
     f.accumulate = (d.flags & LORA_FLAG_ACCUM_GRADS) ? 1 : 0;
+    f.a_col_scale = a_col_scale;
     LAUNCH("grad_final", grad_final, dim3((unsigned)cdiv(d.K * rg + d.N * d.r, 256)), dim3(256), 0, st, f);
     LAUNCH_CHECK("grad_final");
     return LORA_OK;
@@ -613,7 +626,8 @@ void set_members(GemmArgs& g, const Shape& d) {
 // ---------------------------------------------------------------- forward
 lora_status fwd_bf16(const Shape& d, bool quant, const void* X, const void* W, const uint8_t* Wq,
                      const uint16_t* absmax, const float* codebook, const void* A, const void* B, void* H,
-                     float* U_save, void* ws, hipStream_t st, const Tuning& tn = Tuning{}) {
+                     float* U_save, void* ws, hipStream_t st, const Tuning& tn = Tuning{},
+                     const float* row_scale = nullptr) {
     const Plan plan = make_plan(d);
     char* const wsb = static_cast<char*>(ws);
     const int r = (int)d.r;
@@ -624,8 +638,9 @@ lora_status fwd_bf16(const Shape& d, bool quant, const void* X, const void* W, c
     const bool in_tile = d.G == 1 && gemm_in_tile(quant, r, sp);
     float* U = U_save;
     if (!in_tile) {
-        // U = X A^T (all members in one pass over X), read by the GEMM epilogue
-        if (!U) U = reinterpret_cast<float*>(wsb + plan.off_u);
+        // U = X A^T (all members in one pass over X), read by the GEMM epilogue; with
+        // a row scale the pass forms the raw product and the GEMM saves it scaled
+        if (!U || row_scale) U = reinterpret_cast<float*>(wsb + plan.off_u);
         launch_rank_z(d.M, X16, d.K, d.K, A16, d.rg(), U, d.rg(), 0, zpart, st, tn.z_div_f);
         LAUNCH_CHECK("rank_z_lds(U)");
     }
@@ -638,9 +653,10 @@ lora_status fwd_bf16(const Shape& d, bool quant, const void* X, const void* W, c
     g.F = A16;
     g.E = static_cast<const uint16_t*>(B);
     g.Out = static_cast<uint16_t*>(H);
-    g.Zsave = in_tile ? U_save : nullptr;
+    g.Zsave = (in_tile || row_scale) ? U_save : nullptr;
     g.Zin = in_tile ? nullptr : U;
     g.z_ld = (int)d.rg();
+    g.row_scale = row_scale;
     set_members(g, d);
     g.Part = reinterpret_cast<float*>(wsb + plan.off_split);
     g.P = (int)d.M; g.Q = (int)d.N; g.C = (int)d.K; g.r = r;
@@ -660,7 +676,8 @@ lora_status fwd_bf16(const Shape& d, bool quant, const void* X, const void* W, c
 lora_status bwd_bf16(const Shape& d, bool quant, const void* dY, const void* X, const void* W,
                      const uint8_t* Wq, const uint16_t* absmax, const float* codebook, const void* A,
                      const void* B, const float* U_saved, void* dX, void* dA, void* dB, void* ws, hipStream_t st,
-                     const Tuning& tn = Tuning{}) {
+                     const Tuning& tn = Tuning{}, const float* row_scale = nullptr,
+                     const uint16_t* a_col_scale = nullptr) {
     const Plan plan = make_plan(d);
     const int r = (int)d.r;
     const int64_t rg = d.rg();
@@ -676,7 +693,7 @@ lora_status bwd_bf16(const Shape& d, bool quant, const void* dY, const void* X, 
     const float* U = U_saved;
     if (!U) {
         float* Uw = reinterpret_cast<float*>(wsb + plan.off_u);
-        launch_rank_z(d.M, X16, d.K, d.K, A16, rg, Uw, rg, 0, zpart, st, tn.z_div_b);
+        launch_rank_z(d.M, X16, d.K, d.K, A16, rg, Uw, rg, 0, zpart, st, tn.z_div_b, row_scale);
         LAUNCH_CHECK("rank_z_lds(U)");
         U = Uw;
     }
@@ -718,6 +735,7 @@ lora_status bwd_bf16(const Shape& d, bool quant, const void* dY, const void* X, 
             g.Mp = (int)plan.Mp;
         }
         g.Part = reinterpret_cast<float*>(wsb + plan.off_split);
+        g.row_scale = row_scale;
         g.P = (int)d.M; g.Q = (int)d.K; g.C = (int)d.N; g.r = (int)rg;
         g.s = d.alpha / (float)d.r;
         if (quant) launch_gemm<true, true>(g, v_in_tile, sp, st);
@@ -725,7 +743,8 @@ lora_status bwd_bf16(const Shape& d, bool quant, const void* dY, const void* X, 
         LAUNCH_CHECK(quant ? "lora_gemm(4-bit dX)" : "lora_gemm(dX)");
     }
     // 4., 5. dA = s V^T X, dB = s dY^T U
-    const lora_status gst = launch_adapter_grads(d, plan, wsb, X16, V, dY16, U, dA, dB, v_in_tile, st, tn.rank_div);
+    const lora_status gst = launch_adapter_grads(d, plan, wsb, X16, V, dY16, U, dA, dB, v_in_tile, st, tn.rank_div,
+                                                 row_scale, a_col_scale);
     if (gst != LORA_OK) return gst;
     return ok();
 }
@@ -1180,6 +1199,117 @@ lora_status lora_qlinear_bwd(const lora_linear_desc* desc, const void* dY, const
         return bwd_f32(*desc, true, dY, X, nullptr, Wq, absmax, codebook, A, B, U_saved, dX, dA, dB, ws, s);
     return bwd_bf16(shape_of(*desc), true, dY, X, nullptr, Wq, absmax, codebook, A, B, U_saved, dX, dA, dB, ws, s,
                     tuned_for(*desc, true));
+}
+
+// ---------------------------------------------------------------- RMSNorm in front
+static lora_status check_norm(const lora_linear_desc* desc, float eps) {
+    lora_status st = check_desc(desc, false);
+    if (st != LORA_OK) return st;
+    if (desc->dtype != LORA_DTYPE_BF16) return fail(LORA_ERR_UNSUPPORTED, "the RMSNorm path is bf16 only");
+    if (!std::isfinite(eps) || eps < 0.f) return fail(LORA_ERR_INVALID_ARG, "eps must be finite and >= 0");
+    return LORA_OK;
+}
+
+static Shape norm_shape(const lora_linear_desc& d) {
+    Shape s = shape_of(d);
+    s.norm = true;
+    return s;
+}
+
+lora_status lora_norm_linear_workspace_size(const lora_linear_desc* desc, size_t* bytes) {
+    if (!bytes) return fail(LORA_ERR_INVALID_ARG, "bytes is NULL");
+    lora_status st = check_norm(desc, 0.f);
+    if (st != LORA_OK) return st;
+    *bytes = make_plan(norm_shape(*desc)).total;
+    return ok();
+}
+
+lora_status lora_fold_norm_weight(const void* W, const void* g, int64_t N, int64_t K, void* W_out, void* stream) {
+    if (N <= 0 || K <= 0) return fail(LORA_ERR_INVALID_ARG, "N, K must be positive");
+    if (K % 8) return fail(LORA_ERR_UNSUPPORTED, "K must be a multiple of 8 (K=%lld)", (long long)K);
+    if (N * K > kMaxElems) return fail(LORA_ERR_UNSUPPORTED, "W has 2^31 or more elements");
+    lora_status st = check_ptrs({{W, "W"}, {g, "g"}, {W_out, "W_out"}}, {});
+    if (st != LORA_OK) return st;
+    if (W_out == g) return fail(LORA_ERR_INVALID_ARG, "output W_out aliases g");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    LAUNCH("scale_cols", scale_cols_kernel, dim3((unsigned)cdiv(N * K / 8, 256)), dim3(256), 0, s,
+           static_cast<const uint16_t*>(W), static_cast<const uint16_t*>(g), static_cast<uint16_t*>(W_out), N, (int)K);
+    LAUNCH_CHECK("scale_cols");
+    return ok();
+}
+
+lora_status lora_norm_linear_fwd(const lora_linear_desc* desc, float eps, const void* X, const void* g,
+                                 const void* W_g, const void* A, const void* B, void* H, float* U_save,
+                                 float* inv_rms_save, void* ws, size_t ws_bytes, void* stream) {
+    lora_status st = check_norm(desc, eps);
+    if (st != LORA_OK) return st;
+    st = check_ptrs({{X, "X"}, {g, "g"}, {W_g, "W_g"}, {A, "A"}, {B, "B"}, {H, "H"}},
+                    {{U_save, "U_save"}, {inv_rms_save, "inv_rms_save"}});
+    if (st != LORA_OK) return st;
+    st = check_no_alias({{H, "H"}, {U_save, "U_save"}, {inv_rms_save, "inv_rms_save"}},
+                        {{X, "X"}, {g, "g"}, {W_g, "W_g"}, {A, "A"}, {B, "B"}, {H, "H"}, {U_save, "U_save"},
+                         {inv_rms_save, "inv_rms_save"}, {ws, "ws"}});
+    if (st != LORA_OK) return st;
+    const Shape d = norm_shape(*desc);
+    st = check_ws(d, ws, ws_bytes);
+    if (st != LORA_OK) return st;
+    const Plan plan = make_plan(d);
+    char* const wsb = static_cast<char*>(ws);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    float* const inv = inv_rms_save ? inv_rms_save : reinterpret_cast<float*>(wsb + plan.off_inv);
+    uint16_t* const Ag = reinterpret_cast<uint16_t*>(wsb + plan.off_ag);
+    const uint16_t* const X16 = static_cast<const uint16_t*>(X);
+    const uint16_t* const g16 = static_cast<const uint16_t*>(g);
+    LAUNCH("rms_inv", rms_inv_kernel, dim3((unsigned)cdiv(d.M, 4)), dim3(256), 0, s, X16, inv, (int)d.M, (int)d.K, eps);
+    LAUNCH("scale_cols", scale_cols_kernel, dim3((unsigned)cdiv(d.r * d.K / 8, 256)), dim3(256), 0, s,
+           static_cast<const uint16_t*>(A), g16, Ag, d.r, (int)d.K);
+    LAUNCH_CHECK("rms_inv, scale_cols");
+    return fwd_bf16(d, false, X, W_g, nullptr, nullptr, nullptr, Ag, B, H, U_save, ws, s, Tuning{}, inv);
+}
+
+lora_status lora_norm_linear_bwd(const lora_linear_desc* desc, float eps, const void* dY, const void* X,
+                                 const void* g, const void* W_g, const void* A, const void* B, const float* U_saved,
+                                 const float* inv_rms_saved, void* dX, void* dA, void* dB, void* ws, size_t ws_bytes,
+                                 void* stream) {
+    lora_status st = check_norm(desc, eps);
+    if (st != LORA_OK) return st;
+    st = check_ptrs({{dY, "dY"}, {X, "X"}, {g, "g"}, {W_g, "W_g"}, {A, "A"}, {B, "B"}, {dA, "dA"}, {dB, "dB"}},
+                    {{U_saved, "U_saved"}, {inv_rms_saved, "inv_rms_saved"}, {dX, "dX"}});
+    if (st != LORA_OK) return st;
+    st = check_no_alias({{dX, "dX"}, {dA, "dA"}, {dB, "dB"}},
+                        {{dY, "dY"}, {X, "X"}, {g, "g"}, {W_g, "W_g"}, {A, "A"}, {B, "B"}, {U_saved, "U_saved"},
+                         {inv_rms_saved, "inv_rms_saved"}, {dX, "dX"}, {dA, "dA"}, {dB, "dB"}, {ws, "ws"}});
+    if (st != LORA_OK) return st;
+    const Shape d = norm_shape(*desc);
+    st = check_ws(d, ws, ws_bytes);
+    if (st != LORA_OK) return st;
+    const Plan plan = make_plan(d);
+    char* const wsb = static_cast<char*>(ws);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const uint16_t* const X16 = static_cast<const uint16_t*>(X);
+    const uint16_t* const g16 = static_cast<const uint16_t*>(g);
+    const float* inv = inv_rms_saved;
+    if (!inv) {
+        float* const w = reinterpret_cast<float*>(wsb + plan.off_inv);
+        LAUNCH("rms_inv", rms_inv_kernel, dim3((unsigned)cdiv(d.M, 4)), dim3(256), 0, s, X16, w, (int)d.M, (int)d.K,
+               eps);
+        inv = w;
+    }
+    uint16_t* const Ag = reinterpret_cast<uint16_t*>(wsb + plan.off_ag);
+    LAUNCH("scale_cols", scale_cols_kernel, dim3((unsigned)cdiv(d.r * d.K / 8, 256)), dim3(256), 0, s,
+           static_cast<const uint16_t*>(A), g16, Ag, d.r, (int)d.K);
+    LAUNCH_CHECK("rms_inv, scale_cols");
+    // dY W_g + s V A_g into dX, dA = s g (inv V)^T X, dB = s dY^T U
+    st = bwd_bf16(d, false, dY, X, W_g, nullptr, nullptr, nullptr, Ag, B, U_saved, dX, dA, dB, ws, s, Tuning{}, inv,
+                  g16);
+    if (st != LORA_OK) return st;
+    if (dX) {
+        // through the norm: dX = inv D - X (inv^3 / K) <D, X>, D = dY W_g + s V A_g
+        LAUNCH("norm_dx", norm_dx_kernel, dim3((unsigned)cdiv(d.M, 4)), dim3(256), 0, s, static_cast<uint16_t*>(dX),
+               X16, inv, (int)d.M, (int)d.K);
+        LAUNCH_CHECK("norm_dx");
+    }
+    return ok();
 }
 
 lora_status lora_tune_linear(const lora_linear_desc* desc, int32_t quant, const void* X, const void* W,

@@ -239,6 +239,7 @@ struct RankZArgs {
     const uint16_t* Y;
     const uint16_t* F;
     float* out;
+    const float* row_scale;   // optional scale of each output row (applied when out is Z itself)
     size_t chunk_stride;      // floats between the partials of two contraction chunks
     int ldy, z_ld;
     int M, C, f_j0, rl, z_j0, chunk_c;
@@ -311,6 +312,11 @@ __global__ __launch_bounds__(512) void rank_z_lds(const RankZArgs a) {
     vmcnt_le<0>();
     // lane holds Z^T rows j = 16 jb + 4 g4 + e at column m
     if (m < M) {
+        if (a.row_scale) {
+            const float rsc = a.row_scale[m];
+#pragma unroll
+            for (int jb = 0; jb < JB; ++jb) acc[jb] *= rsc;
+        }
         float* const out = a.out + (size_t)blockIdx.y * a.chunk_stride + (size_t)m * a.z_ld + a.z_j0;
         const bool vec = ((a.z_ld | a.z_j0) & 3) == 0;
 #pragma unroll
@@ -329,11 +335,11 @@ __global__ __launch_bounds__(512) void rank_z_lds(const RankZArgs a) {
 
 // rank_stream side planes: hi(j, m) = bf16(Z[m][j]), lo(j, m) = bf16(Z[m][j] - hi),
 // j < r, m < Mp (zero for m >= M), stored at e = zt_index(j, m, r); blockIdx.y
-// selects one of two problems.
+// selects one of two problems; the first one's rows may carry a scale (rs0).
 __global__ __launch_bounds__(256) void zt_hilo(const float* __restrict__ z0, const float* __restrict__ z1,
                                                uint16_t* __restrict__ hi0, uint16_t* __restrict__ lo0,
                                                uint16_t* __restrict__ hi1, uint16_t* __restrict__ lo1, int M, int Mp,
-                                               int r) {
+                                               int r, const float* __restrict__ rs0) {
     const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (e >= (int64_t)r * Mp) return;
     const int64_t blk = e / ((int64_t)r * kSideBlock);
@@ -341,7 +347,7 @@ __global__ __launch_bounds__(256) void zt_hilo(const float* __restrict__ z0, con
     const int j = rem / kSideBlock;
     const int64_t m = blk * kSideBlock + rem % kSideBlock;
     const float* z = blockIdx.y ? z1 : z0;
-    const float v = m < M ? z[(size_t)m * r + j] : 0.f;
+    const float v = m < M ? z[(size_t)m * r + j] * ((!blockIdx.y && rs0) ? rs0[m] : 1.f) : 0.f;
     const __bf16 h = (__bf16)v;
     const __bf16 l = (__bf16)(v - (float)h);
     (blockIdx.y ? hi1 : hi0)[e] = __builtin_bit_cast(uint16_t, h);
@@ -363,7 +369,8 @@ __global__ __launch_bounds__(256) void transpose_rank(const uint16_t* __restrict
 // thread owns 4 consecutive partial elements; the partial loads are issued 8
 // at a time so that their latencies overlap (the additions keep the fixed order).
 __global__ __launch_bounds__(256) void partial_sum(const float* __restrict__ part, float* __restrict__ out, int M,
-                                                   int w, int out_ld, int out_j0, int n_parts) {
+                                                   int w, int out_ld, int out_j0, int n_parts,
+                                                   const float* __restrict__ row_scale) {
     const int64_t n = (int64_t)M * w;
     const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
     if (e0 >= n) return;
@@ -388,7 +395,7 @@ __global__ __launch_bounds__(256) void partial_sum(const float* __restrict__ par
     for (int i = 0; i < cnt; ++i) {
         const int64_t e = e0 + i;
         const int64_t mm = e / w;
-        out[mm * out_ld + out_j0 + (e - mm * w)] = s[i];
+        out[mm * out_ld + out_j0 + (e - mm * w)] = row_scale ? s[i] * row_scale[mm] : s[i];
     }
 }
 
@@ -404,6 +411,7 @@ struct GradFinalArgs {
     int K, N, ra, rb, n_chunk;
     float s;
     int f32_out, accumulate;
+    const uint16_t* a_col_scale;   // optional bf16 scale of dA's column k (the RMSNorm weight g)
 };
 
 __global__ __launch_bounds__(256) void grad_final(const GradFinalArgs a) {
@@ -429,6 +437,7 @@ __global__ __launch_bounds__(256) void grad_final(const GradFinalArgs a) {
     if (isA) {
         const int kk = (int)(f / a.ra), j = (int)(f % a.ra);
         o = (size_t)j * a.K + kk;
+        if (a.a_col_scale) v *= bf16_bits_to_f32(a.a_col_scale[kk]);
     } else {
         o = (size_t)f;
     }

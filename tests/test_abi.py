@@ -292,6 +292,37 @@ def test_group_calls_validate_before_any_hip_call():
                             None) == _lib.LORA_ERR_INVALID_ARG                                       # dX aliases dY
 
 
+def test_norm_calls_validate_before_any_hip_call():
+    """RMSNorm entry points: bf16 only, eps >= 0 and finite, the usual pointer,
+    alias and workspace checks, all before anything is enqueued."""
+    L = lib()
+    desc = lla.Desc(64, 256, 128, 8, 16.0)
+    d = desc.c()
+    need = lla.lora_norm_linear_workspace_size(desc)
+    assert need > lla.lora_linear_workspace_size(desc)          # + inv [M] and A diag(g) [r][K]
+    f32 = lla.Desc(64, 256, 128, 8, 16.0, lla.LORA_DTYPE_F32).c()
+    out = ctypes.c_size_t()
+    assert L.lora_norm_linear_workspace_size(ctypes.byref(f32), ctypes.byref(out)) == _lib.LORA_ERR_UNSUPPORTED
+    p = [ALIGNED + 0x100 * i for i in range(16)]
+    fwd = L.lora_norm_linear_fwd
+    assert fwd(ctypes.byref(f32), 1e-6, *p[:6], None, None, p[9], need, None) == _lib.LORA_ERR_UNSUPPORTED
+    assert fwd(ctypes.byref(d), -1e-6, *p[:6], None, None, p[9], need, None) == _lib.LORA_ERR_INVALID_ARG
+    assert fwd(ctypes.byref(d), float("nan"), *p[:6], None, None, p[9], need, None) == _lib.LORA_ERR_INVALID_ARG
+    assert fwd(ctypes.byref(d), 1e-6, p[0], None, *p[2:6], None, None, p[9], need, None) == _lib.LORA_ERR_INVALID_ARG
+    assert fwd(ctypes.byref(d), 1e-6, *p[:5], MISALIGNED, None, None, p[9], need, None) == _lib.LORA_ERR_MISALIGNED
+    assert fwd(ctypes.byref(d), 1e-6, *p[:6], None, p[0], p[9], need, None) == _lib.LORA_ERR_INVALID_ARG  # inv = X
+    assert fwd(ctypes.byref(d), 1e-6, *p[:6], None, None, p[9], need - 1, None) == _lib.LORA_ERR_WORKSPACE_TOO_SMALL
+    bwd = L.lora_norm_linear_bwd
+    assert bwd(ctypes.byref(d), 1e-6, *p[:6], None, None, p[1], p[7], p[8], p[9], need,
+               None) == _lib.LORA_ERR_INVALID_ARG                                                  # dX aliases X
+    assert bwd(ctypes.byref(d), 1e-6, *p[:6], None, None, p[6], None, p[8], p[9], need,
+               None) == _lib.LORA_ERR_INVALID_ARG                                                  # dA NULL
+    assert L.lora_fold_norm_weight(p[0], p[1], 128, 252, p[2], None) == _lib.LORA_ERR_UNSUPPORTED  # K % 8
+    assert L.lora_fold_norm_weight(p[0], p[1], 0, 256, p[2], None) == _lib.LORA_ERR_INVALID_ARG
+    assert L.lora_fold_norm_weight(p[0], p[1], 128, 256, p[1], None) == _lib.LORA_ERR_INVALID_ARG  # W_out = g
+    assert L.lora_fold_norm_weight(MISALIGNED, p[1], 128, 256, p[2], None) == _lib.LORA_ERR_MISALIGNED
+
+
 # ------------------------------------------------------------ tuning cache (host only)
 def test_tuner_cache_file_round_trip(tmp_path):
     """Entries loaded from a cache file are found for their (architecture,

@@ -31,7 +31,7 @@ from statistics import NormalDist
 import numpy as np
 
 __all__ = [
-    "LinearShape", "Workload", "WORKLOADS", "make_linear_inputs", "codebook4_f32",
+    "LinearShape", "Workload", "WORKLOADS", "make_linear_inputs", "make_norm_inputs", "codebook4_f32",
     "quantize4", "workload",
 ]
 
@@ -180,6 +180,21 @@ def quantize4(W: np.ndarray, codebook: np.ndarray | None = None):
         q = np.searchsorted(mids, y.reshape(w.shape[0], K), side="left").astype(np.uint8)
         codes[r0:r0 + step] = q[:, 0::2] | (q[:, 1::2] << 4)
     return codes, absmax
+
+
+def make_norm_inputs(shape: LinearShape, *, M: int | None = None) -> dict:
+    """Draws of make_linear_inputs for a linear behind an RMSNorm: X becomes a
+    residual-stream input whose rows differ in magnitude (row m of X times
+    exp(0.5 z_m), z_m ~ N(0, 1)), and the frozen norm weight g [K] ~ 1 + N(0,
+    0.2^2) is added; both from a second PCG64 stream seeded seed + 7919, drawn
+    in that order."""
+    d = make_linear_inputs(shape, M=M)
+    M = d["X"].shape[0]
+    rng = np.random.Generator(np.random.PCG64(shape.seed + 7919))
+    row = np.exp(rng.standard_normal(M, dtype=np.float32) * np.float32(0.5))
+    d["X"] = d["X"] * row[:, None]
+    d["g"] = np.float32(1.0) + rng.standard_normal(shape.K, dtype=np.float32) * np.float32(0.2)
+    return d
 
 
 def make_qlora_inputs(shape: LinearShape, *, M: int | None = None) -> dict:
