@@ -34,6 +34,14 @@ Extra modes (used to produce the committed counter summaries):
                         lora_group_bwd: one pass over X for all their U, one
                         GEMM over the stacked weights, the shared input's
                         gradient summed over them)
+  --norm                the linears that read a normalised input (the
+                        projection of attn_proj_4096; q/k/v and gate/up)
+                        run with the RMSNorm in front (lora_norm_linear_* /
+                        lora_norm_group_*: the layer reads the raw X, W is
+                        folded with the norm weight once before timing, dX
+                        is the gradient through the norm).  The norm's own
+                        O(M K) arithmetic is not counted in the FLOPs, its
+                        kernels' time is in the step.
 """
 from __future__ import annotations
 
@@ -62,6 +70,15 @@ KERNEL_SOURCES = ("lora_linear_layer_amd/csrc/lora_gemm.hpp", "lora_linear_layer
 GEMM_FWD, GEMM_DX = "lora_gemm forward", "lora_gemm dX"
 # linears that read the same input (decoder layer): q/k/v share X, gate/up share X
 SHARED_INPUT = {"q": "qkv", "k": "qkv", "v": "qkv", "gate": "gu", "up": "gu"}
+# linears whose input is an RMSNorm output: the attention projections behind
+# the attention norm and gate/up behind the MLP norm (o and down read the
+# attention and SwiGLU outputs); the single 4096 projection stands for q
+NORM_EPS = 1e-6
+NORM_KERNELS = ("norm_prep", "norm_fold", "norm_dx")
+
+
+def behind_norm(name: str) -> bool:
+    return name == "attn_proj_4096" or name.split("_")[-1] in SHARED_INPUT
 
 
 def parse(argv=None):
@@ -82,6 +99,8 @@ def parse(argv=None):
                          "(lora_tune_linear; the probing is outside the timed region)")
     ap.add_argument("--grouped", action="store_true",
                     help="linears sharing an input run as one grouped call (q/k/v, gate/up)")
+    ap.add_argument("--norm", action="store_true",
+                    help="RMSNorm in front of the linears that read a normalised input")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--traffic-from", default=None)
     return ap.parse_args(argv)
@@ -319,6 +338,24 @@ def add_outputs(lla, torch, wl, layer, dev):
     return layer
 
 
+def add_norm(lla, torch, wl, layer, dev, seed):
+    """RMSNorm in front of the linears behind_norm selects: one norm weight g
+    per shared input (the same tensor for q/k/v, and for gate/up), W folded
+    with it in place (once, before timing), a saved 1/rms buffer per linear."""
+    import workloads
+    gs = {}
+    for sh, d in zip(wl.linears, layer):
+        if not behind_norm(sh.name):
+            continue
+        key = SHARED_INPUT.get(sh.name.split("_")[-1], sh.name)
+        if key not in gs:
+            gs[key] = workloads.norm_weight_torch(sh.K, dev, torch.bfloat16, seed + len(gs))
+        d["g"] = gs[key]
+        lla.lora_fold_norm_weight(d["W"], d["g"], d["W"])
+        d["inv"] = torch.empty((sh.M,), dtype=torch.float32, device=dev)
+    return layer
+
+
 def group_layer(lla, torch, wl, layer, units, dev):
     """The per-linear inputs of one step regrouped as units: a group's W, A, B
     and dY stacked (copies made once, before any timing), its outputs H
@@ -335,6 +372,9 @@ def group_layer(lla, torch, wl, layer, units, dev):
              "W": torch.cat([d["W"] for d in ds]).contiguous(), "A": torch.cat([d["A"] for d in ds]).contiguous(),
              "B": torch.cat([d["B"] for d in ds]).contiguous(),
              "dY": torch.cat([d["dY"] for d in ds], dim=1).contiguous()}
+        if "g" in ds[0]:
+            g["g"] = ds[0]["g"]
+            g["inv"] = ds[0]["inv"]
         R = u.G * u.r
         g["H"] = torch.empty((u.M, u.N), dtype=torch.bfloat16, device=dev)
         g["U"] = torch.empty((u.M, R), dtype=torch.float32, device=dev)
@@ -353,14 +393,23 @@ class Stepper:
 
     def __init__(self, lla, torch, layers, dev):
         self.lla = lla
-        self.ws_bytes = max(lla.lora_group_workspace_size(d["gdesc"]) if "gdesc" in d
-                            else lla.lora_linear_workspace_size(d["desc"]) for layer in layers for d in layer)
+        self.ws_bytes = max(self.ws_size(d) for layer in layers for d in layer)
         self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=dev)
         self.current = None          # index of the linear being run (for the per-kernel timing pass)
 
-    def fwd(self, d):
+    def ws_size(self, d):
         lla = self.lla
         if "gdesc" in d:
+            return (lla.lora_norm_group_workspace_size if "g" in d else lla.lora_group_workspace_size)(d["gdesc"])
+        return (lla.lora_norm_linear_workspace_size if "g" in d else lla.lora_linear_workspace_size)(d["desc"])
+
+    def fwd(self, d):
+        lla = self.lla
+        if "g" in d:
+            f = lla.lora_norm_group_fwd if "gdesc" in d else lla.lora_norm_linear_fwd
+            f(d.get("gdesc") or d["desc"], NORM_EPS, d["X"], d["g"], d["W"], d["A"], d["B"], d["H"], d["U"],
+              d["inv"], ws=self.ws, ws_bytes=self.ws_bytes)
+        elif "gdesc" in d:
             lla.lora_group_fwd(d["gdesc"], d["X"], d["W"], d["A"], d["B"], d["H"], d["U"], ws=self.ws,
                                ws_bytes=self.ws_bytes)
         elif "codes" in d:
@@ -372,7 +421,11 @@ class Stepper:
 
     def bwd(self, d):
         lla = self.lla
-        if "gdesc" in d:
+        if "g" in d:
+            f = lla.lora_norm_group_bwd if "gdesc" in d else lla.lora_norm_linear_bwd
+            f(d.get("gdesc") or d["desc"], NORM_EPS, d["dY"], d["X"], d["g"], d["W"], d["A"], d["B"], d["U"],
+              d["inv"], d["dX"], d["dA"], d["dB"], ws=self.ws, ws_bytes=self.ws_bytes)
+        elif "gdesc" in d:
             lla.lora_group_bwd(d["gdesc"], d["dY"], d["X"], d["W"], d["A"], d["B"], d["U"], d["dX"], d["dA"],
                                d["dB"], ws=self.ws, ws_bytes=self.ws_bytes)
         elif "codes" in d:
@@ -515,6 +568,38 @@ def gemm_rooflines(units, kernel_us, traffic):
     return out
 
 
+def norm_bytes(u, label: str) -> int:
+    """Algorithmic HBM bytes of one launch of an RMSNorm row kernel.  The fold
+    of g into A reads A [G r x K] and g and writes A diag(g); the preparation
+    does that and also reads X once for 1/rms (M floats written); the
+    input-gradient correction reads the GEMM's output and X, and 1/rms, and
+    writes dX (bf16)."""
+    M, K, R = u.M, u.K, u.G * u.r
+    fold = 2 * R * K * 2 + 2 * K
+    if label == "norm_prep":
+        return 2 * M * K + 4 * M + fold
+    if label == "norm_dx":
+        return 3 * 2 * M * K + 4 * M
+    return fold
+
+
+def norm_rooflines(units, kernel_us):
+    """HBM rooflines of the RMSNorm row kernels from their measured durations."""
+    out = []
+    for (li, label), durs in sorted(kernel_us.items()):
+        if label not in NORM_KERNELS:
+            continue
+        u = units[li]
+        us = sum(durs) / len(durs)
+        b = norm_bytes(u, label)
+        gbs = b / (us * 1e-6) / 1e9
+        out.append({"kernel": f"{label} ({u.name})", "bound": "hbm", "achieved": round(gbs, 1),
+                    "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBPS, 4),
+                    "avg_launch_us": round(us, 2), "launches_per_step": len(durs),
+                    "algorithmic_bytes_per_launch": b})
+    return out
+
+
 def main(argv=None):
     args = parse(argv)
     if args.gpus != 1:
@@ -546,7 +631,10 @@ def main(argv=None):
             if sh.quant4:
                 d.update(workloads.quantize4_torch(d.pop("W").float()))
             layer.append(d)
-        sets.append(add_outputs(lla, torch, wl, share_inputs(wl, layer), dev))
+        layer = add_outputs(lla, torch, wl, share_inputs(wl, layer), dev)
+        if args.norm:
+            add_norm(lla, torch, wl, layer, dev, seed=7000 + 10 * si)
+        sets.append(layer)
     units = step_units(wl, args.grouped)
     if args.grouped:
         sets = [group_layer(lla, torch, wl, layer, units, dev) for layer in sets]
@@ -555,8 +643,8 @@ def main(argv=None):
     tuned = {}
     if args.tune:
         for u, d in zip(units, sets[0]):
-            if "gdesc" in d:
-                continue                      # grouped calls keep the built-in rules
+            if "gdesc" in d or "g" in d:
+                continue                      # grouped and norm calls keep the built-in rules
             wargs = (dict(Wq=d["codes"], absmax=d["absmax"], codebook=d["codebook"]) if "codes" in d
                      else dict(W=d["W"]))
             tuned[u.name] = lla.lora_tune_linear(d["desc"], d["X"], d["A"], d["B"], d["H"], d["U"], d["dY"], d["dX"],
@@ -634,7 +722,7 @@ def main(argv=None):
         ks = {k: round(sum(v) / len(v), 2) for (i, k), v in kernel_us.items() if i == li}
         per_linear.append({"name": u.name, "kernel_us": ks})
 
-    gemms = gemm_rooflines(units, kernel_us, load_traffic(wl.name))
+    gemms = gemm_rooflines(units, kernel_us, load_traffic(wl.name) if not args.norm else None)
     # dominant kernel: the GEMM with the largest measured time per step
     dominant = max(gemms, key=lambda g: g["avg_launch_us"] * g["launches_per_step"] / args.steps)
     p10, p50, p90 = (percentile(step_ms, q) for q in (0.1, 0.5, 0.9))
@@ -647,7 +735,9 @@ def main(argv=None):
         "data": "synthetic (seeded on-device normal draws; no dataset or checkpoint)",
         "config": {"workload": wl.name, "linears": [[l.name, l.M, l.K, l.N, l.r, l.alpha] for l in wl.linears],
                    "input_sets": args.input_sets, "description": wl.description,
-                   "calls": [u.name for u in units]},
+                   "calls": [u.name for u in units],
+                   "rmsnorm_in_front": [u.name for u in units if behind_norm(wl.linears[u.members[0]].name)]
+                   if args.norm else []},
         "tokens_per_s": round(tokens_s, 1), "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "step_ms_p10_p50_p90": [round(p10, 4), round(p50, 4), round(p90, 4)],
         "timed_kernels_ms_per_step": round(timer_ms_step, 4),
@@ -657,6 +747,8 @@ def main(argv=None):
         "roofline": dict(dominant),
         "gemm_rooflines": gemms,
     }
+    if args.norm:
+        out["norm_rooflines"] = norm_rooflines(units, kernel_us)
     if not args.no_dequant:
         out["hbm_kernels"] = [dequant_rate(lla, workloads, torch, dev, stream),
                               merge_rate(lla, torch, dev, stream, max(wl.linears, key=lambda l: l.N * l.K))]

@@ -218,6 +218,29 @@ lora_status lora_norm_linear_bwd(const lora_linear_desc* desc, float eps,
                                  void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * RMSNorm in front of a group of linears that share the normalised input (the
+ * q/k/v projections behind the attention norm, gate/up behind the MLP norm):
+ * the same operation for every member of a lora_group_desc, with the stacked
+ * layout of lora_group_fwd / _bwd; W_g is the stacked weight with g folded in
+ * (lora_fold_norm_weight over all N_total rows) and dX is the gradient with
+ * respect to the raw X of the summed members.  Workspace from
+ * lora_norm_group_workspace_size; errors as for lora_group_fwd / _bwd plus
+ * eps >= 0.
+ */
+lora_status lora_norm_group_workspace_size(const lora_group_desc* desc, size_t* bytes);
+
+lora_status lora_norm_group_fwd(const lora_group_desc* desc, float eps,
+                                const void* X, const void* g, const void* W_g, const void* A, const void* B,
+                                void* H, float* U_save, float* inv_rms_save,
+                                void* ws, size_t ws_bytes, void* stream);
+
+lora_status lora_norm_group_bwd(const lora_group_desc* desc, float eps,
+                                const void* dY, const void* X, const void* g, const void* W_g,
+                                const void* A, const void* B, const float* U_saved, const float* inv_rms_saved,
+                                void* dX, void* dA, void* dB,
+                                void* ws, size_t ws_bytes, void* stream);
+
+/*
  * 4-bit frozen weight (page "Unsloth — 微调 2-5x 加速", section "核心要点",
  * item 3: 4-bit weights are dequantised inside the matmul, not copied out
  * first).  W is replaced by

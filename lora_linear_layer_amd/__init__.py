@@ -8,7 +8,8 @@ from ._lib import (LIB_PATH, LORA_DTYPE_BF16, LORA_DTYPE_F32, LORA_FLAG_ACCUM_GR
 from .api import (Desc, GroupDesc, LoraError, lora_dequant4, lora_group_bwd, lora_group_fwd,  # noqa: F401
                   lora_group_workspace_size, lora_linear_buffer_ranges, lora_linear_bwd,
                   lora_linear_bwd_noalloc, lora_fold_norm_weight, lora_norm_linear_workspace_size,
-                  lora_norm_linear_fwd, lora_norm_linear_bwd,
+                  lora_norm_linear_fwd, lora_norm_linear_bwd, lora_norm_group_workspace_size,
+                  lora_norm_group_fwd, lora_norm_group_bwd,
                   lora_linear_fwd, lora_linear_workspace_size, lora_merge, lora_qlinear_bwd, lora_qlinear_fwd,
                   lora_set_kernel_timer, lora_tune_linear, lora_tuner_clear, lora_tuner_load,
                   lora_tuner_lookup, lora_tuner_save)
@@ -18,6 +19,7 @@ __all__ = [
     "lora_group_workspace_size", "lora_group_fwd", "lora_group_bwd",
     "lora_linear_bwd_noalloc", "LORA_NOALLOC_SCRATCH_BYTES",
     "lora_fold_norm_weight", "lora_norm_linear_workspace_size", "lora_norm_linear_fwd", "lora_norm_linear_bwd",
+    "lora_norm_group_workspace_size", "lora_norm_group_fwd", "lora_norm_group_bwd",
     "lora_qlinear_fwd", "lora_qlinear_bwd", "lora_dequant4", "lora_merge", "lora_linear_buffer_ranges",
     "lora_set_kernel_timer", "lora_tune_linear", "lora_tuner_lookup", "lora_tuner_save", "lora_tuner_load",
     "lora_tuner_clear", "load", "LIB_PATH",

@@ -31,6 +31,7 @@ EXPORTED = (
     "lora_qlinear_fwd", "lora_qlinear_bwd", "lora_dequant4", "lora_merge",
     "lora_linear_buffer_ranges", "lora_group_workspace_size", "lora_group_fwd", "lora_group_bwd",
     "lora_fold_norm_weight", "lora_norm_linear_workspace_size", "lora_norm_linear_fwd", "lora_norm_linear_bwd",
+    "lora_norm_group_workspace_size", "lora_norm_group_fwd", "lora_norm_group_bwd",
     "lora_tune_linear", "lora_tuner_lookup", "lora_tuner_save", "lora_tuner_load", "lora_tuner_clear",
     "lora_set_kernel_timer", "lora_status_string", "lora_last_error",
 )
@@ -107,6 +108,9 @@ def load() -> ctypes.CDLL:
         "lora_norm_linear_workspace_size": [dp, ctypes.POINTER(sz)],
         "lora_norm_linear_fwd": [dp, f32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "lora_norm_linear_bwd": [dp, f32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "lora_norm_group_workspace_size": [gp, ctypes.POINTER(sz)],
+        "lora_norm_group_fwd": [gp, f32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "lora_norm_group_bwd": [gp, f32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)

@@ -351,6 +351,59 @@ def lora_norm_linear_bwd(desc: Desc, eps: float, dY, X, g, W_g, A, B, U_saved, i
     _check(st, "lora_norm_linear_bwd")
 
 
+def _check_norm_group(gd: GroupDesc, **ts):
+    M, K, N, R, r = gd.M, gd.K, gd.N_total, gd.rank_total, gd.r
+    bf = (torch.bfloat16,)
+    spec = {"X": ((M, K), bf), "g": ((K,), bf), "W_g": ((N, K), bf), "A": ((R, K), bf), "B": ((N, r), bf),
+            "H": ((M, N), bf), "dY": ((M, N), bf), "dX": ((M, K), bf), "dA": ((R, K), bf), "dB": ((N, r), bf),
+            "U_save": ((M, R), (torch.float32,)), "U_saved": ((M, R), (torch.float32,)),
+            "inv_rms_save": ((M,), (torch.float32,)), "inv_rms_saved": ((M,), (torch.float32,))}
+    for name, t in ts.items():
+        _expect(t, name, *spec[name])
+    _same_gpu(**ts)
+
+
+def lora_norm_group_workspace_size(desc: GroupDesc) -> int:
+    out = ctypes.c_size_t(0)
+    d = desc.c()
+    _check(_lib.load().lora_norm_group_workspace_size(ctypes.byref(d), ctypes.byref(out)),
+           "lora_norm_group_workspace_size")
+    return int(out.value)
+
+
+def lora_norm_group_fwd(desc: GroupDesc, eps: float, X, g, W_g, A, B, H, U_save=None, inv_rms_save=None, ws=None,
+                        ws_bytes=None, stream=None):
+    """Every member of the group behind one RMSNorm of X (stacked layout)."""
+    _check_norm_group(desc, X=X, g=g, W_g=W_g, A=A, B=B, H=H, U_save=U_save, inv_rms_save=inv_rms_save)
+    if ws is None:
+        ws_bytes = lora_norm_group_workspace_size(desc)
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=X.device)
+    elif ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    d = desc.c()
+    st = _lib.load().lora_norm_group_fwd(ctypes.byref(d), float(eps), _ptr(X), _ptr(g), _ptr(W_g), _ptr(A), _ptr(B),
+                                         _ptr(H), _ptr(U_save), _ptr(inv_rms_save), _ptr(ws), ws_bytes,
+                                         _stream(stream))
+    _check(st, "lora_norm_group_fwd")
+
+
+def lora_norm_group_bwd(desc: GroupDesc, eps: float, dY, X, g, W_g, A, B, U_saved, inv_rms_saved, dX, dA, dB,
+                        ws=None, ws_bytes=None, stream=None):
+    """dX through the norm of the summed members; dA, dB per member."""
+    _check_norm_group(desc, dY=dY, X=X, g=g, W_g=W_g, A=A, B=B, U_saved=U_saved, inv_rms_saved=inv_rms_saved,
+                      dX=dX, dA=dA, dB=dB)
+    if ws is None:
+        ws_bytes = lora_norm_group_workspace_size(desc)
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dY.device)
+    elif ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    d = desc.c()
+    st = _lib.load().lora_norm_group_bwd(ctypes.byref(d), float(eps), _ptr(dY), _ptr(X), _ptr(g), _ptr(W_g),
+                                         _ptr(A), _ptr(B), _ptr(U_saved), _ptr(inv_rms_saved), _ptr(dX), _ptr(dA),
+                                         _ptr(dB), _ptr(ws), ws_bytes, _stream(stream))
+    _check(st, "lora_norm_group_bwd")
+
+
 _TUNED_FIELDS = ("fwd_split", "bwd_split", "rank_div", "z_div_fwd", "z_div_bwd", "fwd_us", "bwd_us",
                  "default_fwd_us", "default_bwd_us")
 

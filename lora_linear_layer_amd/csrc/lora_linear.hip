@@ -1202,12 +1202,41 @@ lora_status lora_qlinear_bwd(const lora_linear_desc* desc, const void* dY, const
 }
 
 // ---------------------------------------------------------------- RMSNorm in front
+// One launch of norm_prep_kernel: 1/rms of the M rows of X (none when X is
+// NULL), and out = bf16(in diag(g)) for R rows of K columns.
+static void launch_norm_prep(const uint16_t* X, float* inv, int64_t M, int64_t K, float eps, const uint16_t* in,
+                             const uint16_t* g, uint16_t* out, int64_t R, hipStream_t s) {
+    NormPrepArgs a{};
+    a.X = X;
+    a.inv = inv;
+    a.M = (int)M;
+    a.K = (int)K;
+    a.rms_blocks = X ? (int)cdiv(M, 4) : 0;
+    a.eps = eps;
+    a.in = in;
+    a.g = g;
+    a.out = out;
+    a.R = R;
+    const int64_t blocks = a.rms_blocks + cdiv(R * K / 8, 256);
+    if (X) LAUNCH("norm_prep", norm_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    else LAUNCH("norm_fold", norm_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
+}
+
+static void launch_norm_dx(uint16_t* dX, const uint16_t* X, const float* inv, int64_t M, int64_t K, hipStream_t s) {
+    const dim3 grid((unsigned)cdiv(M, 4));
+    if (K <= 8 * kRowChunk) LAUNCH("norm_dx", norm_dx_kernel<8>, grid, dim3(256), 0, s, dX, X, inv, (int)M, (int)K);
+    else if (K <= 16 * kRowChunk)
+        LAUNCH("norm_dx", norm_dx_kernel<16>, grid, dim3(256), 0, s, dX, X, inv, (int)M, (int)K);
+    else LAUNCH("norm_dx", norm_dx_kernel<0>, grid, dim3(256), 0, s, dX, X, inv, (int)M, (int)K);
+}
+
+static lora_status check_eps(float eps);
+
 static lora_status check_norm(const lora_linear_desc* desc, float eps) {
     lora_status st = check_desc(desc, false);
     if (st != LORA_OK) return st;
     if (desc->dtype != LORA_DTYPE_BF16) return fail(LORA_ERR_UNSUPPORTED, "the RMSNorm path is bf16 only");
-    if (!std::isfinite(eps) || eps < 0.f) return fail(LORA_ERR_INVALID_ARG, "eps must be finite and >= 0");
-    return LORA_OK;
+    return check_eps(eps);
 }
 
 static Shape norm_shape(const lora_linear_desc& d) {
@@ -1232,25 +1261,23 @@ lora_status lora_fold_norm_weight(const void* W, const void* g, int64_t N, int64
     if (st != LORA_OK) return st;
     if (W_out == g) return fail(LORA_ERR_INVALID_ARG, "output W_out aliases g");
     hipStream_t s = static_cast<hipStream_t>(stream);
-    LAUNCH("scale_cols", scale_cols_kernel, dim3((unsigned)cdiv(N * K / 8, 256)), dim3(256), 0, s,
-           static_cast<const uint16_t*>(W), static_cast<const uint16_t*>(g), static_cast<uint16_t*>(W_out), N, (int)K);
-    LAUNCH_CHECK("scale_cols");
+    launch_norm_prep(nullptr, nullptr, 0, K, 0.f, static_cast<const uint16_t*>(W), static_cast<const uint16_t*>(g),
+                     static_cast<uint16_t*>(W_out), N, s);
+    LAUNCH_CHECK("norm_prep");
     return ok();
 }
 
-lora_status lora_norm_linear_fwd(const lora_linear_desc* desc, float eps, const void* X, const void* g,
-                                 const void* W_g, const void* A, const void* B, void* H, float* U_save,
-                                 float* inv_rms_save, void* ws, size_t ws_bytes, void* stream) {
-    lora_status st = check_norm(desc, eps);
-    if (st != LORA_OK) return st;
-    st = check_ptrs({{X, "X"}, {g, "g"}, {W_g, "W_g"}, {A, "A"}, {B, "B"}, {H, "H"}},
-                    {{U_save, "U_save"}, {inv_rms_save, "inv_rms_save"}});
+// The RMSNorm path for one layer or a group sharing the input (d.norm set).
+static lora_status norm_fwd(const Shape& d, const void* X, const void* g, const void* W_g, const void* A,
+                            const void* B, void* H, float* U_save, float* inv_rms_save, void* ws, size_t ws_bytes,
+                            float eps, void* stream) {
+    lora_status st = check_ptrs({{X, "X"}, {g, "g"}, {W_g, "W_g"}, {A, "A"}, {B, "B"}, {H, "H"}},
+                                {{U_save, "U_save"}, {inv_rms_save, "inv_rms_save"}});
     if (st != LORA_OK) return st;
     st = check_no_alias({{H, "H"}, {U_save, "U_save"}, {inv_rms_save, "inv_rms_save"}},
                         {{X, "X"}, {g, "g"}, {W_g, "W_g"}, {A, "A"}, {B, "B"}, {H, "H"}, {U_save, "U_save"},
                          {inv_rms_save, "inv_rms_save"}, {ws, "ws"}});
     if (st != LORA_OK) return st;
-    const Shape d = norm_shape(*desc);
     st = check_ws(d, ws, ws_bytes);
     if (st != LORA_OK) return st;
     const Plan plan = make_plan(d);
@@ -1259,12 +1286,62 @@ lora_status lora_norm_linear_fwd(const lora_linear_desc* desc, float eps, const 
     float* const inv = inv_rms_save ? inv_rms_save : reinterpret_cast<float*>(wsb + plan.off_inv);
     uint16_t* const Ag = reinterpret_cast<uint16_t*>(wsb + plan.off_ag);
     const uint16_t* const X16 = static_cast<const uint16_t*>(X);
-    const uint16_t* const g16 = static_cast<const uint16_t*>(g);
-    LAUNCH("rms_inv", rms_inv_kernel, dim3((unsigned)cdiv(d.M, 4)), dim3(256), 0, s, X16, inv, (int)d.M, (int)d.K, eps);
-    LAUNCH("scale_cols", scale_cols_kernel, dim3((unsigned)cdiv(d.r * d.K / 8, 256)), dim3(256), 0, s,
-           static_cast<const uint16_t*>(A), g16, Ag, d.r, (int)d.K);
-    LAUNCH_CHECK("rms_inv, scale_cols");
+    const int64_t rg = d.rg();
+    launch_norm_prep(X16, inv, d.M, d.K, eps, static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(g), Ag,
+                     rg, s);
+    LAUNCH_CHECK("norm_prep");
     return fwd_bf16(d, false, X, W_g, nullptr, nullptr, nullptr, Ag, B, H, U_save, ws, s, Tuning{}, inv);
+}
+
+static lora_status norm_bwd(const Shape& d, const void* dY, const void* X, const void* g, const void* W_g,
+                            const void* A, const void* B, const float* U_saved, const float* inv_rms_saved, void* dX,
+                            void* dA, void* dB, void* ws, size_t ws_bytes, float eps, void* stream) {
+    lora_status st = check_ptrs({{dY, "dY"}, {X, "X"}, {g, "g"}, {W_g, "W_g"}, {A, "A"}, {B, "B"}, {dA, "dA"},
+                                 {dB, "dB"}},
+                                {{U_saved, "U_saved"}, {inv_rms_saved, "inv_rms_saved"}, {dX, "dX"}});
+    if (st != LORA_OK) return st;
+    st = check_no_alias({{dX, "dX"}, {dA, "dA"}, {dB, "dB"}},
+                        {{dY, "dY"}, {X, "X"}, {g, "g"}, {W_g, "W_g"}, {A, "A"}, {B, "B"}, {U_saved, "U_saved"},
+                         {inv_rms_saved, "inv_rms_saved"}, {dX, "dX"}, {dA, "dA"}, {dB, "dB"}, {ws, "ws"}});
+    if (st != LORA_OK) return st;
+    st = check_ws(d, ws, ws_bytes);
+    if (st != LORA_OK) return st;
+    const Plan plan = make_plan(d);
+    char* const wsb = static_cast<char*>(ws);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const uint16_t* const X16 = static_cast<const uint16_t*>(X);
+    const uint16_t* const g16 = static_cast<const uint16_t*>(g);
+    const int64_t rg = d.rg();
+    // 1/rms (unless saved by the forward) and A diag(g) in one launch
+    float* const inv_ws = reinterpret_cast<float*>(wsb + plan.off_inv);
+    const float* const inv = inv_rms_saved ? inv_rms_saved : inv_ws;
+    uint16_t* const Ag = reinterpret_cast<uint16_t*>(wsb + plan.off_ag);
+    launch_norm_prep(inv_rms_saved ? nullptr : X16, inv_ws, d.M, d.K, eps, static_cast<const uint16_t*>(A), g16, Ag,
+                     rg, s);
+    LAUNCH_CHECK("norm_prep");
+    // dY W_g + s V A_g into dX, dA = s g (inv V)^T X, dB = s dY^T U
+    st = bwd_bf16(d, false, dY, X, W_g, nullptr, nullptr, nullptr, Ag, B, U_saved, dX, dA, dB, ws, s, Tuning{}, inv,
+                  g16);
+    if (st != LORA_OK) return st;
+    if (dX) {
+        // through the norm: dX = inv D - X (inv^3 / K) <D, X>, D = dY W_g + s V A_g
+        launch_norm_dx(static_cast<uint16_t*>(dX), X16, inv, d.M, d.K, s);
+        LAUNCH_CHECK("norm_dx");
+    }
+    return ok();
+}
+
+static lora_status check_eps(float eps) {
+    if (!std::isfinite(eps) || eps < 0.f) return fail(LORA_ERR_INVALID_ARG, "eps must be finite and >= 0");
+    return LORA_OK;
+}
+
+lora_status lora_norm_linear_fwd(const lora_linear_desc* desc, float eps, const void* X, const void* g,
+                                 const void* W_g, const void* A, const void* B, void* H, float* U_save,
+                                 float* inv_rms_save, void* ws, size_t ws_bytes, void* stream) {
+    lora_status st = check_norm(desc, eps);
+    if (st != LORA_OK) return st;
+    return norm_fwd(norm_shape(*desc), X, g, W_g, A, B, H, U_save, inv_rms_save, ws, ws_bytes, eps, stream);
 }
 
 lora_status lora_norm_linear_bwd(const lora_linear_desc* desc, float eps, const void* dY, const void* X,
@@ -1273,43 +1350,42 @@ lora_status lora_norm_linear_bwd(const lora_linear_desc* desc, float eps, const 
                                  void* stream) {
     lora_status st = check_norm(desc, eps);
     if (st != LORA_OK) return st;
-    st = check_ptrs({{dY, "dY"}, {X, "X"}, {g, "g"}, {W_g, "W_g"}, {A, "A"}, {B, "B"}, {dA, "dA"}, {dB, "dB"}},
-                    {{U_saved, "U_saved"}, {inv_rms_saved, "inv_rms_saved"}, {dX, "dX"}});
+    return norm_bwd(norm_shape(*desc), dY, X, g, W_g, A, B, U_saved, inv_rms_saved, dX, dA, dB, ws, ws_bytes, eps,
+                    stream);
+}
+
+static Shape norm_group_shape(const lora_group_desc& gd) {
+    Shape s = shape_of(gd);
+    s.norm = true;
+    return s;
+}
+
+lora_status lora_norm_group_workspace_size(const lora_group_desc* desc, size_t* bytes) {
+    if (!bytes) return fail(LORA_ERR_INVALID_ARG, "bytes is NULL");
+    lora_status st = check_group(desc);
     if (st != LORA_OK) return st;
-    st = check_no_alias({{dX, "dX"}, {dA, "dA"}, {dB, "dB"}},
-                        {{dY, "dY"}, {X, "X"}, {g, "g"}, {W_g, "W_g"}, {A, "A"}, {B, "B"}, {U_saved, "U_saved"},
-                         {inv_rms_saved, "inv_rms_saved"}, {dX, "dX"}, {dA, "dA"}, {dB, "dB"}, {ws, "ws"}});
-    if (st != LORA_OK) return st;
-    const Shape d = norm_shape(*desc);
-    st = check_ws(d, ws, ws_bytes);
-    if (st != LORA_OK) return st;
-    const Plan plan = make_plan(d);
-    char* const wsb = static_cast<char*>(ws);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const uint16_t* const X16 = static_cast<const uint16_t*>(X);
-    const uint16_t* const g16 = static_cast<const uint16_t*>(g);
-    const float* inv = inv_rms_saved;
-    if (!inv) {
-        float* const w = reinterpret_cast<float*>(wsb + plan.off_inv);
-        LAUNCH("rms_inv", rms_inv_kernel, dim3((unsigned)cdiv(d.M, 4)), dim3(256), 0, s, X16, w, (int)d.M, (int)d.K,
-               eps);
-        inv = w;
-    }
-    uint16_t* const Ag = reinterpret_cast<uint16_t*>(wsb + plan.off_ag);
-    LAUNCH("scale_cols", scale_cols_kernel, dim3((unsigned)cdiv(d.r * d.K / 8, 256)), dim3(256), 0, s,
-           static_cast<const uint16_t*>(A), g16, Ag, d.r, (int)d.K);
-    LAUNCH_CHECK("rms_inv, scale_cols");
-    // dY W_g + s V A_g into dX, dA = s g (inv V)^T X, dB = s dY^T U
-    st = bwd_bf16(d, false, dY, X, W_g, nullptr, nullptr, nullptr, Ag, B, U_saved, dX, dA, dB, ws, s, Tuning{}, inv,
-                  g16);
-    if (st != LORA_OK) return st;
-    if (dX) {
-        // through the norm: dX = inv D - X (inv^3 / K) <D, X>, D = dY W_g + s V A_g
-        LAUNCH("norm_dx", norm_dx_kernel, dim3((unsigned)cdiv(d.M, 4)), dim3(256), 0, s, static_cast<uint16_t*>(dX),
-               X16, inv, (int)d.M, (int)d.K);
-        LAUNCH_CHECK("norm_dx");
-    }
+    *bytes = make_plan(norm_group_shape(*desc)).total;
     return ok();
+}
+
+lora_status lora_norm_group_fwd(const lora_group_desc* desc, float eps, const void* X, const void* g,
+                                const void* W_g, const void* A, const void* B, void* H, float* U_save,
+                                float* inv_rms_save, void* ws, size_t ws_bytes, void* stream) {
+    lora_status st = check_group(desc);
+    if (st == LORA_OK) st = check_eps(eps);
+    if (st != LORA_OK) return st;
+    return norm_fwd(norm_group_shape(*desc), X, g, W_g, A, B, H, U_save, inv_rms_save, ws, ws_bytes, eps, stream);
+}
+
+lora_status lora_norm_group_bwd(const lora_group_desc* desc, float eps, const void* dY, const void* X,
+                                const void* g, const void* W_g, const void* A, const void* B, const float* U_saved,
+                                const float* inv_rms_saved, void* dX, void* dA, void* dB, void* ws, size_t ws_bytes,
+                                void* stream) {
+    lora_status st = check_group(desc);
+    if (st == LORA_OK) st = check_eps(eps);
+    if (st != LORA_OK) return st;
+    return norm_bwd(norm_group_shape(*desc), dY, X, g, W_g, A, B, U_saved, inv_rms_saved, dX, dA, dB, ws, ws_bytes,
+                    eps, stream);
 }
 
 lora_status lora_tune_linear(const lora_linear_desc* desc, int32_t quant, const void* X, const void* W,

@@ -26,37 +26,66 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-// inv[m] = 1 / sqrt(mean_k X[m][k]^2 + eps): one wave per row (K % 8 == 0),
-// 16-byte loads, float32 sums.
-__global__ __launch_bounds__(256) void rms_inv_kernel(const uint16_t* __restrict__ X, float* __restrict__ inv,
-                                                      int M, int K, float eps) {
-    const int lane = threadIdx.x & 63;
-    const int m = (int)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (m >= M) return;
-    const uint16_t* row = X + (size_t)m * K;
-    float ss = 0.f;
-    for (int c = lane * 8; c < K; c += 64 * 8) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(row + c);
+constexpr int kRowChunk = 64 * 8;      // elements one wave covers with one 16-byte load per lane
+
+__device__ __forceinline__ float dot_bf16x8(u32x4 a, u32x4 b, float acc) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float lo = bf16_bits_to_f32(v[i] & 0xFFFFu), hi = bf16_bits_to_f32(v[i] >> 16);
-            ss += lo * lo + hi * hi;
-        }
+    for (int i = 0; i < 4; ++i) {
+        acc += bf16_bits_to_f32(a[i] & 0xFFFFu) * bf16_bits_to_f32(b[i] & 0xFFFFu);
+        acc += bf16_bits_to_f32(a[i] >> 16) * bf16_bits_to_f32(b[i] >> 16);
     }
-    ss = wave_sum(ss);
-    if (lane == 0) inv[m] = 1.0f / sqrtf(ss / (float)K + eps);
+    return acc;
 }
 
-// out[i][k] = bf16(in[i][k] * g[k]) for R rows of K columns (K % 8 == 0): the
-// norm weight folded into W (once) or A (per call).  out may be in: each
-// thread reads its 8 elements before it writes them.
-__global__ __launch_bounds__(256) void scale_cols_kernel(const uint16_t* in, const uint16_t* __restrict__ g,
-                                                         uint16_t* out, int64_t R, int K) {
-    const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;     // 8 consecutive elements
-    if (e >= R * K) return;
-    const int k = (int)(e % K);
-    const u32x4 v = *reinterpret_cast<const u32x4*>(in + e);
-    const u32x4 w = *reinterpret_cast<const u32x4*>(g + k);
+// Sum of squares of one bf16 row of K elements (K % 8 == 0) over one wave,
+// NV 16-byte loads per lane issued together (the row's bytes in flight at once).
+template <int NV>
+__device__ __forceinline__ float row_sumsq(const uint16_t* row, int K, int lane) {
+    float ss = 0.f;
+    for (int c0 = lane * 8; c0 < K; c0 += kRowChunk * NV) {
+        u32x4 v[NV];
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+            const int c = c0 + u * kRowChunk;
+            v[u] = c < K ? *reinterpret_cast<const u32x4*>(row + c) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < NV; ++u) ss = dot_bf16x8(v[u], v[u], ss);
+    }
+    return wave_sum(ss);
+}
+
+// The norm's per-call preparation, one launch: blocks [0, rms_blocks) write
+// inv[m] = 1 / sqrt(mean_k X[m][k]^2 + eps) (one wave per row, four rows per
+// block; skipped when rms_blocks = 0); the rest write out[i][k] = bf16(in[i][k]
+// g[k]) for R rows of K columns, 8 elements per thread (A diag(g), or W diag(g)
+// when the weight is folded).  out may be in: each thread reads its 8
+// elements before it writes them.
+struct NormPrepArgs {
+    const uint16_t* X;
+    float* inv;
+    int M, K, rms_blocks;
+    float eps;
+    const uint16_t* in;
+    const uint16_t* g;
+    uint16_t* out;
+    int64_t R;
+};
+
+__global__ __launch_bounds__(256) void norm_prep_kernel(const NormPrepArgs a) {
+    if ((int)blockIdx.x < a.rms_blocks) {
+        const int lane = threadIdx.x & 63;
+        const int m = (int)blockIdx.x * 4 + (threadIdx.x >> 6);
+        if (m >= a.M) return;
+        const float ss = row_sumsq<8>(a.X + (size_t)m * a.K, a.K, lane);
+        if (lane == 0) a.inv[m] = 1.0f / sqrtf(ss / (float)a.K + a.eps);
+        return;
+    }
+    const int64_t e = ((int64_t)(blockIdx.x - a.rms_blocks) * 256 + threadIdx.x) * 8;
+    if (e >= a.R * a.K) return;
+    const int k = (int)(e % a.K);
+    const u32x4 v = *reinterpret_cast<const u32x4*>(a.in + e);
+    const u32x4 w = *reinterpret_cast<const u32x4*>(a.g + k);
     u32x4 o;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -64,13 +93,27 @@ __global__ __launch_bounds__(256) void scale_cols_kernel(const uint16_t* in, con
         const float hi = bf16_bits_to_f32(v[i] >> 16) * bf16_bits_to_f32(w[i] >> 16);
         o[i] = pack_bf16x2(lo, hi);
     }
-    *reinterpret_cast<u32x4*>(out + e) = o;
+    *reinterpret_cast<u32x4*>(a.out + e) = o;
 }
 
 // The norm's input gradient, in place: dX[m][k] = inv[m] D[m][k] - X[m][k] c[m]
 // with c[m] = inv[m]^3 / K sum_k D[m][k] X[m][k]; D arrives in dX (bf16).  One
-// wave per row: the row's dot product, then the update (the row's second
-// read is served by the caches).
+// wave per row.  NV > 0 (K <= NV * 512): the row of D and of X is loaded once
+// into registers, all loads issued together, then the dot product and the
+// update.  NV = 0: any K, two streamed passes (the second read served by the
+// caches).
+__device__ __forceinline__ u32x4 norm_dx_apply(u32x4 d, u32x4 x, float iv, float cm) {
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float lo = iv * bf16_bits_to_f32(d[i] & 0xFFFFu) - bf16_bits_to_f32(x[i] & 0xFFFFu) * cm;
+        const float hi = iv * bf16_bits_to_f32(d[i] >> 16) - bf16_bits_to_f32(x[i] >> 16) * cm;
+        o[i] = pack_bf16x2(lo, hi);
+    }
+    return o;
+}
+
+template <int NV>
 __global__ __launch_bounds__(256) void norm_dx_kernel(uint16_t* __restrict__ dX, const uint16_t* __restrict__ X,
                                                       const float* __restrict__ inv, int M, int K) {
     const int lane = threadIdx.x & 63;
@@ -78,30 +121,50 @@ __global__ __launch_bounds__(256) void norm_dx_kernel(uint16_t* __restrict__ dX,
     if (m >= M) return;
     uint16_t* drow = dX + (size_t)m * K;
     const uint16_t* xrow = X + (size_t)m * K;
-    float dot = 0.f;
-    for (int c = lane * 8; c < K; c += 64 * 8) {
-        const u32x4 d = *reinterpret_cast<const u32x4*>(drow + c);
-        const u32x4 x = *reinterpret_cast<const u32x4*>(xrow + c);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            dot += bf16_bits_to_f32(d[i] & 0xFFFFu) * bf16_bits_to_f32(x[i] & 0xFFFFu);
-            dot += bf16_bits_to_f32(d[i] >> 16) * bf16_bits_to_f32(x[i] >> 16);
-        }
-    }
-    dot = wave_sum(dot);
     const float iv = inv[m];
-    const float cm = iv * iv * iv / (float)K * dot;
-    for (int c = lane * 8; c < K; c += 64 * 8) {
-        const u32x4 d = *reinterpret_cast<const u32x4*>(drow + c);
-        const u32x4 x = *reinterpret_cast<const u32x4*>(xrow + c);
-        u32x4 o;
+    if constexpr (NV > 0) {
+        u32x4 d[NV], x[NV];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float lo = iv * bf16_bits_to_f32(d[i] & 0xFFFFu) - bf16_bits_to_f32(x[i] & 0xFFFFu) * cm;
-            const float hi = iv * bf16_bits_to_f32(d[i] >> 16) - bf16_bits_to_f32(x[i] >> 16) * cm;
-            o[i] = pack_bf16x2(lo, hi);
+        for (int u = 0; u < NV; ++u) {
+            const int c = lane * 8 + u * kRowChunk;
+            d[u] = c < K ? *reinterpret_cast<const u32x4*>(drow + c) : u32x4{0u, 0u, 0u, 0u};
+            x[u] = c < K ? *reinterpret_cast<const u32x4*>(xrow + c) : u32x4{0u, 0u, 0u, 0u};
         }
-        *reinterpret_cast<u32x4*>(drow + c) = o;
+        float dot = 0.f;
+#pragma unroll
+        for (int u = 0; u < NV; ++u) dot = dot_bf16x8(d[u], x[u], dot);
+        dot = wave_sum(dot);
+        const float cm = iv * iv * iv / (float)K * dot;
+        // keep the row packed between the two uses: without this the compiler
+        // holds all its float32 conversions live and the kernel spills
+#pragma unroll
+        for (int u = 0; u < NV; ++u) asm volatile("" : "+v"(d[u]), "+v"(x[u]));
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+            const int c = lane * 8 + u * kRowChunk;
+            if (c < K) *reinterpret_cast<u32x4*>(drow + c) = norm_dx_apply(d[u], x[u], iv, cm);
+        }
+    } else {
+        constexpr int U = 4;
+        float dot = 0.f;
+        for (int c0 = lane * 8; c0 < K; c0 += kRowChunk * U) {
+            u32x4 d[U], x[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int c = c0 + u * kRowChunk;
+                d[u] = c < K ? *reinterpret_cast<const u32x4*>(drow + c) : u32x4{0u, 0u, 0u, 0u};
+                x[u] = c < K ? *reinterpret_cast<const u32x4*>(xrow + c) : u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) dot = dot_bf16x8(d[u], x[u], dot);
+        }
+        dot = wave_sum(dot);
+        const float cm = iv * iv * iv / (float)K * dot;
+        for (int c = lane * 8; c < K; c += kRowChunk) {
+            const u32x4 d = *reinterpret_cast<const u32x4*>(drow + c);
+            const u32x4 x = *reinterpret_cast<const u32x4*>(xrow + c);
+            *reinterpret_cast<u32x4*>(drow + c) = norm_dx_apply(d, x, iv, cm);
+        }
     }
 }
 

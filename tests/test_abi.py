@@ -323,6 +323,23 @@ def test_norm_calls_validate_before_any_hip_call():
     assert L.lora_fold_norm_weight(MISALIGNED, p[1], 128, 256, p[2], None) == _lib.LORA_ERR_MISALIGNED
 
 
+def test_norm_group_calls_validate_before_any_hip_call():
+    L = lib()
+    gd = lla.GroupDesc(64, 256, (256, 64), 16, 32.0)
+    d = gd.c()
+    need = lla.lora_norm_group_workspace_size(gd)
+    assert need > lla.lora_group_workspace_size(gd)
+    p = [ALIGNED + 0x100 * i for i in range(16)]
+    fwd, bwd = L.lora_norm_group_fwd, L.lora_norm_group_bwd
+    assert fwd(ctypes.byref(d), -1.0, *p[:6], None, None, p[9], need, None) == _lib.LORA_ERR_INVALID_ARG
+    assert fwd(ctypes.byref(d), 1e-6, *p[:5], None, None, None, p[9], need, None) == _lib.LORA_ERR_INVALID_ARG
+    assert fwd(ctypes.byref(d), 1e-6, *p[:6], None, None, p[9], need - 1, None) == _lib.LORA_ERR_WORKSPACE_TOO_SMALL
+    assert bwd(ctypes.byref(d), 1e-6, *p[:6], None, None, p[0], p[7], p[8], p[9], need,
+               None) == _lib.LORA_ERR_INVALID_ARG                                                  # dX aliases dY
+    bad = lla.GroupDesc(64, 256, (256, 64), 16, 32.0, dtype=lla.LORA_DTYPE_F32).c()
+    assert fwd(ctypes.byref(bad), 1e-6, *p[:6], None, None, p[9], need, None) == _lib.LORA_ERR_UNSUPPORTED
+
+
 # ------------------------------------------------------------ tuning cache (host only)
 def test_tuner_cache_file_round_trip(tmp_path):
     """Entries loaded from a cache file are found for their (architecture,

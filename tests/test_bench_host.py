@@ -133,3 +133,24 @@ def test_grouped_units_and_counts():
         mem = [wl.linears[i] for i in u.members]
         for label in (bench.GEMM_FWD, bench.GEMM_DX):
             assert bench.gemm_flops(u, label) == sum(bench.gemm_flops(m, label) for m in mem)
+
+
+def test_norm_selection_and_row_kernel_bytes():
+    """--norm puts the RMSNorm in front of the linears that read a normalised
+    input (q/k/v, gate/up, the single 4096 projection), not o or down; the row
+    kernels' algorithmic bytes: 1/rms reads X once, the correction reads the
+    GEMM output and X and writes dX, the A fold reads and writes G r x K."""
+    dec = [l.name for l in workloads.workload("decoder_layer_r64").linears]
+    assert [n for n in dec if bench.behind_norm(n)] == ["decoder_q", "decoder_k", "decoder_v", "decoder_gate",
+                                                        "decoder_up"]
+    assert bench.behind_norm("attn_proj_4096")
+    assert not any(bench.behind_norm(l.name) for l in workloads.workload("qlora_28672").linears)
+    u = bench.Unit("qkv", 4096, 4096, 6144, 64, 16.0, 3)
+    fold = 4 * 192 * 4096 + 2 * 4096
+    assert bench.norm_bytes(u, "norm_fold") == fold
+    assert bench.norm_bytes(u, "norm_prep") == 2 * 4096 * 4096 + 4 * 4096 + fold
+    assert bench.norm_bytes(u, "norm_dx") == 6 * 4096 * 4096 + 4 * 4096
+    ks = {(0, "norm_prep"): [10.0, 10.0], (0, "norm_dx"): [20.0], (0, "lora_gemm forward"): [100.0]}
+    rows = bench.norm_rooflines([u], ks)
+    assert [r["kernel"] for r in rows] == ["norm_dx (qkv)", "norm_prep (qkv)"]
+    assert rows[1]["achieved"] == pytest.approx((2 * 4096 * 4096 + 4 * 4096 + fold) / 10e-6 / 1e9, rel=1e-3)

@@ -94,3 +94,56 @@ def test_decoder_layer_grouped_as_benched():
         print(f"  {u.name}: graded errors {errs}", flush=True)
         bad = {k: e for k, e in errs.items() if not e <= BF16_TOL}
         assert not bad, f"{u.name}: {bad} exceed {BF16_TOL}"
+
+
+def test_decoder_layer_grouped_norm_as_benched():
+    """bench.py --grouped --norm: q/k/v and gate/up as grouped calls behind an
+    RMSNorm each (W folded with g in place, the layer reading the raw X), o and
+    down plain.  Members against oracle.norm_forward / norm_backward with the
+    host copy of g; a group's dX against the sum of its members' input
+    gradients; graded bound."""
+    import lora_linear_layer_amd as lla
+    wl = workloads.workload("decoder_layer_r64")
+    dev = torch.device("cuda:0")
+    inps = [workloads.make_linear_inputs(sh) for sh in wl.linears]
+    bench.share_inputs(wl, inps)
+    layer = [device_inputs(inp, "bf16") for inp in inps]
+    bench.share_inputs(wl, layer)
+    bench.add_outputs(lla, torch, wl, layer, dev)
+    bench.add_norm(lla, torch, wl, layer, dev, seed=7000)
+    units = bench.step_units(wl, True)
+    glayer = bench.group_layer(lla, torch, wl, layer, units, dev)
+    stepper = bench.Stepper(lla, torch, [glayer], dev)
+    print(f"grouped decoder layer with RMSNorm: calls {[u.name for u in units]}", flush=True)
+    stepper.step(glayer)
+    torch.cuda.synchronize()
+    eps = bench.NORM_EPS
+    for u, d in zip(units, glayer):
+        got = {k: to_np(d[k]) for k in OUTPUTS}
+        mem = [wl.linears[i] for i in u.members]
+        mi = [inps[i] for i in u.members]
+        s = mem[0].scale
+        X = mi[0]["X"]
+        errs = {}
+        if "g" in d:
+            g = to_np(d["g"])
+            dX = 0.0
+            n0 = 0
+            for k, (sh, m) in enumerate(zip(mem, mi)):
+                H, U, _ = oracle.norm_forward(X, g, eps, m["W"], m["A"], m["B"], s)
+                dXk, dA, dB = oracle.norm_backward(m["dY"], X, g, eps, m["W"], m["A"], m["B"], s)
+                dX = dX + dXk
+                errs[f"{sh.name} H"] = rel_err(got["H"][:, n0:n0 + sh.N], H)
+                errs[f"{sh.name} U"] = rel_err(got["U"][:, k * u.r:(k + 1) * u.r], U)
+                errs[f"{sh.name} dA"] = rel_err(got["dA"][k * u.r:(k + 1) * u.r], dA)
+                errs[f"{sh.name} dB"] = rel_err(got["dB"][n0:n0 + sh.N], dB)
+                n0 += sh.N
+            errs["dX"] = rel_err(got["dX"], dX)
+        else:
+            m = mi[0]
+            H, U = oracle.forward(X, m["W"], m["A"], m["B"], s)
+            dX, dA, dB = oracle.backward(m["dY"], X, m["W"], m["A"], m["B"], s)
+            errs = {k: rel_err(got[k], ref) for k, ref in (("H", H), ("U", U), ("dX", dX), ("dA", dA), ("dB", dB))}
+        print(f"  {u.name}: graded errors {errs}", flush=True)
+        bad = {k: e for k, e in errs.items() if not e <= BF16_TOL}
+        assert not bad, f"{u.name}: {bad} exceed {BF16_TOL}"

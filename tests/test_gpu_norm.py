@@ -6,8 +6,11 @@ dX (through the norm), dA and dB are compared element by element with
 oracle.norm_forward / norm_backward on the float32 draws (graded bound), over
 the kernels' forms: the rank-r product formed inside the GEMM tile (r <= 16,
 whole contraction), the precomputed-Z form with a split contraction (r = 8 on
-few tiles, r = 40, r = 128), the full 4096 x 4096 projection, and the call
-variants (nothing saved, no dX, accumulated gradients, W folded in place).
+few tiles, r = 40, r = 128), the three forms of the row kernels (K up to 4096,
+up to 8192, longer), the full 4096 x 4096 projection, and the call variants
+(nothing saved, no dX, accumulated gradients, W folded in place).  Groups of
+linears behind one norm (lora_norm_group_*) against the members' oracle
+results, and a one-member group bit for bit against the plain norm layer.
 """
 import numpy as np
 import pytest
@@ -28,6 +31,8 @@ CASES = {
     "r8_split": (300, 264, 520, 8),        # few tiles: split contraction, precomputed Z
     "r40": (1000, 1024, 768, 40),          # rank padded to 64, split contraction
     "r128": (2048, 512, 4096, 128),        # rank 128: forward whole tiles, dX split 16 ways
+    "k6144": (260, 6144, 264, 16),         # row kernels: rows of 4097..8192 held in registers
+    "k9224": (130, 9224, 136, 8),          # row kernels: rows longer than 8192, streamed, ragged last chunk
 }
 
 
@@ -161,3 +166,85 @@ def test_norm_linear_is_scale_invariant_bitwise():
         np.testing.assert_array_equal(a[k], b[k], err_msg=k)
     np.testing.assert_array_equal(a["dX"], 2.0 * b["dX"])
     np.testing.assert_array_equal(a["inv"], 2.0 * b["inv"])
+
+
+# ---------------------------------------------------------------- groups behind one norm
+def _group_norm_inputs(M, K, Ns, r, seed):
+    mem = [workloads.make_norm_inputs(workloads.LinearShape(f"gn{i}", M, K, n, r, 2.0 * r, seed + i))
+           for i, n in enumerate(Ns)]
+    return {"X": mem[0]["X"], "g": mem[0]["g"], "W": [m["W"] for m in mem], "A": [m["A"] for m in mem],
+            "B": [m["B"] for m in mem], "dY": [m["dY"] for m in mem]}
+
+
+def _run_group(gi, r, alpha, eps=EPS):
+    import lora_linear_layer_amd as lla
+    M, K = gi["X"].shape
+    Ns = tuple(w.shape[0] for w in gi["W"])
+    desc = lla.GroupDesc(M, K, Ns, r, alpha)
+    X, g = to_dev(gi["X"], BF), to_dev(gi["g"], BF)
+    W = to_dev(np.vstack(gi["W"]), BF)
+    A = to_dev(np.vstack(gi["A"]), BF)
+    B = to_dev(np.vstack(gi["B"]), BF)
+    dY = to_dev(np.hstack(gi["dY"]), BF)
+    N, R = sum(Ns), len(Ns) * r
+    lla.lora_fold_norm_weight(W, g, W)
+    H = torch.empty((M, N), dtype=BF, device="cuda")
+    U = torch.empty((M, R), dtype=torch.float32, device="cuda")
+    inv = torch.empty((M,), dtype=torch.float32, device="cuda")
+    dX = torch.empty((M, K), dtype=BF, device="cuda")
+    dA = torch.empty((R, K), dtype=BF, device="cuda")
+    dB = torch.empty((N, r), dtype=BF, device="cuda")
+    lla.lora_norm_group_fwd(desc, eps, X, g, W, A, B, H, U, inv)
+    lla.lora_norm_group_bwd(desc, eps, dY, X, g, W, A, B, U, inv, dX, dA, dB)
+    torch.cuda.synchronize()
+    cols = np.cumsum((0,) + Ns)
+    return {"H": [to_np(H)[:, cols[i]:cols[i + 1]] for i in range(len(Ns))],
+            "U": [to_np(U)[:, i * r:(i + 1) * r] for i in range(len(Ns))],
+            "dA": [to_np(dA)[i * r:(i + 1) * r] for i in range(len(Ns))],
+            "dB": [to_np(dB)[cols[i]:cols[i + 1]] for i in range(len(Ns))],
+            "dX": to_np(dX)}
+
+
+NORM_GROUPS = [
+    (300, 392, (264, 136, 520), 16),      # member boundaries inside output tiles
+    (513, 256, (1024, 256, 256), 64),     # q / k / v proportions, group rank 192
+    (257, 520, (1000, 1000), 24),         # gate / up
+]
+
+
+@pytest.mark.parametrize("M,K,Ns,r", NORM_GROUPS)
+def test_norm_group_matches_oracle(M, K, Ns, r):
+    """Each member against oracle.norm_forward / norm_backward with the shared
+    X and g; dX against the sum of the members' input gradients (the norm's
+    Jacobian is linear in the gradient it receives)."""
+    print(f"norm group M={M} K={K} N={Ns} r={r}", flush=True)
+    gi = _group_norm_inputs(M, K, Ns, r, seed=M + K)
+    got = _run_group(gi, r, 2.0 * r)
+    s = 2.0
+    errs = {"dX": 0.0}
+    dX = 0.0
+    for i in range(len(Ns)):
+        H, U, _ = oracle.norm_forward(gi["X"], gi["g"], EPS, gi["W"][i], gi["A"][i], gi["B"][i], s)
+        dXi, dA, dB = oracle.norm_backward(gi["dY"][i], gi["X"], gi["g"], EPS, gi["W"][i], gi["A"][i], gi["B"][i], s)
+        dX = dX + dXi
+        for k, ref in (("H", H), ("U", U), ("dA", dA), ("dB", dB)):
+            errs[f"{k}{i}"] = rel_err(got[k][i], ref)
+    errs["dX"] = rel_err(got["dX"], dX)
+    print(f"  graded errors {errs}", flush=True)
+    bad = {k: e for k, e in errs.items() if not e <= BF16_TOL}
+    assert not bad, f"{bad} exceed {BF16_TOL}"
+
+
+@pytest.mark.parametrize("r", [8, 24])
+def test_one_member_norm_group_is_the_norm_layer(r):
+    """A norm group of one member takes the plain norm layer's kernels: every
+    output bit-identical."""
+    M, K, N = 300, 264, 520
+    gi = _group_norm_inputs(M, K, (N,), r, seed=91)
+    got = _run_group(gi, r, 2.0 * r)
+    sh = workloads.LinearShape("gn0", M, K, N, r, 2.0 * r, 91)
+    inp = {"X": gi["X"], "g": gi["g"], "W": gi["W"][0], "A": gi["A"][0], "B": gi["B"][0], "dY": gi["dY"][0]}
+    plain = _run(sh, inp)
+    for k in ("H", "U", "dA", "dB"):
+        np.testing.assert_array_equal(got[k][0].view(np.uint32), plain[k].view(np.uint32), err_msg=k)
+    np.testing.assert_array_equal(got["dX"].view(np.uint32), plain["dX"].view(np.uint32), err_msg="dX")

@@ -225,6 +225,15 @@ def device_inputs_torch(shape: LinearShape, device, dtype, seed: int):
             "B": normal(N, r, 0.02), "dY": normal(M, N, 1.0)}
 
 
+def norm_weight_torch(K: int, device, dtype, seed: int):
+    """Seeded device-side draw of an RMSNorm weight g [K] ~ 1 + N(0, 0.2^2)
+    (benchmark inputs; not the numpy draw of make_norm_inputs)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return (1.0 + 0.2 * torch.randn((K,), generator=g, device=device, dtype=torch.float32)).to(dtype)
+
+
 def quantize4_torch(W):
     """Device-side version of quantize4 for benchmark inputs (float32 arithmetic).
 
