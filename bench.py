@@ -34,6 +34,12 @@ Extra modes (used to produce the committed counter summaries):
                         lora_group_bwd: one pass over X for all their U, one
                         GEMM over the stacked weights, the shared input's
                         gradient summed over them)
+  --w-layout {wt,w}     the frozen weight the backward reads: wt (default)
+                        W^T [K, N], transposed once before timing and kept
+                        beside W (LORA_FLAG_W_TRANSPOSED: the input-gradient
+                        GEMM then reads it in the forward's layout); w: W
+                        itself, gathered with transposing LDS reads.  4-bit
+                        weights always use their codes.
   --norm                the linears that read a normalised input (the
                         projection of attn_proj_4096; q/k/v and gate/up)
                         run with the RMSNorm in front (lora_norm_linear_* /
@@ -99,6 +105,8 @@ def parse(argv=None):
                          "(lora_tune_linear; the probing is outside the timed region)")
     ap.add_argument("--grouped", action="store_true",
                     help="linears sharing an input run as one grouped call (q/k/v, gate/up)")
+    ap.add_argument("--w-layout", choices=("wt", "w"), default="wt",
+                    help="backward weight operand: W^T made once before timing (default), or W")
     ap.add_argument("--norm", action="store_true",
                     help="RMSNorm in front of the linears that read a normalised input")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -252,15 +260,18 @@ def traffic_path(workload):
     return os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
 
 
-def load_traffic(workload):
+def load_traffic(workload, w_layout="wt"):
     """Measured HBM bytes per dispatch of each GEMM, {label: bytes}, or None
-    when no counters were taken for the current kernel sources."""
+    when no counters were taken for the current kernel sources and the same
+    backward weight layout."""
     p = traffic_path(workload)
     if not os.path.exists(p):
         return None
     t = json.load(open(p))
     if t.get("kernel_source_hash") != kernel_source_hash():
         return None          # the kernels changed since the counters were taken
+    if t.get("w_layout", "w") != w_layout:
+        return None          # counters of the other input-gradient GEMM
     return {k: v["hbm_bytes_per_dispatch"] for k, v in t.get("kernels", {}).items()}
 
 
@@ -302,7 +313,7 @@ def write_traffic(args):
                           "hbm_bytes_per_dispatch": round(fetch_k * 1024 / f_fac + write_k * 1024 / w_fac)}
     if not kernels:
         raise SystemExit("missing counters: need FETCH_SIZE and WRITE_SIZE runs of the bench")
-    out = {"workload": args.workload, "kernel_source_hash": kernel_source_hash(),
+    out = {"workload": args.workload, "kernel_source_hash": kernel_source_hash(), "w_layout": args.w_layout,
            "copy_kib_fetch": cfetch_k, "copy_kib_write": cwrite_k, "copy_bytes": COPY_BYTES,
            "copy_fetch_factor": round(f_fac, 4), "copy_write_factor": round(w_fac, 4), "kernels": kernels}
     os.makedirs(os.path.dirname(traffic_path(args.workload)), exist_ok=True)
@@ -356,6 +367,19 @@ def add_norm(lla, torch, wl, layer, dev, seed):
     return layer
 
 
+def add_wt(lla, torch, wl, layer):
+    """W^T of every 16-bit frozen weight (made once, before any timing; after
+    add_norm, so that it is the folded weight's transpose), and the flag that
+    makes the backward read it."""
+    for sh, d in zip(wl.linears, layer):
+        if "W" not in d:
+            continue
+        d["Wt"] = torch.empty((sh.K, sh.N), dtype=d["W"].dtype, device=d["W"].device)
+        lla.lora_transpose_weight(d["W"], d["Wt"])
+        d["desc"] = dataclasses.replace(d["desc"], flags=d["desc"].flags | lla.LORA_FLAG_W_TRANSPOSED)
+    return layer
+
+
 def group_layer(lla, torch, wl, layer, units, dev):
     """The per-linear inputs of one step regrouped as units: a group's W, A, B
     and dY stacked (copies made once, before any timing), its outputs H
@@ -375,6 +399,9 @@ def group_layer(lla, torch, wl, layer, units, dev):
         if "g" in ds[0]:
             g["g"] = ds[0]["g"]
             g["inv"] = ds[0]["inv"]
+        if "Wt" in ds[0]:                    # the stacked weight's transpose [K][sum N]
+            g["Wt"] = torch.cat([d["Wt"] for d in ds], dim=1).contiguous()
+            g["gdesc"] = dataclasses.replace(g["gdesc"], flags=g["gdesc"].flags | lla.LORA_FLAG_W_TRANSPOSED)
         R = u.G * u.r
         g["H"] = torch.empty((u.M, u.N), dtype=torch.bfloat16, device=dev)
         g["U"] = torch.empty((u.M, R), dtype=torch.float32, device=dev)
@@ -421,18 +448,19 @@ class Stepper:
 
     def bwd(self, d):
         lla = self.lla
+        W = d.get("Wt", d.get("W"))          # W^T when the descriptor carries LORA_FLAG_W_TRANSPOSED
         if "g" in d:
             f = lla.lora_norm_group_bwd if "gdesc" in d else lla.lora_norm_linear_bwd
-            f(d.get("gdesc") or d["desc"], NORM_EPS, d["dY"], d["X"], d["g"], d["W"], d["A"], d["B"], d["U"],
+            f(d.get("gdesc") or d["desc"], NORM_EPS, d["dY"], d["X"], d["g"], W, d["A"], d["B"], d["U"],
               d["inv"], d["dX"], d["dA"], d["dB"], ws=self.ws, ws_bytes=self.ws_bytes)
         elif "gdesc" in d:
-            lla.lora_group_bwd(d["gdesc"], d["dY"], d["X"], d["W"], d["A"], d["B"], d["U"], d["dX"], d["dA"],
+            lla.lora_group_bwd(d["gdesc"], d["dY"], d["X"], W, d["A"], d["B"], d["U"], d["dX"], d["dA"],
                                d["dB"], ws=self.ws, ws_bytes=self.ws_bytes)
         elif "codes" in d:
             lla.lora_qlinear_bwd(d["desc"], d["dY"], d["X"], d["codes"], d["absmax"], d["codebook"], d["A"],
                                  d["B"], d["U"], d["dX"], d["dA"], d["dB"], ws=self.ws, ws_bytes=self.ws_bytes)
         else:
-            lla.lora_linear_bwd(d["desc"], d["dY"], d["X"], d["W"], d["A"], d["B"], d["U"], d["dX"], d["dA"],
+            lla.lora_linear_bwd(d["desc"], d["dY"], d["X"], W, d["A"], d["B"], d["U"], d["dX"], d["dA"],
                                 d["dB"], ws=self.ws, ws_bytes=self.ws_bytes)
 
     def step(self, layer):
@@ -634,6 +662,8 @@ def main(argv=None):
         layer = add_outputs(lla, torch, wl, share_inputs(wl, layer), dev)
         if args.norm:
             add_norm(lla, torch, wl, layer, dev, seed=7000 + 10 * si)
+        if args.w_layout == "wt":
+            add_wt(lla, torch, wl, layer)
         sets.append(layer)
     units = step_units(wl, args.grouped)
     if args.grouped:
@@ -647,7 +677,9 @@ def main(argv=None):
                 continue                      # grouped and norm calls keep the built-in rules
             wargs = (dict(Wq=d["codes"], absmax=d["absmax"], codebook=d["codebook"]) if "codes" in d
                      else dict(W=d["W"]))
-            tuned[u.name] = lla.lora_tune_linear(d["desc"], d["X"], d["A"], d["B"], d["H"], d["U"], d["dY"], d["dX"],
+            # the tuner runs both directions with one W: its descriptor without the W^T flag
+            tdesc = dataclasses.replace(d["desc"], flags=d["desc"].flags & ~lla.LORA_FLAG_W_TRANSPOSED)
+            tuned[u.name] = lla.lora_tune_linear(tdesc, d["X"], d["A"], d["B"], d["H"], d["U"], d["dY"], d["dX"],
                                                  d["dA"], d["dB"], ws=stepper.ws, ws_bytes=stepper.ws_bytes, **wargs)
         torch.cuda.synchronize()
     step = lambda i: stepper.step(sets[i % len(sets)])
@@ -722,7 +754,7 @@ def main(argv=None):
         ks = {k: round(sum(v) / len(v), 2) for (i, k), v in kernel_us.items() if i == li}
         per_linear.append({"name": u.name, "kernel_us": ks})
 
-    gemms = gemm_rooflines(units, kernel_us, load_traffic(wl.name) if not args.norm else None)
+    gemms = gemm_rooflines(units, kernel_us, load_traffic(wl.name, args.w_layout) if not args.norm else None)
     # dominant kernel: the GEMM with the largest measured time per step
     dominant = max(gemms, key=lambda g: g["avg_launch_us"] * g["launches_per_step"] / args.steps)
     p10, p50, p90 = (percentile(step_ms, q) for q in (0.1, 0.5, 0.9))
@@ -737,7 +769,9 @@ def main(argv=None):
                    "input_sets": args.input_sets, "description": wl.description,
                    "calls": [u.name for u in units],
                    "rmsnorm_in_front": [u.name for u in units if behind_norm(wl.linears[u.members[0]].name)]
-                   if args.norm else []},
+                   if args.norm else [],
+                   "backward_weight": ("W^T [K, N] of the frozen weight, transposed once before timing"
+                                       if args.w_layout == "wt" else "W [N, K]")},
         "tokens_per_s": round(tokens_s, 1), "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "step_ms_p10_p50_p90": [round(p10, 4), round(p50, 4), round(p90, 4)],
         "timed_kernels_ms_per_step": round(timer_ms_step, 4),

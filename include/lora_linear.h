@@ -55,6 +55,15 @@ typedef enum lora_dtype {
 
 /* flags */
 #define LORA_FLAG_ACCUM_GRADS 0x1u   /* backward adds into dA, dB instead of overwriting */
+/* The W argument of the backward entry points (lora_linear_bwd, _bwd_noalloc,
+ * lora_group_bwd, lora_norm_linear_bwd, lora_norm_group_bwd) is W^T [K, N]
+ * (stacked: [K, N_total]; behind a norm: W_g^T), made once from the frozen
+ * weight with lora_transpose_weight; the forward entry points still take W
+ * [N, K] and ignore the flag.  The input-gradient GEMM then reads its weight
+ * operand like the forward reads W; results are bit-identical to the call
+ * with W.  bf16 weights only (4-bit, float32 mode, the tuner:
+ * LORA_ERR_UNSUPPORTED). */
+#define LORA_FLAG_W_TRANSPOSED 0x2u
 
 /*
  * Problem descriptor (host memory).
@@ -202,6 +211,15 @@ lora_status lora_group_bwd(const lora_group_desc* desc,
  * workspace of lora_norm_linear_workspace_size; eps >= 0; bf16 only
  * (LORA_ERR_UNSUPPORTED otherwise).
  */
+/*
+ * Wt = W^T: W [N, K] bf16 -> Wt [K, N] bf16, for LORA_FLAG_W_TRANSPOSED
+ * (the frozen weight transposed once, kept beside W; the adapter's
+ * re-associated backward of page "Unsloth — 微调 2-5x 加速", section "核心要点",
+ * item 2, then reads it in the forward's layout).  N, K multiples of 8;
+ * Wt must not alias W.  Enqueued on `stream`.
+ */
+lora_status lora_transpose_weight(const void* W, int64_t N, int64_t K, void* Wt, void* stream);
+
 lora_status lora_fold_norm_weight(const void* W, const void* g, int64_t N, int64_t K, void* W_out, void* stream);
 
 lora_status lora_norm_linear_workspace_size(const lora_linear_desc* desc, size_t* bytes);

@@ -22,6 +22,7 @@ LORA_DTYPE_BF16 = 0
 LORA_DTYPE_F32 = 1
 
 LORA_FLAG_ACCUM_GRADS = 0x1
+LORA_FLAG_W_TRANSPOSED = 0x2
 LORA_NOALLOC_SCRATCH_BYTES = 32 << 20
 LORA_MAX_MEMBERS = 8
 LORA_MAX_GROUP_RANK = 192
@@ -30,7 +31,7 @@ EXPORTED = (
     "lora_linear_workspace_size", "lora_linear_fwd", "lora_linear_bwd", "lora_linear_bwd_noalloc",
     "lora_qlinear_fwd", "lora_qlinear_bwd", "lora_dequant4", "lora_merge",
     "lora_linear_buffer_ranges", "lora_group_workspace_size", "lora_group_fwd", "lora_group_bwd",
-    "lora_fold_norm_weight", "lora_norm_linear_workspace_size", "lora_norm_linear_fwd", "lora_norm_linear_bwd",
+    "lora_transpose_weight", "lora_fold_norm_weight", "lora_norm_linear_workspace_size", "lora_norm_linear_fwd", "lora_norm_linear_bwd",
     "lora_norm_group_workspace_size", "lora_norm_group_fwd", "lora_norm_group_bwd",
     "lora_tune_linear", "lora_tuner_lookup", "lora_tuner_save", "lora_tuner_load", "lora_tuner_clear",
     "lora_set_kernel_timer", "lora_status_string", "lora_last_error",
@@ -105,6 +106,7 @@ def load() -> ctypes.CDLL:
         "lora_group_fwd": [gp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "lora_group_bwd": [gp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "lora_fold_norm_weight": [vp, vp, i64, i64, vp, vp],
+        "lora_transpose_weight": [vp, i64, i64, vp, vp],
         "lora_norm_linear_workspace_size": [dp, ctypes.POINTER(sz)],
         "lora_norm_linear_fwd": [dp, f32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "lora_norm_linear_bwd": [dp, f32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],

@@ -119,12 +119,17 @@ def _same_gpu(**ts):
         dev = t.device
 
 
+def _w_shape(desc, N, K, backward: bool):
+    """W [N, K], or W^T [K, N] in a backward call with LORA_FLAG_W_TRANSPOSED."""
+    return (K, N) if backward and (desc.flags & _lib.LORA_FLAG_W_TRANSPOSED) else (N, K)
+
+
 def _check_dense(desc: "Desc", **ts):
     """Operands of a forward or backward call against the descriptor, before
     their addresses go to the library."""
     M, K, N, r = desc.M, desc.K, desc.N, desc.r
     dt = (_TORCH_DTYPE[desc.dtype],) if desc.dtype in _TORCH_DTYPE else ()
-    spec = {"X": ((M, K), dt), "W": ((N, K), dt), "A": ((r, K), dt), "B": ((N, r), dt), "H": ((M, N), dt),
+    spec = {"X": ((M, K), dt), "W": (_w_shape(desc, N, K, "dY" in ts), dt), "A": ((r, K), dt), "B": ((N, r), dt), "H": ((M, N), dt),
             "dY": ((M, N), dt), "dX": ((M, K), dt), "dA": ((r, K), dt), "dB": ((N, r), dt),
             "U_save": ((M, r), (torch.float32,)), "U_saved": ((M, r), (torch.float32,)),
             "Wq": ((N, K // 2), (torch.uint8,)),
@@ -241,7 +246,7 @@ def lora_linear_bwd_noalloc(desc: Desc, dY, X, W, A, B, U_saved, dX, dA, dB, str
 def _check_group(g: GroupDesc, **ts):
     M, K, N, R, r = g.M, g.K, g.N_total, g.rank_total, g.r
     dt = (_TORCH_DTYPE[g.dtype],) if g.dtype in _TORCH_DTYPE else ()
-    spec = {"X": ((M, K), dt), "W": ((N, K), dt), "A": ((R, K), dt), "B": ((N, r), dt), "H": ((M, N), dt),
+    spec = {"X": ((M, K), dt), "W": (_w_shape(g, N, K, "dY" in ts), dt), "A": ((R, K), dt), "B": ((N, r), dt), "H": ((M, N), dt),
             "dY": ((M, N), dt), "dX": ((M, K), dt), "dA": ((R, K), dt), "dB": ((N, r), dt),
             "U_save": ((M, R), (torch.float32,)), "U_saved": ((M, R), (torch.float32,))}
     for name, t in ts.items():
@@ -288,7 +293,8 @@ def lora_group_bwd(desc: GroupDesc, dY, X, W, A, B, U_saved, dX, dA, dB, ws=None
 def _check_norm(desc: Desc, **ts):
     M, K, N, r = desc.M, desc.K, desc.N, desc.r
     bf = (torch.bfloat16,)
-    spec = {"X": ((M, K), bf), "g": ((K,), bf), "W": ((N, K), bf), "W_g": ((N, K), bf), "A": ((r, K), bf),
+    spec = {"X": ((M, K), bf), "g": ((K,), bf), "W": ((N, K), bf), "W_g": (_w_shape(desc, N, K, "dY" in ts), bf),
+            "A": ((r, K), bf),
             "B": ((N, r), bf), "H": ((M, N), bf), "dY": ((M, N), bf), "dX": ((M, K), bf), "dA": ((r, K), bf),
             "dB": ((N, r), bf), "U_save": ((M, r), (torch.float32,)), "U_saved": ((M, r), (torch.float32,)),
             "inv_rms_save": ((M,), (torch.float32,)), "inv_rms_saved": ((M,), (torch.float32,))}
@@ -303,6 +309,16 @@ def lora_norm_linear_workspace_size(desc: Desc) -> int:
     _check(_lib.load().lora_norm_linear_workspace_size(ctypes.byref(d), ctypes.byref(out)),
            "lora_norm_linear_workspace_size")
     return int(out.value)
+
+
+def lora_transpose_weight(W, Wt, stream=None):
+    """Wt = W^T (bf16 [N, K] -> [K, N]): the frozen weight's copy for backward
+    calls with LORA_FLAG_W_TRANSPOSED."""
+    N, K = W.shape
+    _expect(W, "W", (N, K), (torch.bfloat16,))
+    _expect(Wt, "Wt", (K, N), (torch.bfloat16,))
+    _same_gpu(W=W, Wt=Wt)
+    _check(_lib.load().lora_transpose_weight(_ptr(W), N, K, _ptr(Wt), _stream(stream)), "lora_transpose_weight")
 
 
 def lora_fold_norm_weight(W, g, W_out, stream=None):
@@ -354,7 +370,8 @@ def lora_norm_linear_bwd(desc: Desc, eps: float, dY, X, g, W_g, A, B, U_saved, i
 def _check_norm_group(gd: GroupDesc, **ts):
     M, K, N, R, r = gd.M, gd.K, gd.N_total, gd.rank_total, gd.r
     bf = (torch.bfloat16,)
-    spec = {"X": ((M, K), bf), "g": ((K,), bf), "W_g": ((N, K), bf), "A": ((R, K), bf), "B": ((N, r), bf),
+    spec = {"X": ((M, K), bf), "g": ((K,), bf), "W_g": (_w_shape(gd, N, K, "dY" in ts), bf), "A": ((R, K), bf),
+            "B": ((N, r), bf),
             "H": ((M, N), bf), "dY": ((M, N), bf), "dX": ((M, K), bf), "dA": ((R, K), bf), "dB": ((N, r), bf),
             "U_save": ((M, R), (torch.float32,)), "U_saved": ((M, R), (torch.float32,)),
             "inv_rms_save": ((M,), (torch.float32,)), "inv_rms_saved": ((M,), (torch.float32,))}

@@ -194,10 +194,15 @@ struct Frags {
 // rank-r term) that split_finish adds in order and rounds to bf16.  Used when
 // the output has too few tiles to fill the chip (e.g. d_out = 1024: all tiles
 // split) and for the tiles of a last, partly empty round.
-template <bool TRANS, int RPAD, bool ZIN, bool Q4 = false, bool SPLIT = false>
+template <bool TRANS, int RPAD, bool ZIN, bool Q4 = false, bool SPLIT = false, bool RT = false>
 __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
     using namespace g2;
     using namespace g2w;
+    // R rows along q, contiguous in c ([Q][C]): the forward's W, and the input
+    // gradient's when it is given as W^T (RT); otherwise the input gradient's W
+    // is [C][Q] and its fragments are gathered with transposing LDS reads
+    constexpr bool RQC = !TRANS || RT;
+    static_assert(!(RT && (Q4 || !TRANS)), "RT: 16-bit input-gradient weights only");
     using SM = GemmSmem<RPAD, ZIN, Q4>;
     static_assert(ZIN || !Q4, "4-bit GEMMs take Z precomputed");
     static_assert(!SPLIT || ZIN, "split contraction: precomputed Z");
@@ -247,7 +252,7 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
     int chR[LPW == 8 ? 4 : 2] = {};
     if constexpr (Q4) {
         // R tiles come through registers (load_q / decode_q)
-    } else if constexpr (!TRANS) {
+    } else if constexpr (RQC) {
         rsR = make_rsrc(a.R + (size_t)q0 * C, panel_bytes(Q, q0, BQ, C));
         offR = (uint32_t)(kc_row0 * C + kc_ch) * 2u;
     } else {
@@ -363,7 +368,7 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
         for (int i = 0; i < LPW; ++i) g2lds16<TRANS>(rsL, Ls + (wave * LPW + i) * 1024, vL + (uint32_t)(i * 8 * C) * 2u);
         if constexpr (Q4) {
             load_q(kt);
-        } else if constexpr (!TRANS) {
+        } else if constexpr (RQC) {
             const uint32_t vR = lok ? offR + (uint32_t)c0 * 2u : kOOB;
 #pragma unroll
             for (int i = 0; i < LPW; ++i)
@@ -415,7 +420,7 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
     auto chunk_of = [&](int kk) { return (((kk * 4 + g4) ^ (l16 & 7)) << 4) + kc_lane; };
     auto read_r = [&](const uint8_t* Ls, int kk, int i) -> bf16x8 {
         const uint8_t* const Rs = Ls + TILE;
-        if constexpr (!TRANS) {
+        if constexpr (RQC) {
             return lds_b128(Rs + (wq * QB + i) * 2048 + chunk_of(kk));
         } else {
             const int rlo = kk * 32 + g4 * 8 + (l16 >> 2);            // rhi = rlo + 4: same swizzle
@@ -454,7 +459,7 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
     // and then one fragment read after every RA MFMAs, so that neither the
     // LDS queue nor the MFMA pipe runs dry and the last read is issued well
     // before the next step needs it.
-    constexpr int NR_STEP = (TRANS ? 2 * QB : QB) + 8 + (ZIN ? 0 : (TRANS ? 2 * JT : JT));
+    constexpr int NR_STEP = (RQC ? QB : 2 * QB) + 8 + (ZIN ? 0 : (TRANS ? 2 * JT : JT));
     constexpr int NM_STEP = 8 * QB + (ZIN ? 0 : ZB * JT);
     auto step = [&](const Frags<JT, QB>& cur, Frags<JT, QB>& nxt, const uint8_t* nstage, int nkk, auto do_read,
                     auto pre) {

@@ -26,6 +26,7 @@
 #include "dequant4.hpp"
 #include "merge.hpp"
 #include "norm.hpp"
+#include "transpose.hpp"
 #include "f32_kernels.hpp"
 
 using namespace lora;
@@ -293,8 +294,10 @@ lora_status check_desc(const lora_linear_desc* d, bool quant) {
     if (d->dtype != LORA_DTYPE_BF16 && d->dtype != LORA_DTYPE_F32)
         return fail(LORA_ERR_INVALID_ARG, "unknown dtype %d", (int)d->dtype);
     if (!std::isfinite(d->alpha)) return fail(LORA_ERR_INVALID_ARG, "alpha is not finite");
-    if ((d->flags & ~LORA_FLAG_ACCUM_GRADS) != 0)
+    if ((d->flags & ~(LORA_FLAG_ACCUM_GRADS | LORA_FLAG_W_TRANSPOSED)) != 0)
         return fail(LORA_ERR_INVALID_ARG, "unknown flag bits 0x%x", (unsigned)d->flags);
+    if ((d->flags & LORA_FLAG_W_TRANSPOSED) && (quant || d->dtype != LORA_DTYPE_BF16))
+        return fail(LORA_ERR_UNSUPPORTED, "LORA_FLAG_W_TRANSPOSED: bf16 weights only");
     if (d->r > 128) return fail(LORA_ERR_UNSUPPORTED, "r = %lld exceeds 128", (long long)d->r);
     if (d->K % 8 || d->N % 8)
         return fail(LORA_ERR_UNSUPPORTED, "K and N must be multiples of 8 (got K=%lld, N=%lld)",
@@ -342,7 +345,7 @@ lora_status check_group(const lora_group_desc* g) {
         return fail(LORA_ERR_INVALID_ARG, "unknown dtype %d", (int)g->dtype);
     if (g->dtype != LORA_DTYPE_BF16) return fail(LORA_ERR_UNSUPPORTED, "grouped linears are bf16 only");
     if (!std::isfinite(g->alpha)) return fail(LORA_ERR_INVALID_ARG, "alpha is not finite");
-    if ((g->flags & ~LORA_FLAG_ACCUM_GRADS) != 0)
+    if ((g->flags & ~(LORA_FLAG_ACCUM_GRADS | LORA_FLAG_W_TRANSPOSED)) != 0)
         return fail(LORA_ERR_INVALID_ARG, "unknown flag bits 0x%x", (unsigned)g->flags);
     if (g->r > 128) return fail(LORA_ERR_UNSUPPORTED, "r = %lld exceeds 128", (long long)g->r);
     if (g->r * g->n_members > LORA_MAX_GROUP_RANK)
@@ -404,10 +407,11 @@ lora_status launched(const char* what) {
     } while (0)
 
 // ---------------------------------------------------------------- bf16 launches
-template <bool TRANS, int RPAD, bool ZIN, bool Q4>
+template <bool TRANS, int RPAD, bool ZIN, bool Q4, bool RT = false>
 void launch_gemm_t(const GemmArgs& a, hipStream_t st) {
     const int tiles = (int)(cdiv(a.P, g2::BP) * cdiv(a.Q, g2::BQ));
-    LAUNCH(TRANS ? "lora_gemm dX" : "lora_gemm forward", (lora_gemm<TRANS, RPAD, ZIN, Q4>), dim3(tiles), dim3(g2w::NT), 0, st, a);
+    LAUNCH(TRANS ? "lora_gemm dX" : "lora_gemm forward", (lora_gemm<TRANS, RPAD, ZIN, Q4, false, RT>), dim3(tiles),
+           dim3(g2w::NT), 0, st, a);
 }
 
 // In-tile rank-r product for r <= 16 with 16-bit weights: the forward forms
@@ -429,7 +433,7 @@ bool dx_in_tile(bool quant, int r, const SplitPlan& sp) {
 
 // Precomputed-Z form, with the split contraction of gemm_split_plan into
 // a.Part (workspace) plus split_finish when it applies.
-template <bool TRANS, int RPAD, bool Q4>
+template <bool TRANS, int RPAD, bool Q4, bool RT = false>
 void launch_gemm_zin(GemmArgs a, const SplitPlan& sp, hipStream_t st) {
     if (sp.split > 1 && a.Part != nullptr) {
         a.first_split = sp.first;
@@ -437,17 +441,18 @@ void launch_gemm_zin(GemmArgs a, const SplitPlan& sp, hipStream_t st) {
         a.kc = sp.kc;
         const int T = (int)(cdiv(a.P, g2::BP) * cdiv(a.Q, g2::BQ));
         const int units = sp.first + (T - sp.first) * sp.split;
-        LAUNCH(TRANS ? "lora_gemm dX (split)" : "lora_gemm forward (split)", (lora_gemm<TRANS, RPAD, true, Q4, true>), dim3(units), dim3(g2w::NT), 0, st, a);
+        LAUNCH(TRANS ? "lora_gemm dX (split)" : "lora_gemm forward (split)", (lora_gemm<TRANS, RPAD, true, Q4, true, RT>),
+               dim3(units), dim3(g2w::NT), 0, st, a);
         SplitFinishArgs f{a.Part, a.Out, a.P, a.Q, (int)cdiv(a.P, g2::BP), (int)cdiv(a.Q, g2::BQ), sp.first,
                           T - sp.first, sp.split, TRANS ? nullptr : a.row_scale};
         const int64_t n = (int64_t)(T - sp.first) * (g2::BP * g2::BQ / 4);
         LAUNCH("split_finish", split_finish, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, st, f);
         return;
     }
-    launch_gemm_t<TRANS, RPAD, true, Q4>(a, st);
+    launch_gemm_t<TRANS, RPAD, true, Q4, RT>(a, st);
 }
 
-template <bool TRANS, bool Q4>
+template <bool TRANS, bool Q4, bool RT = false>
 void launch_gemm(GemmArgs a, bool in_tile, const SplitPlan& sp, hipStream_t st) {
     if (a.n_members == 0) {              // a plain layer: one member over all output columns
         a.n_members = 1;
@@ -456,13 +461,13 @@ void launch_gemm(GemmArgs a, bool in_tile, const SplitPlan& sp, hipStream_t st) 
     }
     if (a.z_ld == 0) a.z_ld = a.r;
     if constexpr (!Q4) {
-        if (in_tile) { launch_gemm_t<TRANS, 16, false, false>(a, st); return; }
+        if (in_tile) { launch_gemm_t<TRANS, 16, false, false, RT>(a, st); return; }
     }
     switch (rpad_of(a.r)) {
-        case 16: launch_gemm_zin<TRANS, 16, Q4>(a, sp, st); break;
-        case 32: launch_gemm_zin<TRANS, 32, Q4>(a, sp, st); break;
-        case 64: launch_gemm_zin<TRANS, 64, Q4>(a, sp, st); break;
-        default: launch_gemm_zin<TRANS, 128, Q4>(a, sp, st); break;
+        case 16: launch_gemm_zin<TRANS, 16, Q4, RT>(a, sp, st); break;
+        case 32: launch_gemm_zin<TRANS, 32, Q4, RT>(a, sp, st); break;
+        case 64: launch_gemm_zin<TRANS, 64, Q4, RT>(a, sp, st); break;
+        default: launch_gemm_zin<TRANS, 128, Q4, RT>(a, sp, st); break;
     }
 }
 
@@ -739,6 +744,7 @@ lora_status bwd_bf16(const Shape& d, bool quant, const void* dY, const void* X, 
         g.P = (int)d.M; g.Q = (int)d.K; g.C = (int)d.N; g.r = (int)rg;
         g.s = d.alpha / (float)d.r;
         if (quant) launch_gemm<true, true>(g, v_in_tile, sp, st);
+        else if (d.flags & LORA_FLAG_W_TRANSPOSED) launch_gemm<true, false, true>(g, v_in_tile, sp, st);
         else launch_gemm<true, false>(g, v_in_tile, sp, st);
         LAUNCH_CHECK(quant ? "lora_gemm(4-bit dX)" : "lora_gemm(dX)");
     }
@@ -959,11 +965,11 @@ struct RangeList {
 };
 
 void gemm_ranges(RangeList& L, const char* name, bool trans, bool quant, bool in_tile, int64_t P, int64_t Q,
-                 int64_t C, int64_t r) {
+                 int64_t C, int64_t r, bool wt = false) {
     L.add(name, trans ? "dY panel" : "X panel", panel_bytes(P, 0, g2::BP, C));
     if (!quant) {
-        if (trans) L.add(name, "W stage (rows c0 .. c0 + 63)", gemm_wt_stage_bytes(C, Q, 0, 0));
-        else L.add(name, "W panel", panel_bytes(Q, 0, g2::BQ, C));
+        if (trans && !wt) L.add(name, "W stage (rows c0 .. c0 + 63)", gemm_wt_stage_bytes(C, Q, 0, 0));
+        else L.add(name, trans ? "W^T panel" : "W panel", panel_bytes(Q, 0, g2::BQ, C));
     }
     if (in_tile) L.add(name, trans ? "B" : "A", trans ? whole_bytes(C, r) : whole_bytes(r, C));
 }
@@ -985,7 +991,8 @@ void buffer_ranges(const Shape& d, bool quant, RangeList& L) {
     gemm_ranges(L, "lora_gemm (forward)", false, quant, fwd_in_tile, d.M, d.N, d.K, d.r);
     // backward: V streamed per member unless the dX GEMM forms it
     for (int m = 0; m < d.G; ++m) rank_z_ranges(L, "rank_z_lds (V = dY B)", d.M, d.Nm(m), d.N, d.r);
-    gemm_ranges(L, "lora_gemm (dX)", true, quant, d.G == 1 && dx_in_tile(quant, r, spb), d.M, d.K, d.N, d.r);
+    gemm_ranges(L, "lora_gemm (dX)", true, quant, d.G == 1 && dx_in_tile(quant, r, spb), d.M, d.K, d.N, d.r,
+                (d.flags & LORA_FLAG_W_TRANSPOSED) != 0);
     for (int64_t j0 = 0; j0 < rg; j0 += 64) {
         const int64_t rl = std::min<int64_t>(rg - j0, 64);
         const int64_t TM = rpad_of(rl) <= 16 ? kRT : kRT / 2;
@@ -1253,6 +1260,21 @@ lora_status lora_norm_linear_workspace_size(const lora_linear_desc* desc, size_t
     return ok();
 }
 
+lora_status lora_transpose_weight(const void* W, int64_t N, int64_t K, void* Wt, void* stream) {
+    if (N <= 0 || K <= 0) return fail(LORA_ERR_INVALID_ARG, "N, K must be positive");
+    if (N % 8 || K % 8) return fail(LORA_ERR_UNSUPPORTED, "N and K must be multiples of 8 (N=%lld, K=%lld)",
+                                    (long long)N, (long long)K);
+    if (N * K > kMaxElems) return fail(LORA_ERR_UNSUPPORTED, "W has 2^31 or more elements");
+    lora_status st = check_ptrs({{W, "W"}, {Wt, "Wt"}}, {});
+    if (st != LORA_OK) return st;
+    if (W == Wt) return fail(LORA_ERR_INVALID_ARG, "output Wt aliases W");
+    const dim3 grid((unsigned)cdiv(K, 64), (unsigned)cdiv(N, 64));
+    LAUNCH("transpose_weight", transpose_weight_kernel, grid, dim3(256), 0, static_cast<hipStream_t>(stream),
+           static_cast<const uint16_t*>(W), static_cast<uint16_t*>(Wt), (int)N, (int)K);
+    LAUNCH_CHECK("transpose_weight");
+    return ok();
+}
+
 lora_status lora_fold_norm_weight(const void* W, const void* g, int64_t N, int64_t K, void* W_out, void* stream) {
     if (N <= 0 || K <= 0) return fail(LORA_ERR_INVALID_ARG, "N, K must be positive");
     if (K % 8) return fail(LORA_ERR_UNSUPPORTED, "K must be a multiple of 8 (K=%lld)", (long long)K);
@@ -1396,6 +1418,8 @@ lora_status lora_tune_linear(const lora_linear_desc* desc, int32_t quant, const 
     lora_status st = check_desc(desc, q);
     if (st != LORA_OK) return st;
     if (desc->dtype != LORA_DTYPE_BF16) return fail(LORA_ERR_UNSUPPORTED, "only the bf16 path has launch parameters");
+    if (desc->flags & LORA_FLAG_W_TRANSPOSED)
+        return fail(LORA_ERR_UNSUPPORTED, "the tuner runs forward and backward with one W: no LORA_FLAG_W_TRANSPOSED");
     if (reps < 1 || reps > 100) return fail(LORA_ERR_INVALID_ARG, "reps = %d (1 .. 100)", (int)reps);
     st = check_ptrs({{X, "X"}, {A, "A"}, {B, "B"}, {H, "H"}, {U, "U"}, {dY, "dY"}, {dX, "dX"}, {dA, "dA"}, {dB, "dB"}},
                     {{W, "W"}, {Wq, "Wq"}, {absmax, "absmax"}, {codebook, "codebook"}});

@@ -63,8 +63,12 @@ def run_linear(inp: dict, r: int, alpha: float, dtype: str = "bf16", *, quant: b
                              U if save_u else None, dX, dA, dB, ws=ws)
     else:
         W = dd["W"]
+        Wb = W
+        if flags & lla.LORA_FLAG_W_TRANSPOSED:       # the backward reads W^T, made once from W
+            Wb = torch.empty((K, N), dtype=W.dtype, device=W.device)
+            lla.lora_transpose_weight(W, Wb)
         lla.lora_linear_fwd(desc, X, W, A, B, H, U if save_u else None, ws=ws)
-        lla.lora_linear_bwd(desc, dY, X, W, A, B, U if save_u else None, dX, dA, dB, ws=ws)
+        lla.lora_linear_bwd(desc, dY, X, Wb, A, B, U if save_u else None, dX, dA, dB, ws=ws)
     torch.cuda.synchronize()
     out = {"H": to_np(H), "dA": to_np(dA), "dB": to_np(dB)}
     if save_u:

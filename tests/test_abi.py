@@ -340,6 +340,35 @@ def test_norm_group_calls_validate_before_any_hip_call():
     assert fwd(ctypes.byref(bad), 1e-6, *p[:6], None, None, p[9], need, None) == _lib.LORA_ERR_UNSUPPORTED
 
 
+def test_w_transposed_flag_checks():
+    """LORA_FLAG_W_TRANSPOSED: accepted for bf16 layers and groups, refused for
+    the 4-bit and float32 paths and by the tuner; lora_transpose_weight's
+    argument checks; the input-gradient GEMM's W^T resource fits 32 bits."""
+    L = lib()
+    out = ctypes.c_size_t()
+    d = lla.Desc(64, 256, 128, 8, 16.0, flags=lla.LORA_FLAG_W_TRANSPOSED).c()
+    assert L.lora_linear_workspace_size(ctypes.byref(d), ctypes.byref(out)) == _lib.LORA_OK
+    d32 = lla.Desc(64, 256, 128, 8, 16.0, lla.LORA_DTYPE_F32, lla.LORA_FLAG_W_TRANSPOSED).c()
+    assert L.lora_linear_workspace_size(ctypes.byref(d32), ctypes.byref(out)) == _lib.LORA_ERR_UNSUPPORTED
+    p = [ALIGNED + 0x100 * i for i in range(16)]
+    assert L.lora_qlinear_fwd(ctypes.byref(d), *p[:7], None, p[9], 1 << 20, None) == _lib.LORA_ERR_UNSUPPORTED
+    assert L.lora_linear_workspace_size(ctypes.byref(lla.Desc(64, 256, 128, 8, 16.0, flags=0x4).c()),
+                                        ctypes.byref(out)) == _lib.LORA_ERR_INVALID_ARG
+    gd = lla.GroupDesc(64, 256, (256, 64), 16, 32.0, flags=lla.LORA_FLAG_W_TRANSPOSED).c()
+    assert L.lora_group_workspace_size(ctypes.byref(gd), ctypes.byref(out)) == _lib.LORA_OK
+    cfg = _lib.LoraTunedConfig()
+    assert L.lora_tune_linear(ctypes.byref(d), 0, *p[:2], None, None, None, *p[2:11], 1 << 30, None, 3,
+                              ctypes.byref(cfg)) == _lib.LORA_ERR_UNSUPPORTED
+    assert L.lora_transpose_weight(p[0], 128, 252, p[1], None) == _lib.LORA_ERR_UNSUPPORTED
+    assert L.lora_transpose_weight(p[0], 0, 256, p[1], None) == _lib.LORA_ERR_INVALID_ARG
+    assert L.lora_transpose_weight(p[0], 128, 256, p[0], None) == _lib.LORA_ERR_INVALID_ARG
+    assert L.lora_transpose_weight(MISALIGNED, 128, 256, p[1], None) == _lib.LORA_ERR_MISALIGNED
+    big = lla.Desc(4096, 4096, 14336, 64, 16.0, flags=lla.LORA_FLAG_W_TRANSPOSED)
+    ranges = lla.lora_linear_buffer_ranges(big)
+    assert ("lora_gemm (dX)", "W^T panel", 256 * 14336 * 2) in ranges
+    assert all(b <= 2 ** 31 - 1 for _, _, b in ranges)
+
+
 # ------------------------------------------------------------ tuning cache (host only)
 def test_tuner_cache_file_round_trip(tmp_path):
     """Entries loaded from a cache file are found for their (architecture,

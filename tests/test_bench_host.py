@@ -65,7 +65,7 @@ def test_traffic_from_counter_csvs(tmp_path, monkeypatch):
     _write_counters(tmp_path / "copy_WRITE_SIZE_counter_collection.csv", [(neg, "WRITE_SIZE", copy_kib)])
     out = tmp_path / "traffic.json"
     monkeypatch.setattr(bench, "traffic_path", lambda workload: str(out))
-    bench.write_traffic(argparse.Namespace(traffic_from=str(tmp_path), workload="attn_proj_4096"))
+    bench.write_traffic(argparse.Namespace(traffic_from=str(tmp_path), workload="attn_proj_4096", w_layout="wt"))
     t = json.load(open(out))
     f, b = t["kernels"][bench.GEMM_FWD], t["kernels"][bench.GEMM_DX]
     assert f["fetch_kib_per_dispatch"] == 2000.0 and f["write_kib_per_dispatch"] == 500.0
@@ -76,7 +76,9 @@ def test_traffic_from_counter_csvs(tmp_path, monkeypatch):
     assert t["kernel_source_hash"] == bench.kernel_source_hash()
     assert bench.load_traffic("attn_proj_4096") == {bench.GEMM_FWD: 2000 * 2048 + 500 * 1024,
                                                    bench.GEMM_DX: 5000 * 2048 + 700 * 1024}
-    # the stored figures are used only while the GEMM's sources are unchanged
+    # ... only for the backward weight layout they were taken with
+    assert bench.load_traffic("attn_proj_4096", "w") is None
+    # ... and only while the GEMM's sources are unchanged
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 16)
     assert bench.load_traffic("attn_proj_4096") is None
 
@@ -117,7 +119,7 @@ def test_percentile_and_input_sharing():
 def test_missing_counters_are_an_error(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "traffic_path", lambda workload: str(tmp_path / "t.json"))
     with pytest.raises(SystemExit):
-        bench.write_traffic(argparse.Namespace(traffic_from=str(tmp_path), workload="attn_proj_4096"))
+        bench.write_traffic(argparse.Namespace(traffic_from=str(tmp_path), workload="attn_proj_4096", w_layout="wt"))
 
 
 def test_grouped_units_and_counts():

@@ -3,7 +3,8 @@
 Seven LoRA linears (q, k, v, o, gate, up, down; M = 4096, r = 64, alpha = 16)
 go through bench.py's own runner: q/k/v read one X and gate/up read one X
 (bench.share_inputs), every call shares one workspace sized for the largest
-of the seven descriptors (bench.Stepper), the forwards run in order and the
+of the seven descriptors (bench.Stepper), the backward reading W^T
+(bench.add_wt, the default layout), the forwards run in order and the
 backwards in reverse.  Every element of every output of every linear is
 compared with the float64 oracle on the float32 draws (the graded bound), and
 a second step on the same workspace must reproduce the first bit for bit.
@@ -32,6 +33,7 @@ def test_decoder_layer_as_benched():
     bench.share_inputs(wl, layer)
     assert layer[1]["X"] is layer[0]["X"] and layer[5]["X"] is layer[4]["X"]
     bench.add_outputs(lla, torch, wl, layer, dev)
+    bench.add_wt(lla, torch, wl, layer)               # the backward reads W^T, as bench.py does by default
     stepper = bench.Stepper(lla, torch, [layer], dev)
     assert stepper.ws_bytes == max(lla.lora_linear_workspace_size(d["desc"]) for d in layer)
     print(f"decoder layer, one workspace of {stepper.ws_bytes} bytes", flush=True)
@@ -68,6 +70,7 @@ def test_decoder_layer_grouped_as_benched():
     layer = [device_inputs(inp, "bf16") for inp in inps]
     bench.share_inputs(wl, layer)
     bench.add_outputs(lla, torch, wl, layer, dev)
+    bench.add_wt(lla, torch, wl, layer)
     units = bench.step_units(wl, True)
     glayer = bench.group_layer(lla, torch, wl, layer, units, dev)
     stepper = bench.Stepper(lla, torch, [glayer], dev)
@@ -111,6 +114,7 @@ def test_decoder_layer_grouped_norm_as_benched():
     bench.share_inputs(wl, layer)
     bench.add_outputs(lla, torch, wl, layer, dev)
     bench.add_norm(lla, torch, wl, layer, dev, seed=7000)
+    bench.add_wt(lla, torch, wl, layer)
     units = bench.step_units(wl, True)
     glayer = bench.group_layer(lla, torch, wl, layer, units, dev)
     stepper = bench.Stepper(lla, torch, [glayer], dev)

@@ -197,6 +197,21 @@ def test_full_size(wl, idx, dtype):
 
 
 @pytest.mark.slow
+@pytest.mark.parametrize("wl,idx", FULL)
+def test_full_size_w_transposed(wl, idx):
+    """The backward with the frozen weight given as W^T (LORA_FLAG_W_TRANSPOSED,
+    the layout bench.py times): every element against the oracle."""
+    import lora_linear_layer_amd as lla
+    sh = workloads.workload(wl).linears[idx]
+    inp = workloads.make_linear_inputs(sh)
+    print(f"full-size W^T {sh.name} M={sh.M} K={sh.K} N={sh.N} r={sh.r}", flush=True)
+    got = run_linear(inp, sh.r, sh.alpha, "bf16", flags=lla.LORA_FLAG_W_TRANSPOSED)
+    ref = oracle_all(inp, sh.scale)
+    errs = check(got, ref, TOL["bf16"], label=f"{sh.name} W^T graded")
+    print(f"  graded errors {errs}", flush=True)
+
+
+@pytest.mark.slow
 def test_input_over_2gb():
     """X of 262208 x 4096 bf16 (2.15 GB: its last 64 rows lie past 2^31 bytes),
     r = 32, so U = X A^T comes from the streamed pass whose loads address X
