@@ -109,6 +109,8 @@ def parse(argv=None):
                     help="backward weight operand: W^T made once before timing (default), or W")
     ap.add_argument("--norm", action="store_true",
                     help="RMSNorm in front of the linears that read a normalised input")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="also time the vendor GEMM (torch.matmul) on the first linear's X W^T, for reference")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--traffic-from", default=None)
     return ap.parse_args(argv)
@@ -628,6 +630,30 @@ def norm_rooflines(units, kernel_us):
     return out
 
 
+def vendor_gemm(torch, sets, wl, steps, stream):
+    """The first linear's plain product X W^T by torch.matmul (hipBLASLt on
+    ROCm) on the same rotating input sets: a reference for the fused forward
+    GEMM, which also forms U and adds the rank-r term."""
+    l = wl.linears[0]
+    if l.quant4:
+        return None
+    outs = [torch.empty((l.M, l.N), dtype=torch.bfloat16, device=d["X"].device) for d in (s[0] for s in sets)]
+    run = lambda i: torch.matmul(sets[i % len(sets)][0]["X"], sets[i % len(sets)][0]["W"].t(), out=outs[i % len(sets)])
+    for i in range(5):
+        run(i)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for i in range(steps):
+        run(i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / steps
+    fl = 2 * l.M * l.N * l.K
+    return {"kernel": "torch.matmul(X, W.t()) (vendor GEMM, no LoRA terms)", "shape": [l.M, l.K, l.N],
+            "avg_us": round(us, 2), "tflops": round(fl / (us * 1e-6) / 1e12, 1)}
+
+
 def main(argv=None):
     args = parse(argv)
     if args.gpus != 1:
@@ -783,6 +809,8 @@ def main(argv=None):
     }
     if args.norm:
         out["norm_rooflines"] = norm_rooflines(units, kernel_us)
+    if args.vendor_gemm:
+        out["vendor_gemm"] = vendor_gemm(torch, sets, wl, args.steps, stream)
     if not args.no_dequant:
         out["hbm_kernels"] = [dequant_rate(lla, workloads, torch, dev, stream),
                               merge_rate(lla, torch, dev, stream, max(wl.linears, key=lambda l: l.N * l.K))]
