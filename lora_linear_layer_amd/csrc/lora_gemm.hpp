@@ -285,9 +285,9 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
     // publishes it.  512 units per stage, 512 / NT per thread.
     constexpr int QU = Q4 ? 512 / NT : 1;
     u32x4 qreg[QU];
-    float am_reg[QU];
+    uint32_t am_reg[QU];      // fp16 bits: converted at decode, so the load is not waited for at issue
 #pragma unroll
-    for (int u = 0; u < QU; ++u) { qreg[u] = u32x4{0u, 0u, 0u, 0u}; am_reg[u] = 0.f; }
+    for (int u = 0; u < QU; ++u) { qreg[u] = u32x4{0u, 0u, 0u, 0u}; am_reg[u] = 0u; }
     if constexpr (Q4) {
         if (tid < 16) reinterpret_cast<float*>(smem + SM::LUT)[tid] = a.codebook[tid];
     }
@@ -302,14 +302,14 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
                 const bool ok = q0 + q < Q;
                 qreg[u] = ok ? *reinterpret_cast<const u32x4*>(a.Rq + (size_t)(q0 + q) * (C >> 1) + (c0 >> 1) + 16 * hh)
                              : u32x4{0u, 0u, 0u, 0u};
-                am_reg[u] = ok ? f16_bits_to_f32(a.Rabs[(size_t)(q0 + q) * (C >> 6) + kt]) : 0.f;
+                am_reg[u] = ok ? (uint32_t)a.Rabs[(size_t)(q0 + q) * (C >> 6) + kt] : 0u;
             } else {                         // codes [C][Q/2]: row c = unit / 8, weights q0 + 32 (unit % 8) ..
                 const int c = unit >> 3, pp = unit & 7;
                 const bool ok = c0 + c < C && q0 + 32 * pp < Q;
                 const size_t qq = (size_t)q0 + 32 * pp;
                 qreg[u] = ok ? *reinterpret_cast<const u32x4*>(a.Rq + (size_t)(c0 + c) * (Q >> 1) + (qq >> 1))
                              : u32x4{0u, 0u, 0u, 0u};
-                am_reg[u] = ok ? f16_bits_to_f32(a.Rabs[(size_t)(c0 + c) * (Q >> 6) + (qq >> 6)]) : 0.f;
+                am_reg[u] = ok ? (uint32_t)a.Rabs[(size_t)(c0 + c) * (Q >> 6) + (qq >> 6)] : 0u;
             }
         }
     };
@@ -325,13 +325,14 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
             // halves of 4 slots (8 distinct bank groups) instead of one half of
             // 8 slots, of which the swizzle leaves 4 distinct
             u32x4 qv = qreg[u];
+            const float am = f16_bits_to_f32((uint16_t)am_reg[u]);
             const int sh = TRANS ? (unit >> 2) & 1 : 0;
             if (TRANS && sh) qv = u32x4{qv[1], qv[0], qv[3], qv[2]};
             u32x4 outv[4];
 #pragma unroll
             for (int b = 0; b < 16; ++b) {   // byte b holds weights 2b (low nibble) and 2b + 1
                 const uint32_t byte = (qv[b >> 2] >> (8 * (b & 3))) & 0xFFu;
-                const float lo = lut[byte & 15u] * am_reg[u], hi = lut[byte >> 4] * am_reg[u];
+                const float lo = lut[byte & 15u] * am, hi = lut[byte >> 4] * am;
                 outv[b >> 2][b & 3] = pack_bf16x2(lo, hi);
             }
             if constexpr (!TRANS) {          // row q, 16-byte chunks 4h .. 4h + 3, chunk ch at ch ^ (q & 7)
@@ -462,7 +463,7 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
     constexpr int NR_STEP = (RQC ? QB : 2 * QB) + 8 + (ZIN ? 0 : (TRANS ? 2 * JT : JT));
     constexpr int NM_STEP = 8 * QB + (ZIN ? 0 : ZB * JT);
     auto step = [&](const Frags<JT, QB>& cur, Frags<JT, QB>& nxt, const uint8_t* nstage, int nkk, auto do_read,
-                    auto pre) {
+                    auto pre, auto mid) {
         constexpr bool RD = decltype(do_read)::value;
         auto reads = [&] {
             if constexpr (RD) {
@@ -492,8 +493,28 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
         if constexpr (Q4) {
             // the code registers leave no room for both fragment sets during
             // the MFMAs: the reads follow them and the hardware's in-order
-            // issue with the second wave of the SIMD covers their latency
+            // issue with the second wave of the SIMD covers their latency.
+            // `mid` (the next stage's decode) is interleaved with the MFMAs:
+            // its codebook reads, products and packs issue while the MFMA
+            // pipe works, instead of between the steps with the pipe idle
             mfmas();
+            if constexpr (std::decay_t<decltype(mid)>::active()) {
+                mid();
+                // the codebook reads go out over the first half of the MFMAs,
+                // ahead of the products and packs that consume them
+#pragma unroll
+                for (int i = 0; i < NM_STEP / 2; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);    // DS read (codebook)
+                    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);    // VALU (addresses)
+                }
+#pragma unroll
+                for (int i = 0; i < NM_STEP / 2; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);    // VALU (products, packs)
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
             reads();
             return;
         }
@@ -525,6 +546,16 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
         int kt;
         bool on;
         __device__ void operator()() const { (*f)(kt, on); }
+    };
+    struct NoMid {
+        static constexpr bool active() { return false; }
+        __device__ void operator()() const {}
+    };
+    struct DecodeMid {
+        static constexpr bool active() { return true; }
+        decltype(decode_q)* f;
+        int kt;
+        __device__ void operator()() const { (*f)(kt); }
     };
     using Read = std::true_type;
     using NoRead = std::false_type;
@@ -566,20 +597,22 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
     for (int kt = 0; kt + 1 < nk; ++kt) {
         const uint8_t* const cur = smem + (kt & 1) * SM::STAGE;
         const uint8_t* const nxt = smem + ((kt + 1) & 1) * SM::STAGE;
-        step(fa, fb, cur, 1, Read{}, NoPre{});
-        if constexpr (Q4) decode_q(kt + 1);  // R tile of stage kt + 1 from the registers loaded at its issue
+        // (4-bit: the R tile of stage kt + 1 decoded from the registers loaded at
+        // its issue, interleaved with this step's MFMAs)
+        if constexpr (Q4) step(fa, fb, cur, 1, Read{}, NoPre{}, DecodeMid{&decode_q, kt + 1});
+        else step(fa, fb, cur, 1, Read{}, NoPre{}, NoMid{});
         vmcnt_le<0>();           // this wave's loads of stage kt + 1 have landed
         lds_barrier();           // ... and everyone's; stage kt's slot is free
         if constexpr (Q4) {
             if (kt + 2 < nk) { issue_lr(kt + 2, true); issue_f(kt + 2); }
-            step(fb, fa, nxt, 0, Read{}, NoPre{});
+            step(fb, fa, nxt, 0, Read{}, NoPre{}, NoMid{});
         } else {
             if (kt + 2 < nk) issue_f(kt + 2);
-            step(fb, fa, nxt, 0, Read{}, StagePre{&issue_lr, kt + 2, kt + 2 < nk});
+            step(fb, fa, nxt, 0, Read{}, StagePre{&issue_lr, kt + 2, kt + 2 < nk}, NoMid{});
         }
     }
-    step(fa, fb, smem + ((nk - 1) & 1) * SM::STAGE, 1, Read{}, NoPre{});
-    step(fb, fa, smem, 0, NoRead{}, NoPre{});
+    step(fa, fb, smem + ((nk - 1) & 1) * SM::STAGE, 1, Read{}, NoPre{}, NoMid{});
+    step(fb, fa, smem, 0, NoRead{}, NoPre{}, NoMid{});
     vmcnt_le<0>();               // the last iteration's placeholder loads have written their zeros
 
     // ------------------------------------------------------------ epilogue
