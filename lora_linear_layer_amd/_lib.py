@@ -9,7 +9,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "liblora_linear.so")
+# LORA_LINEAR_LIB selects another build of the same library (e.g. one with the
+# host code instrumented by a sanitizer); the in-tree build is the default.
+LIB_PATH = os.environ.get("LORA_LINEAR_LIB") or os.path.join(HERE, "liblora_linear.so")
 
 LORA_OK = 0
 LORA_ERR_INVALID_ARG = 1
