@@ -14,7 +14,7 @@ import math
 import torch
 
 from . import api
-from ._lib import LORA_DTYPE_BF16, LORA_DTYPE_F32
+from ._lib import LORA_DTYPE_BF16, LORA_DTYPE_F32, LORA_FLAG_W_TRANSPOSED
 
 _DTYPES = {torch.bfloat16: LORA_DTYPE_BF16, torch.float32: LORA_DTYPE_F32}
 
@@ -36,10 +36,14 @@ def _same(x, **ts):
 
 
 class LoraLinearFunction(torch.autograd.Function):
-    """H = X W^T + (alpha/r) (X A^T) B^T with W frozen (no gradient for W)."""
+    """H = X W^T + (alpha/r) (X A^T) B^T with W frozen (no gradient for W).
+
+    Wt (optional, bf16 [in, out]): W^T made once from the frozen weight; the
+    backward then reads it (LORA_FLAG_W_TRANSPOSED) instead of W, with
+    bit-identical results."""
 
     @staticmethod
-    def forward(ctx, x, W, A, B, alpha):
+    def forward(ctx, x, W, A, B, alpha, Wt=None):
         lead = x.shape[:-1]
         K = x.shape[-1]
         X = x.reshape(-1, K).contiguous()
@@ -50,6 +54,13 @@ class LoraLinearFunction(torch.autograd.Function):
         U = torch.empty((X.shape[0], r), dtype=torch.float32, device=X.device)
         ws = torch.empty(max(api.lora_linear_workspace_size(desc), 1), dtype=torch.uint8, device=X.device)
         api.lora_linear_fwd(desc, X, W.contiguous(), A.contiguous(), B.contiguous(), H, U, ws=ws)
+        if Wt is not None:
+            _same(X, Wt=Wt)
+            if tuple(Wt.shape) != (K, N):
+                raise ValueError(f"Wt has shape {tuple(Wt.shape)}, expected {(K, N)}")
+            desc = api.Desc(desc.M, desc.K, desc.N, desc.r, desc.alpha, desc.dtype,
+                            desc.flags | LORA_FLAG_W_TRANSPOSED)
+            W = Wt
         ctx.save_for_backward(X, W, A, B, U)
         ctx.desc = desc
         ctx.lead = lead
@@ -66,7 +77,7 @@ class LoraLinearFunction(torch.autograd.Function):
         ws = torch.empty(max(api.lora_linear_workspace_size(desc), 1), dtype=torch.uint8, device=X.device)
         api.lora_linear_bwd(desc, dY, X, W.contiguous(), A.contiguous(), B.contiguous(), U, dX, dA, dB, ws=ws)
         dx = dX.reshape(*ctx.lead, desc.K) if dX is not None else None
-        return dx, None, dA, dB, None
+        return dx, None, dA, dB, None, None
 
 
 class QLoraLinearFunction(torch.autograd.Function):
@@ -106,10 +117,15 @@ class QLoraLinearFunction(torch.autograd.Function):
 class LoraLinear(torch.nn.Module):
     """Frozen W [out, in] plus trainable A [r, in], B [out, r]; s = alpha / r.
 
-    B starts at zero, so the layer starts as the frozen linear.
+    B starts at zero, so the layer starts as the frozen linear.  With
+    keep_transposed_weight (bf16 on a GPU) the module also holds W^T as a
+    buffer, made once, and its backward reads that (faster input-gradient GEMM,
+    bit-identical results, one more copy of W in memory); call
+    refresh_transposed_weight() after changing the weight.
     """
 
-    def __init__(self, in_features, out_features, r, alpha, weight=None, dtype=torch.bfloat16, device=None):
+    def __init__(self, in_features, out_features, r, alpha, weight=None, dtype=torch.bfloat16, device=None,
+                 keep_transposed_weight=False):
         super().__init__()
         self.r, self.alpha = r, float(alpha)
         w = weight if weight is not None else torch.empty(out_features, in_features, dtype=dtype, device=device)
@@ -117,13 +133,24 @@ class LoraLinear(torch.nn.Module):
         self.lora_A = torch.nn.Parameter(torch.empty(r, in_features, dtype=dtype, device=device))
         self.lora_B = torch.nn.Parameter(torch.zeros(out_features, r, dtype=dtype, device=device))
         torch.nn.init.normal_(self.lora_A, std=1.0 / math.sqrt(in_features))
+        self.weight_t = None
+        if keep_transposed_weight:
+            self.register_buffer("weight_t", torch.empty(in_features, out_features, dtype=dtype, device=device))
+            self.refresh_transposed_weight()
+
+    @torch.no_grad()
+    def refresh_transposed_weight(self):
+        """weight_t = weight^T (lora_transpose_weight)."""
+        if self.weight_t is None:
+            raise RuntimeError("the module was built without keep_transposed_weight")
+        api.lora_transpose_weight(self.weight.contiguous(), self.weight_t)
 
     def forward(self, x):
         # the layer computes in its parameters' dtype (e.g. float32 activations
         # from an autocast region are converted to bf16 here)
         if x.dtype != self.weight.dtype:
             x = x.to(self.weight.dtype)
-        return LoraLinearFunction.apply(x, self.weight, self.lora_A, self.lora_B, self.alpha)
+        return LoraLinearFunction.apply(x, self.weight, self.lora_A, self.lora_B, self.alpha, self.weight_t)
 
     @torch.no_grad()
     def merged_weight(self, sign: int = 1) -> torch.Tensor:

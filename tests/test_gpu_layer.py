@@ -90,3 +90,35 @@ def test_module_merged_weight_reproduces_forward(dtype):
         layer.weight.copy_(Wm)
         restored = layer.merged_weight(-1)
     assert rel_err(to_np(restored), hv["W"]) <= (2 ** -7 if dtype == "bf16" else 1e-6)
+
+
+def test_module_with_transposed_weight_is_bit_identical():
+    """LoraLinear(keep_transposed_weight=True): the backward reads the module's
+    W^T buffer; outputs and gradients bit-identical to the module without it,
+    also after the weight changes and refresh_transposed_weight()."""
+    from lora_linear_layer_amd.layer import LoraLinear
+    sh = workloads.LinearShape("layer_wt", 300, 520, 264, 16, 32.0, 23)
+    inp = workloads.make_linear_inputs(sh)
+    bf = torch.bfloat16
+    mods = [LoraLinear(sh.K, sh.N, sh.r, sh.alpha, weight=to_dev(inp["W"], bf), device="cuda",
+                       keep_transposed_weight=k) for k in (False, True)]
+    for m in mods:
+        with torch.no_grad():
+            m.lora_A.copy_(to_dev(inp["A"], bf))
+            m.lora_B.copy_(to_dev(inp["B"], bf))
+    assert mods[1].weight_t.shape == (sh.K, sh.N)
+    for step in range(2):
+        res = []
+        for m in mods:
+            m.zero_grad(set_to_none=True)
+            x = to_dev(inp["X"], bf).requires_grad_(True)
+            y = m(x)
+            y.backward(to_dev(inp["dY"], bf))
+            res.append([y, x.grad, m.lora_A.grad, m.lora_B.grad])
+        torch.cuda.synchronize()
+        for name, a, b in zip(("H", "dX", "dA", "dB"), *res):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"step {step}: {name}"
+        with torch.no_grad():                      # a new frozen weight for the second round
+            for m in mods:
+                m.weight.mul_(0.5)
+            mods[1].refresh_transposed_weight()
