@@ -291,19 +291,38 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
     if constexpr (Q4) {
         if (tid < 16) reinterpret_cast<float*>(smem + SM::LUT)[tid] = a.codebook[tid];
     }
+    // Forward 4-bit codes [Q][C/2]: a stage is 32 bytes of each weight row, half
+    // of a 64-byte request, so the codes of two stages are fetched together as
+    // one 64-byte run per row (pieces 0, 1: the even stage; 2, 3: the odd one).
+    // Lane l of wave w takes piece l % 4 of row 16 w + l / 4 and piece
+    // (l % 4 + 2) % 4 of the row 128 below: one piece of each stage, so each
+    // stage's decode stays one 16-byte piece per lane.
+    static_assert(!Q4 || TRANS || (NT == 512 && QU == 1), "paired code loads: 512 threads");
+    const int qrA = wave * 16 + (lane >> 2), qrB = qrA + 128;
+    const int qp1 = lane & 3, qp2 = (qp1 + 2) & 3;
+    u32x4 qregB = {0u, 0u, 0u, 0u};
+    uint32_t amB = 0u;
     auto load_q = [&](int kt0) {
         const int kt = kbase + kt0;              // stage of the whole contraction
         const int c0 = kt * BK;
+        if constexpr (!TRANS) {
+            if (kt0 & 1) return;                 // fetched with the even stage before it
+            auto piece = [&](int row, int p, u32x4& qv, uint32_t& am) {
+                const int st = kt + (p >> 1);
+                const bool ok = q0 + row < Q && st * BK < C;
+                qv = ok ? *reinterpret_cast<const u32x4*>(a.Rq + (size_t)(q0 + row) * (C >> 1) + (size_t)kt * (BK / 2) +
+                                                          16 * p)
+                        : u32x4{0u, 0u, 0u, 0u};
+                am = ok ? (uint32_t)a.Rabs[(size_t)(q0 + row) * (C >> 6) + st] : 0u;
+            };
+            piece(qrA, qp1, qreg[0], am_reg[0]);
+            piece(qrB, qp2, qregB, amB);
+            return;
+        }
 #pragma unroll
         for (int u = 0; u < QU; ++u) {
             const int unit = tid + u * NT;
-            if constexpr (!TRANS) {          // codes [Q][C/2]: row q = unit / 2, weights c0 + 32 (unit % 2) ..
-                const int q = unit >> 1, hh = unit & 1;
-                const bool ok = q0 + q < Q;
-                qreg[u] = ok ? *reinterpret_cast<const u32x4*>(a.Rq + (size_t)(q0 + q) * (C >> 1) + (c0 >> 1) + 16 * hh)
-                             : u32x4{0u, 0u, 0u, 0u};
-                am_reg[u] = ok ? (uint32_t)a.Rabs[(size_t)(q0 + q) * (C >> 6) + kt] : 0u;
-            } else {                         // codes [C][Q/2]: row c = unit / 8, weights q0 + 32 (unit % 8) ..
+            {                                // codes [C][Q/2]: row c = unit / 8, weights q0 + 32 (unit % 8) ..
                 const int c = unit >> 3, pp = unit & 7;
                 const bool ok = c0 + c < C && q0 + 32 * pp < Q;
                 const size_t qq = (size_t)q0 + 32 * pp;
@@ -325,7 +344,15 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
             // halves of 4 slots (8 distinct bank groups) instead of one half of
             // 8 slots, of which the swizzle leaves 4 distinct
             u32x4 qv = qreg[u];
-            const float am = f16_bits_to_f32((uint16_t)am_reg[u]);
+            uint32_t amb = am_reg[u];
+            int fq = 0, fh = 0;                // forward: the row and half (stage piece) this lane decodes
+            if constexpr (!TRANS) {
+                const bool useA = (qp1 < 2) == ((kt & 1) == 0);
+                if (!useA) { qv = qregB; amb = amB; }
+                fq = useA ? qrA : qrB;
+                fh = (useA ? qp1 : qp2) & 1;
+            }
+            const float am = f16_bits_to_f32((uint16_t)amb);
             const int sh = TRANS ? (unit >> 2) & 1 : 0;
             if (TRANS && sh) qv = u32x4{qv[1], qv[0], qv[3], qv[2]};
             u32x4 outv[4];
@@ -336,7 +363,7 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
                 outv[b >> 2][b & 3] = pack_bf16x2(lo, hi);
             }
             if constexpr (!TRANS) {          // row q, 16-byte chunks 4h .. 4h + 3, chunk ch at ch ^ (q & 7)
-                const int q = unit >> 1, hh = unit & 1;
+                const int q = fq, hh = fh;
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     *reinterpret_cast<u32x4*>(Rs + q * 128 + (((4 * hh + i) ^ (q & 7)) << 4)) = outv[i];

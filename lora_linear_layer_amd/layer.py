@@ -133,9 +133,9 @@ class LoraLinear(torch.nn.Module):
         self.lora_A = torch.nn.Parameter(torch.empty(r, in_features, dtype=dtype, device=device))
         self.lora_B = torch.nn.Parameter(torch.zeros(out_features, r, dtype=dtype, device=device))
         torch.nn.init.normal_(self.lora_A, std=1.0 / math.sqrt(in_features))
-        self.weight_t = None
+        wt = torch.empty(in_features, out_features, dtype=dtype, device=device) if keep_transposed_weight else None
+        self.register_buffer("weight_t", wt, persistent=False)   # derived from weight: not saved
         if keep_transposed_weight:
-            self.register_buffer("weight_t", torch.empty(in_features, out_features, dtype=dtype, device=device))
             self.refresh_transposed_weight()
 
     @torch.no_grad()
