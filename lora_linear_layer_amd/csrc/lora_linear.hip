@@ -1440,7 +1440,7 @@ lora_status lora_tune_linear(const lora_linear_desc* desc, int32_t quant, const 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipEvent_t e0 = nullptr, e1 = nullptr;
     if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
-        if (e0) hipEventDestroy(e0);
+        if (e0) (void)hipEventDestroy(e0);
         return fail(LORA_ERR_HIP, "hipEventCreate failed");
     }
     lora_status err = LORA_OK;
@@ -1457,16 +1457,18 @@ lora_status lora_tune_linear(const lora_linear_desc* desc, int32_t quant, const 
         std::vector<std::vector<float>> t(cand.size());
         for (int round = 0; round <= reps && err == LORA_OK; ++round) {
             for (size_t i = 0; i < cand.size() && err == LORA_OK; ++i) {
-                hipEventRecord(e0, s);
-                err = run(cand[i]);
-                hipEventRecord(e1, s);
-                if (err != LORA_OK) break;
-                if (hipEventSynchronize(e1) != hipSuccess) {
-                    err = fail(LORA_ERR_HIP, "hipEventSynchronize failed");
+                if (hipEventRecord(e0, s) != hipSuccess) {
+                    err = fail(LORA_ERR_HIP, "hipEventRecord failed");
                     break;
                 }
+                err = run(cand[i]);
+                if (err != LORA_OK) break;
                 float ms = 0.f;
-                hipEventElapsedTime(&ms, e0, e1);
+                if (hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+                    hipEventElapsedTime(&ms, e0, e1) != hipSuccess) {
+                    err = fail(LORA_ERR_HIP, "timing a candidate failed");
+                    break;
+                }
                 if (round > 0) t[i].push_back(ms * 1e3f);
             }
         }
@@ -1539,8 +1541,8 @@ lora_status lora_tune_linear(const lora_linear_desc* desc, int32_t quant, const 
     const size_t bb = err == LORA_OK ? pick(mb) : 0;
     best = bc[bb];
     const float t_fwd = mf[bf], t_fwd_default = mf[0], t_bwd = mb[bb], t_bwd_default = mb[0];
-    hipEventDestroy(e0);
-    hipEventDestroy(e1);
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
     if (err != LORA_OK) return err;
     {
         std::lock_guard<std::mutex> lock(g_tune_mu);
