@@ -334,9 +334,9 @@ lora_status lora_linear_buffer_ranges(const lora_linear_desc* desc, int32_t quan
  * with the GPU, the sequence length and the rank, so it is probed on the first
  * run and cached for reuse).  The tuned parameters of the bf16 path are
  *   fwd_split, bwd_split  contraction split of the forward / input-gradient
- *                         GEMM: 0 the built-in rule for the weight format, 1 no
+ *                         GEMM: 0 the built-in rule (the same as 3), 1 no
  *                         split, 2 split outputs of under 128 tiles only, 3 also
- *                         split the tiles of a partly filled last round;
+ *                         split the tiles of a last round at most half full;
  *   rank_div              the adapter-gradient pass's token chunks: the
  *                         built-in count divided by 1, 2 or 4;
  *   z_div_fwd, z_div_bwd  the streamed U (forward) / V and U (backward) passes'

@@ -223,11 +223,15 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
     const int nPt = (P + BP - 1) / BP, nQt = (Q + BQ - 1) / BQ;
     int pt, qt, kbase = 0, slice = -1, stile = 0;   // slice -1: whole tile
     if constexpr (SPLIT) {
-        const int T = nPt * nQt;
-        const int u = xcd_contiguous(blockIdx.x, a.first_split + (T - a.first_split) * a.split);
-        int tile = u;
-        if (u >= a.first_split) {
-            const int v = u - a.first_split;
+        // whole tiles first, then the slices, each set spread evenly over the
+        // XCDs on its own (one mapping over both gave some XCDs only whole
+        // tiles and others only slices)
+        const int T = nPt * nQt, b = blockIdx.x;
+        int tile;
+        if (b < a.first_split) {
+            tile = xcd_contiguous(b, a.first_split);
+        } else {
+            const int v = xcd_contiguous(b - a.first_split, (T - a.first_split) * a.split);
             stile = v / a.split;
             slice = v % a.split;
             kbase = slice * a.kc;

@@ -95,24 +95,24 @@ int rpad_of(int64_t r) { return r <= 16 ? 16 : r <= 32 ? 32 : r <= 64 ? 64 : 128
 
 // Contraction slices of a GEMM (precomputed-Z form).  An output with under
 // 128 tiles of 256 x 256 splits every tile (about 256 workgroups).  With
-// 4-bit weights, an output of more than 256 tiles whose last round is at most
-// half full also splits the tiles of that round, so it runs as a full round
-// of shorter work (measured on 2048 x 8192 -> 28672: 1226 -> 1205 us; the
-// same split of bf16 GEMMs measured slower, 477 -> 498 us on
-// 4096 x 4096 -> 14336, so they keep whole tiles).  Every slice gets at least
-// one 64-wide stage, and at least two when the contraction allows.
+// tail, an output of more than 256 tiles whose last round is at most half full
+// also splits the tiles of that round, so it runs as a full round of shorter
+// work instead of a round with idle CUs, which takes about 80 % of a full
+// round's time (4-bit 2048 x 8192 -> 28672 forward 1040 -> 951-985 us, bf16
+// 4096 x 4096 -> 14336 410 -> 396-402 us).  Every slice gets at least one
+// 64-wide stage, and at least two when the contraction allows.
 struct SplitPlan {
     int first = 0, split = 1, kc = 0;
     size_t part_floats = 0;          // float32 partial tiles in the workspace
 };
 
-SplitPlan gemm_split_plan(int64_t P, int64_t Q, int64_t C, bool quant) {
+SplitPlan gemm_split_plan(int64_t P, int64_t Q, int64_t C, bool tail = true) {
     SplitPlan sp;
     const int64_t T = cdiv(P, 256) * cdiv(Q, 256), nk = cdiv(C, 64);
     int64_t first = 0, want = 1;
     if (T < 128) {
         want = std::min<int64_t>(cdiv(256, T), nk / 2);
-    } else if (quant && T > 256 && T % 256 != 0 && T % 256 <= 128) {
+    } else if (tail && T > 256 && T % 256 != 0 && T % 256 <= 128) {
         first = T - T % 256;
         want = std::min<int64_t>(256 / (T % 256), nk / 2);
     }
@@ -129,19 +129,18 @@ SplitPlan gemm_split_plan(int64_t P, int64_t Q, int64_t C, bool quant) {
 // contraction-split rules whose partial tiles it already holds, and the chunk
 // counts are the model's divided by a power of two.
 struct Tuning {
-    int fwd_split = 0;      // forward GEMM: 0 the rule for the weight format, 1 no split,
+    int fwd_split = 0;      // forward GEMM: 0 the built-in rule (= 3), 1 no split,
     int bwd_split = 0;      //   2 few-tile outputs only, 3 also the last partial round (input gradient: bwd_split)
     int rank_div = 1;       // rank_stream token chunks: the model's count / rank_div
     int z_div_f = 1;        // rank_z_lds contraction chunks (forward U pass): the model's / z_div_f
     int z_div_b = 1;        // (backward V and U passes)
 };
 
-SplitPlan split_for(int mode, int64_t P, int64_t Q, int64_t C, bool quant) {
+SplitPlan split_for(int mode, int64_t P, int64_t Q, int64_t C) {
     switch (mode) {
         case 1: return SplitPlan{};
         case 2: return gemm_split_plan(P, Q, C, false);
-        case 3: return gemm_split_plan(P, Q, C, true);
-        default: return gemm_split_plan(P, Q, C, quant);
+        default: return gemm_split_plan(P, Q, C, true);
     }
 }
 
@@ -196,7 +195,6 @@ struct Shape {
     float alpha = 0.f;
     int32_t dtype = LORA_DTYPE_BF16;
     uint32_t flags = 0;
-    bool quant_capable = true;      // workspace also sized for the 4-bit entry points (plain layers)
     bool norm = false;              // RMSNorm in front (1 / rms per row and A diag(g) in the workspace)
     int64_t rg() const { return (int64_t)G * r; }      // rank of the stacked A, U and V
     int64_t Nm(int m) const { return n0[m + 1] - n0[m]; }
@@ -269,11 +267,10 @@ Plan make_plan(const Shape& d) {
         p.off_bt = cur;                                  // B^T per member: bf16 [r][N_m], members side by side
         cur += align_up((size_t)d.r * d.N * sizeof(uint16_t));
         p.off_split = cur;                               // float32 partial tiles of a split contraction
-        // sized for the 4-bit plans, which split a superset of the bf16 ones, when
-        // the 4-bit entry points share the descriptor
-        const bool q = d.quant_capable;
-        const size_t n_split = std::max(gemm_split_plan(d.M, d.N, d.K, q).part_floats,
-                                        gemm_split_plan(d.M, d.K, d.N, q).part_floats);
+        // sized for the built-in plans, which split a superset of the tiles any
+        // tuned split mode splits
+        const size_t n_split = std::max(gemm_split_plan(d.M, d.N, d.K).part_floats,
+                                        gemm_split_plan(d.M, d.K, d.N).part_floats);
         cur += align_up(n_split * sizeof(float));
         if (d.norm) {
             p.off_inv = cur;
@@ -323,7 +320,6 @@ Shape shape_of(const lora_group_desc& g) {
     s.alpha = g.alpha;
     s.dtype = g.dtype;
     s.flags = g.flags;
-    s.quant_capable = false;
     return s;
 }
 
@@ -639,7 +635,7 @@ lora_status fwd_bf16(const Shape& d, bool quant, const void* X, const void* W, c
     const uint16_t* const X16 = static_cast<const uint16_t*>(X);
     const uint16_t* const A16 = static_cast<const uint16_t*>(A);
     float* const zpart = reinterpret_cast<float*>(wsb + plan.off_zp);
-    const SplitPlan sp = split_for(tn.fwd_split, d.M, d.N, d.K, quant);
+    const SplitPlan sp = split_for(tn.fwd_split, d.M, d.N, d.K);
     const bool in_tile = d.G == 1 && gemm_in_tile(quant, r, sp);
     float* U = U_save;
     if (!in_tile) {
@@ -704,7 +700,7 @@ lora_status bwd_bf16(const Shape& d, bool quant, const void* dY, const void* X, 
     }
     // 2. V = dY B: inside the dX GEMM when it runs in the in-tile form,
     //    else the streamed pass of each member over its columns of dY
-    const SplitPlan sp = split_for(tn.bwd_split, d.M, d.K, d.N, quant);
+    const SplitPlan sp = split_for(tn.bwd_split, d.M, d.K, d.N);
     const bool v_in_tile = dX != nullptr && d.G == 1 && dx_in_tile(quant, r, sp);
     if (!v_in_tile) {
         uint16_t* const BT = reinterpret_cast<uint16_t*>(wsb + plan.off_bt);
@@ -874,12 +870,12 @@ lora_status scratch_on_current_device(void** out) {
 
 // Bytes of the backward's intermediates for a 16-bit weight: the workspace
 // layout up to its last region, plus the float32 slices of the input
-// gradient's own split contraction (the workspace is sized for the 4-bit
-// plans too, whose forward splits more).
+// gradient's own split contraction (the workspace holds the larger of the
+// forward's and the input gradient's).
 size_t bwd_scratch_bytes(const Shape& d) {
     const Plan p = make_plan(d);
     if (d.dtype != LORA_DTYPE_BF16) return p.total;
-    return p.off_split + align_up(gemm_split_plan(d.M, d.K, d.N, false).part_floats * sizeof(float));
+    return p.off_split + align_up(gemm_split_plan(d.M, d.K, d.N).part_floats * sizeof(float));
 }
 
 // ---------------------------------------------------------------- auto-tuner
@@ -983,8 +979,8 @@ void buffer_ranges(const Shape& d, bool quant, RangeList& L) {
     if (d.dtype != LORA_DTYPE_BF16) return;          // the float32 mode uses plain loads only
     const int r = (int)d.r;
     const int64_t rg = d.rg();
-    const SplitPlan spf = gemm_split_plan(d.M, d.N, d.K, quant);
-    const SplitPlan spb = gemm_split_plan(d.M, d.K, d.N, quant);
+    const SplitPlan spf = gemm_split_plan(d.M, d.N, d.K);
+    const SplitPlan spb = gemm_split_plan(d.M, d.K, d.N);
     // forward (U by the streamed pass when it is not formed in the tile)
     const bool fwd_in_tile = d.G == 1 && gemm_in_tile(quant, r, spf);
     rank_z_ranges(L, "rank_z_lds (U = X A^T)", d.M, d.K, d.K, rg);   // forward, or a backward without U
@@ -1493,9 +1489,9 @@ lora_status lora_tune_linear(const lora_linear_desc* desc, int32_t quant, const 
     // distinct split modes of a GEMM (modes giving the same plan are one candidate)
     auto split_modes = [&](int64_t P, int64_t Qd, int64_t C) {
         std::vector<int> modes{0};
-        std::vector<SplitPlan> seen{split_for(0, P, Qd, C, q)};
+        std::vector<SplitPlan> seen{split_for(0, P, Qd, C)};
         for (int mode = 1; mode <= 3; ++mode) {
-            const SplitPlan sp = split_for(mode, P, Qd, C, q);
+            const SplitPlan sp = split_for(mode, P, Qd, C);
             if (std::none_of(seen.begin(), seen.end(), [&](const SplitPlan& o) { return same_split(o, sp); })) {
                 seen.push_back(sp);
                 modes.push_back(mode);
@@ -1513,7 +1509,7 @@ lora_status lora_tune_linear(const lora_linear_desc* desc, int32_t quant, const 
     // forward: contraction split x the U pass's chunks (when U is streamed)
     std::vector<Tuning> fc;
     for (int mode : split_modes(d.M, d.N, d.K)) {
-        const bool u_streamed = !gemm_in_tile(q, (int)d.r, split_for(mode, d.M, d.N, d.K, q));
+        const bool u_streamed = !gemm_in_tile(q, (int)d.r, split_for(mode, d.M, d.N, d.K));
         for (int zd : u_streamed ? divisors(z_chunks(d.M, d.K)) : std::vector<int>{1}) {
             Tuning c;
             c.fwd_split = mode;
@@ -1527,7 +1523,7 @@ lora_status lora_tune_linear(const lora_linear_desc* desc, int32_t quant, const 
     // backward: contraction split x adapter-gradient chunks x the V pass's chunks (when V is streamed)
     std::vector<Tuning> bc;
     for (int mode : split_modes(d.M, d.K, d.N)) {
-        const bool v_streamed = !dx_in_tile(q, (int)d.r, split_for(mode, d.M, d.K, d.N, q));
+        const bool v_streamed = !dx_in_tile(q, (int)d.r, split_for(mode, d.M, d.K, d.N));
         for (int rd : divisors(split_g(d).n_chunk))
             for (int zd : v_streamed ? divisors(z_chunks(d.M, d.N)) : std::vector<int>{1}) {
                 Tuning c = best;
