@@ -50,8 +50,9 @@
 // instead of the direct LDS path: each thread loads 16 code bytes (32 weights
 // of one row inside one 64-block) and that block's absmax when the stage is
 // issued, and one step later decodes them, codebook[code] * absmax in float32
-// rounded to bf16 (the standalone dequantisation's exact values), into the
-// stage's R tile in the same swizzled layout, before the barrier that
+// rounded to bf16 (the standalone dequantisation's exact values; the 16
+// possible values of a block are formed once and looked up in registers), into
+// the stage's R tile in the same swizzled layout, before the barrier that
 // publishes the stage.  Every weight is decoded once per workgroup; the
 // reads, MFMAs and epilogue are the 16-bit kernel's.
 #pragma once
@@ -187,6 +188,50 @@ struct Frags {
     bf16x8 l[8];      // L, 8 p blocks of 16 (slot i = block (i + ZB wq) % 8)
     bf16x8 f[JT];     // F, rank rows
 };
+
+// 4-bit decode in registers.  The 16 values bf16(codebook[n] * absmax) of one
+// absmax block are formed once per lane (16 float32 products, rounded as when
+// each weight's product is formed on its own) and kept as byte tables: lb[g]
+// holds the low bytes of entries 4g .. 4g + 3, hb[g] their high bytes.
+// v_perm_b32 looks up four codes per instruction in each 8-entry half, and one
+// more picks the half by bit 3 of each code.  This replaces one LDS read of the
+// codebook per weight, which held both 4-bit GEMMs back by about 12 %.
+struct Q4Lut {
+    uint32_t lb[4], hb[4];
+};
+
+// byte i of the result = byte sel_i (0 .. 7) of the 8-byte value {hi : lo}
+__device__ __forceinline__ uint32_t vperm(uint32_t hi, uint32_t lo, uint32_t sel) {
+    return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+__device__ __forceinline__ Q4Lut q4_lut(const float* lut, float am) {
+    Q4Lut t;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(lut + 4 * g);   // one address for all lanes
+        const uint32_t t01 = pack_bf16x2(v[0] * am, v[1] * am), t23 = pack_bf16x2(v[2] * am, v[3] * am);
+        t.lb[g] = vperm(t23, t01, 0x06040200u);
+        t.hb[g] = vperm(t23, t01, 0x07050301u);
+    }
+    return t;
+}
+
+// One code dword (byte k: code 2k in the low nibble, code 2k + 1 in the high
+// one) -> o[k] = the bf16 pair of codes 2k, 2k + 1.
+__device__ __forceinline__ void q4_decode8(const Q4Lut& t, uint32_t q, uint32_t* o) {
+    const uint32_t ln = q & 0x0F0F0F0Fu, hn = (q >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t n = vperm(hn, ln, h ? 0x07030602u : 0x05010400u);   // codes 4h .. 4h + 3, one per byte
+        const uint32_t sel = n & 0x07070707u;
+        const uint32_t half = ((n >> 1) & 0x04040404u) | 0x03020100u;      // byte i: i, or i + 4 for codes >= 8
+        const uint32_t lo = vperm(vperm(t.lb[3], t.lb[2], sel), vperm(t.lb[1], t.lb[0], sel), half);
+        const uint32_t hi = vperm(vperm(t.hb[3], t.hb[2], sel), vperm(t.hb[1], t.hb[0], sel), half);
+        o[2 * h] = vperm(hi, lo, 0x05010400u);
+        o[2 * h + 1] = vperm(hi, lo, 0x07030602u);
+    }
+}
 
 // SPLIT = true (precomputed Z only): tiles below first_split run whole; the
 // others run as `split` workgroups each, slice v covering the contraction
@@ -359,12 +404,13 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
             const float am = f16_bits_to_f32((uint16_t)amb);
             const int sh = TRANS ? (unit >> 2) & 1 : 0;
             if (TRANS && sh) qv = u32x4{qv[1], qv[0], qv[3], qv[2]};
+            const Q4Lut tab = q4_lut(lut, am);
             u32x4 outv[4];
 #pragma unroll
-            for (int b = 0; b < 16; ++b) {   // byte b holds weights 2b (low nibble) and 2b + 1
-                const uint32_t byte = (qv[b >> 2] >> (8 * (b & 3))) & 0xFFu;
-                const float lo = lut[byte & 15u] * am, hi = lut[byte >> 4] * am;
-                outv[b >> 2][b & 3] = pack_bf16x2(lo, hi);
+            for (int i = 0; i < 4; ++i) {    // code dword i -> output chunk i (8 weights)
+                uint32_t o[4];
+                q4_decode8(tab, qv[i], o);
+                outv[i] = u32x4{o[0], o[1], o[2], o[3]};
             }
             if constexpr (!TRANS) {          // row q, 16-byte chunks 4h .. 4h + 3, chunk ch at ch ^ (q & 7)
                 const int q = fq, hh = fh;
