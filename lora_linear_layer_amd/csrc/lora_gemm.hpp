@@ -130,12 +130,12 @@ struct GemmArgs {
     const uint16_t* E;      // forward: B [Q][r]; input gradient: A [r][Q]
     const float* Zin;       // precomputed Z [P][r] (ZIN), else unused
     uint16_t* Out;          // [P][Q] bf16
-    float* Zsave;           // [P][r] float32 or nullptr (written by the q-tile-0 workgroups)
+    float* Zsave;           // [P][r] float32 or nullptr (each row by one workgroup of its row panel)
     float* Part;            // split contraction: float32 partial tiles [split][tile - first_split][256][256]
     // Input gradient, in-tile Z only: the bf16 planes hi = bf16(Z^T), lo = bf16(Z^T - hi) of
     // Z = V and of U (read from Uin [P][r] float32), [r][Mp] in the token-block-major order of
-    // zt_index, tokens p >= P zero; written by
-    // the q-tile-0 workgroups for the adapter-gradient pass, or not at all when Zt_hi is nullptr
+    // zt_index, tokens p >= P zero; written (each row by one workgroup of its row panel) for the
+    // adapter-gradient pass, or not at all when Zt_hi is nullptr
     uint16_t *Zt_hi, *Zt_lo, *Ut_hi, *Ut_lo;
     const float* Uin;
     int Mp;
@@ -780,6 +780,13 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
 
     lds_barrier();   // every wave is done with the last stage before LDS is reused
     float* const Zx = reinterpret_cast<float*>(smem);   // [256][RPAD] float32
+    // Side outputs of the rank-r product (saved U, the input gradient's V^T and
+    // U^T planes): every tile of a row panel holds the panel's Z, so the panel's
+    // tiles share the rows, tile qt taking rows [zr0, zr0 + zn) of the 256.  (One
+    // q tile writing them all made its workgroups the last to finish: with a
+    // single round of tiles they set the kernel's end.)
+    const int zrows = (BP + nQt - 1) / nQt;
+    const int zr0 = min(BP, qt * zrows), zn = min(BP, zr0 + zrows) - zr0;
     if constexpr (!ZIN) {
 #pragma unroll
         for (int jt = 0; jt < JT; ++jt)
@@ -789,20 +796,20 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
                 *reinterpret_cast<f32x4*>(Zx + pl * RPAD + jt * 16 + 4 * g4e) = zacc[jt][z];
             }
         lds_barrier();
-        if (a.Zsave != nullptr && qt == 0) {
-            for (int e = tid; e < BP * r; e += NT) {
-                const int pl = e / r, j = e - pl * r;
+        if (a.Zsave != nullptr) {
+            for (int e = tid; e < zn * r; e += NT) {
+                const int pl = zr0 + e / r, j = e % r;
                 if (p0 + pl < P)
                     a.Zsave[(size_t)(p0 + pl) * r + j] =
                         Zx[pl * RPAD + j] * (a.row_scale ? a.row_scale[p0 + pl] : 1.f);
             }
         }
         if constexpr (TRANS) {
-            if (a.Zt_hi != nullptr && qt == 0) {
-                // element (j, pl), pl fastest: each wave stores 128 contiguous bytes per plane
+            if (a.Zt_hi != nullptr) {
+                // element (j, pl), pl fastest: runs of zn contiguous tokens per plane row
                 // (planes token-block major, zt_index: p0 is a multiple of the 128-token block)
-                for (int e = tid; e < BP * r; e += NT) {
-                    const int j = e / BP, pl = e - j * BP, p = p0 + pl;
+                for (int e = tid; e < zn * r; e += NT) {
+                    const int j = e / zn, pl = zr0 + e % zn, p = p0 + pl;
                     if (p >= a.Mp) continue;
                     const float v = p < P ? Zx[pl * RPAD + j] * (a.row_scale ? a.row_scale[p] : 1.f) : 0.f;
                     const float u = p < P ? a.Uin[(size_t)p * r + j] : 0.f;
@@ -820,9 +827,9 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
     // precomputed Z saved row-scaled (RMSNorm in front: Zin is the product with
     // the raw input, the saved U the one with the normalised input; forward only)
     if constexpr (ZIN && !TRANS) {
-        if (a.Zsave != nullptr && qt == 0 && slice <= 0) {
-            for (int e = tid; e < BP * a.z_ld; e += NT) {
-                const int pl = e / a.z_ld, j = e - pl * a.z_ld, p = p0 + pl;
+        if (a.Zsave != nullptr && slice <= 0) {
+            for (int e = tid; e < zn * a.z_ld; e += NT) {
+                const int pl = zr0 + e / a.z_ld, j = e % a.z_ld, p = p0 + pl;
                 if (p < P)
                     a.Zsave[(size_t)p * a.z_ld + j] =
                         a.Zin[(size_t)p * a.z_ld + j] * (a.row_scale ? a.row_scale[p] : 1.f);
