@@ -843,12 +843,138 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
     // one flat loop over (member, rank block) pairs: a nested loop here keeps
     // the accumulators live across two loop levels and spills them
     const int n_it = (m_hi - m_lo + 1) * n_jt;
+    // s z as the MFMA operand: bf16 hi = bf16(s z) of 4 rank columns, then lo = bf16(s z - hi)
+    auto split_hilo = [&](const f32x4& z) {
+        uint32_t hi[4], lo[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float zs = z[i] * s;
+            const __bf16 h = (__bf16)zs;
+            hi[i] = __builtin_bit_cast(uint16_t, h);
+            lo[i] = __builtin_bit_cast(uint16_t, (__bf16)(zs - (float)h));
+        }
+        return u32x4{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
+    };
+    // the rank-r term of a (member, rank block) pair from fragments ef (E) and zv (Z)
+    auto rank_term = [&](const bf16x8 (&ef)[QB], const f32x4 (&zv)[8]) {
+#pragma unroll
+        for (int pi = 0; pi < 8; ++pi) {
+            const bf16x8 zf = as_bf16x8(split_hilo(zv[pi]));
+#pragma unroll
+            for (int qi = 0; qi < QB; ++qi) acc[qi][pi] = mfma16(ef[qi], zf, acc[qi][pi]);
+        }
+    };
+    if constexpr (ZIN && RPAD > 16) {
+        // More than 16 precomputed rank columns: the pairs go in chunks of up to
+        // ZCH whose Z and E slabs the whole workgroup first copies into LDS,
+        // every load of the chunk in flight at once, then reads as fragments:
+        // one global latency per chunk instead of one per rank block.  Z is
+        // staged as the MFMA operand itself (s Z split into bf16 hi / lo once
+        // per element, not once per wave that reads it: the split was most of
+        // a rank block's cost).
+        constexpr int ZCH = 4;
+        constexpr int ZROW = 20;                 // 4-byte words per staged Z row (16 + 4: conflict-free 16-byte reads)
+        constexpr int EROW = 24;                 // bf16 per staged E row (16 + 8)
+        constexpr int ZBLK = BP * ZROW * 4, EBLK = BQ * EROW * 2;
+        static_assert(ZCH * (ZBLK + EBLK) <= SM::TOTAL, "staged rank blocks fit in LDS");
+        static_assert(NT == 2 * BP && NT == 2 * BQ, "staging: two threads per Z and E row");
+        uint8_t* const Zst = smem;
+        uint8_t* const Est = smem + ZCH * ZBLK;
+        const bool e8 = (r & 7) == 0;            // forward E = B rows of r bf16: 16-byte pieces
+        for (int it0 = 0; it0 < n_it; it0 += ZCH) {
+            const int nb = min(ZCH, n_it - it0);
+            f32x4 zl[ZCH][2];
+            u32x4 el[ZCH];
+#pragma unroll
+            for (int b = 0; b < ZCH; ++b) {      // issue every load of the chunk
+                const int it = it0 + b;
+                const int mi = m_lo + it / n_jt, jt = it - (mi - m_lo) * n_jt;
+                const int qlo = member_q0(mi), qhi = member_q0(mi + 1), zc = mi * r;
+                const bool on = b < nb;
+                {   // Z: row tid / 2, 4-float pieces 2 (tid & 1), 2 (tid & 1) + 1
+                    const int p = p0 + (tid >> 1);
+                    const float* const zrow = a.Zin + (size_t)p * a.z_ld + zc;
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const int j = jt * 16 + (2 * (tid & 1) + h) * 4;
+                        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+                        if (on && p < P) {
+                            if (z4) {
+                                if (j < r) v = *reinterpret_cast<const f32x4*>(zrow + j);
+                            } else {
+#pragma unroll
+                                for (int i = 0; i < 4; ++i) v[i] = j + i < r ? zrow[j + i] : 0.f;
+                            }
+                        }
+                        zl[b][h] = v;
+                    }
+                }
+                u32x4 v = {0u, 0u, 0u, 0u};
+                if constexpr (!TRANS) {          // E = B: row q = q0 + tid / 2, rank columns 8 (tid & 1) ..
+                    const int q = q0 + (tid >> 1), j = jt * 16 + 8 * (tid & 1);
+                    if (on && q >= qlo && q < qhi && q < Q) {
+                        const uint16_t* const erow = a.E + (size_t)q * r;
+                        if (e8) {
+                            if (j < r) v = *reinterpret_cast<const u32x4*>(erow + j);
+                        } else {
+                            uint32_t w[8];
+#pragma unroll
+                            for (int i = 0; i < 8; ++i) w[i] = j + i < r ? erow[j + i] : 0u;
+                            v = u32x4{w[0] | (w[1] << 16), w[2] | (w[3] << 16), w[4] | (w[5] << 16),
+                                      w[6] | (w[7] << 16)};
+                        }
+                    }
+                } else {                         // E = A: row j = jt * 16 + tid % 16, columns q0 + 8 (tid / 16) ..
+                    const int j = jt * 16 + (tid & 15), q = q0 + 8 * (tid >> 4);
+                    if (on && j < r && q < Q) v = *reinterpret_cast<const u32x4*>(a.E + (size_t)j * Q + q);
+                }
+                el[b] = v;
+            }
+            lds_barrier();                       // the previous chunk's fragment reads are done
+#pragma unroll
+            for (int b = 0; b < ZCH; ++b) {
+                if (b >= nb) break;
+                // row tid / 2, operand pieces g = 2 (tid & 1), 2 (tid & 1) + 1 (16 bytes each)
+                uint32_t* const zs = reinterpret_cast<uint32_t*>(Zst + b * ZBLK) + (tid >> 1) * ZROW + 8 * (tid & 1);
+                *reinterpret_cast<u32x4*>(zs) = split_hilo(zl[b][0]);
+                *reinterpret_cast<u32x4*>(zs + 4) = split_hilo(zl[b][1]);
+                uint16_t* const es = reinterpret_cast<uint16_t*>(Est + b * EBLK);
+                if constexpr (!TRANS) {          // [q][j] as loaded
+                    *reinterpret_cast<u32x4*>(es + (tid >> 1) * EROW + 8 * (tid & 1)) = el[b];
+                } else {                         // transposed into [q][j]
+                    const int jl = tid & 15, ql = 8 * (tid >> 4);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        es[(ql + i) * EROW + jl] = (uint16_t)(el[b][i >> 1] >> (16 * (i & 1)));
+                }
+            }
+            lds_barrier();
 #pragma unroll 1
-    for (int it = 0; it < n_it; ++it) {
+            for (int b = 0; b < nb; ++b) {
+                const uint16_t* const es = reinterpret_cast<const uint16_t*>(Est + b * EBLK);
+                const uint32_t* const zs = reinterpret_cast<const uint32_t*>(Zst + b * ZBLK);
+                bf16x8 ef[QB];
+#pragma unroll
+                for (int qi = 0; qi < QB; ++qi) {
+                    const u32x2 v = *reinterpret_cast<const u32x2*>(es + (wq * QB * 16 + qi * 16 + l16e) * EROW + 4 * g4e);
+                    ef[qi] = as_bf16x8(u32x4{v[0], v[1], v[0], v[1]});
+                }
+#pragma unroll
+                for (int pi = 0; pi < 8; ++pi) {
+                    const bf16x8 zf = as_bf16x8(*reinterpret_cast<const u32x4*>(
+                        zs + (wp * 128 + ((pi + ZB * wq) & 7) * 16 + l16e) * ZROW + 4 * g4e));
+#pragma unroll
+                    for (int qi = 0; qi < QB; ++qi) acc[qi][pi] = mfma16(ef[qi], zf, acc[qi][pi]);
+                }
+            }
+        }
+    }
+#pragma unroll 1
+    for (int it = 0; it < ((ZIN && RPAD > 16) ? 0 : n_it); ++it) {
         const int mi = m_lo + it / max(n_jt, 1), jt = it - (mi - m_lo) * n_jt;
         const int qlo = ZIN ? member_q0(mi) : 0, qhi = ZIN ? member_q0(mi + 1) : Q, zc = mi * r;
         bf16x8 ef[QB];
-        f32x4 zv[ZIN ? 8 : 1];
+        f32x4 zv[8];
         if (PREF && jt == 0 && mi == m_lo) {
 #pragma unroll
             for (int qi = 0; qi < QB; ++qi) ef[qi] = ef0[qi];
@@ -860,25 +986,14 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
             load_e(jt, ef, qlo, qhi);
             if constexpr (ZIN) load_zin(jt, zv, zc);
         }
+        if constexpr (!ZIN) {
 #pragma unroll
-        for (int pi = 0; pi < 8; ++pi) {
-            const int pl = wp * 128 + ((pi + ZB * wq) & 7) * 16 + l16e;
-            f32x4 z;
-            if constexpr (ZIN) z = zv[pi];
-            else z = *reinterpret_cast<const f32x4*>(Zx + pl * RPAD + jt * 16 + 4 * g4e);
-            uint32_t hi[4], lo[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float zs = z[i] * s;
-                const __bf16 h = (__bf16)zs;
-                hi[i] = __builtin_bit_cast(uint16_t, h);
-                lo[i] = __builtin_bit_cast(uint16_t, (__bf16)(zs - (float)h));
+            for (int pi = 0; pi < 8; ++pi) {
+                const int pl = wp * 128 + ((pi + ZB * wq) & 7) * 16 + l16e;
+                zv[pi] = *reinterpret_cast<const f32x4*>(Zx + pl * RPAD + jt * 16 + 4 * g4e);
             }
-            const bf16x8 zf = as_bf16x8(u32x4{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16),
-                                              lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)});
-#pragma unroll
-            for (int qi = 0; qi < QB; ++qi) acc[qi][pi] = mfma16(ef[qi], zf, acc[qi][pi]);
         }
+        rank_term(ef, zv);
     }
 
     if (!TRANS && a.row_scale != nullptr && !(SPLIT && slice >= 0)) {   // split tiles: in split_finish
