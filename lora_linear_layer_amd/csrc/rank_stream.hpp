@@ -285,15 +285,22 @@ __global__ __launch_bounds__(512) void rank_z_lds(const RankZArgs a) {
     f32x4 acc[JB];
 #pragma unroll
     for (int jb = 0; jb < JB; ++jb) acc[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    bf16x8 yr[D];
+    // Y fragments two slices ahead (2 D loads of 16 bytes in flight per lane):
+    // with one workgroup per CU, one slice ahead left ~64 KB in flight per CU,
+    // about 2 us of the CU's share of HBM bandwidth.  yr[0 .. D) serves the
+    // even slices, yr[D .. 2 D) the odd ones.  The slices run in pairs with
+    // no branch inside (the count rounded up to even: past the chunk F and Y
+    // read zeros and add nothing), so that the compiler's own waits before
+    // each use keep every load of the other slices in flight.
+    bf16x8 yr[2 * D];
     issue_f(0, fs);
 #pragma unroll
-    for (int u = 0; u < D; ++u) yr[u] = ld(u);
-    vmcnt_le<D>();                                     // this wave's part of slice 0 (older than the D Y loads)
+    for (int u = 0; u < 2 * D; ++u) yr[u] = ld(u);
+    vmcnt_le<2 * D>();                                 // this wave's part of slice 0 (older than the 2 D Y loads)
     __syncthreads();
-    for (int sl = 0; sl < nsl; ++sl) {
+    auto slice = [&](int sl, bf16x8* y) {
         const uint8_t* const fb = fs + (sl & 1) * FBYTES;
-        if (sl + 1 < nsl) issue_f(sl + 1, fs + ((sl + 1) & 1) * FBYTES);
+        issue_f(sl + 1, fs + ((sl + 1) & 1) * FBYTES);  // zeros past the chunk
 #pragma unroll
         for (int u = 0; u < D; ++u) {
             bf16x8 ff[JB];
@@ -301,13 +308,15 @@ __global__ __launch_bounds__(512) void rank_z_lds(const RankZArgs a) {
             for (int jb = 0; jb < JB; ++jb)
                 ff[jb] = lds_b128(fb + (jb * 16 + l16) * (SC * 2) + (((u * 4 + g4) ^ l16) << 4));
 #pragma unroll
-            for (int jb = 0; jb < JB; ++jb) acc[jb] = mfma16(ff[jb], yr[u], acc[jb]);
-            yr[u] = ld(sl * D + u + D);                // zeros past the chunk
+            for (int jb = 0; jb < JB; ++jb) acc[jb] = mfma16(ff[jb], y[u], acc[jb]);
+            y[u] = ld(sl * D + u + 2 * D);             // zeros past the chunk
         }
-        if (sl + 1 < nsl) {
-            vmcnt_le<D>();                             // slice sl + 1 (older than this slice's D Y loads)
-            __syncthreads();
-        }
+        vmcnt_le<D>();                                 // slice sl + 1's F and the Y loads older than this slice's D
+        __syncthreads();
+    };
+    for (int sl = 0; sl < nsl; sl += 2) {
+        slice(sl, yr);
+        slice(sl + 1, yr + D);
     }
     vmcnt_le<0>();
     // lane holds Z^T rows j = 16 jb + 4 g4 + e at column m
