@@ -134,7 +134,7 @@ lora_status lora_linear_bwd(const lora_linear_desc* desc,
  * needs more than LORA_NOALLOC_SCRATCH_BYTES of intermediates (large M x r, or
  * many split-M partials) gets LORA_ERR_UNSUPPORTED before anything is enqueued.
  */
-#define LORA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+#define LORA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
 
 lora_status lora_linear_bwd_noalloc(const lora_linear_desc* desc,
                                     const void* dY, const void* X, const void* W,

@@ -25,7 +25,7 @@ LORA_DTYPE_F32 = 1
 
 LORA_FLAG_ACCUM_GRADS = 0x1
 LORA_FLAG_W_TRANSPOSED = 0x2
-LORA_NOALLOC_SCRATCH_BYTES = 32 << 20
+LORA_NOALLOC_SCRATCH_BYTES = 128 << 20
 LORA_MAX_MEMBERS = 8
 LORA_MAX_GROUP_RANK = 192
 
