@@ -704,13 +704,14 @@ lora_status bwd_bf16(const Shape& d, bool quant, const void* dY, const void* X, 
     const bool v_in_tile = dX != nullptr && d.G == 1 && dx_in_tile(quant, r, sp);
     if (!v_in_tile) {
         uint16_t* const BT = reinterpret_cast<uint16_t*>(wsb + plan.off_bt);
-        for (int m = 0; m < d.G; ++m) {
-            uint16_t* const BTm = BT + (size_t)d.r * d.n0[m];
-            LAUNCH("transpose_rank", transpose_rank, dim3((unsigned)cdiv(d.r * d.Nm(m), 256)), dim3(256), 0, st,
-                   B16 + (size_t)d.n0[m] * d.r, BTm, (int)d.Nm(m), r);
-            launch_rank_z(d.M, dY16 + d.n0[m], d.N, d.Nm(m), BTm, d.r, V, rg, (int64_t)m * d.r, zpart, st,
-                          tn.z_div_b);
-        }
+        TransposeRankArgs ta{};
+        ta.G = d.G;
+        ta.r = r;
+        for (int m = 0; m <= d.G; ++m) ta.n0[m] = (int)d.n0[m];
+        LAUNCH("transpose_rank", transpose_rank, dim3((unsigned)cdiv(d.r * d.N, 256)), dim3(256), 0, st, B16, BT, ta);
+        for (int m = 0; m < d.G; ++m)
+            launch_rank_z(d.M, dY16 + d.n0[m], d.N, d.Nm(m), BT + (size_t)d.r * d.n0[m], d.r, V, rg,
+                          (int64_t)m * d.r, zpart, st, tn.z_div_b);
         LAUNCH_CHECK("rank_z_lds(V)");
     }
     // 3. dX = dY W + s V A  (summed over the members: one contraction over all N columns)

@@ -364,12 +364,24 @@ __global__ __launch_bounds__(256) void zt_hilo(const float* __restrict__ z0, con
 }
 
 // F^T rows for the Z-mode pass over dY: out[j][n] = B[n][j].
+// Every member of a group in one launch: member m's B^T [r][N_m] (rows n0[m] ..
+// n0[m + 1] - 1 of B) at out + r n0[m], the members side by side.
+struct TransposeRankArgs {
+    int n0[kMaxMembers + 1];
+    int G, r;
+};
+
 __global__ __launch_bounds__(256) void transpose_rank(const uint16_t* __restrict__ B, uint16_t* __restrict__ out,
-                                                      int N, int r) {
+                                                      const TransposeRankArgs a) {
     const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (e >= (int64_t)r * N) return;
-    const int j = (int)(e / N), n = (int)(e % N);
-    out[e] = B[(size_t)n * r + j];
+    if (e >= (int64_t)a.r * a.n0[a.G]) return;
+    int m = 0;                                          // member whose block holds e
+#pragma unroll
+    for (int k = 1; k < kMaxMembers; ++k) m += (k < a.G && e >= (int64_t)a.r * a.n0[k]) ? 1 : 0;
+    const int64_t loc = e - (int64_t)a.r * a.n0[m];
+    const int nm = a.n0[m + 1] - a.n0[m];
+    const int j = (int)(loc / nm), n = a.n0[m] + (int)(loc % nm);
+    out[e] = B[(size_t)n * a.r + j];
 }
 
 // out[m * out_ld + out_j0 + j] = sum over k < n_parts of part[k * M * w + m * w + j]
