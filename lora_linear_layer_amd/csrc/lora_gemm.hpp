@@ -51,7 +51,8 @@
 // of one row inside one 64-block) and that block's absmax when the stage is
 // issued, and one step later decodes them, codebook[code] * absmax in float32
 // rounded to bf16 (the standalone dequantisation's exact values; the 16
-// possible values of a block are formed once and looked up in registers), into
+// possible values of a block are formed once per lane pair and looked up in
+// registers), into
 // the stage's R tile in the same swizzled layout, before the barrier that
 // publishes the stage.  Every weight is decoded once per workgroup; the
 // reads, MFMAs and epilogue are the 16-bit kernel's.
@@ -185,19 +186,25 @@ struct GemmSmem {
 template <int JT, int QB>
 struct Frags {
     bf16x8 r[QB];     // R, QB q blocks of 16
-    bf16x8 l[8];      // L, 8 p blocks of 16 (slot i = block (i + ZB wq) % 8)
+    bf16x8 l[8];      // L, 8 p blocks of 16 (slot i = block (i + ZROT wq) % 8)
     bf16x8 f[JT];     // F, rank rows
 };
 
 // 4-bit decode in registers.  The 16 values bf16(codebook[n] * absmax) of one
-// absmax block are formed once per lane (16 float32 products, rounded as when
-// each weight's product is formed on its own) and kept as byte tables: lb[g]
-// holds the low bytes of entries 4g .. 4g + 3, hb[g] their high bytes.
-// v_perm_b32 looks up four codes per instruction in each 8-entry half, and one
-// more picks the half by bit 3 of each code.  This replaces one LDS read of the
-// codebook per weight, which held both 4-bit GEMMs back by about 12 %.
+// absmax block are formed once per lane pair (float32 products, rounded as
+// when each weight's product is formed on its own) and kept as byte tables:
+// low bytes in lb, high bytes in hb, four entries per register.  The two lanes
+// of an even / odd pair decode the same block: each forms one 8-entry half
+// (the even lane codes 0..7, the odd lane codes 8..15) and takes the other
+// half from its partner with a DPP swap, so lb / hb[0..1] hold the lane's own
+// half and [2..3] the partner's.  v_perm_b32 looks up four codes per
+// instruction in each half, and one more picks the half by bit 3 of each code
+// (cl flips that choice on odd lanes).  This replaces one LDS read of the
+// codebook per weight, which held both 4-bit GEMMs back by about 12 %; sharing
+// the table removes 20 of the ~200 VALU instructions per stage and lane.
 struct Q4Lut {
     uint32_t lb[4], hb[4];
+    uint32_t cl;        // 0x03020100 (even lane), 0x07060504 (odd lane)
 };
 
 // byte i of the result = byte sel_i (0 .. 7) of the 8-byte value {hi : lo}
@@ -205,14 +212,21 @@ __device__ __forceinline__ uint32_t vperm(uint32_t hi, uint32_t lo, uint32_t sel
     return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
-__device__ __forceinline__ Q4Lut q4_lut(const float* lut, float am) {
+// Every lane of the wave must call this (the swap reads the partner lane).
+__device__ __forceinline__ Q4Lut q4_lut(const float* lut, float am, int odd, uint32_t cl) {
     Q4Lut t;
+    t.cl = cl;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(lut + 4 * g);   // one address for all lanes
+    for (int g = 0; g < 2; ++g) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(lut + 8 * odd + 4 * g);
         const uint32_t t01 = pack_bf16x2(v[0] * am, v[1] * am), t23 = pack_bf16x2(v[2] * am, v[3] * am);
         t.lb[g] = vperm(t23, t01, 0x06040200u);
         t.hb[g] = vperm(t23, t01, 0x07050301u);
+    }
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {       // quad_perm [1, 0, 3, 2]: swap with lane ^ 1
+        t.lb[2 + g] = (uint32_t)__builtin_amdgcn_mov_dpp((int)t.lb[g], 0xB1, 0xF, 0xF, false);
+        t.hb[2 + g] = (uint32_t)__builtin_amdgcn_mov_dpp((int)t.hb[g], 0xB1, 0xF, 0xF, false);
     }
     return t;
 }
@@ -225,7 +239,8 @@ __device__ __forceinline__ void q4_decode8(const Q4Lut& t, uint32_t q, uint32_t*
     for (int h = 0; h < 2; ++h) {
         const uint32_t n = vperm(hn, ln, h ? 0x07030602u : 0x05010400u);   // codes 4h .. 4h + 3, one per byte
         const uint32_t sel = n & 0x07070707u;
-        const uint32_t half = ((n >> 1) & 0x04040404u) | 0x03020100u;      // byte i: i, or i + 4 for codes >= 8
+        // byte i: i for codes in the lane's own half, i + 4 for the partner's
+        const uint32_t half = ((n >> 1) & 0x04040404u) ^ t.cl;
         const uint32_t lo = vperm(vperm(t.lb[3], t.lb[2], sel), vperm(t.lb[1], t.lb[0], sel), half);
         const uint32_t hi = vperm(vperm(t.hb[3], t.hb[2], sel), vperm(t.hb[1], t.hb[0], sel), half);
         o[2 * h] = vperm(hi, lo, 0x05010400u);
@@ -252,6 +267,10 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
     static_assert(ZIN || !Q4, "4-bit GEMMs take Z precomputed");
     static_assert(!SPLIT || ZIN, "split contraction: precomputed Z");
     constexpr int JT = ZIN ? 1 : RPAD / 16;
+    // L fragment slot i holds p block (i + ZROT wq) % 8: with the rank-r product
+    // formed in the tile, slots 0 .. ZB - 1 are the wave's own Z blocks; with Z
+    // precomputed the order is plain, so every fragment read has a constant offset
+    constexpr int ZROT = ZIN ? 0 : ZB;
     constexpr int F_LOADS = SM::F_BYTES / 1024;   // done by waves 0 .. F_LOADS - 1
     static_assert(F_LOADS <= 8, "F tile larger than one load per wave");
     __shared__ __attribute__((aligned(1024))) uint8_t smem[SM::TOTAL];
@@ -381,6 +400,10 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
             }
         }
     };
+    // lanes l and l ^ 1 decode the same absmax block in both directions (the
+    // same row and stage; the input gradient's 64-wide q block) and share its table
+    const int q4odd = lane & 1;
+    const uint32_t q4cl = q4odd ? 0x07060504u : 0x03020100u;
     auto decode_q = [&](int kt) {
         uint8_t* const Rs = smem + (kt & 1) * SM::STAGE + TILE;
         const float* const lut = reinterpret_cast<const float*>(smem + SM::LUT);
@@ -404,7 +427,7 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
             const float am = f16_bits_to_f32((uint16_t)amb);
             const int sh = TRANS ? (unit >> 2) & 1 : 0;
             if (TRANS && sh) qv = u32x4{qv[1], qv[0], qv[3], qv[2]};
-            const Q4Lut tab = q4_lut(lut, am);
+            const Q4Lut tab = q4_lut(lut, am, q4odd, q4cl);
             u32x4 outv[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {    // code dword i -> output chunk i (8 weights)
@@ -507,7 +530,7 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
         }
     };
     auto read_l = [&](const uint8_t* Ls, int kk, int i) -> bf16x8 {
-        return lds_b128(Ls + wp * 16384 + ((i + ZB * wq) & 7) * 2048 + chunk_of(kk));
+        return lds_b128(Ls + wp * 16384 + ((i + ZROT * wq) & 7) * 2048 + chunk_of(kk));
     };
     auto read_f = [&](const uint8_t* Ls, int kk, int jt) -> bf16x8 {
         if constexpr (!TRANS) {
@@ -734,7 +757,7 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
     auto load_zin = [&](int jt, f32x4 (&zv)[8], int zc) {
 #pragma unroll
         for (int pi = 0; pi < 8; ++pi) {
-            const int p = p0 + wp * 128 + ((pi + ZB * wq) & 7) * 16 + l16e;
+            const int p = p0 + wp * 128 + ((pi + ZROT * wq) & 7) * 16 + l16e;
             const float* const zrow = a.Zin + (size_t)p * a.z_ld + zc;
             if (z4) {
                 const int j = jt * 16 + 4 * g4e;
@@ -962,7 +985,7 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
 #pragma unroll
                 for (int pi = 0; pi < 8; ++pi) {
                     const bf16x8 zf = as_bf16x8(*reinterpret_cast<const u32x4*>(
-                        zs + (wp * 128 + ((pi + ZB * wq) & 7) * 16 + l16e) * ZROW + 4 * g4e));
+                        zs + (wp * 128 + ((pi + ZROT * wq) & 7) * 16 + l16e) * ZROW + 4 * g4e));
 #pragma unroll
                     for (int qi = 0; qi < QB; ++qi) acc[qi][pi] = mfma16(ef[qi], zf, acc[qi][pi]);
                 }
@@ -989,7 +1012,7 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
         if constexpr (!ZIN) {
 #pragma unroll
             for (int pi = 0; pi < 8; ++pi) {
-                const int pl = wp * 128 + ((pi + ZB * wq) & 7) * 16 + l16e;
+                const int pl = wp * 128 + ((pi + ZROT * wq) & 7) * 16 + l16e;
                 zv[pi] = *reinterpret_cast<const f32x4*>(Zx + pl * RPAD + jt * 16 + 4 * g4e);
             }
         }
@@ -999,7 +1022,7 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
     if (!TRANS && a.row_scale != nullptr && !(SPLIT && slice >= 0)) {   // split tiles: in split_finish
 #pragma unroll
         for (int pi = 0; pi < 8; ++pi) {
-            const int p = p0 + wp * 128 + ((pi + ZB * wq) & 7) * 16 + l16e;
+            const int p = p0 + wp * 128 + ((pi + ZROT * wq) & 7) * 16 + l16e;
             const float rsc = p < P ? a.row_scale[p] : 0.f;
 #pragma unroll
             for (int qi = 0; qi < QB; ++qi) acc[qi][pi] *= rsc;
@@ -1015,7 +1038,7 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
             const int ql = wq * QB * 16 + qi * 16 + 4 * g4e;
 #pragma unroll
             for (int pi = 0; pi < 8; ++pi) {
-                const int pl = wp * 128 + ((pi + ZB * wq) & 7) * 16 + l16e;
+                const int pl = wp * 128 + ((pi + ZROT * wq) & 7) * 16 + l16e;
                 *reinterpret_cast<f32x4*>(out + pl * BQ + ql) = acc[qi][pi];
             }
         }
@@ -1033,7 +1056,7 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
         const int ql = wq * QB * 16 + qi * 16 + 4 * g4e;
 #pragma unroll
         for (int pi = 0; pi < 8; ++pi) {
-            const int pl = wp * 128 + ((pi + ZB * wq) & 7) * 16 + l16e;
+            const int pl = wp * 128 + ((pi + ZROT * wq) & 7) * 16 + l16e;
             const f32x4 v = acc[qi][pi];
             const u32x2 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
             *reinterpret_cast<u32x2*>(smem + pl * 512 + (((ql >> 3) ^ (pl & 31)) << 4) + (ql & 7) * 2) = o;
