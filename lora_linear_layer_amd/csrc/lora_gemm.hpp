@@ -78,6 +78,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, kRsrcWord3);
 }
 
+// A range known to be below 2^31 bytes (32-bit arithmetic, no clipping).  Base
+// and range are uniform; passing them through readfirstlane says so, which
+// keeps the compiler from wrapping the loads in a per-lane descriptor loop
+// when it has kept a uniform address in vector registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc32(const void* base, int bytes) {
+    const uint64_t b = (uint64_t)(size_t)base;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    void* const ub = (void*)(size_t)(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, __builtin_amdgcn_readfirstlane(bytes), kRsrcWord3);
+}
+
 // 16 bytes per lane from global (rsrc + voff) into LDS at lds_wave_base + 16 * lane.
 // UNTRACKED = true issues it as asm, hidden from the compiler's wait-count
 // bookkeeping: the compiler cannot tell a transposing LDS read
@@ -370,21 +382,32 @@ __global__ __launch_bounds__(g2w::NT) void lora_gemm(const GemmArgs a) {
     const int qp1 = lane & 3, qp2 = (qp1 + 2) & 3;
     u32x4 qregB = {0u, 0u, 0u, 0u};
     uint32_t amB = 0u;
+    // Forward codes and absmax come through buffer resources built per stage
+    // (scalar work) on the stage's first byte of the panel's 256 rows, so each
+    // lane's offsets stay constant and rows past the weight's end read zeros;
+    // the odd stage's pieces of the last row past C read zeros too, and a stage
+    // past C elsewhere is fetched but never decoded.  (The input gradient keeps
+    // plain loads: the same change made its loop slower.)
+    uint32_t qoffA = 0, qoffB = 0, aoffA = 0, aoffB = 0;
+    if constexpr (Q4 && !TRANS) {
+        qoffA = (uint32_t)(qrA * (C >> 1) + 16 * qp1);
+        qoffB = (uint32_t)(qrB * (C >> 1) + 16 * qp2);
+        aoffA = (uint32_t)(qrA * (C >> 6) + (qp1 >> 1)) * 2u;
+        aoffB = (uint32_t)(qrB * (C >> 6) + (qp2 >> 1)) * 2u;
+    }
     auto load_q = [&](int kt0) {
         const int kt = kbase + kt0;              // stage of the whole contraction
         const int c0 = kt * BK;
         if constexpr (!TRANS) {
             if (kt0 & 1) return;                 // fetched with the even stage before it
-            auto piece = [&](int row, int p, u32x4& qv, uint32_t& am) {
-                const int st = kt + (p >> 1);
-                const bool ok = q0 + row < Q && st * BK < C;
-                qv = ok ? *reinterpret_cast<const u32x4*>(a.Rq + (size_t)(q0 + row) * (C >> 1) + (size_t)kt * (BK / 2) +
-                                                          16 * p)
-                        : u32x4{0u, 0u, 0u, 0u};
-                am = ok ? (uint32_t)a.Rabs[(size_t)(q0 + row) * (C >> 6) + st] : 0u;
-            };
-            piece(qrA, qp1, qreg[0], am_reg[0]);
-            piece(qrB, qp2, qregB, amB);
+            const __amdgpu_buffer_rsrc_t rc =
+                make_rsrc32(a.Rq + (size_t)q0 * (C >> 1) + (c0 >> 1), q4_code_bytes(Q, q0, BQ, C, c0));
+            const __amdgpu_buffer_rsrc_t ra =
+                make_rsrc32(a.Rabs + (size_t)q0 * (C >> 6) + (c0 >> 6), q4_absmax_bytes(Q, q0, BQ, C, c0));
+            qreg[0] = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)qoffA, 0, 0);
+            am_reg[0] = __builtin_amdgcn_raw_buffer_load_b16(ra, (int)aoffA, 0, 0);
+            qregB = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)qoffB, 0, 0);
+            amB = __builtin_amdgcn_raw_buffer_load_b16(ra, (int)aoffB, 0, 0);
             return;
         }
 #pragma unroll

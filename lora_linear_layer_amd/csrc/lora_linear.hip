@@ -967,6 +967,9 @@ void gemm_ranges(RangeList& L, const char* name, bool trans, bool quant, bool in
     if (!quant) {
         if (trans && !wt) L.add(name, "W stage (rows c0 .. c0 + 63)", gemm_wt_stage_bytes(C, Q, 0, 0));
         else L.add(name, trans ? "W^T panel" : "W panel", panel_bytes(Q, 0, g2::BQ, C));
+    } else if (!trans) {
+        L.add(name, "4-bit codes (256 rows)", (uint64_t)q4_code_bytes<int64_t>(Q, 0, g2::BQ, C, 0));
+        L.add(name, "absmax (256 rows)", (uint64_t)q4_absmax_bytes<int64_t>(Q, 0, g2::BQ, C, 0));
     }
     if (in_tile) L.add(name, trans ? "B" : "A", trans ? whole_bytes(C, r) : whole_bytes(r, C));
 }

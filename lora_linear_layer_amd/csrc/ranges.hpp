@@ -63,6 +63,25 @@ __host__ __device__ inline uint64_t stream_side_bytes(int64_t rl, int64_t TM) {
     return ((uint64_t)(rl - 1) * kSideBlock + (uint64_t)TM) * 2u;
 }
 
+// 4-bit weights: codes [total][cols / 2] bytes (two per byte) and absmax
+// [total][cols / 64] fp16.  One contraction stage of the 4-bit forward GEMM
+// reads rows [row0, row0 + rows) from column col0 on, the last row only up to
+// its end (256 weight rows at stage column c0).  The host lists them in
+// int64_t; the kernel evaluates them in int (scalar instructions), exact
+// because a weight matrix has fewer than 2^31 elements.
+template <typename I>
+__host__ __device__ inline I q4_rows(I total, I row0, I rows) {    // row0 < total
+    return total - row0 < rows ? total - row0 : rows;
+}
+template <typename I>
+__host__ __device__ inline I q4_code_bytes(I total, I row0, I rows, I cols, I col0) {
+    return (q4_rows(total, row0, rows) - 1) * (cols / 2) + (cols - col0) / 2;
+}
+template <typename I>
+__host__ __device__ inline I q4_absmax_bytes(I total, I row0, I rows, I cols, I col0) {
+    return ((q4_rows(total, row0, rows) - 1) * (cols / 64) + (cols - col0) / 64) * 2;
+}
+
 // Small whole operands: A [r][K], B [N][r], B^T [r][N] (bf16).
 __host__ __device__ inline uint64_t whole_bytes(int64_t rows, int64_t cols) {
     return (uint64_t)rows * (uint64_t)cols * 2u;
