@@ -471,44 +471,79 @@ void launch_gemm(GemmArgs a, bool in_tile, const SplitPlan& sp, hipStream_t st) 
 // Y bf16 [M][C] with row stride ldy; F bf16 rows [f_rows][C]: A itself, or
 // B^T from transpose_rank), streamed over Y by rank_z_lds, up to 192 rank
 // columns per pass.  The contraction is split into z_chunks chunks whose
-// float32 partials partial_sum adds in a fixed order.
+// float32 partials partial_sum adds in a fixed order.  Several members (the
+// linears of a group: their own columns of Y, their own F, their own rank
+// columns of Z, f_rows <= 192) run as one launch; the group's chunks are
+// shared out in proportion to the members' columns, so that their partials
+// together fit where one pass of all the columns would put its own.
+struct ZMember {
+    const uint16_t* Y;      // first column of the member's Y
+    const uint16_t* F;
+    int64_t C;
+    int64_t z_j0;           // first column of the member's Z
+    const float* row_scale;
+};
+
 template <int JB, int SC>
 void launch_rank_z_t(const RankZArgs& a, dim3 grid, hipStream_t st) {
     LAUNCH("rank_z_lds", (rank_z_lds<JB, SC>), grid, dim3(512), 0, st, a);
 }
 
-void launch_rank_z(int64_t M, const uint16_t* Y, int64_t ldy, int64_t C, const uint16_t* F, int64_t f_rows,
-                   float* Z, int64_t z_ld, int64_t z_j0, float* zpart, hipStream_t st, int z_div = 1,
-                   const float* row_scale = nullptr) {
-    const int n_chunk = std::max(1, z_chunks(M, C) / std::max(z_div, 1));
+void launch_rank_z_members(int64_t M, int64_t ldy, const ZMember* mem, int G, int64_t f_rows, float* Z,
+                           int64_t z_ld, float* zpart, hipStream_t st, int z_div = 1) {
+    int64_t c_all = 0;
+    for (int m = 0; m < G; ++m) c_all += mem[m].C;
+    const int total = std::max(1, z_chunks(M, c_all) / std::max(z_div, 1));
     for (int64_t j0 = 0; j0 < f_rows; j0 += kMaxZCols) {
         const int rl = (int)std::min<int64_t>(f_rows - j0, kMaxZCols);
         const int jb = (int)cdiv(rl, 16);
         const int sc = jb > 8 ? 128 : 256;                // F slices of 16 jb rows must fit twice in LDS
-        const int chunk_c = (int)(cdiv(cdiv(C, n_chunk), sc) * sc);
-        const int n_used = (int)cdiv(C, chunk_c);
         RankZArgs a{};
-        a.Y = Y;
-        a.F = F;
         a.ldy = (int)ldy;
         a.M = (int)M;
-        a.C = (int)C;
         a.f_j0 = (int)j0;
         a.rl = rl;
-        a.chunk_c = chunk_c;
-        if (n_used > 1) {                                 // compact partials [chunk][M][rl]
-            a.out = zpart;
-            a.z_ld = rl;
-            a.z_j0 = 0;
-            a.chunk_stride = (size_t)M * rl;
-        } else {
-            a.out = Z;
-            a.z_ld = (int)z_ld;
-            a.z_j0 = (int)(z_j0 + j0);
-            a.chunk_stride = 0;
-            a.row_scale = row_scale;
+        PartialSumArgs ps{};
+        ps.out = Z;
+        ps.M = (int)M;
+        ps.w = rl;
+        ps.out_ld = (int)z_ld;
+        size_t poff = 0;
+        int max_used = 1;
+        bool any_part = false;
+        for (int m = 0; m < G; ++m) {
+            const int64_t C = mem[m].C;
+            const int n_chunk = G == 1 ? total : std::max<int>(1, (int)(total * C / c_all));
+            const int chunk_c = (int)(cdiv(cdiv(C, n_chunk), sc) * sc);
+            const int n_used = (int)cdiv(C, chunk_c);
+            RankZMember& mb = a.mem[m];
+            mb.Y = mem[m].Y;
+            mb.F = mem[m].F;
+            mb.C = (int)C;
+            mb.chunk_c = chunk_c;
+            mb.n_used = n_used;
+            if (n_used > 1) {                             // compact partials [chunk][M][rl]
+                mb.out = zpart + poff;
+                mb.z_ld = rl;
+                mb.z_j0 = 0;
+                mb.chunk_stride = (size_t)M * rl;
+                ps.part[m] = mb.out;
+                ps.n_parts[m] = n_used;
+                ps.out_j0[m] = (int)(mem[m].z_j0 + j0);
+                ps.row_scale[m] = mem[m].row_scale;
+                poff += (size_t)n_used * M * rl;
+                any_part = true;
+            } else {
+                mb.out = Z;
+                mb.z_ld = (int)z_ld;
+                mb.z_j0 = (int)(mem[m].z_j0 + j0);
+                mb.chunk_stride = 0;
+                mb.row_scale = mem[m].row_scale;
+                ps.n_parts[m] = 1;
+            }
+            max_used = std::max(max_used, n_used);
         }
-        const dim3 grid((unsigned)cdiv(M, 128), (unsigned)n_used, 1);
+        const dim3 grid((unsigned)cdiv(M, 128), (unsigned)max_used, (unsigned)G);
         switch (jb) {
             case 1: launch_rank_z_t<1, 256>(a, grid, st); break;
             case 2: launch_rank_z_t<2, 256>(a, grid, st); break;
@@ -517,12 +552,18 @@ void launch_rank_z(int64_t M, const uint16_t* Y, int64_t ldy, int64_t C, const u
             case 5: case 6: case 7: case 8: launch_rank_z_t<8, 256>(a, grid, st); break;
             default: launch_rank_z_t<12, 128>(a, grid, st); break;
         }
-        if (n_used > 1) {
-            const int64_t n = M * rl;
-            LAUNCH("partial_sum", partial_sum, dim3((unsigned)cdiv(n, 1024)), dim3(256), 0, st, zpart, Z, (int)M,
-                   rl, (int)z_ld, (int)(z_j0 + j0), n_used, row_scale);
+        if (any_part) {
+            LAUNCH("partial_sum", partial_sum, dim3((unsigned)cdiv(M * rl, 1024), (unsigned)G), dim3(256), 0, st,
+                   ps);
         }
     }
+}
+
+void launch_rank_z(int64_t M, const uint16_t* Y, int64_t ldy, int64_t C, const uint16_t* F, int64_t f_rows,
+                   float* Z, int64_t z_ld, int64_t z_j0, float* zpart, hipStream_t st, int z_div = 1,
+                   const float* row_scale = nullptr) {
+    const ZMember one{Y, F, C, z_j0, row_scale};
+    launch_rank_z_members(M, ldy, &one, 1, f_rows, Z, z_ld, zpart, st, z_div);
 }
 
 // bf16 planes [G r][Mp] of V^T and U^T in the workspace: V^T hi, V^T lo, U^T hi, U^T lo.
@@ -709,9 +750,10 @@ lora_status bwd_bf16(const Shape& d, bool quant, const void* dY, const void* X, 
         ta.r = r;
         for (int m = 0; m <= d.G; ++m) ta.n0[m] = (int)d.n0[m];
         LAUNCH("transpose_rank", transpose_rank, dim3((unsigned)cdiv(d.r * d.N, 256)), dim3(256), 0, st, B16, BT, ta);
+        ZMember mem[kMaxMembers];
         for (int m = 0; m < d.G; ++m)
-            launch_rank_z(d.M, dY16 + d.n0[m], d.N, d.Nm(m), BT + (size_t)d.r * d.n0[m], d.r, V, rg,
-                          (int64_t)m * d.r, zpart, st, tn.z_div_b);
+            mem[m] = ZMember{dY16 + d.n0[m], BT + (size_t)d.r * d.n0[m], d.Nm(m), (int64_t)m * d.r, nullptr};
+        launch_rank_z_members(d.M, d.N, mem, d.G, d.r, V, rg, zpart, st, tn.z_div_b);
         LAUNCH_CHECK("rank_z_lds(V)");
     }
     // 3. dX = dY W + s V A  (summed over the members: one contraction over all N columns)

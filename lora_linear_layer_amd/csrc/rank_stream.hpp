@@ -235,18 +235,25 @@ __global__ __launch_bounds__(256) void rank_stream(const RankArgs a) {
 // feeds JB MFMAs, so one pass over Y forms up to 16 JB rank columns (JB = 12:
 // 192, with 128-column slices to stay within LDS).  Out-of-range rows, columns
 // and rank rows read zero.  Writes out[y * chunk_stride + m * z_ld + z_j0 + j].
-struct RankZArgs {
-    const uint16_t* Y;
+// The linears of a group run as one launch, member blockIdx.z: each with its
+// own columns of Y (the member's columns of dY), its F, its contraction chunks
+// and its output (its rank columns of Z, or its own region of partials).
+struct RankZMember {
+    const uint16_t* Y;        // the member's first column of Y
     const uint16_t* F;
     float* out;
-    const float* row_scale;   // optional scale of each output row (applied when out is Z itself)
+    const float* row_scale;   // optional scale of each output row (when out is Z itself)
     size_t chunk_stride;      // floats between the partials of two contraction chunks
-    int ldy, z_ld;
-    int M, C, f_j0, rl, z_j0, chunk_c;
+    int C, z_ld, z_j0, chunk_c, n_used;
+};
+
+struct RankZArgs {
+    RankZMember mem[kMaxMembers];
+    int ldy, M, f_j0, rl;
 };
 
 template <int JB, int SC>
-__global__ __launch_bounds__(512) void rank_z_lds(const RankZArgs a) {
+__global__ __launch_bounds__(512) void rank_z_lds(const RankZArgs args) {
     constexpr int D = SC / 32;                         // steps in flight = steps per slice
     constexpr int FBYTES = 16 * JB * SC * 2;           // one F slice
     constexpr int RPL = 1024 / (2 * SC);               // F rows per 1 KB load (2 or 4)
@@ -256,16 +263,18 @@ __global__ __launch_bounds__(512) void rank_z_lds(const RankZArgs a) {
     __shared__ __attribute__((aligned(1024))) uint8_t fs[2 * FBYTES];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int l16 = lane & 15, g4 = lane >> 4;
-    const int M = a.M, C = a.C;
+    const RankZMember& a = args.mem[blockIdx.z];
+    if ((int)blockIdx.y >= a.n_used) return;            // a member with fewer chunks than the grid
+    const int M = args.M, C = a.C, ldy = args.ldy;
     const int m0 = (int)blockIdx.x * 128;
     const int m = m0 + wave * 16 + l16;
     const int cb = (int)blockIdx.y * a.chunk_c;
     const int ce = min(C, cb + a.chunk_c);
     const int nsl = (ce - cb + SC - 1) / SC;
-    const int rl = a.rl;
-    const __amdgpu_buffer_rsrc_t rsY = make_rsrc(a.Y + (size_t)m0 * a.ldy, strided_panel_bytes(M, m0, 128, C, a.ldy));
-    const __amdgpu_buffer_rsrc_t rsF = make_rsrc(a.F + (size_t)a.f_j0 * C, whole_bytes(rl, C));
-    const uint32_t yoff = m < M ? (uint32_t)((m - m0) * a.ldy + cb + 8 * g4) * 2u : kOOB;
+    const int rl = args.rl;
+    const __amdgpu_buffer_rsrc_t rsY = make_rsrc(a.Y + (size_t)m0 * ldy, strided_panel_bytes(M, m0, 128, C, ldy));
+    const __amdgpu_buffer_rsrc_t rsF = make_rsrc(a.F + (size_t)args.f_j0 * C, whole_bytes(rl, C));
+    const uint32_t yoff = m < M ? (uint32_t)((m - m0) * ldy + cb + 8 * g4) * 2u : kOOB;
     // F slice: load i (1 KB) covers rows RPL i .. RPL i + RPL - 1; wave w issues i = FLW w ..
     auto issue_f = [&](int sl, uint8_t* buf) {
 #pragma unroll
@@ -386,12 +395,28 @@ __global__ __launch_bounds__(256) void transpose_rank(const uint16_t* __restrict
 
 // out[m * out_ld + out_j0 + j] = sum over k < n_parts of part[k * M * w + m * w + j]
 // (j < w), added in increasing k: the contraction-chunk partials of one
-// rank_z_lds launch (compact rows of w columns) into its columns of Z.  Each
-// thread owns 4 consecutive partial elements; the partial loads are issued 8
-// at a time so that their latencies overlap (the additions keep the fixed order).
-__global__ __launch_bounds__(256) void partial_sum(const float* __restrict__ part, float* __restrict__ out, int M,
-                                                   int w, int out_ld, int out_j0, int n_parts,
-                                                   const float* __restrict__ row_scale) {
+// rank_z_lds launch (compact rows of w columns) into its columns of Z, for
+// member blockIdx.y of the launch (members with one chunk wrote Z themselves).
+// Each thread owns 4 consecutive partial elements; the partial loads are
+// issued 8 at a time so that their latencies overlap (the additions keep the
+// fixed order).
+struct PartialSumArgs {
+    const float* part[kMaxMembers];
+    const float* row_scale[kMaxMembers];
+    int out_j0[kMaxMembers];
+    int n_parts[kMaxMembers];
+    float* out;
+    int M, w, out_ld;
+};
+
+__global__ __launch_bounds__(256) void partial_sum(const PartialSumArgs args) {
+    const int mem = blockIdx.y;
+    const int n_parts = args.n_parts[mem];
+    if (n_parts <= 1) return;
+    const float* __restrict__ const part = args.part[mem];
+    const float* __restrict__ const row_scale = args.row_scale[mem];
+    float* __restrict__ const out = args.out;
+    const int M = args.M, w = args.w, out_ld = args.out_ld, out_j0 = args.out_j0[mem];
     const int64_t n = (int64_t)M * w;
     const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
     if (e0 >= n) return;
