@@ -478,15 +478,16 @@ void launch_gemm(GemmArgs a, bool in_tile, const SplitPlan& sp, hipStream_t st) 
 // together fit where one pass of all the columns would put its own.
 struct ZMember {
     const uint16_t* Y;      // first column of the member's Y
-    const uint16_t* F;
+    const uint16_t* F;      // F rows [f_rows][C], or (f_ld > 0) B's rows [C][f_ld]
     int64_t C;
     int64_t z_j0;           // first column of the member's Z
     const float* row_scale;
+    int64_t f_ld;           // 0, or B's row stride (a multiple of 8; the same for all members)
 };
 
-template <int JB, int SC>
+template <int JB, int SC, bool FB = false>
 void launch_rank_z_t(const RankZArgs& a, dim3 grid, hipStream_t st) {
-    LAUNCH("rank_z_lds", (rank_z_lds<JB, SC>), grid, dim3(512), 0, st, a);
+    LAUNCH("rank_z_lds", (rank_z_lds<JB, SC, FB>), grid, dim3(512), 0, st, a);
 }
 
 void launch_rank_z_members(int64_t M, int64_t ldy, const ZMember* mem, int G, int64_t f_rows, float* Z,
@@ -494,6 +495,7 @@ void launch_rank_z_members(int64_t M, int64_t ldy, const ZMember* mem, int G, in
     int64_t c_all = 0;
     for (int m = 0; m < G; ++m) c_all += mem[m].C;
     const int total = std::max(1, z_chunks(M, c_all) / std::max(z_div, 1));
+    const bool fb = mem[0].f_ld > 0;                     // F from B's rows (then f_rows <= 128)
     for (int64_t j0 = 0; j0 < f_rows; j0 += kMaxZCols) {
         const int rl = (int)std::min<int64_t>(f_rows - j0, kMaxZCols);
         const int jb = (int)cdiv(rl, 16);
@@ -503,6 +505,7 @@ void launch_rank_z_members(int64_t M, int64_t ldy, const ZMember* mem, int G, in
         a.M = (int)M;
         a.f_j0 = (int)j0;
         a.rl = rl;
+        a.f_ld = (int)mem[0].f_ld;
         PartialSumArgs ps{};
         ps.out = Z;
         ps.M = (int)M;
@@ -544,7 +547,14 @@ void launch_rank_z_members(int64_t M, int64_t ldy, const ZMember* mem, int G, in
             max_used = std::max(max_used, n_used);
         }
         const dim3 grid((unsigned)cdiv(M, 128), (unsigned)max_used, (unsigned)G);
-        switch (jb) {
+        if (fb) {
+            switch (jb) {
+                case 1: launch_rank_z_t<1, 256, true>(a, grid, st); break;
+                case 2: launch_rank_z_t<2, 256, true>(a, grid, st); break;
+                case 3: case 4: launch_rank_z_t<4, 256, true>(a, grid, st); break;
+                default: launch_rank_z_t<8, 256, true>(a, grid, st); break;
+            }
+        } else switch (jb) {
             case 1: launch_rank_z_t<1, 256>(a, grid, st); break;
             case 2: launch_rank_z_t<2, 256>(a, grid, st); break;
             case 3: launch_rank_z_t<3, 256>(a, grid, st); break;
@@ -562,7 +572,7 @@ void launch_rank_z_members(int64_t M, int64_t ldy, const ZMember* mem, int G, in
 void launch_rank_z(int64_t M, const uint16_t* Y, int64_t ldy, int64_t C, const uint16_t* F, int64_t f_rows,
                    float* Z, int64_t z_ld, int64_t z_j0, float* zpart, hipStream_t st, int z_div = 1,
                    const float* row_scale = nullptr) {
-    const ZMember one{Y, F, C, z_j0, row_scale};
+    const ZMember one{Y, F, C, z_j0, row_scale, 0};
     launch_rank_z_members(M, ldy, &one, 1, f_rows, Z, z_ld, zpart, st, z_div);
 }
 
@@ -744,15 +754,24 @@ lora_status bwd_bf16(const Shape& d, bool quant, const void* dY, const void* X, 
     const SplitPlan sp = split_for(tn.bwd_split, d.M, d.K, d.N);
     const bool v_in_tile = dX != nullptr && d.G == 1 && dx_in_tile(quant, r, sp);
     if (!v_in_tile) {
+        // B's rows are whole 16-byte pieces when r % 8 == 0: the pass reads B
+        // itself; otherwise transpose_rank writes every member's B^T first
+        const bool b_rows = d.r % 8 == 0;
         uint16_t* const BT = reinterpret_cast<uint16_t*>(wsb + plan.off_bt);
-        TransposeRankArgs ta{};
-        ta.G = d.G;
-        ta.r = r;
-        for (int m = 0; m <= d.G; ++m) ta.n0[m] = (int)d.n0[m];
-        LAUNCH("transpose_rank", transpose_rank, dim3((unsigned)cdiv(d.r * d.N, 256)), dim3(256), 0, st, B16, BT, ta);
+        if (!b_rows) {
+            TransposeRankArgs ta{};
+            ta.G = d.G;
+            ta.r = r;
+            for (int m = 0; m <= d.G; ++m) ta.n0[m] = (int)d.n0[m];
+            LAUNCH("transpose_rank", transpose_rank, dim3((unsigned)cdiv(d.r * d.N, 256)), dim3(256), 0, st, B16,
+                   BT, ta);
+        }
         ZMember mem[kMaxMembers];
         for (int m = 0; m < d.G; ++m)
-            mem[m] = ZMember{dY16 + d.n0[m], BT + (size_t)d.r * d.n0[m], d.Nm(m), (int64_t)m * d.r, nullptr};
+            mem[m] = b_rows ? ZMember{dY16 + d.n0[m], B16 + (size_t)d.n0[m] * d.r, d.Nm(m), (int64_t)m * d.r,
+                                      nullptr, d.r}
+                            : ZMember{dY16 + d.n0[m], BT + (size_t)d.r * d.n0[m], d.Nm(m), (int64_t)m * d.r,
+                                      nullptr, 0};
         launch_rank_z_members(d.M, d.N, mem, d.G, d.r, V, rg, zpart, st, tn.z_div_b);
         LAUNCH_CHECK("rank_z_lds(V)");
     }

@@ -250,15 +250,29 @@ struct RankZMember {
 struct RankZArgs {
     RankZMember mem[kMaxMembers];
     int ldy, M, f_j0, rl;
+    int f_ld;                 // FB: row stride of F given as B [C][f_ld] (rank columns contiguous)
 };
 
-template <int JB, int SC>
+// FB = true: F(j, c) = B[c][f_j0 + j] from B's own rows (f_ld = its row stride,
+// a multiple of 8), so that V = dY B needs no transposed copy of B: the slice
+// holds SC rows c of 32 JB bytes (rank columns 0 .. 16 JB - 1, zeros past rl),
+// and the fragments are gathered down its columns with ds_read_b64_tr_b16, as
+// the input-gradient GEMM gathers B.  One such read touches rows c, c + 1, c + 2,
+// c + 3 and the same four 8 rows on, 32 bytes each; to give those 8 rows 8
+// distinct bank groups, the 32-byte column slot s of row c is stored at
+// s ^ fb_swz(c) (JB >= 2), and with one slot per row (JB = 1) row c at
+// fb_row(c) (bit 2 flipped by bit 3).  The swizzle is applied on the global
+// side of the DMA, which writes each 1 KB load contiguously.
+template <int JB, int SC, bool FB = false>
 __global__ __launch_bounds__(512) void rank_z_lds(const RankZArgs args) {
     constexpr int D = SC / 32;                         // steps in flight = steps per slice
     constexpr int FBYTES = 16 * JB * SC * 2;           // one F slice
-    constexpr int RPL = 1024 / (2 * SC);               // F rows per 1 KB load (2 or 4)
-    constexpr int FLW = 16 * JB / RPL / 8;             // F loads per wave per slice
-    static_assert(FLW >= 1 && 16 * JB == FLW * 8 * RPL, "F slice is whole loads for 8 waves");
+    constexpr int RPL = FB ? 32 / JB : 1024 / (2 * SC);   // F rows per 1 KB load
+    constexpr int FLW = FB ? JB : 16 * JB / RPL / 8;   // F loads per wave per slice
+    constexpr int ROWB = 32 * JB;                      // FB: bytes of one slice row
+    static_assert(!FB || (SC == 256 && (JB == 1 || JB == 2 || JB == 4 || JB == 8)), "FB: whole rows per load");
+    static_assert(FB || (FLW >= 1 && 16 * JB == FLW * 8 * RPL), "F slice is whole loads for 8 waves");
+    static_assert(!FB || FLW * 8 * RPL == SC, "FB: the slice's rows are whole loads for 8 waves");
     static_assert(2 * FBYTES <= 160 * 1024, "LDS budget");
     __shared__ __attribute__((aligned(1024))) uint8_t fs[2 * FBYTES];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -273,17 +287,40 @@ __global__ __launch_bounds__(512) void rank_z_lds(const RankZArgs args) {
     const int nsl = (ce - cb + SC - 1) / SC;
     const int rl = args.rl;
     const __amdgpu_buffer_rsrc_t rsY = make_rsrc(a.Y + (size_t)m0 * ldy, strided_panel_bytes(M, m0, 128, C, ldy));
-    const __amdgpu_buffer_rsrc_t rsF = make_rsrc(a.F + (size_t)args.f_j0 * C, whole_bytes(rl, C));
+    const __amdgpu_buffer_rsrc_t rsF =
+        FB ? make_rsrc(a.F, whole_bytes(C, args.f_ld)) : make_rsrc(a.F + (size_t)args.f_j0 * C, whole_bytes(rl, C));
     const uint32_t yoff = m < M ? (uint32_t)((m - m0) * ldy + cb + 8 * g4) * 2u : kOOB;
     // F slice: load i (1 KB) covers rows RPL i .. RPL i + RPL - 1; wave w issues i = FLW w ..
+    auto fb_swz = [](int c) -> int {                   // JB >= 2: slot XOR for row c
+        if constexpr (JB == 2) return (c >> 3) & 1;
+        else if constexpr (JB == 4) return ((c >> 1) & 1) | (((c >> 3) & 1) << 1);
+        else return (c & 3) | (((c >> 3) & 1) << 2);
+    };
+    auto fb_row = [](int c) -> int { return c ^ (((c >> 3) & 1) << 2); };   // JB = 1 (its own inverse)
     auto issue_f = [&](int sl, uint8_t* buf) {
 #pragma unroll
         for (int t = 0; t < FLW; ++t) {
             const int i = wave * FLW + t;
-            const int row = RPL * i + lane / (SC / 8);
-            const int col = cb + sl * SC + (((lane % (SC / 8)) ^ (row & 15)) << 3);
-            const uint32_t off = (row < rl && col < ce) ? (uint32_t)(row * C + col) * 2u : kOOB;
-            g2lds16<true>(rsF, buf + i * 1024, off);
+            if constexpr (FB) {                        // slice row p, 16-byte piece q of the load's lane
+                const int p = RPL * i + lane / (2 * JB), q = lane % (2 * JB);
+                int row, j;
+                if constexpr (JB == 1) {
+                    row = fb_row(p);
+                    j = 8 * q;
+                } else {
+                    row = p;
+                    j = 16 * ((q >> 1) ^ fb_swz(p)) + 8 * (q & 1);
+                }
+                const int c = cb + sl * SC + row;
+                const uint32_t off =
+                    (c < ce && j < rl) ? (uint32_t)(c * args.f_ld + args.f_j0 + j) * 2u : kOOB;
+                g2lds16<true>(rsF, buf + i * 1024, off);
+            } else {
+                const int row = RPL * i + lane / (SC / 8);
+                const int col = cb + sl * SC + (((lane % (SC / 8)) ^ (row & 15)) << 3);
+                const uint32_t off = (row < rl && col < ce) ? (uint32_t)(row * C + col) * 2u : kOOB;
+                g2lds16<true>(rsF, buf + i * 1024, off);
+            }
         }
     };
     auto ld = [&](int step) -> bf16x8 {
@@ -314,8 +351,20 @@ __global__ __launch_bounds__(512) void rank_z_lds(const RankZArgs args) {
         for (int u = 0; u < D; ++u) {
             bf16x8 ff[JB];
 #pragma unroll
-            for (int jb = 0; jb < JB; ++jb)
-                ff[jb] = lds_b128(fb + (jb * 16 + l16) * (SC * 2) + (((u * 4 + g4) ^ l16) << 4));
+            for (int jb = 0; jb < JB; ++jb) {
+                if constexpr (FB) {                    // rows c = 32 u + 8 g4 + (0 .. 7), column jb 16 + l16
+                    const int c = u * 32 + g4 * 8 + (l16 >> 2);   // bit 2 clear: c + 4 keeps fb_swz
+                    if constexpr (JB == 1) {
+                        const uint8_t* const p = fb + (l16 & 3) * 8;
+                        ff[jb] = cat_tr(lds_tr4(p + fb_row(c) * ROWB), lds_tr4(p + fb_row(c + 4) * ROWB));
+                    } else {
+                        const uint8_t* const p = fb + c * ROWB + ((jb ^ fb_swz(c)) << 5) + (l16 & 3) * 8;
+                        ff[jb] = cat_tr(lds_tr4(p), lds_tr4(p + 4 * ROWB));
+                    }
+                } else {
+                    ff[jb] = lds_b128(fb + (jb * 16 + l16) * (SC * 2) + (((u * 4 + g4) ^ l16) << 4));
+                }
+            }
 #pragma unroll
             for (int jb = 0; jb < JB; ++jb) acc[jb] = mfma16(ff[jb], y[u], acc[jb]);
             y[u] = ld(sl * D + u + 2 * D);             // zeros past the chunk
