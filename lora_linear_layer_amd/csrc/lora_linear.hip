@@ -664,7 +664,10 @@ lora_status launch_adapter_grads(const Shape& d, const Plan& plan, char* wsb, co
     f.f32_out = 0;
     f.accumulate = (d.flags & LORA_FLAG_ACCUM_GRADS) ? 1 : 0;
     f.a_col_scale = a_col_scale;
-    LAUNCH("grad_final", grad_final, dim3((unsigned)cdiv(d.K * rg + d.N * d.r, 256)), dim3(256), 0, st, f);
+    f.tiled = rg >= 64 ? 1 : 0;
+    const int64_t n_tiles = f.tiled ? cdiv(d.K, 64) * cdiv(rg, 64) : 0;
+    const int64_t n_flat = (f.tiled ? 0 : d.K * rg) + d.N * d.r;
+    LAUNCH("grad_final", grad_final, dim3((unsigned)(n_tiles + cdiv(n_flat, 256))), dim3(256), 0, st, f);
     LAUNCH_CHECK("grad_final");
     return LORA_OK;
 }

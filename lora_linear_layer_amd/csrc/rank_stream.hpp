@@ -507,11 +507,80 @@ struct GradFinalArgs {
     float s;
     int f32_out, accumulate;
     const uint16_t* a_col_scale;   // optional bf16 scale of dA's column k (the RMSNorm weight g)
+    int tiled;                     // dA through LDS tiles (blocks before the element blocks)
 };
 
+// tiled = 1 (ra >= 64): dA in tiles of 64 k x 64 j, one workgroup each, through
+// LDS, so that the partial reads (rows of j) and the transposed dA writes (rows
+// of k) are whole segments instead of one 2-byte write per line; the element
+// blocks after them then cover dB alone.  Every element adds its chunks in the
+// same order either way.
+__device__ __forceinline__ void grad_store(const GradFinalArgs& a, void* dst, size_t o, float v) {
+    if (a.f32_out) {
+        float* p = reinterpret_cast<float*>(dst);
+        if (a.accumulate) v += p[o];
+        p[o] = v;
+    } else {
+        uint16_t* p = reinterpret_cast<uint16_t*>(dst);
+        if (a.accumulate) v += bf16_bits_to_f32(p[o]);
+        p[o] = __builtin_bit_cast(uint16_t, (__bf16)v);
+    }
+}
+
 __global__ __launch_bounds__(256) void grad_final(const GradFinalArgs a) {
+    __shared__ float tile[64 * 65];
     const int64_t na = (int64_t)a.K * a.ra, nb = (int64_t)a.N * a.rb;
-    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int nkt = (a.K + 63) / 64;
+    const int nta = a.tiled ? nkt * ((a.ra + 63) / 64) : 0;
+    if ((int)blockIdx.x < nta) {
+        const int k0 = ((int)blockIdx.x % nkt) * 64, j0 = ((int)blockIdx.x / nkt) * 64;
+        const int lo = threadIdx.x & 63, hi = threadIdx.x >> 6;
+        // sums: element i of the thread is k = k0 + hi + 4 i, j = j0 + lo
+        const int j = j0 + lo;
+        float acc[16];
+        size_t off[16];
+        bool ok[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int k = k0 + hi + 4 * i;
+            ok[i] = j < a.ra && k < a.K;
+            off[i] = ok[i] ? (size_t)k * a.ra + j : 0;
+            acc[i] = 0.f;
+        }
+        int c = 0;
+        for (; c + 2 <= a.n_chunk; c += 2) {        // two chunks of loads in flight, added in chunk order
+            float v0[16], v1[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                v0[i] = ok[i] ? a.ga[(size_t)c * na + off[i]] : 0.f;
+                v1[i] = ok[i] ? a.ga[(size_t)(c + 1) * na + off[i]] : 0.f;
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[i] += v0[i];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[i] += v1[i];
+        }
+        for (; c < a.n_chunk; ++c) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[i] += ok[i] ? a.ga[(size_t)c * na + off[i]] : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int kl = hi + 4 * i;
+            float v = acc[i] * a.s;
+            if (a.a_col_scale && ok[i]) v *= bf16_bits_to_f32(a.a_col_scale[k0 + kl]);
+            tile[lo * 65 + kl] = v;
+        }
+        __syncthreads();
+        // stores: element i is j = j0 + hi + 4 i, k = k0 + lo
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int jl = hi + 4 * i, jj = j0 + jl, k = k0 + lo;
+            if (jj < a.ra && k < a.K) grad_store(a, a.dA, (size_t)jj * a.K + k, tile[jl * 65 + lo]);
+        }
+        return;
+    }
+    const int64_t e = ((int64_t)blockIdx.x - nta) * 256 + threadIdx.x + (a.tiled ? na : 0);
     if (e >= na + nb) return;
     const bool isA = e < na;
     const int64_t f = isA ? e : e - na;
@@ -536,16 +605,7 @@ __global__ __launch_bounds__(256) void grad_final(const GradFinalArgs a) {
     } else {
         o = (size_t)f;
     }
-    void* dst = isA ? a.dA : a.dB;
-    if (a.f32_out) {
-        float* p = reinterpret_cast<float*>(dst);
-        if (a.accumulate) v += p[o];
-        p[o] = v;
-    } else {
-        uint16_t* p = reinterpret_cast<uint16_t*>(dst);
-        if (a.accumulate) v += bf16_bits_to_f32(p[o]);
-        p[o] = __builtin_bit_cast(uint16_t, (__bf16)v);
-    }
+    grad_store(a, isA ? a.dA : a.dB, o, v);
 }
 
 }  // namespace lora
