@@ -606,8 +606,10 @@ lora_status launch_adapter_grads(const Shape& d, const Plan& plan, char* wsb, co
     uint16_t* const ut_hi = zt_plane(plan, wsb, rg, 2);
     uint16_t* const ut_lo = zt_plane(plan, wsb, rg, 3);
     if (!planes_ready) {
-        LAUNCH("zt_hilo", zt_hilo, dim3((unsigned)cdiv(rg * plan.Mp, 256), 2), dim3(256), 0, st, V, U, vt_hi,
-               vt_lo, ut_hi, ut_lo, (int)d.M, (int)plan.Mp, (int)rg, v_row_scale);
+        const int zt_tiled = rg >= 32 ? 1 : 0;
+        const int64_t zt_blocks = zt_tiled ? (plan.Mp / kSideBlock) * cdiv(rg, 32) : cdiv(rg * plan.Mp, 256);
+        LAUNCH("zt_hilo", zt_hilo, dim3((unsigned)zt_blocks, 2), dim3(256), 0, st, V, U, vt_hi, vt_lo, ut_hi,
+               ut_lo, (int)d.M, (int)plan.Mp, (int)rg, v_row_scale, zt_tiled);
         LAUNCH_CHECK("zt_hilo");
     }
     // the problems, by rank padding (16, 32 or 64 columns)

@@ -403,22 +403,69 @@ __global__ __launch_bounds__(512) void rank_z_lds(const RankZArgs args) {
 // rank_stream side planes: hi(j, m) = bf16(Z[m][j]), lo(j, m) = bf16(Z[m][j] - hi),
 // j < r, m < Mp (zero for m >= M), stored at e = zt_index(j, m, r); blockIdx.y
 // selects one of two problems; the first one's rows may carry a scale (rs0).
+// tiled = 1 (r >= 32): one workgroup per 128-token block and 32 rank rows, the
+// block's Z rows read as whole 128-byte segments into LDS and written out as
+// plane rows; otherwise one thread per plane element (reads r floats apart).
+__device__ __forceinline__ void zt_hilo_put(uint16_t* hi, uint16_t* lo, size_t e, float v) {
+    const __bf16 h = (__bf16)v;
+    const __bf16 l = (__bf16)(v - (float)h);
+    hi[e] = __builtin_bit_cast(uint16_t, h);
+    lo[e] = __builtin_bit_cast(uint16_t, l);
+}
+
 __global__ __launch_bounds__(256) void zt_hilo(const float* __restrict__ z0, const float* __restrict__ z1,
                                                uint16_t* __restrict__ hi0, uint16_t* __restrict__ lo0,
                                                uint16_t* __restrict__ hi1, uint16_t* __restrict__ lo1, int M, int Mp,
-                                               int r, const float* __restrict__ rs0) {
+                                               int r, const float* __restrict__ rs0, int tiled) {
+    const float* z = blockIdx.y ? z1 : z0;
+    uint16_t* const hi = blockIdx.y ? hi1 : hi0;
+    uint16_t* const lo = blockIdx.y ? lo1 : lo0;
+    const float* const rs = blockIdx.y ? nullptr : rs0;
+    if (tiled) {
+        __shared__ float tile[32 * 129];
+        const int njt = (r + 31) / 32;
+        const int tb = (int)blockIdx.x / njt, j0 = ((int)blockIdx.x % njt) * 32;
+        const int m0 = tb * kSideBlock;
+        const int t = threadIdx.x;
+        // reads, all issued before the first LDS store: element i is
+        // m = m0 + t / 32 + 8 i, j = j0 + t % 32
+        // (buffer loads: rows past M and columns past r read zeros, no branch per load)
+        const int j = j0 + (t & 31);
+        const int rows = max(0, min(M - m0, kSideBlock));
+        const __amdgpu_buffer_rsrc_t rz = make_rsrc(z + (size_t)m0 * r, (uint64_t)rows * r * 4u);
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int ml = (t >> 5) + 8 * i;
+            const uint32_t off = j < r ? (uint32_t)(ml * r + j) * 4u : kOOB;
+            v[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rz, off, 0, 0));
+        }
+        if (rs) {
+            const __amdgpu_buffer_rsrc_t rr = make_rsrc(rs + m0, (uint64_t)rows * 4u);
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                v[i] *= __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                      rr, (uint32_t)((t >> 5) + 8 * i) * 4u, 0, 0));
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) tile[(t & 31) * 129 + (t >> 5) + 8 * i] = v[i];
+        __syncthreads();
+        // writes: element i is j = j0 + t / 128 + 2 i, m = m0 + t % 128
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int jl = (t >> 7) + 2 * i, jj = j0 + jl;
+            if (jj < r) zt_hilo_put(hi, lo, zt_index(jj, m0 + (t & 127), r), tile[jl * 129 + (t & 127)]);
+        }
+        return;
+    }
     const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (e >= (int64_t)r * Mp) return;
     const int64_t blk = e / ((int64_t)r * kSideBlock);
     const int rem = (int)(e - blk * r * kSideBlock);
     const int j = rem / kSideBlock;
     const int64_t m = blk * kSideBlock + rem % kSideBlock;
-    const float* z = blockIdx.y ? z1 : z0;
-    const float v = m < M ? z[(size_t)m * r + j] * ((!blockIdx.y && rs0) ? rs0[m] : 1.f) : 0.f;
-    const __bf16 h = (__bf16)v;
-    const __bf16 l = (__bf16)(v - (float)h);
-    (blockIdx.y ? hi1 : hi0)[e] = __builtin_bit_cast(uint16_t, h);
-    (blockIdx.y ? lo1 : lo0)[e] = __builtin_bit_cast(uint16_t, l);
+    const float v = m < M ? z[(size_t)m * r + j] * (rs ? rs[m] : 1.f) : 0.f;
+    zt_hilo_put(hi, lo, (size_t)e, v);
 }
 
 // F^T rows for the Z-mode pass over dY: out[j][n] = B[n][j].
