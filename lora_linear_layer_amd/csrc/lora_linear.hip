@@ -495,7 +495,7 @@ void launch_rank_z_members(int64_t M, int64_t ldy, const ZMember* mem, int G, in
     int64_t c_all = 0;
     for (int m = 0; m < G; ++m) c_all += mem[m].C;
     const int total = std::max(1, z_chunks(M, c_all) / std::max(z_div, 1));
-    const bool fb = mem[0].f_ld > 0;                     // F from B's rows (then f_rows <= 128)
+    const bool fb = mem[0].f_ld > 0;                     // F from B's rows (callers keep f_rows <= 128)
     for (int64_t j0 = 0; j0 < f_rows; j0 += kMaxZCols) {
         const int rl = (int)std::min<int64_t>(f_rows - j0, kMaxZCols);
         const int jb = (int)cdiv(rl, 16);
@@ -760,8 +760,9 @@ lora_status bwd_bf16(const Shape& d, bool quant, const void* dY, const void* X, 
     const bool v_in_tile = dX != nullptr && d.G == 1 && dx_in_tile(quant, r, sp);
     if (!v_in_tile) {
         // B's rows are whole 16-byte pieces when r % 8 == 0: the pass reads B
-        // itself; otherwise transpose_rank writes every member's B^T first
-        const bool b_rows = d.r % 8 == 0;
+        // itself (its slices hold up to 128 rank columns, r's limit); otherwise
+        // transpose_rank writes every member's B^T first
+        const bool b_rows = d.r % 8 == 0 && d.r <= 128;
         uint16_t* const BT = reinterpret_cast<uint16_t*>(wsb + plan.off_bt);
         if (!b_rows) {
             TransposeRankArgs ta{};
