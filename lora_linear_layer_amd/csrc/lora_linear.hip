@@ -467,10 +467,10 @@ void launch_gemm(GemmArgs a, bool in_tile, const SplitPlan& sp, hipStream_t st) 
     }
 }
 
-// Z[m][z_j0 + j] = sum_c Y[m][c] F[j][c] for j < f_rows (Z float32 rows of z_ld;
-// Y bf16 [M][C] with row stride ldy; F bf16 rows [f_rows][C]: A itself, or
-// B^T from transpose_rank), streamed over Y by rank_z_lds, up to 192 rank
-// columns per pass.  The contraction is split into z_chunks chunks whose
+// Z[m][z_j0 + j] = sum_c Y[m][c] F(j, c) for j < f_rows (Z float32 rows of z_ld;
+// Y bf16 [M][C] with row stride ldy; F bf16 rows [f_rows][C]: A itself, or B^T
+// from transpose_rank; or B's own rows [C][f_ld] when f_ld > 0), streamed over
+// Y by rank_z_lds, up to 192 rank columns per pass.  The contraction is split into z_chunks chunks whose
 // float32 partials partial_sum adds in a fixed order.  Several members (the
 // linears of a group: their own columns of Y, their own F, their own rank
 // columns of Z, f_rows <= 192) run as one launch; the group's chunks are
