@@ -67,6 +67,7 @@ import hashlib
 import json
 import os
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -587,6 +588,79 @@ def percentile(vals, q):
     return v[lo] + (v[hi] - v[lo]) * (x - lo)
 
 
+def parse_sclk_mhz(text):
+    """Current shader clock from a DRM device's pp_dpm_sclk: the level marked
+    with '*' (lines like '1: 2394Mhz *'); None when no level is marked."""
+    for line in text.splitlines():
+        if line.rstrip().endswith("*"):
+            for tok in line.replace(":", " ").split():
+                t = tok.lower()
+                if t.endswith("mhz") and t[:-3].isdigit():
+                    return int(t[:-3])
+    return None
+
+
+class ClockSampler:
+    """Shader clock (pp_dpm_sclk) and socket power (hwmon power1_input, in
+    microwatts) of the first DRM device that has both, read from sysfs every
+    `period` seconds in a background thread while the steps run.  The chip
+    sets its clock under load by its power limit, so these say what clock the
+    measured rates were taken at."""
+
+    def __init__(self, period=0.02):
+        self.period, self.samples, self.sclk_path, self.power_path = period, [], None, None
+        for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+            sclk = os.path.join(dev, "pp_dpm_sclk")
+            power = sorted(glob.glob(os.path.join(dev, "hwmon", "hwmon*", "power1_input")))
+            if os.path.exists(sclk) and power:
+                self.sclk_path, self.power_path = sclk, power[0]
+                break
+        self._stop = threading.Event()
+        self._thread = None
+
+    def _read(self):
+        try:
+            with open(self.sclk_path) as f:
+                mhz = parse_sclk_mhz(f.read())
+            with open(self.power_path) as f:
+                watts = int(f.read().strip()) / 1e6
+        except (OSError, ValueError):
+            return None
+        return time.perf_counter(), mhz, watts
+
+    def _run(self):
+        while not self._stop.is_set():
+            s = self._read()
+            if s is not None:
+                self.samples.append(s)
+            self._stop.wait(self.period)
+
+    def start(self):
+        if self.sclk_path is not None:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        return self
+
+    def stop(self):
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join()
+
+    def summary(self, t_from):
+        """Medians and p10 / p90 over the samples taken from t_from on."""
+        use = [(m, w) for t, m, w in self.samples if t >= t_from and m is not None]
+        if not use:
+            return None
+        mhz, watts = [m for m, _ in use], [w for _, w in use]
+        return {"sclk_mhz_p50": round(percentile(mhz, 0.5)),
+                "sclk_mhz_p10_p90": [round(percentile(mhz, 0.1)), round(percentile(mhz, 0.9))],
+                "power_w_p50": round(percentile(watts, 0.5)),
+                "power_w_p10_p90": [round(percentile(watts, 0.1)), round(percentile(watts, 0.9))],
+                "samples": len(use),
+                "window": "second half of the device warm-up through the kernel-timer pass",
+                "source": "sysfs pp_dpm_sclk (marked level), hwmon power1_input"}
+
+
 def gemm_rooflines(units, kernel_us, traffic):
     """Roofline entries of the fused GEMMs from their measured mean durations
     (kernel_us: {(unit index, label): [launch durations in us]})."""
@@ -708,6 +782,7 @@ def main(argv=None):
     torch.cuda.synchronize()
     # device warm-up: real steps for a fixed wall time, until the clocks have
     # settled under load (before the tuner's probes and the counted warm-up)
+    clock = ClockSampler().start()
     ramp_steps, ramp0 = 0, time.perf_counter()
     while time.perf_counter() - ramp0 < args.device_warmup_s:
         for _ in range(8):
@@ -786,6 +861,7 @@ def main(argv=None):
         torch.cuda.synchronize()
     finally:
         lla.lora_set_kernel_timer(None)
+        clock.stop()
     kernel_us = {}
     first = {}
     for si, li, kernel, a, b in records:
@@ -816,6 +892,7 @@ def main(argv=None):
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "device_warmup": {"seconds": round(ramp_s, 3), "steps": ramp_steps},
+        "clock": clock.summary(ramp0 + ramp_s / 2),
         "warm_operands": {"ms_per_step": round(warm_ms_step, 4),
                           "value": round(wl.flops() / (warm_ms_step * 1e-3) / 1e12, 2),
                           "note": "one input set reused every step (the headline value rotates input sets)"},

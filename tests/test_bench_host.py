@@ -156,3 +156,19 @@ def test_norm_selection_and_row_kernel_bytes():
     rows = bench.norm_rooflines([u], ks)
     assert [r["kernel"] for r in rows] == ["norm_dx (qkv)", "norm_prep (qkv)"]
     assert rows[1]["achieved"] == pytest.approx((2 * 4096 * 4096 + 4 * 4096 + fold) / 10e-6 / 1e9, rel=1e-3)
+
+
+def test_clock_sampler_parsing_and_summary():
+    """pp_dpm_sclk's marked level is the current clock; the summary keeps only the
+    samples from the given time on and reports medians and p10 / p90."""
+    assert bench.parse_sclk_mhz("S: 101Mhz *\n0: 500Mhz\n1: 2400Mhz\n") == 101
+    assert bench.parse_sclk_mhz("S: 101Mhz\n0: 500Mhz\n1: 2394Mhz *\n") == 2394
+    assert bench.parse_sclk_mhz("0: 500Mhz\n1: 2400Mhz\n") is None
+    c = bench.ClockSampler()
+    c.samples = [(0.0, 157, 253.0), (1.0, 2100, 1340.0), (2.0, 2130, 1350.0), (3.0, 2140, 1360.0),
+                 (4.0, None, 1000.0)]
+    s = c.summary(1.0)
+    assert s["samples"] == 3
+    assert s["sclk_mhz_p50"] == 2130 and s["power_w_p50"] == 1350
+    assert s["sclk_mhz_p10_p90"] == [2106, 2138]
+    assert c.summary(5.0) is None
